@@ -1,0 +1,162 @@
+/*
+ * hils.h - C ABI of the HiLS (Hierarchical Landmark Sparse) attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is that of "Hierarchical Sparse Attention Done Right: Toward
+ * Infinite Context Modeling" (Hu et al.). Each query, offset by a low-rank
+ * calibration (Q-Cal), scores every distant chunk with a surrogate built from
+ * the chunk's landmark key and entropy bias, keeps the top-K chunks, runs exact
+ * softmax attention inside each of them and inside a local sliding window, and
+ * fuses the per-chunk outputs with a softmax over the chunk scores and the
+ * window's log-sum-exp.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; every tensor
+ *   is dense row-major with the layout given below. The library allocates no
+ *   device memory and keeps no state between calls: scratch comes from the
+ *   caller's workspace, sized by hils_workspace_size() for the same problem
+ *   and op. The workspace must be 256-byte aligned.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *   and the call returns without synchronising. Calls on different streams
+ *   with different workspaces may run concurrently.
+ * - Validation happens before anything is enqueued and has no side effects.
+ *   Errors: HILS_ERR_INVALID (null required pointer, size <= 0, Hq % Hkv != 0,
+ *   Nq/Nk inconsistent with the op), HILS_ERR_UNSUPPORTED (a valid problem
+ *   outside what the kernels implement, e.g. d not in {64,128}, S != 64,
+ *   K > 64, Hq/Hkv not in {1,2,4,8}), HILS_ERR_WORKSPACE (ws too small or
+ *   misaligned), HILS_ERR_HIP (a kernel launch failed). A fault inside a
+ *   kernel surfaces at the caller's next synchronisation. Nothing prints,
+ *   aborts or throws across this boundary.
+ *
+ * Notation (the paper's): B batch, Hq query heads, Hkv KV heads, G = Hq/Hkv
+ * (query head h uses KV head h / G), d head dim, S chunk size, C = Nk / S
+ * complete chunks, K top-K, W window, D hidden size, r Q-Cal rank,
+ * scale = 1/sqrt(d) unless given.
+ *
+ * Geometry (a reading of the paper's chunk/window statement, where the pages
+ * leave the boundary open): the query at position i sees the distant chunks
+ * c < n_dist(i) = max(0, floor((i - W + 1) / S)) (chunks whose newest token is
+ * at least W positions older than i) and the window of tokens
+ * [n_dist(i) * S, i].
+ *
+ * Layouts
+ *   q        [B, Hq, Nq, d]      (decode: [B, Hq, d])
+ *   k, v     [B, Hkv, Nk, d]
+ *   kL       [B, Hkv, C, d]      landmark key of each complete chunk
+ *   e        [B, Hkv, C]         entropy bias of each complete chunk
+ *   h        [B, Nq, D]          hidden state feeding Q-Cal (decode: [B, D])
+ *   W_down   [Hq, r, D]          (qcal_shared: [r, D])
+ *   W_up     [Hq, d, r]          (qcal_shared: [d, r])
+ *   o        [B, Hq, Nq, d]      in the input dtype (decode: [B, Hq, d])
+ *   lse      [B, Hq, Nq] fp32    fusion log-normaliser L
+ *   topk_idx [B, Hkv, Nq, K] int32, ascending chunk ids, -1 in unused slots
+ *   gradients: fp32, same shapes as the tensors they belong to.
+ */
+#ifndef HILS_H_
+#define HILS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HILS_OK = 0,
+  HILS_ERR_INVALID = 1,
+  HILS_ERR_UNSUPPORTED = 2,
+  HILS_ERR_WORKSPACE = 3,
+  HILS_ERR_HIP = 4
+} hils_status;
+
+typedef enum { HILS_FP32 = 0, HILS_BF16 = 1 } hils_dtype;
+
+/* Operation ids for hils_workspace_size. */
+typedef enum { HILS_OP_ROUTE = 0, HILS_OP_FWD = 1, HILS_OP_BWD = 2, HILS_OP_DECODE = 3 } hils_op;
+
+typedef struct {
+  int32_t dtype;        /* hils_dtype of q, k, v, kL, e, h, W_down, W_up, o, dO */
+  int32_t B, Hq, Hkv, d;
+  int32_t Nq, Nk;       /* prefill/backward: Nq == Nk (query i at position i);
+                           decode: Nq == 1, Nk = cache capacity */
+  int32_t S, K, W;      /* chunk size, top-K (>= 1), window in tokens (>= 1) */
+  int32_t D, r;         /* Q-Cal hidden size and rank; r == 0 => no Q-Cal */
+  int32_t qcal_shared;  /* 1 => one (W_down, W_up) pair shared by all heads */
+  float scale;          /* 0 => 1/sqrt(d) */
+} hils_problem;
+
+/* Text for a status code (static storage). */
+const char* hils_status_string(hils_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t hils_version(void);
+
+/* Bytes of workspace that `op` needs for problem `p` (written to *bytes). */
+hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes);
+
+/*
+ * Routing only: Q-Cal, surrogate scores, GQA max and top-K selection
+ * (paper: Q-Cal worked example and surrogate-score step of "The
+ * HiLS-Attention Mechanism"; Fig. 3; GQA paragraph of the Q-Cal section).
+ *   s_{h,c} = scale * q_hat_h . kL_{g(h),c} + e_{g(h),c}, c < n_dist(i),
+ *   q_hat = q + W_up (W_down h) (q_hat = q when r == 0);
+ *   the group's selection score is the max over its heads; the K best
+ *   (score desc, lower index first on ties) distant chunks are kept.
+ * Outputs: topk_idx (required); topk_score [B, Hq, Nq, K] fp32 (nullable):
+ * s_{h,c} of each selected chunk in topk_idx order (NaN in unused slots).
+ */
+hils_status hils_route(const hils_problem* p, const void* q, const void* kL, const void* e,
+                       const void* h, const void* W_down, const void* W_up, int32_t* topk_idx,
+                       float* topk_score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Prefill forward (paper Fig. 3 and the engineersofai abstract: per-chunk
+ * attention fused by the retrieval scores). For each row (b, h, i):
+ *   L = log( sum_{c in T} exp(s_{h,c}) + exp(lse_W) ),
+ *   o = sum_{c in T} exp(s_{h,c} - L) O_c + exp(lse_W - L) O_W,
+ * with O_c, lse_c the exact softmax attention of the raw q over chunk c's
+ * S tokens and O_W, lse_W over the window. Writes o, lse and topk_idx (all
+ * required); topk_idx and lse are the saved tensors hils_attn_bwd consumes.
+ */
+hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, const void* v,
+                          const void* kL, const void* e, const void* h, const void* W_down,
+                          const void* W_up, void* o, float* lse, int32_t* topk_idx, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Training backward of hils_attn_fwd with the selection topk_idx held fixed
+ * (the paper trains the landmark keys end to end through the fusion softmax,
+ * Fig. 3 caption; top-K itself is not differentiated). Inputs are the forward
+ * inputs, its outputs o and lse, topk_idx and the upstream gradient dO
+ * [B, Hq, Nq, d]. Outputs (fp32, overwritten, all required except dh):
+ * dq, dk, dv, dkL, de; dW_down, dW_up when r > 0 (ignored when r == 0);
+ * dh [B, Nq, D] (nullable).
+ */
+hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,
+                          const void* kL, const void* e, const void* h, const void* W_down,
+                          const void* W_up, const void* o, const float* lse,
+                          const int32_t* topk_idx, const void* dO, float* dq, float* dk, float* dv,
+                          float* dkL, float* de, float* dW_down, float* dW_up, float* dh,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode step: one new query per sequence at position seq_len[b]-1, its key
+ * and value already in the cache (the paper's per-token decode, Fig. 6).
+ * q [B, Hq, d]; k_cache, v_cache [B, Hkv, Nk, d]; seq_len [B] int32 device
+ * (NULL => every sequence holds Nk tokens; each must be in [1, Nk]);
+ * kL [B, Hkv, Nk/S, d], e [B, Hkv, Nk/S] (only the first seq_len/S are read);
+ * h [B, D] (only when r > 0). Writes o [B, Hq, d], lse [B, Hq] and, if
+ * non-NULL, topk_idx [B, Hkv, K].
+ */
+hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* seq_len, const void* kL, const void* e,
+                        const void* h, const void* W_down, const void* W_up, void* o, float* lse,
+                        int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HILS_H_ */

@@ -1,0 +1,411 @@
+"""HiLS attention: plain fp64 CPU oracle (test infrastructure, not product code).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this module. It shares no code with the GPU library and does not
+import it.
+
+It follows the method as described in "Hierarchical Sparse Attention Done
+Right: Toward Infinite Context Modeling" (Hu et al.; pages: the paperglide
+reader, the engineersofai abstract, the dev.to and nestfrontier summaries),
+step by step and row by row, in float64 NumPy:
+
+  1. Q-Cal (paperglide, "Implementation and Training Recipes", the Q-Cal
+     worked example; dev.to, "Engineering Details"): the scoring query is
+     q_hat = q + W_up (W_down h); token-level attention keeps the raw q.
+  2. Surrogate chunk score (paperglide, "The HiLS-Attention Mechanism", the
+     worked surrogate-score step and Fig. 3): s_c = q_hat . kL_c / sqrt(d) + e_c
+     for every distant chunk, i.e. a complete chunk whose newest token is at
+     least W positions older than the query.
+  3. GQA (paperglide, Q-Cal section, the paragraph on query heads sharing a
+     KV head): each head scores the chunks, the group selects on the
+     maximum over its heads.
+  4. Top-K selection (paperglide, worked example "top-K = 2 chunks are
+     kept"; nestfrontier, "The routing problem"): the K best distant chunks
+     by score, ties going to the lower chunk index.
+  5. Token-level softmax inside each selected chunk and inside the local
+     sliding window (paperglide, "Limitations of Naive Sparse Attention" and
+     the intra-chunk step; nestfrontier, "The routing problem").
+  6. Hierarchical fusion (paperglide Fig. 3: inter-chunk softmax assigns each
+     chunk its mass, the intra-chunk softmax spreads it over the tokens;
+     engineersofai abstract: the per-chunk outputs are fused according to
+     the retrieval scores): a softmax over {s_c of the selected chunks,
+     log-sum-exp of the window} weights the per-chunk outputs and the
+     window output.
+
+Readings taken where the pages are silent (each is listed in the design
+notes of the repository):
+  * the window is every token after the last distant chunk, so it spans
+    W .. W+S-1 tokens and starts on a chunk boundary; its chunk-level term in
+    the fusion is its exact log-sum-exp;
+  * only complete chunks carry a landmark;
+  * the scale 1/sqrt(d) applies to both the surrogate and the token logits
+    (paperglide Q-Cal example divides by sqrt(d); Fig. 3 omits it "for
+    simplicity");
+  * each head fuses with its own scores s_{h,c} over the group's shared set;
+  * fewer than K distant chunks: all are taken; none: plain causal window
+    attention.
+
+The backward pass is not printed on the pages; it is the chain rule applied
+to steps 1-6 with the selected set held fixed (selection is not
+differentiated), and is pinned by finite differences in the tests.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# helpers
+# --------------------------------------------------------------------------
+def f64(x) -> np.ndarray:
+    """Exact upcast of a torch tensor (any dtype) or array to float64 NumPy."""
+    if hasattr(x, "detach"):
+        import torch
+        return x.detach().to(torch.float64).cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def n_distant(i: int, W: int, S: int) -> int:
+    """Number of distant chunks for the query at position i: chunks c with
+    newest token c*S + S - 1 <= i - W."""
+    return max(0, (i - W + 1) // S)
+
+
+def window_start(i: int, W: int, S: int) -> int:
+    return n_distant(i, W, S) * S
+
+
+def logsumexp(x: np.ndarray, axis=-1) -> np.ndarray:
+    m = np.max(x, axis=axis, keepdims=True)
+    return (m + np.log(np.sum(np.exp(x - m), axis=axis, keepdims=True))).squeeze(axis)
+
+
+def softmax(x: np.ndarray, axis=-1) -> np.ndarray:
+    return np.exp(x - np.expand_dims(logsumexp(x, axis), axis))
+
+
+def select_topk(sel: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k best entries of `sel` ordered by (score desc, index
+    asc), returned in ascending index order."""
+    if k <= 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((np.arange(sel.shape[0]), -sel))
+    return np.sort(order[:k])
+
+
+def qcal(q: np.ndarray, hvec: Optional[np.ndarray], W_down: Optional[np.ndarray],
+         W_up: Optional[np.ndarray]):
+    """Calibrated scoring query for each head of one token.
+
+    q: [G, d]; hvec: [D]; W_down: [G, r, D]; W_up: [G, d, r].
+    Returns (q_hat [G, d], u [G, r] or None)."""
+    if W_down is None or W_down.shape[1] == 0:
+        return q.copy(), None
+    u = np.einsum("grD,D->gr", W_down, hvec)
+    dq = np.einsum("gdr,gr->gd", W_up, u)
+    return q + dq, u
+
+
+# --------------------------------------------------------------------------
+# one query position of one KV group
+# --------------------------------------------------------------------------
+@dataclass
+class RowResult:
+    T: np.ndarray           # selected chunk ids, ascending
+    s: np.ndarray           # [G, nd] surrogate scores of all distant chunks
+    sel: np.ndarray         # [nd] group selection score (max over heads)
+    o: np.ndarray           # [G, d]
+    lse: np.ndarray         # [G] fusion log-normaliser L
+    l_W: np.ndarray         # [G] window log-sum-exp
+    O_W: np.ndarray         # [G, d] window output (normalised)
+    l_c: np.ndarray         # [G, |T|] per-chunk log-sum-exp
+    O_c: np.ndarray         # [G, |T|, d] per-chunk outputs (normalised)
+    s_T: np.ndarray         # [G, |T|] scores used in the fusion
+    q_hat: np.ndarray       # [G, d]
+    u: Optional[np.ndarray]  # [G, r]
+
+
+def row_forward(q: np.ndarray, q_hat: np.ndarray, K: np.ndarray, V: np.ndarray,
+                kL: np.ndarray, e: np.ndarray, i: int, S: int, Ktop: int, W: int,
+                scale: float, forced_T: Optional[Sequence[int]] = None,
+                forced_s_T: Optional[np.ndarray] = None, u=None) -> RowResult:
+    """HiLS forward for query position i of one KV group.
+
+    q, q_hat: [G, d]; K, V: [>= i+1, d] keys/values of the group; kL: [C, d];
+    e: [C]. forced_T replaces the selection; forced_s_T ([G, |T|]) replaces
+    the fusion scores of the selected chunks."""
+    nd = n_distant(i, W, S)
+    # step 2: surrogate scores of every distant chunk, per head
+    s = scale * (q_hat @ kL[:nd].T) + e[None, :nd]
+    # step 3/4: group selection on the max over heads, then top-K
+    sel = s.max(axis=0) if nd > 0 else np.zeros(0)
+    if forced_T is None:
+        T = select_topk(sel, min(Ktop, nd))
+    else:
+        T = np.asarray(sorted(int(c) for c in forced_T if c >= 0), dtype=np.int64)
+    s_T = s[:, T] if forced_s_T is None else np.asarray(forced_s_T, dtype=np.float64)
+    # step 5a: window [nd*S, i] (causal), exact softmax
+    ws = nd * S
+    xw = scale * (q @ K[ws:i + 1].T)               # [G, i+1-ws]
+    l_W = logsumexp(xw)
+    O_W = softmax(xw) @ V[ws:i + 1]
+    # step 5b: each selected chunk, exact softmax over its S tokens
+    G, d = q.shape
+    l_c = np.zeros((G, len(T)))
+    O_c = np.zeros((G, len(T), d))
+    for t, c in enumerate(T):
+        xc = scale * (q @ K[c * S:(c + 1) * S].T)  # [G, S]
+        l_c[:, t] = logsumexp(xc)
+        O_c[:, t] = softmax(xc) @ V[c * S:(c + 1) * S]
+    # step 6: fusion softmax over {s_c, c in T} and the window's log-sum-exp
+    terms = np.concatenate([s_T, l_W[:, None]], axis=1)  # [G, |T|+1]
+    L = logsumexp(terms)
+    w = np.exp(terms - L[:, None])
+    o = np.einsum("gt,gtd->gd", w[:, :-1], O_c) + w[:, -1:] * O_W
+    return RowResult(T=T, s=s, sel=sel, o=o, lse=L, l_W=l_W, O_W=O_W, l_c=l_c, O_c=O_c,
+                     s_T=s_T, q_hat=q_hat, u=u)
+
+
+@dataclass
+class RowGrads:
+    dq: np.ndarray        # [G, d] (token path + surrogate path)
+    dq_hat: np.ndarray    # [G, d] surrogate path only
+    ds: np.ndarray        # [G, |T|] gradient of each selected fusion score
+    dlW: np.ndarray       # [G] gradient of the window's log-sum-exp term
+
+
+def row_backward(r: RowResult, q: np.ndarray, K: np.ndarray, V: np.ndarray, kL: np.ndarray,
+                 i: int, S: int, W: int, scale: float, dO: np.ndarray,
+                 dK: np.ndarray, dV: np.ndarray, dkL: np.ndarray, de: np.ndarray) -> RowGrads:
+    """Chain rule through row_forward with the selection held fixed.
+
+    Accumulates into dK, dV ([N, d]), dkL ([C, d]) and de ([C]); returns the
+    per-row query gradients."""
+    G, d = q.shape
+    T = r.T
+    nd = n_distant(i, W, S)
+    ws = nd * S
+    D = np.einsum("gd,gd->g", dO, r.o)                       # dO . O
+    w_c = np.exp(r.s_T - r.lse[:, None])                       # fusion weights
+    w_W = np.exp(r.l_W - r.lse)
+    delta_c = np.einsum("gd,gtd->gt", dO, r.O_c)               # dO . O_c
+    delta_W = np.einsum("gd,gd->g", dO, r.O_W)
+    ds = w_c * (delta_c - D[:, None])                           # d loss / d s_c
+    dlW = w_W * (delta_W - D)
+    dq = np.zeros((G, d))
+    # window tokens: a_j = exp(x_j - L); dx_j = a_j (dO.v_j - D)
+    xw = scale * (q @ K[ws:i + 1].T)
+    a = np.exp(xw - r.lse[:, None])
+    dp = dO @ V[ws:i + 1].T
+    dx = a * (dp - D[:, None])
+    dq += scale * dx @ K[ws:i + 1]
+    dK[ws:i + 1] += scale * dx.T @ q
+    dV[ws:i + 1] += a.T @ dO
+    # selected chunk tokens: a_j = w_c p_j; dx_j = a_j (dO.v_j - delta_c)
+    for t, c in enumerate(T):
+        sl = slice(c * S, (c + 1) * S)
+        xc = scale * (q @ K[sl].T)
+        p = np.exp(xc - r.l_c[:, t:t + 1])
+        a = w_c[:, t:t + 1] * p
+        dp = dO @ V[sl].T
+        dx = a * (dp - delta_c[:, t:t + 1])
+        dq += scale * dx @ K[sl]
+        dK[sl] += scale * dx.T @ q
+        dV[sl] += a.T @ dO
+    # surrogate path: s_c = scale q_hat . kL_c + e_c
+    dq_hat = scale * ds @ kL[T] if len(T) else np.zeros((G, d))
+    if len(T):
+        dkL[T] += scale * ds.T @ r.q_hat
+        de[T] += ds.sum(axis=0)
+    return RowGrads(dq=dq + dq_hat, dq_hat=dq_hat, ds=ds, dlW=dlW)
+
+
+# --------------------------------------------------------------------------
+# whole-tensor drivers
+# --------------------------------------------------------------------------
+def _scale(d, scale):
+    return 1.0 / math.sqrt(d) if not scale else float(scale)
+
+
+class Problem:
+    """fp64 copies of one call's inputs (prefill layout, see workloads)."""
+
+    def __init__(self, t: dict, S: int, K: int, W: int, scale: Optional[float] = None):
+        self.q = f64(t["q"])
+        self.k = f64(t["k"])
+        self.v = f64(t["v"])
+        self.kL = f64(t["kL"])
+        self.e = f64(t["e"])
+        self.h = f64(t["h"]) if t.get("h") is not None else None
+        self.W_down = f64(t["W_down"]) if t.get("W_down") is not None else None
+        self.W_up = f64(t["W_up"]) if t.get("W_up") is not None else None
+        self.S, self.K, self.W = S, K, W
+        self.B, self.Hq = self.q.shape[0], self.q.shape[1]
+        self.Hkv = self.k.shape[1]
+        self.G = self.Hq // self.Hkv
+        self.d = self.q.shape[-1]
+        self.scale = _scale(self.d, scale)
+
+    def heads(self, g):
+        return slice(g * self.G, (g + 1) * self.G)
+
+    def qhat_row(self, b, g, i, q_row):
+        if self.W_down is None:
+            return q_row.copy(), None
+        hs = self.heads(g)
+        return qcal(q_row, self.h[b, i], self.W_down[hs], self.W_up[hs])
+
+
+def hils_forward(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
+                 rows: Optional[Sequence[int]] = None, batches: Optional[Sequence[int]] = None,
+                 groups: Optional[Sequence[int]] = None, forced_topk=None, keep_rows=False):
+    """Prefill forward. Returns dict with o [B,Hq,N,d], lse [B,Hq,N],
+    topk [B,Hkv,N,K] (ascending, -1 padded). When rows/batches/groups are
+    given only those (b, g, i) are computed (others stay NaN / -2)."""
+    P = Problem(t, S, K, W, scale)
+    B, Hq, N, d = P.q.shape
+    o = np.full((B, Hq, N, d), np.nan)
+    lse = np.full((B, Hq, N), np.nan)
+    topk = np.full((B, P.Hkv, N, K), -2, dtype=np.int64)
+    rowres = {}
+    forced = None if forced_topk is None else np.asarray(forced_topk)
+    for b in (range(B) if batches is None else batches):
+        for g in (range(P.Hkv) if groups is None else groups):
+            hs = P.heads(g)
+            for i in (range(N) if rows is None else rows):
+                q_row = P.q[b, hs, i]
+                q_hat, u = P.qhat_row(b, g, i, q_row)
+                fT = None if forced is None else forced[b, g, i]
+                r = row_forward(q_row, q_hat, P.k[b, g], P.v[b, g], P.kL[b, g], P.e[b, g], i,
+                                S, K, W, P.scale, forced_T=fT, u=u)
+                o[b, hs, i] = r.o
+                lse[b, hs, i] = r.lse
+                topk[b, g, i] = -1
+                topk[b, g, i, :len(r.T)] = r.T
+                if keep_rows:
+                    rowres[(b, g, i)] = r
+    out = dict(o=o, lse=lse, topk=topk)
+    if keep_rows:
+        out["rows"] = rowres
+    return out
+
+
+def hils_backward(t: dict, dO, S: int, K: int, W: int, scale: Optional[float] = None,
+                  forced_topk=None, batches: Optional[Sequence[int]] = None,
+                  groups: Optional[Sequence[int]] = None):
+    """Training backward (whole sequences of the chosen batches / groups).
+
+    Returns fp64 gradients dq, dk, dv, dkL, de, dW_down, dW_up, dh (Q-Cal ones
+    only when Q-Cal is on), plus the forward outputs it recomputed."""
+    P = Problem(t, S, K, W, scale)
+    dO = f64(dO)
+    B, Hq, N, d = P.q.shape
+    C = P.kL.shape[2]
+    dq = np.zeros_like(P.q)
+    dk = np.zeros_like(P.k)
+    dv = np.zeros_like(P.v)
+    dkL = np.zeros_like(P.kL)
+    de = np.zeros_like(P.e)
+    qc = P.W_down is not None
+    dWd = np.zeros_like(P.W_down) if qc else None
+    dWu = np.zeros_like(P.W_up) if qc else None
+    dh = np.zeros_like(P.h) if qc else None
+    o = np.full((B, Hq, N, d), np.nan)
+    lse = np.full((B, Hq, N), np.nan)
+    topk = np.full((B, P.Hkv, N, K), -2, dtype=np.int64)
+    forced = None if forced_topk is None else np.asarray(forced_topk)
+    for b in (range(B) if batches is None else batches):
+        for g in (range(P.Hkv) if groups is None else groups):
+            hs = P.heads(g)
+            for i in range(N):
+                q_row = P.q[b, hs, i]
+                q_hat, u = P.qhat_row(b, g, i, q_row)
+                fT = None if forced is None else forced[b, g, i]
+                r = row_forward(q_row, q_hat, P.k[b, g], P.v[b, g], P.kL[b, g], P.e[b, g], i,
+                                S, K, W, P.scale, forced_T=fT, u=u)
+                o[b, hs, i] = r.o
+                lse[b, hs, i] = r.lse
+                topk[b, g, i] = -1
+                topk[b, g, i, :len(r.T)] = r.T
+                gr = row_backward(r, q_row, P.k[b, g], P.v[b, g], P.kL[b, g], i, S, W, P.scale,
+                                  dO[b, hs, i], dk[b, g], dv[b, g], dkL[b, g], de[b, g])
+                dq[b, hs, i] = gr.dq
+                if qc:
+                    # q_hat = q + W_up u, u = W_down h: back through the low-rank map
+                    ddq = gr.dq_hat                                   # [G, d]
+                    dWu[hs] += np.einsum("gd,gr->gdr", ddq, u)
+                    du = np.einsum("gdr,gd->gr", P.W_up[hs], ddq)
+                    dWd[hs] += np.einsum("gr,D->grD", du, P.h[b, i])
+                    dh[b, i] += np.einsum("grD,gr->D", P.W_down[hs], du)
+    return dict(dq=dq, dk=dk, dv=dv, dkL=dkL, de=de, dW_down=dWd, dW_up=dWu, dh=dh,
+                o=o, lse=lse, topk=topk)
+
+
+def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
+                batches: Optional[Sequence[int]] = None, groups: Optional[Sequence[int]] = None,
+                forced_topk=None):
+    """Single-query decode: the new token sits at position seq_len[b]-1 and
+    its key/value are already in the cache. q: [B,Hq,d]; k/v cache
+    [B,Hkv,Nmax,d]; h: [B,D]. Returns o [B,Hq,d], lse [B,Hq], topk [B,Hkv,K]."""
+    q = f64(t["q"])
+    B, Hq, d = q.shape
+    Hkv = t["k"].shape[1]
+    G = Hq // Hkv
+    sc = _scale(d, scale)
+    seq = [int(x) for x in (t["seq_len"].tolist() if t.get("seq_len") is not None
+                            else [t["k"].shape[2]] * B)]
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    topk = np.full((B, Hkv, K), -2, dtype=np.int64)
+    qc = t.get("W_down") is not None
+    for b in (range(B) if batches is None else batches):
+        n = seq[b]
+        i = n - 1
+        for g in (range(Hkv) if groups is None else groups):
+            hs = slice(g * G, (g + 1) * G)
+            Kc = f64(t["k"][b, g, :n])
+            Vc = f64(t["v"][b, g, :n])
+            C = n // S
+            kL = f64(t["kL"][b, g, :C])
+            e = f64(t["e"][b, g, :C])
+            if qc:
+                q_hat, u = qcal(q[b, hs], f64(t["h"][b]), f64(t["W_down"][hs]), f64(t["W_up"][hs]))
+            else:
+                q_hat, u = q[b, hs].copy(), None
+            fT = None if forced_topk is None else np.asarray(forced_topk)[b, g]
+            r = row_forward(q[b, hs], q_hat, Kc, Vc, kL, e, i, S, K, W, sc, forced_T=fT, u=u)
+            o[b, hs] = r.o
+            lse[b, hs] = r.lse
+            topk[b, g] = -1
+            topk[b, g, :len(r.T)] = r.T
+    return dict(o=o, lse=lse, topk=topk)
+
+
+def hils_route(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
+               rows: Optional[Sequence[int]] = None, batches=None, groups=None):
+    """Selection only: topk [B,Hkv,N,K] and the sorted selection scores of
+    every row (for near-tie checks): sel_sorted[(b,g,i)] = scores in
+    (score desc, index asc) order."""
+    P = Problem(t, S, K, W, scale)
+    B, Hq, N, d = P.q.shape
+    topk = np.full((B, P.Hkv, N, K), -2, dtype=np.int64)
+    ranked = {}
+    for b in (range(B) if batches is None else batches):
+        for g in (range(P.Hkv) if groups is None else groups):
+            hs = P.heads(g)
+            for i in (range(N) if rows is None else rows):
+                q_row = P.q[b, hs, i]
+                q_hat, _ = P.qhat_row(b, g, i, q_row)
+                nd = n_distant(i, W, S)
+                s = P.scale * (q_hat @ P.kL[b, g, :nd].T) + P.e[b, g, None, :nd]
+                sel = s.max(axis=0) if nd else np.zeros(0)
+                T = select_topk(sel, min(K, nd))
+                topk[b, g, i] = -1
+                topk[b, g, i, :len(T)] = T
+                order = np.lexsort((np.arange(nd), -sel))
+                ranked[(b, g, i)] = (sel[order], order)
+    return dict(topk=topk, ranked=ranked)

@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the HiLS attention hot path on one MI355X.
+
+Default workload: the 345M-shape prefill forward (batch 4, 16 heads, d 64,
+8192 tokens, chunk 64, top-16, 512-token window, Q-Cal rank 32 from hidden
+1024), bf16, seeded synthetic inputs resident in HBM. One step = one
+hils_attn_fwd call: Q-Cal, routing (scores + GQA max + top-K), window and
+selected-chunk attention, fusion.
+
+Prints ONE JSON line: prefill tokens/s, the roofline of the dominant kernel
+(its average duration measured with HIP events around each of its launches in
+the timed region) and the fp64 CPU oracle timed on a bounded sample of the
+same workload. Optional extra legs: --decode (the 512K-context decode step,
+microseconds per step against the HBM roofline) and --train (forward +
+backward tokens/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+
+
+def n_distant(i, W, S):
+    return max(0, (i - W + 1) // S)
+
+
+def fwd_algorithmic_flops(wl):
+    """Flops the method must do in the attention kernel: 4*d per
+    (query head, attended token) over the window and the selected chunks."""
+    win = 0
+    chk = 0
+    for i in range(wl.N):
+        nd = n_distant(i, wl.W, wl.S)
+        win += i + 1 - nd * wl.S
+        chk += min(wl.K, nd) * wl.S
+    per_pair = 4 * wl.d
+    rows = wl.B * wl.Hq
+    return rows * per_pair * win, rows * per_pair * chk
+
+
+def route_algorithmic_flops(wl):
+    tot = sum(n_distant(i, wl.W, wl.S) for i in range(wl.N))
+    return wl.B * wl.Hq * 2 * wl.d * tot
+
+
+def qcal_algorithmic_flops(wl):
+    return wl.B * wl.N * wl.Hq * (2 * wl.r * wl.D + 2 * wl.d * wl.r) if wl.r else 0
+
+
+def timed_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def event_ring(n, torch):
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    sp = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in st + sp:
+        e.record()  # creates the HIP event handle
+    torch.cuda.synchronize()
+    return st, sp
+
+
+def avg_ms(st, sp):
+    return sum(a.elapsed_time(b) for a, b in zip(st, sp)) / len(st)
+
+
+def cpu_baseline_prefill(wl, budget_s=12.0):
+    """The fp64 oracle on stride-sampled query positions of a few (batch, KV
+    group) pairs, run until about budget_s seconds of oracle time, then
+    extrapolated to tokens/s of the whole workload (a token costs Hkv
+    group-rows). The oracle is single-threaded NumPy/Python."""
+    from workloads import make_group_inputs
+    from oracle import hils_oracle as H
+    stride = 64
+    groups = [(b, (5 * b) % wl.Hkv) for b in range(wl.B)]
+    rows_done = 0
+    t_used = 0.0
+    passes = 0
+    for b, g in groups:
+        t = make_group_inputs(wl, b, g)
+        for offset in range(0, stride, 7):
+            rows = list(range(offset, wl.N, stride))
+            t0 = time.perf_counter()
+            H.hils_forward(t, wl.S, wl.K, wl.W, rows=rows)
+            t_used += time.perf_counter() - t0
+            rows_done += len(rows)
+            passes += 1
+            if t_used >= budget_s:
+                break
+        if t_used >= budget_s:
+            break
+    per_row = t_used / rows_done
+    tok_s = 1.0 / (per_row * wl.Hkv)
+    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} query positions ({passes} passes of every {stride}th position "
+                      f"over {min(len(groups), 1 + passes // 10)} (batch, KV head) pairs), "
+                      f"{t_used:.1f} s of fp64 oracle time on one core, scaled by {wl.Hkv} KV "
+                      f"heads per token"}
+
+
+def bench_prefill(args, torch, L, W_):
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS[args.workload]
+    t = make_inputs(wl, device="cuda")
+    bufs = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+
+    def step():
+        L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W, h=t.get("h"),
+                        W_down=t.get("W_down"), W_up=t.get("W_up"), out=bufs)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    rings = {}
+    for sid in (L.STEP_QCAL, L.STEP_ROUTE, L.STEP_ATTN_FWD):
+        rings[sid] = event_ring(args.steps, torch)
+        L.hils_set_timing_events(sid, *rings[sid])
+    sec = timed_steps(step, args.steps, 0, torch)
+    for sid in rings:
+        L.hils_set_timing_events(sid)
+    k_ms = {sid: avg_ms(*rings[sid]) for sid in rings}
+    win_f, chk_f = fwd_algorithmic_flops(wl)
+    attn_flops = win_f + chk_f
+    attn_tf = attn_flops / (k_ms[L.STEP_ATTN_FWD] * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    tokens = wl.B * wl.N
+    res = {
+        "metric": "HiLS prefill tokens/s (345M-shape forward: Q-Cal + routing + window/chunk "
+                  "attention + fusion)",
+        "value": tokens / sec, "unit": "tokens/s", "ms_per_step": sec * 1e3,
+        "roofline": {"bound": "mfma", "achieved": attn_tf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": attn_tf / peak, "traffic": None,
+                     "kernel": "k_attn_fwd (window + selected chunks + fusion)",
+                     "algorithmic_flop_per_launch": attn_flops,
+                     "avg_launch_ms": k_ms[L.STEP_ATTN_FWD]},
+        "steps_ms": {"qcal": k_ms[L.STEP_QCAL], "route": k_ms[L.STEP_ROUTE],
+                     "attn_fwd": k_ms[L.STEP_ATTN_FWD]},
+        "step_tflops": {
+            "qcal": qcal_algorithmic_flops(wl) / (k_ms[L.STEP_QCAL] * 1e-3) / 1e12,
+            "route": route_algorithmic_flops(wl) / (k_ms[L.STEP_ROUTE] * 1e-3) / 1e12,
+            "attn_window_plus_chunks": attn_tf},
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "config": {"workload": wl.name, "batch": wl.B, "heads_q": wl.Hq, "heads_kv": wl.Hkv,
+                   "head_dim": wl.d, "seq_len": wl.N, "chunk": wl.S, "top_k": wl.K,
+                   "window": wl.W, "qcal_hidden": wl.D, "qcal_rank": wl.r},
+    }
+    del t, bufs
+    torch.cuda.empty_cache()
+    return res, wl
+
+
+def decode_bytes(wl):
+    """Algorithmic HBM bytes of one decode step: every distant landmark key and
+    bias, the K selected chunks and the window, K and V, per (sequence, KV head)."""
+    el = 2 if wl.dtype == "bf16" else 4
+    tot = 0
+    for n in ([wl.N] * wl.B if wl.seq_len is None else wl.seq_len):
+        i = n - 1
+        nd = n_distant(i, wl.W, wl.S)
+        toks = min(wl.K, nd) * wl.S + (i + 1 - nd * wl.S)
+        tot += wl.Hkv * (nd * (wl.d * el + el) + toks * 2 * wl.d * el)
+    return tot
+
+
+def bench_decode(args, torch, L):
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS[args.decode_workload]
+    t = make_inputs(wl, device="cuda")
+    bufs = L.decode_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+    # a buffer larger than the 256 MiB last-level cache, rewritten between steps
+    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+
+    def step():
+        L.hils_decode(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
+                      seq_len=t["seq_len"], h=t.get("h"), W_down=t.get("W_down"),
+                      W_up=t.get("W_up"), out=bufs)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    n = args.decode_steps
+    st, sp = event_ring(n, torch)
+    L.hils_set_timing_events(L.STEP_DECODE, st, sp)
+    for _ in range(n):
+        flush.fill_(1.0)
+        step()
+    torch.cuda.synchronize()
+    L.hils_set_timing_events(L.STEP_DECODE)
+    times = sorted(a.elapsed_time(b) for a, b in zip(st, sp))
+    med = times[len(times) // 2]
+    nbytes = decode_bytes(wl)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    out = {"workload": wl.name, "us_per_step": med * 1e3, "median_of": n, "cold_cache": True,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+    del t, bufs, flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_345m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--decode", action="store_true", help="also time the 512K decode step")
+    ap.add_argument("--decode-workload", default="decode_7b_512k")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import learnable_chunk_sparse_amd as L
+    L.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    res, wl = bench_prefill(args, torch, L, None)
+    if args.decode:
+        res["decode"] = bench_decode(args, torch, L)
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, args.cpu_budget)
+    res["vs_baseline"] = None
+    line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": res.pop("vs_baseline"), "dtype": res.pop("dtype"),
+            "data": "synthetic (seeded counter-based generator)", "config": res.pop("config")}
+    line.update(res)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -155,6 +155,31 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
                         const void* h, const void* W_down, const void* W_up, void* o, float* lse,
                         int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement hook (not part of the method): ids of the launch steps whose
+ * device time can be recorded with caller-owned events.
+ */
+typedef enum {
+  HILS_STEP_QCAL = 0,       /* Q-Cal (fp32 calibrated queries) */
+  HILS_STEP_ROUTE = 1,      /* scoring + GQA max + top-K (prefill) */
+  HILS_STEP_ATTN_FWD = 2,   /* window + selected chunks + fusion (prefill) */
+  HILS_STEP_DECODE = 3,     /* the whole decode step after Q-Cal */
+  HILS_STEP_BWD = 4,        /* the whole backward */
+  HILS_STEP_COUNT = 5
+} hils_step;
+
+/*
+ * Registers a ring of n (start, stop) event pairs (hipEvent_t handles created
+ * by the caller, n >= 1) for step `step`: every later launch of that step
+ * records start[j] before and stop[j] after it on the call's stream, with j
+ * cycling 0, 1, ..., n-1, 0, ... from the registration on. n == 0 or NULL
+ * arrays unregister. The handles are borrowed (the caller keeps them alive
+ * while registered). Process-wide state: meant for benchmarks, not for
+ * concurrent use from several threads. Returns HILS_ERR_INVALID for a bad
+ * step id or n < 0.
+ */
+hils_status hils_set_timing_events(int32_t step, void* const* start, void* const* stop, int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

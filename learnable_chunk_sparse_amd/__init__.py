@@ -1,0 +1,256 @@
+"""HiLS attention for AMD Instinct MI355X: thin Python binding of libhils.so.
+
+The functions here only marshal arguments: they allocate outputs and the
+workspace with torch on the inputs' device, pass raw device pointers and the
+current HIP stream to the C ABI (include/hils.h) and raise on a non-zero
+status. Every step of the computation runs in the library's HIP kernels;
+there is no fallback path. If libhils.so is missing, importing succeeds but
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhils.so")
+
+HILS_FP32, HILS_BF16 = 0, 1
+OP_ROUTE, OP_FWD, OP_BWD, OP_DECODE = 0, 1, 2, 3
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
+          3: "workspace too small or misaligned", 4: "HIP launch failure"}
+
+EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
+           "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_set_timing_events")
+STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
+
+
+class HilsError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} (status {code})")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nk", ctypes.c_int32), ("S", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("D", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("qcal_shared", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (ctypes.CDLL). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m learnable_chunk_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        P = ctypes.POINTER(Problem)
+        L.hils_status_string.restype = ctypes.c_char_p
+        L.hils_status_string.argtypes = [ctypes.c_int]
+        L.hils_version.restype = i32
+        L.hils_workspace_size.restype = ctypes.c_int
+        L.hils_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz)]
+        L.hils_route.restype = ctypes.c_int
+        L.hils_route.argtypes = [P] + [vp] * 9 + [sz, vp]
+        L.hils_attn_fwd.restype = ctypes.c_int
+        L.hils_attn_fwd.argtypes = [P] + [vp] * 12 + [sz, vp]
+        L.hils_attn_bwd.restype = ctypes.c_int
+        L.hils_attn_bwd.argtypes = [P] + [vp] * 21 + [sz, vp]
+        L.hils_decode.restype = ctypes.c_int
+        L.hils_decode.argtypes = [P] + [vp] * 13 + [sz, vp]
+        L.hils_set_timing_events.restype = ctypes.c_int
+        L.hils_set_timing_events.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HILS_BF16
+    if t.dtype == torch.float32:
+        return HILS_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise HilsError(fn, code)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_problem(q, k, S, K, W, h=None, W_down=None, scale=0.0, decode=False) -> Problem:
+    B, Hq = q.shape[0], q.shape[1]
+    d = q.shape[-1]
+    Hkv = k.shape[1]
+    Nk = k.shape[2]
+    Nq = 1 if decode else q.shape[2]
+    r = 0 if W_down is None else W_down.shape[-2]
+    D = 0 if h is None else h.shape[-1]
+    return Problem(_dtype_code(q), B, Hq, Hkv, d, Nq, Nk, S, K, W, D, r, 0, float(scale))
+
+
+def workspace_size(p: Problem, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("hils_workspace_size", lib().hils_workspace_size(ctypes.byref(p), op, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(p: Problem, op: int, device) -> torch.Tensor:
+    n = workspace_size(p, op)
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def hils_route(q, kL, e, S: int, K: int, W: int, h=None, W_down=None, W_up=None, scale=0.0,
+               with_scores=False, Nk: Optional[int] = None):
+    """Top-K chunk selection. q [B,Hq,N,d]; kL [B,Hkv,C,d]; e [B,Hkv,C].
+    Returns topk_idx [B,Hkv,N,K] int32 (and topk_score [B,Hq,N,K] fp32)."""
+    _contig(q, kL, e, h, W_down, W_up)
+    B, Hq, N, d = q.shape
+    Hkv = kL.shape[1]
+    fake_k = torch.empty((B, Hkv, N, 0), device=q.device)
+    p = make_problem(q, fake_k, S, K, W, h, W_down, scale)
+    dev = q.device
+    idx = torch.empty((B, Hkv, N, K), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, Hq, N, K), dtype=torch.float32, device=dev) if with_scores else None
+    ws = _workspace(p, OP_ROUTE, dev)
+    _check("hils_route", lib().hils_route(ctypes.byref(p), _ptr(q), _ptr(kL), _ptr(e), _ptr(h),
+                                          _ptr(W_down), _ptr(W_up), _ptr(idx), _ptr(sc), _ptr(ws),
+                                          ws.numel(), _stream(dev)))
+    return (idx, sc) if with_scores else idx
+
+
+def hils_attn_fwd(q, k, v, kL, e, S: int, K: int, W: int, h=None, W_down=None, W_up=None,
+                  scale=0.0, out=None):
+    """Prefill forward. Returns (o [B,Hq,N,d], lse [B,Hq,N] fp32, topk_idx [B,Hkv,N,K])."""
+    _contig(q, k, v, kL, e, h, W_down, W_up)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    p = make_problem(q, k, S, K, W, h, W_down, scale)
+    dev = q.device
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Hkv, N, K), dtype=torch.int32, device=dev)
+        ws = _workspace(p, OP_FWD, dev)
+    else:
+        o, lse, idx, ws = out
+    _check("hils_attn_fwd", lib().hils_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kL),
+                                                _ptr(e), _ptr(h), _ptr(W_down), _ptr(W_up), _ptr(o),
+                                                _ptr(lse), _ptr(idx), _ptr(ws), ws.numel(),
+                                                _stream(dev)))
+    return o, lse, idx
+
+
+def fwd_buffers(q, k, S, K, W, h=None, W_down=None, scale=0.0):
+    """Preallocated (o, lse, topk_idx, workspace) for repeated hils_attn_fwd calls."""
+    B, Hq, N, d = q.shape
+    p = make_problem(q, k, S, K, W, h, W_down, scale)
+    dev = q.device
+    return (torch.empty_like(q), torch.empty((B, Hq, N), dtype=torch.float32, device=dev),
+            torch.empty((B, k.shape[1], N, K), dtype=torch.int32, device=dev),
+            _workspace(p, OP_FWD, dev))
+
+
+def hils_attn_bwd(q, k, v, kL, e, o, lse, topk_idx, dO, S: int, K: int, W: int, h=None, W_down=None,
+                  W_up=None, scale=0.0, want_dh=False, out=None):
+    """Backward with the forward's selection held fixed. Returns a dict of fp32
+    gradients dq, dk, dv, dkL, de (+ dW_down, dW_up, dh with Q-Cal)."""
+    _contig(q, k, v, kL, e, h, W_down, W_up, o, lse, topk_idx, dO)
+    p = make_problem(q, k, S, K, W, h, W_down, scale)
+    dev = q.device
+    f = dict(dtype=torch.float32, device=dev)
+    if out is None:
+        g = dict(dq=torch.empty(q.shape, **f), dk=torch.empty(k.shape, **f),
+                 dv=torch.empty(v.shape, **f), dkL=torch.empty(kL.shape, **f),
+                 de=torch.empty(e.shape, **f))
+        if W_down is not None:
+            g["dW_down"] = torch.empty(W_down.shape, **f)
+            g["dW_up"] = torch.empty(W_up.shape, **f)
+            if want_dh:
+                g["dh"] = torch.empty(h.shape, **f)
+        ws = _workspace(p, OP_BWD, dev)
+    else:
+        g, ws = out
+    _check("hils_attn_bwd", lib().hils_attn_bwd(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kL), _ptr(e), _ptr(h), _ptr(W_down),
+        _ptr(W_up), _ptr(o), _ptr(lse), _ptr(topk_idx), _ptr(dO), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["dkL"]), _ptr(g["de"]), _ptr(g.get("dW_down")), _ptr(g.get("dW_up")),
+        _ptr(g.get("dh")), _ptr(ws), ws.numel(), _stream(dev)))
+    return g
+
+
+def hils_decode(q, k_cache, v_cache, kL, e, S: int, K: int, W: int, seq_len=None, h=None,
+                W_down=None, W_up=None, scale=0.0, out=None, with_topk=True):
+    """One decode step. q [B,Hq,d]; caches [B,Hkv,Nk,d]; seq_len [B] int32 (device).
+    Returns (o [B,Hq,d], lse [B,Hq], topk_idx [B,Hkv,K] or None)."""
+    _contig(q, k_cache, v_cache, kL, e, h, W_down, W_up, seq_len)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    p = make_problem(q, k_cache, S, K, W, h, W_down, scale, decode=True)
+    dev = q.device
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Hkv, K), dtype=torch.int32, device=dev) if with_topk else None
+        ws = _workspace(p, OP_DECODE, dev)
+    else:
+        o, lse, idx, ws = out
+    _check("hils_decode", lib().hils_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(seq_len), _ptr(kL), _ptr(e), _ptr(h), _ptr(W_down),
+                                            _ptr(W_up), _ptr(o), _ptr(lse), _ptr(idx), _ptr(ws),
+                                            ws.numel(), _stream(dev)))
+    return o, lse, idx
+
+
+def decode_buffers(q, k_cache, S, K, W, h=None, W_down=None, scale=0.0):
+    B, Hq, d = q.shape
+    p = make_problem(q, k_cache, S, K, W, h, W_down, scale, decode=True)
+    dev = q.device
+    return (torch.empty_like(q), torch.empty((B, Hq), dtype=torch.float32, device=dev),
+            torch.empty((B, k_cache.shape[1], K), dtype=torch.int32, device=dev),
+            _workspace(p, OP_DECODE, dev))
+
+
+_event_keepalive = {}
+
+
+def hils_set_timing_events(step: int, starts=None, stops=None):
+    """Record a (start, stop) pair of torch.cuda.Event(enable_timing=True)
+    around every later launch of `step`, cycling through the given lists.
+    Call with no events to unregister. The events must have been recorded
+    once (so that their HIP handles exist)."""
+    if not starts:
+        _event_keepalive.pop(step, None)
+        _check("hils_set_timing_events", lib().hils_set_timing_events(step, None, None, 0))
+        return
+    n = len(starts)
+    a = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in starts])
+    b = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in stops])
+    _event_keepalive[step] = (a, b, starts, stops)
+    _check("hils_set_timing_events", lib().hils_set_timing_events(step, a, b, n))

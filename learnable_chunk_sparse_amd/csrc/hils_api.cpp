@@ -1,0 +1,296 @@
+// C ABI of the HiLS library: validation, workspace carving and the launch
+// sequence of each operation. No device memory is allocated here; every
+// launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "../../include/hils.h"
+#include "hils_internal.h"
+
+using hils::Dims;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += up(bytes);
+    return p;
+  }
+};
+
+bool pow2ish_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+// Structural checks shared by every op. Returns HILS_OK or the error.
+hils_status check_problem(const hils_problem* p, int op) {
+  if (p == nullptr) return HILS_ERR_INVALID;
+  if (p->dtype != HILS_FP32 && p->dtype != HILS_BF16) return HILS_ERR_UNSUPPORTED;
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->d <= 0 || p->Nq <= 0 || p->Nk <= 0 ||
+      p->S <= 0 || p->K <= 0 || p->W <= 0)
+    return HILS_ERR_INVALID;
+  if (p->Hq % p->Hkv != 0) return HILS_ERR_INVALID;
+  if (p->r < 0 || (p->r > 0 && p->D <= 0)) return HILS_ERR_INVALID;
+  if (!(p->scale >= 0.f) || std::isinf(p->scale)) return HILS_ERR_INVALID;
+  if (op == HILS_OP_DECODE) {
+    if (p->Nq != 1) return HILS_ERR_INVALID;
+  } else {
+    if (p->Nq != p->Nk) return HILS_ERR_INVALID;
+  }
+  if (p->d != 64 && p->d != 128) return HILS_ERR_UNSUPPORTED;
+  if (p->S != 64) return HILS_ERR_UNSUPPORTED;
+  if (p->qcal_shared != 0) return HILS_ERR_UNSUPPORTED;
+  const int G = p->Hq / p->Hkv;
+  if (!pow2ish_group(G)) return HILS_ERR_UNSUPPORTED;
+  if (p->r > 0) {
+    if (!(p->r == 16 || p->r == 32 || p->r == 64)) return HILS_ERR_UNSUPPORTED;
+    if (p->D % 32 != 0) return HILS_ERR_UNSUPPORTED;
+    if ((p->Hq * p->r) % 64 != 0) return HILS_ERR_UNSUPPORTED;
+  }
+  if (op != HILS_OP_DECODE) {
+    if (G > 4) return HILS_ERR_UNSUPPORTED;
+    if (p->K > 32) return HILS_ERR_UNSUPPORTED;
+  } else {
+    if (p->K > 64) return HILS_ERR_UNSUPPORTED;
+  }
+  if ((long long)p->Nk > (1LL << 26)) return HILS_ERR_UNSUPPORTED;
+  return HILS_OK;
+}
+
+Dims dims_of(const hils_problem* p) {
+  Dims d;
+  d.dtype = p->dtype;
+  d.B = p->B;
+  d.Hq = p->Hq;
+  d.Hkv = p->Hkv;
+  d.G = p->Hq / p->Hkv;
+  d.d = p->d;
+  d.N = p->Nk;
+  d.S = p->S;
+  d.K = p->K;
+  d.W = p->W;
+  d.C = p->Nk / p->S;
+  d.D = p->D;
+  d.r = p->r;
+  d.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+  return d;
+}
+
+// Workspace layout of each op (the same function computes sizes and carves).
+struct FwdWs {
+  float* qhat;
+  float* s_T;
+};
+size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
+  Carver c(ws);
+  const size_t rows = (size_t)d.B * d.Hq * d.N;
+  out->qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
+  out->s_T = (float*)c.take(rows * d.K * sizeof(float));
+  return c.used;
+}
+size_t carve_route(const Dims& d, void* ws, float** qhat) {
+  Carver c(ws);
+  const size_t rows = (size_t)d.B * d.Hq * d.N;
+  *qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
+  return c.used;
+}
+
+hils_status ws_check(void* ws, size_t have, size_t need) {
+  if (need > have) return HILS_ERR_WORKSPACE;
+  if (need > 0 && (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (ALIGN - 1)) != 0))
+    return HILS_ERR_WORKSPACE;
+  return HILS_OK;
+}
+
+hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
+
+bool fwd_fits_lds(const Dims& d) { return hils::attn_fwd_lds_bytes(d) <= 160 * 1024; }
+
+// ---------------------------------------------------------------- timing hook
+struct EventRing {
+  void* const* start = nullptr;
+  void* const* stop = nullptr;
+  int n = 0;
+  int next = 0;
+};
+EventRing g_rings[HILS_STEP_COUNT];
+
+template <typename F>
+hipError_t timed(int step, hipStream_t st, F&& launch) {
+  EventRing& r = g_rings[step];
+  if (r.n <= 0) return launch();
+  const int j = r.next;
+  r.next = (r.next + 1) % r.n;
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(r.start[j]), st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(static_cast<hipEvent_t>(r.stop[j]), st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hils_status_string(hils_status s) {
+  switch (s) {
+    case HILS_OK: return "ok";
+    case HILS_ERR_INVALID: return "invalid argument";
+    case HILS_ERR_UNSUPPORTED: return "unsupported problem";
+    case HILS_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case HILS_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+int32_t hils_version(void) { return 100; }
+
+hils_status hils_set_timing_events(int32_t step, void* const* start, void* const* stop, int32_t n) {
+  if (step < 0 || step >= HILS_STEP_COUNT || n < 0) return HILS_ERR_INVALID;
+  EventRing& r = g_rings[step];
+  if (n == 0 || start == nullptr || stop == nullptr) {
+    r = EventRing();
+    return HILS_OK;
+  }
+  r.start = start;
+  r.stop = stop;
+  r.n = n;
+  r.next = 0;
+  return HILS_OK;
+}
+
+hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes) {
+  if (bytes == nullptr) return HILS_ERR_INVALID;
+  if (op < HILS_OP_ROUTE || op > HILS_OP_DECODE) return HILS_ERR_INVALID;
+  hils_status s = check_problem(p, op);
+  if (s != HILS_OK) return s;
+  const Dims d = dims_of(p);
+  switch (op) {
+    case HILS_OP_ROUTE: {
+      float* q;
+      *bytes = carve_route(d, nullptr, &q);
+      return HILS_OK;
+    }
+    case HILS_OP_FWD: {
+      if (!fwd_fits_lds(d)) return HILS_ERR_UNSUPPORTED;
+      FwdWs w;
+      *bytes = carve_fwd(d, nullptr, &w);
+      return HILS_OK;
+    }
+    case HILS_OP_BWD:
+      *bytes = hils::bwd_workspace(d);
+      return *bytes == (size_t)-1 ? HILS_ERR_UNSUPPORTED : HILS_OK;
+    case HILS_OP_DECODE:
+      *bytes = hils::decode_workspace(d);
+      return *bytes == (size_t)-1 ? HILS_ERR_UNSUPPORTED : HILS_OK;
+  }
+  return HILS_ERR_INVALID;
+}
+
+hils_status hils_route(const hils_problem* p, const void* q, const void* kL, const void* e,
+                       const void* h, const void* W_down, const void* W_up, int32_t* topk_idx,
+                       float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  hils_status s = check_problem(p, HILS_OP_ROUTE);
+  if (s != HILS_OK) return s;
+  if (!q || !kL || !e || !topk_idx) return HILS_ERR_INVALID;
+  if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  const Dims d = dims_of(p);
+  float* qhat = nullptr;
+  const size_t need = carve_route(d, nullptr, &qhat);
+  if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  carve_route(d, ws, &qhat);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d.r > 0) {
+    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
+      return s;
+    return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, qhat, true, kL, e, topk_idx, topk_score, st); }));
+  }
+  return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, st); }));
+}
+
+hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, const void* v,
+                          const void* kL, const void* e, const void* h, const void* W_down,
+                          const void* W_up, void* o, float* lse, int32_t* topk_idx, void* ws,
+                          size_t ws_bytes, void* stream) {
+  hils_status s = check_problem(p, HILS_OP_FWD);
+  if (s != HILS_OK) return s;
+  if (!q || !k || !v || !kL || !e || !o || !lse || !topk_idx) return HILS_ERR_INVALID;
+  if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  const Dims d = dims_of(p);
+  if (!fwd_fits_lds(d)) return HILS_ERR_UNSUPPORTED;
+  FwdWs w;
+  const size_t need = carve_fwd(d, nullptr, &w);
+  if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  carve_fwd(d, ws, &w);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d.r > 0) {
+    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, w.qhat, nullptr, st); }))) != HILS_OK)
+      return s;
+    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, w.s_T, st); }));
+  } else {
+    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, w.s_T, st); }));
+  }
+  if (s != HILS_OK) return s;
+  return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, topk_idx, w.s_T, o, lse, st); }));
+}
+
+hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,
+                          const void* kL, const void* e, const void* h, const void* W_down,
+                          const void* W_up, const void* o, const float* lse,
+                          const int32_t* topk_idx, const void* dO, float* dq, float* dk, float* dv,
+                          float* dkL, float* de, float* dW_down, float* dW_up, float* dh,
+                          void* ws, size_t ws_bytes, void* stream) {
+  hils_status s = check_problem(p, HILS_OP_BWD);
+  if (s != HILS_OK) return s;
+  if (!q || !k || !v || !kL || !e || !o || !lse || !topk_idx || !dO || !dq || !dk || !dv || !dkL ||
+      !de)
+    return HILS_ERR_INVALID;
+  if (p->r > 0 && (!h || !W_down || !W_up || !dW_down || !dW_up)) return HILS_ERR_INVALID;
+  const Dims d = dims_of(p);
+  const size_t need = hils::bwd_workspace(d);
+  if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed(HILS_STEP_BWD, st, [&] {
+    return hils::launch_bwd(d, q, k, v, kL, e, h, W_down, W_up, o, lse, topk_idx, dO, dq, dk, dv,
+                            dkL, de, dW_down, dW_up, dh, ws, st);
+  }));
+}
+
+hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* seq_len, const void* kL, const void* e,
+                        const void* h, const void* W_down, const void* W_up, void* o, float* lse,
+                        int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+  hils_status s = check_problem(p, HILS_OP_DECODE);
+  if (s != HILS_OK) return s;
+  if (!q || !k_cache || !v_cache || !kL || !e || !o || !lse) return HILS_ERR_INVALID;
+  if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  const Dims d = dims_of(p);
+  const size_t need = hils::decode_workspace(d);
+  if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the decode workspace starts with the fp32 calibrated queries when Q-Cal is on
+  const void* qs = q;
+  bool qf32 = d.dtype == HILS_FP32;
+  if (d.r > 0) {
+    float* qhat = static_cast<float*>(ws);
+    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, 1, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
+      return s;
+    qs = qhat;
+    qf32 = true;
+  }
+  return hip_status(timed(HILS_STEP_DECODE, st, [&] {
+    return hils::launch_decode(d, qs, qf32, q, k_cache, v_cache, seq_len, kL, e, o, lse, topk_idx,
+                               ws, st);
+  }));
+}
+
+}  // extern "C"

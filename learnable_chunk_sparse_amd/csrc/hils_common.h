@@ -1,0 +1,101 @@
+// Device-side building blocks shared by the HiLS kernels (gfx950 / CDNA4).
+//
+// MFMA fragment convention used everywhere (checked on the device): for the
+// 16x16x32 bf16 product D = A * B (+C),
+//   lane l holds A[row = l % 16][k = 8 * (l / 16) + e], e = 0..7,
+//             B[k = 8 * (l / 16) + e][col = l % 16],
+//             D[row = 4 * (l / 16) + i][col = l % 16], i = 0..3.
+// fp32 inputs use eight 16x16x4 fp32 products with the same per-lane
+// element layout (element e feeds product e), so every kernel is written
+// once over the element type T (uint16_t holding bf16 bits, or float).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr float NEG_INF = -__builtin_inff();
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round to nearest even (inputs are finite)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t x) { return bf2f(x); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f<uint16_t>(float x) { return f2bf(x); }
+
+// ---------------------------------------------------------------- fragments
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+// 8 consecutive elements (16 B for bf16, 32 B for fp32; aligned)
+template <typename T> __device__ __forceinline__ typename Frag<T>::type ld8(const T* p);
+template <> __device__ __forceinline__ bf16x8 ld8<uint16_t>(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ __forceinline__ f32x8 ld8<float>(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+  return c;
+}
+
+// 8 floats -> fragment of T
+template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
+template <> __device__ __forceinline__ bf16x8 pack8<uint16_t>(const float* x) {
+  u16x8 u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = f2bf(x[j]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
+  f32x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = x[j];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Completes this wave's outstanding LDS operations and stops the compiler
+// from moving memory accesses across: used where lanes of ONE wave exchange
+// data through LDS (the other waves are not involved).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int n_distant(int i, int W, int S) {
+  const int x = i - W + 1;
+  return x <= 0 ? 0 : x / S;
+}
+
+// cross-lane helpers (lanes xor-ed within the wave)
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, WAVE); }
+
+}  // namespace hils

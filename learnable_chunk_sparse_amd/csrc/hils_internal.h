@@ -1,0 +1,51 @@
+// Host-side launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hils {
+
+struct Dims {
+  int dtype;  // 0 fp32, 1 bf16
+  int B, Hq, Hkv, G, d;
+  int N;      // query/key length (prefill) or cache capacity (decode)
+  int S, K, W;
+  int C;      // N / S
+  int D, r;
+  float scale;
+};
+
+// Q-Cal: q_hat = q + W_up (W_down h) in fp32; u = W_down h (fp32, optional).
+// ntok tokens; token t = b * Nq + i. q: [B, Hq, Nq, d].
+hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, const void* W_down,
+                       const void* W_up, float* q_hat, float* u, hipStream_t st);
+
+// Routing over a prefill sequence: scores every distant chunk, GQA max,
+// top-K. qs: scoring queries ([B, Hq, N, d], fp32 when q_is_f32 else in the
+// input dtype). Writes topk_idx and, if non-null, topk_score.
+hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void* kL, const void* e,
+                        int32_t* topk_idx, float* topk_score, hipStream_t st);
+
+// Fused window attention + selected-chunk attention + fusion.
+hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v,
+                           const int32_t* topk_idx, const float* topk_score, void* o, float* lse,
+                           hipStream_t st);
+size_t attn_fwd_lds_bytes(const Dims& p);
+
+// Decode.
+size_t decode_workspace(const Dims& p);
+hipError_t launch_decode(const Dims& p, const void* q_or_qhat, bool q_is_f32, const void* q,
+                         const void* k, const void* v, const int32_t* seq_len, const void* kL,
+                         const void* e, void* o, float* lse, int32_t* topk_idx, void* ws,
+                         hipStream_t st);
+
+// Backward.
+size_t bwd_workspace(const Dims& p);
+hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v, const void* kL,
+                      const void* e, const void* h, const void* W_down, const void* W_up,
+                      const void* o, const float* lse, const int32_t* topk_idx, const void* dO,
+                      float* dq, float* dk, float* dv, float* dkL, float* de, float* dW_down,
+                      float* dW_up, float* dh, void* ws, hipStream_t st);
+
+}  // namespace hils

@@ -1,0 +1,83 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point of include/hils.h, sizes workspaces and rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import learnable_chunk_sparse_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "hils.h")).read()
+    return sorted(set(re.findall(r"\b(hils_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    names = header_functions()
+    assert {"hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_route"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(L.EXPORTS) == set(names)
+
+
+def prob(**kw):
+    base = dict(dtype=1, B=4, Hq=16, Hkv=16, d=64, Nq=8192, Nk=8192, S=64, K=16, W=512, D=1024,
+                r=32, qcal_shared=0, scale=0.0)
+    base.update(kw)
+    return L.Problem(*[base[f[0]] for f in L.Problem._fields_])
+
+
+def ws(p, op):
+    n = ctypes.c_size_t(0)
+    st = L.lib().hils_workspace_size(ctypes.byref(p), op, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    st, n = ws(prob(), L.OP_FWD)
+    assert st == 0
+    rows = 4 * 16 * 8192
+    assert n >= rows * 64 * 4 + rows * 16 * 4  # fp32 q_hat + selected scores
+    st, n2 = ws(prob(r=0, D=0), L.OP_FWD)
+    assert st == 0 and n2 < n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), 1), (dict(B=0), 1), (dict(K=0), 1), (dict(Nq=100, Nk=200), 1),
+    (dict(d=96), 2), (dict(S=32), 2), (dict(dtype=7), 2), (dict(qcal_shared=1), 2),
+    (dict(r=8), 2), (dict(Hq=16, Hkv=1), 2), (dict(scale=-1.0), 1),
+    (dict(dtype=0, d=128), 2),
+])
+def test_validation_codes(kw, code):
+    st, _ = ws(prob(**kw), L.OP_FWD)
+    assert st == code, (kw, st)
+
+
+def test_calls_reject_before_launch():
+    lib = L.lib()
+    p = prob()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    # missing required pointer
+    st = lib.hils_attn_fwd(ctypes.byref(p), null, fake, fake, fake, fake, fake, fake, fake, fake,
+                           fake, fake, fake, 1 << 40, null)
+    assert st == 1
+    # workspace too small
+    st = lib.hils_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                           fake, fake, ctypes.c_void_p(4096), 16, null)
+    assert st == 3
+    # misaligned workspace
+    st = lib.hils_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                           fake, fake, ctypes.c_void_p(4096 + 8), 1 << 40, null)
+    assert st == 3
+    # decode needs Nq == 1
+    st = lib.hils_decode(ctypes.byref(p), fake, fake, fake, null, fake, fake, fake, fake, fake, fake,
+                         fake, null, fake, 1 << 40, null)
+    assert st == 1
+    assert lib.hils_status_string(3) == b"workspace too small or misaligned"

@@ -289,34 +289,79 @@ def plant_needles(wl: Workload, t: dict) -> None:
     chunk should be selected by (and dominate for) that query."""
     if wl.needle == "none":
         return
-    d, S = wl.d, wl.S
+    for b in range(t["q"].shape[0]):
+        for g in range(t["k"].shape[1]):
+            _plant_group(wl, t, b, g, b, g)
+
+
+def _plant_group(wl: Workload, t: dict, tb: int, tg: int, b: int, g: int) -> None:
+    """Plant the needles of (batch b, KV group g) of the workload into slot
+    (tb, tg) of the tensors in t (whose q holds that group's heads at
+    tg*G .. tg*G+G-1)."""
+    d, S, G = wl.d, wl.S, wl.G
     rd = math.sqrt(d)
+    dec = wl.mode == "decode"
     if wl.needle == "chunk7":
-        # tiny workload: chunk 7, aligned with the last query of batch 0 / head 0
-        for b in range(wl.B):
-            for g in range(wl.Hkv):
-                ql = t["q"][b, g * wl.G, wl.N - 1].to(torch.float64).cpu()
-                key = (3.0 * rd * _unit(ql)).to(wl.torch_dtype)
-                t["k"][b, g, 7 * S:8 * S] = key.to(t["k"].device)[None, :]
-                t["kL"][b, g, 7] = ql.to(wl.torch_dtype).to(t["kL"].device)
+        ql = t["q"][tb, tg * G, wl.N - 1].to(torch.float64).cpu()
+        key = (3.0 * rd * _unit(ql)).to(wl.torch_dtype)
+        t["k"][tb, tg, 7 * S:8 * S] = key.to(t["k"].device)[None, :]
+        t["kL"][tb, tg, 7] = ql.to(wl.torch_dtype).to(t["kL"].device)
     elif wl.needle == "segments":
         seg = 16384
-        for b in range(wl.B):
-            for g in range(wl.Hkv):
-                chunks = needle_chunks_segments(wl, g)
-                for s, c in enumerate(chunks):
-                    u = segment_mean_query(wl, t["q"], b, g, s * seg, (s + 1) * seg)
-                    t["k"][b, g, c * S:(c + 1) * S] = (3.0 * rd * u).to(wl.torch_dtype).to(t["k"].device)[None, :]
-                    t["kL"][b, g, c] = (rd * u).to(wl.torch_dtype).to(t["kL"].device)
+        for s, c in enumerate(needle_chunks_segments(wl, g)):
+            acc = torch.zeros(d, dtype=torch.float64)
+            for hh in range(G):
+                acc += t["q"][tb, tg * G + hh, s * seg:(s + 1) * seg].to(torch.float64).cpu().sum(dim=0)
+            u = _unit(acc)
+            t["k"][tb, tg, c * S:(c + 1) * S] = (3.0 * rd * u).to(wl.torch_dtype).to(t["k"].device)[None, :]
+            t["kL"][tb, tg, c] = (rd * u).to(wl.torch_dtype).to(t["kL"].device)
     elif wl.needle == "decode_random":
-        for b in range(wl.B):
-            for g in range(wl.Hkv):
-                c = needle_chunk_decode(wl, b, g)
-                ql = t["q"][b, g * wl.G].to(torch.float64).cpu()
-                t["k"][b, g, c * S:(c + 1) * S] = (3.0 * rd * _unit(ql)).to(wl.torch_dtype).to(t["k"].device)[None, :]
-                t["kL"][b, g, c] = ql.to(wl.torch_dtype).to(t["kL"].device)
+        c = needle_chunk_decode(wl, b, g)
+        ql = (t["q"][tb, tg * G] if dec else t["q"][tb, tg * G, -1]).to(torch.float64).cpu()
+        t["k"][tb, tg, c * S:(c + 1) * S] = (3.0 * rd * _unit(ql)).to(wl.torch_dtype).to(t["k"].device)[None, :]
+        t["kL"][tb, tg, c] = ql.to(wl.torch_dtype).to(t["kL"].device)
     else:
         raise ValueError(wl.needle)
+
+
+def make_group_inputs(wl: Workload, b: int, g: int, h_rows: Optional[Sequence[int]] = None,
+                      kv_len: Optional[int] = None) -> dict:
+    """The slabs of one (batch b, KV group g) as a stand-alone CPU problem
+    (B = 1, Hkv = 1, Hq = G), bit-identical to the same slabs of
+    make_inputs(wl) on any device. HiLS rows of one group depend on nothing
+    else, so the oracle can check a full-size run group by group.
+
+    h_rows: generate only these rows of the hidden state (others are NaN).
+    kv_len: decode only, generate only the first kv_len cache tokens."""
+    G, d, N, C = wl.G, wl.d, wl.N, wl.C
+    dec = wl.mode == "decode"
+    n = N if kv_len is None else kv_len
+    out = {}
+    qs = [gen_slab(wl, "q", b, g * G + hh, (d,) if dec else (N, d)) for hh in range(G)]
+    out["q"] = torch.stack(qs)[None]
+    out["k"] = gen_slab(wl, "k", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
+    out["v"] = gen_slab(wl, "v", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
+    out["kL"] = gen_slab(wl, "kL", b, g, (C, d))[None, None]
+    out["e"] = gen_slab(wl, "e", b, g, (C,))[None, None]
+    if wl.r > 0:
+        if dec:
+            out["h"] = gen_slab(wl, "h", b, 0, (wl.D,))[None]
+        elif h_rows is None:
+            out["h"] = gen_slab(wl, "h", b, 0, (N, wl.D))[None]
+        else:
+            hr = torch.full((N, wl.D), float("nan"), dtype=wl.torch_dtype)
+            rows = torch.tensor(sorted(set(int(i) for i in h_rows)), dtype=torch.int64)
+            hr[rows] = gen_slab(wl, "h", b, 0, None, rows=rows, row_len=wl.D)
+            out["h"] = hr[None]
+        out["W_down"] = torch.stack([gen_slab(wl, "W_down", 0, g * G + hh, (wl.r, wl.D)) for hh in range(G)])
+        out["W_up"] = torch.stack([gen_slab(wl, "W_up", 0, g * G + hh, (d, wl.r)) for hh in range(G)])
+    if wl.mode == "train":
+        out["dO"] = torch.stack([gen_slab(wl, "dO", b, g * G + hh, (N, d)) for hh in range(G)])[None]
+    if wl.needle != "none":
+        _plant_group(wl, out, 0, 0, b, g)
+    if dec:
+        out["seq_len"] = torch.tensor([seq_lens(wl)[b]], dtype=torch.int32)
+    return out
 
 
 def segment_mean_query(wl: Workload, q: torch.Tensor, b: int, g: int, lo: int, hi: int) -> torch.Tensor:

@@ -10,9 +10,9 @@ selected-chunk attention, fusion.
 Prints ONE JSON line: prefill tokens/s, the roofline of the dominant kernel
 (its average duration measured with HIP events around each of its launches in
 the timed region) and the fp64 CPU oracle timed on a bounded sample of the
-same workload. Optional extra legs: --decode (the 512K-context decode step,
-microseconds per step against the HBM roofline) and --train (forward +
-backward tokens/s).
+same workload. Extra legs in the same line: "decode" (the 512K-context decode
+step of 32 sequences, microseconds per step against the HBM roofline, cold
+last-level cache) and "train" (forward + backward tokens/s).
 """
 from __future__ import annotations
 
@@ -223,7 +223,7 @@ def main():
     ap.add_argument("--workload", default="prefill_345m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--decode", action="store_true", help="also time the 512K decode step")
+    ap.add_argument("--no-decode", action="store_true", help="skip the 512K decode leg")
     ap.add_argument("--decode-workload", default="decode_7b_512k")
     ap.add_argument("--decode-steps", type=int, default=20)
     args = ap.parse_args()
@@ -237,7 +237,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     res, wl = bench_prefill(args, torch, L, None)
-    if args.decode:
+    if not args.no_decode:
         res["decode"] = bench_decode(args, torch, L)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, args.cpu_budget)
     res["vs_baseline"] = None

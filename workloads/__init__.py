@@ -325,22 +325,32 @@ def _plant_group(wl: Workload, t: dict, tb: int, tg: int, b: int, g: int) -> Non
 
 
 def make_group_inputs(wl: Workload, b: int, g: int, h_rows: Optional[Sequence[int]] = None,
-                      kv_len: Optional[int] = None) -> dict:
+                      kv_len: Optional[int] = None, kv_rows: Optional[Sequence[int]] = None) -> dict:
     """The slabs of one (batch b, KV group g) as a stand-alone CPU problem
     (B = 1, Hkv = 1, Hq = G), bit-identical to the same slabs of
     make_inputs(wl) on any device. HiLS rows of one group depend on nothing
     else, so the oracle can check a full-size run group by group.
 
     h_rows: generate only these rows of the hidden state (others are NaN).
-    kv_len: decode only, generate only the first kv_len cache tokens."""
+    kv_len: decode only, generate only the first kv_len cache tokens.
+    kv_rows: generate only these key/value rows (others are NaN); needle
+    rows are always planted."""
     G, d, N, C = wl.G, wl.d, wl.N, wl.C
     dec = wl.mode == "decode"
     n = N if kv_len is None else kv_len
     out = {}
     qs = [gen_slab(wl, "q", b, g * G + hh, (d,) if dec else (N, d)) for hh in range(G)]
     out["q"] = torch.stack(qs)[None]
-    out["k"] = gen_slab(wl, "k", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
-    out["v"] = gen_slab(wl, "v", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
+    if kv_rows is None:
+        out["k"] = gen_slab(wl, "k", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
+        out["v"] = gen_slab(wl, "v", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
+    else:
+        rr = torch.tensor(sorted(set(int(i) for i in kv_rows)), dtype=torch.int64)
+        for name in ("k", "v"):
+            full = torch.full((n, d), float("nan"), dtype=wl.torch_dtype)
+            if rr.numel():
+                full[rr] = gen_slab(wl, name, b, g, None, rows=rr, row_len=d)
+            out[name] = full[None, None]
     out["kL"] = gen_slab(wl, "kL", b, g, (C, d))[None, None]
     out["e"] = gen_slab(wl, "e", b, g, (C,))[None, None]
     if wl.r > 0:

@@ -129,10 +129,11 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
  * Training backward of hils_attn_fwd with the selection topk_idx held fixed
  * (the paper trains the landmark keys end to end through the fusion softmax,
  * Fig. 3 caption; top-K itself is not differentiated). Inputs are the forward
- * inputs, its outputs o and lse, topk_idx and the upstream gradient dO
- * [B, Hq, Nq, d]. Outputs (fp32, overwritten, all required except dh):
- * dq, dk, dv, dkL, de; dW_down, dW_up when r > 0 (ignored when r == 0);
- * dh [B, Nq, D] (nullable).
+ * inputs, its lse and topk_idx, and the upstream gradient dO [B, Hq, Nq, d].
+ * o may be NULL and is not read: dO . o is recomputed in fp32 from the
+ * attention weights, so the rounding of o does not enter the gradients.
+ * Outputs (fp32, overwritten, all required except dh): dq, dk, dv, dkL, de;
+ * dW_down, dW_up when r > 0 (ignored when r == 0); dh [B, Nq, D] (nullable).
  */
 hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,
                           const void* kL, const void* e, const void* h, const void* W_down,

@@ -1,16 +1,1030 @@
-// Training backward (filled in below).
+// HiLS training backward (paper Fig. 3 caption: the chunk-mass surrogate
+// parameterises the forward attention weights, so the language-modelling
+// gradient reaches the compressed keys; dev.to / nestfrontier: gradients flow
+// into the landmark representations through the fusion). The pages print no
+// backward formulas; these are the chain rule through the forward with the
+// selection T held fixed. Per row (b, h, i), with O the forward output,
+// L its log-normaliser, w_c = exp(s_c - L), p_j = softmax within chunk c:
+//   D = dO . O,  delta_c = dO . O_c = sum_j p_j (dO . v_j)
+//   chunk token j:  a_j = w_c p_j,         dx_j = a_j (dO . v_j - delta_c)
+//   window token j: a_j = exp(x_j - L),    dx_j = a_j (dO . v_j - D)
+//   dq += scale sum_j dx_j k_j;  dk_j += scale dx_j q;  dv_j += a_j dO
+//   ds_c = w_c (delta_c - D):  dq_hat = scale sum_c ds_c kL_c (added to dq),
+//   dkL_c += scale ds_c q_hat,  de_c += ds_c
+//   Q-Cal: d(delta q) = dq_hat, du = W_up^T dq_hat, dW_up += dq_hat u^T,
+//   dW_down += du h^T, dh += W_down^T du.
+//
+// Launch sequence:
+//   (Q-Cal forward again for q_hat and u)
+//   k_bwd_prep     D per row and the fp32 scores s_c of the selected chunks
+//   inverse index  chunk -> (position, slot) lists (count, scan, fill)
+//   k_bwd_dq       query tiles: window band + compacted chunk groups (as in
+//                  the forward), dq; per (row, chunk) ds_c, beta_c = s_c - L -
+//                  lse_c (so that a_j = exp(x_j + beta_c)) and delta_c
+//   k_bwd_dkdv     one workgroup per 64-token key block: every row attending
+//                  to it through the window or through a selection; dk, dv
+//                  and (complete chunks) dkL, de, without atomics to HBM
+//   Q-Cal backward on the batched MFMA GEMM.
 #include "hils_common.h"
 #include "hils_internal.h"
 
+#include <algorithm>
+
 namespace hils {
 
-size_t bwd_workspace(const Dims&) { return (size_t)-1; }
+namespace {
+constexpr int KPAD = 8;  // padding (elements) of the transposed staging rows
+}
 
-hipError_t launch_bwd(const Dims&, const void*, const void*, const void*, const void*, const void*,
-                      const void*, const void*, const void*, const void*, const float*,
-                      const int32_t*, const void*, float*, float*, float*, float*, float*, float*,
-                      float*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+// --------------------------------------------------------------- small kernels
+__global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+__global__ void k_fill_i32(int* __restrict__ p, size_t n, int v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// One wave per row (b, h, i): the fp32 score s_c of each selected slot.
+template <typename T, typename QT, int DH>
+__global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, const T* __restrict__ kL,
+                                                  const T* __restrict__ e,
+                                                  const int32_t* __restrict__ topk_idx,
+                                                  float* __restrict__ sT, long rows, int N, int Hq,
+                                                  int Hkv, int G, int C, int K, float scale) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int i = (int)(row % N);
+  const long bh = row / N;
+  const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+  const int g = h / G;
+  const long bg = (long)b * Hkv + g;
+  const int32_t* ti = topk_idx + (bg * N + i) * K;
+  for (int k = 0; k < K; ++k) {
+    const int c = ti[k];
+    float s = 0.f;
+    if (c >= 0) {
+      for (int dd = lane; dd < DH; dd += 64) s += to_f<QT>(qs[row * DH + dd]) * to_f<T>(kL[(bg * C + c) * DH + dd]);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+      s = fmaf(s, scale, to_f<T>(e[bg * C + c]));
+    }
+    if (lane == 0) sT[row * K + k] = c >= 0 ? s : __builtin_nanf("");
+  }
+}
+
+// inverse index: count, scan, fill
+__global__ void k_inv_count(const int32_t* __restrict__ topk_idx, int* __restrict__ cnt, long total,
+                            int N, int K, int C) {
+  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (long)gridDim.x * blockDim.x) {
+    const int c = topk_idx[x];
+    if (c >= 0 && c < C) {
+      const long bg = x / ((long)N * K);
+      atomicAdd(&cnt[bg * C + c], 1);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_inv_scan(const int* __restrict__ cnt, int* __restrict__ off, int C) {
+  __shared__ int wsum[4];
+  __shared__ int carry;
+  const int bg = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int* cb = cnt + (long)bg * C;
+  int* ob = off + (long)bg * (C + 1);
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < C; base += 256) {
+    const int x = base + t < C ? cb[base + t] : 0;
+    int v = x;
+#pragma unroll
+    for (int o2 = 1; o2 < 64; o2 <<= 1) {
+      const int y = __shfl_up(v, o2, 64);
+      if (lane >= o2) v += y;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    int pre = carry;
+    for (int j = 0; j < w; ++j) pre += wsum[j];
+    if (base + t < C) ob[base + t] = pre + v - x;
+    __syncthreads();
+    if (t == 255) carry = pre + v;
+    __syncthreads();
+  }
+  if (t == 0) ob[C] = carry;
+}
+
+__global__ void k_inv_fill(const int32_t* __restrict__ topk_idx, const int* __restrict__ off,
+                           int* __restrict__ cur, int* __restrict__ lst, long total, int N, int K,
+                           int C) {
+  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (long)gridDim.x * blockDim.x) {
+    const int c = topk_idx[x];
+    if (c >= 0 && c < C) {
+      const long bg = x / ((long)N * K);
+      const long rem = x - bg * N * K;
+      const int i = (int)(rem / K), k = (int)(rem - (long)i * K);
+      const int slot = atomicAdd(&cur[bg * C + c], 1);
+      lst[bg * (long)N * K + off[bg * (C + 1) + c] + slot] = (i << 6) | k;
+    }
+  }
+}
+
+// --------------------------------------------------------------- LDS helpers
+// Stage a 64-token block of K ([64][DH] from ksrc) transposed into
+// kt[DH][64 + KPAD] (one wave; tokens >= nvalid read row 0).
+template <typename T, int DH>
+__device__ __forceinline__ void stage_t64(const T* __restrict__ src, int nvalid, T* dst, int lane) {
+  const int tp = lane & 31, half = lane >> 5;
+  const int t0 = 2 * tp, t1 = 2 * tp + 1;
+  const T* r0 = src + (size_t)(t0 < nvalid ? t0 : 0) * DH + half * (DH / 2);
+  const T* r1 = src + (size_t)(t1 < nvalid ? t1 : 0) * DH + half * (DH / 2);
+  constexpr int VS = 64 + KPAD;
+#pragma unroll
+  for (int j = 0; j < DH / 2; j += 8) {
+    const auto a = ld8<T>(r0 + j);
+    const auto bb = ld8<T>(r1 + j);
+    if constexpr (sizeof(T) == 2) {
+      const u16x8 ua = __builtin_bit_cast(u16x8, a), ub = __builtin_bit_cast(u16x8, bb);
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2)
+        *reinterpret_cast<uint32_t*>(dst + (half * (DH / 2) + j + e2) * VS + t0) =
+            (uint32_t)ua[e2] | ((uint32_t)ub[e2] << 16);
+    } else {
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        float2 pr;
+        pr.x = a[e2];
+        pr.y = bb[e2];
+        *reinterpret_cast<float2*>(dst + (half * (DH / 2) + j + e2) * VS + t0) = pr;
+      }
+    }
+  }
+}
+
+// fragment of a transposed [rows d][cols] LDS tile: rows 16*mb + lane%16, the
+// 8 columns {4g..4g+3, 16+4g..16+4g+3} + 32*ks (g = lane/16)
+template <typename T, int PITCH>
+__device__ __forceinline__ typename Frag<T>::type ld_tfrag(const T* t, int mb, int ks, int lane) {
+  const T* p = t + (16 * mb + (lane & 15)) * PITCH + 32 * ks + 4 * (lane >> 4);
+  if constexpr (sizeof(T) == 2) {
+    const u16x4 a = *reinterpret_cast<const u16x4*>(p);
+    const u16x4 bb = *reinterpret_cast<const u16x4*>(p + 16);
+    u16x8 u;
+    u[0] = a[0]; u[1] = a[1]; u[2] = a[2]; u[3] = a[3];
+    u[4] = bb[0]; u[5] = bb[1]; u[6] = bb[2]; u[7] = bb[3];
+    return __builtin_bit_cast(bf16x8, u);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 bb = *reinterpret_cast<const f32x4*>(p + 16);
+    f32x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+    r[4] = bb[0]; r[5] = bb[1]; r[6] = bb[2]; r[7] = bb[3];
+    return r;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type pk8(const f32x4& s0, const f32x4& s1) {
+  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  return pack8<T>(x);
+}
+
+__device__ int bwd_block_scan(int* a, int n, int* wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int seg = (n + 255) / 256;
+  const int lo = min(n, t * seg), hi = min(n, lo + seg);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  int v = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int base = v - s;
+  for (int j = 0; j < w; ++j) base += wsum[j];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  for (int i = lo; i < hi; ++i) {
+    const int x = a[i];
+    a[i] = base;
+    base += x;
+  }
+  __syncthreads();
+  return total;
+}
+
+// --------------------------------------------------------------- dq pass
+// D = dO . O is not taken from the rounded output o: with a_j the forward
+// weights, D = sum_window a_j (dO . v_j) + sum_c w_c delta_c exactly, so the
+// chunks are processed first (their terms do not involve D), then the window
+// accumulates U1 = sum a_j (dO . v_j) k_j and U2 = sum a_j k_j so that its dq
+// part scale (U1 - D U2) is formed once D is known.
+template <typename T, int G, int DH, int CB>
+__global__ __launch_bounds__(256) void k_bwd_dq(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dO, const T* __restrict__ kL, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ sT, const float* __restrict__ lse, float* __restrict__ Dv,
+    float* __restrict__ dq, float* __restrict__ dqhat, float* __restrict__ ds_o,
+    float* __restrict__ beta_o, float* __restrict__ delta_o, int N, int Hkv, int K, int W, int S,
+    float scale, int ntiles, int C) {
+  typedef typename Frag<T>::type FT;
+  constexpr int R = 64 * CB, TP = R / G, PPG = 16 / G;
+  constexpr int KS = DH / 32, MB = DH / 16;
+  constexpr int AS = R + 4;
+  constexpr int VS = 64 + KPAD;
+  constexpr int EPT = TP * 32 / 256;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* accT = reinterpret_cast<float*>(smem);  // [DH][AS]
+  float* Ls = accT + DH * AS;                    // [R]
+  float* Ds = Ls + R;                            // [R] chunk part of D, then D
+  float* wcS = Ds + R;                           // [R][K] fusion weight w_c
+  float* dlS = wcS + R * K;                      // [R][K] delta_c
+  T* ktb = reinterpret_cast<T*>(dlS + R * K);    // [4][DH][VS]
+  int* off = reinterpret_cast<int*>(ktb + 4 * DH * VS);
+  int* gb = off + C;
+  int* grp = gb + C;
+  const int NGMAX = min(TP * K, TP * K / PPG + C + 1);
+  uint16_t* ent = reinterpret_cast<uint16_t*>(grp + 2 * NGMAX);
+  __shared__ int wsum[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tile = ntiles - 1 - blockIdx.x;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int Hq = Hkv * G;
+  const int p0 = tile * TP;
+  const int plast = min(p0 + TP - 1, N - 1);
+  const int ndmax = n_distant(plast, W, S);
+  const T* kg = k + (size_t)bg * N * DH;
+  const T* vg = v + (size_t)bg * N * DH;
+  T* kt = ktb + w * DH * VS;
+
+  for (int x = tid; x < R * K; x += 256) {
+    wcS[x] = 0.f;
+    dlS[x] = 0.f;
+  }
+  for (int x = tid; x < DH * AS; x += 256) accT[x] = 0.f;
+  for (int x = tid; x < R; x += 256) {
+    const int pos = p0 + x / G, hh = x % G;
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + (pos < N ? pos : N - 1);
+    Ls[x] = lse[ro];
+    Ds[x] = 0.f;
+  }
+  // bucket the tile's selections by chunk
+  for (int x = tid; x < ndmax; x += 256) off[x] = 0;
+  __syncthreads();
+  int my_c[EPT], my_r[EPT];
+  const int E = TP * K;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int x = tid + 256 * j;
+    my_c[j] = -1;
+    my_r[j] = 0;
+    if (x < E) {
+      const int pl = x / K, kk = x - pl * K;
+      const int pos = p0 + pl;
+      const int c = pos < N ? topk_idx[((size_t)bg * N + pos) * K + kk] : -1;
+      if (c >= 0 && c < ndmax) {
+        my_c[j] = c;
+        my_r[j] = atomicAdd(&off[c], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int x = tid; x < ndmax; x += 256) gb[x] = (off[x] + PPG - 1) / PPG;
+  __syncthreads();
+  const int Etot = bwd_block_scan(off, ndmax, wsum);
+  const int NG = bwd_block_scan(gb, ndmax, wsum);
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int c = my_c[j];
+    if (c >= 0) {
+      const int x = tid + 256 * j;
+      const int pl = x / K, kk = x - pl * K;
+      const int r = my_r[j];
+      ent[off[c] + r] = (uint16_t)((pl << 6) | kk);
+      if (r % PPG == 0) {
+        const int gi = gb[c] + r / PPG;
+        const int n = (c + 1 < ndmax ? off[c + 1] : Etot) - off[c] - r;
+        grp[2 * gi] = c;
+        grp[2 * gi + 1] = ((off[c] + r) << 5) | (n < PPG ? n : PPG);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- selected chunks (terms free of D)
+  for (int gi = w; gi < NG; gi += 4) {
+    const int c = grp[2 * gi];
+    const int gdesc = grp[2 * gi + 1];
+    const int st = gdesc >> 5, n = gdesc & 31;
+    const int col = lane & 15;
+    const int ei = col / G, hh = col % G;
+    const bool valid = ei < n;
+    const int en = ent[st + (valid ? ei : 0)];
+    const int pl = en >> 6, kk = en & 63;
+    const int pos = p0 + pl;
+    const int row = pl * G + hh;
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+    FT qf[KS], df[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = ld8<T>(q + ro * DH + 8 * (lane >> 4) + 32 * ks);
+      df[ks] = ld8<T>(dO + ro * DH + 8 * (lane >> 4) + 32 * ks);
+    }
+    const T* kc = kg + (size_t)c * 64 * DH;
+    const T* vc = vg + (size_t)c * 64 * DH;
+    f32x4 sa[4], pa[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const size_t to = (size_t)(16 * tb + (lane & 15)) * DH + 8 * (lane >> 4);
+      sa[tb] = zero4();
+      pa[tb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sa[tb] = mma16(ld8<T>(kc + to + 32 * ks), qf[ks], sa[tb]);
+        pa[tb] = mma16(ld8<T>(vc + to + 32 * ks), df[ks], pa[tb]);
+      }
+    }
+    wave_lds_sync();
+    stage_t64<T, DH>(kc, 64, kt, lane);
+    float mx = NEG_INF;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[tb][i] *= scale;
+        mx = fmaxf(mx, sa[tb][i]);
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    float ls = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __expf(sa[tb][i] - mx);
+        sa[tb][i] = pv;
+        ls += pv;
+      }
+    ls += shfl_xor(ls, 16);
+    ls += shfl_xor(ls, 32);
+    const float inv = 1.f / ls;
+    float dl = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[tb][i] *= inv;  // p within the chunk
+        dl += sa[tb][i] * pa[tb][i];
+      }
+    dl += shfl_xor(dl, 16);
+    dl += shfl_xor(dl, 32);  // delta_c = sum p (dO . v)
+    const float sc = valid ? sT[ro * K + kk] : 0.f;
+    const float Lrow = Ls[row];
+    const float wc = valid ? __expf(sc - Lrow) : 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[tb][i] = wc * sa[tb][i] * (pa[tb][i] - dl);  // dx
+    wave_lds_sync();
+    f32x4 dqc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dqc[mb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const FT pf = pk8<T>(sa[2 * ks], sa[2 * ks + 1]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) dqc[mb] = mma16(ld_tfrag<T, VS>(kt, mb, ks, lane), pf, dqc[mb]);
+    }
+    if (valid) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          atomicAdd(&accT[(16 * mb + 4 * (lane >> 4) + i) * AS + row], dqc[mb][i] * scale);
+      if ((lane >> 4) == 0) {
+        wcS[row * K + kk] = wc;
+        dlS[row * K + kk] = dl;
+        atomicAdd(&Ds[row], wc * dl);
+        beta_o[ro * K + kk] = sc - Lrow - (mx + __logf(ls));
+        delta_o[ro * K + kk] = dl;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- window: U1, U2 and its part of D
+  {
+    const int rbase = w * 16 * CB;
+    const int pw_lo = p0 + rbase / G;
+    const int pw_hi = min(p0 + (rbase + 16 * CB - 1) / G, N - 1);
+    FT qf[CB][KS], df[CB][KS];
+    int prow[CB], wsr[CB];
+    float Lr[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int r = rbase + 16 * cb + (lane & 15);
+      const int pos = p0 + r / G, hh = r % G;
+      prow[cb] = pos < N ? pos : -1;
+      wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
+      const int pc = pos < N ? pos : N - 1;
+      const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pc;
+      Lr[cb] = Ls[r];
+      const T* qs = q + ro * DH + 8 * (lane >> 4);
+      const T* ds = dO + ro * DH + 8 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[cb][ks] = ld8<T>(qs + 32 * ks);
+        df[cb][ks] = ld8<T>(ds + 32 * ks);
+      }
+    }
+    f32x4 u1[MB][CB], u2[MB][CB];
+    float dw[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      dw[cb] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        u1[mb][cb] = zero4();
+        u2[mb][cb] = zero4();
+      }
+    }
+    if (pw_lo < N) {
+      const int kv_lo = n_distant(pw_lo, W, S) * S;
+      for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 64) {
+        const int nvalid = min(64, N - kv0);
+        f32x4 sa[4][CB], pa[4][CB];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          int tok = 16 * tb + (lane & 15);
+          tok = tok < nvalid ? tok : 0;
+          const T* ksrc = kg + (size_t)(kv0 + tok) * DH + 8 * (lane >> 4);
+          const T* vsrc = vg + (size_t)(kv0 + tok) * DH + 8 * (lane >> 4);
+          FT kf[KS], vf[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            kf[ks] = ld8<T>(ksrc + 32 * ks);
+            vf[ks] = ld8<T>(vsrc + 32 * ks);
+          }
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            sa[tb][cb] = zero4();
+            pa[tb][cb] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              sa[tb][cb] = mma16(kf[ks], qf[cb][ks], sa[tb][cb]);
+              pa[tb][cb] = mma16(vf[ks], df[cb][ks], pa[tb][cb]);
+            }
+          }
+        }
+        wave_lds_sync();
+        stage_t64<T, DH>(kg + (size_t)kv0 * DH, nvalid, kt, lane);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = kv0 + 16 * tb + 4 * (lane >> 4) + i;
+              const bool ok = prow[cb] >= 0 && j <= prow[cb] && j >= wsr[cb];
+              const float a = ok ? __expf(sa[tb][cb][i] * scale - Lr[cb]) : 0.f;
+              const float adp = a * pa[tb][cb][i];
+              dw[cb] += adp;
+              sa[tb][cb][i] = a;
+              pa[tb][cb][i] = adp;
+            }
+        wave_lds_sync();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const FT kf = ld_tfrag<T, VS>(kt, mb, ks, lane);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+              u1[mb][cb] = mma16(kf, pk8<T>(pa[2 * ks][cb], pa[2 * ks + 1][cb]), u1[mb][cb]);
+              u2[mb][cb] = mma16(kf, pk8<T>(sa[2 * ks][cb], sa[2 * ks + 1][cb]), u2[mb][cb]);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float dsum = dw[cb];
+      dsum += shfl_xor(dsum, 16);
+      dsum += shfl_xor(dsum, 32);
+      const int r = rbase + 16 * cb + (lane & 15);
+      const float D = dsum + Ds[r];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          accT[(16 * mb + 4 * (lane >> 4) + i) * AS + r] += scale * (u1[mb][cb][i] - D * u2[mb][cb][i]);
+      wave_lds_sync();
+      if ((lane >> 4) == 0) {
+        Ds[r] = D;
+        if (prow[cb] >= 0) Dv[((size_t)b * Hq + g * G + r % G) * N + prow[cb]] = D;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- ds_c = w_c (delta_c - D); dq = token part + scale sum_c ds_c kL_c
+  for (int x = tid; x < R * K; x += 256) {
+    const int r = x / K, kk = x - r * K;
+    const int pos = p0 + r / G, hh = r % G;
+    if (pos >= N) continue;
+    const float dsv = wcS[x] * (dlS[x] - Ds[r]);
+    wcS[x] = dsv;
+    ds_o[(((size_t)b * Hq + g * G + hh) * N + pos) * K + kk] = dsv;
+  }
+  __syncthreads();
+  for (int x = tid; x < R * DH; x += 256) {
+    const int dd = x % DH, r = x / DH;
+    const int pos = p0 + r / G, hh = r % G;
+    if (pos >= N) continue;
+    const int32_t* ti = topk_idx + ((size_t)bg * N + pos) * K;
+    float sur = 0.f;
+    for (int kk = 0; kk < K; ++kk) {
+      const int c = ti[kk];
+      if (c >= 0) sur += wcS[r * K + kk] * to_f<T>(kL[((size_t)bg * C + c) * DH + dd]);
+    }
+    sur *= scale;
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+    dq[ro * DH + dd] = accT[dd * AS + r] + sur;
+    if (dqhat != nullptr) dqhat[ro * DH + dd] = sur;
+  }
+}
+
+// --------------------------------------------------------------- dk / dv pass
+template <typename T, typename QT, int G, int DH>
+__global__ __launch_bounds__(256) void k_bwd_dkdv(
+    const T* __restrict__ q, const QT* __restrict__ qs, const T* __restrict__ k,
+    const T* __restrict__ v, const T* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ Dv, const int* __restrict__ ioff, const int* __restrict__ ilst,
+    const float* __restrict__ ds_i, const float* __restrict__ beta_i,
+    const float* __restrict__ delta_i, float* __restrict__ dk, float* __restrict__ dv,
+    float* __restrict__ dkL, float* __restrict__ de, int N, int Hkv, int K, int W, int S,
+    float scale, int C) {
+  typedef typename Frag<T>::type FT;
+  constexpr int KS = DH / 32, MB = DH / 16;
+  constexpr int RP = 32 + KPAD;  // pitch of the transposed 32-row staging
+  // dynamic LDS: per-wave Q^T / dO^T staging, later reused for the reduction
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* qt_all = reinterpret_cast<T*>(smem);               // [4][DH * RP]
+  T* dt_all = qt_all + 4 * DH * RP;                     // [4][DH * RP]
+  float* red = reinterpret_cast<float*>(smem);          // [2][64 * DH] (after the loop)
+  __shared__ float redl[DH + 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int blk = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int Hq = Hkv * G;
+  const int kv0 = blk * 64;
+  const int nvalid = min(64, N - kv0);
+  for (int x = tid; x <= DH; x += 256) redl[x] = 0.f;
+  // this block's keys/values as B operands of S = Q K^T and dP = dO V^T
+  FT kb[4][KS], vb[4][KS];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    int tok = 16 * tb + (lane & 15);
+    tok = tok < nvalid ? tok : 0;
+    const size_t to = ((size_t)bg * N + kv0 + tok) * DH + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kb[tb][ks] = ld8<T>(k + to + 32 * ks);
+      vb[tb][ks] = ld8<T>(v + to + 32 * ks);
+    }
+  }
+  __syncthreads();
+  // rows: window rows (positions kv0 .. i_hi, all heads) then the rows that
+  // selected this chunk (all heads)
+  const int i_hi = min(N - 1, kv0 + 64 + W - 2);
+  const int nw = (i_hi - kv0 + 1) * G;
+  const bool chunk = blk < C;
+  const int e0 = chunk ? ioff[(size_t)bg * (C + 1) + blk] : 0;
+  const int ne = chunk ? ioff[(size_t)bg * (C + 1) + blk + 1] - e0 : 0;
+  const int* lst = ilst + (size_t)bg * N * K + e0;
+  const int ngw = (nw + 31) / 32, ngc = (ne * G + 31) / 32;
+  f32x4 dka[4][MB], dva[4][MB];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
+      dka[tb][nb] = zero4();
+      dva[tb][nb] = zero4();
+    }
+  float dkl[(DH + 63) / 64];
+#pragma unroll
+  for (int j = 0; j < (DH + 63) / 64; ++j) dkl[j] = 0.f;
+  float dea = 0.f;
+  T* qt = qt_all + w * DH * RP;
+  T* dt = dt_all + w * DH * RP;
+  for (int gi = w; gi < ngw + ngc; gi += 4) {
+    const bool isw = gi < ngw;
+    const int rb0 = 32 * (isw ? gi : gi - ngw);
+    // A fragments: rows r = 16*rb + lane%16 of the group
+    FT qa[2][KS], da[2][KS];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int rr = rb0 + 16 * rb + (lane & 15);
+      int pos, hh;
+      bool ok;
+      if (isw) {
+        ok = rr < nw;
+        pos = kv0 + (ok ? rr : 0) / G;
+        hh = (ok ? rr : 0) % G;
+      } else {
+        ok = rr < ne * G;
+        const int en = lst[(ok ? rr : 0) / G];
+        pos = en >> 6;
+        hh = (ok ? rr : 0) % G;
+      }
+      const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qa[rb][ks] = ld8<T>(q + ro * DH + 8 * (lane >> 4) + 32 * ks);
+        da[rb][ks] = ld8<T>(dO + ro * DH + 8 * (lane >> 4) + 32 * ks);
+      }
+    }
+    // per-lane rows of the D layout: 4*(lane/16) + i (+16 rb)
+    float bias[2][4], dlt[2][4];
+    int rpos[2][4], rws[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = rb0 + 16 * rb + 4 * (lane >> 4) + i;
+        if (isw) {
+          const bool ok = rr < nw;
+          const int pos = kv0 + (ok ? rr : 0) / G, hh = (ok ? rr : 0) % G;
+          const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+          rpos[rb][i] = ok ? pos : -1;
+          rws[rb][i] = n_distant(pos, W, S) * S;
+          bias[rb][i] = -lse[ro];
+          dlt[rb][i] = Dv[ro];
+        } else {
+          const bool ok = rr < ne * G;
+          const int en = lst[(ok ? rr : 0) / G];
+          const int pos = en >> 6, kk = en & 63, hh = (ok ? rr : 0) % G;
+          const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+          rpos[rb][i] = ok ? 1 : -1;
+          rws[rb][i] = 0;
+          bias[rb][i] = beta_i[ro * K + kk];
+          dlt[rb][i] = delta_i[ro * K + kk];
+        }
+      }
+    f32x4 sa[2][4], pa[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        sa[rb][tb] = zero4();
+        pa[rb][tb] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sa[rb][tb] = mma16(qa[rb][ks], kb[tb][ks], sa[rb][tb]);
+          pa[rb][tb] = mma16(da[rb][ks], vb[tb][ks], pa[rb][tb]);
+        }
+      }
+    // p (a_j) and dS (dx_j) in the D layout: row 4g+i (+16 rb), token lane%16 (+16 tb)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * tb + (lane & 15);
+          const int j = kv0 + tok;
+          bool ok = rpos[rb][i] >= 0 && tok < nvalid;
+          if (isw) ok = ok && j <= rpos[rb][i] && j >= rws[rb][i];
+          const float a = ok ? __expf(sa[rb][tb][i] * scale + bias[rb][i]) : 0.f;
+          sa[rb][tb][i] = a;
+          pa[rb][tb][i] = a * (pa[rb][tb][i] - dlt[rb][i]);
+        }
+    // stage Q^T and dO^T of the group's 32 rows: [d][row]
+    wave_lds_sync();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int rr = 16 * rb + (lane & 15);
+        if constexpr (sizeof(T) == 2) {
+          const u16x8 uq = __builtin_bit_cast(u16x8, qa[rb][ks]);
+          const u16x8 ud = __builtin_bit_cast(u16x8, da[rb][ks]);
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) {
+            const int dd = 8 * (lane >> 4) + 32 * ks + e2;
+            qt[dd * RP + rr] = uq[e2];
+            dt[dd * RP + rr] = ud[e2];
+          }
+        } else {
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) {
+            const int dd = 8 * (lane >> 4) + 32 * ks + e2;
+            qt[dd * RP + rr] = qa[rb][ks][e2];
+            dt[dd * RP + rr] = da[rb][ks][e2];
+          }
+        }
+      }
+    wave_lds_sync();
+    // dV += P^T dO, dK += dS^T Q over the 32 rows (one 32-deep step)
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb) {
+      const FT dof = ld_tfrag<T, RP>(dt, nb, 0, lane);
+      const FT qf = ld_tfrag<T, RP>(qt, nb, 0, lane);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        dva[tb][nb] = mma16(pk8<T>(sa[0][tb], sa[1][tb]), dof, dva[tb][nb]);
+        dka[tb][nb] = mma16(pk8<T>(pa[0][tb], pa[1][tb]), qf, dka[tb][nb]);
+      }
+    }
+    // surrogate gradients of this chunk: dkL += scale ds q_hat, de += ds
+    if (!isw) {
+      const int nrows = min(32, ne * G - rb0);
+      for (int r = 0; r < nrows; ++r) {
+        const int rr = rb0 + r;
+        const int en = lst[rr / G];
+        const int pos = en >> 6, kk = en & 63, hh = rr % G;
+        const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+        const float dsv = ds_i[ro * K + kk];
+#pragma unroll
+        for (int j = 0; j < (DH + 63) / 64; ++j) {
+          const int dd = lane + 64 * j;
+          if (dd < DH) dkl[j] += dsv * to_f<QT>(qs[ro * DH + dd]);
+        }
+        dea += dsv;
+      }
+    }
+  }
+  // reduce the four waves' partial sums in LDS (reusing the staging space), then write
+  __syncthreads();
+  for (int x = tid; x < 2 * 64 * DH; x += 256) red[x] = 0.f;
+  __syncthreads();
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int nb = 0; nb < MB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tb + 4 * (lane >> 4) + i;
+        const int dd = 16 * nb + (lane & 15);
+        atomicAdd(&red[tok * DH + dd], dka[tb][nb][i]);
+        atomicAdd(&red[64 * DH + tok * DH + dd], dva[tb][nb][i]);
+      }
+#pragma unroll
+  for (int j = 0; j < (DH + 63) / 64; ++j)
+    if (lane + 64 * j < DH) atomicAdd(&redl[lane + 64 * j], dkl[j]);
+  if (lane == 0) atomicAdd(&redl[DH], dea);
+  __syncthreads();
+  for (int x = tid; x < 64 * DH; x += 256) {
+    const int tok = x / DH;
+    if (tok < nvalid) {
+      const size_t o = ((size_t)bg * N + kv0 + tok) * DH + (x - tok * DH);
+      dk[o] = red[x] * scale;
+      dv[o] = red[64 * DH + x];
+    }
+  }
+  if (chunk) {
+    for (int x = tid; x < DH; x += 256) dkL[((size_t)bg * C + blk) * DH + x] = redl[x] * scale;
+    if (tid == 0) de[(size_t)bg * C + blk] = redl[DH];
+  }
+}
+
+// --------------------------------------------------------------- host side
+namespace {
+struct BwdWs {
+  float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du;
+  int *cnt, *off, *cur, *lst;
+};
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t carve(const Dims& p, void* base, BwdWs* w) {
+  char* c = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    void* ptr = c ? c + o : nullptr;
+    o += up256(bytes);
+    return ptr;
+  };
+  const size_t rows = (size_t)p.B * p.Hq * p.N;
+  const size_t bg = (size_t)p.B * p.Hkv;
+  const bool qc = p.r > 0;
+  w->qhat = (float*)take(qc ? rows * p.d * 4 : 0);
+  w->u = (float*)take(qc ? (size_t)p.B * p.N * p.Hq * p.r * 4 : 0);
+  w->Dv = (float*)take(rows * 4);
+  w->sT = (float*)take(rows * p.K * 4);
+  w->ds = (float*)take(rows * p.K * 4);
+  w->beta = (float*)take(rows * p.K * 4);
+  w->delta = (float*)take(rows * p.K * 4);
+  w->dqhat = (float*)take(qc ? rows * p.d * 4 : 0);
+  w->du = (float*)take(qc ? (size_t)p.B * p.N * p.Hq * p.r * 4 : 0);
+  w->cnt = (int*)take(bg * p.C * 4);
+  w->off = (int*)take(bg * (p.C + 1) * 4);
+  w->cur = (int*)take(bg * p.C * 4);
+  w->lst = (int*)take(bg * (size_t)p.N * p.K * 4);
+  return o;
+}
+
+template <typename T, int G, int DH, int CB>
+size_t dq_lds(const Dims& p) {
+  constexpr int R = 64 * CB, TP = R / G, PPG = 16 / G;
+  const int ngmax = std::min(TP * p.K, TP * p.K / PPG + p.C + 1);
+  size_t s = sizeof(float) * ((size_t)DH * (R + 4) + 2 * R + 2 * (size_t)R * p.K);
+  s += sizeof(T) * 4 * DH * (64 + KPAD);
+  s += sizeof(int) * (2 * (size_t)p.C + 2 * (size_t)ngmax);
+  s += sizeof(uint16_t) * (size_t)TP * p.K;
+  return (s + 15) & ~(size_t)15;
+}
+
+template <typename T, int CB>
+size_t dq_lds_g(const Dims& p) {
+  switch (p.G) {
+    case 1: return p.d == 64 ? dq_lds<T, 1, 64, CB>(p) : dq_lds<T, 1, 128, CB>(p);
+    case 2: return p.d == 64 ? dq_lds<T, 2, 64, CB>(p) : dq_lds<T, 2, 128, CB>(p);
+    case 4: return p.d == 64 ? dq_lds<T, 4, 64, CB>(p) : dq_lds<T, 4, 128, CB>(p);
+    default: return (size_t)-1;
+  }
+}
+
+size_t dq_lds_bytes(const Dims& p) {
+  return (p.dtype == 1 ? dq_lds_g<uint16_t, 2>(p) : dq_lds_g<float, 1>(p)) + 64;
+}
+
+size_t dkdv_lds(const Dims& p) {
+  const size_t el = p.dtype == 1 ? 2 : 4;
+  return std::max(2 * 4 * (size_t)p.d * (32 + KPAD) * el, 2 * 64 * (size_t)p.d * 4);
+}
+
+unsigned grid1(size_t n) { return (unsigned)std::min<size_t>((n + 255) / 256, 65535 * 4); }
+}  // namespace
+
+size_t bwd_workspace(const Dims& p) {
+  if (dq_lds_bytes(p) > 160 * 1024 || dkdv_lds(p) + 1024 > 160 * 1024) return (size_t)-1;
+  if ((size_t)p.N * p.K >= (1u << 31)) return (size_t)-1;
+  BwdWs w;
+  return carve(p, nullptr, &w);
+}
+
+template <typename T, typename QT, int G, int DH>
+static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const void* k,
+                         const void* v, const void* kL, const void* e, const void* o,
+                         const float* lse, const int32_t* topk_idx, const void* dO, float* dq,
+                         float* dk, float* dv, float* dkL, float* de, BwdWs& w, hipStream_t st) {
+  constexpr int CB = sizeof(T) == 2 ? 2 : 1;
+  const size_t rows = (size_t)p.B * p.Hq * p.N;
+  const size_t bg = (size_t)p.B * p.Hkv;
+  hipError_t err;
+  hipLaunchKernelGGL((k_bwd_prep<T, QT, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     (const QT*)qsrc, (const T*)kL, (const T*)e, topk_idx, w.sT, (long)rows, p.N,
+                     p.Hq, p.Hkv, G, p.C, p.K, p.scale);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // inverse index
+  hipLaunchKernelGGL(k_fill_i32, dim3(grid1(bg * p.C)), dim3(256), 0, st, w.cnt, bg * p.C, 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(grid1(bg * p.C)), dim3(256), 0, st, w.cur, bg * p.C, 0);
+  const long total = (long)bg * p.N * p.K;
+  hipLaunchKernelGGL(k_inv_count, dim3(grid1(total)), dim3(256), 0, st, topk_idx, w.cnt, total, p.N,
+                     p.K, p.C);
+  hipLaunchKernelGGL(k_inv_scan, dim3((unsigned)bg), dim3(256), 0, st, w.cnt, w.off, p.C);
+  hipLaunchKernelGGL(k_inv_fill, dim3(grid1(total)), dim3(256), 0, st, topk_idx, w.off, w.cur, w.lst,
+                     total, p.N, p.K, p.C);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // dq pass
+  {
+    constexpr int TP = 64 * CB / G;
+    const int ntiles = (p.N + TP - 1) / TP;
+    const size_t lds = dq_lds<T, G, DH, CB>(p);
+    auto kern = k_bwd_dq<T, G, DH, CB>;
+    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+      return err;
+    hipLaunchKernelGGL(kern, dim3(ntiles, (unsigned)bg), dim3(256), lds, st, (const T*)q, (const T*)k,
+                       (const T*)v, (const T*)dO, (const T*)kL, topk_idx, w.sT, lse, w.Dv, dq,
+                       w.dqhat, w.ds, w.beta, w.delta, p.N, p.Hkv, p.K, p.W, p.S, p.scale, ntiles,
+                       p.C);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  // dk / dv pass
+  {
+    const int nblk = (p.N + 63) / 64;
+    const size_t lds = dkdv_lds(p);
+    auto kern = k_bwd_dkdv<T, QT, G, DH>;
+    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+      return err;
+    hipLaunchKernelGGL(kern, dim3(nblk, (unsigned)bg), dim3(256), lds, st,
+                       (const T*)q, (const QT*)qsrc, (const T*)k, (const T*)v, (const T*)dO, lse,
+                       w.Dv, w.off, w.lst, w.ds, w.beta, w.delta, dk, dv, dkL, de, p.N, p.Hkv, p.K,
+                       p.W, p.S, p.scale, p.C);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+template <typename T, typename QT, int G>
+static hipError_t bwd_d(const Dims& p, const void* q, const void* qs, const void* k, const void* v,
+                        const void* kL, const void* e, const void* o, const float* lse,
+                        const int32_t* idx, const void* dO, float* dq, float* dk, float* dv,
+                        float* dkL, float* de, BwdWs& w, hipStream_t st) {
+  if (p.d == 64) return bwd_go<T, QT, G, 64>(p, q, qs, k, v, kL, e, o, lse, idx, dO, dq, dk, dv, dkL, de, w, st);
+  return bwd_go<T, QT, G, 128>(p, q, qs, k, v, kL, e, o, lse, idx, dO, dq, dk, dv, dkL, de, w, st);
+}
+
+template <typename T, typename QT>
+static hipError_t bwd_g(const Dims& p, const void* q, const void* qs, const void* k, const void* v,
+                        const void* kL, const void* e, const void* o, const float* lse,
+                        const int32_t* idx, const void* dO, float* dq, float* dk, float* dv,
+                        float* dkL, float* de, BwdWs& w, hipStream_t st) {
+  switch (p.G) {
+    case 1: return bwd_d<T, QT, 1>(p, q, qs, k, v, kL, e, o, lse, idx, dO, dq, dk, dv, dkL, de, w, st);
+    case 2: return bwd_d<T, QT, 2>(p, q, qs, k, v, kL, e, o, lse, idx, dO, dq, dk, dv, dkL, de, w, st);
+    case 4: return bwd_d<T, QT, 4>(p, q, qs, k, v, kL, e, o, lse, idx, dO, dq, dk, dv, dkL, de, w, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v, const void* kL,
+                      const void* e, const void* h, const void* W_down, const void* W_up,
+                      const void* o, const float* lse, const int32_t* topk_idx, const void* dO,
+                      float* dq, float* dk, float* dv, float* dkL, float* de, float* dW_down,
+                      float* dW_up, float* dh, void* ws, hipStream_t st) {
+  BwdWs w;
+  carve(p, ws, &w);
+  const bool qc = p.r > 0;
+  hipError_t err;
+  if (qc) {
+    if ((err = launch_qcal(p, p.N, q, h, W_down, W_up, w.qhat, w.u, st)) != hipSuccess) return err;
+  } else {
+    w.dqhat = nullptr;
+  }
+  if (p.dtype == 1) {
+    err = qc ? bwd_g<uint16_t, float>(p, q, w.qhat, k, v, kL, e, o, lse, topk_idx, dO, dq, dk, dv, dkL, de, w, st)
+             : bwd_g<uint16_t, uint16_t>(p, q, q, k, v, kL, e, o, lse, topk_idx, dO, dq, dk, dv, dkL, de, w, st);
+  } else {
+    err = bwd_g<float, float>(p, q, qc ? (const void*)w.qhat : q, k, v, kL, e, o, lse, topk_idx, dO,
+                              dq, dk, dv, dkL, de, w, st);
+  }
+  if (err != hipSuccess || !qc) return err;
+  // ---- Q-Cal backward
+  const long Hr = (long)p.Hq * p.r;
+  const long NHr = (long)p.N * Hr;
+  const int dt = p.dtype == 1 ? 1 : 0;
+  // du[b, i, h, :] = W_up[h]^T dq_hat[b, h, i, :]
+  {
+    GemmArgs g;
+    g.M = p.N; g.N = p.r; g.K = p.d;
+    g.akm = false; g.bkm = false;
+    g.lda = p.d; g.ldb = p.r; g.ldc = Hr;
+    g.n1 = p.B; g.n2 = p.Hq;
+    g.sA1 = (long)p.Hq * p.N * p.d; g.sA2 = (long)p.N * p.d;
+    g.sB1 = 0; g.sB2 = (long)p.d * p.r;
+    g.sC1 = NHr; g.sC2 = p.r;
+    g.C = w.du;
+    if ((err = gemm(g, w.dqhat, 0, W_up, dt, st)) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid1((size_t)Hr * p.D)), dim3(256), 0, st, dW_down, (size_t)Hr * p.D, 0.f);
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid1((size_t)p.Hq * p.d * p.r)), dim3(256), 0, st, dW_up, (size_t)p.Hq * p.d * p.r, 0.f);
+  // dW_up[h] += sum_i dq_hat[b, h, i, :] (x) u[b, i, h, :]
+  {
+    GemmArgs g;
+    g.M = p.d; g.N = p.r; g.K = p.N;
+    g.akm = true; g.bkm = false;
+    g.lda = p.d; g.ldb = Hr; g.ldc = p.r;
+    g.n1 = p.B; g.n2 = p.Hq;
+    g.sA1 = (long)p.Hq * p.N * p.d; g.sA2 = (long)p.N * p.d;
+    g.sB1 = NHr; g.sB2 = p.r;
+    g.sC1 = 0; g.sC2 = (long)p.d * p.r;
+    g.C = dW_up;
+    g.splits = std::max(1, p.N / 1024);
+    g.accumulate = true;
+    if ((err = gemm(g, w.dqhat, 0, w.u, 0, st)) != hipSuccess) return err;
+  }
+  // dW_down[h] += sum_i du[b, i, h, :] (x) h[b, i, :]
+  {
+    GemmArgs g;
+    g.M = p.r; g.N = p.D; g.K = p.N;
+    g.akm = true; g.bkm = false;
+    g.lda = Hr; g.ldb = p.D; g.ldc = p.D;
+    g.n1 = p.B; g.n2 = p.Hq;
+    g.sA1 = NHr; g.sA2 = p.r;
+    g.sB1 = (long)p.N * p.D; g.sB2 = 0;
+    g.sC1 = 0; g.sC2 = (long)p.r * p.D;
+    g.C = dW_down;
+    g.splits = std::max(1, p.N / 1024);
+    g.accumulate = true;
+    if ((err = gemm(g, w.du, 0, h, dt, st)) != hipSuccess) return err;
+  }
+  // dh[b, i, :] = sum_{h, j} du[b, i, h, j] W_down[h, j, :]
+  if (dh != nullptr) {
+    GemmArgs g;
+    g.M = p.N; g.N = p.D; g.K = (int)Hr;
+    g.akm = false; g.bkm = false;
+    g.lda = Hr; g.ldb = p.D; g.ldc = p.D;
+    g.n1 = p.B; g.n2 = 1;
+    g.sA1 = NHr; g.sB1 = 0; g.sC1 = (long)p.N * p.D;
+    g.C = dh;
+    if ((err = gemm(g, w.du, 0, W_down, dt, st)) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace hils

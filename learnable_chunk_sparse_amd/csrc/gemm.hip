@@ -1,0 +1,184 @@
+// Batched C (+)= A * B on bf16 MFMA, used by the Q-Cal backward (weight and
+// input gradients of the low-rank query calibration).
+//
+// A is M x K and B is K x N; each may be stored "row-major" (A[m][k],
+// B[k][n]) or "k-major" (A[k][m], B[n][k]) through the template flags, so
+// the transposed products of a backward pass (X^T dY, dY W^T) need no
+// separate transpose. fp32 operands are split into a bf16 hi part and a bf16
+// lo part (x = hi + lo + O(2^-16 |x|)); products of the parts are exact in
+// the MFMA and accumulate in fp32, which keeps ~16 significant bits per
+// product term (hi*hi + hi*lo + lo*hi). bf16 operands are used as they are.
+// Tiles of 64 x 64 with a 32-deep k step are staged through LDS in the
+// [row][k] layout the fragments read; split-K adds partial tiles atomically.
+#include "hils_common.h"
+#include "hils_internal.h"
+
+namespace hils {
+
+template <typename TA, typename TB, bool AKM, bool BKM>
+__global__ __launch_bounds__(256) void k_gemm(const TA* __restrict__ A, const TB* __restrict__ B,
+                                              float* __restrict__ Cm, int M, int N, int K, long lda,
+                                              long ldb, long ldc, long sA1, long sA2, long sB1,
+                                              long sB2, long sC1, long sC2, int nz2, int kchunk,
+                                              int splits, int accumulate) {
+  constexpr bool ALO = sizeof(TA) == 4, BLO = sizeof(TB) == 4;
+  constexpr int KP = 40;  // padded k pitch (elements) of the LDS tiles
+  __shared__ __align__(16) uint16_t as_hi[64 * KP], bs_hi[64 * KP];
+  __shared__ __align__(16) uint16_t as_lo[ALO ? 64 * KP : 8], bs_lo[BLO ? 64 * KP : 8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int bz = blockIdx.z / splits, sp = blockIdx.z - bz * splits;
+  const int z1 = bz / nz2, z2 = bz - z1 * nz2;
+  A += z1 * sA1 + z2 * sA2;
+  B += z1 * sB1 + z2 * sB2;
+  Cm += z1 * sC1 + z2 * sC2;
+  const int k_begin = sp * kchunk, k_end = min(K, k_begin + kchunk);
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = zero4();
+
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    // ---- stage A (64 x 32) and B (32 x 64) as [row][k]
+    {
+      float x[8];
+      int r, kk;
+      if (!AKM) {  // A[m][k]: thread loads 8 k of one m
+        r = tid >> 2;
+        kk = (tid & 3) * 8;
+        const int m = m0 + r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = k0 + kk + j;
+          x[j] = (m < M && k < k_end) ? to_f<TA>(A[(long)m * lda + k]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint16_t hi = f2bf(x[j]);
+          as_hi[r * KP + kk + j] = hi;
+          if constexpr (ALO) as_lo[r * KP + kk + j] = f2bf(x[j] - bf2f(hi));
+        }
+      } else {  // A[k][m]: thread loads 8 m of one k
+        kk = tid >> 3;
+        r = (tid & 7) * 8;
+        const int k = k0 + kk;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int m = m0 + r + j;
+          x[j] = (m < M && k < k_end) ? to_f<TA>(A[(long)k * lda + m]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint16_t hi = f2bf(x[j]);
+          as_hi[(r + j) * KP + kk] = hi;
+          if constexpr (ALO) as_lo[(r + j) * KP + kk] = f2bf(x[j] - bf2f(hi));
+        }
+      }
+      if (!BKM) {  // B[k][n]: thread loads 8 n of one k
+        kk = tid >> 3;
+        r = (tid & 7) * 8;
+        const int k = k0 + kk;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int n = n0 + r + j;
+          x[j] = (n < N && k < k_end) ? to_f<TB>(B[(long)k * ldb + n]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint16_t hi = f2bf(x[j]);
+          bs_hi[(r + j) * KP + kk] = hi;
+          if constexpr (BLO) bs_lo[(r + j) * KP + kk] = f2bf(x[j] - bf2f(hi));
+        }
+      } else {  // B[n][k]: thread loads 8 k of one n
+        r = tid >> 2;
+        kk = (tid & 3) * 8;
+        const int n = n0 + r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = k0 + kk + j;
+          x[j] = (n < N && k < k_end) ? to_f<TB>(B[(long)n * ldb + k]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint16_t hi = f2bf(x[j]);
+          bs_hi[r * KP + kk + j] = hi;
+          if constexpr (BLO) bs_lo[r * KP + kk + j] = f2bf(x[j] - bf2f(hi));
+        }
+      }
+    }
+    __syncthreads();
+    bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int off = (32 * wm + 16 * mb + (lane & 15)) * KP + 8 * (lane >> 4);
+      ah[mb] = *reinterpret_cast<const bf16x8*>(as_hi + off);
+      if constexpr (ALO) al[mb] = *reinterpret_cast<const bf16x8*>(as_lo + off);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int off = (32 * wn + 16 * nb + (lane & 15)) * KP + 8 * (lane >> 4);
+      bh[nb] = *reinterpret_cast<const bf16x8*>(bs_hi + off);
+      if constexpr (BLO) bl[nb] = *reinterpret_cast<const bf16x8*>(bs_lo + off);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[mb][nb] = mma16(ah[mb], bh[nb], acc[mb][nb]);
+        if constexpr (BLO) acc[mb][nb] = mma16(ah[mb], bl[nb], acc[mb][nb]);
+        if constexpr (ALO) acc[mb][nb] = mma16(al[mb], bh[nb], acc[mb][nb]);
+      }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 32 * wm + 16 * mb + 4 * (lane >> 4) + i;
+        const int n = n0 + 32 * wn + 16 * nb + (lane & 15);
+        if (m < M && n < N) {
+          float* c = Cm + (long)m * ldc + n;
+          if (splits > 1 || accumulate)
+            atomicAdd(c, acc[mb][nb][i]);
+          else
+            *c = acc[mb][nb][i];
+        }
+      }
+}
+
+// C[z] (+)= A[z] * B[z] over the batch z = (z1, z2), z1 < g.n1, z2 < g.n2.
+template <typename TA, typename TB, bool AKM, bool BKM>
+static hipError_t gemm_go(const GemmArgs& g, const TA* A, const TB* B, hipStream_t st) {
+  int splits = g.splits < 1 ? 1 : g.splits;
+  int kchunk = (g.K + splits - 1) / splits;
+  kchunk = (kchunk + 31) / 32 * 32;
+  splits = (g.K + kchunk - 1) / kchunk;
+  dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, g.n1 * g.n2 * splits);
+  hipLaunchKernelGGL((k_gemm<TA, TB, AKM, BKM>), grid, dim3(256), 0, st, A, B, g.C, g.M, g.N, g.K,
+                     g.lda, g.ldb, g.ldc, g.sA1, g.sA2, g.sB1, g.sB2, g.sC1, g.sC2, g.n2, kchunk,
+                     splits, g.accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <typename TA, typename TB>
+static hipError_t gemm_t(const GemmArgs& g, const TA* A, const TB* B, hipStream_t st) {
+  if (!g.akm && !g.bkm) return gemm_go<TA, TB, false, false>(g, A, B, st);
+  if (!g.akm && g.bkm) return gemm_go<TA, TB, false, true>(g, A, B, st);
+  if (g.akm && !g.bkm) return gemm_go<TA, TB, true, false>(g, A, B, st);
+  return gemm_go<TA, TB, true, true>(g, A, B, st);
+}
+
+hipError_t gemm(const GemmArgs& g, const void* A, int a_dtype, const void* B, int b_dtype,
+                hipStream_t st) {
+  // dtype codes: 0 fp32, 1 bf16
+  if (a_dtype == 0 && b_dtype == 0) return gemm_t<float, float>(g, (const float*)A, (const float*)B, st);
+  if (a_dtype == 0 && b_dtype == 1) return gemm_t<float, uint16_t>(g, (const float*)A, (const uint16_t*)B, st);
+  if (a_dtype == 1 && b_dtype == 0) return gemm_t<uint16_t, float>(g, (const uint16_t*)A, (const float*)B, st);
+  return gemm_t<uint16_t, uint16_t>(g, (const uint16_t*)A, (const uint16_t*)B, st);
+}
+
+}  // namespace hils

@@ -249,8 +249,7 @@ hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, c
                           void* ws, size_t ws_bytes, void* stream) {
   hils_status s = check_problem(p, HILS_OP_BWD);
   if (s != HILS_OK) return s;
-  if (!q || !k || !v || !kL || !e || !o || !lse || !topk_idx || !dO || !dq || !dk || !dv || !dkL ||
-      !de)
+  if (!q || !k || !v || !kL || !e || !lse || !topk_idx || !dO || !dq || !dk || !dv || !dkL || !de)
     return HILS_ERR_INVALID;
   if (p->r > 0 && (!h || !W_down || !W_up || !dW_down || !dW_up)) return HILS_ERR_INVALID;
   const Dims d = dims_of(p);

@@ -40,6 +40,26 @@ hipError_t launch_decode(const Dims& p, const void* q_or_qhat, bool q_is_f32, co
                          const void* e, void* o, float* lse, int32_t* topk_idx, void* ws,
                          hipStream_t st);
 
+// Batched GEMM C (+)= A * B on bf16 MFMA (fp32 operands split hi + lo).
+// A is M x K: element (m, k) at A[m * lda + k] (akm = false) or A[k * lda + m]
+// (akm = true); B is K x N: (k, n) at B[k * ldb + n] (bkm = false) or
+// B[n * ldb + k] (bkm = true); C is M x N fp32 at C[m * ldc + n]. Batch
+// z = (z1, z2) offsets the operands by z1 * s?1 + z2 * s?2 elements.
+// splits > 1 splits K and adds partial tiles atomically (C must be zeroed);
+// accumulate adds into C.
+struct GemmArgs {
+  int M, N, K;
+  bool akm, bkm;
+  long lda, ldb, ldc;
+  int n1 = 1, n2 = 1;
+  long sA1 = 0, sA2 = 0, sB1 = 0, sB2 = 0, sC1 = 0, sC2 = 0;
+  float* C;
+  int splits = 1;
+  bool accumulate = false;
+};
+hipError_t gemm(const GemmArgs& g, const void* A, int a_dtype, const void* B, int b_dtype,
+                hipStream_t st);
+
 // Backward.
 size_t bwd_workspace(const Dims& p);
 hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v, const void* kL,

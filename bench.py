@@ -96,7 +96,7 @@ def cpu_baseline_prefill(wl, budget_s=12.0):
     passes = 0
     for b, g in groups:
         t = make_group_inputs(wl, b, g)
-        for offset in range(0, stride, 7):
+        for offset in range(0, stride):
             rows = list(range(offset, wl.N, stride))
             t0 = time.perf_counter()
             H.hils_forward(t, wl.S, wl.K, wl.W, rows=rows)
@@ -215,6 +215,53 @@ def bench_decode(args, torch, L):
     return out
 
 
+def train_algorithmic_flops(wl):
+    """Forward 4*d and backward 10*d flops per (query head, attended token)
+    (backward: S, dP, dq, dk and dv products), plus the routing scores."""
+    win_f, chk_f = fwd_algorithmic_flops(wl)
+    attn = win_f + chk_f
+    return attn + attn * 10 // 4 + route_algorithmic_flops(wl)
+
+
+def bench_train(args, torch, L):
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["train_345m"]
+    t = make_inputs(wl, device="cuda")
+    fb = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+    gb = None
+
+    def step():
+        nonlocal gb
+        o, lse, idx = L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
+                                      h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=fb)
+        g = L.hils_attn_bwd(t["q"], t["k"], t["v"], t["kL"], t["e"], o, lse, idx, t["dO"], wl.S,
+                            wl.K, wl.W, h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=gb)
+        if gb is None:
+            gb = (g, L._workspace(L.make_problem(t["q"], t["k"], wl.S, wl.K, wl.W, t["h"],
+                                                 t["W_down"]), L.OP_BWD, t["q"].device))
+
+    for _ in range(max(2, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 2)
+    rings = {sid: event_ring(n, torch) for sid in (L.STEP_ATTN_FWD, L.STEP_BWD)}
+    for sid, r in rings.items():
+        L.hils_set_timing_events(sid, *r)
+    sec = timed_steps(step, n, 0, torch)
+    for sid in rings:
+        L.hils_set_timing_events(sid)
+    ms = {sid: avg_ms(*r) for sid, r in rings.items()}
+    fl = train_algorithmic_flops(wl)
+    tf = fl / sec / 1e12
+    out = {"workload": wl.name, "tokens_per_s": wl.B * wl.N / sec, "ms_per_step": sec * 1e3,
+           "attn_fwd_ms": ms[L.STEP_ATTN_FWD], "bwd_ms": ms[L.STEP_BWD],
+           "mfma": {"achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flop_per_step": fl}}
+    del t, fb, gb
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +273,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the 512K decode leg")
     ap.add_argument("--decode-workload", default="decode_7b_512k")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-train", action="store_true", help="skip the training (fwd+bwd) leg")
+    ap.add_argument("--legs", default="prefill,decode,train",
+                    help="comma list of legs to run (prefill is always reported)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
@@ -237,8 +287,11 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     res, wl = bench_prefill(args, torch, L, None)
-    if not args.no_decode:
+    legs = set(args.legs.split(","))
+    if not args.no_decode and "decode" in legs:
         res["decode"] = bench_decode(args, torch, L)
+    if not args.no_train and "train" in legs:
+        res["train"] = bench_train(args, torch, L)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, args.cpu_budget)
     res["vs_baseline"] = None
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),

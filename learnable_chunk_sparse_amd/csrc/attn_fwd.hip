@@ -11,31 +11,60 @@
 //   L = log(sum_{c in T} exp(s_c) + exp(lse_W))
 //   o = sum_{c in T} exp(s_c - L) O_c + exp(lse_W - L) O_W
 //
+// Products use the transposed form S^T = K Q^T (tokens x rows), whose
+// accumulator layout is exactly the P^T operand of O^T = V^T P^T once the
+// token order inside each 32-token step is permuted identically on both
+// operands. V is transposed once per call into a token-permuted copy
+// (k_vt_perm), after which every MFMA operand is one aligned 16-byte global
+// load: no LDS staging, and the next key block / chunk is prefetched into a
+// second register set while the current one is multiplied.
+//
 // Tile: R = 64 * CB rows = TP positions x G heads of one (batch, KV head),
-// 4 waves. Products use the transposed form S^T = K Q^T (tokens x rows) so
-// that the probabilities land in registers exactly where the P^T operand of
-// O^T = V^T P^T needs them (the token order inside each 32-token step is
-// permuted identically on both operands; V is staged transposed in LDS).
-//   Phase A (window): wave w runs a banded flash attention over its own
-//     16*CB rows; the fusion normaliser L follows from lse_W and the
-//     selected scores, and exp(lse_W - L) O_W seeds an fp32 row accumulator
-//     in LDS.
-//   Phase B (chunks): the tile's (position, slot) selections are bucketed by
-//     chunk id (counting sort in LDS) and cut into groups of up to 16/G
-//     positions x G heads sharing one chunk; each group is one 64-token block
-//     of MFMA work, and exp(s_c - L) O_c is added to the rows' accumulators
-//     with LDS atomics. Compaction keeps MFMA columns busy even when adjacent
-//     queries pick different chunks.
+// four waves.
+//   Window phase: wave w runs a banded flash attention over its 16*CB rows.
+//     The fusion normaliser L follows from lse_W and the selected scores, and
+//     exp(lse_W - L) O_W seeds an fp32 row accumulator in LDS.
+//   Chunk phase: the tile's (position, slot) selections are bucketed by chunk
+//     (counting sort in LDS). Waves take chunks dynamically; a chunk's K and
+//     V^T fragments are loaded once and reused by all its row blocks (16 rows
+//     = 16/G positions x G heads), each adding exp(s_c - L) O_c to the rows'
+//     accumulators with LDS atomics. This compaction keeps MFMA columns
+//     filled even when adjacent queries choose different chunks.
 #include "hils_common.h"
 #include "hils_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace hils {
 
-constexpr int VPAD = 8;  // Vt row padding (elements)
+// ---------------------------------------------------------------- V^T copy
+// vt[bg][d][Np] (Np = N rounded up to 64, zero padded) with the tokens of
+// every 32-token group stored in the order 0-3,16-19, 4-7,20-23, 8-11,24-27,
+// 12-15,28-31, so that lane group g of an MFMA fragment finds its 8 tokens
+// {4g..4g+3, 16+4g..16+4g+3} contiguous at slots 8g..8g+7.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_vt_perm(const T* __restrict__ v, T* __restrict__ vt, int N,
+                                                 int Np) {
+  __shared__ T tile[64][DH + 1];
+  const int bg = blockIdx.y, t0 = blockIdx.x * 64;
+  const T* src = v + (size_t)bg * N * DH;
+  for (int x = threadIdx.x; x < 64 * DH; x += 256) {
+    const int t = x / DH, dd = x - t * DH;
+    tile[t][dd] = (t0 + t < N) ? src[(size_t)(t0 + t) * DH + dd] : from_f<T>(0.f);
+  }
+  __syncthreads();
+  T* dst = vt + (size_t)bg * DH * Np + t0;
+  for (int x = threadIdx.x; x < 64 * DH; x += 256) {
+    const int dd = x / 64, s = x - dd * 64;  // storage slot within the 64-token block
+    const int half = s >> 5, sl = s & 31;
+    const int g8 = sl >> 3, e = sl & 7;
+    const int t = 32 * half + (e < 4 ? 4 * g8 + e : 16 + 4 * g8 + (e - 4));
+    dst[(size_t)dd * Np + s] = tile[t][dd];
+  }
+}
 
-// In-place exclusive scan of a[0..n) by the whole block; returns the total.
+// In-place exclusive scan of a[0..n) by the whole block (256 threads); returns the total.
 __device__ int block_excl_scan(int* a, int n, int* wsum) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int seg = (n + 255) / 256;
@@ -62,97 +91,73 @@ __device__ int block_excl_scan(int* a, int n, int* wsum) {
   return total;
 }
 
-// Stage a 64-token block of V ([64][DH] rows starting at vsrc, row stride DH)
-// transposed into vt[DH][64 + VPAD]. One wave. Tokens >= nvalid read row 0.
-template <typename T, int DH>
-__device__ __forceinline__ void stage_vt(const T* __restrict__ vsrc, int nvalid, T* vt, int lane) {
-  const int tp = lane & 31, half = lane >> 5;
-  const int t0 = 2 * tp, t1 = 2 * tp + 1;
-  const T* r0 = vsrc + (size_t)(t0 < nvalid ? t0 : 0) * DH + half * (DH / 2);
-  const T* r1 = vsrc + (size_t)(t1 < nvalid ? t1 : 0) * DH + half * (DH / 2);
-  constexpr int VS = 64 + VPAD;
-#pragma unroll
-  for (int j = 0; j < DH / 2; j += 8) {
-    const auto a = ld8<T>(r0 + j);
-    const auto b = ld8<T>(r1 + j);
-    if constexpr (sizeof(T) == 2) {
-      const u16x8 ua = __builtin_bit_cast(u16x8, a), ub = __builtin_bit_cast(u16x8, b);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = half * (DH / 2) + j + e;
-        *reinterpret_cast<uint32_t*>(vt + dd * VS + t0) = (uint32_t)ua[e] | ((uint32_t)ub[e] << 16);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = half * (DH / 2) + j + e;
-        float2 pr;
-        pr.x = a[e];
-        pr.y = b[e];
-        *reinterpret_cast<float2*>(vt + dd * VS + t0) = pr;
-      }
-    }
-  }
-}
-
-// V^T fragment (A operand of O^T = V^T P^T): rows d = 16*mb + lane%16, the 8
-// tokens {4g..4g+3, 16+4g..16+4g+3} (+32*ks), g = lane/16.
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type ld_vt(const T* vt, int mb, int ks, int lane) {
-  constexpr int VS = 64 + VPAD;
-  const T* p = vt + (16 * mb + (lane & 15)) * VS + 32 * ks + 4 * (lane >> 4);
-  if constexpr (sizeof(T) == 2) {
-    const u16x4 a = *reinterpret_cast<const u16x4*>(p);
-    const u16x4 b = *reinterpret_cast<const u16x4*>(p + 16);
-    u16x8 u;
-    u[0] = a[0]; u[1] = a[1]; u[2] = a[2]; u[3] = a[3];
-    u[4] = b[0]; u[5] = b[1]; u[6] = b[2]; u[7] = b[3];
-    return __builtin_bit_cast(bf16x8, u);
-  } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
-    f32x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-    return r;
-  }
-}
-
-// P^T fragment (B operand) for token step ks from the S^T accumulators.
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::type p_frag(const f32x4& s0, const f32x4& s1) {
   float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
   return pack8<T>(x);
 }
 
+template <typename T, int DH>
+struct BlockFrags {
+  typename Frag<T>::type k[4][DH / 32];  // A operand of S^T: K rows (tokens)
+  typename Frag<T>::type v[DH / 16][2];  // A operand of O^T: V^T rows (dims)
+};
+
+// K rows kbase + 16*tb + lane%16 (clamped below nvalid) and the permuted V^T
+// columns vtbase + 32*ks + 8*(lane/16) of dims 16*mb + lane%16.
+template <typename T, int DH>
+__device__ __forceinline__ void load_block(BlockFrags<T, DH>& f, const T* __restrict__ kbase, int nvalid,
+                                           const T* __restrict__ vtbase, int Np, int lane) {
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    int tok = 16 * tb + (lane & 15);
+    tok = tok < nvalid ? tok : 0;
+    const T* src = kbase + (size_t)tok * DH + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) f.k[tb][ks] = ld8<T>(src + 32 * ks);
+  }
+#pragma unroll
+  for (int mb = 0; mb < DH / 16; ++mb) {
+    const T* src = vtbase + (size_t)(16 * mb + (lane & 15)) * Np + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) f.v[mb][ks] = ld8<T>(src + 32 * ks);
+  }
+}
+
+template <typename T, int DH>
+struct RowFrags {
+  typename Frag<T>::type q[DH / 32];
+  float s;     // fusion score of the row's chunk
+  int row;     // tile row
+  bool valid;
+};
+
 template <typename T, int G, int DH, int CB>
-__global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const T* __restrict__ k,
-                                                  const T* __restrict__ v,
-                                                  const int32_t* __restrict__ topk_idx,
-                                                  const float* __restrict__ topk_score,
-                                                  T* __restrict__ o, float* __restrict__ lse,
-                                                  int N, int Hkv, int K, int W, int S, float scale,
-                                                  int ntiles, int C) {
+__global__ __launch_bounds__(256) void k_attn_fwd(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score, T* __restrict__ o,
+    float* __restrict__ lse, int N, int Np, int Hkv, int K, int W, int S, float scale, int ntiles,
+    int C) {
   typedef typename Frag<T>::type FT;
   constexpr int R = 64 * CB;        // rows per tile
   constexpr int TP = R / G;         // positions per tile
-  constexpr int PPG = 16 / G;       // positions per chunk group
   constexpr int KS = DH / 32;
   constexpr int MB = DH / 16;
-  constexpr int AS = R + 4;         // accT row stride
-  constexpr int VS = 64 + VPAD;
+  constexpr int RS = DH + 4;        // accumulator row stride (floats)
   constexpr int EPT = TP * 32 / 256;  // max entries per thread (K <= 32)
+  constexpr bool PF = DH == 64;     // double-buffered prefetch (register budget)
 
   extern __shared__ __align__(16) unsigned char smem[];
-  float* accT = reinterpret_cast<float*>(smem);                 // [DH][AS]
-  float* Ls = accT + DH * AS;                                   // [R]
-  T* vtb = reinterpret_cast<T*>(Ls + R);                        // [4][DH][VS]
-  int* off = reinterpret_cast<int*>(vtb + 4 * DH * VS);         // [C] counts, then offsets
-  int* gb = off + C;                                            // [C] group counts, then bases
-  int* grp = gb + C;                                            // [2 * NGMAX]
-  const int NGMAX = min(TP * K, TP * K / PPG + C + 1);
-  uint16_t* ent = reinterpret_cast<uint16_t*>(grp + 2 * NGMAX);  // [TP*K]
+  // one accumulator copy per wave: waves add their chunk contributions to
+  // their own copy with plain read-modify-write (no LDS atomics), and the
+  // copies are summed when the tile is written out
+  float* accT = reinterpret_cast<float*>(smem);          // [4][R][RS]
+  float* Ls = accT + 4 * R * RS;                         // [R]
+  int* off = reinterpret_cast<int*>(Ls + R);             // [C + 1] counts -> offsets
+  int* nzl = off + C + 1;                                // [C] ranks -> nonempty chunk ids
+  uint16_t* ent = reinterpret_cast<uint16_t*>(nzl + C);  // [TP*K]
   __shared__ int wsum[4];
+  __shared__ int ctr;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int tile = ntiles - 1 - blockIdx.x;
@@ -163,11 +168,13 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
   const int plast = min(p0 + TP - 1, N - 1);
   const int ndmax = n_distant(plast, W, S);  // chunks any row of the tile can select
   const T* kg = k + (size_t)bg * N * DH;
-  const T* vg = v + (size_t)bg * N * DH;
-  T* vt = vtb + w * DH * VS;
+  const T* vtg = vt + (size_t)bg * DH * Np;
+  float* accW = accT + w * R * RS;  // this wave's accumulator copy
 
   // ------------------------------------------------ bucket selections by chunk
-  for (int x = tid; x < ndmax; x += 256) off[x] = 0;
+  for (int x = tid; x <= ndmax; x += 256) off[x] = 0;
+  if (tid == 0) ctr = 0;
+  for (int x = tid; x < R * RS; x += 256) reinterpret_cast<f32x4*>(accT)[x] = zero4();
   __syncthreads();
   int my_c[EPT], my_r[EPT];
   const int E = TP * K;
@@ -187,28 +194,32 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
     }
   }
   __syncthreads();
-  for (int x = tid; x < ndmax; x += 256) gb[x] = (off[x] + PPG - 1) / PPG;
+  for (int x = tid; x < ndmax; x += 256) nzl[x] = off[x] > 0 ? 1 : 0;
   __syncthreads();
   const int Etot = block_excl_scan(off, ndmax, wsum);
-  const int NG = block_excl_scan(gb, ndmax, wsum);
+  const int NZ = block_excl_scan(nzl, ndmax, wsum);
+  if (tid == 0) off[ndmax] = Etot;
+  __syncthreads();
+  // ranks -> list of nonempty chunk ids (a rank never exceeds its chunk id, so
+  // reading a block of ranks before writing keeps later ranks intact)
+  for (int base = 0; base < ndmax; base += 256) {
+    const int x = base + tid;
+    const int rk = (x < ndmax && off[x + 1] > off[x]) ? nzl[x] : -1;
+    __syncthreads();
+    if (rk >= 0) nzl[rk] = x;
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int c = my_c[j];
     if (c >= 0) {
       const int x = tid + 256 * j;
       const int pl = x / K, kk = x - pl * K;
-      const int r = my_r[j];
-      ent[off[c] + r] = (uint16_t)((pl << 6) | kk);
-      if (r % PPG == 0) {
-        const int gi = gb[c] + r / PPG;
-        const int n = (c + 1 < ndmax ? off[c + 1] : Etot) - off[c] - r;
-        grp[2 * gi] = c;
-        grp[2 * gi + 1] = ((off[c] + r) << 5) | (n < PPG ? n : PPG);
-      }
+      ent[off[c] + my_r[j]] = (uint16_t)((pl << 6) | kk);
     }
   }
 
-  // ------------------------------------------------ phase A: window
+  // ------------------------------------------------ window phase
   {
     const int rbase = w * 16 * CB;                 // first tile row of this wave
     const int pw_lo = p0 + rbase / G;
@@ -235,73 +246,101 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] = zero4();
     }
-    if (pw_lo < N) {
-      const int kv_lo = n_distant(pw_lo, W, S) * S;
-      for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 64) {
-        const int nvalid = min(64, N - kv0);
-        f32x4 sacc[4][CB];
+    // rows of this wave whose window does not cover a whole block need masks;
+    // a block strictly inside every row's window is processed without them
+    int minpos = 1 << 30, maxws = 0;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          int tok = 16 * tb + (lane & 15);
-          tok = tok < nvalid ? tok : 0;
-          const T* src = kg + (size_t)(kv0 + tok) * DH + 8 * (lane >> 4);
-          FT kf[KS];
+    for (int cb = 0; cb < CB; ++cb) {
+      minpos = min(minpos, prow[cb] >= 0 ? prow[cb] : -1);
+      maxws = max(maxws, wsr[cb]);
+    }
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kf[ks] = ld8<T>(src + 32 * ks);
+    for (int m2 = 1; m2 < 16; m2 <<= 1) {
+      minpos = min(minpos, __shfl_xor(minpos, m2, 64));
+      maxws = max(maxws, __shfl_xor(maxws, m2, 64));
+    }
+    const float sc2 = scale * LOG2E;  // logits in base 2
+    auto compute = [&](const BlockFrags<T, DH>& f, int kv0, auto masked) __attribute__((always_inline)) {
+      f32x4 sacc[4][CB];
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            sacc[tb][cb] = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sacc[tb][cb] = mma16(kf[ks], qf[cb][ks], sacc[tb][cb]);
-          }
-        }
-        wave_lds_sync();  // previous block's V^T reads are complete
-        stage_vt<T, DH>(vg + (size_t)kv0 * DH, nvalid, vt, lane);
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          float bmax = NEG_INF;
+          sacc[tb][cb] = zero4();
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb)
+          for (int ks = 0; ks < KS; ++ks) sacc[tb][cb] = mma16(f.k[tb][ks], qf[cb][ks], sacc[tb][cb]);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+      for (int cb = 0; cb < CB; ++cb) {
+        float bmax = NEG_INF;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sacc[tb][cb][i] * sc2;
+            if constexpr (decltype(masked)::value) {
               const int j = kv0 + 16 * tb + 4 * (lane >> 4) + i;
-              const bool ok = prow[cb] >= 0 && j <= prow[cb] && j >= wsr[cb];
-              const float x = ok ? sacc[tb][cb][i] * scale : NEG_INF;
-              sacc[tb][cb][i] = x;
-              bmax = fmaxf(bmax, x);
+              x = (j <= prow[cb] && j >= wsr[cb]) ? x : NEG_INF;
             }
-          bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-          bmax = fmaxf(bmax, shfl_xor(bmax, 32));
-          const float mnew = fmaxf(m[cb], bmax);
-          const float alpha = (m[cb] == NEG_INF) ? 0.f : __expf(m[cb] - mnew);
-          float ps = 0.f;
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float x = sacc[tb][cb][i];
-              const float pv = (x == NEG_INF) ? 0.f : __expf(x - mnew);
-              sacc[tb][cb][i] = pv;
-              ps += pv;
-            }
-          lsum[cb] = lsum[cb] * alpha + ps;
-          m[cb] = mnew;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
-        }
-        wave_lds_sync();  // V^T staged
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          FT pf[CB];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) pf[cb] = p_frag<T>(sacc[2 * ks][cb], sacc[2 * ks + 1][cb]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const FT vf = ld_vt<T>(vt, mb, ks, lane);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) oacc[mb][cb] = mma16(vf, pf[cb], oacc[mb][cb]);
+            sacc[tb][cb][i] = x;
+            bmax = fmaxf(bmax, x);
           }
-        }
+        bmax = fmaxf(bmax, shfl_xor(bmax, 16));
+        bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+        const float mnew = fmaxf(m[cb], bmax);
+        const float mref = mnew == NEG_INF ? 0.f : mnew;
+        const float alpha = fast_exp2(m[cb] - mref);
+        float ps = 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = fast_exp2(sacc[tb][cb][i] - mref);
+            sacc[tb][cb][i] = pv;
+            ps += pv;
+          }
+        lsum[cb] = lsum[cb] * alpha + ps;
+        m[cb] = mnew;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        FT pf[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) pf[cb] = p_frag<T>(sacc[2 * ks][cb], sacc[2 * ks + 1][cb]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) oacc[mb][cb] = mma16(f.v[mb][ks], pf[cb], oacc[mb][cb]);
+      }
+    };
+    auto run = [&](const BlockFrags<T, DH>& f, int kv0) __attribute__((always_inline)) {
+      const bool clean = minpos >= 0 && kv0 >= maxws && kv0 + 63 <= minpos;
+      if (clean)
+        compute(f, kv0, std::false_type());
+      else
+        compute(f, kv0, std::true_type());
+    };
+    if (pw_lo < N && !PF) {
+      const int kv_lo = n_distant(pw_lo, W, S) * S;
+      BlockFrags<T, DH> fa;
+      for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 64) {
+        load_block<T, DH>(fa, kg + (size_t)kv0 * DH, min(64, N - kv0), vtg + kv0, Np, lane);
+        run(fa, kv0);
+      }
+    } else if (pw_lo < N) {
+      const int kv_lo = n_distant(pw_lo, W, S) * S;
+      BlockFrags<T, DH> fa, fb;
+      load_block<T, DH>(fa, kg + (size_t)kv_lo * DH, min(64, N - kv_lo), vtg + kv_lo, Np, lane);
+      for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 128) {
+        const int k1 = kv0 + 64;
+        if (k1 <= pw_hi) load_block<T, DH>(fb, kg + (size_t)k1 * DH, min(64, N - k1), vtg + k1, Np, lane);
+        run(fa, kv0);
+        if (k1 > pw_hi) break;
+        const int k2 = kv0 + 128;
+        if (k2 <= pw_hi) load_block<T, DH>(fa, kg + (size_t)k2 * DH, min(64, N - k2), vtg + k2, Np, lane);
+        run(fb, k1);
       }
     }
     // window log-sum-exp, fusion normaliser, window contribution
@@ -311,127 +350,182 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const T* __restrict__ q, const
       ls += shfl_xor(ls, 16);
       ls += shfl_xor(ls, 32);
       const int r = rbase + 16 * cb + (lane & 15);
-      float L = 0.f, coef = 0.f;
-      if (prow[cb] >= 0) {
-        const float lW = m[cb] + __logf(ls);
-        const int hh = r % G;
-        const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + prow[cb];
-        const int32_t* ti = topk_idx + ((size_t)bg * N + prow[cb]) * K;
-        const float* ts = topk_score + rowoff * K;
-        float mx = lW;
-        for (int kk = 0; kk < K; ++kk)
-          if (ti[kk] >= 0) mx = fmaxf(mx, ts[kk]);
-        float tot = __expf(lW - mx);
-        for (int kk = 0; kk < K; ++kk)
-          if (ti[kk] >= 0) tot += __expf(ts[kk] - mx);
-        L = mx + __logf(tot);
-        coef = __expf(m[cb] - L);
-        if ((lane >> 4) == 0) lse[rowoff] = L;
+      const int hh = r % G;
+      const int pc = prow[cb] >= 0 ? prow[cb] : N - 1;
+      const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + pc;
+      const int32_t* ti = topk_idx + ((size_t)bg * N + pc) * K;
+      const float* ts = topk_score + rowoff * K;
+      const float lW = (m[cb] + __log2f(ls)) * LN2;  // natural log-sum-exp of the window
+      // the four lanes holding this row each reduce a quarter of its slots
+      float mx = lW;
+      for (int kk = lane >> 4; kk < K; kk += 4)
+        if (ti[kk] >= 0) mx = fmaxf(mx, ts[kk]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      float tot = 0.f;
+      for (int kk = lane >> 4; kk < K; kk += 4)
+        if (ti[kk] >= 0) tot += __expf(ts[kk] - mx);
+      tot += shfl_xor(tot, 16);
+      tot += shfl_xor(tot, 32);
+      tot += __expf(lW - mx);
+      const bool live = prow[cb] >= 0;
+      const float L = live ? mx + __logf(tot) : 0.f;
+      const float coef = live ? fast_exp2(m[cb] - L * LOG2E) : 0.f;
+      if ((lane >> 4) == 0) {
+        Ls[r] = L;
+        if (live) lse[rowoff] = L;
       }
-      if ((lane >> 4) == 0) Ls[r] = L;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accT[(16 * mb + 4 * (lane >> 4) + i) * AS + r] = oacc[mb][cb][i] * coef;
+        *reinterpret_cast<f32x4*>(accW + r * RS + 16 * mb + 4 * (lane >> 4)) = oacc[mb][cb] * coef;
     }
   }
   __syncthreads();
 
-  // ------------------------------------------------ phase B: selected chunks
-  for (int gi = w; gi < NG; gi += 4) {
-    const int c = grp[2 * gi];
-    const int gdesc = grp[2 * gi + 1];
-    const int st = gdesc >> 5, n = gdesc & 31;
-    const int col = lane & 15;
-    const int ei = col / G, hh = col % G;
-    const bool valid = ei < n;
-    const int en = ent[st + (valid ? ei : 0)];
-    const int pl = en >> 6, kk = en & 63;
-    const int pos = p0 + pl;
-    const int row = pl * G + hh;
-    const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + pos;
-    FT qf[KS];
-    {
+  // ------------------------------------------------ chunk phase
+  {
+    auto grab = [&]() __attribute__((always_inline)) {
+      int it = 0;
+      if (lane == 0) it = atomicAdd(&ctr, 1);
+      return __shfl(it, 0, 64);
+    };
+    // row fragments of row block cbk of a chunk whose entries are e0 .. e0 + n
+    auto load_rows = [&](RowFrags<T, DH>& rf, int e0, int n, int cbk) __attribute__((always_inline)) {
+      const int rr = 16 * cbk + (lane & 15);
+      rf.valid = rr < n * G;
+      const int ei = (rf.valid ? rr : 0) / G, hh = (rf.valid ? rr : 0) % G;
+      const int en = ent[e0 + ei];
+      const int pl = en >> 6, kk = en & 63;
+      rf.row = pl * G + hh;
+      const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + p0 + pl;
       const T* src = q + rowoff * DH + 8 * (lane >> 4);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = ld8<T>(src + 32 * ks);
-    }
-    const T* kc = kg + (size_t)c * 64 * DH;
-    f32x4 sacc[4];
+      for (int ks = 0; ks < KS; ++ks) rf.q[ks] = ld8<T>(src + 32 * ks);
+      rf.s = topk_score[rowoff * K + kk];
+    };
+    auto process_rows = [&](const BlockFrags<T, DH>& f, const RowFrags<T, DH>& rf) __attribute__((always_inline)) {
+      f32x4 sacc[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const T* src = kc + (size_t)(16 * tb + (lane & 15)) * DH + 8 * (lane >> 4);
-      sacc[tb] = zero4();
+      for (int tb = 0; tb < 4; ++tb) {
+        sacc[tb] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(ld8<T>(src + 32 * ks), qf[ks], sacc[tb]);
-    }
-    wave_lds_sync();
-    stage_vt<T, DH>(vg + (size_t)c * 64 * DH, 64, vt, lane);
-    float mx = NEG_INF;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sacc[tb][i] *= scale;
-        mx = fmaxf(mx, sacc[tb][i]);
+        for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(f.k[tb][ks], rf.q[ks], sacc[tb]);
       }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    float ps = 0.f;
+      const float sc2 = scale * LOG2E;
+      float mx = NEG_INF;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __expf(sacc[tb][i] - mx);
-        sacc[tb][i] = pv;
-        ps += pv;
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tb][i]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float mref = mx * sc2;
+      float ps = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = fast_exp2(fmaf(sacc[tb][i], sc2, -mref));
+          sacc[tb][i] = pv;
+          ps += pv;
+        }
+      ps += shfl_xor(ps, 16);
+      ps += shfl_xor(ps, 32);
+      f32x4 oc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oc[mb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const FT pf = p_frag<T>(sacc[2 * ks], sacc[2 * ks + 1]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oc[mb] = mma16(f.v[mb][ks], pf, oc[mb]);
       }
-    ps += shfl_xor(ps, 16);
-    ps += shfl_xor(ps, 32);
-    wave_lds_sync();
-    f32x4 oc[MB];
+      if (rf.valid) {
+        const float alpha = fast_exp2((rf.s - Ls[rf.row]) * LOG2E) / ps;
+        float* dst = accW + rf.row * RS + 4 * (lane >> 4);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) oc[mb] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const FT pf = p_frag<T>(sacc[2 * ks], sacc[2 * ks + 1]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oc[mb] = mma16(ld_vt<T>(vt, mb, ks, lane), pf, oc[mb]);
+        for (int mb = 0; mb < MB; ++mb) {
+          f32x4 cur = *reinterpret_cast<const f32x4*>(dst + 16 * mb);
+          cur += alpha * oc[mb];
+          *reinterpret_cast<f32x4*>(dst + 16 * mb) = cur;
+        }
+      }
+    };
+    auto process_chunk = [&](const BlockFrags<T, DH>& f, RowFrags<T, DH>& r0, int c) __attribute__((always_inline)) {
+      const int e0 = off[c], n = off[c + 1] - e0;
+      const int nb = (n * G + 15) / 16;
+      RowFrags<T, DH> r1;
+      for (int cbk = 0; cbk < nb; cbk += 2) {
+        if (cbk + 1 < nb) load_rows(r1, e0, n, cbk + 1);
+        process_rows(f, r0);
+        if (cbk + 1 >= nb) break;
+        if (cbk + 2 < nb) load_rows(r0, e0, n, cbk + 2);
+        process_rows(f, r1);
+      }
+    };
+    auto load_chunk = [&](BlockFrags<T, DH>& f, RowFrags<T, DH>& r0, int c) __attribute__((always_inline)) {
+      load_block<T, DH>(f, kg + (size_t)c * 64 * DH, 64, vtg + (size_t)c * 64, Np, lane);
+      load_rows(r0, off[c], off[c + 1] - off[c], 0);
+    };
+    if constexpr (!PF) {
+      BlockFrags<T, DH> fa;
+      RowFrags<T, DH> ra;
+      for (int a = grab(); a < NZ; a = grab()) {
+        load_chunk(fa, ra, nzl[a]);
+        process_chunk(fa, ra, nzl[a]);
+      }
+    } else {
+    BlockFrags<T, DH> fa, fb;
+    RowFrags<T, DH> ra, rb;
+    int a = grab();
+    if (a < NZ) load_chunk(fa, ra, nzl[a]);
+    while (a < NZ) {
+      const int bb = grab();
+      if (bb < NZ) load_chunk(fb, rb, nzl[bb]);
+      process_chunk(fa, ra, nzl[a]);
+      if (bb >= NZ) break;
+      a = grab();
+      if (a < NZ) load_chunk(fa, ra, nzl[a]);
+      process_chunk(fb, rb, nzl[bb]);
     }
-    if (valid) {
-      const float s = topk_score[rowoff * K + kk];
-      const float alpha = __expf(s - Ls[row]) / ps;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          atomicAdd(&accT[(16 * mb + 4 * (lane >> 4) + i) * AS + row], alpha * oc[mb][i]);
     }
   }
   __syncthreads();
 
   // ------------------------------------------------ write o
-  for (int x = tid; x < R * DH; x += 256) {
-    const int dd = x % DH, r = x / DH;
+  for (int x = tid; x < R * DH / 4; x += 256) {
+    const int r = x / (DH / 4), d4 = 4 * (x - r * (DH / 4));
     const int pos = p0 + r / G, hh = r % G;
-    if (pos < N) o[(((size_t)b * Hq + g * G + hh) * N + pos) * DH + dd] = from_f<T>(accT[dd * AS + r]);
+    const int a0 = r * RS + d4;
+    const f32x4 sum = *reinterpret_cast<const f32x4*>(accT + a0) +
+                      *reinterpret_cast<const f32x4*>(accT + R * RS + a0) +
+                      *reinterpret_cast<const f32x4*>(accT + 2 * R * RS + a0) +
+                      *reinterpret_cast<const f32x4*>(accT + 3 * R * RS + a0);
+    if (pos < N) {
+      T* dst = o + (((size_t)b * Hq + g * G + hh) * N + pos) * DH + d4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j] = from_f<T>(sum[j]);
+    }
   }
 }
 
 template <typename T, int G, int DH, int CB>
 static size_t fwd_lds(const Dims& p) {
-  constexpr int R = 64 * CB, TP = R / G, PPG = 16 / G;
-  const int ngmax = std::min(TP * p.K, TP * p.K / PPG + p.C + 1);
-  size_t s = sizeof(float) * ((size_t)DH * (R + 4) + R);
-  s += sizeof(T) * 4 * DH * (64 + VPAD);
-  s += sizeof(int) * (2 * (size_t)p.C + 2 * (size_t)ngmax);
+  constexpr int R = 64 * CB, TP = R / G;
+  size_t s = sizeof(float) * (4 * (size_t)R * (DH + 4) + R);
+  s += sizeof(int) * (2 * (size_t)p.C + 1);
   s += sizeof(uint16_t) * (size_t)TP * p.K;
   return (s + 15) & ~(size_t)15;
 }
 
-template <typename T, int G, int DH, int CB>
-static hipError_t fwd_go(const Dims& p, const void* q, const void* k, const void* v,
+// row blocks per wave in the window phase
+template <typename T, int DH> struct FwdCB { static constexpr int v = 1; };
+template <> struct FwdCB<uint16_t, 64> { static constexpr int v = 2; };
+
+template <typename T, int G, int DH>
+static hipError_t fwd_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                          const int32_t* idx, const float* sc, void* o, float* lse, hipStream_t st) {
+  constexpr int CB = FwdCB<T, DH>::v;
   constexpr int TP = 64 * CB / G;
   const int ntiles = (p.N + TP - 1) / TP;
   const size_t lds = fwd_lds<T, G, DH, CB>(p);
@@ -439,52 +533,64 @@ static hipError_t fwd_go(const Dims& p, const void* q, const void* k, const void
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const T*)q, (const T*)k,
-                     (const T*)v, idx, sc, (T*)o, lse, p.N, p.Hkv, p.K, p.W, p.S, p.scale, ntiles,
-                     p.C);
+                     (const T*)vt, idx, sc, (T*)o, lse, p.N, Np, p.Hkv, p.K, p.W, p.S, p.scale,
+                     ntiles, p.C);
   return hipGetLastError();
 }
 
-template <typename T, int G>
-static hipError_t fwd_d(const Dims& p, const void* q, const void* k, const void* v, const int32_t* idx,
-                        const float* sc, void* o, float* lse, hipStream_t st) {
-  constexpr int CB = sizeof(T) == 2 ? 2 : 1;
-  if (p.d == 64) return fwd_go<T, G, 64, CB>(p, q, k, v, idx, sc, o, lse, st);
-  return fwd_go<T, G, 128, CB>(p, q, k, v, idx, sc, o, lse, st);
+template <typename T, int DH>
+static hipError_t vt_go(const Dims& p, const void* v, void* vt, int Np, hipStream_t st) {
+  hipLaunchKernelGGL((k_vt_perm<T, DH>), dim3(Np / 64, p.B * p.Hkv), dim3(256), 0, st, (const T*)v,
+                     (T*)vt, p.N, Np);
+  return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t fwd_g(const Dims& p, const void* q, const void* k, const void* v, const int32_t* idx,
-                        const float* sc, void* o, float* lse, hipStream_t st) {
-  switch (p.G) {
-    case 1: return fwd_d<T, 1>(p, q, k, v, idx, sc, o, lse, st);
-    case 2: return fwd_d<T, 2>(p, q, k, v, idx, sc, o, lse, st);
-    case 4: return fwd_d<T, 4>(p, q, k, v, idx, sc, o, lse, st);
+static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void* v, void* vt,
+                        const int32_t* idx, const float* sc, void* o, float* lse, hipStream_t st) {
+  const int Np = (p.N + 63) / 64 * 64;
+  hipError_t err = p.d == 64 ? vt_go<T, 64>(p, v, vt, Np, st) : vt_go<T, 128>(p, v, vt, Np, st);
+  if (err != hipSuccess) return err;
+  switch (p.G * 1000 + p.d) {
+    case 1064: return fwd_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, o, lse, st);
+    case 1128: return fwd_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, o, lse, st);
+    case 2064: return fwd_go<T, 2, 64>(p, q, k, vt, Np, idx, sc, o, lse, st);
+    case 2128: return fwd_go<T, 2, 128>(p, q, k, vt, Np, idx, sc, o, lse, st);
+    case 4064: return fwd_go<T, 4, 64>(p, q, k, vt, Np, idx, sc, o, lse, st);
+    case 4128: return fwd_go<T, 4, 128>(p, q, k, vt, Np, idx, sc, o, lse, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, int CB>
-static size_t lds_by_g(const Dims& p) {
-  switch (p.G) {
-    case 1: return p.d == 64 ? fwd_lds<T, 1, 64, CB>(p) : fwd_lds<T, 1, 128, CB>(p);
-    case 2: return p.d == 64 ? fwd_lds<T, 2, 64, CB>(p) : fwd_lds<T, 2, 128, CB>(p);
-    case 4: return p.d == 64 ? fwd_lds<T, 4, 64, CB>(p) : fwd_lds<T, 4, 128, CB>(p);
+template <typename T>
+static size_t lds_t(const Dims& p) {
+  constexpr int C64 = FwdCB<T, 64>::v, C128 = FwdCB<T, 128>::v;
+  switch (p.G * 1000 + p.d) {
+    case 1064: return fwd_lds<T, 1, 64, C64>(p);
+    case 1128: return fwd_lds<T, 1, 128, C128>(p);
+    case 2064: return fwd_lds<T, 2, 64, C64>(p);
+    case 2128: return fwd_lds<T, 2, 128, C128>(p);
+    case 4064: return fwd_lds<T, 4, 64, C64>(p);
+    case 4128: return fwd_lds<T, 4, 128, C128>(p);
     default: return (size_t)-1;
   }
 }
 
 size_t attn_fwd_lds_bytes(const Dims& p) {
-  // dynamic LDS plus the kernel's static scan scratch
   const size_t stat = 64;
-  if (p.dtype == 1) return lds_by_g<uint16_t, 2>(p) + stat;
-  return lds_by_g<float, 1>(p) + stat;
+  return (p.dtype == 1 ? lds_t<uint16_t>(p) : lds_t<float>(p)) + stat;
 }
 
-hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v,
+size_t attn_fwd_vt_bytes(const Dims& p) {
+  const size_t el = p.dtype == 1 ? 2 : 4;
+  return (size_t)p.B * p.Hkv * p.d * ((p.N + 63) / 64 * 64) * el;
+}
+
+hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v, void* vt,
                            const int32_t* topk_idx, const float* topk_score, void* o, float* lse,
                            hipStream_t st) {
-  if (p.dtype == 1) return fwd_g<uint16_t>(p, q, k, v, topk_idx, topk_score, o, lse, st);
-  return fwd_g<float>(p, q, k, v, topk_idx, topk_score, o, lse, st);
+  if (p.dtype == 1) return fwd_t<uint16_t>(p, q, k, v, vt, topk_idx, topk_score, o, lse, st);
+  return fwd_t<float>(p, q, k, v, vt, topk_idx, topk_score, o, lse, st);
 }
 
 }  // namespace hils

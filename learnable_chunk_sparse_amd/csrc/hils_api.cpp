@@ -87,12 +87,14 @@ Dims dims_of(const hils_problem* p) {
 struct FwdWs {
   float* qhat;
   float* s_T;
+  void* vt;
 };
 size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
   Carver c(ws);
   const size_t rows = (size_t)d.B * d.Hq * d.N;
   out->qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
   out->s_T = (float*)c.take(rows * d.K * sizeof(float));
+  out->vt = c.take(hils::attn_fwd_vt_bytes(d));
   return c.used;
 }
 size_t carve_route(const Dims& d, void* ws, float** qhat) {
@@ -238,7 +240,7 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
     s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, w.s_T, st); }));
   }
   if (s != HILS_OK) return s;
-  return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, topk_idx, w.s_T, o, lse, st); }));
+  return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, o, lse, st); }));
 }
 
 hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,

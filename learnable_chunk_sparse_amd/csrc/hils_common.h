@@ -25,12 +25,13 @@ constexpr float NEG_INF = -__builtin_inff();
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// round to nearest even (inputs are finite)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// 2^x with one v_exp_f32 (exp2(-inf) = 0)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 template <typename T> __device__ __forceinline__ float to_f(T x);
 template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
@@ -71,10 +72,10 @@ __device__ __forceinline__ f32x4 mma16(const f32x8& a, const f32x8& b, f32x4 c) 
 // 8 floats -> fragment of T
 template <typename T> __device__ __forceinline__ typename Frag<T>::type pack8(const float* x);
 template <> __device__ __forceinline__ bf16x8 pack8<uint16_t>(const float* x) {
-  u16x8 u;
+  bf16x8 r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = f2bf(x[j]);
-  return __builtin_bit_cast(bf16x8, u);
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
+  return r;
 }
 template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
   f32x8 r;

@@ -28,10 +28,12 @@ hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void
                         int32_t* topk_idx, float* topk_score, hipStream_t st);
 
 // Fused window attention + selected-chunk attention + fusion.
-hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v,
+// vt: workspace for the transposed, token-permuted copy of V (attn_fwd_vt_bytes).
+hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v, void* vt,
                            const int32_t* topk_idx, const float* topk_score, void* o, float* lse,
                            hipStream_t st);
 size_t attn_fwd_lds_bytes(const Dims& p);
+size_t attn_fwd_vt_bytes(const Dims& p);
 
 // Decode.
 size_t decode_workspace(const Dims& p);

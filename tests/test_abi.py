@@ -52,11 +52,15 @@ def test_workspace_sizes():
     (dict(Hq=6, Hkv=4), 1), (dict(B=0), 1), (dict(K=0), 1), (dict(Nq=100, Nk=200), 1),
     (dict(d=96), 2), (dict(S=32), 2), (dict(dtype=7), 2), (dict(qcal_shared=1), 2),
     (dict(r=8), 2), (dict(Hq=16, Hkv=1), 2), (dict(scale=-1.0), 1),
-    (dict(dtype=0, d=128), 2),
 ])
 def test_validation_codes(kw, code):
     st, _ = ws(prob(**kw), L.OP_FWD)
     assert st == code, (kw, st)
+
+
+def test_fp32_d128_backward_is_unsupported():
+    st, _ = ws(prob(dtype=0, d=128), L.OP_BWD)
+    assert st == 2
 
 
 def test_calls_reject_before_launch():

@@ -31,6 +31,7 @@ SMALL = [
     ("gqa4_d64_r64", "bf16", 1, 4, 1, 64, 777, 3, 64, 64, 64, 2.0),
     ("fp32_d64", "fp32", 1, 2, 1, 64, 700, 4, 128, 0, 0, 4.0),
     ("fp32_d64_qcal_gqa2", "fp32", 1, 4, 2, 64, 520, 3, 64, 64, 32, 1.0),
+    ("fp32_d128_gqa4", "fp32", 1, 8, 2, 128, 450, 3, 64, 0, 0, 2.0),
 ]
 
 

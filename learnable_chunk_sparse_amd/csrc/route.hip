@@ -8,19 +8,68 @@
 //   sel_c(i)   = max_{h in group} s_{h,c}(i)
 //   T(i)       = the K best c by (sel desc, c asc)
 //
-// Workgroup = 4 waves = 64 consecutive positions of one (batch, KV head);
-// wave w owns 16 positions x G heads. Scores come from 16x16x32 bf16 MFMAs:
-// the fp32 q_hat is split into hi + lo bf16 parts (two products with fp32
-// accumulation, landmark keys are exact bf16), which keeps each score within
-// ~1e-6 of its fp64 value. Chunks are scanned in ascending order, 16 per step;
-// candidates that beat a position's current K-th score are staged in LDS and
-// inserted by the lane owning that position, so ties keep the lower index.
+// Workgroup = 4 waves of 16 * RB consecutive positions of one (batch, KV head)
+// (RB = 4 / G row groups, so that a wave's MFMA rows are 64 (position, head)
+// pairs for G <= 4). Landmark keys stream
+// through LDS in tiles of 64 chunks shared by the four waves (the next tile
+// is prefetched into registers while the current one is scored). Scores come
+// from 16x16x32 bf16 MFMAs: the fp32 q_hat is split into hi + lo bf16 parts
+// (two products with fp32 accumulation; landmark keys are exact bf16), which
+// keeps each score within ~1e-6 of its fp64 value.
+// Selection: the max-over-heads score tile of each 16-chunk step is turned
+// around through LDS so that one lane holds one position's 16 candidates, and
+// each lane keeps its own running top-K in registers (see TopK below).
 #include "hils_common.h"
 #include "hils_internal.h"
 
 namespace hils {
 
-template <typename T, typename QT, int G, int DH>
+namespace {
+constexpr int RT_TC = 64;   // chunks per LDS tile
+constexpr int RT_PAD = 8;   // kL tile row padding (elements)
+
+}  // namespace
+
+// One lane per position keeps that position's running top-KC (KC >= K) in
+// registers, sorted by (score desc, chunk asc). A candidate that beats the
+// K-th entry is bubbled in by a fixed compare-exchange chain (no divergence
+// inside the chain); the wave skips the chain when no lane's candidate
+// qualifies.
+template <int KC>
+struct TopK {
+  float s[KC];
+  int c[KC];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      s[k] = NEG_INF;
+      c[k] = -1;
+    }
+  }
+  __device__ __forceinline__ float kth(int K) const {
+    if (K == KC) return s[KC - 1];
+    float t = NEG_INF;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) t = (k == K - 1) ? s[k] : t;
+    return t;
+  }
+  // insert (v, ci) when it beats the current entries; equal scores keep the
+  // earlier (lower) chunk since chunks arrive in ascending order
+  __device__ __forceinline__ void insert(float v, int ci) {
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const bool sw = v > s[k];
+      const float ts = s[k];
+      const int tc = c[k];
+      s[k] = sw ? v : ts;
+      c[k] = sw ? ci : tc;
+      v = sw ? ts : v;
+      ci = sw ? tc : ci;
+    }
+  }
+};
+
+template <typename T, typename QT, int G, int DH, int KC>
 __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                const T* __restrict__ e, int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_score, int N, int C, int Hkv,
@@ -28,202 +77,239 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
   typedef typename Frag<T>::type FT;
   constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
   constexpr int KS = DH / 32;
-  extern __shared__ float lds[];
-  const int KP = K + 1;
-  float* lst_s = lds;                            // [64][KP]
-  int* lst_i = (int*)(lst_s + 64 * KP);          // [64][KP]
-  float* lst_h = (float*)(lst_i + 64 * KP);      // [64][KP][G]
-  float* thr_s = lst_h + 64 * KP * G;            // [64]
-  int* cnt_s = (int*)(thr_s + 64);               // [64]
-  float* st = (float*)(cnt_s + 64);              // [4][16][17]
-  float* st_h = st + 4 * 16 * 17;                // [4][G][16][17]
+  constexpr int KP = DH + RT_PAD;
+  constexpr int RB = G >= 4 ? 1 : 4 / G;   // 16-position row groups per wave
+  constexpr int PW = 16 * RB;              // positions per wave
+  constexpr int PWG = 4 * PW;              // positions per workgroup
+  constexpr int TILE_ELEMS = RT_TC * DH;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NV = TILE_ELEMS / 256 / VEC;
+  __shared__ __align__(16) T kl_s[RT_TC * KP];
+  __shared__ float e_s[RT_TC];
+  __shared__ __align__(16) float sc_s[4][PW][16 + 4];  // per-wave score tile (positions x chunks)
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int grp = lane >> 4, col = lane & 15;
   const int tile = ntiles - 1 - blockIdx.x;      // heavy (late) tiles first
-  const int bg = blockIdx.y;                      // b * Hkv + g
+  const int bg = blockIdx.y;                     // b * Hkv + g
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
-  const int p0 = tile * 64;
+  const int pw0 = tile * PWG + w * PW;           // first position of this wave
 
-  if (threadIdx.x < 64) {
-    thr_s[threadIdx.x] = NEG_INF;
-    cnt_s[threadIdx.x] = 0;
-  }
-
-  // A fragments: rows = 16 positions of this wave, one block per head
-  FT ahi[G][KS];
-  FT alo[G][HAS_LO ? KS : 1];
-  {
-    int pos = p0 + 16 * w + (lane & 15);
+  // A fragments: row block rb = 16 positions (pw0 + 16 rb + lane%16), per head
+  FT ahi[RB][G][KS];
+  FT alo[RB][G][HAS_LO ? KS : 1];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int pos = pw0 + 16 * rb + col;
     pos = pos < N ? pos : N - 1;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const QT* src = qs + (((size_t)b * Hq + g * G + hh) * N + pos) * DH + 8 * (lane >> 4);
+      const QT* src = qs + (((size_t)b * Hq + g * G + hh) * N + pos) * DH + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = to_f<QT>(src[32 * ks + j]);
-        ahi[hh][ks] = pack8<T>(x);
+        ahi[rb][hh][ks] = pack8<T>(x);
         if constexpr (HAS_LO) {
-          const u16x8 hb = __builtin_bit_cast(u16x8, ahi[hh][ks]);
+          const u16x8 hb = __builtin_bit_cast(u16x8, ahi[rb][hh][ks]);
           float y[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) y[j] = x[j] - bf2f(hb[j]);
-          alo[hh][ks] = pack8<T>(y);
+          alo[rb][hh][ks] = pack8<T>(y);
         }
       }
     }
   }
-  __syncthreads();
-
-  const int plast = min(p0 + 16 * w + 15, N - 1);
-  const int nd_w = (p0 + 16 * w < N) ? n_distant(plast, W, S) : 0;
-  int nd_i[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = p0 + 16 * w + 4 * (lane >> 4) + i;
-    nd_i[i] = pos < N ? n_distant(pos, W, S) : 0;
-  }
+  // selection state: lane p < PW owns position pw0 + p
+  const int mypos = pw0 + lane;
+  const int mynd = (lane < PW && mypos < N) ? n_distant(mypos, W, S) : 0;
+  TopK<KC> top;
+  top.init();
+  float thr = NEG_INF;
+  const int nd_w = (pw0 < N) ? n_distant(min(pw0 + PW - 1, N - 1), W, S) : 0;
+  const int nd_wg = n_distant(min(tile * PWG + PWG - 1, N - 1), W, S);
   const T* kLg = kL + (size_t)bg * C * DH;
   const T* eg = e + (size_t)bg * C;
-  float* stw = st + w * 16 * 17;
-  float* sthw = st_h + w * G * 16 * 17;
 
-  for (int c0 = 0; c0 < nd_w; c0 += 16) {
-    const int c = c0 + (lane & 15);
-    const int cl = c < nd_w ? c : nd_w - 1;
-    FT bf[KS];
+  typedef typename Frag<T>::type VT;
+  VT pre[NV > 0 ? NV : 1];
+  float pre_e = 0.f;
+  auto fetch = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bf[ks] = ld8<T>(kLg + (size_t)cl * DH + 8 * (lane >> 4) + 32 * ks);
-    const float ev = to_f<T>(eg[cl]);
-    f32x4 acc[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      acc[hh] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        acc[hh] = mma16(ahi[hh][ks], bf[ks], acc[hh]);
-        if constexpr (HAS_LO) acc[hh] = mma16(alo[hh][ks], bf[ks], acc[hh]);
+    for (int v = 0; v < NV; ++v) {
+      const int el = (tid * NV + v) * VEC;
+      const int row = el / DH, cc = el - row * DH;
+      const int c = min(t0 + row, C - 1);
+      if constexpr (sizeof(T) == 2) {
+        pre[v] = *reinterpret_cast<const VT*>(kLg + (size_t)c * DH + cc);
+      } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(kLg + (size_t)c * DH + cc);
+        VT r;
+        r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+        pre[v] = r;
       }
     }
-    float sel[4];
-    bool pass = false;
+    if (tid < RT_TC) pre_e = to_f<T>(eg[min(t0 + tid, C - 1)]);
+  };
+  auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float best = NEG_INF;
+    for (int v = 0; v < NV; ++v) {
+      const int el = (tid * NV + v) * VEC;
+      const int row = el / DH, cc = el - row * DH;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<VT*>(kl_s + row * KP + cc) = pre[v];
+      } else {
+        f32x4 a;
+        a[0] = pre[v][0]; a[1] = pre[v][1]; a[2] = pre[v][2]; a[3] = pre[v][3];
+        *reinterpret_cast<f32x4*>(kl_s + row * KP + cc) = a;
+      }
+    }
+    if (tid < RT_TC) e_s[tid] = pre_e;
+  };
+
+  if (nd_wg > 0) fetch(0);
+  for (int t0 = 0; t0 < nd_wg; t0 += RT_TC) {
+    __syncthreads();  // previous tile fully consumed
+    store();
+    __syncthreads();
+    if (t0 + RT_TC < nd_wg) fetch(t0 + RT_TC);
+    const int c_end = min(t0 + RT_TC, nd_w);
+    for (int c0 = t0; c0 < c_end; c0 += 16) {
+      FT bf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bf[ks] = *reinterpret_cast<const FT*>(kl_s + (c0 + col - t0) * KP + 8 * grp + 32 * ks);
+      const float ev = e_s[c0 + col - t0];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f32x4 best;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            acc = mma16(ahi[rb][hh][ks], bf[ks], acc);
+            if constexpr (HAS_LO) acc = mma16(alo[rb][hh][ks], bf[ks], acc);
+          }
+          if (hh == 0)
+            best = acc;
+          else
+#pragma unroll
+            for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], acc[i]);
+        }
+        // D layout: position 16 rb + 4 grp + i, chunk c0 + col
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc_s[w][16 * rb + 4 * grp + i][col] = fmaf(best[i], scale, ev);
+      }
+      wave_lds_sync();
+      if (lane < PW) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
+          v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = (c0 + j < mynd) ? v[j] : NEG_INF;
+        // candidates in ascending chunk order
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bool pass = v[j] > thr;
+          if (__ballot(pass) != 0) {
+            if (pass) top.insert(v[j], c0 + j);
+            thr = top.kth(K);
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // output: indices ascending, -1 padded; per-head fp32 scores of the selected chunks
+  if (lane < PW && mypos < N) {
+    // sort the K best by chunk id (insertion sort over a small register array)
+    int ids[KC];
+    float sv[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      ids[k] = (k < K && top.c[k] >= 0) ? top.c[k] : 0x7FFFFFFF;
+      sv[k] = top.s[k];
+    }
+#pragma unroll
+    for (int a = 0; a < KC; ++a)
+#pragma unroll
+      for (int bb = KC - 1; bb > a; --bb) {
+        const bool sw = ids[bb] < ids[bb - 1];
+        const int ti = ids[bb];
+        const float ts = sv[bb];
+        ids[bb] = sw ? ids[bb - 1] : ti;
+        sv[bb] = sw ? sv[bb - 1] : ts;
+        ids[bb - 1] = sw ? ti : ids[bb - 1];
+        sv[bb - 1] = sw ? ts : sv[bb - 1];
+      }
+    int32_t* dst = topk_idx + ((size_t)bg * N + mypos) * K;
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+      if (k < K) dst[k] = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
+    if (topk_score != nullptr) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        acc[hh][i] = fmaf(acc[hh][i], scale, ev);
-        best = fmaxf(best, acc[hh][i]);
-      }
-      sel[i] = (c < nd_i[i]) ? best : NEG_INF;
-      pass |= sel[i] > thr_s[16 * w + 4 * (lane >> 4) + i];
-    }
-    if (__ballot(pass) == 0) continue;
+        float* ds = topk_score + (((size_t)b * Hq + g * G + hh) * N + mypos) * K;
+        if constexpr (G == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pr = 4 * (lane >> 4) + i;
-      stw[pr * 17 + (lane & 15)] = sel[i];
+          for (int k = 0; k < KC; ++k)
+            if (k < K) ds[k] = ids[k] == 0x7FFFFFFF ? __builtin_nanf("") : sv[k];
+        } else {
+          const QT* qh = qs + (((size_t)b * Hq + g * G + hh) * N + mypos) * DH;
+          for (int k = 0; k < K; ++k) {
+            const int ck = ids[k < KC ? k : 0];
+            if (ck == 0x7FFFFFFF) {
+              ds[k] = __builtin_nanf("");
+              continue;
+            }
+            const T* kr = kLg + (size_t)ck * DH;
+            float a = 0.f;
+            for (int dd = 0; dd < DH; dd += 8) {
+              const auto kv = ld8<T>(kr + dd);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) sthw[(hh * 16 + pr) * 17 + (lane & 15)] = acc[hh][i];
-    }
-    wave_lds_sync();
-    if (lane < 16) {
-      const int pl = 16 * w + lane;
-      float thr = thr_s[pl];
-      int n = cnt_s[pl];
-      float* ls = lst_s + pl * KP;
-      int* li = lst_i + pl * KP;
-      float* lh = lst_h + pl * KP * G;
-      for (int j = 0; j < 16; ++j) {
-        const float v = stw[lane * 17 + j];
-        if (!(v > thr)) continue;
-        // insert below every entry that scores >= v (earlier chunks win ties)
-        int at = n < K ? n : K - 1;
-        while (at > 0 && ls[at - 1] < v) {
-          ls[at] = ls[at - 1];
-          li[at] = li[at - 1];
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) lh[at * G + hh] = lh[(at - 1) * G + hh];
-          --at;
-        }
-        ls[at] = v;
-        li[at] = c0 + j;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) lh[at * G + hh] = sthw[(hh * 16 + lane) * 17 + j];
-        n = n < K ? n + 1 : K;
-        if (n == K) thr = ls[K - 1];
-      }
-      thr_s[pl] = thr;
-      cnt_s[pl] = n;
-    }
-    wave_lds_sync();
-  }
-
-  // write this wave's positions: indices ascending, -1 / NaN padded
-  if (lane < 16) {
-    const int pl = 16 * w + lane;
-    const int pos = p0 + pl;
-    if (pos < N) {
-      const int n = cnt_s[pl];
-      int* li = lst_i + pl * KP;
-      float* lh = lst_h + pl * KP * G;
-      // insertion sort by chunk id (n <= 64)
-      for (int a = 1; a < n; ++a) {
-        const int key = li[a];
-        float hv[G];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) hv[hh] = lh[a * G + hh];
-        int bpos = a;
-        while (bpos > 0 && li[bpos - 1] > key) {
-          li[bpos] = li[bpos - 1];
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) lh[bpos * G + hh] = lh[(bpos - 1) * G + hh];
-          --bpos;
-        }
-        li[bpos] = key;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) lh[bpos * G + hh] = hv[hh];
-      }
-      int32_t* dst = topk_idx + ((size_t)bg * N + pos) * K;
-      for (int k = 0; k < K; ++k) dst[k] = k < n ? li[k] : -1;
-      if (topk_score != nullptr) {
-        for (int hh = 0; hh < G; ++hh) {
-          float* ds = topk_score + (((size_t)b * Hq + g * G + hh) * N + pos) * K;
-          for (int k = 0; k < K; ++k) ds[k] = k < n ? lh[k * G + hh] : __builtin_nanf("");
+              for (int j = 0; j < 8; ++j) a = fmaf(to_f<QT>(qh[dd + j]), (float)kv[j], a);
+            }
+            ds[k] = fmaf(a, scale, to_f<T>(eg[ck]));
+          }
         }
       }
     }
   }
 }
 
-static size_t route_lds(int K, int G) {
-  const int KP = K + 1;
-  return sizeof(float) * (size_t)(64 * KP * 2 + 64 * KP * G + 128 + 4 * 16 * 17 * (1 + G));
-}
-
-template <typename T, typename QT, int G, int DH>
+template <typename T, typename QT, int G, int DH, int KC>
 static hipError_t route_go(const Dims& p, const void* qs, const void* kL, const void* e,
                            int32_t* idx, float* sc, hipStream_t st) {
-  const int ntiles = (p.N + 63) / 64;
-  const size_t lds = route_lds(p.K, G);
-  auto kern = k_route<T, QT, G, DH>;
-  if (lds > 64 * 1024) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const QT*)qs,
+  constexpr int PWG = 4 * 16 * (G >= 4 ? 1 : 4 / G);
+  const int ntiles = (p.N + PWG - 1) / PWG;
+  auto kern = k_route<T, QT, G, DH, KC>;
+  hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), 0, st, (const QT*)qs,
                      (const T*)kL, (const T*)e, idx, sc, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
                      ntiles);
   return hipGetLastError();
 }
 
+template <typename T, typename QT, int G, int DH>
+static hipError_t route_k(const Dims& p, const void* qs, const void* kL, const void* e,
+                          int32_t* idx, float* sc, hipStream_t st) {
+  if (p.K <= 4) return route_go<T, QT, G, DH, 4>(p, qs, kL, e, idx, sc, st);
+  if (p.K <= 8) return route_go<T, QT, G, DH, 8>(p, qs, kL, e, idx, sc, st);
+  if (p.K <= 16) return route_go<T, QT, G, DH, 16>(p, qs, kL, e, idx, sc, st);
+  return route_go<T, QT, G, DH, 32>(p, qs, kL, e, idx, sc, st);
+}
+
 template <typename T, typename QT, int G>
 static hipError_t route_d(const Dims& p, const void* qs, const void* kL, const void* e, int32_t* idx,
                           float* sc, hipStream_t st) {
-  if (p.d == 64) return route_go<T, QT, G, 64>(p, qs, kL, e, idx, sc, st);
-  return route_go<T, QT, G, 128>(p, qs, kL, e, idx, sc, st);
+  if (p.d == 64) return route_k<T, QT, G, 64>(p, qs, kL, e, idx, sc, st);
+  return route_k<T, QT, G, 128>(p, qs, kL, e, idx, sc, st);
 }
 
 template <typename T, typename QT>

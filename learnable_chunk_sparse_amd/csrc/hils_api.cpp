@@ -52,7 +52,6 @@ hils_status check_problem(const hils_problem* p, int op) {
   if (p->r > 0) {
     if (!(p->r == 16 || p->r == 32 || p->r == 64)) return HILS_ERR_UNSUPPORTED;
     if (p->D % 32 != 0) return HILS_ERR_UNSUPPORTED;
-    if ((p->Hq * p->r) % 64 != 0) return HILS_ERR_UNSUPPORTED;
   }
   if (op != HILS_OP_DECODE) {
     if (G > 4) return HILS_ERR_UNSUPPORTED;

@@ -2,15 +2,26 @@
 // "Implementation and Training Recipes", Q-Cal; dev.to "Engineering
 // Details": delta_q = W_up W_down h). The calibrated query only feeds the
 // chunk scores, so it is produced in fp32:
-//   u[t, h*r + j] = sum_D h[t, D] W_down[h, j, D]   (bf16 MFMA, exact products,
-//                                                   fp32 accumulation)
-//   q_hat[b, h, i, :] = q[b, h, i, :] + W_up[h] u[t, h*r : h*r + r]   (fp32 FMA)
-// One workgroup computes 64 tokens x 64 columns of u (64 / r heads) with four
-// waves in a 2 x 2 arrangement of 32 x 32 sub-tiles, then the heads' q_hat.
+//   u[t, h*r + j] = sum_D h[t, D] W_down[h, j, D]        (GEMM 1)
+//   q_hat[b, h, i, :] = q[b, h, i, :] + W_up[h] u[t, h*r : h*r + r]   (GEMM 2)
+// One workgroup owns 128 tokens x 128 columns of u (128 / r heads).
+// GEMM 1 runs on 16x16x32 bf16 MFMAs (exact products, fp32 accumulation)
+// over LDS tiles of 32-deep k steps, with the next step's global loads
+// prefetched into registers while the current one is multiplied. GEMM 2
+// (k = r) reuses the u tile from LDS, split into hi + lo bf16 halves so that
+// the fp32 u keeps ~16 significant bits, and adds q in the epilogue.
 #include "hils_common.h"
 #include "hils_internal.h"
 
+#include <algorithm>
+
 namespace hils {
+
+namespace {
+constexpr int QT_M = 128, QT_N = 128, QT_K = 32;
+constexpr int QT_KP = QT_K + 8;     // padded k pitch of the bf16 tiles (elements)
+constexpr int QT_UP = QT_N + 4;     // pitch of the fp32 u tile
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* __restrict__ hs,
@@ -18,86 +29,155 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
                                               float* __restrict__ qhat, float* __restrict__ u_out,
                                               int ntok, int Nq, int Hq, int d, int D, int r) {
   typedef typename Frag<T>::type FT;
-  __shared__ float us[64][65];
-  extern __shared__ float wu_s[];  // [nh][d][r + 1]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // LDS: two k-step tiles of A (tokens) and B (u columns), later reused for u
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* As = reinterpret_cast<T*>(smem);            // [QT_M][QT_KP]
+  T* Bs = As + QT_M * QT_KP;                     // [QT_N][QT_KP]
+  float* us = reinterpret_cast<float*>(smem);    // [QT_M][QT_UP] after the k loop
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = lane >> 4, col = lane & 15;
   const int wm = w & 1, wn = w >> 1;
-  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int t0 = blockIdx.x * QT_M, c0 = blockIdx.y * QT_N;
   const int ncol = Hq * r;
 
-  f32x4 acc[2][2];
+  // global -> register prefetch: each thread moves 16 elements of A and of B
+  // per k step (two 8-element vectors each)
+  constexpr int VEC = 8;
+  const int lrow = tid >> 1, lk = (tid & 1) * 16;  // row in tile, first k of this thread
+  const int ta = min(t0 + lrow, ntok - 1);
+  const int cb = min(c0 + lrow, ncol - 1);          // columns past Hq*r are never stored
+  const T* asrc = hs + (size_t)ta * D + lk;
+  const T* bsrc = Wd + (size_t)cb * D + lk;
+  FT ra[2], rbv[2];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int v = 0; v < 2; ++v) {
+      ra[v] = ld8<T>(asrc + k0 + VEC * v);
+      rbv[v] = ld8<T>(bsrc + k0 + VEC * v);
+    }
+  };
+  auto stash = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = zero4();
+    for (int v = 0; v < 2; ++v) {
+      *reinterpret_cast<FT*>(As + lrow * QT_KP + lk + VEC * v) = ra[v];
+      *reinterpret_cast<FT*>(Bs + lrow * QT_KP + lk + VEC * v) = rbv[v];
+    }
+  };
 
-  const T* arow[2];
-  const T* brow[2];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    int t = t0 + 32 * wm + 16 * mb + (lane & 15);
-    t = t < ntok ? t : ntok - 1;
-    arow[mb] = hs + (size_t)t * D + 8 * (lane >> 4);
-  }
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int c = c0 + 32 * wn + 16 * nb + (lane & 15);
-    brow[nb] = Wd + (size_t)c * D + 8 * (lane >> 4);
-  }
-  for (int k0 = 0; k0 < D; k0 += 32) {
-    FT A0 = ld8<T>(arow[0] + k0), A1 = ld8<T>(arow[1] + k0);
-    FT B0 = ld8<T>(brow[0] + k0), B1 = ld8<T>(brow[1] + k0);
-    acc[0][0] = mma16(A0, B0, acc[0][0]);
-    acc[0][1] = mma16(A0, B1, acc[0][1]);
-    acc[1][0] = mma16(A1, B0, acc[1][0]);
-    acc[1][1] = mma16(A1, B1, acc[1][1]);
-  }
+    for (int b2 = 0; b2 < 4; ++b2) acc[a][b2] = zero4();
+
+  fetch(0);
+  for (int k0 = 0; k0 < D; k0 += QT_K) {
+    __syncthreads();
+    stash();
+    __syncthreads();
+    if (k0 + QT_K < D) fetch(k0 + QT_K);
+    FT af[4], bfr[4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
+      af[mb] = *reinterpret_cast<const FT*>(As + (64 * wm + 16 * mb + col) * QT_KP + 8 * grp);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
+      bfr[nb] = *reinterpret_cast<const FT*>(Bs + (64 * wn + 16 * nb + col) * QT_KP + 8 * grp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 32 * wm + 16 * mb + 4 * (lane >> 4) + i;
-        const int col = 32 * wn + 16 * nb + (lane & 15);
-        us[row][col] = acc[mb][nb][i];
-        if (u_out != nullptr && t0 + row < ntok) u_out[(size_t)(t0 + row) * ncol + c0 + col] = acc[mb][nb][i];
-      }
-  // stage W_up of this tile's heads as fp32, rows padded to r + 1
-  const int nh = 64 / r, h0 = c0 / r;
-  for (int x = threadIdx.x; x < nh * d * r; x += 256) {
-    const int j = x % r, dd = (x / r) % d, hl = x / (r * d);
-    wu_s[(hl * d + dd) * (r + 1) + j] = to_f<T>(Wu[((size_t)(h0 + hl) * d + dd) * r + j]);
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma16(af[mb], bfr[nb], acc[mb][nb]);
   }
   __syncthreads();
-  const int total = 64 * nh * d;
-  for (int x = threadIdx.x; x < total; x += 256) {
-    const int dd = x % d, hl = (x / d) % nh, tok = x / (d * nh);
-    const int t = t0 + tok;
-    if (t >= ntok) continue;
-    const float* wrow = wu_s + (hl * d + dd) * (r + 1);
-    const float* urow = &us[tok][hl * r];
-    float s = 0.f;
-    for (int j = 0; j < r; ++j) s = fmaf(wrow[j], urow[j], s);
-    const int bb = t / Nq, i = t - bb * Nq;
-    const size_t off = (((size_t)bb * Hq + h0 + hl) * Nq + i) * d + dd;
-    qhat[off] = to_f<T>(q[off]) + s;
+  // u tile -> LDS (fp32), and optionally to global
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        us[(64 * wm + 16 * mb + 4 * grp + i) * QT_UP + 64 * wn + 16 * nb + col] = acc[mb][nb][i];
+  __syncthreads();
+  if (u_out != nullptr) {
+    for (int x = tid; x < QT_M * QT_N; x += 256) {
+      const int rr = x / QT_N, cc = x - rr * QT_N;
+      if (t0 + rr < ntok && c0 + cc < ncol) u_out[(size_t)(t0 + rr) * ncol + c0 + cc] = us[rr * QT_UP + cc];
+    }
+  }
+
+  // GEMM 2: for each head of the tile, q_hat rows = q + u_h W_up[h]^T.
+  // Work items: (head, 16-token block, 16-dim block); k = r in 32-deep steps.
+  const int h0 = c0 / r, nh = min(QT_N / r, Hq - h0);
+  const int nmb = QT_M / 16, nnb = d / 16;
+  const int items = nh * nmb * nnb;
+  for (int it = w; it < items; it += 4) {
+    const int hl = it / (nmb * nnb);
+    const int rem = it - hl * nmb * nnb;
+    const int mb = rem / nnb, nb = rem - mb * nnb;
+    const int h = h0 + hl;
+    f32x4 o = zero4();
+    for (int kk = 0; kk < r; kk += 32) {
+      // A: u[token 16 mb + col][j = kk + 8 grp .. +8], split hi / lo
+      // (r = 16 leaves the upper half of the 32-deep step empty)
+      const bool kv = kk + 8 * grp < r;
+      const float* ur = us + (16 * mb + col) * QT_UP + hl * r + kk + 8 * grp;
+      float x[8], y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = kv ? ur[j] : 0.f;
+      const FT ahi = pack8<T>(x);
+      // B: W_up[h][dim 16 nb + col][j]
+      FT bw;
+      if (kv) {
+        bw = ld8<T>(Wu + ((size_t)h * d + 16 * nb + col) * r + kk + 8 * grp);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = 0.f;
+        bw = pack8<T>(y);
+      }
+      o = mma16(ahi, bw, o);
+      if constexpr (sizeof(T) == 2) {
+        const u16x8 hb = __builtin_bit_cast(u16x8, ahi);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = x[j] - bf2f(hb[j]);
+        o = mma16(pack8<T>(y), bw, o);
+      }
+    }
+    // D layout: token 16 mb + 4 grp + i, dim 16 nb + col
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * mb + 4 * grp + i;
+      if (t < ntok) {
+        const int bb = t / Nq, ii = t - bb * Nq;
+        const size_t off = (((size_t)bb * Hq + h) * Nq + ii) * d + 16 * nb + col;
+        qhat[off] = to_f<T>(q[off]) + o[i];
+      }
+    }
   }
 }
 
 hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, const void* W_down,
                        const void* W_up, float* q_hat, float* u, hipStream_t st) {
   const int ntok = p.B * Nq;
-  dim3 grid((ntok + 63) / 64, p.Hq * p.r / 64);
-  const size_t lds = (size_t)(64 / p.r) * p.d * (p.r + 1) * sizeof(float);
-  if (p.dtype == 1)
-    hipLaunchKernelGGL(k_qcal<uint16_t>, grid, dim3(256), lds, st, (const uint16_t*)q,
-                       (const uint16_t*)h, (const uint16_t*)W_down, (const uint16_t*)W_up, q_hat,
-                       u, ntok, Nq, p.Hq, p.d, p.D, p.r);
-  else
-    hipLaunchKernelGGL(k_qcal<float>, grid, dim3(256), lds, st, (const float*)q, (const float*)h,
-                       (const float*)W_down, (const float*)W_up, q_hat, u, ntok, Nq, p.Hq, p.d,
-                       p.D, p.r);
+  dim3 grid((ntok + QT_M - 1) / QT_M, (p.Hq * p.r + QT_N - 1) / QT_N);
+  const size_t el = p.dtype == 1 ? 2 : 4;
+  const size_t lds = std::max<size_t>((size_t)(QT_M + QT_N) * QT_KP * el, (size_t)QT_M * QT_UP * 4);
+  hipError_t err;
+  if (p.dtype == 1) {
+    auto kern = k_qcal<uint16_t>;
+    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+      return err;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint16_t*)q, (const uint16_t*)h,
+                       (const uint16_t*)W_down, (const uint16_t*)W_up, q_hat, u, ntok, Nq, p.Hq,
+                       p.d, p.D, p.r);
+  } else {
+    auto kern = k_qcal<float>;
+    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+      return err;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const float*)q, (const float*)h,
+                       (const float*)W_down, (const float*)W_up, q_hat, u, ntok, Nq, p.Hq, p.d, p.D,
+                       p.r);
+  }
   return hipGetLastError();
 }
 

@@ -29,12 +29,17 @@
 #include "hils_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace hils {
 
 namespace {
 constexpr int KPAD = 8;  // padding (elements) of the transposed staging rows
 }
+
+// token-permuted transposed copy of a [N][d] tensor (defined with the forward)
+template <typename T, int DH>
+__global__ void k_vt_perm(const T* __restrict__ v, T* __restrict__ vt, int N, int Np);
 
 // --------------------------------------------------------------- small kernels
 __global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
@@ -222,33 +227,64 @@ __device__ int bwd_block_scan(int* a, int n, int* wsum) {
 // chunks are processed first (their terms do not involve D), then the window
 // accumulates U1 = sum a_j (dO . v_j) k_j and U2 = sum a_j k_j so that its dq
 // part scale (U1 - D U2) is formed once D is known.
+// As in the forward, S^T = K Q^T and dP^T = V dO^T keep the probabilities in
+// the operand layout of dq^T = K^T dS^T, with K^T read from a token-permuted
+// transposed copy; waves take whole chunks dynamically and add into private
+// accumulator copies (no LDS atomics on the d-vectors).
+template <typename T, int DH>
+struct BwdChunkFrags {
+  typename Frag<T>::type k[4][DH / 32];   // K rows (A of S^T)
+  typename Frag<T>::type v[4][DH / 32];   // V rows (A of dP^T)
+  typename Frag<T>::type kt[DH / 16][2];  // K^T rows (A of dq^T)
+};
+
+template <typename T, int DH>
+__device__ __forceinline__ void bwd_load_block(BwdChunkFrags<T, DH>& f, const T* __restrict__ kb,
+                                               const T* __restrict__ vb, int nvalid,
+                                               const T* __restrict__ ktb, int Np, int lane) {
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    int tok = 16 * tb + (lane & 15);
+    tok = tok < nvalid ? tok : 0;
+    const size_t o = (size_t)tok * DH + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) {
+      f.k[tb][ks] = ld8<T>(kb + o + 32 * ks);
+      f.v[tb][ks] = ld8<T>(vb + o + 32 * ks);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < DH / 16; ++mb) {
+    const T* src = ktb + (size_t)(16 * mb + (lane & 15)) * Np + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) f.kt[mb][ks] = ld8<T>(src + 32 * ks);
+  }
+}
+
 template <typename T, int G, int DH, int CB>
 __global__ __launch_bounds__(256) void k_bwd_dq(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ dO, const T* __restrict__ kL, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ sT, const float* __restrict__ lse, float* __restrict__ Dv,
-    float* __restrict__ dq, float* __restrict__ dqhat, float* __restrict__ ds_o,
-    float* __restrict__ beta_o, float* __restrict__ delta_o, int N, int Hkv, int K, int W, int S,
-    float scale, int ntiles, int C) {
+    const T* __restrict__ kt, int Np, const T* __restrict__ dO, const T* __restrict__ kL,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ sT,
+    const float* __restrict__ lse, float* __restrict__ Dv, float* __restrict__ dq,
+    float* __restrict__ dqhat, float* __restrict__ ds_o, float* __restrict__ beta_o,
+    float* __restrict__ delta_o, int N, int Hkv, int K, int W, int S, float scale, int ntiles,
+    int C) {
   typedef typename Frag<T>::type FT;
-  constexpr int R = 64 * CB, TP = R / G, PPG = 16 / G;
+  constexpr int R = 64 * CB, TP = R / G;
   constexpr int KS = DH / 32, MB = DH / 16;
-  constexpr int AS = R + 4;
-  constexpr int VS = 64 + KPAD;
+  constexpr int RS = DH + 4;  // accumulator row stride
   constexpr int EPT = TP * 32 / 256;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* accT = reinterpret_cast<float*>(smem);  // [DH][AS]
-  float* Ls = accT + DH * AS;                    // [R]
-  float* Ds = Ls + R;                            // [R] chunk part of D, then D
-  float* wcS = Ds + R;                           // [R][K] fusion weight w_c
-  float* dlS = wcS + R * K;                      // [R][K] delta_c
-  T* ktb = reinterpret_cast<T*>(dlS + R * K);    // [4][DH][VS]
-  int* off = reinterpret_cast<int*>(ktb + 4 * DH * VS);
-  int* gb = off + C;
-  int* grp = gb + C;
-  const int NGMAX = min(TP * K, TP * K / PPG + C + 1);
-  uint16_t* ent = reinterpret_cast<uint16_t*>(grp + 2 * NGMAX);
+  float* accT = reinterpret_cast<float*>(smem);     // [4][R][RS] per-wave copies
+  float* Ls = accT + 4 * R * RS;                    // [R]
+  float* Ds = Ls + R;                               // [R] chunk part of D, then D
+  float* dsS = Ds + R;                              // [R][K]
+  int* off = reinterpret_cast<int*>(dsS + R * K);   // [C + 1]
+  int* nzl = off + C + 1;                           // [C]
+  uint16_t* ent = reinterpret_cast<uint16_t*>(nzl + C);
   __shared__ int wsum[4];
+  __shared__ int ctr;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int tile = ntiles - 1 - blockIdx.x;
@@ -260,21 +296,20 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
   const int ndmax = n_distant(plast, W, S);
   const T* kg = k + (size_t)bg * N * DH;
   const T* vg = v + (size_t)bg * N * DH;
-  T* kt = ktb + w * DH * VS;
+  const T* ktg = kt + (size_t)bg * DH * Np;
+  float* accW = accT + w * R * RS;
 
-  for (int x = tid; x < R * K; x += 256) {
-    wcS[x] = 0.f;
-    dlS[x] = 0.f;
-  }
-  for (int x = tid; x < DH * AS; x += 256) accT[x] = 0.f;
+  for (int x = tid; x < R * RS; x += 256) reinterpret_cast<f32x4*>(accT)[x] = zero4();
   for (int x = tid; x < R; x += 256) {
     const int pos = p0 + x / G, hh = x % G;
     const size_t ro = ((size_t)b * Hq + g * G + hh) * N + (pos < N ? pos : N - 1);
     Ls[x] = lse[ro];
     Ds[x] = 0.f;
   }
+  for (int x = tid; x < R * K; x += 256) dsS[x] = 0.f;
   // bucket the tile's selections by chunk
-  for (int x = tid; x < ndmax; x += 256) off[x] = 0;
+  for (int x = tid; x <= ndmax; x += 256) off[x] = 0;
+  if (tid == 0) ctr = 0;
   __syncthreads();
   int my_c[EPT], my_r[EPT];
   const int E = TP * K;
@@ -294,124 +329,130 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
     }
   }
   __syncthreads();
-  for (int x = tid; x < ndmax; x += 256) gb[x] = (off[x] + PPG - 1) / PPG;
+  for (int x = tid; x < ndmax; x += 256) nzl[x] = off[x] > 0 ? 1 : 0;
   __syncthreads();
   const int Etot = bwd_block_scan(off, ndmax, wsum);
-  const int NG = bwd_block_scan(gb, ndmax, wsum);
+  const int NZ = bwd_block_scan(nzl, ndmax, wsum);
+  if (tid == 0) off[ndmax] = Etot;
+  __syncthreads();
+  for (int base = 0; base < ndmax; base += 256) {
+    const int x = base + tid;
+    const int rk = (x < ndmax && off[x + 1] > off[x]) ? nzl[x] : -1;
+    __syncthreads();
+    if (rk >= 0) nzl[rk] = x;
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int c = my_c[j];
     if (c >= 0) {
       const int x = tid + 256 * j;
       const int pl = x / K, kk = x - pl * K;
-      const int r = my_r[j];
-      ent[off[c] + r] = (uint16_t)((pl << 6) | kk);
-      if (r % PPG == 0) {
-        const int gi = gb[c] + r / PPG;
-        const int n = (c + 1 < ndmax ? off[c + 1] : Etot) - off[c] - r;
-        grp[2 * gi] = c;
-        grp[2 * gi + 1] = ((off[c] + r) << 5) | (n < PPG ? n : PPG);
-      }
+      ent[off[c] + my_r[j]] = (uint16_t)((pl << 6) | kk);
     }
   }
   __syncthreads();
 
+  const float sc2 = scale * LOG2E;
   // ---------------- selected chunks (terms free of D)
-  for (int gi = w; gi < NG; gi += 4) {
-    const int c = grp[2 * gi];
-    const int gdesc = grp[2 * gi + 1];
-    const int st = gdesc >> 5, n = gdesc & 31;
-    const int col = lane & 15;
-    const int ei = col / G, hh = col % G;
-    const bool valid = ei < n;
-    const int en = ent[st + (valid ? ei : 0)];
-    const int pl = en >> 6, kk = en & 63;
-    const int pos = p0 + pl;
-    const int row = pl * G + hh;
-    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-    FT qf[KS], df[KS];
+  {
+    auto grab = [&]() __attribute__((always_inline)) {
+      int it = 0;
+      if (lane == 0) it = atomicAdd(&ctr, 1);
+      return __shfl(it, 0, 64);
+    };
+    BwdChunkFrags<T, DH> f;
+    for (int a = grab(); a < NZ; a = grab()) {
+      const int c = nzl[a];
+      const int e0 = off[c], n = off[c + 1] - e0;
+      bwd_load_block<T, DH>(f, kg + (size_t)c * 64 * DH, vg + (size_t)c * 64 * DH, 64, ktg + (size_t)c * 64, Np, lane);
+      const int nb = (n * G + 15) / 16;
+      for (int cbk = 0; cbk < nb; ++cbk) {
+        const int rr = 16 * cbk + (lane & 15);
+        const bool valid = rr < n * G;
+        const int ei = (valid ? rr : 0) / G, hh = (valid ? rr : 0) % G;
+        const int en = ent[e0 + ei];
+        const int pl = en >> 6, kk = en & 63;
+        const int row = pl * G + hh;
+        const size_t ro = ((size_t)b * Hq + g * G + hh) * N + p0 + pl;
+        FT qf[KS], df[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = ld8<T>(q + ro * DH + 8 * (lane >> 4) + 32 * ks);
-      df[ks] = ld8<T>(dO + ro * DH + 8 * (lane >> 4) + 32 * ks);
-    }
-    const T* kc = kg + (size_t)c * 64 * DH;
-    const T* vc = vg + (size_t)c * 64 * DH;
-    f32x4 sa[4], pa[4];
+        for (int ks = 0; ks < KS; ++ks) {
+          qf[ks] = ld8<T>(q + ro * DH + 8 * (lane >> 4) + 32 * ks);
+          df[ks] = ld8<T>(dO + ro * DH + 8 * (lane >> 4) + 32 * ks);
+        }
+        const float sc = valid ? sT[ro * K + kk] : 0.f;
+        f32x4 sa[4], pa[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const size_t to = (size_t)(16 * tb + (lane & 15)) * DH + 8 * (lane >> 4);
-      sa[tb] = zero4();
-      pa[tb] = zero4();
+        for (int tb = 0; tb < 4; ++tb) {
+          sa[tb] = zero4();
+          pa[tb] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sa[tb] = mma16(ld8<T>(kc + to + 32 * ks), qf[ks], sa[tb]);
-        pa[tb] = mma16(ld8<T>(vc + to + 32 * ks), df[ks], pa[tb]);
-      }
-    }
-    wave_lds_sync();
-    stage_t64<T, DH>(kc, 64, kt, lane);
-    float mx = NEG_INF;
+          for (int ks = 0; ks < KS; ++ks) {
+            sa[tb] = mma16(f.k[tb][ks], qf[ks], sa[tb]);
+            pa[tb] = mma16(f.v[tb][ks], df[ks], pa[tb]);
+          }
+        }
+        float mx = NEG_INF;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[tb][i] *= scale;
-        mx = fmaxf(mx, sa[tb][i]);
-      }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    float ls = 0.f;
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sa[tb][i]);
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float mref = mx * sc2;
+        float ls = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __expf(sa[tb][i] - mx);
-        sa[tb][i] = pv;
-        ls += pv;
-      }
-    ls += shfl_xor(ls, 16);
-    ls += shfl_xor(ls, 32);
-    const float inv = 1.f / ls;
-    float dl = 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const float pv = fast_exp2(fmaf(sa[tb][i], sc2, -mref));
+            sa[tb][i] = pv;
+            ls += pv;
+          }
+        ls += shfl_xor(ls, 16);
+        ls += shfl_xor(ls, 32);
+        const float inv = 1.f / ls;
+        float dl = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[tb][i] *= inv;  // p within the chunk
-        dl += sa[tb][i] * pa[tb][i];
-      }
-    dl += shfl_xor(dl, 16);
-    dl += shfl_xor(dl, 32);  // delta_c = sum p (dO . v)
-    const float sc = valid ? sT[ro * K + kk] : 0.f;
-    const float Lrow = Ls[row];
-    const float wc = valid ? __expf(sc - Lrow) : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            sa[tb][i] *= inv;  // p within the chunk
+            dl += sa[tb][i] * pa[tb][i];
+          }
+        dl += shfl_xor(dl, 16);
+        dl += shfl_xor(dl, 32);  // delta_c = sum p (dO . v)
+        const float Lrow = Ls[row];
+        const float wc = valid ? fast_exp2((sc - Lrow) * LOG2E) : 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[tb][i] = wc * sa[tb][i] * (pa[tb][i] - dl);  // dx
-    wave_lds_sync();
-    f32x4 dqc[MB];
+          for (int i = 0; i < 4; ++i) sa[tb][i] = wc * sa[tb][i] * (pa[tb][i] - dl);  // dx
+        f32x4 dqc[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) dqc[mb] = zero4();
+        for (int mb = 0; mb < MB; ++mb) dqc[mb] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const FT pf = pk8<T>(sa[2 * ks], sa[2 * ks + 1]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const FT pf = pk8<T>(sa[2 * ks], sa[2 * ks + 1]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) dqc[mb] = mma16(ld_tfrag<T, VS>(kt, mb, ks, lane), pf, dqc[mb]);
-    }
-    if (valid) {
+          for (int mb = 0; mb < MB; ++mb) dqc[mb] = mma16(f.kt[mb][ks], pf, dqc[mb]);
+        }
+        if (valid) {
+          float* dst = accW + row * RS + 4 * (lane >> 4);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          atomicAdd(&accT[(16 * mb + 4 * (lane >> 4) + i) * AS + row], dqc[mb][i] * scale);
-      if ((lane >> 4) == 0) {
-        wcS[row * K + kk] = wc;
-        dlS[row * K + kk] = dl;
-        atomicAdd(&Ds[row], wc * dl);
-        beta_o[ro * K + kk] = sc - Lrow - (mx + __logf(ls));
-        delta_o[ro * K + kk] = dl;
+          for (int mb = 0; mb < MB; ++mb) {
+            f32x4 cur = *reinterpret_cast<const f32x4*>(dst + 16 * mb);
+            cur += scale * dqc[mb];
+            *reinterpret_cast<f32x4*>(dst + 16 * mb) = cur;
+          }
+          if ((lane >> 4) == 0) {
+            dsS[row * K + kk] = wc;  // fusion weight, turned into ds once D is known
+            atomicAdd(&Ds[row], wc * dl);
+            beta_o[ro * K + kk] = sc - Lrow - (mx * scale + __logf(ls));
+            delta_o[ro * K + kk] = dl;
+          }
+        }
       }
     }
   }
@@ -433,13 +474,13 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
       wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
       const int pc = pos < N ? pos : N - 1;
       const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pc;
-      Lr[cb] = Ls[r];
-      const T* qs = q + ro * DH + 8 * (lane >> 4);
-      const T* ds = dO + ro * DH + 8 * (lane >> 4);
+      Lr[cb] = Ls[r] * LOG2E;
+      const T* qs2 = q + ro * DH + 8 * (lane >> 4);
+      const T* ds2 = dO + ro * DH + 8 * (lane >> 4);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qf[cb][ks] = ld8<T>(qs + 32 * ks);
-        df[cb][ks] = ld8<T>(ds + 32 * ks);
+        qf[cb][ks] = ld8<T>(qs2 + 32 * ks);
+        df[cb][ks] = ld8<T>(ds2 + 32 * ks);
       }
     }
     f32x4 u1[MB][CB], u2[MB][CB];
@@ -455,34 +496,23 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
     }
     if (pw_lo < N) {
       const int kv_lo = n_distant(pw_lo, W, S) * S;
+      BwdChunkFrags<T, DH> f;
       for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 64) {
         const int nvalid = min(64, N - kv0);
+        bwd_load_block<T, DH>(f, kg + (size_t)kv0 * DH, vg + (size_t)kv0 * DH, nvalid, ktg + kv0, Np, lane);
         f32x4 sa[4][CB], pa[4][CB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          int tok = 16 * tb + (lane & 15);
-          tok = tok < nvalid ? tok : 0;
-          const T* ksrc = kg + (size_t)(kv0 + tok) * DH + 8 * (lane >> 4);
-          const T* vsrc = vg + (size_t)(kv0 + tok) * DH + 8 * (lane >> 4);
-          FT kf[KS], vf[KS];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = ld8<T>(ksrc + 32 * ks);
-            vf[ks] = ld8<T>(vsrc + 32 * ks);
-          }
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             sa[tb][cb] = zero4();
             pa[tb][cb] = zero4();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-              sa[tb][cb] = mma16(kf[ks], qf[cb][ks], sa[tb][cb]);
-              pa[tb][cb] = mma16(vf[ks], df[cb][ks], pa[tb][cb]);
+              sa[tb][cb] = mma16(f.k[tb][ks], qf[cb][ks], sa[tb][cb]);
+              pa[tb][cb] = mma16(f.v[tb][ks], df[cb][ks], pa[tb][cb]);
             }
           }
-        }
-        wave_lds_sync();
-        stage_t64<T, DH>(kg + (size_t)kv0 * DH, nvalid, kt, lane);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -490,25 +520,22 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int j = kv0 + 16 * tb + 4 * (lane >> 4) + i;
-              const bool ok = prow[cb] >= 0 && j <= prow[cb] && j >= wsr[cb];
-              const float a = ok ? __expf(sa[tb][cb][i] * scale - Lr[cb]) : 0.f;
+              const bool ok = j <= prow[cb] && j >= wsr[cb];
+              const float a = ok ? fast_exp2(fmaf(sa[tb][cb][i], sc2, -Lr[cb])) : 0.f;
               const float adp = a * pa[tb][cb][i];
               dw[cb] += adp;
               sa[tb][cb][i] = a;
               pa[tb][cb][i] = adp;
             }
-        wave_lds_sync();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const FT kf = ld_tfrag<T, VS>(kt, mb, ks, lane);
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-              u1[mb][cb] = mma16(kf, pk8<T>(pa[2 * ks][cb], pa[2 * ks + 1][cb]), u1[mb][cb]);
-              u2[mb][cb] = mma16(kf, pk8<T>(sa[2 * ks][cb], sa[2 * ks + 1][cb]), u2[mb][cb]);
+              u1[mb][cb] = mma16(f.kt[mb][ks], pk8<T>(pa[2 * ks][cb], pa[2 * ks + 1][cb]), u1[mb][cb]);
+              u2[mb][cb] = mma16(f.kt[mb][ks], pk8<T>(sa[2 * ks][cb], sa[2 * ks + 1][cb]), u2[mb][cb]);
             }
-          }
       }
     }
 #pragma unroll
@@ -518,11 +545,13 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
       dsum += shfl_xor(dsum, 32);
       const int r = rbase + 16 * cb + (lane & 15);
       const float D = dsum + Ds[r];
+      float* dst = accW + r * RS + 4 * (lane >> 4);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          accT[(16 * mb + 4 * (lane >> 4) + i) * AS + r] += scale * (u1[mb][cb][i] - D * u2[mb][cb][i]);
+      for (int mb = 0; mb < MB; ++mb) {
+        f32x4 cur = *reinterpret_cast<const f32x4*>(dst + 16 * mb);
+        cur += scale * (u1[mb][cb] - D * u2[mb][cb]);
+        *reinterpret_cast<f32x4*>(dst + 16 * mb) = cur;
+      }
       wave_lds_sync();
       if ((lane >> 4) == 0) {
         Ds[r] = D;
@@ -537,25 +566,37 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
     const int r = x / K, kk = x - r * K;
     const int pos = p0 + r / G, hh = r % G;
     if (pos >= N) continue;
-    const float dsv = wcS[x] * (dlS[x] - Ds[r]);
-    wcS[x] = dsv;
-    ds_o[(((size_t)b * Hq + g * G + hh) * N + pos) * K + kk] = dsv;
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
+    const float wc = dsS[x];
+    const float dsv = wc == 0.f ? 0.f : wc * (delta_o[ro * K + kk] - Ds[r]);
+    dsS[x] = dsv;
+    ds_o[ro * K + kk] = dsv;
   }
   __syncthreads();
-  for (int x = tid; x < R * DH; x += 256) {
-    const int dd = x % DH, r = x / DH;
+  for (int x = tid; x < R * DH / 4; x += 256) {
+    const int r = x / (DH / 4), d4 = 4 * (x - r * (DH / 4));
     const int pos = p0 + r / G, hh = r % G;
     if (pos >= N) continue;
     const int32_t* ti = topk_idx + ((size_t)bg * N + pos) * K;
-    float sur = 0.f;
+    f32x4 sur = zero4();
     for (int kk = 0; kk < K; ++kk) {
       const int c = ti[kk];
-      if (c >= 0) sur += wcS[r * K + kk] * to_f<T>(kL[((size_t)bg * C + c) * DH + dd]);
+      if (c >= 0) {
+        const float dsv = dsS[r * K + kk];
+        const T* kr = kL + ((size_t)bg * C + c) * DH + d4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sur[j] += dsv * to_f<T>(kr[j]);
+      }
     }
     sur *= scale;
+    const int a0 = r * RS + d4;
+    const f32x4 tok = *reinterpret_cast<const f32x4*>(accT + a0) +
+                      *reinterpret_cast<const f32x4*>(accT + R * RS + a0) +
+                      *reinterpret_cast<const f32x4*>(accT + 2 * R * RS + a0) +
+                      *reinterpret_cast<const f32x4*>(accT + 3 * R * RS + a0);
     const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-    dq[ro * DH + dd] = accT[dd * AS + r] + sur;
-    if (dqhat != nullptr) dqhat[ro * DH + dd] = sur;
+    *reinterpret_cast<f32x4*>(dq + ro * DH + d4) = tok + sur;
+    if (dqhat != nullptr) *reinterpret_cast<f32x4*>(dqhat + ro * DH + d4) = sur;
   }
 }
 
@@ -744,40 +785,69 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
     // surrogate gradients of this chunk: dkL += scale ds q_hat, de += ds
     if (!isw) {
       const int nrows = min(32, ne * G - rb0);
-      for (int r = 0; r < nrows; ++r) {
-        const int rr = rb0 + r;
+      // lane r < nrows fetches row r's gradient and offset; the q_hat rows are
+      // then read eight at a time so their loads overlap
+      float dsl = 0.f;
+      long rol = 0;
+      if (lane < nrows) {
+        const int rr = rb0 + lane;
         const int en = lst[rr / G];
         const int pos = en >> 6, kk = en & 63, hh = rr % G;
-        const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-        const float dsv = ds_i[ro * K + kk];
+        rol = (long)(((size_t)b * Hq + g * G + hh) * N + pos);
+        dsl = ds_i[rol * K + kk];
+      }
+      float dsum = dsl;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, 64);
+      dea += dsum;
+      for (int r0 = 0; r0 < nrows; r0 += 8) {
+        float dv8[8];
+        long ro8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dv8[u] = __shfl(dsl, r0 + u, 64);
+          const int lo = __shfl((int)(rol & 0xFFFFFFFF), r0 + u, 64);
+          const int hi = __shfl((int)(rol >> 32), r0 + u, 64);
+          ro8[u] = ((long)hi << 32) | (unsigned)lo;
+        }
 #pragma unroll
         for (int j = 0; j < (DH + 63) / 64; ++j) {
           const int dd = lane + 64 * j;
-          if (dd < DH) dkl[j] += dsv * to_f<QT>(qs[ro * DH + dd]);
+          if (dd < DH) {
+            float qv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) qv[u] = (r0 + u < nrows) ? to_f<QT>(qs[ro8[u] * DH + dd]) : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dkl[j] += dv8[u] * qv[u];
+          }
         }
-        dea += dsv;
       }
     }
   }
-  // reduce the four waves' partial sums in LDS (reusing the staging space), then write
-  __syncthreads();
-  for (int x = tid; x < 2 * 64 * DH; x += 256) red[x] = 0.f;
-  __syncthreads();
+  // reduce the four waves' partial sums in LDS (reusing the staging space):
+  // the waves add in turn with plain read-modify-write, then write out
+  for (int turn = 0; turn < 4; ++turn) {
+    __syncthreads();
+    if (w == turn) {
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int nb = 0; nb < MB; ++nb)
+        for (int nb = 0; nb < MB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * tb + 4 * (lane >> 4) + i;
-        const int dd = 16 * nb + (lane & 15);
-        atomicAdd(&red[tok * DH + dd], dka[tb][nb][i]);
-        atomicAdd(&red[64 * DH + tok * DH + dd], dva[tb][nb][i]);
-      }
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * tb + 4 * (lane >> 4) + i;
+            const int dd = 16 * nb + (lane & 15);
+            const float a = turn ? red[tok * DH + dd] : 0.f;
+            const float c = turn ? red[64 * DH + tok * DH + dd] : 0.f;
+            red[tok * DH + dd] = a + dka[tb][nb][i];
+            red[64 * DH + tok * DH + dd] = c + dva[tb][nb][i];
+          }
 #pragma unroll
-  for (int j = 0; j < (DH + 63) / 64; ++j)
-    if (lane + 64 * j < DH) atomicAdd(&redl[lane + 64 * j], dkl[j]);
-  if (lane == 0) atomicAdd(&redl[DH], dea);
+      for (int j = 0; j < (DH + 63) / 64; ++j)
+        if (lane + 64 * j < DH) redl[lane + 64 * j] += dkl[j];
+      if (lane == 0) redl[DH] += dea;
+    }
+  }
   __syncthreads();
   for (int x = tid; x < 64 * DH; x += 256) {
     const int tok = x / DH;
@@ -798,6 +868,8 @@ namespace {
 struct BwdWs {
   float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du;
   int *cnt, *off, *cur, *lst;
+  void* kt;
+  int Np;
 };
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carve(const Dims& p, void* base, BwdWs* w) {
@@ -824,33 +896,41 @@ size_t carve(const Dims& p, void* base, BwdWs* w) {
   w->off = (int*)take(bg * (p.C + 1) * 4);
   w->cur = (int*)take(bg * p.C * 4);
   w->lst = (int*)take(bg * (size_t)p.N * p.K * 4);
+  w->Np = (p.N + 63) / 64 * 64;
+  w->kt = take(bg * (size_t)p.d * w->Np * (p.dtype == 1 ? 2 : 4));
   return o;
 }
 
 template <typename T, int G, int DH, int CB>
 size_t dq_lds(const Dims& p) {
-  constexpr int R = 64 * CB, TP = R / G, PPG = 16 / G;
-  const int ngmax = std::min(TP * p.K, TP * p.K / PPG + p.C + 1);
-  size_t s = sizeof(float) * ((size_t)DH * (R + 4) + 2 * R + 2 * (size_t)R * p.K);
-  s += sizeof(T) * 4 * DH * (64 + KPAD);
-  s += sizeof(int) * (2 * (size_t)p.C + 2 * (size_t)ngmax);
+  constexpr int R = 64 * CB, TP = R / G;
+  size_t s = sizeof(float) * (4 * (size_t)R * (DH + 4) + 2 * R + (size_t)R * p.K);
+  s += sizeof(int) * (2 * (size_t)p.C + 1);
   s += sizeof(uint16_t) * (size_t)TP * p.K;
-  return (s + 15) & ~(size_t)15;
+  return ((s + 15) & ~(size_t)15) + 64;
 }
 
-template <typename T, int CB>
-size_t dq_lds_g(const Dims& p) {
-  switch (p.G) {
-    case 1: return p.d == 64 ? dq_lds<T, 1, 64, CB>(p) : dq_lds<T, 1, 128, CB>(p);
-    case 2: return p.d == 64 ? dq_lds<T, 2, 64, CB>(p) : dq_lds<T, 2, 128, CB>(p);
-    case 4: return p.d == 64 ? dq_lds<T, 4, 64, CB>(p) : dq_lds<T, 4, 128, CB>(p);
+// row blocks per wave of the dq pass: two when the LDS budget allows
+template <typename T, int G, int DH>
+int dq_cb(const Dims& p) {
+  if (sizeof(T) == 2 && dq_lds<T, G, DH, 2>(p) <= 160 * 1024) return 2;
+  return 1;
+}
+
+template <typename T>
+size_t dq_lds_t(const Dims& p) {
+  switch (p.G * 1000 + p.d) {
+    case 1064: return dq_cb<T, 1, 64>(p) == 2 ? dq_lds<T, 1, 64, 2>(p) : dq_lds<T, 1, 64, 1>(p);
+    case 1128: return dq_cb<T, 1, 128>(p) == 2 ? dq_lds<T, 1, 128, 2>(p) : dq_lds<T, 1, 128, 1>(p);
+    case 2064: return dq_cb<T, 2, 64>(p) == 2 ? dq_lds<T, 2, 64, 2>(p) : dq_lds<T, 2, 64, 1>(p);
+    case 2128: return dq_cb<T, 2, 128>(p) == 2 ? dq_lds<T, 2, 128, 2>(p) : dq_lds<T, 2, 128, 1>(p);
+    case 4064: return dq_cb<T, 4, 64>(p) == 2 ? dq_lds<T, 4, 64, 2>(p) : dq_lds<T, 4, 64, 1>(p);
+    case 4128: return dq_cb<T, 4, 128>(p) == 2 ? dq_lds<T, 4, 128, 2>(p) : dq_lds<T, 4, 128, 1>(p);
     default: return (size_t)-1;
   }
 }
 
-size_t dq_lds_bytes(const Dims& p) {
-  return (p.dtype == 1 ? dq_lds_g<uint16_t, 2>(p) : dq_lds_g<float, 1>(p)) + 64;
-}
+size_t dq_lds_bytes(const Dims& p) { return p.dtype == 1 ? dq_lds_t<uint16_t>(p) : dq_lds_t<float>(p); }
 
 size_t dkdv_lds(const Dims& p) {
   const size_t el = p.dtype == 1 ? 2 : 4;
@@ -872,7 +952,6 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
                          const void* v, const void* kL, const void* e, const void* o,
                          const float* lse, const int32_t* topk_idx, const void* dO, float* dq,
                          float* dk, float* dv, float* dkL, float* de, BwdWs& w, hipStream_t st) {
-  constexpr int CB = sizeof(T) == 2 ? 2 : 1;
   const size_t rows = (size_t)p.B * p.Hq * p.N;
   const size_t bg = (size_t)p.B * p.Hkv;
   hipError_t err;
@@ -890,19 +969,26 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
   hipLaunchKernelGGL(k_inv_fill, dim3(grid1(total)), dim3(256), 0, st, topk_idx, w.off, w.cur, w.lst,
                      total, p.N, p.K, p.C);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // dq pass
+  // dq pass (K^T copy first)
   {
-    constexpr int TP = 64 * CB / G;
-    const int ntiles = (p.N + TP - 1) / TP;
-    const size_t lds = dq_lds<T, G, DH, CB>(p);
-    auto kern = k_bwd_dq<T, G, DH, CB>;
-    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-      return err;
-    hipLaunchKernelGGL(kern, dim3(ntiles, (unsigned)bg), dim3(256), lds, st, (const T*)q, (const T*)k,
-                       (const T*)v, (const T*)dO, (const T*)kL, topk_idx, w.sT, lse, w.Dv, dq,
-                       w.dqhat, w.ds, w.beta, w.delta, p.N, p.Hkv, p.K, p.W, p.S, p.scale, ntiles,
-                       p.C);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_vt_perm<T, DH>), dim3(w.Np / 64, (unsigned)bg), dim3(256), 0, st,
+                       (const T*)k, (T*)w.kt, p.N, w.Np);
+    auto go = [&](auto cbc) -> hipError_t {
+      constexpr int CBv = decltype(cbc)::value;
+      constexpr int TP = 64 * CBv / G;
+      const int ntiles = (p.N + TP - 1) / TP;
+      const size_t lds = dq_lds<T, G, DH, CBv>(p);
+      auto kern = k_bwd_dq<T, G, DH, CBv>;
+      hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e2 != hipSuccess) return e2;
+      hipLaunchKernelGGL(kern, dim3(ntiles, (unsigned)bg), dim3(256), lds, st, (const T*)q,
+                         (const T*)k, (const T*)v, (const T*)w.kt, w.Np, (const T*)dO,
+                         (const T*)kL, topk_idx, w.sT, lse, w.Dv, dq, w.dqhat, w.ds, w.beta,
+                         w.delta, p.N, p.Hkv, p.K, p.W, p.S, p.scale, ntiles, p.C);
+      return hipGetLastError();
+    };
+    err = dq_cb<T, G, DH>(p) == 2 ? go(std::integral_constant<int, 2>()) : go(std::integral_constant<int, 1>());
+    if (err != hipSuccess) return err;
   }
   // dk / dv pass
   {

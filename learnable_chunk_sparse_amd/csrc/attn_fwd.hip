@@ -64,6 +64,11 @@ __global__ __launch_bounds__(256) void k_vt_perm(const T* __restrict__ v, T* __r
   }
 }
 
+template __global__ void k_vt_perm<uint16_t, 64>(const uint16_t*, uint16_t*, int, int);
+template __global__ void k_vt_perm<uint16_t, 128>(const uint16_t*, uint16_t*, int, int);
+template __global__ void k_vt_perm<float, 64>(const float*, float*, int, int);
+template __global__ void k_vt_perm<float, 128>(const float*, float*, int, int);
+
 // In-place exclusive scan of a[0..n) by the whole block (256 threads); returns the total.
 __device__ int block_excl_scan(int* a, int n, int* wsum) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;

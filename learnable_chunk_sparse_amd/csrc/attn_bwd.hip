@@ -46,62 +46,104 @@ __global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = v;
 }
-__global__ void k_fill_i32(int* __restrict__ p, size_t n, int v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
 
-// One wave per row (b, h, i): the fp32 score s_c of each selected slot.
+// fp32 score s_c = scale q_hat . kL_c + e_c of every selected slot. A
+// workgroup takes 16 consecutive query rows: their q_hat rows are staged in
+// LDS with coalesced loads, then each thread owns (row, slot) pairs and reads
+// the selected landmark row with 16-byte loads (landmarks stay in L2).
 template <typename T, typename QT, int DH>
 __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
                                                   const int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ sT, long rows, int N, int Hq,
                                                   int Hkv, int G, int C, int K, float scale) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int i = (int)(row % N);
-  const long bh = row / N;
-  const int h = (int)(bh % Hq), b = (int)(bh / Hq);
-  const int g = h / G;
-  const long bg = (long)b * Hkv + g;
-  const int32_t* ti = topk_idx + (bg * N + i) * K;
-  for (int k = 0; k < K; ++k) {
-    const int c = ti[k];
-    float s = 0.f;
-    if (c >= 0) {
-      for (int dd = lane; dd < DH; dd += 64) s += to_f<QT>(qs[row * DH + dd]) * to_f<T>(kL[(bg * C + c) * DH + dd]);
+  constexpr int PR = 16, QP = DH + 4;
+  __shared__ __align__(16) float qrow[PR * QP];
+  const int tid = threadIdx.x;
+  const long r0 = (long)blockIdx.x * PR;
+  for (int x = tid; x < PR * DH / 4; x += 256) {
+    const int rr = x / (DH / 4), d4 = 4 * (x - rr * (DH / 4));
+    const long row = r0 + rr;
+    f32x4 v = zero4();
+    if (row < rows) {
+      if constexpr (sizeof(QT) == 4) {
+        v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(qs) + row * DH + d4);
+      } else {
+        const u16x4 h4 = *reinterpret_cast<const u16x4*>(qs + row * DH + d4);
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-      s = fmaf(s, scale, to_f<T>(e[bg * C + c]));
+        for (int j = 0; j < 4; ++j) v[j] = bf2f(h4[j]);
+      }
     }
-    if (lane == 0) sT[row * K + k] = c >= 0 ? s : __builtin_nanf("");
+    *reinterpret_cast<f32x4*>(qrow + rr * QP + d4) = v;
+  }
+  __syncthreads();
+  for (int x = tid; x < PR * K; x += 256) {
+    const int rr = x / K, kk = x - rr * K;
+    const long row = r0 + rr;
+    if (row >= rows) break;
+    const int i = (int)(row % N);
+    const long bh = row / N;
+    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+    const long bg = (long)b * Hkv + h / G;
+    const int c = topk_idx[(bg * N + i) * K + kk];
+    float s = __builtin_nanf("");
+    if (c >= 0) {
+      const T* kr = kL + (bg * C + c) * DH;
+      const float* qr = qrow + rr * QP;
+      float acc = 0.f;
+#pragma unroll
+      for (int d8 = 0; d8 < DH; d8 += 8) {
+        const typename Frag<T>::type kv = ld8<T>(kr + d8);
+        const f32x4 qa = *reinterpret_cast<const f32x4*>(qr + d8);
+        const f32x4 qb = *reinterpret_cast<const f32x4*>(qr + d8 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = fmaf(qa[j], (float)kv[j], acc);
+          acc = fmaf(qb[j], (float)kv[j + 4], acc);
+        }
+      }
+      s = fmaf(acc, scale, to_f<T>(e[bg * C + c]));
+    }
+    sT[row * K + kk] = s;
   }
 }
 
-// inverse index: count, scan, fill
-__global__ void k_inv_count(const int32_t* __restrict__ topk_idx, int* __restrict__ cnt, long total,
-                            int N, int K, int C) {
-  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (long)gridDim.x * blockDim.x) {
-    const int c = topk_idx[x];
-    if (c >= 0 && c < C) {
-      const long bg = x / ((long)N * K);
-      atomicAdd(&cnt[bg * C + c], 1);
-    }
+// Inverse index (for each chunk, the (position, slot) pairs that selected
+// it), built as a counting sort per (b, kv head): the positions are cut into
+// `ns` ranges, each range histograms its selections in LDS, an exclusive scan
+// over (chunk, range) gives every range its first slot per chunk, and the
+// fill pass places the entries through LDS cursors.
+__global__ __launch_bounds__(256) void k_inv_hist(const int32_t* __restrict__ topk_idx,
+                                                  int* __restrict__ cnt, int N, int K, int C, int ns) {
+  extern __shared__ int hist[];
+  const int sp = blockIdx.x, bg = blockIdx.y, tid = threadIdx.x;
+  for (int c = tid; c < C; c += 256) hist[c] = 0;
+  __syncthreads();
+  const long per = ((long)N + ns - 1) / ns;
+  const long i0 = sp * per, i1 = min((long)N, i0 + per);
+  const int32_t* src = topk_idx + (long)bg * N * K;
+  for (long x = i0 * K + tid; x < i1 * K; x += 256) {
+    const int c = src[x];
+    if (c >= 0 && c < C) atomicAdd(&hist[c], 1);
   }
+  __syncthreads();
+  int* dst = cnt + (long)bg * C * ns;
+  for (int c = tid; c < C; c += 256) dst[(long)c * ns + sp] = hist[c];
 }
 
-__global__ __launch_bounds__(256) void k_inv_scan(const int* __restrict__ cnt, int* __restrict__ off, int C) {
+// exclusive scan of cnt[bg][c][range] in place; off[bg][c] = first slot of chunk c
+__global__ __launch_bounds__(256) void k_inv_scan(int* __restrict__ cnt, int* __restrict__ off, int C, int ns) {
   __shared__ int wsum[4];
   __shared__ int carry;
   const int bg = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int* cb = cnt + (long)bg * C;
+  int* cb = cnt + (long)bg * C * ns;
   int* ob = off + (long)bg * (C + 1);
+  const long n = (long)C * ns;
   if (t == 0) carry = 0;
   __syncthreads();
-  for (int base = 0; base < C; base += 256) {
-    const int x = base + t < C ? cb[base + t] : 0;
+  for (long base = 0; base < n; base += 256) {
+    const long idx = base + t;
+    const int x = idx < n ? cb[idx] : 0;
     int v = x;
 #pragma unroll
     for (int o2 = 1; o2 < 64; o2 <<= 1) {
@@ -112,7 +154,10 @@ __global__ __launch_bounds__(256) void k_inv_scan(const int* __restrict__ cnt, i
     __syncthreads();
     int pre = carry;
     for (int j = 0; j < w; ++j) pre += wsum[j];
-    if (base + t < C) ob[base + t] = pre + v - x;
+    if (idx < n) {
+      cb[idx] = pre + v - x;
+      if (idx % ns == 0) ob[idx / ns] = pre + v - x;
+    }
     __syncthreads();
     if (t == 255) carry = pre + v;
     __syncthreads();
@@ -120,17 +165,23 @@ __global__ __launch_bounds__(256) void k_inv_scan(const int* __restrict__ cnt, i
   if (t == 0) ob[C] = carry;
 }
 
-__global__ void k_inv_fill(const int32_t* __restrict__ topk_idx, const int* __restrict__ off,
-                           int* __restrict__ cur, int* __restrict__ lst, long total, int N, int K,
-                           int C) {
-  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (long)gridDim.x * blockDim.x) {
-    const int c = topk_idx[x];
+__global__ __launch_bounds__(256) void k_inv_fill(const int32_t* __restrict__ topk_idx,
+                                                  const int* __restrict__ start, int* __restrict__ lst,
+                                                  int N, int K, int C, int ns) {
+  extern __shared__ int cur[];
+  const int sp = blockIdx.x, bg = blockIdx.y, tid = threadIdx.x;
+  const int* sb = start + (long)bg * C * ns;
+  for (int c = tid; c < C; c += 256) cur[c] = sb[(long)c * ns + sp];
+  __syncthreads();
+  const long per = ((long)N + ns - 1) / ns;
+  const long i0 = sp * per, i1 = min((long)N, i0 + per);
+  const int32_t* src = topk_idx + (long)bg * N * K;
+  int* dst = lst + (long)bg * N * K;
+  for (long x = i0 * K + tid; x < i1 * K; x += 256) {
+    const int c = src[x];
     if (c >= 0 && c < C) {
-      const long bg = x / ((long)N * K);
-      const long rem = x - bg * N * K;
-      const int i = (int)(rem / K), k = (int)(rem - (long)i * K);
-      const int slot = atomicAdd(&cur[bg * C + c], 1);
-      lst[bg * (long)N * K + off[bg * (C + 1) + c] + slot] = (i << 6) | k;
+      const int i = (int)(x / K), k = (int)(x - (long)i * K);
+      dst[atomicAdd(&cur[c], 1)] = (i << 6) | k;
     }
   }
 }
@@ -867,10 +918,18 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
 namespace {
 struct BwdWs {
   float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du;
-  int *cnt, *off, *cur, *lst;
+  int *cnt, *off, *lst;
   void* kt;
-  int Np;
+  int Np, ns;
 };
+// position ranges of the inverse-index counting sort: enough workgroups to
+// fill the chip, at least 256 positions each
+int inv_ranges(const Dims& p) {
+  const long bg = (long)p.B * p.Hkv;
+  long ns = (2048 + bg - 1) / bg;
+  ns = std::min<long>(ns, (p.N + 255) / 256);
+  return (int)std::max<long>(ns, 1);
+}
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carve(const Dims& p, void* base, BwdWs* w) {
   char* c = static_cast<char*>(base);
@@ -892,9 +951,9 @@ size_t carve(const Dims& p, void* base, BwdWs* w) {
   w->delta = (float*)take(rows * p.K * 4);
   w->dqhat = (float*)take(qc ? rows * p.d * 4 : 0);
   w->du = (float*)take(qc ? (size_t)p.B * p.N * p.Hq * p.r * 4 : 0);
-  w->cnt = (int*)take(bg * p.C * 4);
+  w->ns = inv_ranges(p);
+  w->cnt = (int*)take(bg * p.C * w->ns * 4);
   w->off = (int*)take(bg * (p.C + 1) * 4);
-  w->cur = (int*)take(bg * p.C * 4);
   w->lst = (int*)take(bg * (size_t)p.N * p.K * 4);
   w->Np = (p.N + 63) / 64 * 64;
   w->kt = take(bg * (size_t)p.d * w->Np * (p.dtype == 1 ? 2 : 4));
@@ -943,6 +1002,7 @@ unsigned grid1(size_t n) { return (unsigned)std::min<size_t>((n + 255) / 256, 65
 size_t bwd_workspace(const Dims& p) {
   if (dq_lds_bytes(p) > 160 * 1024 || dkdv_lds(p) + 1024 > 160 * 1024) return (size_t)-1;
   if ((size_t)p.N * p.K >= (1u << 31)) return (size_t)-1;
+  if ((size_t)p.C * sizeof(int) > 64 * 1024) return (size_t)-1;
   BwdWs w;
   return carve(p, nullptr, &w);
 }
@@ -955,19 +1015,17 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
   const size_t rows = (size_t)p.B * p.Hq * p.N;
   const size_t bg = (size_t)p.B * p.Hkv;
   hipError_t err;
-  hipLaunchKernelGGL((k_bwd_prep<T, QT, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_bwd_prep<T, QT, DH>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
                      (const QT*)qsrc, (const T*)kL, (const T*)e, topk_idx, w.sT, (long)rows, p.N,
                      p.Hq, p.Hkv, G, p.C, p.K, p.scale);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // inverse index
-  hipLaunchKernelGGL(k_fill_i32, dim3(grid1(bg * p.C)), dim3(256), 0, st, w.cnt, bg * p.C, 0);
-  hipLaunchKernelGGL(k_fill_i32, dim3(grid1(bg * p.C)), dim3(256), 0, st, w.cur, bg * p.C, 0);
-  const long total = (long)bg * p.N * p.K;
-  hipLaunchKernelGGL(k_inv_count, dim3(grid1(total)), dim3(256), 0, st, topk_idx, w.cnt, total, p.N,
-                     p.K, p.C);
-  hipLaunchKernelGGL(k_inv_scan, dim3((unsigned)bg), dim3(256), 0, st, w.cnt, w.off, p.C);
-  hipLaunchKernelGGL(k_inv_fill, dim3(grid1(total)), dim3(256), 0, st, topk_idx, w.off, w.cur, w.lst,
-                     total, p.N, p.K, p.C);
+  const size_t hl = (size_t)p.C * sizeof(int);
+  hipLaunchKernelGGL(k_inv_hist, dim3(w.ns, (unsigned)bg), dim3(256), hl, st, topk_idx, w.cnt, p.N,
+                     p.K, p.C, w.ns);
+  hipLaunchKernelGGL(k_inv_scan, dim3((unsigned)bg), dim3(256), 0, st, w.cnt, w.off, p.C, w.ns);
+  hipLaunchKernelGGL(k_inv_fill, dim3(w.ns, (unsigned)bg), dim3(256), hl, st, topk_idx, w.cnt, w.lst,
+                     p.N, p.K, p.C, w.ns);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // dq pass (K^T copy first)
   {

@@ -33,10 +33,6 @@
 
 namespace hils {
 
-namespace {
-constexpr int KPAD = 8;  // padding (elements) of the transposed staging rows
-}
-
 // token-permuted transposed copy of a [N][d] tensor (defined with the forward)
 template <typename T, int DH>
 __global__ void k_vt_perm(const T* __restrict__ v, T* __restrict__ vt, int N, int Np);
@@ -186,60 +182,7 @@ __global__ __launch_bounds__(256) void k_inv_fill(const int32_t* __restrict__ to
   }
 }
 
-// --------------------------------------------------------------- LDS helpers
-// Stage a 64-token block of K ([64][DH] from ksrc) transposed into
-// kt[DH][64 + KPAD] (one wave; tokens >= nvalid read row 0).
-template <typename T, int DH>
-__device__ __forceinline__ void stage_t64(const T* __restrict__ src, int nvalid, T* dst, int lane) {
-  const int tp = lane & 31, half = lane >> 5;
-  const int t0 = 2 * tp, t1 = 2 * tp + 1;
-  const T* r0 = src + (size_t)(t0 < nvalid ? t0 : 0) * DH + half * (DH / 2);
-  const T* r1 = src + (size_t)(t1 < nvalid ? t1 : 0) * DH + half * (DH / 2);
-  constexpr int VS = 64 + KPAD;
-#pragma unroll
-  for (int j = 0; j < DH / 2; j += 8) {
-    const auto a = ld8<T>(r0 + j);
-    const auto bb = ld8<T>(r1 + j);
-    if constexpr (sizeof(T) == 2) {
-      const u16x8 ua = __builtin_bit_cast(u16x8, a), ub = __builtin_bit_cast(u16x8, bb);
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2)
-        *reinterpret_cast<uint32_t*>(dst + (half * (DH / 2) + j + e2) * VS + t0) =
-            (uint32_t)ua[e2] | ((uint32_t)ub[e2] << 16);
-    } else {
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        float2 pr;
-        pr.x = a[e2];
-        pr.y = bb[e2];
-        *reinterpret_cast<float2*>(dst + (half * (DH / 2) + j + e2) * VS + t0) = pr;
-      }
-    }
-  }
-}
-
-// fragment of a transposed [rows d][cols] LDS tile: rows 16*mb + lane%16, the
-// 8 columns {4g..4g+3, 16+4g..16+4g+3} + 32*ks (g = lane/16)
-template <typename T, int PITCH>
-__device__ __forceinline__ typename Frag<T>::type ld_tfrag(const T* t, int mb, int ks, int lane) {
-  const T* p = t + (16 * mb + (lane & 15)) * PITCH + 32 * ks + 4 * (lane >> 4);
-  if constexpr (sizeof(T) == 2) {
-    const u16x4 a = *reinterpret_cast<const u16x4*>(p);
-    const u16x4 bb = *reinterpret_cast<const u16x4*>(p + 16);
-    u16x8 u;
-    u[0] = a[0]; u[1] = a[1]; u[2] = a[2]; u[3] = a[3];
-    u[4] = bb[0]; u[5] = bb[1]; u[6] = bb[2]; u[7] = bb[3];
-    return __builtin_bit_cast(bf16x8, u);
-  } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(p + 16);
-    f32x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = bb[0]; r[5] = bb[1]; r[6] = bb[2]; r[7] = bb[3];
-    return r;
-  }
-}
-
+// --------------------------------------------------------------- helpers
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::type pk8(const f32x4& s0, const f32x4& s1) {
   float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -338,8 +281,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
   __shared__ int ctr;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int tile = ntiles - 1 - blockIdx.x;
-  const int bg = blockIdx.y;
+  int tx, bg;
+  xcd_block(tx, bg);
+  const int tile = ntiles - 1 - tx;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   const int p0 = tile * TP;
@@ -652,251 +596,297 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
 }
 
 // --------------------------------------------------------------- dk / dv pass
-template <typename T, typename QT, int G, int DH>
+// One workgroup per 64-token key block. Its rows are the window rows (every
+// position whose window covers the block, all heads of the group) and the
+// rows that selected the block as a chunk. A wave owns TW 16-token blocks
+// and a share of the 32-row groups and keeps dK / dV of its tokens in
+// registers; the waves of a token group add their sums at the end.
+// dK = dS^T Q and dV = P^T dO contract over rows, so Q and dO are needed with
+// the rows as the per-lane k index: the row-major fragments already in
+// registers are turned into that layout by a product with the identity
+// (exact: every product is x * 1 or x * 0).
+// The rows' data are prefetched (list entries two groups ahead; biases,
+// deltas, q / dO fragments and u rows one group ahead) so their latency hides
+// behind the current group's products.
+// dkL_c = scale sum_rows ds q_hat with q_hat = q + W_up u: the q part is one
+// more product of the transposed q fragments with ds (hi + lo bf16 halves);
+// the u part is added by k_bwd_dklu.
+struct DkdvRow {
+  int ro;      // query row (b, h, i) of this lane's group row
+  int pos;     // position (masking), -1 for padding rows
+  float bias;  // raw -lse (window) or beta (chunk)
+  float dlt;   // D (window) or delta_c (chunk)
+  float dsv;   // ds_c of the slot (chunk rows)
+};
+
+template <typename T, int G, int DH>
 __global__ __launch_bounds__(256) void k_bwd_dkdv(
-    const T* __restrict__ q, const QT* __restrict__ qs, const T* __restrict__ k,
-    const T* __restrict__ v, const T* __restrict__ dO, const float* __restrict__ lse,
-    const float* __restrict__ Dv, const int* __restrict__ ioff, const int* __restrict__ ilst,
-    const float* __restrict__ ds_i, const float* __restrict__ beta_i,
-    const float* __restrict__ delta_i, float* __restrict__ dk, float* __restrict__ dv,
-    float* __restrict__ dkL, float* __restrict__ de, int N, int Hkv, int K, int W, int S,
-    float scale, int C) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dv,
+    const int* __restrict__ ioff, const int* __restrict__ ilst, const float* __restrict__ ds_i,
+    const float* __restrict__ beta_i, const float* __restrict__ delta_i, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dkL, float* __restrict__ de, int N, int Hkv,
+    int K, int W, float scale, int C) {
   typedef typename Frag<T>::type FT;
   constexpr int KS = DH / 32, MB = DH / 16;
-  constexpr int RP = 32 + KPAD;  // pitch of the transposed 32-row staging
-  // dynamic LDS: per-wave Q^T / dO^T staging, later reused for the reduction
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* qt_all = reinterpret_cast<T*>(smem);               // [4][DH * RP]
-  T* dt_all = qt_all + 4 * DH * RP;                     // [4][DH * RP]
-  float* red = reinterpret_cast<float*>(smem);          // [2][64 * DH] (after the loop)
-  __shared__ float redl[DH + 1];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int blk = blockIdx.x, bg = blockIdx.y;
+  constexpr int TW = DH == 64 ? 4 : 2;        // 16-token blocks per wave
+  constexpr int NTG = 4 / TW, WPG = 4 / NTG;  // token groups, waves per token group
+  constexpr int MBL = MB / NTG;               // d blocks of the dkL product per token group
+  extern __shared__ __align__(16) float red[];  // [2][64][DH]
+  __shared__ float redl[DH];
+  __shared__ float redd;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int gl = lane >> 4, cl = lane & 15;
+  const int tg = w / WPG, wi = w - tg * WPG;
+  int blk, bg;
+  xcd_block(blk, bg);
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   const int kv0 = blk * 64;
   const int nvalid = min(64, N - kv0);
-  for (int x = tid; x <= DH; x += 256) redl[x] = 0.f;
-  // this block's keys/values as B operands of S = Q K^T and dP = dO V^T
-  FT kb[4][KS], vb[4][KS];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    int tok = 16 * tb + (lane & 15);
-    tok = tok < nvalid ? tok : 0;
-    const size_t to = ((size_t)bg * N + kv0 + tok) * DH + 8 * (lane >> 4);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kb[tb][ks] = ld8<T>(k + to + 32 * ks);
-      vb[tb][ks] = ld8<T>(v + to + 32 * ks);
-    }
+  for (int x = tid; x < DH; x += 256) redl[x] = 0.f;
+  if (tid == 0) redd = 0.f;
+
+  // the block's K / V rows in LDS (padded pitch: conflict-free fragment
+  // reads); they are the B operands of S = Q K^T and dP = dO V^T
+  constexpr int KP = DH + 16 / (int)sizeof(T);
+  T* ks_l = reinterpret_cast<T*>(red);  // [64][KP]
+  T* vs_l = ks_l + 64 * KP;             // [64][KP]
+  for (int x = tid; x < 64 * DH / 8; x += 256) {
+    const int tok = x / (DH / 8), d8 = 8 * (x - tok * (DH / 8));
+    const int tk = tok < nvalid ? tok : 0;
+    const size_t o = ((size_t)bg * N + kv0 + tk) * DH + d8;
+    *reinterpret_cast<FT*>(ks_l + tok * KP + d8) = ld8<T>(k + o);
+    *reinterpret_cast<FT*>(vs_l + tok * KP + d8) = ld8<T>(v + o);
   }
   __syncthreads();
-  // rows: window rows (positions kv0 .. i_hi, all heads) then the rows that
-  // selected this chunk (all heads)
+  // identity fragments: I_h[k][col] = (k == 16 h + col)
+  FT idf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float x[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) x[e2] = (8 * gl + e2 == 16 * h + cl) ? 1.f : 0.f;
+    idf[h] = pack8<T>(x);
+  }
+
   const int i_hi = min(N - 1, kv0 + 64 + W - 2);
   const int nw = (i_hi - kv0 + 1) * G;
   const bool chunk = blk < C;
   const int e0 = chunk ? ioff[(size_t)bg * (C + 1) + blk] : 0;
   const int ne = chunk ? ioff[(size_t)bg * (C + 1) + blk + 1] - e0 : 0;
   const int* lst = ilst + (size_t)bg * N * K + e0;
-  const int ngw = (nw + 31) / 32, ngc = (ne * G + 31) / 32;
-  f32x4 dka[4][MB], dva[4][MB];
+  const int ngw = (nw + 31) / 32, ngt = ngw + (ne * G + 31) / 32;
+  const int rowx = lane & 31;  // group row whose data this lane fetches
+
+  // Row data are fetched without branches (out-of-range groups read a valid
+  // dummy address) and checked where they are used, so the loads stay in
+  // flight behind the current group's products.
+  auto fetch_e = [&](int gi) __attribute__((always_inline)) {
+    const int rr = 32 * (gi - ngw) + rowx;
+    const bool ok = gi >= ngw && rr < ne * G;
+    return *(ok ? lst + rr / G : ioff);
+  };
+  auto fetch_m = [&](int gi, int en) __attribute__((always_inline)) {
+    DkdvRow m;
+    const bool isw = gi < ngw;
+    const int rw = 32 * gi + rowx, rc = 32 * (gi - ngw) + rowx;
+    const bool okw = rw < nw, okc = !isw && rc < ne * G;
+    const int posw = kv0 + (okw ? rw : 0) / G, hhw = (okw ? rw : 0) % G;
+    const int posc = okc ? en >> 6 : 0, kk = okc ? en & 63 : 0, hhc = rowx % G;
+    const int pos = isw ? posw : posc, hh = isw ? hhw : hhc;
+    m.ro = (b * Hq + g * G + hh) * N + pos;
+    m.pos = isw ? (okw ? pos : -1) : (okc ? N : -1);
+    const size_t idx = isw ? (size_t)m.ro : (size_t)m.ro * K + kk;
+    m.bias = (isw ? lse : beta_i)[idx];
+    m.dlt = (isw ? Dv : delta_i)[idx];
+    m.dsv = ds_i[isw ? 0 : idx];
+    return m;
+  };
+  auto fetch_q = [&](const DkdvRow& m, FT (&qa)[2][KS], FT (&da)[2][KS]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+    for (int rb = 0; rb < 2; ++rb) {
+      const int ro = __shfl(m.ro, 16 * rb + cl, 64);
+      const size_t o = (size_t)ro * DH + 8 * gl;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qa[rb][ks] = ld8<T>(q + o + 32 * ks);
+        da[rb][ks] = ld8<T>(dO + o + 32 * ks);
+      }
+    }
+  };
+  // per-wave slots of the current group's row values (bias, delta, pos, ds)
+  __shared__ f32x4 mrow_all[4][32];
+  f32x4* mrow = mrow_all[w];
+  f32x4 dka[TW][MB], dva[TW][MB], dklm[MBL];
+#pragma unroll
+  for (int tb = 0; tb < TW; ++tb)
 #pragma unroll
     for (int nb = 0; nb < MB; ++nb) {
       dka[tb][nb] = zero4();
       dva[tb][nb] = zero4();
     }
-  float dkl[(DH + 63) / 64];
 #pragma unroll
-  for (int j = 0; j < (DH + 63) / 64; ++j) dkl[j] = 0.f;
-  float dea = 0.f;
-  T* qt = qt_all + w * DH * RP;
-  T* dt = dt_all + w * DH * RP;
-  for (int gi = w; gi < ngw + ngc; gi += 4) {
+  for (int nb = 0; nb < MBL; ++nb) dklm[nb] = zero4();
+  float dsum = 0.f;
+  const float sc2 = scale * LOG2E;
+
+  auto compute = [&](int gi, const DkdvRow& m, const FT (&qa)[2][KS], const FT (&da)[2][KS],
+                     auto masked) __attribute__((always_inline)) {
+    constexpr bool MSK = decltype(masked)::value;
     const bool isw = gi < ngw;
-    const int rb0 = 32 * (isw ? gi : gi - ngw);
-    // A fragments: rows r = 16*rb + lane%16 of the group
-    FT qa[2][KS], da[2][KS];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int rr = rb0 + 16 * rb + (lane & 15);
-      int pos, hh;
-      bool ok;
-      if (isw) {
-        ok = rr < nw;
-        pos = kv0 + (ok ? rr : 0) / G;
-        hh = (ok ? rr : 0) % G;
-      } else {
-        ok = rr < ne * G;
-        const int en = lst[(ok ? rr : 0) / G];
-        pos = en >> 6;
-        hh = (ok ? rr : 0) % G;
-      }
-      const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        qa[rb][ks] = ld8<T>(q + ro * DH + 8 * (lane >> 4) + 32 * ks);
-        da[rb][ks] = ld8<T>(dO + ro * DH + 8 * (lane >> 4) + 32 * ks);
-      }
+    // Row values reach the lanes of the D layout (row 16 rb + 4 gl + i)
+    // through the wave's LDS slots: plain stores and loads, which (unlike
+    // lane shuffles) stay correct when the compiler predicates their uses.
+    {
+      const bool okr = m.pos >= 0;
+      f32x4 mv;
+      mv[0] = okr ? (isw ? -m.bias : m.bias) * LOG2E : NEG_INF;
+      mv[1] = okr ? m.dlt : 0.f;
+      mv[2] = __int_as_float(m.pos);
+      mv[3] = okr ? m.dsv : 0.f;
+      mrow[rowx] = mv;
+      wave_lds_sync();
     }
-    // per-lane rows of the D layout: 4*(lane/16) + i (+16 rb)
-    float bias[2][4], dlt[2][4];
-    int rpos[2][4], rws[2][4];
+    float bi[2][4], dl[2][4], dsr[2][4];
+    int ps[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = rb0 + 16 * rb + 4 * (lane >> 4) + i;
-        if (isw) {
-          const bool ok = rr < nw;
-          const int pos = kv0 + (ok ? rr : 0) / G, hh = (ok ? rr : 0) % G;
-          const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-          rpos[rb][i] = ok ? pos : -1;
-          rws[rb][i] = n_distant(pos, W, S) * S;
-          bias[rb][i] = -lse[ro];
-          dlt[rb][i] = Dv[ro];
-        } else {
-          const bool ok = rr < ne * G;
-          const int en = lst[(ok ? rr : 0) / G];
-          const int pos = en >> 6, kk = en & 63, hh = (ok ? rr : 0) % G;
-          const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-          rpos[rb][i] = ok ? 1 : -1;
-          rws[rb][i] = 0;
-          bias[rb][i] = beta_i[ro * K + kk];
-          dlt[rb][i] = delta_i[ro * K + kk];
-        }
+        const f32x4 rv = mrow[16 * rb + 4 * gl + i];
+        bi[rb][i] = rv[0];
+        dl[rb][i] = rv[1];
+        ps[rb][i] = __float_as_int(rv[2]);
+        dsr[rb][i] = rv[3];
       }
-    f32x4 sa[2][4], pa[2][4];
+    // per 16-token block: S and dP, then P (a_j) and dS packed as the A
+    // operands P^T and dS^T (token 16 (tg TW + tb) + cl)
+    FT pA[TW], sA[TW];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int tb = 0; tb < TW; ++tb) {
+      f32x4 sa[2], pa[2];
+      const int trow = (16 * (tg * TW + tb) + cl) * KP + 8 * gl;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        sa[rb][tb] = zero4();
-        pa[rb][tb] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sa[rb][tb] = mma16(qa[rb][ks], kb[tb][ks], sa[rb][tb]);
-          pa[rb][tb] = mma16(da[rb][ks], vb[tb][ks], pa[rb][tb]);
-        }
+      for (int rb = 0; rb < 2; ++rb) {
+        sa[rb] = zero4();
+        pa[rb] = zero4();
       }
-    // p (a_j) and dS (dx_j) in the D layout: row 4g+i (+16 rb), token lane%16 (+16 tb)
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * tb + (lane & 15);
-          const int j = kv0 + tok;
-          bool ok = rpos[rb][i] >= 0 && tok < nvalid;
-          if (isw) ok = ok && j <= rpos[rb][i] && j >= rws[rb][i];
-          const float a = ok ? __expf(sa[rb][tb][i] * scale + bias[rb][i]) : 0.f;
-          sa[rb][tb][i] = a;
-          pa[rb][tb][i] = a * (pa[rb][tb][i] - dlt[rb][i]);
-        }
-    // stage Q^T and dO^T of the group's 32 rows: [d][row]
-    wave_lds_sync();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int rr = 16 * rb + (lane & 15);
-        if constexpr (sizeof(T) == 2) {
-          const u16x8 uq = __builtin_bit_cast(u16x8, qa[rb][ks]);
-          const u16x8 ud = __builtin_bit_cast(u16x8, da[rb][ks]);
+        const FT kf = *reinterpret_cast<const FT*>(ks_l + trow + 32 * ks);
+        const FT vf = *reinterpret_cast<const FT*>(vs_l + trow + 32 * ks);
 #pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) {
-            const int dd = 8 * (lane >> 4) + 32 * ks + e2;
-            qt[dd * RP + rr] = uq[e2];
-            dt[dd * RP + rr] = ud[e2];
-          }
-        } else {
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) {
-            const int dd = 8 * (lane >> 4) + 32 * ks + e2;
-            qt[dd * RP + rr] = qa[rb][ks][e2];
-            dt[dd * RP + rr] = da[rb][ks][e2];
-          }
+        for (int rb = 0; rb < 2; ++rb) {
+          sa[rb] = mma16(qa[rb][ks], kf, sa[rb]);
+          pa[rb] = mma16(da[rb][ks], vf, pa[rb]);
         }
       }
-    wave_lds_sync();
-    // dV += P^T dO, dK += dS^T Q over the 32 rows (one 32-deep step)
+      const int tok = 16 * (tg * TW + tb) + cl;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = fast_exp2(fmaf(sa[rb][i], sc2, bi[rb][i]));
+          if constexpr (MSK) a = (tok < nvalid && kv0 + tok <= ps[rb][i]) ? a : 0.f;
+          sa[rb][i] = a;
+          pa[rb][i] = a * (pa[rb][i] - dl[rb][i]);
+        }
+      pA[tb] = pk8<T>(sa[0], sa[1]);
+      sA[tb] = pk8<T>(pa[0], pa[1]);
+    }
+    // ds of the group rows as the first row of an A operand (hi + lo halves)
+    FT dsh, dsl;
+    const bool dkl_here = !isw;
+    if (dkl_here) {
+      float hi[8], lo[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) hi[e2] = cl == 0 ? dsr[e2 >> 2][e2 & 3] : 0.f;
+      dsh = pack8<T>(hi);
+      if constexpr (sizeof(T) == 2) {
+        const u16x8 hb = __builtin_bit_cast(u16x8, dsh);
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) lo[e2] = hi[e2] - bf2f(hb[e2]);
+        dsl = pack8<T>(lo);
+      }
+      dsum += (tg == 0 && lane < 32 && m.pos >= 0) ? m.dsv : 0.f;
+    }
 #pragma unroll
     for (int nb = 0; nb < MB; ++nb) {
-      const FT dof = ld_tfrag<T, RP>(dt, nb, 0, lane);
-      const FT qf = ld_tfrag<T, RP>(qt, nb, 0, lane);
+      const int ks = nb >> 1, h = nb & 1;
+      const FT qT = pk8<T>(mma16(qa[0][ks], idf[h], zero4()), mma16(qa[1][ks], idf[h], zero4()));
+      const FT dT = pk8<T>(mma16(da[0][ks], idf[h], zero4()), mma16(da[1][ks], idf[h], zero4()));
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        dva[tb][nb] = mma16(pk8<T>(sa[0][tb], sa[1][tb]), dof, dva[tb][nb]);
-        dka[tb][nb] = mma16(pk8<T>(pa[0][tb], pa[1][tb]), qf, dka[tb][nb]);
+      for (int tb = 0; tb < TW; ++tb) {
+        dva[tb][nb] = mma16(pA[tb], dT, dva[tb][nb]);
+        dka[tb][nb] = mma16(sA[tb], qT, dka[tb][nb]);
+      }
+      if (dkl_here && nb / MBL == tg) {
+        dklm[nb % MBL] = mma16(dsh, qT, dklm[nb % MBL]);
+        if constexpr (sizeof(T) == 2) dklm[nb % MBL] = mma16(dsl, qT, dklm[nb % MBL]);
       }
     }
-    // surrogate gradients of this chunk: dkL += scale ds q_hat, de += ds
-    if (!isw) {
-      const int nrows = min(32, ne * G - rb0);
-      // lane r < nrows fetches row r's gradient and offset; the q_hat rows are
-      // then read eight at a time so their loads overlap
-      float dsl = 0.f;
-      long rol = 0;
-      if (lane < nrows) {
-        const int rr = rb0 + lane;
-        const int en = lst[rr / G];
-        const int pos = en >> 6, kk = en & 63, hh = rr % G;
-        rol = (long)(((size_t)b * Hq + g * G + hh) * N + pos);
-        dsl = ds_i[rol * K + kk];
-      }
-      float dsum = dsl;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, 64);
-      dea += dsum;
-      for (int r0 = 0; r0 < nrows; r0 += 8) {
-        float dv8[8];
-        long ro8[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          dv8[u] = __shfl(dsl, r0 + u, 64);
-          const int lo = __shfl((int)(rol & 0xFFFFFFFF), r0 + u, 64);
-          const int hi = __shfl((int)(rol >> 32), r0 + u, 64);
-          ro8[u] = ((long)hi << 32) | (unsigned)lo;
-        }
-#pragma unroll
-        for (int j = 0; j < (DH + 63) / 64; ++j) {
-          const int dd = lane + 64 * j;
-          if (dd < DH) {
-            float qv[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) qv[u] = (r0 + u < nrows) ? to_f<QT>(qs[ro8[u] * DH + dd]) : 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) dkl[j] += dv8[u] * qv[u];
-          }
-        }
-      }
+  };
+
+  // two register sets take turns: while one group is computed the next
+  // group's data load into the other set
+  {
+    FT qa0[2][KS], da0[2][KS], qa1[2][KS], da1[2][KS];
+    int gi = wi;
+    int en0 = fetch_e(gi), en1 = fetch_e(gi + WPG);
+    DkdvRow m0 = fetch_m(gi, en0), m1;
+    fetch_q(m0, qa0, da0);
+    auto run = [&](int gc, const DkdvRow& m, const FT (&qa)[2][KS], const FT (&da)[2][KS])
+        __attribute__((always_inline)) {
+      if (gc < ngw && (32 * gc / G < 63 || nvalid < 64)) compute(gc, m, qa, da, std::true_type());
+      else compute(gc, m, qa, da, std::false_type());
+    };
+    while (gi < ngt) {
+      en0 = fetch_e(gi + 2 * WPG);
+      m1 = fetch_m(gi + WPG, en1);
+      fetch_q(m1, qa1, da1);
+      run(gi, m0, qa0, da0);
+      gi += WPG;
+      if (gi >= ngt) break;
+      en1 = fetch_e(gi + 2 * WPG);
+      m0 = fetch_m(gi + WPG, en0);
+      fetch_q(m0, qa0, da0);
+      run(gi, m1, qa1, da1);
+      gi += WPG;
     }
   }
-  // reduce the four waves' partial sums in LDS (reusing the staging space):
-  // the waves add in turn with plain read-modify-write, then write out
-  for (int turn = 0; turn < 4; ++turn) {
+
+  // ---- reductions: dK / dV by the waves of each token group in turn
+  for (int turn = 0; turn < WPG; ++turn) {
     __syncthreads();
-    if (w == turn) {
+    if (wi == turn) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < TW; ++tb)
 #pragma unroll
         for (int nb = 0; nb < MB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = 16 * tb + 4 * (lane >> 4) + i;
-            const int dd = 16 * nb + (lane & 15);
-            const float a = turn ? red[tok * DH + dd] : 0.f;
-            const float c = turn ? red[64 * DH + tok * DH + dd] : 0.f;
-            red[tok * DH + dd] = a + dka[tb][nb][i];
-            red[64 * DH + tok * DH + dd] = c + dva[tb][nb][i];
+            const int tok = 16 * (tg * TW + tb) + 4 * gl + i;
+            const int x = tok * DH + 16 * nb + cl;
+            const float a = turn ? red[x] : 0.f;
+            const float c = turn ? red[64 * DH + x] : 0.f;
+            red[x] = a + dka[tb][nb][i];
+            red[64 * DH + x] = c + dva[tb][nb][i];
           }
+    }
+  }
+  if (chunk) {
+    if (lane < 16) {
 #pragma unroll
-      for (int j = 0; j < (DH + 63) / 64; ++j)
-        if (lane + 64 * j < DH) redl[lane + 64 * j] += dkl[j];
-      if (lane == 0) redl[DH] += dea;
+      for (int nb = 0; nb < MBL; ++nb) atomicAdd(&redl[16 * (tg * MBL + nb) + cl], dklm[nb][0]);
+    }
+    if (tg == 0) {
+      float s2 = dsum;
+#pragma unroll
+      for (int m2 = 32; m2 >= 1; m2 >>= 1) s2 += __shfl_xor(s2, m2, 64);
+      if (lane == 0) atomicAdd(&redd, s2);
     }
   }
   __syncthreads();
@@ -910,7 +900,69 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
   }
   if (chunk) {
     for (int x = tid; x < DH; x += 256) dkL[((size_t)bg * C + blk) * DH + x] = redl[x] * scale;
-    if (tid == 0) de[(size_t)bg * C + blk] = redl[DH];
+    if (tid == 0) de[(size_t)bg * C + blk] = redd;
+  }
+}
+
+// Q-Cal part of the landmark gradient: dkL_c += scale sum_h W_up[h] U_h with
+// U_h = sum over the rows of head h that selected chunk c of ds u_row. One
+// workgroup per chunk; r lanes share a row (u rows are read whole).
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_dklu(const int* __restrict__ ioff,
+                                                  const int* __restrict__ ilst,
+                                                  const float* __restrict__ ds_i,
+                                                  const float* __restrict__ u,
+                                                  const T* __restrict__ W_up,
+                                                  float* __restrict__ dkL, int N, int Hkv, int G,
+                                                  int K, int C, int d, int r, float scale) {
+  __shared__ float us[4 * 64];  // [G][r]
+  int c, bg;
+  xcd_block(c, bg);
+  const int tid = threadIdx.x;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int Hq = Hkv * G;
+  for (int x = tid; x < G * r; x += 256) us[x] = 0.f;
+  __syncthreads();
+  const int e0 = ioff[(size_t)bg * (C + 1) + c];
+  const int nrow = (ioff[(size_t)bg * (C + 1) + c + 1] - e0) * G;
+  const int* lst = ilst + (size_t)bg * N * K + e0;
+  const int j = tid % r, slot = tid / r, nslot = 256 / r;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int x = slot;
+  for (; x + 3 * nslot < nrow; x += 4 * nslot) {
+    float dsv[4], uv[4];
+    int hh[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int xx = x + t * nslot;
+      const int en = lst[xx / G];
+      hh[t] = xx % G;
+      const int pos = en >> 6, kk = en & 63;
+      dsv[t] = ds_i[((size_t)(b * Hq + g * G + hh[t]) * N + pos) * K + kk];
+      uv[t] = u[((size_t)(b * N + pos) * Hq + g * G + hh[t]) * r + j];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int h2 = 0; h2 < 4; ++h2) acc[h2] += hh[t] == h2 ? dsv[t] * uv[t] : 0.f;
+  }
+  for (; x < nrow; x += nslot) {
+    const int en = lst[x / G], h1 = x % G;
+    const int pos = en >> 6, kk = en & 63;
+    const float dsv = ds_i[((size_t)(b * Hq + g * G + h1) * N + pos) * K + kk];
+    const float uv = u[((size_t)(b * N + pos) * Hq + g * G + h1) * r + j];
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2) acc[h2] += h1 == h2 ? dsv * uv : 0.f;
+  }
+  for (int h2 = 0; h2 < G; ++h2) atomicAdd(&us[h2 * r + j], acc[h2]);
+  __syncthreads();
+  for (int dd = tid; dd < d; dd += 256) {
+    float val = 0.f;
+    for (int h2 = 0; h2 < G; ++h2) {
+      const T* wr = W_up + ((size_t)(g * G + h2) * d + dd) * r;
+      for (int jj = 0; jj < r; ++jj) val = fmaf(to_f<T>(wr[jj]), us[h2 * r + jj], val);
+    }
+    dkL[((size_t)bg * C + c) * d + dd] += val * scale;
   }
 }
 
@@ -920,6 +972,7 @@ struct BwdWs {
   float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du;
   int *cnt, *off, *lst;
   void* kt;
+  const void* W_up;
   int Np, ns;
 };
 // position ranges of the inverse-index counting sort: enough workgroups to
@@ -993,7 +1046,7 @@ size_t dq_lds_bytes(const Dims& p) { return p.dtype == 1 ? dq_lds_t<uint16_t>(p)
 
 size_t dkdv_lds(const Dims& p) {
   const size_t el = p.dtype == 1 ? 2 : 4;
-  return std::max(2 * 4 * (size_t)p.d * (32 + KPAD) * el, 2 * 64 * (size_t)p.d * 4);
+  return std::max(2 * 64 * (size_t)p.d * sizeof(float), 2 * 64 * ((size_t)p.d * el + 16));
 }
 
 unsigned grid1(size_t n) { return (unsigned)std::min<size_t>((n + 255) / 256, 65535 * 4); }
@@ -1052,13 +1105,18 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
   {
     const int nblk = (p.N + 63) / 64;
     const size_t lds = dkdv_lds(p);
-    auto kern = k_bwd_dkdv<T, QT, G, DH>;
+    auto kern = k_bwd_dkdv<T, G, DH>;
     if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
       return err;
-    hipLaunchKernelGGL(kern, dim3(nblk, (unsigned)bg), dim3(256), lds, st,
-                       (const T*)q, (const QT*)qsrc, (const T*)k, (const T*)v, (const T*)dO, lse,
-                       w.Dv, w.off, w.lst, w.ds, w.beta, w.delta, dk, dv, dkL, de, p.N, p.Hkv, p.K,
-                       p.W, p.S, p.scale, p.C);
+    hipLaunchKernelGGL(kern, dim3(nblk, (unsigned)bg), dim3(256), lds, st, (const T*)q, (const T*)k,
+                       (const T*)v, (const T*)dO, lse, w.Dv, w.off, w.lst, w.ds, w.beta, w.delta,
+                       dk, dv, dkL, de, p.N, p.Hkv, p.K, p.W, p.scale, p.C);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (p.r > 0 && p.C > 0) {
+    hipLaunchKernelGGL(k_bwd_dklu<T>, dim3(p.C, (unsigned)bg), dim3(256), 0, st, w.off, w.lst, w.ds,
+                       (const float*)w.u, (const T*)w.W_up, dkL, p.N, p.Hkv, G, p.K, p.C, p.d, p.r,
+                       p.scale);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
@@ -1093,6 +1151,7 @@ hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v
                       float* dW_up, float* dh, void* ws, hipStream_t st) {
   BwdWs w;
   carve(p, ws, &w);
+  w.W_up = W_up;
   const bool qc = p.r > 0;
   hipError_t err;
   if (qc) {

@@ -165,8 +165,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
   __shared__ int ctr;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int tile = ntiles - 1 - blockIdx.x;
-  const int bg = blockIdx.y;
+  int tx, bg;
+  xcd_block(tx, bg);
+  const int tile = ntiles - 1 - tx;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   const int p0 = tile * TP;

@@ -96,6 +96,22 @@ __device__ __forceinline__ int n_distant(int i, int W, int S) {
   return x <= 0 ? 0 : x / S;
 }
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// linear id. xcd_block renumbers a 2-D grid (x fastest) so that every XCD
+// walks one contiguous range of it: the x-neighbours of one y, which read the
+// same (b, kv head) keys, values and queries, then share an L2.
+constexpr int NXCD = 8;
+__device__ __forceinline__ void xcd_block(int& x, int& y) {
+  const int gx = gridDim.x;
+  const int T = gx * gridDim.y;
+  const int L = blockIdx.x + gx * blockIdx.y;
+  const int xcd = L % NXCD, k = L / NXCD;
+  const int q = T / NXCD, rem = T % NXCD;
+  const int Lp = xcd * q + min(xcd, rem) + k;
+  y = Lp / gx;
+  x = Lp - y * gx;
+}
+
 // cross-lane helpers (lanes xor-ed within the wave)
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, WAVE); }
 

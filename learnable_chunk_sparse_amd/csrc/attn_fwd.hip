@@ -140,9 +140,9 @@ struct RowFrags {
 template <typename T, int G, int DH, int CB>
 __global__ __launch_bounds__(256) void k_attn_fwd(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score, T* __restrict__ o,
-    float* __restrict__ lse, int N, int Np, int Hkv, int K, int W, int S, float scale, int ntiles,
-    int C) {
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score,
+    const float* __restrict__ sel_lse, T* __restrict__ o, float* __restrict__ lse, int N, int Np,
+    int Hkv, int K, int W, int S, float scale, int ntiles, int C) {
   typedef typename Frag<T>::type FT;
   constexpr int R = 64 * CB;        // rows per tile
   constexpr int TP = R / G;         // positions per tile
@@ -232,6 +232,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
     const int pw_hi = min(p0 + (rbase + 16 * CB - 1) / G, N - 1);
     FT qf[CB][KS];
     int prow[CB], wsr[CB];
+    float lsel[CB];  // log-sum-exp of the row's selected chunk scores
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int r = rbase + 16 * cb + (lane & 15);
@@ -239,6 +240,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
       prow[cb] = pos < N ? pos : -1;
       wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
       const int pc = pos < N ? pos : N - 1;
+      lsel[cb] = sel_lse[((size_t)b * Hq + g * G + hh) * N + pc];
       const T* src = q + (((size_t)b * Hq + g * G + hh) * N + pc) * DH + 8 * (lane >> 4);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld8<T>(src + 32 * ks);
@@ -359,23 +361,11 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
       const int hh = r % G;
       const int pc = prow[cb] >= 0 ? prow[cb] : N - 1;
       const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + pc;
-      const int32_t* ti = topk_idx + ((size_t)bg * N + pc) * K;
-      const float* ts = topk_score + rowoff * K;
       const float lW = (m[cb] + __log2f(ls)) * LN2;  // natural log-sum-exp of the window
-      // the four lanes holding this row each reduce a quarter of its slots
-      float mx = lW;
-      for (int kk = lane >> 4; kk < K; kk += 4)
-        if (ti[kk] >= 0) mx = fmaxf(mx, ts[kk]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      float tot = 0.f;
-      for (int kk = lane >> 4; kk < K; kk += 4)
-        if (ti[kk] >= 0) tot += __expf(ts[kk] - mx);
-      tot += shfl_xor(tot, 16);
-      tot += shfl_xor(tot, 32);
-      tot += __expf(lW - mx);
+      // L = log(exp(lW) + sum over the selected chunks of exp(s_c))
+      const float mx = fmaxf(lW, lsel[cb]);
       const bool live = prow[cb] >= 0;
-      const float L = live ? mx + __logf(tot) : 0.f;
+      const float L = live ? mx + __logf(__expf(lW - mx) + __expf(lsel[cb] - mx)) : 0.f;
       const float coef = live ? fast_exp2(m[cb] - L * LOG2E) : 0.f;
       if ((lane >> 4) == 0) {
         Ls[r] = L;
@@ -498,19 +488,24 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
   }
   __syncthreads();
 
-  // ------------------------------------------------ write o
-  for (int x = tid; x < R * DH / 4; x += 256) {
-    const int r = x / (DH / 4), d4 = 4 * (x - r * (DH / 4));
+  // ------------------------------------------------ write o (8 elements per thread)
+  for (int x = tid; x < R * DH / 8; x += 256) {
+    const int r = x / (DH / 8), d8 = 8 * (x - r * (DH / 8));
     const int pos = p0 + r / G, hh = r % G;
-    const int a0 = r * RS + d4;
-    const f32x4 sum = *reinterpret_cast<const f32x4*>(accT + a0) +
-                      *reinterpret_cast<const f32x4*>(accT + R * RS + a0) +
-                      *reinterpret_cast<const f32x4*>(accT + 2 * R * RS + a0) +
-                      *reinterpret_cast<const f32x4*>(accT + 3 * R * RS + a0);
-    if (pos < N) {
-      T* dst = o + (((size_t)b * Hq + g * G + hh) * N + pos) * DH + d4;
+    float sum[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = from_f<T>(sum[j]);
+    for (int h4 = 0; h4 < 2; ++h4) {
+      const int a0 = r * RS + d8 + 4 * h4;
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(accT + a0) +
+                       *reinterpret_cast<const f32x4*>(accT + R * RS + a0) +
+                       *reinterpret_cast<const f32x4*>(accT + 2 * R * RS + a0) +
+                       *reinterpret_cast<const f32x4*>(accT + 3 * R * RS + a0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[4 * h4 + j] = s4[j];
+    }
+    if (pos < N) {
+      T* dst = o + (((size_t)b * Hq + g * G + hh) * N + pos) * DH + d8;
+      *reinterpret_cast<typename Frag<T>::type*>(dst) = pack8<T>(sum);
     }
   }
 }
@@ -530,7 +525,8 @@ template <> struct FwdCB<uint16_t, 64> { static constexpr int v = 2; };
 
 template <typename T, int G, int DH>
 static hipError_t fwd_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                         const int32_t* idx, const float* sc, void* o, float* lse, hipStream_t st) {
+                         const int32_t* idx, const float* sc, const float* sl, void* o, float* lse,
+                         hipStream_t st) {
   constexpr int CB = FwdCB<T, DH>::v;
   constexpr int TP = 64 * CB / G;
   const int ntiles = (p.N + TP - 1) / TP;
@@ -539,7 +535,7 @@ static hipError_t fwd_go(const Dims& p, const void* q, const void* k, const void
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const T*)q, (const T*)k,
-                     (const T*)vt, idx, sc, (T*)o, lse, p.N, Np, p.Hkv, p.K, p.W, p.S, p.scale,
+                     (const T*)vt, idx, sc, sl, (T*)o, lse, p.N, Np, p.Hkv, p.K, p.W, p.S, p.scale,
                      ntiles, p.C);
   return hipGetLastError();
 }
@@ -553,17 +549,18 @@ static hipError_t vt_go(const Dims& p, const void* v, void* vt, int Np, hipStrea
 
 template <typename T>
 static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void* v, void* vt,
-                        const int32_t* idx, const float* sc, void* o, float* lse, hipStream_t st) {
+                        const int32_t* idx, const float* sc, const float* sl, void* o, float* lse,
+                        hipStream_t st) {
   const int Np = (p.N + 63) / 64 * 64;
   hipError_t err = p.d == 64 ? vt_go<T, 64>(p, v, vt, Np, st) : vt_go<T, 128>(p, v, vt, Np, st);
   if (err != hipSuccess) return err;
   switch (p.G * 1000 + p.d) {
-    case 1064: return fwd_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, o, lse, st);
-    case 1128: return fwd_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, o, lse, st);
-    case 2064: return fwd_go<T, 2, 64>(p, q, k, vt, Np, idx, sc, o, lse, st);
-    case 2128: return fwd_go<T, 2, 128>(p, q, k, vt, Np, idx, sc, o, lse, st);
-    case 4064: return fwd_go<T, 4, 64>(p, q, k, vt, Np, idx, sc, o, lse, st);
-    case 4128: return fwd_go<T, 4, 128>(p, q, k, vt, Np, idx, sc, o, lse, st);
+    case 1064: return fwd_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
+    case 1128: return fwd_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
+    case 2064: return fwd_go<T, 2, 64>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
+    case 2128: return fwd_go<T, 2, 128>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
+    case 4064: return fwd_go<T, 4, 64>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
+    case 4128: return fwd_go<T, 4, 128>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -593,10 +590,10 @@ size_t attn_fwd_vt_bytes(const Dims& p) {
 }
 
 hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v, void* vt,
-                           const int32_t* topk_idx, const float* topk_score, void* o, float* lse,
-                           hipStream_t st) {
-  if (p.dtype == 1) return fwd_t<uint16_t>(p, q, k, v, vt, topk_idx, topk_score, o, lse, st);
-  return fwd_t<float>(p, q, k, v, vt, topk_idx, topk_score, o, lse, st);
+                           const int32_t* topk_idx, const float* topk_score, const float* sel_lse,
+                           void* o, float* lse, hipStream_t st) {
+  if (p.dtype == 1) return fwd_t<uint16_t>(p, q, k, v, vt, topk_idx, topk_score, sel_lse, o, lse, st);
+  return fwd_t<float>(p, q, k, v, vt, topk_idx, topk_score, sel_lse, o, lse, st);
 }
 
 }  // namespace hils

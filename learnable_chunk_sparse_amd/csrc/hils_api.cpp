@@ -86,6 +86,7 @@ Dims dims_of(const hils_problem* p) {
 struct FwdWs {
   float* qhat;
   float* s_T;
+  float* sel_lse;
   void* vt;
 };
 size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
@@ -93,6 +94,7 @@ size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
   const size_t rows = (size_t)d.B * d.Hq * d.N;
   out->qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
   out->s_T = (float*)c.take(rows * d.K * sizeof(float));
+  out->sel_lse = (float*)c.take(rows * sizeof(float));
   out->vt = c.take(hils::attn_fwd_vt_bytes(d));
   return c.used;
 }
@@ -211,9 +213,9 @@ hils_status hils_route(const hils_problem* p, const void* q, const void* kL, con
   if (d.r > 0) {
     if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
       return s;
-    return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, qhat, true, kL, e, topk_idx, topk_score, st); }));
+    return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, qhat, true, kL, e, topk_idx, topk_score, nullptr, st); }));
   }
-  return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, st); }));
+  return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, nullptr, st); }));
 }
 
 hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, const void* v,
@@ -234,12 +236,12 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
   if (d.r > 0) {
     if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, w.qhat, nullptr, st); }))) != HILS_OK)
       return s;
-    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, w.s_T, st); }));
+    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, w.s_T, w.sel_lse, st); }));
   } else {
-    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, w.s_T, st); }));
+    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, w.s_T, w.sel_lse, st); }));
   }
   if (s != HILS_OK) return s;
-  return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, o, lse, st); }));
+  return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
 }
 
 hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,

@@ -25,13 +25,13 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
 // top-K. qs: scoring queries ([B, Hq, N, d], fp32 when q_is_f32 else in the
 // input dtype). Writes topk_idx and, if non-null, topk_score.
 hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void* kL, const void* e,
-                        int32_t* topk_idx, float* topk_score, hipStream_t st);
+                        int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st);
 
 // Fused window attention + selected-chunk attention + fusion.
 // vt: workspace for the transposed, token-permuted copy of V (attn_fwd_vt_bytes).
 hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v, void* vt,
-                           const int32_t* topk_idx, const float* topk_score, void* o, float* lse,
-                           hipStream_t st);
+                           const int32_t* topk_idx, const float* topk_score, const float* sel_lse,
+                           void* o, float* lse, hipStream_t st);
 size_t attn_fwd_lds_bytes(const Dims& p);
 size_t attn_fwd_vt_bytes(const Dims& p);
 

@@ -72,7 +72,8 @@ struct TopK {
 template <typename T, typename QT, int G, int DH, int KC>
 __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                const T* __restrict__ e, int32_t* __restrict__ topk_idx,
-                                               float* __restrict__ topk_score, int N, int C, int Hkv,
+                                               float* __restrict__ topk_score,
+                                               float* __restrict__ sel_lse, int N, int C, int Hkv,
                                                int K, int W, int S, float scale, int ntiles) {
   typedef typename Frag<T>::type FT;
   constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
@@ -257,10 +258,21 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float* ds = topk_score + (((size_t)b * Hq + g * G + hh) * N + mypos) * K;
+        // log-sum-exp of the head's selected scores (-inf when none is valid)
+        float lm = NEG_INF, ls = 0.f;
+        auto lse_add = [&](float x) __attribute__((always_inline)) {
+          const float mn = fmaxf(lm, x);
+          ls = ls * __expf(lm - mn) + __expf(x - mn);
+          lm = mn;
+        };
         if constexpr (G == 1) {
 #pragma unroll
           for (int k = 0; k < KC; ++k)
-            if (k < K) ds[k] = ids[k] == 0x7FFFFFFF ? __builtin_nanf("") : sv[k];
+            if (k < K) {
+              const bool ok = ids[k] != 0x7FFFFFFF;
+              ds[k] = ok ? sv[k] : __builtin_nanf("");
+              if (ok) lse_add(sv[k]);
+            }
         } else {
           const QT* qh = qs + (((size_t)b * Hq + g * G + hh) * N + mypos) * DH;
           for (int k = 0; k < K; ++k) {
@@ -277,8 +289,11 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
               for (int j = 0; j < 8; ++j) a = fmaf(to_f<QT>(qh[dd + j]), (float)kv[j], a);
             }
             ds[k] = fmaf(a, scale, to_f<T>(eg[ck]));
+            lse_add(ds[k]);
           }
         }
+        if (sel_lse != nullptr)
+          sel_lse[((size_t)b * Hq + g * G + hh) * N + mypos] = lm == NEG_INF ? NEG_INF : lm + __logf(ls);
       }
     }
   }
@@ -286,50 +301,50 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
 
 template <typename T, typename QT, int G, int DH, int KC>
 static hipError_t route_go(const Dims& p, const void* qs, const void* kL, const void* e,
-                           int32_t* idx, float* sc, hipStream_t st) {
+                           int32_t* idx, float* sc, float* sl, hipStream_t st) {
   constexpr int PWG = 4 * 16 * (G >= 4 ? 1 : 4 / G);
   const int ntiles = (p.N + PWG - 1) / PWG;
   auto kern = k_route<T, QT, G, DH, KC>;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), 0, st, (const QT*)qs,
-                     (const T*)kL, (const T*)e, idx, sc, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
+                     (const T*)kL, (const T*)e, idx, sc, sl, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
                      ntiles);
   return hipGetLastError();
 }
 
 template <typename T, typename QT, int G, int DH>
 static hipError_t route_k(const Dims& p, const void* qs, const void* kL, const void* e,
-                          int32_t* idx, float* sc, hipStream_t st) {
-  if (p.K <= 4) return route_go<T, QT, G, DH, 4>(p, qs, kL, e, idx, sc, st);
-  if (p.K <= 8) return route_go<T, QT, G, DH, 8>(p, qs, kL, e, idx, sc, st);
-  if (p.K <= 16) return route_go<T, QT, G, DH, 16>(p, qs, kL, e, idx, sc, st);
-  return route_go<T, QT, G, DH, 32>(p, qs, kL, e, idx, sc, st);
+                          int32_t* idx, float* sc, float* sl, hipStream_t st) {
+  if (p.K <= 4) return route_go<T, QT, G, DH, 4>(p, qs, kL, e, idx, sc, sl, st);
+  if (p.K <= 8) return route_go<T, QT, G, DH, 8>(p, qs, kL, e, idx, sc, sl, st);
+  if (p.K <= 16) return route_go<T, QT, G, DH, 16>(p, qs, kL, e, idx, sc, sl, st);
+  return route_go<T, QT, G, DH, 32>(p, qs, kL, e, idx, sc, sl, st);
 }
 
 template <typename T, typename QT, int G>
 static hipError_t route_d(const Dims& p, const void* qs, const void* kL, const void* e, int32_t* idx,
-                          float* sc, hipStream_t st) {
-  if (p.d == 64) return route_k<T, QT, G, 64>(p, qs, kL, e, idx, sc, st);
-  return route_k<T, QT, G, 128>(p, qs, kL, e, idx, sc, st);
+                          float* sc, float* sl, hipStream_t st) {
+  if (p.d == 64) return route_k<T, QT, G, 64>(p, qs, kL, e, idx, sc, sl, st);
+  return route_k<T, QT, G, 128>(p, qs, kL, e, idx, sc, sl, st);
 }
 
 template <typename T, typename QT>
 static hipError_t route_g(const Dims& p, const void* qs, const void* kL, const void* e, int32_t* idx,
-                          float* sc, hipStream_t st) {
+                          float* sc, float* sl, hipStream_t st) {
   switch (p.G) {
-    case 1: return route_d<T, QT, 1>(p, qs, kL, e, idx, sc, st);
-    case 2: return route_d<T, QT, 2>(p, qs, kL, e, idx, sc, st);
-    case 4: return route_d<T, QT, 4>(p, qs, kL, e, idx, sc, st);
+    case 1: return route_d<T, QT, 1>(p, qs, kL, e, idx, sc, sl, st);
+    case 2: return route_d<T, QT, 2>(p, qs, kL, e, idx, sc, sl, st);
+    case 4: return route_d<T, QT, 4>(p, qs, kL, e, idx, sc, sl, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void* kL, const void* e,
-                        int32_t* topk_idx, float* topk_score, hipStream_t st) {
+                        int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st) {
   if (p.dtype == 1) {
-    if (q_is_f32) return route_g<uint16_t, float>(p, qs, kL, e, topk_idx, topk_score, st);
-    return route_g<uint16_t, uint16_t>(p, qs, kL, e, topk_idx, topk_score, st);
+    if (q_is_f32) return route_g<uint16_t, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, st);
+    return route_g<uint16_t, uint16_t>(p, qs, kL, e, topk_idx, topk_score, sel_lse, st);
   }
-  return route_g<float, float>(p, qs, kL, e, topk_idx, topk_score, st);
+  return route_g<float, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, st);
 }
 
 }  // namespace hils

@@ -58,9 +58,9 @@ def test_validation_codes(kw, code):
     assert st == code, (kw, st)
 
 
-def test_fp32_d128_backward_is_unsupported():
-    st, _ = ws(prob(dtype=0, d=128), L.OP_BWD)
-    assert st == 2
+def test_fp32_d128_backward_has_a_workspace():
+    st, nbytes = ws(prob(dtype=0, d=128), L.OP_BWD)
+    assert st == 0 and nbytes > 0
 
 
 def test_calls_reject_before_launch():

@@ -39,6 +39,7 @@ SMALL = [
     ("gqa4_d128_qcal", "bf16", 1, 8, 2, 128, 1100, 6, 256, 128, 32, 3.0),
     ("gqa2_d64", "bf16", 1, 4, 2, 64, 900, 5, 192, 0, 0, 8.0),
     ("fp32_d64_qcal", "fp32", 1, 2, 1, 64, 600, 3, 64, 64, 32, 1.0),
+    ("fp32_d128_gqa2_r16", "fp32", 1, 4, 2, 128, 500, 4, 128, 64, 16, 1.0),
 ]
 
 

@@ -183,11 +183,6 @@ __global__ __launch_bounds__(256) void k_inv_fill(const int32_t* __restrict__ to
 }
 
 // --------------------------------------------------------------- helpers
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type pk8(const f32x4& s0, const f32x4& s1) {
-  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  return pack8<T>(x);
-}
 
 __device__ int bwd_block_scan(int* a, int n, int* wsum) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;

@@ -14,22 +14,27 @@
 // Products use the transposed form S^T = K Q^T (tokens x rows), whose
 // accumulator layout is exactly the P^T operand of O^T = V^T P^T once the
 // token order inside each 32-token step is permuted identically on both
-// operands. V is transposed once per call into a token-permuted copy
-// (k_vt_perm), after which every MFMA operand is one aligned 16-byte global
-// load: no LDS staging, and the next key block / chunk is prefetched into a
-// second register set while the current one is multiplied.
+// operands; V is transposed once per call into a token-permuted copy
+// (k_vt_perm).
 //
-// Tile: R = 64 * CB rows = TP positions x G heads of one (batch, KV head),
-// four waves.
-//   Window phase: wave w runs a banded flash attention over its 16*CB rows.
-//     The fusion normaliser L follows from lse_W and the selected scores, and
-//     exp(lse_W - L) O_W seeds an fp32 row accumulator in LDS.
-//   Chunk phase: the tile's (position, slot) selections are bucketed by chunk
-//     (counting sort in LDS). Waves take chunks dynamically; a chunk's K and
-//     V^T fragments are loaded once and reused by all its row blocks (16 rows
-//     = 16/G positions x G heads), each adding exp(s_c - L) O_c to the rows'
-//     accumulators with LDS atomics. This compaction keeps MFMA columns
-//     filled even when adjacent queries choose different chunks.
+// Shared-block strategy (this file): a tile is 128 rows (128/G positions x G
+// heads) of one (batch, KV head); wave w owns rows 32w .. 32w+31 and keeps
+// their output accumulators in registers. The tile's work is a list of
+// 64-token blocks: its window blocks, then the union of the chunks its rows
+// selected (ascending). Each block's K and V^T are staged once into an LDS
+// slot (two slots; the next blocks' global loads are in flight in registers
+// while the current one is multiplied) and read by all four waves.
+//   Window blocks: banded flash attention of each wave's rows (blocks outside
+//     a wave's windows are skipped, masks only on edge blocks).
+//   After the window: L = log(exp(lse_W) + exp(lse_sel)) with lse_sel the
+//     log-sum-exp of the row's selected scores, and the window output is
+//     scaled by exp(lse_W - L).
+//   Chunk blocks: every row keeps a cursor into its ascending selection list;
+//     row blocks where no row selected the chunk are skipped, the others add
+//     exp(s_c - L) O_c (rows that did not select it get weight 0).
+// With no per-wave accumulator copies the tile needs ~55 KB of LDS (d = 64),
+// so two tiles share a CU. Tiles whose selections are spread over many more
+// chunks than they select use the bucketed strategy of attn_fwd_sparse.hip.
 #include "hils_common.h"
 #include "hils_internal.h"
 
@@ -69,102 +74,46 @@ template __global__ void k_vt_perm<uint16_t, 128>(const uint16_t*, uint16_t*, in
 template __global__ void k_vt_perm<float, 64>(const float*, float*, int, int);
 template __global__ void k_vt_perm<float, 128>(const float*, float*, int, int);
 
-// In-place exclusive scan of a[0..n) by the whole block (256 threads); returns the total.
-__device__ int block_excl_scan(int* a, int n, int* wsum) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int seg = (n + 255) / 256;
-  const int lo = min(n, t * seg), hi = min(n, lo + seg);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += a[i];
-  int v = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  int base = v - s;
-  for (int j = 0; j < w; ++j) base += wsum[j];
-  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  for (int i = lo; i < hi; ++i) {
-    const int x = a[i];
-    a[i] = base;
-    base += x;
-  }
-  __syncthreads();
-  return total;
-}
-
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type p_frag(const f32x4& s0, const f32x4& s1) {
-  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  return pack8<T>(x);
-}
-
+// LDS slot holding one 64-token block: K rows and V^T rows (token-permuted),
+// pitches padded by 16 bytes so the 16-byte fragment reads of 16 lanes hit
+// distinct banks.
 template <typename T, int DH>
-struct BlockFrags {
-  typename Frag<T>::type k[4][DH / 32];  // A operand of S^T: K rows (tokens)
-  typename Frag<T>::type v[DH / 16][2];  // A operand of O^T: V^T rows (dims)
+struct Slot {
+  static constexpr int VE = 16 / (int)sizeof(T);         // elements per 16-byte vector
+  static constexpr int KP = DH + VE;                      // K row pitch
+  static constexpr int VP = 64 + VE;                      // V^T row pitch
+  static constexpr int KE = 64 * KP;                      // K part (elements)
+  static constexpr int ELEMS = KE + DH * VP;
+  static constexpr int KV = 64 * DH / VE;                 // 16-byte vectors of K
+  static constexpr int VPT = 2 * KV / 256;                // vectors per thread (K then V^T)
 };
 
-// K rows kbase + 16*tb + lane%16 (clamped below nvalid) and the permuted V^T
-// columns vtbase + 32*ks + 8*(lane/16) of dims 16*mb + lane%16.
-template <typename T, int DH>
-__device__ __forceinline__ void load_block(BlockFrags<T, DH>& f, const T* __restrict__ kbase, int nvalid,
-                                           const T* __restrict__ vtbase, int Np, int lane) {
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    int tok = 16 * tb + (lane & 15);
-    tok = tok < nvalid ? tok : 0;
-    const T* src = kbase + (size_t)tok * DH + 8 * (lane >> 4);
-#pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) f.k[tb][ks] = ld8<T>(src + 32 * ks);
-  }
-#pragma unroll
-  for (int mb = 0; mb < DH / 16; ++mb) {
-    const T* src = vtbase + (size_t)(16 * mb + (lane & 15)) * Np + 8 * (lane >> 4);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) f.v[mb][ks] = ld8<T>(src + 32 * ks);
-  }
-}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int DH>
-struct RowFrags {
-  typename Frag<T>::type q[DH / 32];
-  float s;     // fusion score of the row's chunk
-  int row;     // tile row
-  bool valid;
-};
-
-template <typename T, int G, int DH, int CB>
-__global__ __launch_bounds__(256) void k_attn_fwd(
+template <typename T, int G, int DH>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_attn_fwd(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score,
     const float* __restrict__ sel_lse, T* __restrict__ o, float* __restrict__ lse, int N, int Np,
     int Hkv, int K, int W, int S, float scale, int ntiles, int C) {
   typedef typename Frag<T>::type FT;
-  constexpr int R = 64 * CB;        // rows per tile
-  constexpr int TP = R / G;         // positions per tile
+  typedef Slot<T, DH> SG;
+  constexpr int R = 128;      // rows per tile: 2 row blocks of 16 per wave
+  constexpr int TP = R / G;   // positions per tile
   constexpr int KS = DH / 32;
   constexpr int MB = DH / 16;
-  constexpr int RS = DH + 4;        // accumulator row stride (floats)
-  constexpr int EPT = TP * 32 / 256;  // max entries per thread (K <= 32)
-  constexpr bool PF = DH == 64;     // double-buffered prefetch (register budget)
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // one accumulator copy per wave: waves add their chunk contributions to
-  // their own copy with plain read-modify-write (no LDS atomics), and the
-  // copies are summed when the tile is written out
-  float* accT = reinterpret_cast<float*>(smem);          // [4][R][RS]
-  float* Ls = accT + 4 * R * RS;                         // [R]
-  int* off = reinterpret_cast<int*>(Ls + R);             // [C + 1] counts -> offsets
-  int* nzl = off + C + 1;                                // [C] ranks -> nonempty chunk ids
-  uint16_t* ent = reinterpret_cast<uint16_t*>(nzl + C);  // [TP*K]
+  T* slots = reinterpret_cast<T*>(smem);                             // [2][ELEMS]
+  int* tkc = reinterpret_cast<int*>(slots + 2 * SG::ELEMS);          // [TP][K] selected chunks
+  float* tks = reinterpret_cast<float*>(tkc + TP * K);              // [R][K] their scores
+  int* flg = reinterpret_cast<int*>(tks + R * K);                   // [C + 1] union flags / offsets
+  int* ulist = flg + C + 1;                                         // [min(C, TP K)] union, ascending
   __shared__ int wsum[4];
-  __shared__ int ctr;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gl = lane >> 4, cl = lane & 15;
   int tx, bg;
   xcd_block(tx, bg);
   const int tile = ntiles - 1 - tx;
@@ -172,242 +121,240 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
   const int Hq = Hkv * G;
   const int p0 = tile * TP;
   const int plast = min(p0 + TP - 1, N - 1);
-  const int ndmax = n_distant(plast, W, S);  // chunks any row of the tile can select
+  const int ndmax = n_distant(plast, W, S);
   const T* kg = k + (size_t)bg * N * DH;
   const T* vtg = vt + (size_t)bg * DH * Np;
-  float* accW = accT + w * R * RS;  // this wave's accumulator copy
 
-  // ------------------------------------------------ bucket selections by chunk
-  for (int x = tid; x <= ndmax; x += 256) off[x] = 0;
-  if (tid == 0) ctr = 0;
-  for (int x = tid; x < R * RS; x += 256) reinterpret_cast<f32x4*>(accT)[x] = zero4();
+  // ------------------------------------------------ selections of the tile
+  for (int x = tid; x <= ndmax; x += 256) flg[x] = 0;
+  for (int x = tid; x < TP * K; x += 256) {
+    const int pos = p0 + x / K;
+    tkc[x] = pos < N ? topk_idx[((size_t)bg * N + p0) * K + x] : -1;
+  }
+  for (int x = tid; x < R * K; x += 256) {
+    const int r = x / K, kk = x - r * K;
+    const int pos = p0 + r / G;
+    tks[x] = pos < N ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
+  }
   __syncthreads();
-  int my_c[EPT], my_r[EPT];
-  const int E = TP * K;
+  for (int x = tid; x < TP * K; x += 256) {
+    const int c = tkc[x];
+    if (c >= 0 && c < ndmax) flg[c] = 1;
+  }
+  __syncthreads();
+  // union of the selected chunks, ascending: flg becomes offsets, ulist the ids
+  int NU = 0;
+  if (ndmax > 0) {
+    NU = block_excl_scan(flg, ndmax, wsum);
+    if (tid == 0) flg[ndmax] = NU;
+    __syncthreads();
+    for (int c = tid; c < ndmax; c += 256)
+      if (flg[c + 1] > flg[c]) ulist[flg[c]] = c;
+  }
+
+  // ------------------------------------------------ per-lane rows
+  // wave w owns rows 32 w + 16 cb + cl, cb = 0, 1 (all four lanes of a
+  // column hold the same row)
+  FT qf[2][KS];
+  int prow[2], wsr[2], plc[2], rr[2], cur[2];
+  size_t rowoff[2];
+  float lsel[2], Lr[2];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int x = tid + 256 * j;
-    my_c[j] = -1;
-    my_r[j] = 0;
-    if (x < E) {
-      const int pl = x / K, kk = x - pl * K;
-      const int pos = p0 + pl;
-      const int c = pos < N ? topk_idx[((size_t)bg * N + pos) * K + kk] : -1;
-      if (c >= 0 && c < ndmax) {
-        my_c[j] = c;
-        my_r[j] = atomicAdd(&off[c], 1);
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = 32 * w + 16 * cb + cl;
+    const int pos = p0 + r / G, hh = r % G;
+    rr[cb] = r;
+    plc[cb] = r / G;
+    prow[cb] = pos < N ? pos : -1;
+    wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
+    const int pc = pos < N ? pos : N - 1;
+    rowoff[cb] = ((size_t)b * Hq + g * G + hh) * N + pc;
+    lsel[cb] = sel_lse[rowoff[cb]];
+    cur[cb] = 0;
+    const T* src = q + rowoff[cb] * DH + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld8<T>(src + 32 * ks);
+  }
+  // rows of this wave: positions pw_lo .. pw_hi; masks are needed on blocks
+  // that are not strictly inside every row's window
+  const int pw_lo = p0 + 32 * w / G;
+  const int pw_hi = min(p0 + (32 * w + 31) / G, N - 1);
+  const bool wave_live = pw_lo < N;
+  const bool all_valid = p0 + (32 * w + 31) / G < N;
+  const int ws_lo = wave_live ? n_distant(pw_lo, W, S) * S : 0;
+  const int ws_hi = wave_live ? n_distant(pw_hi, W, S) * S : 0;
+
+  float m[2], lsum[2];
+  f32x4 oacc[MB][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    m[cb] = NEG_INF;
+    lsum[cb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] = zero4();
+  }
+  const float sc2 = scale * LOG2E;
+
+  // ------------------------------------------------ work items
+  // items 0 .. nW-1: window blocks kv_lo + 64 n; then the NU union chunks
+  const int kv_lo = n_distant(p0, W, S) * S;
+  const int nW = (plast - kv_lo) / 64 + 1;
+  const int NIT = nW + NU;
+  auto item_kv0 = [&](int n) __attribute__((always_inline)) {
+    n = min(n, NIT - 1);
+    return n < nW ? kv_lo + 64 * n : 64 * ulist[n - nW];
+  };
+  // block staging: thread vectors s < VPT/2 are K (token, 16-byte part), the
+  // rest V^T (dim, part); two blocks are in flight in registers
+  u32x4 stg[2][SG::VPT];
+  auto issue = [&](u32x4 (&rg)[SG::VPT], int n) __attribute__((always_inline)) {
+    const int kv0 = item_kv0(n);
+#pragma unroll
+    for (int s = 0; s < SG::VPT; ++s) {
+      const int vi = tid + 256 * s;
+      const T* src;
+      if (s < SG::VPT / 2) {
+        const int tok = vi / (DH / SG::VE), part = vi - tok * (DH / SG::VE);
+        src = kg + (size_t)min(kv0 + tok, N - 1) * DH + part * SG::VE;
+      } else {
+        const int vj = vi - SG::KV;
+        const int dd = vj / (64 / SG::VE), part = vj - dd * (64 / SG::VE);
+        src = vtg + (size_t)dd * Np + kv0 + part * SG::VE;
+      }
+      rg[s] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto commit = [&](const u32x4 (&rg)[SG::VPT], int slot) __attribute__((always_inline)) {
+    T* base = slots + slot * SG::ELEMS;
+#pragma unroll
+    for (int s = 0; s < SG::VPT; ++s) {
+      const int vi = tid + 256 * s;
+      T* dst;
+      if (s < SG::VPT / 2) {
+        const int tok = vi / (DH / SG::VE), part = vi - tok * (DH / SG::VE);
+        dst = base + tok * SG::KP + part * SG::VE;
+      } else {
+        const int vj = vi - SG::KV;
+        const int dd = vj / (64 / SG::VE), part = vj - dd * (64 / SG::VE);
+        dst = base + SG::KE + dd * SG::VP + part * SG::VE;
+      }
+      *reinterpret_cast<u32x4*>(dst) = rg[s];
+    }
+  };
+
+  // ---- window block: banded flash attention over the wave's rows
+  auto window_block = [&](const T* sl, int kv0, auto masked) __attribute__((always_inline)) {
+    constexpr bool MSK = decltype(masked)::value;
+    f32x4 sacc[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const FT kf = ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = mma16(kf, qf[cb][ks], sacc[tb][cb]);
       }
     }
-  }
-  __syncthreads();
-  for (int x = tid; x < ndmax; x += 256) nzl[x] = off[x] > 0 ? 1 : 0;
-  __syncthreads();
-  const int Etot = block_excl_scan(off, ndmax, wsum);
-  const int NZ = block_excl_scan(nzl, ndmax, wsum);
-  if (tid == 0) off[ndmax] = Etot;
-  __syncthreads();
-  // ranks -> list of nonempty chunk ids (a rank never exceeds its chunk id, so
-  // reading a block of ranks before writing keeps later ranks intact)
-  for (int base = 0; base < ndmax; base += 256) {
-    const int x = base + tid;
-    const int rk = (x < ndmax && off[x + 1] > off[x]) ? nzl[x] : -1;
-    __syncthreads();
-    if (rk >= 0) nzl[rk] = x;
-    __syncthreads();
-  }
+    FT pf[2][2];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int c = my_c[j];
-    if (c >= 0) {
-      const int x = tid + 256 * j;
-      const int pl = x / K, kk = x - pl * K;
-      ent[off[c] + my_r[j]] = (uint16_t)((pl << 6) | kk);
-    }
-  }
-
-  // ------------------------------------------------ window phase
-  {
-    const int rbase = w * 16 * CB;                 // first tile row of this wave
-    const int pw_lo = p0 + rbase / G;
-    const int pw_hi = min(p0 + (rbase + 16 * CB - 1) / G, N - 1);
-    FT qf[CB][KS];
-    int prow[CB], wsr[CB];
-    float lsel[CB];  // log-sum-exp of the row's selected chunk scores
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int r = rbase + 16 * cb + (lane & 15);
-      const int pos = p0 + r / G, hh = r % G;
-      prow[cb] = pos < N ? pos : -1;
-      wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
-      const int pc = pos < N ? pos : N - 1;
-      lsel[cb] = sel_lse[((size_t)b * Hq + g * G + hh) * N + pc];
-      const T* src = q + (((size_t)b * Hq + g * G + hh) * N + pc) * DH + 8 * (lane >> 4);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld8<T>(src + 32 * ks);
-    }
-    float m[CB], lsum[CB];
-    f32x4 oacc[MB][CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      m[cb] = NEG_INF;
-      lsum[cb] = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] = zero4();
-    }
-    // rows of this wave whose window does not cover a whole block need masks;
-    // a block strictly inside every row's window is processed without them
-    int minpos = 1 << 30, maxws = 0;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      minpos = min(minpos, prow[cb] >= 0 ? prow[cb] : -1);
-      maxws = max(maxws, wsr[cb]);
-    }
-#pragma unroll
-    for (int m2 = 1; m2 < 16; m2 <<= 1) {
-      minpos = min(minpos, __shfl_xor(minpos, m2, 64));
-      maxws = max(maxws, __shfl_xor(maxws, m2, 64));
-    }
-    const float sc2 = scale * LOG2E;  // logits in base 2
-    auto compute = [&](const BlockFrags<T, DH>& f, int kv0, auto masked) __attribute__((always_inline)) {
-      f32x4 sacc[4][CB];
+    for (int cb = 0; cb < 2; ++cb) {
+      float bmax = NEG_INF;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          sacc[tb][cb] = zero4();
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) sacc[tb][cb] = mma16(f.k[tb][ks], qf[cb][ks], sacc[tb][cb]);
+        for (int i = 0; i < 4; ++i) {
+          float x = sacc[tb][cb][i] * sc2;
+          if constexpr (MSK) {
+            const int j = kv0 + 16 * tb + 4 * gl + i;
+            x = (j <= prow[cb] && j >= wsr[cb]) ? x : NEG_INF;
+          }
+          sacc[tb][cb][i] = x;
+          bmax = fmaxf(bmax, x);
         }
+      bmax = fmaxf(bmax, shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+      const float mnew = fmaxf(m[cb], bmax);
+      const float mref = mnew == NEG_INF ? 0.f : mnew;
+      const float alpha = fast_exp2(m[cb] - mref);
+      float ps = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        float bmax = NEG_INF;
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int i = 0; i < 4; ++i) {
+          const float pv = fast_exp2(sacc[tb][cb][i] - mref);
+          sacc[tb][cb][i] = pv;
+          ps += pv;
+        }
+      lsum[cb] = lsum[cb] * alpha + ps;
+      m[cb] = mnew;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sacc[tb][cb][i] * sc2;
-            if constexpr (decltype(masked)::value) {
-              const int j = kv0 + 16 * tb + 4 * (lane >> 4) + i;
-              x = (j <= prow[cb] && j >= wsr[cb]) ? x : NEG_INF;
-            }
-            sacc[tb][cb][i] = x;
-            bmax = fmaxf(bmax, x);
-          }
-        bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-        bmax = fmaxf(bmax, shfl_xor(bmax, 32));
-        const float mnew = fmaxf(m[cb], bmax);
-        const float mref = mnew == NEG_INF ? 0.f : mnew;
-        const float alpha = fast_exp2(m[cb] - mref);
-        float ps = 0.f;
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+      for (int ks = 0; ks < 2; ++ks) pf[cb][ks] = pk8<T>(sacc[2 * ks][cb], sacc[2 * ks + 1][cb]);
+    }
+    const T* vb = sl + SG::KE;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = fast_exp2(sacc[tb][cb][i] - mref);
-            sacc[tb][cb][i] = pv;
-            ps += pv;
-          }
-        lsum[cb] = lsum[cb] * alpha + ps;
-        m[cb] = mnew;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
-      }
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        FT pf[CB];
+        const FT vf = ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) pf[cb] = p_frag<T>(sacc[2 * ks][cb], sacc[2 * ks + 1][cb]);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[mb][cb] = mma16(f.v[mb][ks], pf[cb], oacc[mb][cb]);
+        for (int cb = 0; cb < 2; ++cb) oacc[mb][cb] = mma16(vf, pf[cb][ks], oacc[mb][cb]);
       }
-    };
-    auto run = [&](const BlockFrags<T, DH>& f, int kv0) __attribute__((always_inline)) {
-      const bool clean = minpos >= 0 && kv0 >= maxws && kv0 + 63 <= minpos;
-      if (clean)
-        compute(f, kv0, std::false_type());
-      else
-        compute(f, kv0, std::true_type());
-    };
-    if (pw_lo < N && !PF) {
-      const int kv_lo = n_distant(pw_lo, W, S) * S;
-      BlockFrags<T, DH> fa;
-      for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 64) {
-        load_block<T, DH>(fa, kg + (size_t)kv0 * DH, min(64, N - kv0), vtg + kv0, Np, lane);
-        run(fa, kv0);
-      }
-    } else if (pw_lo < N) {
-      const int kv_lo = n_distant(pw_lo, W, S) * S;
-      BlockFrags<T, DH> fa, fb;
-      load_block<T, DH>(fa, kg + (size_t)kv_lo * DH, min(64, N - kv_lo), vtg + kv_lo, Np, lane);
-      for (int kv0 = kv_lo; kv0 <= pw_hi; kv0 += 128) {
-        const int k1 = kv0 + 64;
-        if (k1 <= pw_hi) load_block<T, DH>(fb, kg + (size_t)k1 * DH, min(64, N - k1), vtg + k1, Np, lane);
-        run(fa, kv0);
-        if (k1 > pw_hi) break;
-        const int k2 = kv0 + 128;
-        if (k2 <= pw_hi) load_block<T, DH>(fa, kg + (size_t)k2 * DH, min(64, N - k2), vtg + k2, Np, lane);
-        run(fb, k1);
-      }
-    }
-    // window log-sum-exp, fusion normaliser, window contribution
+  };
+
+  // ---- fusion normaliser once the window is done: L, and the window weight
+  auto fuse = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int cb = 0; cb < 2; ++cb) {
       float ls = lsum[cb];
       ls += shfl_xor(ls, 16);
       ls += shfl_xor(ls, 32);
-      const int r = rbase + 16 * cb + (lane & 15);
-      const int hh = r % G;
-      const int pc = prow[cb] >= 0 ? prow[cb] : N - 1;
-      const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + pc;
-      const float lW = (m[cb] + __log2f(ls)) * LN2;  // natural log-sum-exp of the window
-      // L = log(exp(lW) + sum over the selected chunks of exp(s_c))
+      const float lW = (m[cb] + __log2f(ls)) * LN2;
       const float mx = fmaxf(lW, lsel[cb]);
       const bool live = prow[cb] >= 0;
       const float L = live ? mx + __logf(__expf(lW - mx) + __expf(lsel[cb] - mx)) : 0.f;
       const float coef = live ? fast_exp2(m[cb] - L * LOG2E) : 0.f;
-      if ((lane >> 4) == 0) {
-        Ls[r] = L;
-        if (live) lse[rowoff] = L;
-      }
+      Lr[cb] = L;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        *reinterpret_cast<f32x4*>(accW + r * RS + 16 * mb + 4 * (lane >> 4)) = oacc[mb][cb] * coef;
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= coef;
     }
-  }
-  __syncthreads();
+  };
 
-  // ------------------------------------------------ chunk phase
-  {
-    auto grab = [&]() __attribute__((always_inline)) {
-      int it = 0;
-      if (lane == 0) it = atomicAdd(&ctr, 1);
-      return __shfl(it, 0, 64);
-    };
-    // row fragments of row block cbk of a chunk whose entries are e0 .. e0 + n
-    auto load_rows = [&](RowFrags<T, DH>& rf, int e0, int n, int cbk) __attribute__((always_inline)) {
-      const int rr = 16 * cbk + (lane & 15);
-      rf.valid = rr < n * G;
-      const int ei = (rf.valid ? rr : 0) / G, hh = (rf.valid ? rr : 0) % G;
-      const int en = ent[e0 + ei];
-      const int pl = en >> 6, kk = en & 63;
-      rf.row = pl * G + hh;
-      const size_t rowoff = ((size_t)b * Hq + g * G + hh) * N + p0 + pl;
-      const T* src = q + rowoff * DH + 8 * (lane >> 4);
+  // ---- chunk block: rows that selected chunk c add exp(s_c - L) O_c
+  auto chunk_block = [&](const T* sl, int c) __attribute__((always_inline)) {
+    bool sel[2];
+    float sc[2];
+    unsigned long long anysel = 0;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) rf.q[ks] = ld8<T>(src + 32 * ks);
-      rf.s = topk_score[rowoff * K + kk];
-    };
-    auto process_rows = [&](const BlockFrags<T, DH>& f, const RowFrags<T, DH>& rf) __attribute__((always_inline)) {
+    for (int cb = 0; cb < 2; ++cb) {
+      const int kk = min(cur[cb], K - 1);
+      const int kc = (prow[cb] >= 0 && cur[cb] < K) ? tkc[plc[cb] * K + kk] : -1;
+      sel[cb] = kc == c;
+      sc[cb] = tks[rr[cb] * K + kk];
+      cur[cb] += sel[cb] ? 1 : 0;
+    }
+    const unsigned long long b0 = __ballot(sel[0]), b1 = __ballot(sel[1]);
+    anysel = b0 | b1;
+    if (anysel == 0) return;
+    FT kf[4][KS];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks);
+    const T* vb = sl + SG::KE;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      if ((cb == 0 ? b0 : b1) == 0) continue;
       f32x4 sacc[4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         sacc[tb] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(f.k[tb][ks], rf.q[ks], sacc[tb]);
+        for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(kf[tb][ks], qf[cb][ks], sacc[tb]);
       }
-      const float sc2 = scale * LOG2E;
       float mx = NEG_INF;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
@@ -432,106 +379,80 @@ __global__ __launch_bounds__(256) void k_attn_fwd(
       for (int mb = 0; mb < MB; ++mb) oc[mb] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const FT pf = p_frag<T>(sacc[2 * ks], sacc[2 * ks + 1]);
+        const FT pf = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) oc[mb] = mma16(f.v[mb][ks], pf, oc[mb]);
+        for (int mb = 0; mb < MB; ++mb)
+          oc[mb] = mma16(ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks), pf, oc[mb]);
       }
-      if (rf.valid) {
-        const float alpha = fast_exp2((rf.s - Ls[rf.row]) * LOG2E) / ps;
-        float* dst = accW + rf.row * RS + 4 * (lane >> 4);
+      const float alpha = sel[cb] ? fast_exp2((sc[cb] - Lr[cb]) * LOG2E) / ps : 0.f;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          f32x4 cur = *reinterpret_cast<const f32x4*>(dst + 16 * mb);
-          cur += alpha * oc[mb];
-          *reinterpret_cast<f32x4*>(dst + 16 * mb) = cur;
-        }
-      }
-    };
-    auto process_chunk = [&](const BlockFrags<T, DH>& f, RowFrags<T, DH>& r0, int c) __attribute__((always_inline)) {
-      const int e0 = off[c], n = off[c + 1] - e0;
-      const int nb = (n * G + 15) / 16;
-      RowFrags<T, DH> r1;
-      for (int cbk = 0; cbk < nb; cbk += 2) {
-        if (cbk + 1 < nb) load_rows(r1, e0, n, cbk + 1);
-        process_rows(f, r0);
-        if (cbk + 1 >= nb) break;
-        if (cbk + 2 < nb) load_rows(r0, e0, n, cbk + 2);
-        process_rows(f, r1);
-      }
-    };
-    auto load_chunk = [&](BlockFrags<T, DH>& f, RowFrags<T, DH>& r0, int c) __attribute__((always_inline)) {
-      load_block<T, DH>(f, kg + (size_t)c * 64 * DH, 64, vtg + (size_t)c * 64, Np, lane);
-      load_rows(r0, off[c], off[c + 1] - off[c], 0);
-    };
-    if constexpr (!PF) {
-      BlockFrags<T, DH> fa;
-      RowFrags<T, DH> ra;
-      for (int a = grab(); a < NZ; a = grab()) {
-        load_chunk(fa, ra, nzl[a]);
-        process_chunk(fa, ra, nzl[a]);
-      }
-    } else {
-    BlockFrags<T, DH> fa, fb;
-    RowFrags<T, DH> ra, rb;
-    int a = grab();
-    if (a < NZ) load_chunk(fa, ra, nzl[a]);
-    while (a < NZ) {
-      const int bb = grab();
-      if (bb < NZ) load_chunk(fb, rb, nzl[bb]);
-      process_chunk(fa, ra, nzl[a]);
-      if (bb >= NZ) break;
-      a = grab();
-      if (a < NZ) load_chunk(fa, ra, nzl[a]);
-      process_chunk(fb, rb, nzl[bb]);
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] += alpha * oc[mb];
     }
-    }
-  }
-  __syncthreads();
+  };
 
-  // ------------------------------------------------ write o (8 elements per thread)
-  for (int x = tid; x < R * DH / 8; x += 256) {
-    const int r = x / (DH / 8), d8 = 8 * (x - r * (DH / 8));
-    const int pos = p0 + r / G, hh = r % G;
-    float sum[8];
-#pragma unroll
-    for (int h4 = 0; h4 < 2; ++h4) {
-      const int a0 = r * RS + d8 + 4 * h4;
-      const f32x4 s4 = *reinterpret_cast<const f32x4*>(accT + a0) +
-                       *reinterpret_cast<const f32x4*>(accT + R * RS + a0) +
-                       *reinterpret_cast<const f32x4*>(accT + 2 * R * RS + a0) +
-                       *reinterpret_cast<const f32x4*>(accT + 3 * R * RS + a0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sum[4 * h4 + j] = s4[j];
+  // ------------------------------------------------ pipelined item loop
+  issue(stg[0], 0);
+  issue(stg[1], 1);
+  commit(stg[0], 0);
+  issue(stg[0], 2);
+  __syncthreads();
+  for (int n = 0; n < NIT; ++n) {
+    commit(stg[(n + 1) & 1], (n + 1) & 1);  // item n + 1 (its slot's old item is done)
+    issue(stg[(n + 1) & 1], n + 3);
+    const T* sl = slots + (n & 1) * SG::ELEMS;
+    if (n < nW) {
+      const int kv0 = kv_lo + 64 * n;
+      if (wave_live && kv0 <= pw_hi && kv0 + 63 >= ws_lo) {
+        const bool clean = all_valid && kv0 >= ws_hi && kv0 + 63 <= pw_lo;
+        if (clean)
+          window_block(sl, kv0, std::false_type());
+        else
+          window_block(sl, kv0, std::true_type());
+      }
+      if (n == nW - 1) fuse();
+    } else {
+      chunk_block(sl, __builtin_amdgcn_readfirstlane(ulist[n - nW]));
     }
-    if (pos < N) {
-      T* dst = o + (((size_t)b * Hq + g * G + hh) * N + pos) * DH + d8;
-      *reinterpret_cast<typename Frag<T>::type*>(dst) = pack8<T>(sum);
+    __syncthreads();
+  }
+
+  // ------------------------------------------------ write o and lse
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (prow[cb] < 0) continue;
+    if (gl == 0) lse[rowoff[cb]] = Lr[cb];
+    T* dst = o + rowoff[cb] * DH + 4 * gl;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (sizeof(T) == 2) {
+        u16x4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = f2bf(oacc[mb][cb][i]);
+        *reinterpret_cast<u16x4*>(dst + 16 * mb) = hv;
+      } else {
+        *reinterpret_cast<f32x4*>(dst + 16 * mb) = oacc[mb][cb];
+      }
     }
   }
 }
 
-template <typename T, int G, int DH, int CB>
+template <typename T, int G, int DH>
 static size_t fwd_lds(const Dims& p) {
-  constexpr int R = 64 * CB, TP = R / G;
-  size_t s = sizeof(float) * (4 * (size_t)R * (DH + 4) + R);
-  s += sizeof(int) * (2 * (size_t)p.C + 1);
-  s += sizeof(uint16_t) * (size_t)TP * p.K;
+  constexpr int R = 128, TP = R / G;
+  size_t s = sizeof(T) * 2 * (size_t)Slot<T, DH>::ELEMS;
+  s += sizeof(int) * (size_t)TP * p.K + sizeof(float) * (size_t)R * p.K;
+  s += sizeof(int) * ((size_t)p.C + 1 + std::min<size_t>(p.C, (size_t)TP * p.K));
   return (s + 15) & ~(size_t)15;
 }
-
-// row blocks per wave in the window phase
-template <typename T, int DH> struct FwdCB { static constexpr int v = 1; };
-template <> struct FwdCB<uint16_t, 64> { static constexpr int v = 2; };
 
 template <typename T, int G, int DH>
 static hipError_t fwd_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                          const int32_t* idx, const float* sc, const float* sl, void* o, float* lse,
                          hipStream_t st) {
-  constexpr int CB = FwdCB<T, DH>::v;
-  constexpr int TP = 64 * CB / G;
+  constexpr int TP = 128 / G;
   const int ntiles = (p.N + TP - 1) / TP;
-  const size_t lds = fwd_lds<T, G, DH, CB>(p);
-  auto kern = k_attn_fwd<T, G, DH, CB>;
+  const size_t lds = fwd_lds<T, G, DH>(p);
+  auto kern = k_attn_fwd<T, G, DH>;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const T*)q, (const T*)k,
@@ -547,6 +468,18 @@ static hipError_t vt_go(const Dims& p, const void* v, void* vt, int Np, hipStrea
   return hipGetLastError();
 }
 
+// Strategy: the shared-block kernel streams the union of a tile's selected
+// chunks through LDS for all four waves, which pays off when the tile's
+// selections concentrate on a modest number of chunks (the tile selects at
+// least four times as many slots as there are chunks). Otherwise most
+// streamed chunks would serve a single row block, and the bucketed kernel
+// (rows of a chunk packed into dense row blocks, chunks taken by waves
+// independently) does less work.
+static bool fwd_use_shared(const Dims& p) {
+  const long tp = 128 / p.G;
+  return tp * p.K >= 4L * p.C;
+}
+
 template <typename T>
 static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void* v, void* vt,
                         const int32_t* idx, const float* sc, const float* sl, void* o, float* lse,
@@ -554,6 +487,7 @@ static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void*
   const int Np = (p.N + 63) / 64 * 64;
   hipError_t err = p.d == 64 ? vt_go<T, 64>(p, v, vt, Np, st) : vt_go<T, 128>(p, v, vt, Np, st);
   if (err != hipSuccess) return err;
+  if (!fwd_use_shared(p)) return launch_fwd_sparse(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
   switch (p.G * 1000 + p.d) {
     case 1064: return fwd_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
     case 1128: return fwd_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
@@ -567,19 +501,19 @@ static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void*
 
 template <typename T>
 static size_t lds_t(const Dims& p) {
-  constexpr int C64 = FwdCB<T, 64>::v, C128 = FwdCB<T, 128>::v;
   switch (p.G * 1000 + p.d) {
-    case 1064: return fwd_lds<T, 1, 64, C64>(p);
-    case 1128: return fwd_lds<T, 1, 128, C128>(p);
-    case 2064: return fwd_lds<T, 2, 64, C64>(p);
-    case 2128: return fwd_lds<T, 2, 128, C128>(p);
-    case 4064: return fwd_lds<T, 4, 64, C64>(p);
-    case 4128: return fwd_lds<T, 4, 128, C128>(p);
+    case 1064: return fwd_lds<T, 1, 64>(p);
+    case 1128: return fwd_lds<T, 1, 128>(p);
+    case 2064: return fwd_lds<T, 2, 64>(p);
+    case 2128: return fwd_lds<T, 2, 128>(p);
+    case 4064: return fwd_lds<T, 4, 64>(p);
+    case 4128: return fwd_lds<T, 4, 128>(p);
     default: return (size_t)-1;
   }
 }
 
 size_t attn_fwd_lds_bytes(const Dims& p) {
+  if (!fwd_use_shared(p)) return fwd_sparse_lds_bytes(p);
   const size_t stat = 64;
   return (p.dtype == 1 ? lds_t<uint16_t>(p) : lds_t<float>(p)) + stat;
 }

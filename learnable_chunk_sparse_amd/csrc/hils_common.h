@@ -86,6 +86,43 @@ template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// two accumulator quads (rows 4 g + i of two 16-row blocks) -> one operand
+// fragment; the k order {0..3, 16..19}-style permutation is the same on
+// whichever operand is built this way
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type pk8(const f32x4& s0, const f32x4& s1) {
+  float x[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  return pack8<T>(x);
+}
+
+// In-place exclusive scan of a[0..n) by the whole block (256 threads);
+// returns the total. Contains barriers: call from uniform control flow.
+__device__ __forceinline__ int block_excl_scan(int* a, int n, int* wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int seg = (n + 255) / 256;
+  const int lo = min(n, t * seg), hi = min(n, lo + seg);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  int v = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int base = v - s;
+  for (int j = 0; j < w; ++j) base += wsum[j];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  for (int i = lo; i < hi; ++i) {
+    const int x = a[i];
+    a[i] = base;
+    base += x;
+  }
+  __syncthreads();
+  return total;
+}
+
 // Completes this wave's outstanding LDS operations and stops the compiler
 // from moving memory accesses across: used where lanes of ONE wave exchange
 // data through LDS (the other waves are not involved).

@@ -33,6 +33,11 @@ hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const vo
                            const int32_t* topk_idx, const float* topk_score, const float* sel_lse,
                            void* o, float* lse, hipStream_t st);
 size_t attn_fwd_lds_bytes(const Dims& p);
+// bucketed chunk strategy of the forward (attn_fwd_sparse.hip)
+size_t fwd_sparse_lds_bytes(const Dims& p);
+hipError_t launch_fwd_sparse(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                             const int32_t* idx, const float* sc, const float* sl, void* o,
+                             float* lse, hipStream_t st);
 size_t attn_fwd_vt_bytes(const Dims& p);
 
 // Decode.

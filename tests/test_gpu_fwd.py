@@ -32,6 +32,11 @@ SMALL = [
     ("fp32_d64", "fp32", 1, 2, 1, 64, 700, 4, 128, 0, 0, 4.0),
     ("fp32_d64_qcal_gqa2", "fp32", 1, 4, 2, 64, 520, 3, 64, 64, 32, 1.0),
     ("fp32_d128_gqa4", "fp32", 1, 8, 2, 128, 450, 3, 64, 0, 0, 2.0),
+    # selections spread over many chunks relative to a tile's slots: these
+    # take the bucketed chunk strategy ((128 / G) * K < 4 * N / 64)
+    ("spread_gqa4_d128_qcal", "bf16", 1, 8, 2, 128, 2300, 4, 256, 64, 32, 2.0),
+    ("spread_mha_d64_fp32", "fp32", 1, 2, 2, 64, 4500, 2, 128, 0, 0, 3.0),
+    ("spread_gqa2_d64_qcal", "bf16", 1, 4, 2, 64, 3000, 2, 192, 64, 16, 1.0),
 ]
 
 

@@ -125,33 +125,6 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   const T* kg = k + (size_t)bg * N * DH;
   const T* vtg = vt + (size_t)bg * DH * Np;
 
-  // ------------------------------------------------ selections of the tile
-  for (int x = tid; x <= ndmax; x += 256) flg[x] = 0;
-  for (int x = tid; x < TP * K; x += 256) {
-    const int pos = p0 + x / K;
-    tkc[x] = pos < N ? topk_idx[((size_t)bg * N + p0) * K + x] : -1;
-  }
-  for (int x = tid; x < R * K; x += 256) {
-    const int r = x / K, kk = x - r * K;
-    const int pos = p0 + r / G;
-    tks[x] = pos < N ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
-  }
-  __syncthreads();
-  for (int x = tid; x < TP * K; x += 256) {
-    const int c = tkc[x];
-    if (c >= 0 && c < ndmax) flg[c] = 1;
-  }
-  __syncthreads();
-  // union of the selected chunks, ascending: flg becomes offsets, ulist the ids
-  int NU = 0;
-  if (ndmax > 0) {
-    NU = block_excl_scan(flg, ndmax, wsum);
-    if (tid == 0) flg[ndmax] = NU;
-    __syncthreads();
-    for (int c = tid; c < ndmax; c += 256)
-      if (flg[c + 1] > flg[c]) ulist[flg[c]] = c;
-  }
-
   // ------------------------------------------------ per-lane rows
   // wave w owns rows 32 w + 16 cb + cl, cb = 0, 1 (all four lanes of a
   // column hold the same row)
@@ -196,19 +169,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   const float sc2 = scale * LOG2E;
 
   // ------------------------------------------------ work items
-  // items 0 .. nW-1: window blocks kv_lo + 64 n; then the NU union chunks
+  // items 0 .. nW-1: window blocks kv_lo + 64 n; then the NU union chunks.
+  // Block staging: thread vectors s < VPT/2 are K (token, 16-byte part), the
+  // rest V^T (dim, part); two blocks are in flight in registers.
   const int kv_lo = n_distant(p0, W, S) * S;
   const int nW = (plast - kv_lo) / 64 + 1;
-  const int NIT = nW + NU;
-  auto item_kv0 = [&](int n) __attribute__((always_inline)) {
-    n = min(n, NIT - 1);
-    return n < nW ? kv_lo + 64 * n : 64 * ulist[n - nW];
-  };
-  // block staging: thread vectors s < VPT/2 are K (token, 16-byte part), the
-  // rest V^T (dim, part); two blocks are in flight in registers
   u32x4 stg[2][SG::VPT];
-  auto issue = [&](u32x4 (&rg)[SG::VPT], int n) __attribute__((always_inline)) {
-    const int kv0 = item_kv0(n);
+  auto issue_kv = [&](u32x4 (&rg)[SG::VPT], int kv0) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < SG::VPT; ++s) {
       const int vi = tid + 256 * s;
@@ -240,6 +207,42 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
       }
       *reinterpret_cast<u32x4*>(dst) = rg[s];
     }
+  };
+  // the first window blocks do not depend on the selections: start them now
+  issue_kv(stg[0], kv_lo);
+  if (nW > 1) issue_kv(stg[1], kv_lo + 64);
+
+  // ------------------------------------------------ selections of the tile
+  for (int x = tid; x <= ndmax; x += 256) flg[x] = 0;
+  for (int x = tid; x < TP * K; x += 256) {
+    const int pos = p0 + x / K;
+    tkc[x] = pos < N ? topk_idx[((size_t)bg * N + p0) * K + x] : -1;
+  }
+  for (int x = tid; x < R * K; x += 256) {
+    const int r = x / K, kk = x - r * K;
+    const int pos = p0 + r / G;
+    tks[x] = pos < N ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
+  }
+  __syncthreads();
+  for (int x = tid; x < TP * K; x += 256) {
+    const int c = tkc[x];
+    if (c >= 0 && c < ndmax) flg[c] = 1;
+  }
+  __syncthreads();
+  // union of the selected chunks, ascending: flg becomes offsets, ulist the ids
+  int NU = 0;
+  if (ndmax > 0) {
+    NU = block_excl_scan(flg, ndmax, wsum);
+    if (tid == 0) flg[ndmax] = NU;
+    __syncthreads();
+    for (int c = tid; c < ndmax; c += 256)
+      if (flg[c + 1] > flg[c]) ulist[flg[c]] = c;
+  }
+
+  const int NIT = nW + NU;
+  auto issue = [&](u32x4 (&rg)[SG::VPT], int n) __attribute__((always_inline)) {
+    n = min(n, NIT - 1);
+    issue_kv(rg, n < nW ? kv_lo + 64 * n : 64 * ulist[n - nW]);
   };
 
   // ---- window block: banded flash attention over the wave's rows
@@ -391,14 +394,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   };
 
   // ------------------------------------------------ pipelined item loop
-  issue(stg[0], 0);
-  issue(stg[1], 1);
+  if (nW < 2) issue(stg[1], 1);
   commit(stg[0], 0);
   issue(stg[0], 2);
   __syncthreads();
-  for (int n = 0; n < NIT; ++n) {
-    commit(stg[(n + 1) & 1], (n + 1) & 1);  // item n + 1 (its slot's old item is done)
-    issue(stg[(n + 1) & 1], n + 3);
+  // one step: publish item n + 1 from register set rg into the other slot
+  // (whose item n - 1 every wave has finished), reload rg with item n + 3,
+  // then multiply item n. Unrolled by two so the register sets stay fixed.
+  auto step = [&](int n, u32x4 (&rg)[SG::VPT]) __attribute__((always_inline)) {
+    commit(rg, (n + 1) & 1);
+    issue(rg, n + 3);
     const T* sl = slots + (n & 1) * SG::ELEMS;
     if (n < nW) {
       const int kv0 = kv_lo + 64 * n;
@@ -414,6 +419,11 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
       chunk_block(sl, __builtin_amdgcn_readfirstlane(ulist[n - nW]));
     }
     __syncthreads();
+  };
+  for (int n = 0; n < NIT; n += 2) {
+    step(n, stg[1]);
+    if (n + 1 >= NIT) break;
+    step(n + 1, stg[0]);
   }
 
   // ------------------------------------------------ write o and lse

@@ -14,6 +14,7 @@
 #include "hils_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace hils {
 
@@ -106,52 +107,89 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
     }
   }
 
-  // GEMM 2: for each head of the tile, q_hat rows = q + u_h W_up[h]^T.
-  // Work items: (head, 16-token block, 16-dim block); k = r in 32-deep steps.
+  // GEMM 2, transposed so that every lane ends with 4 consecutive dims of one
+  // token: q_hat^T[dims][tokens] = W_up[h] u_h^T + q^T. Wave w takes the
+  // tile's heads w, w + 4, ...; W_up[h] is the A operand (16 dims x 32 of r,
+  // loaded once per head), u^T the B operand read from LDS and split into hi
+  // + lo bf16 halves (fp32 u keeps ~16 significant bits); the q values for
+  // the next 16 tokens are fetched while the current ones are multiplied.
   const int h0 = c0 / r, nh = min(QT_N / r, Hq - h0);
-  const int nmb = QT_M / 16, nnb = d / 16;
-  const int items = nh * nmb * nnb;
-  for (int it = w; it < items; it += 4) {
-    const int hl = it / (nmb * nnb);
-    const int rem = it - hl * nmb * nnb;
-    const int mb = rem / nnb, nb = rem - mb * nnb;
+  const int nks = (r + 31) / 32;
+  for (int hl = w; hl < nh; hl += 4) {
     const int h = h0 + hl;
-    f32x4 o = zero4();
-    for (int kk = 0; kk < r; kk += 32) {
-      // A: u[token 16 mb + col][j = kk + 8 grp .. +8], split hi / lo
-      // (r = 16 leaves the upper half of the 32-deep step empty)
-      const bool kv = kk + 8 * grp < r;
-      const float* ur = us + (16 * mb + col) * QT_UP + hl * r + kk + 8 * grp;
-      float x[8], y[8];
+    constexpr int NBM = 8;  // 16-dim blocks for d <= 128
+    const int nnb = d / 16;
+    FT wa[NBM][2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = kv ? ur[j] : 0.f;
-      const FT ahi = pack8<T>(x);
-      // B: W_up[h][dim 16 nb + col][j]
-      FT bw;
-      if (kv) {
-        bw = ld8<T>(Wu + ((size_t)h * d + 16 * nb + col) * r + kk + 8 * grp);
-      } else {
+    for (int nb = 0; nb < NBM; ++nb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = 0.f;
-        bw = pack8<T>(y);
+      for (int ks = 0; ks < 2; ++ks) {
+        float z[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = 0.f;
+        wa[nb][ks] = pack8<T>(z);
+        if (nb < nnb && ks < nks && 32 * ks + 8 * grp < r)
+          wa[nb][ks] = ld8<T>(Wu + ((size_t)h * d + 16 * nb + col) * r + 32 * ks + 8 * grp);
       }
-      o = mma16(ahi, bw, o);
-      if constexpr (sizeof(T) == 2) {
-        const u16x8 hb = __builtin_bit_cast(u16x8, ahi);
+    // q^T fragments of token block mb: 4 consecutive dims per (lane, nb)
+    typedef typename std::conditional<sizeof(T) == 2, u16x4, f32x4>::type QV;
+    auto qrow = [&](int mb) __attribute__((always_inline)) {
+      const int t = min(t0 + 16 * mb + col, ntok - 1);
+      const int bb = t / Nq, ii = t - bb * Nq;
+      return (((size_t)bb * Hq + h) * Nq + ii) * d + 4 * grp;
+    };
+    QV qv[NBM], qn[NBM];
+    {
+      const size_t ro = qrow(0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = x[j] - bf2f(hb[j]);
-        o = mma16(pack8<T>(y), bw, o);
-      }
+      for (int nb = 0; nb < NBM; ++nb)
+        if (nb < nnb) qv[nb] = *reinterpret_cast<const QV*>(q + ro + 16 * nb);
     }
-    // D layout: token 16 mb + 4 grp + i, dim 16 nb + col
+    for (int mb = 0; mb < QT_M / 16; ++mb) {
+      if (mb + 1 < QT_M / 16) {
+        const size_t rn = qrow(mb + 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * mb + 4 * grp + i;
-      if (t < ntok) {
-        const int bb = t / Nq, ii = t - bb * Nq;
-        const size_t off = (((size_t)bb * Hq + h) * Nq + ii) * d + 16 * nb + col;
-        qhat[off] = to_f<T>(q[off]) + o[i];
+        for (int nb = 0; nb < NBM; ++nb)
+          if (nb < nnb) qn[nb] = *reinterpret_cast<const QV*>(q + rn + 16 * nb);
       }
+      f32x4 acc[NBM];
+#pragma unroll
+      for (int nb = 0; nb < NBM; ++nb) acc[nb] = zero4();
+      for (int ks = 0; ks < nks; ++ks) {
+        const bool kv = 32 * ks + 8 * grp < r;
+        const float* ur = us + (16 * mb + col) * QT_UP + hl * r + 32 * ks + 8 * grp;
+        float x[8], y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = kv ? ur[j] : 0.f;
+        const FT bhi = pack8<T>(x);
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb)
+          if (nb < nnb) acc[nb] = mma16(wa[nb][ks], bhi, acc[nb]);
+        if constexpr (sizeof(T) == 2) {
+          const u16x8 hb = __builtin_bit_cast(u16x8, bhi);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[j] = x[j] - bf2f(hb[j]);
+          const FT blo = pack8<T>(y);
+#pragma unroll
+          for (int nb = 0; nb < NBM; ++nb)
+            if (nb < nnb) acc[nb] = mma16(wa[nb][ks], blo, acc[nb]);
+        }
+      }
+      // D layout: dims 16 nb + 4 grp + i of token 16 mb + col
+      const int t = t0 + 16 * mb + col;
+      if (t < ntok) {
+        const size_t ro = qrow(mb);
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+          if (nb >= nnb) continue;
+          f32x4 o = acc[nb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] += to_f<T>(qv[nb][i]);
+          *reinterpret_cast<f32x4*>(qhat + ro + 16 * nb) = o;
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBM; ++nb) qv[nb] = qn[nb];
     }
   }
 }

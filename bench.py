@@ -241,8 +241,11 @@ def bench_decode(args, torch, L):
     wl = WORKLOADS[args.decode_workload]
     t = make_inputs(wl, device="cuda")
     bufs = L.decode_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
-    # a buffer larger than the 256 MiB last-level cache, rewritten between steps
-    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+    # a buffer larger than the 256 MiB last-level cache, read between steps so
+    # that the step starts with none of its data cached (a read leaves clean
+    # lines: no write-back of the flush competes with the step's reads)
+    flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def step():
         L.hils_decode(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
@@ -255,7 +258,7 @@ def bench_decode(args, torch, L):
     st, sp = event_ring(n, torch)
     L.hils_set_timing_events(L.STEP_DECODE, st, sp)
     for _ in range(n):
-        flush.fill_(1.0)
+        torch.sum(flush, dim=0, out=sink)
         step()
     torch.cuda.synchronize()
     L.hils_set_timing_events(L.STEP_DECODE)
@@ -266,7 +269,7 @@ def bench_decode(args, torch, L):
     out = {"workload": wl.name, "us_per_step": med * 1e3, "median_of": n, "cold_cache": True,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
-    del t, bufs, flush
+    del t, bufs, flush, sink
     torch.cuda.empty_cache()
     return out
 

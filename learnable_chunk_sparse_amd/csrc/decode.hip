@@ -5,17 +5,21 @@
 // The step is bound by HBM bandwidth: every distant landmark key is read once
 // (the O(L/S) per-token retrieval term), then only the K selected chunks and
 // the window. Four launches:
-//   k_dec_scan    split landmark scan: each workgroup scores CPW chunks of one
-//                 (sequence, KV head) with 16x16x32 MFMAs (rows = chunks, columns
-//                 = the group's heads, hi and lo halves of the fp32 query), takes
-//                 the max over heads, and keeps its own top-K (rank count).
-//   k_dec_merge   per (sequence, KV head): bitonic sort of the splits' lists,
-//                 final top-K in ascending chunk order.
+//   k_dec_scan    streaming landmark scan: each workgroup scores CPW chunks of
+//                 one (sequence, KV head) with 16x16x32 MFMAs (rows = chunks,
+//                 columns = the group's heads, hi and lo halves of the fp32
+//                 query), takes the max over heads and stores the score.
+//   k_dec_select  per (sequence, KV head): the K-th largest score by a 4-pass
+//                 8-bit radix select over order-preserving integer keys, ties
+//                 resolved by lower chunk index, and the chosen ids written in
+//                 ascending order by a prefix sum (no sort).
 //   k_dec_attn    one wave per 64-token unit (a selected chunk or a window
 //                 block) for all G heads: S^T = K Q^T on MFMA, softmax, O^T =
-//                 V^T P^T with V staged transposed in LDS. A chunk unit leaves
-//                 (log-weight s_c, weight 1, O_c); a window block leaves its
-//                 (max, sum, unnormalised output).
+//                 V^T P^T; the V^T operands come from the row-major V
+//                 fragments by a product with the identity (exact), so nothing
+//                 is staged in LDS. A chunk unit leaves (log-weight s_c,
+//                 weight 1, O_c); a window block leaves its (max, sum,
+//                 unnormalised output).
 //   k_dec_combine per (sequence, query head): log-sum-exp merge of all units,
 //                 which is exactly the fusion softmax over {s_c} and lse_W.
 #include "hils_common.h"
@@ -28,7 +32,6 @@ namespace hils {
 namespace {
 
 constexpr int CPW = 256;  // chunks per scan workgroup
-constexpr int VPADD = 8;
 
 __device__ __forceinline__ int seq_n(const int32_t* seq_len, int b, int N) {
   if (seq_len == nullptr) return N;
@@ -41,14 +44,6 @@ __device__ __forceinline__ uint32_t ord_f(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float unord_f(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-// sort key: larger score first, then lower chunk index first
-__device__ __forceinline__ uint64_t mkkey(float s, int c) {
-  return ((uint64_t)ord_f(s) << 32) | (uint32_t)(~(uint32_t)c);
-}
-constexpr uint64_t EMPTY_KEY = 0;  // below every real key
 
 }  // namespace
 
@@ -57,24 +52,33 @@ template <typename T, typename QT, int G, int DH>
 __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
                                                   const int32_t* __restrict__ seq_len,
-                                                  uint64_t* __restrict__ lists, int N, int C, int Hkv,
-                                                  int K, int W, int S, float scale, int nsplit) {
+                                                  float* __restrict__ scores, int N, int C, int Cp,
+                                                  int Hkv, int W, int S, float scale) {
   typedef typename Frag<T>::type FT;
   constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
   constexpr int KS = DH / 32;
   constexpr int NPART = HAS_LO ? 2 : 1;
-  __shared__ float sc_s[CPW];
+  constexpr int ST = CPW / 64;  // 16-chunk steps per wave
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   const int n = seq_n(seq_len, b, N);
   const int nd = n_distant(n - 1, W, S);
-  const int c_lo = split * CPW;
-  uint64_t* out = lists + ((size_t)bg * nsplit + split) * K;
-  if (c_lo >= nd) {
-    for (int k = threadIdx.x; k < K; k += 256) out[k] = EMPTY_KEY;
-    return;
+  const int c_w = split * CPW + 64 * w;  // this wave's first chunk
+  if (c_w >= nd) return;
+  const T* kLg = kL + (size_t)bg * C * DH;
+  const T* eg = e + (size_t)bg * C;
+  // all of the wave's landmark rows are requested before any product
+  FT ka[ST][KS];
+  float eb[ST];
+#pragma unroll
+  for (int st = 0; st < ST; ++st) {
+    const int c = min(c_w + 16 * st + (lane & 15), nd - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[st][ks] = ld8<T>(kLg + (size_t)c * DH + 8 * (lane >> 4) + 32 * ks);
+    const int ce = min(c_w + 16 * st + 4 * ((lane >> 4) & 3) + (lane & 3), nd - 1);
+    eb[st] = to_f<T>(eg[ce]);
   }
   // B operand: column col = part * G + h holds the hi (part 0) or lo (part 1)
   // bf16 half of query head h; other columns are zero.
@@ -100,18 +104,12 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
       bq[ks] = pack8<T>(x);
     }
   }
-  const T* kLg = kL + (size_t)bg * C * DH;
-  const T* eg = e + (size_t)bg * C;
-  // each wave: 4 steps of 16 chunks
+  float* dst = scores + (size_t)bg * Cp;
 #pragma unroll
-  for (int st = 0; st < CPW / 64; ++st) {
-    const int cb = c_lo + 64 * w + 16 * st;
-    const int c = cb + (lane & 15);
-    const int cl = c < nd ? c : nd - 1;
+  for (int st = 0; st < ST; ++st) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = mma16(ld8<T>(kLg + (size_t)cl * DH + 8 * (lane >> 4) + 32 * ks), bq[ks], acc);
+    for (int ks = 0; ks < KS; ++ks) acc = mma16(ka[st][ks], bq[ks], acc);
     // lane holds D[chunk 4*(lane/16)+i][col lane%16]: add hi + lo, max over heads
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -121,152 +119,156 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
       for (int m = 1; m < G; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
       acc[i] = v;
     }
-    if ((lane & 15) == 0) {
+    // the bias of chunk 4*(lane/16)+i was fetched by lane 16*(lane/16) + i
+    f32x4 out;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int cc = cb + 4 * (lane >> 4) + i;
-        sc_s[64 * w + 16 * st + 4 * (lane >> 4) + i] =
-            cc < nd ? fmaf(acc[i], scale, to_f<T>(eg[cc])) : NEG_INF;
-      }
-    }
-  }
-  __syncthreads();
-  // rank count: fewer than K better candidates -> slot = rank
-  const int t = threadIdx.x;
-  const float my = sc_s[t];
-  const int myc = c_lo + t;
-  if (t < K) out[t] = EMPTY_KEY;
-  __syncthreads();
-  if (my != NEG_INF) {
-    int rank = 0;
-    for (int j = 0; j < CPW; ++j) {
-      const float o = sc_s[j];
-      rank += (o > my) || (o == my && j < t);
-    }
-    if (rank < K) out[rank] = mkkey(my, myc);
+    for (int i = 0; i < 4; ++i) out[i] = fmaf(acc[i], scale, __shfl(eb[st], (lane & 48) + i, 64));
+    if ((lane & 15) == 0) *reinterpret_cast<f32x4*>(dst + c_w + 16 * st + 4 * (lane >> 4)) = out;
   }
 }
 
-// ---------------------------------------------------------------- merge
-__global__ __launch_bounds__(1024) void k_dec_merge(const uint64_t* __restrict__ lists,
-                                                    int32_t* __restrict__ sel,
-                                                    int32_t* __restrict__ topk_out, int nsplit,
-                                                    int K) {
-  extern __shared__ uint64_t keys[];
-  const int bg = blockIdx.x;
-  const int n = nsplit * K;
-  int P = 1;
-  while (P < n) P <<= 1;
-  const uint64_t* src = lists + (size_t)bg * n;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) keys[i] = i < n ? src[i] : EMPTY_KEY;
+// ---------------------------------------------------------------- select
+// exclusive prefix sum of v over the 1024 threads of the block; total as well
+__device__ __forceinline__ int block_scan1024(int v, int* wsum, int& total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
-  // bitonic sort, descending
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = keys[i], bb = keys[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a < bb) : (a > bb)) {
-            keys[i] = bb;
-            keys[ixj] = a;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int s2 = wsum[j];
+    base += j < w ? s2 : 0;
+    tot += s2;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+// The K largest scores of one (sequence, KV head) by (score desc, index asc),
+// written as ascending chunk ids, -1 padded.
+__global__ __launch_bounds__(1024) void k_dec_select(const float* __restrict__ scores,
+                                                     const int32_t* __restrict__ seq_len,
+                                                     int32_t* __restrict__ sel,
+                                                     int32_t* __restrict__ topk_out, int N, int Cp,
+                                                     int Hkv, int K, int W, int S) {
+  __shared__ int hist[256];
+  __shared__ int wsum[16];
+  __shared__ uint32_t s_prefix, s_mask;
+  __shared__ int s_krem;
+  const int t = threadIdx.x;
+  const int bg = blockIdx.x, b = bg / Hkv;
+  const int nd = n_distant(seq_n(seq_len, b, N) - 1, W, S);
+  const float* src = scores + (size_t)bg * Cp;
+  const bool take_all = nd <= K;
+  if (t == 0) {
+    s_prefix = 0u;
+    s_mask = 0u;
+    s_krem = K;
+  }
+  __syncthreads();
+  // radix select: the exact key T of the K-th largest score, and how many of
+  // the keys equal to T are taken (krem)
+  if (!take_all) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (t < 256) hist[t] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix, mask = s_mask;
+      for (int c = t; c < nd; c += 1024) {
+        const uint32_t key = ord_f(src[c]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (t < 64) {
+        // lane t holds bins 4t .. 4t+3; keys in higher bins rank above
+        int h4[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h4[j] = hist[4 * t + j];
+          sum += h4[j];
+        }
+        int x = sum;  // suffix sum over lanes >= t
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_down(x, o, 64);
+          if (t + o < 64) x += y;
+        }
+        const int krem = s_krem;
+        int above = x - sum;
+        for (int j = 3; j >= 0; --j) {
+          const int with = above + h4[j];
+          if (above < krem && krem <= with) {
+            s_prefix = prefix | ((uint32_t)(4 * t + j) << shift);
+            s_mask = mask | (255u << shift);
+            s_krem = krem - above;
           }
+          above = with;
         }
       }
       __syncthreads();
     }
   }
-  // top K in ascending chunk order
-  __shared__ int ids[64];
-  if (threadIdx.x < K) {
-    const uint64_t kk = keys[threadIdx.x];
-    ids[threadIdx.x] = kk == EMPTY_KEY ? 0x7FFFFFFF : (int)(~(uint32_t)(kk & 0xFFFFFFFFu));
+  const uint32_t T = s_prefix;
+  const int krem = s_krem;
+  // contiguous index ranges per thread, so that prefix sums follow index order
+  const int per = (nd + 1023) / 1024;
+  const int lo = min(nd, t * per), hi = min(nd, lo + per);
+  int ties = 0;
+  if (!take_all)
+    for (int c = lo; c < hi; ++c) ties += ord_f(src[c]) == T;
+  int tot;
+  const int tie0 = block_scan1024(ties, wsum, tot);
+  auto taken = [&](int c, int& tr) {
+    if (take_all) return true;
+    const uint32_t key = ord_f(src[c]);
+    const bool tk = key > T || (key == T && tr < krem);
+    tr += key == T;
+    return tk;
+  };
+  int cnt = 0;
+  {
+    int tr = tie0;
+    for (int c = lo; c < hi; ++c) cnt += taken(c, tr) ? 1 : 0;
   }
-  __syncthreads();
-  if (threadIdx.x < K) {
-    const int me = ids[threadIdx.x];
-    int r = 0;
-    for (int j = 0; j < K; ++j) r += ids[j] < me;
-    const int v = me == 0x7FFFFFFF ? -1 : me;
-    // empties all sort last with equal ids; place them after the real ones
-    int slot = r;
-    if (me == 0x7FFFFFFF) {
-      int before = 0;
-      for (int j = 0; j < threadIdx.x; ++j) before += ids[j] == 0x7FFFFFFF;
-      slot = r + before;
+  const int out0 = block_scan1024(cnt, wsum, tot);
+  {
+    int tr = tie0, o = out0;
+    for (int c = lo; c < hi; ++c) {
+      if (taken(c, tr)) {
+        sel[(size_t)bg * K + o] = c;
+        if (topk_out != nullptr) topk_out[(size_t)bg * K + o] = c;
+        ++o;
+      }
     }
-    sel[(size_t)bg * K + slot] = v;
-    if (topk_out != nullptr) topk_out[(size_t)bg * K + slot] = v;
+  }
+  for (int k2 = tot + t; k2 < K; k2 += 1024) {
+    sel[(size_t)bg * K + k2] = -1;
+    if (topk_out != nullptr) topk_out[(size_t)bg * K + k2] = -1;
   }
 }
 
 // ---------------------------------------------------------------- attention units
-// Stage a 64-token V block transposed into vt[DH][64 + VPADD] (one wave).
-template <typename T, int DH>
-__device__ __forceinline__ void dec_stage_vt(const T* __restrict__ vsrc, int nvalid, T* vt, int lane) {
-  const int tp = lane & 31, half = lane >> 5;
-  const int t0 = 2 * tp, t1 = 2 * tp + 1;
-  const T* r0 = vsrc + (size_t)(t0 < nvalid ? t0 : 0) * DH + half * (DH / 2);
-  const T* r1 = vsrc + (size_t)(t1 < nvalid ? t1 : 0) * DH + half * (DH / 2);
-  constexpr int VS = 64 + VPADD;
-#pragma unroll
-  for (int j = 0; j < DH / 2; j += 8) {
-    const auto a = ld8<T>(r0 + j);
-    const auto bb = ld8<T>(r1 + j);
-    if constexpr (sizeof(T) == 2) {
-      const u16x8 ua = __builtin_bit_cast(u16x8, a), ub = __builtin_bit_cast(u16x8, bb);
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2)
-        *reinterpret_cast<uint32_t*>(vt + (half * (DH / 2) + j + e2) * VS + t0) =
-            (uint32_t)ua[e2] | ((uint32_t)ub[e2] << 16);
-    } else {
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        float2 pr;
-        pr.x = a[e2];
-        pr.y = bb[e2];
-        *reinterpret_cast<float2*>(vt + (half * (DH / 2) + j + e2) * VS + t0) = pr;
-      }
-    }
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type dec_ld_vt(const T* vt, int mb, int ks, int lane) {
-  constexpr int VS = 64 + VPADD;
-  const T* p = vt + (16 * mb + (lane & 15)) * VS + 32 * ks + 4 * (lane >> 4);
-  if constexpr (sizeof(T) == 2) {
-    const u16x4 a = *reinterpret_cast<const u16x4*>(p);
-    const u16x4 bb = *reinterpret_cast<const u16x4*>(p + 16);
-    u16x8 u;
-    u[0] = a[0]; u[1] = a[1]; u[2] = a[2]; u[3] = a[3];
-    u[4] = bb[0]; u[5] = bb[1]; u[6] = bb[2]; u[7] = bb[3];
-    return __builtin_bit_cast(bf16x8, u);
-  } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(p + 16);
-    f32x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-    r[4] = bb[0]; r[5] = bb[1]; r[6] = bb[2]; r[7] = bb[3];
-    return r;
-  }
-}
-
-// partial layout per (bg, unit, head): [m, l, U[0..DH)]
+// partials per (bg, unit, head): pml = [m, l], po = U[0..DH)
 template <typename T, typename QT, int G, int DH>
 __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const QT* __restrict__ qs,
                                                   const T* __restrict__ k, const T* __restrict__ v,
                                                   const T* __restrict__ kL, const T* __restrict__ e,
                                                   const int32_t* __restrict__ seq_len,
                                                   const int32_t* __restrict__ sel,
-                                                  float* __restrict__ part, int N, int C, int Hkv,
-                                                  int K, int W, int S, float scale, int units) {
+                                                  float* __restrict__ pml, float* __restrict__ po,
+                                                  int N, int C, int Hkv, int K, int W, int S,
+                                                  float scale, int units) {
   typedef typename Frag<T>::type FT;
   constexpr int KS = DH / 32, MB = DH / 16;
-  constexpr int VS = 64 + VPADD;
-  __shared__ __align__(16) T vt_s[4][DH * VS];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int gl = lane >> 4, col = lane & 15;
   const int u = blockIdx.x * 4 + w;
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg - b * Hkv;
@@ -276,7 +278,8 @@ __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const
   const int i = n - 1;
   const int nd = n_distant(i, W, S);
   const int ws = nd * S;
-  float* pout = part + ((size_t)bg * units + u) * G * (DH + 2);
+  float* pm = pml + ((size_t)bg * units + u) * G * 2;
+  float* pv = po + ((size_t)bg * units + u) * G * DH;
   // what this unit covers
   int t0, cnt, chunk = -1;
   if (u < K) {
@@ -287,19 +290,35 @@ __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const
     t0 = ws + 64 * (u - K);
     cnt = min(64, n - t0);
   }
-  const int col = lane & 15;
   if (cnt <= 0) {
-    if (col < G && (lane >> 4) == 0) {
-      pout[col * (DH + 2)] = NEG_INF;
-      pout[col * (DH + 2) + 1] = 0.f;
+    // an empty unit: weight 0 and a zero vector (the combine multiplies
+    // every unit's vector by its weight without branching)
+    if (lane < G) {
+      pm[2 * lane] = NEG_INF;
+      pm[2 * lane + 1] = 0.f;
     }
+    for (int x = lane; x < G * DH / 4; x += 64) reinterpret_cast<f32x4*>(pv)[x] = zero4();
     return;
+  }
+  // K and V rows as row-major fragments: token 16 tb + col, dims 8 gl + 32 ks
+  const T* kb = k + ((size_t)bg * N + t0) * DH;
+  const T* vb = v + ((size_t)bg * N + t0) * DH;
+  FT kf[4][KS], vf[4][KS];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    int tok = 16 * tb + col;
+    tok = tok < cnt ? tok : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[tb][ks] = ld8<T>(kb + (size_t)tok * DH + 8 * gl + 32 * ks);
+      vf[tb][ks] = ld8<T>(vb + (size_t)tok * DH + 8 * gl + 32 * ks);
+    }
   }
   // Q^T operand: column col = head col (raw query), zero beyond G
   FT qf[KS];
   {
     const int h = col < G ? col : 0;
-    const T* src = q + ((size_t)b * Hq + g * G + h) * DH + 8 * (lane >> 4);
+    const T* src = q + ((size_t)b * Hq + g * G + h) * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float x[8];
@@ -308,26 +327,37 @@ __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const
       qf[ks] = pack8<T>(x);
     }
   }
-  const T* kb = k + ((size_t)bg * N + t0) * DH;
-  const T* vb = v + ((size_t)bg * N + t0) * DH;
-  T* vt = vt_s[w];
-  dec_stage_vt<T, DH>(vb, cnt, vt, lane);
+  // per-head fusion score of a selected chunk: s_h = scale q_hat_h . kL_c + e_c
+  float s_head[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) s_head[h] = 0.f;
+  if (chunk >= 0) {
+    const T* kr = kL + ((size_t)bg * C + chunk) * DH;
+    const float eb = to_f<T>(e[(size_t)bg * C + chunk]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const QT* qh = qs + ((size_t)b * Hq + g * G + h) * DH;
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < DH / 64; ++j) a = fmaf(to_f<QT>(qh[lane + 64 * j]), to_f<T>(kr[lane + 64 * j]), a);
+#pragma unroll
+      for (int m2 = 32; m2 >= 1; m2 >>= 1) a += __shfl_xor(a, m2, 64);
+      s_head[h] = fmaf(a, scale, eb);
+    }
+  }
   f32x4 sacc[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    int tok = 16 * tb + (lane & 15);
-    tok = tok < cnt ? tok : 0;
     sacc[tb] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sacc[tb] = mma16(ld8<T>(kb + (size_t)tok * DH + 8 * (lane >> 4) + 32 * ks), qf[ks], sacc[tb]);
+    for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(kf[tb][ks], qf[ks], sacc[tb]);
   }
   float mx = NEG_INF;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const int tok = 16 * tb + 4 * (lane >> 4) + ii;
+      const int tok = 16 * tb + 4 * gl + ii;
       const float x = tok < cnt ? sacc[tb][ii] * scale : NEG_INF;
       sacc[tb][ii] = x;
       mx = fmaxf(mx, x);
@@ -346,48 +376,62 @@ __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const
     }
   ls += shfl_xor(ls, 16);
   ls += shfl_xor(ls, 32);
-  wave_lds_sync();
+  // identity fragments: I_h[k][c] = (k == 16 h + c)
+  FT idf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (8 * gl + j == 16 * h + col) ? 1.f : 0.f;
+    idf[h] = pack8<T>(x);
+  }
   f32x4 oacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) oacc[mb] = zero4();
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    float x[8] = {sacc[2 * ks][0], sacc[2 * ks][1], sacc[2 * ks][2], sacc[2 * ks][3],
-                  sacc[2 * ks + 1][0], sacc[2 * ks + 1][1], sacc[2 * ks + 1][2], sacc[2 * ks + 1][3]};
-    const FT pf = pack8<T>(x);
+  for (int ks = 0; ks < 2; ++ks) {  // 32-token steps
+    const FT pf = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) oacc[mb] = mma16(dec_ld_vt<T>(vt, mb, ks, lane), pf, oacc[mb]);
+    for (int mb = 0; mb < MB; ++mb) {
+      // V^T rows 16 mb .. 16 mb + 15 over the step's tokens, in the token
+      // order of the P^T fragment
+      const int kd = mb >> 1, hs = mb & 1;
+      const FT vt = pk8<T>(mma16(vf[2 * ks][kd], idf[hs], zero4()),
+                           mma16(vf[2 * ks + 1][kd], idf[hs], zero4()));
+      oacc[mb] = mma16(vt, pf, oacc[mb]);
+    }
   }
   if (col < G) {
-    float* ph = pout + col * (DH + 2);
     float mval = mx, lval = ls, coef = 1.f;
     if (chunk >= 0) {
       // a selected chunk enters the fusion as one term: log-weight s_c,
       // weight 1, vector O_c
-      const QT* qh = qs + ((size_t)b * Hq + g * G + col) * DH;
-      const T* kr = kL + ((size_t)bg * C + chunk) * DH;
-      float s = 0.f;
-      for (int dd = 0; dd < DH; ++dd) s = fmaf(to_f<QT>(qh[dd]), to_f<T>(kr[dd]), s);
-      mval = fmaf(s, scale, to_f<T>(e[(size_t)bg * C + chunk]));
+      float sh = s_head[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) sh = col == h ? s_head[h] : sh;
+      mval = sh;
       lval = 1.f;
       coef = 1.f / ls;
     }
-    if ((lane >> 4) == 0) {
-      ph[0] = mval;
-      ph[1] = lval;
+    if (gl == 0) {
+      pm[2 * col] = mval;
+      pm[2 * col + 1] = lval;
     }
+    float* ph = pv + (size_t)col * DH + 4 * gl;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) ph[2 + 16 * mb + 4 * (lane >> 4) + ii] = oacc[mb][ii] * coef;
+    for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(ph + 16 * mb) = oacc[mb] * coef;
   }
 }
 
 // ---------------------------------------------------------------- combine
+// one wave per (sequence, query head): lanes first take units (max, weights),
+// then dims (the weighted sum, eight units' loads in flight at a time)
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k_dec_combine(const float* __restrict__ part, T* __restrict__ o,
+__global__ __launch_bounds__(64) void k_dec_combine(const float* __restrict__ pml,
+                                                    const float* __restrict__ po, T* __restrict__ o,
                                                     float* __restrict__ lse, int Hkv, int G,
                                                     int units) {
+  __shared__ float wgt[256];
   const int bh = blockIdx.x;  // b * Hq + h
   const int Hq = Hkv * G;
   const int b = bh / Hq, h = bh - b * Hq;
@@ -395,20 +439,39 @@ __global__ __launch_bounds__(64) void k_dec_combine(const float* __restrict__ pa
   const int bg = b * Hkv + g;
   const int lane = threadIdx.x;
   float M = NEG_INF;
-  for (int u = 0; u < units; ++u) M = fmaxf(M, part[(((size_t)bg * units + u) * G + hh) * (DH + 2)]);
+  for (int u = lane; u < units; u += 64) M = fmaxf(M, pml[(((size_t)bg * units + u) * G + hh) * 2]);
+#pragma unroll
+  for (int m2 = 32; m2 >= 1; m2 >>= 1) M = fmaxf(M, __shfl_xor(M, m2, 64));
   float Z = 0.f;
+  for (int u = lane; u < units; u += 64) {
+    const float* p = pml + (((size_t)bg * units + u) * G + hh) * 2;
+    const float m = p[0];
+    const float wu = m == NEG_INF ? 0.f : __expf(m - M);
+    wgt[u] = wu;
+    Z += wu * p[1];
+  }
+#pragma unroll
+  for (int m2 = 32; m2 >= 1; m2 >>= 1) Z += __shfl_xor(Z, m2, 64);
+  __syncthreads();
   float acc[DH / 64];
 #pragma unroll
   for (int j = 0; j < DH / 64; ++j) acc[j] = 0.f;
-  for (int u = 0; u < units; ++u) {
-    const float* p = part + (((size_t)bg * units + u) * G + hh) * (DH + 2);
-    const float m = p[0];
-    if (m == NEG_INF) continue;
-    const float wgt = __expf(m - M);
-    Z += wgt * p[1];
+  const float* base = po + ((size_t)bg * units * G + hh) * DH;
+  int u = 0;
+  for (; u + 8 <= units; u += 8) {
+    float x[8][DH / 64];
 #pragma unroll
-    for (int j = 0; j < DH / 64; ++j) acc[j] += wgt * p[2 + lane + 64 * j];
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < DH / 64; ++j) x[t][j] = base[(size_t)(u + t) * G * DH + lane + 64 * j];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < DH / 64; ++j) acc[j] = fmaf(wgt[u + t], x[t][j], acc[j]);
   }
+  for (; u < units; ++u)
+#pragma unroll
+    for (int j = 0; j < DH / 64; ++j) acc[j] = fmaf(wgt[u], base[(size_t)u * G * DH + lane + 64 * j], acc[j]);
 #pragma unroll
   for (int j = 0; j < DH / 64; ++j) o[(size_t)bh * DH + lane + 64 * j] = from_f<T>(acc[j] / Z);
   if (lane == 0) lse[bh] = M + __logf(Z);
@@ -418,26 +481,29 @@ __global__ __launch_bounds__(64) void k_dec_combine(const float* __restrict__ pa
 namespace {
 struct DecWs {
   float* qhat;
-  uint64_t* lists;
+  float* scores;
   int32_t* sel;
-  float* part;
-  int nsplit, units;
+  float *pml, *po;
+  int nsplit, units, Cp;
 };
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carve(const Dims& p, void* base, DecWs* w) {
   char* c = static_cast<char*>(base);
   size_t off = 0;
   w->nsplit = std::max(1, (p.C + CPW - 1) / CPW);
+  w->Cp = w->nsplit * CPW;
   w->units = p.K + (p.W + p.S - 1 + 63) / 64 + 1;
   auto take = [&](size_t bytes) {
     void* ptr = c ? c + off : nullptr;
     off += up256(bytes);
     return ptr;
   };
+  const size_t bg = (size_t)p.B * p.Hkv;
   w->qhat = (float*)take(p.r > 0 ? (size_t)p.B * p.Hq * p.d * sizeof(float) : 0);
-  w->lists = (uint64_t*)take((size_t)p.B * p.Hkv * w->nsplit * p.K * sizeof(uint64_t));
-  w->sel = (int32_t*)take((size_t)p.B * p.Hkv * p.K * sizeof(int32_t));
-  w->part = (float*)take((size_t)p.B * p.Hkv * w->units * p.G * (p.d + 2) * sizeof(float));
+  w->scores = (float*)take(bg * w->Cp * sizeof(float));
+  w->sel = (int32_t*)take(bg * p.K * sizeof(int32_t));
+  w->pml = (float*)take(bg * w->units * p.G * 2 * sizeof(float));
+  w->po = (float*)take(bg * w->units * p.G * p.d * sizeof(float));
   return off;
 }
 }  // namespace
@@ -445,7 +511,7 @@ size_t carve(const Dims& p, void* base, DecWs* w) {
 size_t decode_workspace(const Dims& p) {
   DecWs w;
   const size_t s = carve(p, nullptr, &w);
-  if ((size_t)w.nsplit * p.K > 8192) return (size_t)-1;  // merge sort capacity
+  if (w.units > 256) return (size_t)-1;  // combine weight buffer
   return s;
 }
 
@@ -454,27 +520,20 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
                          const int32_t* seq_len, const void* kL, const void* e, void* o, float* lse,
                          int32_t* topk_idx, const DecWs& w, hipStream_t st) {
   hipLaunchKernelGGL((k_dec_scan<T, QT, G, DH>), dim3(w.nsplit, p.B * p.Hkv), dim3(256), 0, st,
-                     (const QT*)qs, (const T*)kL, (const T*)e, seq_len, w.lists, p.N, p.C, p.Hkv,
-                     p.K, p.W, p.S, p.scale, w.nsplit);
+                     (const QT*)qs, (const T*)kL, (const T*)e, seq_len, w.scores, p.N, p.C, w.Cp,
+                     p.Hkv, p.W, p.S, p.scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int P = 1;
-  while (P < w.nsplit * p.K) P <<= 1;
-  const size_t lds = (size_t)P * sizeof(uint64_t);
-  if (lds > 64 * 1024) {
-    err = hipFuncSetAttribute((const void*)k_dec_merge, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(k_dec_merge, dim3(p.B * p.Hkv), dim3(1024), lds, st, w.lists, w.sel, topk_idx,
-                     w.nsplit, p.K);
+  hipLaunchKernelGGL(k_dec_select, dim3(p.B * p.Hkv), dim3(1024), 0, st, (const float*)w.scores,
+                     seq_len, w.sel, topk_idx, p.N, w.Cp, p.Hkv, p.K, p.W, p.S);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((k_dec_attn<T, QT, G, DH>), dim3((w.units + 3) / 4, p.B * p.Hkv), dim3(256), 0,
                      st, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
-                     (const T*)e, seq_len, w.sel, w.part, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
-                     w.units);
+                     (const T*)e, seq_len, w.sel, w.pml, w.po, p.N, p.C, p.Hkv, p.K, p.W, p.S,
+                     p.scale, w.units);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, w.part, (T*)o, lse,
-                     p.Hkv, G, w.units);
+  hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, (const float*)w.pml,
+                     (const float*)w.po, (T*)o, lse, p.Hkv, G, w.units);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ namespace hils {
 
 namespace {
 
-constexpr int CPW = 256;  // chunks per scan workgroup
+constexpr int CPW = 512;  // chunks per scan workgroup
 
 __device__ __forceinline__ int seq_n(const int32_t* seq_len, int b, int N) {
   if (seq_len == nullptr) return N;

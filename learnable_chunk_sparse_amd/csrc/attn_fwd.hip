@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   constexpr int TP = R / G;   // positions per tile
   constexpr int KS = DH / 32;
   constexpr int MB = DH / 16;
+  constexpr bool FIXREF = DH == 64;  // chunk softmax against the window maximum
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* slots = reinterpret_cast<T*>(smem);                             // [2][ELEMS]
@@ -130,7 +131,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   // column hold the same row)
   FT qf[2][KS];
   int prow[2], wsr[2], plc[2], rr[2], cur[2];
-  size_t rowoff[2];
+  // global row index (b, head, position) of row block cb (recomputed where
+  // needed rather than held across the item loop)
+  auto row_off = [&](int cb) __attribute__((always_inline)) -> size_t {
+    const int r = 32 * w + 16 * cb + cl;
+    const int pos = min(p0 + r / G, N - 1);
+    return ((size_t)b * Hq + g * G + r % G) * N + pos;
+  };
   float lsel[2], Lr[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -141,10 +148,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
     prow[cb] = pos < N ? pos : -1;
     wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
     const int pc = pos < N ? pos : N - 1;
-    rowoff[cb] = ((size_t)b * Hq + g * G + hh) * N + pc;
-    lsel[cb] = sel_lse[rowoff[cb]];
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pc;
+    lsel[cb] = sel_lse[ro];
     cur[cb] = 0;
-    const T* src = q + rowoff[cb] * DH + 8 * gl;
+    const T* src = q + ro * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld8<T>(src + 32 * ks);
   }
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   const int ws_hi = wave_live ? n_distant(pw_hi, W, S) * S : 0;
 
   float m[2], lsum[2];
-  f32x4 oacc[MB][2];
+  f32x4 oacc[MB][2], cneg[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     m[cb] = NEG_INF;
@@ -323,6 +330,39 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
       Lr[cb] = L;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= coef;
+      // chunk phase: scores come out of the MFMA already in log2 units and
+      // shifted by the window maximum (the product's accumulator starts at
+      // -m), so each probability is one exp2
+      const float mr = live ? m[cb] : 0.f;
+      cneg[cb] = f32x4{-mr, -mr, -mr, -mr};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = scale_frag<T>(qf[cb][ks], sc2);
+    }
+  };
+
+  // ---- exp2 of a 64-token score block (log2 units, already shifted) into
+  // P^T operands; returns the row sum of the rounded probabilities (for bf16
+  // an MFMA with an all-ones operand, exactly the weights the PV product uses)
+  auto chunk_probs = [&](f32x4 (&sacc)[4], FT (&pf)[2]) __attribute__((always_inline)) -> float {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[tb][i] = fast_exp2(sacc[tb][i]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pf[ks] = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
+    if constexpr (sizeof(T) == 2) {
+      f32x4 s4 = mma16(ones_frag(), pf[0], zero4());
+      s4 = mma16(ones_frag(), pf[1], s4);
+      return s4[0];
+    } else {
+      float ps = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps += sacc[tb][i];
+      ps += shfl_xor(ps, 16);
+      ps += shfl_xor(ps, 32);
+      return ps;
     }
   };
 
@@ -351,43 +391,55 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       if ((cb == 0 ? b0 : b1) == 0) continue;
+      // d = 64: probabilities relative to the window maximum; a chunk whose
+      // scores sit out of fp32 range from it (sum not in [2^-100, 2^120]) is
+      // redone with its own maximum, which d = 128 always uses
       f32x4 sacc[4];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        sacc[tb] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(kf[tb][ks], qf[cb][ks], sacc[tb]);
-      }
-      float mx = NEG_INF;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tb][i]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mref = mx * sc2;
+      FT pf[2];
       float ps = 0.f;
+      bool redo = true;
+      if constexpr (FIXREF) {
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb) {
+          sacc[tb] = cneg[cb];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(fmaf(sacc[tb][i], sc2, -mref));
-          sacc[tb][i] = pv;
-          ps += pv;
+          for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(kf[tb][ks], qf[cb][ks], sacc[tb]);
         }
-      ps += shfl_xor(ps, 16);
-      ps += shfl_xor(ps, 32);
+        ps = chunk_probs(sacc, pf);
+        redo = __ballot(!(ps >= 0x1p-100f && ps <= 0x1p+120f)) != 0;
+      }
+      if (redo) {
+        // (d = 64 reads K from the slot again, so the fragments need not stay
+        // live through the common path)
+        if constexpr (FIXREF) asm volatile("" ::: "memory");
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          sacc[tb] = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            sacc[tb] = mma16(FIXREF ? ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks) : kf[tb][ks],
+                             qf[cb][ks], sacc[tb]);
+        }
+        float mx = NEG_INF;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tb][i]);
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) sacc[tb] -= mx;
+        ps = chunk_probs(sacc, pf);
+      }
       f32x4 oc[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oc[mb] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const FT pf = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          oc[mb] = mma16(ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks), pf, oc[mb]);
-      }
-      const float alpha = sel[cb] ? fast_exp2((sc[cb] - Lr[cb]) * LOG2E) / ps : 0.f;
+          oc[mb] = mma16(ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks), pf[ks], oc[mb]);
+      const float alpha = sel[cb] ? fast_exp2((sc[cb] - Lr[cb]) * LOG2E) * __builtin_amdgcn_rcpf(ps) : 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] += alpha * oc[mb];
     }
@@ -400,38 +452,55 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   __syncthreads();
   // one step: publish item n + 1 from register set rg into the other slot
   // (whose item n - 1 every wave has finished), reload rg with item n + 3,
-  // then multiply item n. Unrolled by two so the register sets stay fixed.
-  auto step = [&](int n, u32x4 (&rg)[SG::VPT]) __attribute__((always_inline)) {
+  // then multiply item n. Even items use register set 1, odd items set 0
+  // (loops unrolled by two so the sets stay fixed); the window items and the
+  // chunk items run in loops of their own.
+  auto wstep = [&](int n, u32x4 (&rg)[SG::VPT]) __attribute__((always_inline)) {
     commit(rg, (n + 1) & 1);
     issue(rg, n + 3);
     const T* sl = slots + (n & 1) * SG::ELEMS;
-    if (n < nW) {
-      const int kv0 = kv_lo + 64 * n;
-      if (wave_live && kv0 <= pw_hi && kv0 + 63 >= ws_lo) {
-        const bool clean = all_valid && kv0 >= ws_hi && kv0 + 63 <= pw_lo;
-        if (clean)
-          window_block(sl, kv0, std::false_type());
-        else
-          window_block(sl, kv0, std::true_type());
-      }
-      if (n == nW - 1) fuse();
-    } else {
-      chunk_block(sl, __builtin_amdgcn_readfirstlane(ulist[n - nW]));
+    const int kv0 = kv_lo + 64 * n;
+    if (wave_live && kv0 <= pw_hi && kv0 + 63 >= ws_lo) {
+      const bool clean = all_valid && kv0 >= ws_hi && kv0 + 63 <= pw_lo;
+      if (clean)
+        window_block(sl, kv0, std::false_type());
+      else
+        window_block(sl, kv0, std::true_type());
     }
     __syncthreads();
   };
-  for (int n = 0; n < NIT; n += 2) {
-    step(n, stg[1]);
-    if (n + 1 >= NIT) break;
-    step(n + 1, stg[0]);
+  auto cstep = [&](int n, u32x4 (&rg)[SG::VPT]) __attribute__((always_inline)) {
+    commit(rg, (n + 1) & 1);
+    issue(rg, n + 3);
+    chunk_block(slots + (n & 1) * SG::ELEMS, __builtin_amdgcn_readfirstlane(ulist[n - nW]));
+    __syncthreads();
+  };
+  int n = 0;
+  for (; n + 1 < nW; n += 2) {
+    wstep(n, stg[1]);
+    wstep(n + 1, stg[0]);
   }
+  if (n < nW) wstep(n++, stg[1]);
+  fuse();
+  auto chunk_loop = [&](u32x4 (&ra)[SG::VPT], u32x4 (&rb)[SG::VPT]) __attribute__((always_inline)) {
+    for (; n < NIT; n += 2) {
+      cstep(n, ra);
+      if (n + 1 >= NIT) break;
+      cstep(n + 1, rb);
+    }
+  };
+  if (nW & 1)
+    chunk_loop(stg[0], stg[1]);
+  else
+    chunk_loop(stg[1], stg[0]);
 
   // ------------------------------------------------ write o and lse
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     if (prow[cb] < 0) continue;
-    if (gl == 0) lse[rowoff[cb]] = Lr[cb];
-    T* dst = o + rowoff[cb] * DH + 4 * gl;
+    const size_t ro = row_off(cb);
+    if (gl == 0) lse[ro] = Lr[cb];
+    T* dst = o + ro * DH + 4 * gl;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if constexpr (sizeof(T) == 2) {

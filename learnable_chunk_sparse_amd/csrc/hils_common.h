@@ -86,6 +86,27 @@ template <> __device__ __forceinline__ f32x8 pack8<float>(const float* x) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// operand whose every element is 1: ones x P^T puts the column sums of P^T
+// into every row of the product
+__device__ __forceinline__ bf16x8 ones_frag() {
+  const __bf16 o = (__bf16)1.0f;
+  return bf16x8{o, o, o, o, o, o, o, o};
+}
+
+// every element of a fragment times c (rounded back to T)
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type scale_frag(const typename Frag<T>::type& f, float c) {
+  typename Frag<T>::type r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (sizeof(T) == 2)
+      r[j] = (__bf16)((float)f[j] * c);
+    else
+      r[j] = f[j] * c;
+  }
+  return r;
+}
+
 // two accumulator quads (rows 4 g + i of two 16-row blocks) -> one operand
 // fragment; the k order {0..3, 16..19}-style permutation is the same on
 // whichever operand is built this way

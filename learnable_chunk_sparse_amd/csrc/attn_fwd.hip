@@ -88,8 +88,6 @@ struct Slot {
   static constexpr int VPT = 2 * KV / 256;                // vectors per thread (K then V^T)
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 template <typename T, int G, int DH>
 __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_attn_fwd(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
@@ -106,9 +104,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
 
   extern __shared__ __align__(16) unsigned char smem[];
   T* slots = reinterpret_cast<T*>(smem);                             // [2][ELEMS]
-  int* tkc = reinterpret_cast<int*>(slots + 2 * SG::ELEMS);          // [TP][K] selected chunks
-  float* tks = reinterpret_cast<float*>(tkc + TP * K);              // [R][K] their scores
-  int* flg = reinterpret_cast<int*>(tks + R * K);                   // [C + 1] union flags / offsets
+  const int K1 = K + 1;  // selection lists end with a sentinel (-1 / 0)
+  int* tkc = reinterpret_cast<int*>(slots + 2 * SG::ELEMS);          // [TP][K + 1] selected chunks
+  float* tks = reinterpret_cast<float*>(tkc + TP * K1);             // [R][K + 1] their scores
+  int* flg = reinterpret_cast<int*>(tks + R * K1);                  // [C + 1] union flags / offsets
   int* ulist = flg + C + 1;                                         // [min(C, TP K)] union, ascending
   __shared__ int wsum[4];
 
@@ -123,14 +122,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   const int p0 = tile * TP;
   const int plast = min(p0 + TP - 1, N - 1);
   const int ndmax = n_distant(plast, W, S);
-  const T* kg = k + (size_t)bg * N * DH;
-  const T* vtg = vt + (size_t)bg * DH * Np;
+  // K and V^T of this (batch, KV head) through buffer resources: K rows past
+  // N read as zero (they are masked), V^T is padded to Np
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)bg * N * DH, N * DH * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)bg * DH * Np, DH * Np * (int)sizeof(T));
 
   // ------------------------------------------------ per-lane rows
   // wave w owns rows 32 w + 16 cb + cl, cb = 0, 1 (all four lanes of a
   // column hold the same row)
   FT qf[2][KS];
-  int prow[2], wsr[2], plc[2], rr[2], cur[2];
+  int prow[2], wsr[2], cbase[2], sbase[2], cur[2];
   // global row index (b, head, position) of row block cb (recomputed where
   // needed rather than held across the item loop)
   auto row_off = [&](int cb) __attribute__((always_inline)) -> size_t {
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   for (int cb = 0; cb < 2; ++cb) {
     const int r = 32 * w + 16 * cb + cl;
     const int pos = p0 + r / G, hh = r % G;
-    rr[cb] = r;
-    plc[cb] = r / G;
+    cbase[cb] = (r / G) * K1;
+    sbase[cb] = r * K1;
     prow[cb] = pos < N ? pos : -1;
     wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
     const int pc = pos < N ? pos : N - 1;
@@ -164,12 +165,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   const int ws_lo = wave_live ? n_distant(pw_lo, W, S) * S : 0;
   const int ws_hi = wave_live ? n_distant(pw_hi, W, S) * S : 0;
 
+  // m: the row's reference (log2 units) that probabilities are taken
+  // against, -inf until the row's first scores; cneg = -m in every element,
+  // the initial accumulator of the chunk score products
   float m[2], lsum[2];
   f32x4 oacc[MB][2], cneg[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     m[cb] = NEG_INF;
     lsum[cb] = 0.f;
+    cneg[cb] = zero4();
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] = zero4();
   }
@@ -186,16 +191,14 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
 #pragma unroll
     for (int s = 0; s < SG::VPT; ++s) {
       const int vi = tid + 256 * s;
-      const T* src;
       if (s < SG::VPT / 2) {
         const int tok = vi / (DH / SG::VE), part = vi - tok * (DH / SG::VE);
-        src = kg + (size_t)min(kv0 + tok, N - 1) * DH + part * SG::VE;
+        rg[s] = buf_ld16(krs, ((kv0 + tok) * DH + part * SG::VE) * (int)sizeof(T));
       } else {
         const int vj = vi - SG::KV;
         const int dd = vj / (64 / SG::VE), part = vj - dd * (64 / SG::VE);
-        src = vtg + (size_t)dd * Np + kv0 + part * SG::VE;
+        rg[s] = buf_ld16(vrs, (dd * Np + kv0 + part * SG::VE) * (int)sizeof(T));
       }
-      rg[s] = *reinterpret_cast<const u32x4*>(src);
     }
   };
   auto commit = [&](const u32x4 (&rg)[SG::VPT], int slot) __attribute__((always_inline)) {
@@ -221,17 +224,18 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
 
   // ------------------------------------------------ selections of the tile
   for (int x = tid; x <= ndmax; x += 256) flg[x] = 0;
-  for (int x = tid; x < TP * K; x += 256) {
-    const int pos = p0 + x / K;
-    tkc[x] = pos < N ? topk_idx[((size_t)bg * N + p0) * K + x] : -1;
+  for (int x = tid; x < TP * K1; x += 256) {
+    const int pl = x / K1, kk = x - pl * K1;
+    const int pos = p0 + pl;
+    tkc[x] = (pos < N && kk < K) ? topk_idx[((size_t)bg * N + pos) * K + kk] : -1;
   }
-  for (int x = tid; x < R * K; x += 256) {
-    const int r = x / K, kk = x - r * K;
+  for (int x = tid; x < R * K1; x += 256) {
+    const int r = x / K1, kk = x - r * K1;
     const int pos = p0 + r / G;
-    tks[x] = pos < N ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
+    tks[x] = (pos < N && kk < K) ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
   }
   __syncthreads();
-  for (int x = tid; x < TP * K; x += 256) {
+  for (int x = tid; x < TP * K1; x += 256) {
     const int c = tkc[x];
     if (c >= 0 && c < ndmax) flg[c] = 1;
   }
@@ -252,9 +256,14 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
     issue_kv(rg, n < nW ? kv_lo + 64 * n : 64 * ulist[n - nW]);
   };
 
-  // ---- window block: banded flash attention over the wave's rows
+  // ---- window block: banded flash attention over the wave's rows. The
+  // reference m moves only when a block's scores exceed it by more than 16
+  // (log2 units), or on a row's first scores; the accumulators are rescaled
+  // only then. (Scores stay in the exact fp32 product of q and k here: the
+  // window log-sum-exp is an output.)
   auto window_block = [&](const T* sl, int kv0, auto masked) __attribute__((always_inline)) {
     constexpr bool MSK = decltype(masked)::value;
+    constexpr float SHIFT_AT = 16.f;
     f32x4 sacc[4][2];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -267,7 +276,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
         for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = mma16(kf, qf[cb][ks], sacc[tb][cb]);
       }
     }
-    FT pf[2][2];
+    float bmx[2];
+    bool shift = false;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       float bmax = NEG_INF;
@@ -275,32 +285,45 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = sacc[tb][cb][i] * sc2;
+          float x = sacc[tb][cb][i];
           if constexpr (MSK) {
             const int j = kv0 + 16 * tb + 4 * gl + i;
             x = (j <= prow[cb] && j >= wsr[cb]) ? x : NEG_INF;
+            sacc[tb][cb][i] = x;
           }
-          sacc[tb][cb][i] = x;
           bmax = fmaxf(bmax, x);
         }
-      bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, shfl_xor(bmax, 32));
-      const float mnew = fmaxf(m[cb], bmax);
-      const float mref = mnew == NEG_INF ? 0.f : mnew;
-      const float alpha = fast_exp2(m[cb] - mref);
+      // block maximum relative to the reference (0 before the first scores)
+      bmx[cb] = col_max4(bmax) * sc2 - (m[cb] == NEG_INF ? 0.f : m[cb]);
+      shift |= bmx[cb] > SHIFT_AT || (m[cb] == NEG_INF && bmx[cb] != NEG_INF);
+    }
+    if (__ballot(shift) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const bool first = m[cb] == NEG_INF;
+        const bool up = bmx[cb] > SHIFT_AT || (first && bmx[cb] != NEG_INF);
+        const float dlt = up ? bmx[cb] : 0.f;
+        const float alpha = first ? 0.f : fast_exp2(-dlt);
+        if (up) m[cb] = (first ? 0.f : m[cb]) + dlt;
+        lsum[cb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
+      }
+    }
+    FT pf[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float mc = m[cb] == NEG_INF ? 0.f : m[cb];
       float ps = 0.f;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(sacc[tb][cb][i] - mref);
+          const float pv = fast_exp2(fmaf(sacc[tb][cb][i], sc2, -mc));
           sacc[tb][cb][i] = pv;
           ps += pv;
         }
-      lsum[cb] = lsum[cb] * alpha + ps;
-      m[cb] = mnew;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
+      lsum[cb] += ps;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) pf[cb][ks] = pk8<T>(sacc[2 * ks][cb], sacc[2 * ks + 1][cb]);
     }
@@ -319,9 +342,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
   auto fuse = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      float ls = lsum[cb];
-      ls += shfl_xor(ls, 16);
-      ls += shfl_xor(ls, 32);
+      const float ls = col_sum4(lsum[cb]);
       const float lW = (m[cb] + __log2f(ls)) * LN2;
       const float mx = fmaxf(lW, lsel[cb]);
       const bool live = prow[cb] >= 0;
@@ -330,24 +351,21 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
       Lr[cb] = L;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= coef;
-      // chunk phase: scores come out of the MFMA already in log2 units and
-      // shifted by the window maximum (the product's accumulator starts at
-      // -m), so each probability is one exp2
-      const float mr = live ? m[cb] : 0.f;
-      cneg[cb] = f32x4{-mr, -mr, -mr, -mr};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = scale_frag<T>(qf[cb][ks], sc2);
+      // chunk phase: the score products start from -m (in score units), so
+      // each probability is exp2 of one product times log2(e)/sqrt(d)
+      const float mr = live ? -m[cb] / sc2 : 0.f;
+      cneg[cb] = f32x4{mr, mr, mr, mr};
     }
   };
 
-  // ---- exp2 of a 64-token score block (log2 units, already shifted) into
+  // ---- exp2(x log2(e)/sqrt(d)) of a 64-token block of shifted scores into
   // P^T operands; returns the row sum of the rounded probabilities (for bf16
   // an MFMA with an all-ones operand, exactly the weights the PV product uses)
   auto chunk_probs = [&](f32x4 (&sacc)[4], FT (&pf)[2]) __attribute__((always_inline)) -> float {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[tb][i] = fast_exp2(sacc[tb][i]);
+      for (int i = 0; i < 4; ++i) sacc[tb][i] = fast_exp2(sacc[tb][i] * sc2);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) pf[ks] = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
     if constexpr (sizeof(T) == 2) {
@@ -360,9 +378,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) ps += sacc[tb][i];
-      ps += shfl_xor(ps, 16);
-      ps += shfl_xor(ps, 32);
-      return ps;
+      return col_sum4(ps);
     }
   };
 
@@ -373,10 +389,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
     unsigned long long anysel = 0;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int kk = min(cur[cb], K - 1);
-      const int kc = (prow[cb] >= 0 && cur[cb] < K) ? tkc[plc[cb] * K + kk] : -1;
-      sel[cb] = kc == c;
-      sc[cb] = tks[rr[cb] * K + kk];
+      sel[cb] = tkc[cbase[cb] + cur[cb]] == c;
+      sc[cb] = tks[sbase[cb] + cur[cb]];
       cur[cb] += sel[cb] ? 1 : 0;
     }
     const unsigned long long b0 = __ballot(sel[0]), b1 = __ballot(sel[1]);
@@ -425,8 +439,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tb][i]);
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = col_max4(mx);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) sacc[tb] -= mx;
         ps = chunk_probs(sacc, pf);
@@ -519,7 +532,7 @@ template <typename T, int G, int DH>
 static size_t fwd_lds(const Dims& p) {
   constexpr int R = 128, TP = R / G;
   size_t s = sizeof(T) * 2 * (size_t)Slot<T, DH>::ELEMS;
-  s += sizeof(int) * (size_t)TP * p.K + sizeof(float) * (size_t)R * p.K;
+  s += sizeof(int) * (size_t)TP * (p.K + 1) + sizeof(float) * (size_t)R * (p.K + 1);
   s += sizeof(int) * ((size_t)p.C + 1 + std::min<size_t>(p.C, (size_t)TP * p.K));
   return (s + 15) & ~(size_t)15;
 }

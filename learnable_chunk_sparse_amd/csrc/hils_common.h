@@ -93,6 +93,17 @@ __device__ __forceinline__ bf16x8 ones_frag() {
   return bf16x8{o, o, o, o, o, o, o, o};
 }
 
+// bf16 fragment times c as a sum of two bf16 fragments (hi + lo carries
+// ~16 significant bits of each product)
+__device__ __forceinline__ void scale_split(const bf16x8& f, float c, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float x = (float)f[j] * c;
+    hi[j] = (__bf16)x;
+    lo[j] = (__bf16)(x - (float)hi[j]);
+  }
+}
+
 // every element of a fragment times c (rounded back to T)
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::type scale_frag(const typename Frag<T>::type& f, float c) {
@@ -172,5 +183,30 @@ __device__ __forceinline__ void xcd_block(int& x, int& y) {
 
 // cross-lane helpers (lanes xor-ed within the wave)
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, WAVE); }
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one column of an MFMA
+// D fragment) with the gfx950 row-swap permutes: swapping a copy of x with
+// itself leaves {x[l], x[l^16]} (then {x[l], x[l^32]}) in the two results
+__device__ __forceinline__ float col_max4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// buffer resource over [base, base + bytes): loads past the end return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
 }  // namespace hils

@@ -52,6 +52,25 @@ def test_fwd_small_all_rows(case):
     fwd_parity(t, out, wl.S, wl.K, wl.W, dt, label=name)
 
 
+def test_fwd_extreme_token_scores():
+    """Keys of some distant chunks scaled up (token scores far above the
+    window's: exp2 against the window maximum overflows) and keys of the
+    last tokens scaled up (window maxima far above the distant chunks'
+    scores: the chunk probabilities underflow); both take the exact
+    per-chunk maximum instead."""
+    wl = Workload("extreme", seed=12, dtype="bf16", B=1, Hq=2, Hkv=2, d=64, N=1100, S=64, K=6, W=128,
+                  D=0, r=0, e_range=2.0, e_shift=6.0)
+    say("case extreme token scores")
+    t = make_inputs(wl)
+    k = t["k"].float()
+    k[:, :, 128:384] *= 45.0
+    k[:, :, 1004:] *= 45.0
+    t["k"] = k.to(torch.bfloat16)
+    out = run_fwd(wl, t)
+    torch.cuda.synchronize()
+    fwd_parity(t, out, wl.S, wl.K, wl.W, "bf16", label="extreme")
+
+
 def test_fwd_tiny_workload():
     wl = WORKLOADS["tiny"]
     say("case tiny (fp32, needle chunk 7)")

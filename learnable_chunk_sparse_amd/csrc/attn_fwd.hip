@@ -382,6 +382,77 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
     }
   };
 
+  // ---- d = 64 chunk block, both row blocks in one straight-line pass (the
+  // products of one row block overlap the softmax of the other): scores
+  // relative to the window reference; if any row's sum leaves [2^-100,
+  // 2^120] (exp2 overflow or underflow) both are redone against each row's
+  // own chunk maximum
+  auto chunk_both = [&](const T* sl, const bool (&sel)[2], const float (&sc)[2]) __attribute__((always_inline)) {
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) sacc[cb][tb] = cneg[cb];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const FT kf = ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) sacc[cb][tb] = mma16(kf, qf[cb][ks], sacc[cb][tb]);
+      }
+    }
+    FT pf[2][2];
+    float ps[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) ps[cb] = chunk_probs(sacc[cb], pf[cb]);
+    const bool bad = !(ps[0] >= 0x1p-100f && ps[0] <= 0x1p+120f) || !(ps[1] >= 0x1p-100f && ps[1] <= 0x1p+120f);
+    if (__ballot(bad) != 0) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) sacc[cb][tb] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const FT kf = ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) sacc[cb][tb] = mma16(kf, qf[cb][ks], sacc[cb][tb]);
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        float mx = NEG_INF;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[cb][tb][i]);
+        mx = col_max4(mx);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) sacc[cb][tb] -= mx;
+        ps[cb] = chunk_probs(sacc[cb], pf[cb]);
+      }
+    }
+    const T* vb = sl + SG::KE;
+    f32x4 oc[2][MB];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oc[cb][mb] = zero4();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const FT vf = ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) oc[cb][mb] = mma16(vf, pf[cb][ks], oc[cb][mb]);
+      }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float alpha = sel[cb] ? fast_exp2((sc[cb] - Lr[cb]) * LOG2E) * __builtin_amdgcn_rcpf(ps[cb]) : 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] += alpha * oc[cb][mb];
+    }
+  };
+
   // ---- chunk block: rows that selected chunk c add exp(s_c - L) O_c
   auto chunk_block = [&](const T* sl, int c) __attribute__((always_inline)) {
     bool sel[2];
@@ -396,6 +467,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
     const unsigned long long b0 = __ballot(sel[0]), b1 = __ballot(sel[1]);
     anysel = b0 | b1;
     if (anysel == 0) return;
+    if constexpr (FIXREF) {
+      chunk_both(sl, sel, sc);
+      return;
+    }
     FT kf[4][KS];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)

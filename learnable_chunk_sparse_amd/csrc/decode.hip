@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   const int Hq = Hkv * G;
   const int n = seq_n(seq_len, b, N);
   const int nd = n_distant(n - 1, W, S);
-  const int c_w = split * CPW + 64 * w;  // this wave's first chunk
+  const int c_w = split * CPW + (CPW / 4) * w;  // this wave's first chunk (16 ST chunks per wave)
   if (c_w >= nd) return;
   const T* kLg = kL + (size_t)bg * C * DH;
   const T* eg = e + (size_t)bg * C;

@@ -31,7 +31,7 @@ namespace hils {
 
 namespace {
 
-constexpr int CPW = 512;  // chunks per scan workgroup
+constexpr int CPW = 2048;  // chunks per scan workgroup
 
 __device__ __forceinline__ int seq_n(const int32_t* seq_len, int b, int N) {
   if (seq_len == nullptr) return N;
@@ -48,6 +48,10 @@ __device__ __forceinline__ uint32_t ord_f(float f) {
 }  // namespace
 
 // ---------------------------------------------------------------- scan
+// D[head][chunk] = q_h . kL_c: the query heads are the A operand (rows; hi
+// and lo bf16 halves of an fp32 query accumulate into the same product), the
+// landmark rows the B operand (columns), so lane (g, c) ends with the scores
+// of chunk c for heads 4 g .. 4 g + 3 and the max over heads is in-lane.
 template <typename T, typename QT, int G, int DH>
 __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
@@ -57,73 +61,79 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   typedef typename Frag<T>::type FT;
   constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
   constexpr int KS = DH / 32;
-  constexpr int NPART = HAS_LO ? 2 : 1;
-  constexpr int ST = CPW / 64;  // 16-chunk steps per wave
+  constexpr int NST = CPW / 64;  // 16-chunk steps per wave
+  constexpr int PD = 4;          // steps in flight per wave
+  static_assert(G <= 8 && NST % PD == 0, "scan shape");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int gl = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   const int n = seq_n(seq_len, b, N);
   const int nd = n_distant(n - 1, W, S);
-  const int c_w = split * CPW + (CPW / 4) * w;  // this wave's first chunk (16 ST chunks per wave)
+  const int c_w = split * CPW + (CPW / 4) * w;  // this wave's first chunk
   if (c_w >= nd) return;
+  const int last = min(NST, (nd - c_w + 15) / 16);  // steps holding a distant chunk
   const T* kLg = kL + (size_t)bg * C * DH;
   const T* eg = e + (size_t)bg * C;
-  // all of the wave's landmark rows are requested before any product
-  FT ka[ST][KS];
-  float eb[ST];
+  // ring of PD steps: landmark rows chunk c_w + 16 st + col, dims 8 gl + 32 ks
+  // (B operand), and the chunk's bias
+  FT kb[PD][KS];
+  float eb[PD];
+  auto load = [&](int st, FT (&kd)[KS], float& ed) __attribute__((always_inline)) {
+    const int c = min(c_w + 16 * st + col, nd - 1);
 #pragma unroll
-  for (int st = 0; st < ST; ++st) {
-    const int c = min(c_w + 16 * st + (lane & 15), nd - 1);
+    for (int ks = 0; ks < KS; ++ks) kd[ks] = ld8<T>(kLg + (size_t)c * DH + 8 * gl + 32 * ks);
+    ed = to_f<T>(eg[c]);
+  };
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[st][ks] = ld8<T>(kLg + (size_t)c * DH + 8 * (lane >> 4) + 32 * ks);
-    const int ce = min(c_w + 16 * st + 4 * ((lane >> 4) & 3) + (lane & 3), nd - 1);
-    eb[st] = to_f<T>(eg[ce]);
-  }
-  // B operand: column col = part * G + h holds the hi (part 0) or lo (part 1)
-  // bf16 half of query head h; other columns are zero.
-  FT bq[KS];
+  for (int j = 0; j < PD; ++j) load(j, kb[j], eb[j]);
+  // A operand: row h < G holds query head h (hi part; lo part in qlo)
+  FT qa[KS], qlo[HAS_LO ? KS : 1];
   {
-    const int col = lane & 15;
-    const int h = col % G, part = col / G;
-    const bool live = col < NPART * G;
-    const QT* src = qs + ((size_t)b * Hq + g * G + h) * DH + 8 * (lane >> 4);
+    const bool live = col < G;
+    const QT* src = qs + ((size_t)b * Hq + g * G + (live ? col : 0)) * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // one vector load per fragment (no per-element branches: those drain
+      // the landmark loads already in flight)
+      const auto raw = ld8<QT>(src + 32 * ks);
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = live ? to_f<QT>(src[32 * ks + j]) : 0.f;
+      for (int j = 0; j < 8; ++j) x[j] = live ? (float)raw[j] : 0.f;
+      qa[ks] = pack8<T>(x);
       if constexpr (HAS_LO) {
-        const auto hi = pack8<T>(x);
-        if (part == 1) {
-          const u16x8 hb = __builtin_bit_cast(u16x8, hi);
+        const u16x8 hb = __builtin_bit_cast(u16x8, qa[ks]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = x[j] - bf2f(hb[j]);
-        }
+        for (int j = 0; j < 8; ++j) x[j] -= bf2f(hb[j]);
+        qlo[ks] = pack8<T>(x);
       }
-      bq[ks] = pack8<T>(x);
     }
   }
-  float* dst = scores + (size_t)bg * Cp;
+  float* dst = scores + (size_t)bg * Cp + c_w;
+  // fully unrolled, so the waits on the ring are exact (a loop back edge
+  // would drain every load in flight)
 #pragma unroll
-  for (int st = 0; st < ST; ++st) {
-    f32x4 acc = zero4();
+  for (int st = 0; st < NST; st += PD) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = mma16(ka[st][ks], bq[ks], acc);
-    // lane holds D[chunk 4*(lane/16)+i][col lane%16]: add hi + lo, max over heads
+    for (int j = 0; j < PD; ++j) {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = acc[i];
-      if constexpr (HAS_LO) v += __shfl_xor(v, G, 64);
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = mma16(qa[ks], kb[j][ks], acc);
+        if constexpr (HAS_LO) acc = mma16(qlo[ks], kb[j][ks], acc);
+      }
+      float v = acc[0];
 #pragma unroll
-      for (int m = 1; m < G; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-      acc[i] = v;
+      for (int i = 1; i < (G < 4 ? G : 4); ++i) v = fmaxf(v, acc[i]);
+      if constexpr (G == 8) {  // heads 4..7 sit in the lanes 16 above
+        auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float out = fmaf(v, scale, eb[j]);
+      if (gl == 0 && st + j < last) dst[16 * (st + j) + col] = out;
+      if (st + j + PD < NST) load(st + j + PD, kb[j], eb[j]);
     }
-    // the bias of chunk 4*(lane/16)+i was fetched by lane 16*(lane/16) + i
-    f32x4 out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = fmaf(acc[i], scale, __shfl(eb[st], (lane & 48) + i, 64));
-    if ((lane & 15) == 0) *reinterpret_cast<f32x4*>(dst + c_w + 16 * st + 4 * (lane >> 4)) = out;
   }
 }
 
@@ -321,9 +331,10 @@ __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const
     const T* src = q + ((size_t)b * Hq + g * G + h) * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      const FT raw = ld8<T>(src + 32 * ks);
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = col < G ? to_f<T>(src[32 * ks + j]) : 0.f;
+      for (int j = 0; j < 8; ++j) x[j] = col < G ? (float)raw[j] : 0.f;
       qf[ks] = pack8<T>(x);
     }
   }

@@ -73,15 +73,19 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   const int nd = n_distant(n - 1, W, S);
   const int c_w = split * CPW + (CPW / 4) * w;  // this wave's first chunk
   if (c_w >= nd) return;
-  const int last = min(NST, (nd - c_w + 15) / 16);  // steps holding a distant chunk
   const T* kLg = kL + (size_t)bg * C * DH;
   const T* eg = e + (size_t)bg * C;
   // ring of PD steps: landmark rows chunk c_w + 16 st + col, dims 8 gl + 32 ks
   // (B operand), and the chunk's bias
   FT kb[PD][KS];
   float eb[PD];
+  // waves walk their steps from different starting points, so that the
+  // thousands of concurrent streams (whose bases are a power of two apart)
+  // spread over the HBM channels instead of moving through them in lockstep
+  const int rot = (bg * 7 + split * 13 + w * 5) & (NST - 1);
+  auto cstep = [&](int st) __attribute__((always_inline)) { return c_w + 16 * ((st + rot) & (NST - 1)); };
   auto load = [&](int st, FT (&kd)[KS], float& ed) __attribute__((always_inline)) {
-    const int c = min(c_w + 16 * st + col, nd - 1);
+    const int c = min(cstep(st) + col, nd - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kd[ks] = ld8<T>(kLg + (size_t)c * DH + 8 * gl + 32 * ks);
     ed = to_f<T>(eg[c]);
@@ -110,7 +114,10 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
       }
     }
   }
-  float* dst = scores + (size_t)bg * Cp + c_w;
+  // scores are collected in LDS and written once per wave as whole lines
+  // (scattered 64-byte stores between the reads cost ~10% of the scan)
+  __shared__ __align__(16) float sbuf[4][CPW / 4];
+  float* sw = sbuf[w];
   // fully unrolled, so the waits on the ring are exact (a loop back edge
   // would drain every load in flight)
 #pragma unroll
@@ -131,9 +138,16 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
         v = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       const float out = fmaf(v, scale, eb[j]);
-      if (gl == 0 && st + j < last) dst[16 * (st + j) + col] = out;
+      if (gl == 0) sw[cstep(st + j) - c_w + col] = out;
       if (st + j + PD < NST) load(st + j + PD, kb[j], eb[j]);
     }
+  }
+  wave_lds_sync();
+  float* dst = scores + (size_t)bg * Cp + c_w;
+#pragma unroll
+  for (int x = 0; x < CPW / 4 / 256; ++x) {
+    const int o = 4 * (lane + 64 * x);
+    *reinterpret_cast<f32x4*>(dst + o) = *reinterpret_cast<const f32x4*>(sw + o);
   }
 }
 

@@ -5,21 +5,25 @@
 // The step is bound by HBM bandwidth: every distant landmark key is read once
 // (the O(L/S) per-token retrieval term), then only the K selected chunks and
 // the window. Four launches:
-//   k_dec_scan    streaming landmark scan: each workgroup scores CPW chunks of
-//                 one (sequence, KV head) with 16x16x32 MFMAs (rows = chunks,
-//                 columns = the group's heads, hi and lo halves of the fp32
-//                 query), takes the max over heads and stores the score.
-//   k_dec_select  per (sequence, KV head): the K-th largest score by a 4-pass
-//                 8-bit radix select over order-preserving integer keys, ties
-//                 resolved by lower chunk index, and the chosen ids written in
-//                 ascending order by a prefix sum (no sort).
-//   k_dec_attn    one wave per 64-token unit (a selected chunk or a window
-//                 block) for all G heads: S^T = K Q^T on MFMA, softmax, O^T =
-//                 V^T P^T; the V^T operands come from the row-major V
-//                 fragments by a product with the identity (exact), so nothing
-//                 is staged in LDS. A chunk unit leaves (log-weight s_c,
-//                 weight 1, O_c); a window block leaves its (max, sum,
-//                 unnormalised output).
+//   k_dec_scan    streaming landmark scan: each wave scores CPW/4 chunks of
+//                 one (sequence, KV head) with 16x16x32 MFMAs (rows = the
+//                 group's query heads, hi and lo halves of an fp32 query;
+//                 columns = chunks), a ring of four 16-chunk steps in flight;
+//                 the max over heads is in-lane; scores go out through LDS.
+//   k_dec_select_window
+//                 blocks 0 .. B Hkv - 1: the top-K of one (sequence, KV head)
+//                 by a 4-pass 8-bit radix select over order-preserving integer
+//                 keys held in registers, ties resolved by lower chunk index,
+//                 the chosen ids written in ascending order by a prefix sum (no
+//                 sort). The other blocks run the window units, which do not
+//                 depend on the selection and keep HBM busy meanwhile.
+//   k_dec_chunks  the selected-chunk units.
+//                 A unit is one wave over 64 tokens for all G heads: S^T = K Q^T
+//                 on MFMA, softmax, O^T = V^T P^T; the V^T operands come from
+//                 the row-major V fragments by a product with the identity
+//                 (exact), so nothing is staged in LDS. A chunk unit leaves
+//                 (log-weight s_c, weight 1, O_c); a window block leaves its
+//                 (max, sum, unnormalised output).
 //   k_dec_combine per (sequence, query head): log-sum-exp merge of all units,
 //                 which is exactly the fusion softmax over {s_c} and lse_W.
 #include "hils_common.h"
@@ -152,8 +156,8 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
 }
 
 // ---------------------------------------------------------------- select
-// exclusive prefix sum of v over the 1024 threads of the block; total as well
-__device__ __forceinline__ int block_scan1024(int v, int* wsum, int& total) {
+// exclusive prefix sum of v over the 256 threads of the block; total as well
+__device__ __forceinline__ int block_scan256(int v, int* wsum, int& total) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int x = v;
 #pragma unroll
@@ -165,7 +169,7 @@ __device__ __forceinline__ int block_scan1024(int v, int* wsum, int& total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const int s2 = wsum[j];
     base += j < w ? s2 : 0;
     tot += s2;
@@ -176,39 +180,57 @@ __device__ __forceinline__ int block_scan1024(int v, int* wsum, int& total) {
 }
 
 // The K largest scores of one (sequence, KV head) by (score desc, index asc),
-// written as ascending chunk ids, -1 padded.
-__global__ __launch_bounds__(1024) void k_dec_select(const float* __restrict__ scores,
-                                                     const int32_t* __restrict__ seq_len,
-                                                     int32_t* __restrict__ sel,
-                                                     int32_t* __restrict__ topk_out, int N, int Cp,
-                                                     int Hkv, int K, int W, int S) {
+// written as ascending chunk ids, -1 padded; one 256-thread block. Thread t
+// holds the order-preserving integer keys of chunks [t PER, t PER + PER) in
+// registers (contiguous ranges, so prefix sums follow index order); the exact
+// key T of the K-th largest score comes from a 4-pass 8-bit radix select,
+// and krem of the keys equal to T (the lowest indices) are taken.
+template <int PER>
+__device__ __forceinline__ void select_block(const float* __restrict__ src, int nd, int K,
+                                             int32_t* __restrict__ sel, int32_t* __restrict__ topk_out) {
   __shared__ int hist[256];
-  __shared__ int wsum[16];
+  __shared__ int wsum[4];
   __shared__ uint32_t s_prefix, s_mask;
   __shared__ int s_krem;
   const int t = threadIdx.x;
-  const int bg = blockIdx.x, b = bg / Hkv;
-  const int nd = n_distant(seq_n(seq_len, b, N) - 1, W, S);
-  const float* src = scores + (size_t)bg * Cp;
+  const int lo = t * PER;
+  // vector loads (the score buffer is padded to at least 256 PER entries);
+  // key 0 marks a slot past the last distant chunk (no finite score maps to 0)
+  uint32_t key[PER];
+#pragma unroll
+  for (int j4 = 0; j4 < PER / 4; ++j4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + lo + 4 * j4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[4 * j4 + i] = lo + 4 * j4 + i < nd ? ord_f(x[i]) : 0u;
+  }
   const bool take_all = nd <= K;
   if (t == 0) {
     s_prefix = 0u;
     s_mask = 0u;
     s_krem = K;
   }
-  __syncthreads();
-  // radix select: the exact key T of the K-th largest score, and how many of
-  // the keys equal to T are taken (krem)
   if (!take_all) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      if (t < 256) hist[t] = 0;
+      hist[t] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix, mask = s_mask;
-      for (int c = t; c < nd; c += 1024) {
-        const uint32_t key = ord_f(src[c]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      // neighbouring chunks mostly share the high digits: runs of one bin are
+      // added at once (far fewer lanes hit one LDS address per instruction)
+      int pb = -1, pc = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (key[j] != 0u && (key[j] & mask) == prefix) {
+          const int bin = (key[j] >> shift) & 255;
+          if (bin != pb) {
+            if (pc > 0) atomicAdd(&hist[pb], pc);
+            pb = bin;
+            pc = 0;
+          }
+          ++pc;
+        }
       }
+      if (pc > 0) atomicAdd(&hist[pb], pc);
       __syncthreads();
       if (t < 64) {
         // lane t holds bins 4t .. 4t+3; keys in higher bins rank above
@@ -238,63 +260,196 @@ __global__ __launch_bounds__(1024) void k_dec_select(const float* __restrict__ s
       }
       __syncthreads();
     }
+  } else {
+    __syncthreads();
   }
   const uint32_t T = s_prefix;
   const int krem = s_krem;
-  // contiguous index ranges per thread, so that prefix sums follow index order
-  const int per = (nd + 1023) / 1024;
-  const int lo = min(nd, t * per), hi = min(nd, lo + per);
   int ties = 0;
-  if (!take_all)
-    for (int c = lo; c < hi; ++c) ties += ord_f(src[c]) == T;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) ties += (!take_all && key[j] == T) ? 1 : 0;
   int tot;
-  const int tie0 = block_scan1024(ties, wsum, tot);
-  auto taken = [&](int c, int& tr) {
-    if (take_all) return true;
-    const uint32_t key = ord_f(src[c]);
-    const bool tk = key > T || (key == T && tr < krem);
-    tr += key == T;
+  const int tie0 = block_scan256(ties, wsum, tot);
+  // chunk lo + j is taken: above T, or equal to T among the first krem ties
+  // (tr counts the ties before it)
+  auto taken = [&](int j, int& tr) __attribute__((always_inline)) {
+    const bool valid = key[j] != 0u;
+    const bool eq = !take_all && key[j] == T;
+    const bool tk = valid && (take_all || key[j] > T || (eq && tr < krem));
+    tr += eq ? 1 : 0;
     return tk;
   };
   int cnt = 0;
   {
     int tr = tie0;
-    for (int c = lo; c < hi; ++c) cnt += taken(c, tr) ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cnt += taken(j, tr) ? 1 : 0;
   }
-  const int out0 = block_scan1024(cnt, wsum, tot);
+  int o = block_scan256(cnt, wsum, tot);
   {
-    int tr = tie0, o = out0;
-    for (int c = lo; c < hi; ++c) {
-      if (taken(c, tr)) {
-        sel[(size_t)bg * K + o] = c;
-        if (topk_out != nullptr) topk_out[(size_t)bg * K + o] = c;
+    int tr = tie0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (taken(j, tr)) {
+        sel[o] = lo + j;
+        if (topk_out != nullptr) topk_out[o] = lo + j;
         ++o;
       }
     }
   }
-  for (int k2 = tot + t; k2 < K; k2 += 1024) {
-    sel[(size_t)bg * K + k2] = -1;
-    if (topk_out != nullptr) topk_out[(size_t)bg * K + k2] = -1;
+  for (int k2 = tot + t; k2 < K; k2 += 256) {
+    sel[k2] = -1;
+    if (topk_out != nullptr) topk_out[k2] = -1;
+  }
+}
+
+// larger chunk counts: keys re-read from the score buffer on every pass,
+// eight per thread and iteration (the buffer is padded to a multiple of 2048)
+__device__ __forceinline__ void select_block_big(const float* __restrict__ src, int nd, int K,
+                                                 int32_t* __restrict__ sel, int32_t* __restrict__ topk_out) {
+  __shared__ int hist[256];
+  __shared__ int wsum[4];
+  __shared__ uint32_t s_prefix, s_mask;
+  __shared__ int s_krem;
+  const int t = threadIdx.x;
+  const bool take_all = nd <= K;
+  if (t == 0) {
+    s_prefix = 0u;
+    s_mask = 0u;
+    s_krem = K;
+  }
+  __syncthreads();
+  auto keys8 = [&](int c0, uint32_t (&kk)[8]) __attribute__((always_inline)) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(src + c0);
+    const f32x4 b2 = *reinterpret_cast<const f32x4*>(src + c0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kk[i] = c0 + i < nd ? ord_f(a[i]) : 0u;
+      kk[4 + i] = c0 + 4 + i < nd ? ord_f(b2[i]) : 0u;
+    }
+  };
+  if (!take_all) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[t] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix, mask = s_mask;
+      for (int c0 = 8 * t; c0 < nd; c0 += 2048) {
+        uint32_t kk[8];
+        keys8(c0, kk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (kk[i] != 0u && (kk[i] & mask) == prefix) atomicAdd(&hist[(kk[i] >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (t < 64) {
+        int h4[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h4[j] = hist[4 * t + j];
+          sum += h4[j];
+        }
+        int x = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_down(x, o, 64);
+          if (t + o < 64) x += y;
+        }
+        const int krem = s_krem;
+        int above = x - sum;
+        for (int j = 3; j >= 0; --j) {
+          const int with = above + h4[j];
+          if (above < krem && krem <= with) {
+            s_prefix = prefix | ((uint32_t)(4 * t + j) << shift);
+            s_mask = mask | (255u << shift);
+            s_krem = krem - above;
+          }
+          above = with;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const uint32_t T = s_prefix;
+  const int krem = s_krem;
+  // contiguous ranges of a multiple of 8 chunks per thread (prefix sums follow
+  // index order)
+  const int per = ((nd + 255) / 256 + 7) / 8 * 8;
+  const int lo = min(nd, t * per), hi = min(nd, lo + per);
+  int ties = 0;
+  if (!take_all)
+    for (int c0 = lo; c0 < hi; c0 += 8) {
+      uint32_t kk[8];
+      keys8(c0, kk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ties += kk[i] == T ? 1 : 0;
+    }
+  int tot;
+  const int tie0 = block_scan256(ties, wsum, tot);
+  auto taken = [&](uint32_t key, int& tr) __attribute__((always_inline)) {
+    const bool eq = !take_all && key == T;
+    const bool tk = key != 0u && (take_all || key > T || (eq && tr < krem));
+    tr += eq ? 1 : 0;
+    return tk;
+  };
+  int cnt = 0;
+  {
+    int tr = tie0;
+    for (int c0 = lo; c0 < hi; c0 += 8) {
+      uint32_t kk[8];
+      keys8(c0, kk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cnt += taken(kk[i], tr) ? 1 : 0;
+    }
+  }
+  const int out0 = block_scan256(cnt, wsum, tot);
+  {
+    int tr = tie0, o = out0;
+    for (int c0 = lo; c0 < hi; c0 += 8) {
+      uint32_t kk[8];
+      keys8(c0, kk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (taken(kk[i], tr)) {
+          sel[o] = c0 + i;
+          if (topk_out != nullptr) topk_out[o] = c0 + i;
+          ++o;
+        }
+      }
+    }
+  }
+  for (int k2 = tot + t; k2 < K; k2 += 256) {
+    sel[k2] = -1;
+    if (topk_out != nullptr) topk_out[k2] = -1;
   }
 }
 
 // ---------------------------------------------------------------- attention units
 // partials per (bg, unit, head): pml = [m, l], po = U[0..DH)
+struct DecArgs {
+  const int32_t* seq_len;
+  const int32_t* sel;
+  float *pml, *po;
+  int N, C, Hkv, K, W, S, units;
+  float scale;
+};
+
+// one wave: unit u of (sequence, KV head) bg
 template <typename T, typename QT, int G, int DH>
-__global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const QT* __restrict__ qs,
-                                                  const T* __restrict__ k, const T* __restrict__ v,
-                                                  const T* __restrict__ kL, const T* __restrict__ e,
-                                                  const int32_t* __restrict__ seq_len,
-                                                  const int32_t* __restrict__ sel,
-                                                  float* __restrict__ pml, float* __restrict__ po,
-                                                  int N, int C, int Hkv, int K, int W, int S,
-                                                  float scale, int units) {
+__device__ __forceinline__ void dec_unit(const T* __restrict__ q, const QT* __restrict__ qs,
+                                         const T* __restrict__ k, const T* __restrict__ v,
+                                         const T* __restrict__ kL, const T* __restrict__ e,
+                                         const DecArgs& a, int bg, int u) {
   typedef typename Frag<T>::type FT;
   constexpr int KS = DH / 32, MB = DH / 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int gl = lane >> 4, col = lane & 15;
-  const int u = blockIdx.x * 4 + w;
-  const int bg = blockIdx.y;
+  const int32_t* seq_len = a.seq_len;
+  const int32_t* sel = a.sel;
+  float* pml = a.pml;
+  float* po = a.po;
+  const int N = a.N, C = a.C, Hkv = a.Hkv, K = a.K, W = a.W, S = a.S, units = a.units;
+  const float scale = a.scale;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   if (u >= units) return;
@@ -448,6 +603,45 @@ __global__ __launch_bounds__(256) void k_dec_attn(const T* __restrict__ q, const
   }
 }
 
+// selections (one block per (sequence, KV head)) and, alongside in the same
+// launch, the window units, which do not depend on them
+template <typename T, typename QT, int G, int DH, int PER>
+__global__ __launch_bounds__(256) void k_dec_select_window(const float* __restrict__ scores,
+                                                           int32_t* __restrict__ topk_out, int Cp,
+                                                           int nbg, int wpb, const T* __restrict__ q,
+                                                           const QT* __restrict__ qs,
+                                                           const T* __restrict__ k,
+                                                           const T* __restrict__ v,
+                                                           const T* __restrict__ kL,
+                                                           const T* __restrict__ e, DecArgs a) {
+  const int blk = blockIdx.x;
+  if (blk < nbg) {
+    const int bg = blk, b = bg / a.Hkv;
+    const int nd = n_distant(seq_n(a.seq_len, b, a.N) - 1, a.W, a.S);
+    int32_t* sl = const_cast<int32_t*>(a.sel) + (size_t)bg * a.K;
+    int32_t* to = topk_out != nullptr ? topk_out + (size_t)bg * a.K : nullptr;
+    if (nd <= 256 * PER)
+      select_block<PER>(scores + (size_t)bg * Cp, nd, a.K, sl, to);
+    else
+      select_block_big(scores + (size_t)bg * Cp, nd, a.K, sl, to);
+    return;
+  }
+  const int x = blk - nbg;
+  const int bg = x / wpb;
+  const int u = a.K + 4 * (x - bg * wpb) + (threadIdx.x >> 6);
+  if (u < a.units) dec_unit<T, QT, G, DH>(q, qs, k, v, kL, e, a, bg, u);
+}
+
+// the selected-chunk units
+template <typename T, typename QT, int G, int DH>
+__global__ __launch_bounds__(256) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
+                                                    const T* __restrict__ k, const T* __restrict__ v,
+                                                    const T* __restrict__ kL, const T* __restrict__ e,
+                                                    DecArgs a) {
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (u < a.K) dec_unit<T, QT, G, DH>(q, qs, k, v, kL, e, a, blockIdx.y, u);
+}
+
 // ---------------------------------------------------------------- combine
 // one wave per (sequence, query head): lanes first take units (max, weights),
 // then dims (the weighted sum, eight units' loads in flight at a time)
@@ -516,7 +710,9 @@ size_t carve(const Dims& p, void* base, DecWs* w) {
   char* c = static_cast<char*>(base);
   size_t off = 0;
   w->nsplit = std::max(1, (p.C + CPW - 1) / CPW);
-  w->Cp = w->nsplit * CPW;
+  // scores padded for the selection's vector loads: a multiple of 2048 and
+  // at least 256 * 32 (one register set of keys per thread)
+  w->Cp = std::max(w->nsplit * CPW, 8192);
   w->units = p.K + (p.W + p.S - 1 + 63) / 64 + 1;
   auto take = [&](size_t bytes) {
     void* ptr = c ? c + off : nullptr;
@@ -549,13 +745,21 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
                      p.Hkv, p.W, p.S, p.scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_dec_select, dim3(p.B * p.Hkv), dim3(1024), 0, st, (const float*)w.scores,
-                     seq_len, w.sel, topk_idx, p.N, w.Cp, p.Hkv, p.K, p.W, p.S);
+  DecArgs a;
+  a.seq_len = seq_len;
+  a.sel = w.sel;
+  a.pml = w.pml;
+  a.po = w.po;
+  a.N = p.N; a.C = p.C; a.Hkv = p.Hkv; a.K = p.K; a.W = p.W; a.S = p.S; a.units = w.units;
+  a.scale = p.scale;
+  const int nbg = p.B * p.Hkv;
+  const int wpb = (w.units - p.K + 3) / 4;  // window units: four per block
+  hipLaunchKernelGGL((k_dec_select_window<T, QT, G, DH, 32>), dim3(nbg * (1 + wpb)), dim3(256), 0, st,
+                     (const float*)w.scores, topk_idx, w.Cp, nbg, wpb, (const T*)q, (const QT*)qs,
+                     (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((k_dec_attn<T, QT, G, DH>), dim3((w.units + 3) / 4, p.B * p.Hkv), dim3(256), 0,
-                     st, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
-                     (const T*)e, seq_len, w.sel, w.pml, w.po, p.N, p.C, p.Hkv, p.K, p.W, p.S,
-                     p.scale, w.units);
+  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH>), dim3((p.K + 3) / 4, nbg), dim3(256), 0, st,
+                     (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, (const float*)w.pml,
                      (const float*)w.po, (T*)o, lse, p.Hkv, G, w.units);

@@ -5,18 +5,22 @@
 // The step is bound by HBM bandwidth: every distant landmark key is read once
 // (the O(L/S) per-token retrieval term), then only the K selected chunks and
 // the window. Four launches:
-//   k_dec_scan    streaming landmark scan: each wave scores CPW/4 chunks of
+//   k_dec_scan    streaming landmark scan: each wave scores 512 chunks of
 //                 one (sequence, KV head) with 16x16x32 MFMAs (rows = the
 //                 group's query heads, hi and lo halves of an fp32 query;
 //                 columns = chunks), a ring of four 16-chunk steps in flight;
-//                 the max over heads is in-lane; scores go out through LDS.
+//                 the max over heads is in-lane. The wave then keeps the top
+//                 min(K, 512) of its 512 scores (by score, then lower index;
+//                 a wave-level radix select in LDS) as candidates, in chunk
+//                 order: every chunk of the overall top-K is among them.
 //   k_dec_select_window
-//                 blocks 0 .. B Hkv - 1: the top-K of one (sequence, KV head)
-//                 by a 4-pass 8-bit radix select over order-preserving integer
-//                 keys held in registers, ties resolved by lower chunk index,
-//                 the chosen ids written in ascending order by a prefix sum (no
-//                 sort). The other blocks run the window units, which do not
-//                 depend on the selection and keep HBM busy meanwhile.
+//                 blocks 0 .. B Hkv - 1: the top-K of one (sequence, KV head)'s
+//                 candidates by a 4-pass 8-bit radix select over
+//                 order-preserving integer keys held in registers, ties
+//                 resolved by lower chunk index, the chosen ids written in
+//                 ascending order by a prefix sum (no sort). The other blocks
+//                 run the window units, which do not depend on the selection
+//                 and keep HBM busy meanwhile.
 //   k_dec_chunks  the selected-chunk units.
 //                 A unit is one wave over 64 tokens for all G heads: S^T = K Q^T
 //                 on MFMA, softmax, O^T = V^T P^T; the V^T operands come from
@@ -51,6 +55,122 @@ __device__ __forceinline__ uint32_t ord_f(float f) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- wave top-K
+// exclusive prefix sum over the 64 lanes of a wave; total as well
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, 63, 64);
+  return x - v;
+}
+
+// The kc = min(Kc, valid) best of 512 scores sc[0..512) (chunk ids c0 + i,
+// those >= nd absent) by (score desc, index asc), written in ascending chunk
+// order to os / oi; slots kc .. Kc-1 get id -1. One wave; lane l holds
+// entries 8l .. 8l + 7 as order-preserving keys; the exact key T of the
+// kc-th best comes from a 4-pass 8-bit radix select over a wave-private
+// LDS histogram, and the first krem keys equal to T (lowest indices) are
+// taken. Any chunk of the overall top-K is in the top-K of its own 512.
+__device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, int nd, int Kc,
+                                          float* __restrict__ os, int32_t* __restrict__ oi,
+                                          int* __restrict__ hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kk[8];
+  float sv[8];
+  {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(sc + 8 * lane);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(sc + 8 * lane + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = x0[i];
+      sv[4 + i] = x1[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kk[i] = c0 + 8 * lane + i < nd ? ord_f(sv[i]) : 0u;
+  }
+  const int nv = min(512, nd - c0);
+  const int kc = min(Kc, nv);
+  const bool all = nv <= kc;
+  uint32_t prefix = 0u, mask = 0u;
+  int krem = kc;
+  if (!all) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      *reinterpret_cast<int4*>(hist + 4 * lane) = int4{0, 0, 0, 0};
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (kk[i] != 0u && (kk[i] & mask) == prefix) atomicAdd(&hist[(kk[i] >> shift) & 255], 1);
+      wave_lds_sync();
+      const int4 h = *reinterpret_cast<const int4*>(hist + 4 * lane);
+      const int h4[4] = {h.x, h.y, h.z, h.w};
+      const int sum = h4[0] + h4[1] + h4[2] + h4[3];
+      int x = sum;  // sum over lanes >= this one (higher bins rank above)
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(x, o, 64);
+        if (lane + o < 64) x += y;
+      }
+      int above = x - sum, hit_bin = -1, hit_k = 0;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const int with = above + h4[j];
+        if (above < krem && krem <= with) {
+          hit_bin = 4 * lane + j;
+          hit_k = krem - above;
+        }
+        above = with;
+      }
+      const unsigned long long hb = __ballot(hit_bin >= 0);
+      const int src = __builtin_ctzll(hb);
+      const int bin = __shfl(hit_bin, src, 64);
+      krem = __shfl(hit_k, src, 64);
+      prefix |= (uint32_t)bin << shift;
+      mask |= 255u << shift;
+      wave_lds_sync();
+    }
+  }
+  const uint32_t T = prefix;
+  int ties = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ties += (!all && kk[i] == T) ? 1 : 0;
+  int tot;
+  const int tie0 = wave_excl_scan(ties, tot);
+  auto taken = [&](int i, int& tr) __attribute__((always_inline)) {
+    const bool eq = !all && kk[i] == T;
+    const bool tk = kk[i] != 0u && (all || kk[i] > T || (eq && tr < krem));
+    tr += eq ? 1 : 0;
+    return tk;
+  };
+  int cnt = 0;
+  {
+    int tr = tie0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += taken(i, tr) ? 1 : 0;
+  }
+  int o = wave_excl_scan(cnt, tot);
+  {
+    int tr = tie0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (taken(i, tr)) {
+        os[o] = sv[i];
+        oi[o] = c0 + 8 * lane + i;
+        ++o;
+      }
+    }
+  }
+  for (int x = tot + lane; x < Kc; x += 64) {
+    os[x] = 0.f;
+    oi[x] = -1;
+  }
+}
+
 // ---------------------------------------------------------------- scan
 // D[head][chunk] = q_h . kL_c: the query heads are the A operand (rows; hi
 // and lo bf16 halves of an fp32 query accumulate into the same product), the
@@ -60,14 +180,15 @@ template <typename T, typename QT, int G, int DH>
 __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
                                                   const int32_t* __restrict__ seq_len,
-                                                  float* __restrict__ scores, int N, int C, int Cp,
-                                                  int Hkv, int W, int S, float scale) {
+                                                  float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
+                                                  int cstride, int Kc, int N, int C, int Hkv, int W,
+                                                  int S, float scale) {
   typedef typename Frag<T>::type FT;
   constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
   constexpr int KS = DH / 32;
   constexpr int NST = CPW / 64;  // 16-chunk steps per wave
   constexpr int PD = 4;          // steps in flight per wave
-  static_assert(G <= 8 && NST % PD == 0, "scan shape");
+  static_assert(G <= 8 && NST % PD == 0 && CPW / 4 == 512, "scan shape");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int gl = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, bg = blockIdx.y;
@@ -118,9 +239,10 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
       }
     }
   }
-  // scores are collected in LDS and written once per wave as whole lines
-  // (scattered 64-byte stores between the reads cost ~10% of the scan)
+  // scores are collected in LDS; the wave then keeps its own top-K as
+  // candidates for the selection
   __shared__ __align__(16) float sbuf[4][CPW / 4];
+  __shared__ __align__(16) int whist[4][256];
   float* sw = sbuf[w];
   // fully unrolled, so the waits on the ring are exact (a loop back edge
   // would drain every load in flight)
@@ -147,12 +269,8 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
     }
   }
   wave_lds_sync();
-  float* dst = scores + (size_t)bg * Cp + c_w;
-#pragma unroll
-  for (int x = 0; x < CPW / 4 / 256; ++x) {
-    const int o = 4 * (lane + 64 * x);
-    *reinterpret_cast<f32x4*>(dst + o) = *reinterpret_cast<const f32x4*>(sw + o);
-  }
+  const size_t ob = (size_t)bg * cstride + (size_t)(c_w / (CPW / 4)) * Kc;
+  wave_topk(sw, c_w, nd, Kc, cand_s + ob, cand_i + ob, whist[w]);
 }
 
 // ---------------------------------------------------------------- select
@@ -179,31 +297,45 @@ __device__ __forceinline__ int block_scan256(int v, int* wsum, int& total) {
   return base + x - v;
 }
 
-// The K largest scores of one (sequence, KV head) by (score desc, index asc),
-// written as ascending chunk ids, -1 padded; one 256-thread block. Thread t
-// holds the order-preserving integer keys of chunks [t PER, t PER + PER) in
-// registers (contiguous ranges, so prefix sums follow index order); the exact
-// key T of the K-th largest score comes from a 4-pass 8-bit radix select,
-// and krem of the keys equal to T (the lowest indices) are taken.
+// The K best of the candidate list (sc, id)[0..n) of one (sequence, KV head)
+// by (score desc, chunk asc), written as ascending chunk ids, -1 padded; one
+// 256-thread block. The list is in ascending chunk order (id -1 = no entry),
+// so list order breaks ties. Thread t holds the order-preserving integer keys
+// of entries [t PER, t PER + PER) in registers (contiguous ranges, so prefix
+// sums follow list order); the exact key T of the K-th best comes from a
+// 4-pass 8-bit radix select, and the first krem keys equal to T are taken.
 template <int PER>
-__device__ __forceinline__ void select_block(const float* __restrict__ src, int nd, int K,
-                                             int32_t* __restrict__ sel, int32_t* __restrict__ topk_out) {
+__device__ __forceinline__ void select_block(const float* __restrict__ sc, const int32_t* __restrict__ id,
+                                             int n, int K, int32_t* __restrict__ sel,
+                                             int32_t* __restrict__ topk_out) {
   __shared__ int hist[256];
   __shared__ int wsum[4];
   __shared__ uint32_t s_prefix, s_mask;
   __shared__ int s_krem;
   const int t = threadIdx.x;
   const int lo = t * PER;
-  // vector loads (the score buffer is padded to at least 256 PER entries);
-  // key 0 marks a slot past the last distant chunk (no finite score maps to 0)
+  // vector loads (the lists are padded to at least 256 PER entries); key 0
+  // marks no entry (no finite score maps to 0)
   uint32_t key[PER];
+  int cid[PER];
 #pragma unroll
   for (int j4 = 0; j4 < PER / 4; ++j4) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(src + lo + 4 * j4);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(sc + lo + 4 * j4);
+    const int4 y = *reinterpret_cast<const int4*>(id + lo + 4 * j4);
+    const int yy[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) key[4 * j4 + i] = lo + 4 * j4 + i < nd ? ord_f(x[i]) : 0u;
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = lo + 4 * j4 + i < n && yy[i] >= 0;
+      key[4 * j4 + i] = ok ? ord_f(x[i]) : 0u;
+      cid[4 * j4 + i] = yy[i];
+    }
   }
-  const bool take_all = nd <= K;
+  int nv = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) nv += key[j] != 0u ? 1 : 0;
+  int tot;
+  nv = block_scan256(nv, wsum, tot);
+  const bool take_all = tot <= K;
   if (t == 0) {
     s_prefix = 0u;
     s_mask = 0u;
@@ -215,22 +347,9 @@ __device__ __forceinline__ void select_block(const float* __restrict__ src, int 
       hist[t] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix, mask = s_mask;
-      // neighbouring chunks mostly share the high digits: runs of one bin are
-      // added at once (far fewer lanes hit one LDS address per instruction)
-      int pb = -1, pc = 0;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (key[j] != 0u && (key[j] & mask) == prefix) {
-          const int bin = (key[j] >> shift) & 255;
-          if (bin != pb) {
-            if (pc > 0) atomicAdd(&hist[pb], pc);
-            pb = bin;
-            pc = 0;
-          }
-          ++pc;
-        }
-      }
-      if (pc > 0) atomicAdd(&hist[pb], pc);
+      for (int j = 0; j < PER; ++j)
+        if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255], 1);
       __syncthreads();
       if (t < 64) {
         // lane t holds bins 4t .. 4t+3; keys in higher bins rank above
@@ -268,14 +387,12 @@ __device__ __forceinline__ void select_block(const float* __restrict__ src, int 
   int ties = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) ties += (!take_all && key[j] == T) ? 1 : 0;
-  int tot;
   const int tie0 = block_scan256(ties, wsum, tot);
-  // chunk lo + j is taken: above T, or equal to T among the first krem ties
-  // (tr counts the ties before it)
+  // entry j is taken: above T, or equal to T among the first krem ties (tr
+  // counts the ties before it)
   auto taken = [&](int j, int& tr) __attribute__((always_inline)) {
-    const bool valid = key[j] != 0u;
     const bool eq = !take_all && key[j] == T;
-    const bool tk = valid && (take_all || key[j] > T || (eq && tr < krem));
+    const bool tk = key[j] != 0u && (take_all || key[j] > T || (eq && tr < krem));
     tr += eq ? 1 : 0;
     return tk;
   };
@@ -291,8 +408,8 @@ __device__ __forceinline__ void select_block(const float* __restrict__ src, int 
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       if (taken(j, tr)) {
-        sel[o] = lo + j;
-        if (topk_out != nullptr) topk_out[o] = lo + j;
+        sel[o] = cid[j];
+        if (topk_out != nullptr) topk_out[o] = cid[j];
         ++o;
       }
     }
@@ -303,40 +420,57 @@ __device__ __forceinline__ void select_block(const float* __restrict__ src, int 
   }
 }
 
-// larger chunk counts: keys re-read from the score buffer on every pass,
-// eight per thread and iteration (the buffer is padded to a multiple of 2048)
-__device__ __forceinline__ void select_block_big(const float* __restrict__ src, int nd, int K,
-                                                 int32_t* __restrict__ sel, int32_t* __restrict__ topk_out) {
+// longer candidate lists: keys re-read on every pass, eight per thread and
+// iteration (the lists are padded to a multiple of 8)
+__device__ __forceinline__ void select_block_big(const float* __restrict__ sc, const int32_t* __restrict__ id,
+                                                 int n, int K, int32_t* __restrict__ sel,
+                                                 int32_t* __restrict__ topk_out) {
   __shared__ int hist[256];
   __shared__ int wsum[4];
   __shared__ uint32_t s_prefix, s_mask;
   __shared__ int s_krem;
   const int t = threadIdx.x;
-  const bool take_all = nd <= K;
+  auto keys8 = [&](int c0, uint32_t (&kk)[8], int (&ci)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(sc + c0 + 4 * h);
+      const int4 y = *reinterpret_cast<const int4*>(id + c0 + 4 * h);
+      const int yy[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = c0 + 4 * h + i < n && yy[i] >= 0;
+        kk[4 * h + i] = ok ? ord_f(a[i]) : 0u;
+        ci[4 * h + i] = yy[i];
+      }
+    }
+  };
+  int nv = 0;
+  for (int c0 = 8 * t; c0 < n; c0 += 2048) {
+    uint32_t kk[8];
+    int ci[8];
+    keys8(c0, kk, ci);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) nv += kk[i] != 0u ? 1 : 0;
+  }
+  int tot;
+  block_scan256(nv, wsum, tot);
+  const bool take_all = tot <= K;
   if (t == 0) {
     s_prefix = 0u;
     s_mask = 0u;
     s_krem = K;
   }
   __syncthreads();
-  auto keys8 = [&](int c0, uint32_t (&kk)[8]) __attribute__((always_inline)) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src + c0);
-    const f32x4 b2 = *reinterpret_cast<const f32x4*>(src + c0 + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kk[i] = c0 + i < nd ? ord_f(a[i]) : 0u;
-      kk[4 + i] = c0 + 4 + i < nd ? ord_f(b2[i]) : 0u;
-    }
-  };
   if (!take_all) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       hist[t] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix, mask = s_mask;
-      for (int c0 = 8 * t; c0 < nd; c0 += 2048) {
+      for (int c0 = 8 * t; c0 < n; c0 += 2048) {
         uint32_t kk[8];
-        keys8(c0, kk);
+        int ci[8];
+        keys8(c0, kk, ci);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (kk[i] != 0u && (kk[i] & mask) == prefix) atomicAdd(&hist[(kk[i] >> shift) & 255], 1);
@@ -372,19 +506,19 @@ __device__ __forceinline__ void select_block_big(const float* __restrict__ src, 
   }
   const uint32_t T = s_prefix;
   const int krem = s_krem;
-  // contiguous ranges of a multiple of 8 chunks per thread (prefix sums follow
-  // index order)
-  const int per = ((nd + 255) / 256 + 7) / 8 * 8;
-  const int lo = min(nd, t * per), hi = min(nd, lo + per);
+  // contiguous ranges of a multiple of 8 entries per thread (prefix sums
+  // follow list order)
+  const int per = ((n + 255) / 256 + 7) / 8 * 8;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
   int ties = 0;
   if (!take_all)
     for (int c0 = lo; c0 < hi; c0 += 8) {
       uint32_t kk[8];
-      keys8(c0, kk);
+      int ci[8];
+      keys8(c0, kk, ci);
 #pragma unroll
       for (int i = 0; i < 8; ++i) ties += kk[i] == T ? 1 : 0;
     }
-  int tot;
   const int tie0 = block_scan256(ties, wsum, tot);
   auto taken = [&](uint32_t key, int& tr) __attribute__((always_inline)) {
     const bool eq = !take_all && key == T;
@@ -397,7 +531,8 @@ __device__ __forceinline__ void select_block_big(const float* __restrict__ src, 
     int tr = tie0;
     for (int c0 = lo; c0 < hi; c0 += 8) {
       uint32_t kk[8];
-      keys8(c0, kk);
+      int ci[8];
+      keys8(c0, kk, ci);
 #pragma unroll
       for (int i = 0; i < 8; ++i) cnt += taken(kk[i], tr) ? 1 : 0;
     }
@@ -407,12 +542,13 @@ __device__ __forceinline__ void select_block_big(const float* __restrict__ src, 
     int tr = tie0, o = out0;
     for (int c0 = lo; c0 < hi; c0 += 8) {
       uint32_t kk[8];
-      keys8(c0, kk);
+      int ci[8];
+      keys8(c0, kk, ci);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         if (taken(kk[i], tr)) {
-          sel[o] = c0 + i;
-          if (topk_out != nullptr) topk_out[o] = c0 + i;
+          sel[o] = ci[i];
+          if (topk_out != nullptr) topk_out[o] = ci[i];
           ++o;
         }
       }
@@ -434,181 +570,191 @@ struct DecArgs {
   float scale;
 };
 
-// one wave: unit u of (sequence, KV head) bg
-template <typename T, typename QT, int G, int DH>
-__device__ __forceinline__ void dec_unit(const T* __restrict__ q, const QT* __restrict__ qs,
-                                         const T* __restrict__ k, const T* __restrict__ v,
-                                         const T* __restrict__ kL, const T* __restrict__ e,
-                                         const DecArgs& a, int bg, int u) {
+// One wave: units u0, u0 + us, ... (up to NUW of them) of (sequence, KV
+// head) bg, software-pipelined: the next unit's K rows are requested as soon
+// as the current scores are formed, its V rows as soon as the current output
+// is, so loads stay in flight while the wave computes.
+template <typename T, typename QT, int G, int DH, int NUW>
+__device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __restrict__ qs,
+                                          const T* __restrict__ k, const T* __restrict__ v,
+                                          const T* __restrict__ kL, const T* __restrict__ e,
+                                          const DecArgs& a, int bg, int u0, int us) {
   typedef typename Frag<T>::type FT;
   constexpr int KS = DH / 32, MB = DH / 16;
+  constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
   const int lane = threadIdx.x & 63;
   const int gl = lane >> 4, col = lane & 15;
-  const int32_t* seq_len = a.seq_len;
-  const int32_t* sel = a.sel;
-  float* pml = a.pml;
-  float* po = a.po;
-  const int N = a.N, C = a.C, Hkv = a.Hkv, K = a.K, W = a.W, S = a.S, units = a.units;
+  const int N = a.N, C = a.C, Hkv = a.Hkv, K = a.K, S = a.S, units = a.units;
   const float scale = a.scale;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
-  if (u >= units) return;
-  const int n = seq_n(seq_len, b, N);
-  const int i = n - 1;
-  const int nd = n_distant(i, W, S);
-  const int ws = nd * S;
-  float* pm = pml + ((size_t)bg * units + u) * G * 2;
-  float* pv = po + ((size_t)bg * units + u) * G * DH;
-  // what this unit covers
-  int t0, cnt, chunk = -1;
-  if (u < K) {
-    chunk = sel[(size_t)bg * K + u];
-    t0 = chunk * S;
-    cnt = chunk >= 0 ? S : 0;
-  } else {
-    t0 = ws + 64 * (u - K);
-    cnt = min(64, n - t0);
-  }
-  if (cnt <= 0) {
-    // an empty unit: weight 0 and a zero vector (the combine multiplies
-    // every unit's vector by its weight without branching)
-    if (lane < G) {
-      pm[2 * lane] = NEG_INF;
-      pm[2 * lane + 1] = 0.f;
-    }
-    for (int x = lane; x < G * DH / 4; x += 64) reinterpret_cast<f32x4*>(pv)[x] = zero4();
-    return;
-  }
-  // K and V rows as row-major fragments: token 16 tb + col, dims 8 gl + 32 ks
-  const T* kb = k + ((size_t)bg * N + t0) * DH;
-  const T* vb = v + ((size_t)bg * N + t0) * DH;
-  FT kf[4][KS], vf[4][KS];
+  const int n = seq_n(a.seq_len, b, N);
+  const int ws = n_distant(n - 1, a.W, S) * S;
+  // what each unit covers (wave-uniform): a selected chunk, or a window block
+  int uu[NUW], t0[NUW], cnt[NUW], chunk[NUW];
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    int tok = 16 * tb + col;
-    tok = tok < cnt ? tok : 0;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[tb][ks] = ld8<T>(kb + (size_t)tok * DH + 8 * gl + 32 * ks);
-      vf[tb][ks] = ld8<T>(vb + (size_t)tok * DH + 8 * gl + 32 * ks);
+  for (int j = 0; j < NUW; ++j) {
+    const int u = u0 + j * us;
+    uu[j] = u;
+    chunk[j] = -1;
+    if (u < K) {
+      chunk[j] = __builtin_amdgcn_readfirstlane(a.sel[(size_t)bg * K + u]);
+      t0[j] = chunk[j] >= 0 ? chunk[j] * S : 0;
+      cnt[j] = chunk[j] >= 0 ? S : 0;
+    } else {
+      t0[j] = ws + 64 * (u - K);
+      cnt[j] = u < units ? min(64, n - t0[j]) : 0;
+      if (cnt[j] <= 0) t0[j] = 0;
     }
   }
-  // Q^T operand: column col = head col (raw query), zero beyond G
-  FT qf[KS];
+  // loop-invariant operands: raw query heads (B operand of S^T = K Q^T), the
+  // calibrated query heads for the landmark score (B operand; hi + lo of an
+  // fp32 query), identity fragments I_h[k][c] = (k == 16 h + c)
+  FT qf[KS], qsf[KS], qsl[HAS_LO ? KS : 1], idf[2];
   {
     const int h = col < G ? col : 0;
     const T* src = q + ((size_t)b * Hq + g * G + h) * DH + 8 * gl;
+    const QT* srs = qs + ((size_t)b * Hq + g * G + h) * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const FT raw = ld8<T>(src + 32 * ks);
+      const auto rs = ld8<QT>(srs + 32 * ks);
+      float x[8], y[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        x[jj] = col < G ? (float)raw[jj] : 0.f;
+        y[jj] = col < G ? (float)rs[jj] : 0.f;
+      }
+      qf[ks] = pack8<T>(x);
+      qsf[ks] = pack8<T>(y);
+      if constexpr (HAS_LO) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) y[jj] -= (float)qsf[ks][jj];
+        qsl[ks] = pack8<T>(y);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = col < G ? (float)raw[j] : 0.f;
-      qf[ks] = pack8<T>(x);
+      for (int jj = 0; jj < 8; ++jj) x[jj] = (8 * gl + jj == 16 * hh + col) ? 1.f : 0.f;
+      idf[hh] = pack8<T>(x);
     }
   }
-  // per-head fusion score of a selected chunk: s_h = scale q_hat_h . kL_c + e_c
-  float s_head[G];
+  // register sets of one unit: K and V rows (token 16 tb + col, dims 8 gl +
+  // 32 ks) and the chunk's landmark row (every A row = kL_c)
+  FT kf[4][KS], vf[4][KS], kr[KS];
+  auto loadK = [&](int j) __attribute__((always_inline)) {
+    const T* kb = k + ((size_t)bg * N + t0[j]) * DH;
 #pragma unroll
-  for (int h = 0; h < G; ++h) s_head[h] = 0.f;
-  if (chunk >= 0) {
-    const T* kr = kL + ((size_t)bg * C + chunk) * DH;
-    const float eb = to_f<T>(e[(size_t)bg * C + chunk]);
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tok = 16 * tb + col < cnt[j] ? 16 * tb + col : 0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const QT* qh = qs + ((size_t)b * Hq + g * G + h) * DH;
-      float a = 0.f;
-#pragma unroll
-      for (int j = 0; j < DH / 64; ++j) a = fmaf(to_f<QT>(qh[lane + 64 * j]), to_f<T>(kr[lane + 64 * j]), a);
-#pragma unroll
-      for (int m2 = 32; m2 >= 1; m2 >>= 1) a += __shfl_xor(a, m2, 64);
-      s_head[h] = fmaf(a, scale, eb);
+      for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = ld8<T>(kb + (size_t)tok * DH + 8 * gl + 32 * ks);
     }
-  }
-  f32x4 sacc[4];
+    const T* krow = kL + ((size_t)bg * C + (chunk[j] >= 0 ? chunk[j] : 0)) * DH + 8 * gl;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    sacc[tb] = zero4();
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = ld8<T>(krow + 32 * ks);
+  };
+  auto loadV = [&](int j) __attribute__((always_inline)) {
+    const T* vb = v + ((size_t)bg * N + t0[j]) * DH;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(kf[tb][ks], qf[ks], sacc[tb]);
-  }
-  float mx = NEG_INF;
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tok = 16 * tb + col < cnt[j] ? 16 * tb + col : 0;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int tok = 16 * tb + 4 * gl + ii;
-      const float x = tok < cnt ? sacc[tb][ii] * scale : NEG_INF;
-      sacc[tb][ii] = x;
-      mx = fmaxf(mx, x);
+      for (int ks = 0; ks < KS; ++ks) vf[tb][ks] = ld8<T>(vb + (size_t)tok * DH + 8 * gl + 32 * ks);
     }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
-  mx = fmaxf(mx, shfl_xor(mx, 32));
-  float ls = 0.f;
+  };
+  loadK(0);
+  loadV(0);
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int j = 0; j < NUW; ++j) {
+    // scores of the unit's tokens, and (chunk units) the landmark score of
+    // every head: D[row][col = h] = kL_c . q_hat_h
+    f32x4 sacc[4], lm = zero4();
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const float x = sacc[tb][ii];
-      const float p = x == NEG_INF ? 0.f : __expf(x - mx);
-      sacc[tb][ii] = p;
-      ls += p;
+    for (int tb = 0; tb < 4; ++tb) {
+      sacc[tb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(kf[tb][ks], qf[ks], sacc[tb]);
     }
-  ls += shfl_xor(ls, 16);
-  ls += shfl_xor(ls, 32);
-  // identity fragments: I_h[k][c] = (k == 16 h + c)
-  FT idf[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (8 * gl + j == 16 * h + col) ? 1.f : 0.f;
-    idf[h] = pack8<T>(x);
-  }
-  f32x4 oacc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) oacc[mb] = zero4();
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {  // 32-token steps
-    const FT pf = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      // V^T rows 16 mb .. 16 mb + 15 over the step's tokens, in the token
-      // order of the P^T fragment
-      const int kd = mb >> 1, hs = mb & 1;
-      const FT vt = pk8<T>(mma16(vf[2 * ks][kd], idf[hs], zero4()),
-                           mma16(vf[2 * ks + 1][kd], idf[hs], zero4()));
-      oacc[mb] = mma16(vt, pf, oacc[mb]);
+    for (int ks = 0; ks < KS; ++ks) {
+      lm = mma16(kr[ks], qsf[ks], lm);
+      if constexpr (HAS_LO) lm = mma16(kr[ks], qsl[ks], lm);
     }
-  }
-  if (col < G) {
-    float mval = mx, lval = ls, coef = 1.f;
-    if (chunk >= 0) {
-      // a selected chunk enters the fusion as one term: log-weight s_c,
-      // weight 1, vector O_c
-      float sh = s_head[0];
+    const int cj = cnt[j], chj = chunk[j];
+    const float ebias = chj >= 0 ? to_f<T>(e[(size_t)bg * C + chj]) : 0.f;
+    if (j + 1 < NUW) loadK(j + 1);
+    float mx = NEG_INF;
 #pragma unroll
-      for (int h = 1; h < G; ++h) sh = col == h ? s_head[h] : sh;
-      mval = sh;
-      lval = 1.f;
-      coef = 1.f / ls;
-    }
-    if (gl == 0) {
-      pm[2 * col] = mval;
-      pm[2 * col + 1] = lval;
-    }
-    float* ph = pv + (size_t)col * DH + 4 * gl;
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(ph + 16 * mb) = oacc[mb] * coef;
+      for (int ii = 0; ii < 4; ++ii) {
+        const int tok = 16 * tb + 4 * gl + ii;
+        const float x = tok < cj ? sacc[tb][ii] * scale : NEG_INF;
+        sacc[tb][ii] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = col_max4(mx);
+    float ls = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const float x = sacc[tb][ii];
+        const float p = x == NEG_INF ? 0.f : __expf(x - mx);
+        sacc[tb][ii] = p;
+        ls += p;
+      }
+    ls = col_sum4(ls);
+    f32x4 oacc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oacc[mb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {  // 32-token steps
+      const FT pf = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // V^T rows 16 mb .. 16 mb + 15 over the step's tokens, in the token
+        // order of the P^T fragment
+        const int kd = mb >> 1, hs = mb & 1;
+        const FT vt = pk8<T>(mma16(vf[2 * ks][kd], idf[hs], zero4()),
+                             mma16(vf[2 * ks + 1][kd], idf[hs], zero4()));
+        oacc[mb] = mma16(vt, pf, oacc[mb]);
+      }
+    }
+    if (j + 1 < NUW) loadV(j + 1);
+    const int u = uu[j];
+    if (u < units && col < G) {
+      float mval = mx, lval = ls, coef = 1.f;
+      if (chj >= 0) {
+        // a selected chunk enters the fusion as one term: log-weight s_c,
+        // weight 1, vector O_c
+        mval = fmaf(lm[0], scale, ebias);
+        lval = 1.f;
+        coef = 1.f / ls;
+      }
+      float* pm = a.pml + ((size_t)bg * units + u) * G * 2;
+      float* pv = a.po + ((size_t)bg * units + u) * G * DH;
+      if (gl == 0) {
+        pm[2 * col] = mval;
+        pm[2 * col + 1] = lval;
+      }
+      float* ph = pv + (size_t)col * DH + 4 * gl;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(ph + 16 * mb) = oacc[mb] * coef;
+    }
   }
 }
 
 // selections (one block per (sequence, KV head)) and, alongside in the same
 // launch, the window units, which do not depend on them
 template <typename T, typename QT, int G, int DH, int PER>
-__global__ __launch_bounds__(256) void k_dec_select_window(const float* __restrict__ scores,
-                                                           int32_t* __restrict__ topk_out, int Cp,
-                                                           int nbg, int wpb, const T* __restrict__ q,
+__global__ __launch_bounds__(256) void k_dec_select_window(const float* __restrict__ cand_s,
+                                                           const int32_t* __restrict__ cand_i,
+                                                           int32_t* __restrict__ topk_out, int cstride,
+                                                           int Kc, int nbg, int wpb, const T* __restrict__ q,
                                                            const QT* __restrict__ qs,
                                                            const T* __restrict__ k,
                                                            const T* __restrict__ v,
@@ -618,28 +764,34 @@ __global__ __launch_bounds__(256) void k_dec_select_window(const float* __restri
   if (blk < nbg) {
     const int bg = blk, b = bg / a.Hkv;
     const int nd = n_distant(seq_n(a.seq_len, b, a.N) - 1, a.W, a.S);
+    // candidates: Kc per 512 scanned chunks
+    const int n = (nd + 511) / 512 * Kc;
     int32_t* sl = const_cast<int32_t*>(a.sel) + (size_t)bg * a.K;
     int32_t* to = topk_out != nullptr ? topk_out + (size_t)bg * a.K : nullptr;
-    if (nd <= 256 * PER)
-      select_block<PER>(scores + (size_t)bg * Cp, nd, a.K, sl, to);
+    const float* cs = cand_s + (size_t)bg * cstride;
+    const int32_t* ci = cand_i + (size_t)bg * cstride;
+    if (n <= 256 * PER)
+      select_block<PER>(cs, ci, n, a.K, sl, to);
     else
-      select_block_big(scores + (size_t)bg * Cp, nd, a.K, sl, to);
+      select_block_big(cs, ci, n, a.K, sl, to);
     return;
   }
   const int x = blk - nbg;
   const int bg = x / wpb;
   const int u = a.K + 4 * (x - bg * wpb) + (threadIdx.x >> 6);
-  if (u < a.units) dec_unit<T, QT, G, DH>(q, qs, k, v, kL, e, a, bg, u);
+  if (u < a.units) dec_units<T, QT, G, DH, 1>(q, qs, k, v, kL, e, a, bg, u, 1);
 }
 
-// the selected-chunk units
+// the selected-chunk units: wave x of a (sequence, KV head) takes units x,
+// x + wpg, ... (DEC_NUW of them)
+constexpr int DEC_NUW = 2;
 template <typename T, typename QT, int G, int DH>
-__global__ __launch_bounds__(256) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
                                                     const T* __restrict__ k, const T* __restrict__ v,
                                                     const T* __restrict__ kL, const T* __restrict__ e,
-                                                    DecArgs a) {
-  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (u < a.K) dec_unit<T, QT, G, DH>(q, qs, k, v, kL, e, a, blockIdx.y, u);
+                                                    DecArgs a, int wpg) {
+  const int x = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (x < wpg) dec_units<T, QT, G, DH, DEC_NUW>(q, qs, k, v, kL, e, a, blockIdx.y, x, wpg);
 }
 
 // ---------------------------------------------------------------- combine
@@ -700,19 +852,21 @@ __global__ __launch_bounds__(64) void k_dec_combine(const float* __restrict__ pm
 namespace {
 struct DecWs {
   float* qhat;
-  float* scores;
+  float* cand_s;
+  int32_t* cand_i;
   int32_t* sel;
   float *pml, *po;
-  int nsplit, units, Cp;
+  int nsplit, units, Kc, cstride;
 };
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t carve(const Dims& p, void* base, DecWs* w) {
   char* c = static_cast<char*>(base);
   size_t off = 0;
   w->nsplit = std::max(1, (p.C + CPW - 1) / CPW);
-  // scores padded for the selection's vector loads: a multiple of 2048 and
-  // at least 256 * 32 (one register set of keys per thread)
-  w->Cp = std::max(w->nsplit * CPW, 8192);
+  // candidate lists: the top min(K, 512) of every 512 scanned chunks, padded
+  // for the selection's vector loads (a multiple of 8, at least 256 * 8)
+  w->Kc = std::min(p.K, 512);
+  w->cstride = std::max((w->nsplit * 4 * w->Kc + 7) / 8 * 8, 2048);
   w->units = p.K + (p.W + p.S - 1 + 63) / 64 + 1;
   auto take = [&](size_t bytes) {
     void* ptr = c ? c + off : nullptr;
@@ -721,7 +875,8 @@ size_t carve(const Dims& p, void* base, DecWs* w) {
   };
   const size_t bg = (size_t)p.B * p.Hkv;
   w->qhat = (float*)take(p.r > 0 ? (size_t)p.B * p.Hq * p.d * sizeof(float) : 0);
-  w->scores = (float*)take(bg * w->Cp * sizeof(float));
+  w->cand_s = (float*)take(bg * w->cstride * sizeof(float));
+  w->cand_i = (int32_t*)take(bg * w->cstride * sizeof(int32_t));
   w->sel = (int32_t*)take(bg * p.K * sizeof(int32_t));
   w->pml = (float*)take(bg * w->units * p.G * 2 * sizeof(float));
   w->po = (float*)take(bg * w->units * p.G * p.d * sizeof(float));
@@ -741,8 +896,8 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
                          const int32_t* seq_len, const void* kL, const void* e, void* o, float* lse,
                          int32_t* topk_idx, const DecWs& w, hipStream_t st) {
   hipLaunchKernelGGL((k_dec_scan<T, QT, G, DH>), dim3(w.nsplit, p.B * p.Hkv), dim3(256), 0, st,
-                     (const QT*)qs, (const T*)kL, (const T*)e, seq_len, w.scores, p.N, p.C, w.Cp,
-                     p.Hkv, p.W, p.S, p.scale);
+                     (const QT*)qs, (const T*)kL, (const T*)e, seq_len, w.cand_s, w.cand_i, w.cstride,
+                     w.Kc, p.N, p.C, p.Hkv, p.W, p.S, p.scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   DecArgs a;
@@ -754,12 +909,15 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
   a.scale = p.scale;
   const int nbg = p.B * p.Hkv;
   const int wpb = (w.units - p.K + 3) / 4;  // window units: four per block
-  hipLaunchKernelGGL((k_dec_select_window<T, QT, G, DH, 32>), dim3(nbg * (1 + wpb)), dim3(256), 0, st,
-                     (const float*)w.scores, topk_idx, w.Cp, nbg, wpb, (const T*)q, (const QT*)qs,
-                     (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a);
+  hipLaunchKernelGGL((k_dec_select_window<T, QT, G, DH, 8>), dim3(nbg * (1 + wpb)), dim3(256), 0, st,
+                     (const float*)w.cand_s, (const int32_t*)w.cand_i, topk_idx, w.cstride, w.Kc, nbg,
+                     wpb, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
+                     (const T*)e, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH>), dim3((p.K + 3) / 4, nbg), dim3(256), 0, st,
-                     (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a);
+  const int wpg = (p.K + DEC_NUW - 1) / DEC_NUW;
+  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH>), dim3((wpg + 3) / 4, nbg), dim3(256), 0, st,
+                     (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a,
+                     wpg);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, (const float*)w.pml,
                      (const float*)w.po, (T*)o, lse, p.Hkv, G, w.units);

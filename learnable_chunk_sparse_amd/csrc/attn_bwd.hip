@@ -1196,18 +1196,21 @@ hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v
     g.accumulate = true;
     if ((err = gemm(g, w.dqhat, 0, w.u, 0, st)) != hipSuccess) return err;
   }
-  // dW_down[h] += sum_i du[b, i, h, :] (x) h[b, i, :]
+  // dW_down[h] += sum_i du[b, i, h, :] (x) h[b, i, :], all heads in one
+  // product per batch element: rows (h, j) of du^T [Hq r x N] times h [N x D]
   {
     GemmArgs g;
-    g.M = p.r; g.N = p.D; g.K = p.N;
+    g.M = (int)Hr; g.N = p.D; g.K = p.N;
     g.akm = true; g.bkm = false;
     g.lda = Hr; g.ldb = p.D; g.ldc = p.D;
-    g.n1 = p.B; g.n2 = p.Hq;
-    g.sA1 = NHr; g.sA2 = p.r;
+    g.n1 = p.B; g.n2 = 1;
+    g.sA1 = NHr; g.sA2 = 0;
     g.sB1 = (long)p.N * p.D; g.sB2 = 0;
-    g.sC1 = 0; g.sC2 = (long)p.r * p.D;
+    g.sC1 = 0; g.sC2 = 0;
     g.C = dW_down;
-    g.splits = std::max(1, p.N / 1024);
+    // split K so the launch holds ~2048 64x64 tiles
+    const long tiles = (long)((Hr + 63) / 64) * ((p.D + 63) / 64) * p.B;
+    g.splits = (int)std::max(1L, std::min((long)(p.N / 256), (2048 + tiles - 1) / tiles));
     g.accumulate = true;
     if ((err = gemm(g, w.du, 0, h, dt, st)) != hipSuccess) return err;
   }

@@ -150,6 +150,145 @@ __global__ __launch_bounds__(256) void k_gemm(const TA* __restrict__ A, const TB
       }
 }
 
+// Same product for shapes whose M, N, K, leading dimensions and batch strides
+// are multiples of 8 elements (16-byte aligned operands): every thread's
+// eight elements of a stage are one contiguous vector, loaded without
+// per-element branches (a vector is wholly inside or outside the matrix;
+// outside ones are clamped and zeroed), and the next k-step's vectors are
+// in flight while the current one is multiplied.
+template <typename T> struct V8;
+template <> struct V8<uint16_t> { typedef u16x8 type; };
+template <> struct V8<float> { typedef f32x8 type; };
+
+template <typename T>
+__device__ __forceinline__ typename V8<T>::type ldv8(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const u16x8*>(p);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+template <typename T>
+__device__ __forceinline__ float v8f(const typename V8<T>::type& v, int j) {
+  if constexpr (sizeof(T) == 2)
+    return bf2f(v[j]);
+  else
+    return v[j];
+}
+
+template <typename TA, typename TB, bool AKM, bool BKM>
+__global__ __launch_bounds__(256) void k_gemm_v(const TA* __restrict__ A, const TB* __restrict__ B,
+                                                float* __restrict__ Cm, int M, int N, int K, long lda,
+                                                long ldb, long ldc, long sA1, long sA2, long sB1,
+                                                long sB2, long sC1, long sC2, int nz2, int kchunk,
+                                                int splits, int accumulate) {
+  constexpr bool ALO = sizeof(TA) == 4, BLO = sizeof(TB) == 4;
+  constexpr int KP = 40;
+  __shared__ __align__(16) uint16_t as_hi[64 * KP], bs_hi[64 * KP];
+  __shared__ __align__(16) uint16_t as_lo[ALO ? 64 * KP : 8], bs_lo[BLO ? 64 * KP : 8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int bz = blockIdx.z / splits, sp = blockIdx.z - bz * splits;
+  const int z1 = bz / nz2, z2 = bz - z1 * nz2;
+  A += z1 * sA1 + z2 * sA2;
+  B += z1 * sB1 + z2 * sB2;
+  Cm += z1 * sC1 + z2 * sC2;
+  const int k_begin = sp * kchunk, k_end = min(K, k_begin + kchunk);
+  // this thread's vector of each stage: (row, k offset) for row-major
+  // operands, (k offset, row) for k-major ones
+  const int ar = AKM ? (tid & 7) * 8 : tid >> 2, ak = AKM ? tid >> 3 : (tid & 3) * 8;
+  const int br = BKM ? tid >> 2 : (tid & 7) * 8, bk = BKM ? (tid & 3) * 8 : tid >> 3;
+  const bool a_in = m0 + ar < M, b_in = n0 + br < N;
+  auto lda_v = [&](int k0, typename V8<TA>::type& x, bool& ok) __attribute__((always_inline)) {
+    const int k = k0 + ak;
+    ok = a_in && k < k_end;
+    const int kc = ok ? k : k_begin, mc = a_in ? m0 + ar : 0;
+    x = ldv8<TA>(AKM ? A + (long)kc * lda + mc : A + (long)mc * lda + kc);
+  };
+  auto ldb_v = [&](int k0, typename V8<TB>::type& x, bool& ok) __attribute__((always_inline)) {
+    const int k = k0 + bk;
+    ok = b_in && k < k_end;
+    const int kc = ok ? k : k_begin, nc = b_in ? n0 + br : 0;
+    x = ldv8<TB>(BKM ? B + (long)nc * ldb + kc : B + (long)kc * ldb + nc);
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = zero4();
+  typename V8<TA>::type xa;
+  typename V8<TB>::type xb;
+  bool oka, okb;
+  lda_v(k_begin, xa, oka);
+  ldb_v(k_begin, xb, okb);
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    // publish the stage held in registers as [row][k] bf16 (hi, lo)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = oka ? v8f<TA>(xa, j) : 0.f;
+      const uint16_t hi = f2bf(v);
+      const int o = AKM ? (ar + j) * KP + ak : ar * KP + ak + j;
+      as_hi[o] = hi;
+      if constexpr (ALO) as_lo[o] = f2bf(v - bf2f(hi));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = okb ? v8f<TB>(xb, j) : 0.f;
+      const uint16_t hi = f2bf(v);
+      const int o = BKM ? br * KP + bk + j : (br + j) * KP + bk;
+      bs_hi[o] = hi;
+      if constexpr (BLO) bs_lo[o] = f2bf(v - bf2f(hi));
+    }
+    __syncthreads();
+    // next stage's vectors in flight during the products
+    if (k0 + 32 < k_end) {
+      lda_v(k0 + 32, xa, oka);
+      ldb_v(k0 + 32, xb, okb);
+    }
+    bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int off = (32 * wm + 16 * mb + (lane & 15)) * KP + 8 * (lane >> 4);
+      ah[mb] = *reinterpret_cast<const bf16x8*>(as_hi + off);
+      if constexpr (ALO) al[mb] = *reinterpret_cast<const bf16x8*>(as_lo + off);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int off = (32 * wn + 16 * nb + (lane & 15)) * KP + 8 * (lane >> 4);
+      bh[nb] = *reinterpret_cast<const bf16x8*>(bs_hi + off);
+      if constexpr (BLO) bl[nb] = *reinterpret_cast<const bf16x8*>(bs_lo + off);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[mb][nb] = mma16(ah[mb], bh[nb], acc[mb][nb]);
+        if constexpr (BLO) acc[mb][nb] = mma16(ah[mb], bl[nb], acc[mb][nb]);
+        if constexpr (ALO) acc[mb][nb] = mma16(al[mb], bh[nb], acc[mb][nb]);
+      }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 32 * wm + 16 * mb + 4 * (lane >> 4) + i;
+        const int n = n0 + 32 * wn + 16 * nb + (lane & 15);
+        if (m < M && n < N) {
+          float* c = Cm + (long)m * ldc + n;
+          if (splits > 1 || accumulate)
+            atomicAdd(c, acc[mb][nb][i]);
+          else
+            *c = acc[mb][nb][i];
+        }
+      }
+}
+
 // C[z] (+)= A[z] * B[z] over the batch z = (z1, z2), z1 < g.n1, z2 < g.n2.
 template <typename TA, typename TB, bool AKM, bool BKM>
 static hipError_t gemm_go(const GemmArgs& g, const TA* A, const TB* B, hipStream_t st) {
@@ -158,6 +297,15 @@ static hipError_t gemm_go(const GemmArgs& g, const TA* A, const TB* B, hipStream
   kchunk = (kchunk + 31) / 32 * 32;
   splits = (g.K + kchunk - 1) / kchunk;
   dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, g.n1 * g.n2 * splits);
+  auto m8 = [](long x) { return x % 8 == 0; };
+  const bool vec = m8(g.M) && m8(g.N) && m8(g.K) && m8(g.lda) && m8(g.ldb) && m8(g.sA1) && m8(g.sA2) &&
+                   m8(g.sB1) && m8(g.sB2) && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0);
+  if (vec) {
+    hipLaunchKernelGGL((k_gemm_v<TA, TB, AKM, BKM>), grid, dim3(256), 0, st, A, B, g.C, g.M, g.N, g.K,
+                       g.lda, g.ldb, g.ldc, g.sA1, g.sA2, g.sB1, g.sB2, g.sC1, g.sC2, g.n2, kchunk,
+                       splits, g.accumulate ? 1 : 0);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_gemm<TA, TB, AKM, BKM>), grid, dim3(256), 0, st, A, B, g.C, g.M, g.N, g.K,
                      g.lda, g.ldb, g.ldc, g.sA1, g.sA2, g.sB1, g.sB2, g.sC1, g.sC2, g.n2, kchunk,
                      splits, g.accumulate ? 1 : 0);

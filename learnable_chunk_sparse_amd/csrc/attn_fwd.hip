@@ -224,15 +224,58 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
 
   // ------------------------------------------------ selections of the tile
   for (int x = tid; x <= ndmax; x += 256) flg[x] = 0;
-  for (int x = tid; x < TP * K1; x += 256) {
-    const int pl = x / K1, kk = x - pl * K1;
-    const int pos = p0 + pl;
-    tkc[x] = (pos < N && kk < K) ? topk_idx[((size_t)bg * N + pos) * K + kk] : -1;
-  }
-  for (int x = tid; x < R * K1; x += 256) {
-    const int r = x / K1, kk = x - r * K1;
-    const int pos = p0 + r / G;
-    tks[x] = (pos < N && kk < K) ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
+  if (K % 4 == 0) {
+    // 16-byte vectors, every load issued before any is used (clamped
+    // addresses, no per-element branches); at most four per thread (K <= 32)
+    // (ids: TP positions; scores: R = TP G rows)
+    const int KV4 = K >> 2, nvi = TP * KV4, nvs = R * KV4;
+    int4 vi[4];
+    f32x4 vs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = tid + 256 * j;
+      const int vc = min(v, nvi - 1), rc = vc / KV4, pc = vc - rc * KV4;
+      vi[j] = *reinterpret_cast<const int4*>(topk_idx + ((size_t)bg * N + min(p0 + rc, N - 1)) * K + 4 * pc);
+      const int ws2 = min(v, nvs - 1), rs = ws2 / KV4, qs2 = ws2 - rs * KV4;
+      vs[j] = *reinterpret_cast<const f32x4*>(
+          topk_score + (((size_t)b * Hq + g * G + rs % G) * N + min(p0 + rs / G, N - 1)) * K + 4 * qs2);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = tid + 256 * j;
+      const int r = v / KV4, part = v - r * KV4;
+      if (v < nvi) {
+        const bool li = p0 + r < N;
+        int* dc = tkc + r * K1 + 4 * part;
+        dc[0] = li ? vi[j].x : -1;
+        dc[1] = li ? vi[j].y : -1;
+        dc[2] = li ? vi[j].z : -1;
+        dc[3] = li ? vi[j].w : -1;
+      }
+      if (v < nvs) {
+        const bool ls = p0 + r / G < N;
+        float* dsc = tks + r * K1 + 4 * part;
+        dsc[0] = ls ? vs[j][0] : 0.f;
+        dsc[1] = ls ? vs[j][1] : 0.f;
+        dsc[2] = ls ? vs[j][2] : 0.f;
+        dsc[3] = ls ? vs[j][3] : 0.f;
+      }
+    }
+    for (int x = tid; x < R; x += 256) {
+      if (x < TP) tkc[x * K1 + K] = -1;
+      tks[x * K1 + K] = 0.f;
+    }
+  } else {
+    for (int x = tid; x < TP * K1; x += 256) {
+      const int pl = x / K1, kk = x - pl * K1;
+      const int pos = p0 + pl;
+      tkc[x] = (pos < N && kk < K) ? topk_idx[((size_t)bg * N + pos) * K + kk] : -1;
+    }
+    for (int x = tid; x < R * K1; x += 256) {
+      const int r = x / K1, kk = x - r * K1;
+      const int pos = p0 + r / G;
+      tks[x] = (pos < N && kk < K) ? topk_score[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] : 0.f;
+    }
   }
   __syncthreads();
   for (int x = tid; x < TP * K1; x += 256) {

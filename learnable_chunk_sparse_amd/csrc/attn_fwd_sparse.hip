@@ -108,20 +108,22 @@ __global__ __launch_bounds__(256) void k_attn_fwd_sparse(
   __syncthreads();
   int my_c[EPT], my_r[EPT];
   const int E = TP * K;
+  // all of the thread's ids are requested before any is used (clamped
+  // addresses; guarded per-element loads would each wait for the previous)
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int x = min(tid + 256 * j, E - 1);
+    const int pl = x / K, kk = x - pl * K;
+    my_c[j] = topk_idx[((size_t)bg * N + min(p0 + pl, N - 1)) * K + kk];
+  }
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int x = tid + 256 * j;
-    my_c[j] = -1;
+    const int c = my_c[j];
     my_r[j] = 0;
-    if (x < E) {
-      const int pl = x / K, kk = x - pl * K;
-      const int pos = p0 + pl;
-      const int c = pos < N ? topk_idx[((size_t)bg * N + pos) * K + kk] : -1;
-      if (c >= 0 && c < ndmax) {
-        my_c[j] = c;
-        my_r[j] = atomicAdd(&off[c], 1);
-      }
-    }
+    const bool ok = x < E && p0 + x / K < N && c >= 0 && c < ndmax;
+    my_c[j] = ok ? c : -1;
+    if (ok) my_r[j] = atomicAdd(&off[c], 1);
   }
   __syncthreads();
   for (int x = tid; x < ndmax; x += 256) nzl[x] = off[x] > 0 ? 1 : 0;

@@ -554,15 +554,32 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
   __syncthreads();
 
   // ---------------- ds_c = w_c (delta_c - D); dq = token part + scale sum_c ds_c kL_c
-  for (int x = tid; x < R * K; x += 256) {
-    const int r = x / K, kk = x - r * K;
-    const int pos = p0 + r / G, hh = r % G;
-    if (pos >= N) continue;
-    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pos;
-    const float wc = dsS[x];
-    const float dsv = wc == 0.f ? 0.f : wc * (delta_o[ro * K + kk] - Ds[r]);
-    dsS[x] = dsv;
-    ds_o[ro * K + kk] = dsv;
+  // (loads are issued in batches before their values are used: a guarded
+  // load per element would wait for each in turn)
+  {
+    constexpr int XB = 8;
+    for (int x0 = 0; x0 < R * K; x0 += 256 * XB) {
+      float dl[XB];
+#pragma unroll
+      for (int j = 0; j < XB; ++j) {
+        const int x = min(x0 + tid + 256 * j, R * K - 1);
+        const int r = x / K, kk = x - r * K;
+        const int pos = min(p0 + r / G, N - 1);
+        dl[j] = delta_o[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk];
+      }
+#pragma unroll
+      for (int j = 0; j < XB; ++j) {
+        const int x = x0 + tid + 256 * j;
+        if (x >= R * K) continue;
+        const int r = x / K, kk = x - r * K;
+        const int pos = p0 + r / G;
+        if (pos >= N) continue;
+        const float wc = dsS[x];
+        const float dsv = wc == 0.f ? 0.f : wc * (dl[j] - Ds[r]);
+        dsS[x] = dsv;
+        ds_o[(((size_t)b * Hq + g * G + r % G) * N + pos) * K + kk] = dsv;
+      }
+    }
   }
   __syncthreads();
   for (int x = tid; x < R * DH / 4; x += 256) {
@@ -571,13 +588,32 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
     if (pos >= N) continue;
     const int32_t* ti = topk_idx + ((size_t)bg * N + pos) * K;
     f32x4 sur = zero4();
-    for (int kk = 0; kk < K; ++kk) {
-      const int c = ti[kk];
-      if (c >= 0) {
-        const float dsv = dsS[r * K + kk];
-        const T* kr = kL + ((size_t)bg * C + c) * DH + d4;
+    // the row's chunk ids, then their landmark rows, each batch of eight
+    // requested at once
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      int cc[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sur[j] += dsv * to_f<T>(kr[j]);
+      for (int j = 0; j < 8; ++j) cc[j] = ti[min(k0 + j, K - 1)];
+      float kv[8][4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const T* kr = kL + ((size_t)bg * C + (cc[j] >= 0 ? cc[j] : 0)) * DH + d4;
+        if constexpr (sizeof(T) == 2) {
+          const u16x4 hv = *reinterpret_cast<const u16x4*>(kr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kv[j][i] = bf2f(hv[i]);
+        } else {
+          const f32x4 fv = *reinterpret_cast<const f32x4*>(kr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kv[j][i] = fv[i];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = k0 + j < K && cc[j] >= 0;
+        const float dsv = ok ? dsS[r * K + min(k0 + j, K - 1)] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sur[i] += dsv * kv[j][i];
       }
     }
     sur *= scale;

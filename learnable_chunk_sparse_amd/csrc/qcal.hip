@@ -24,7 +24,7 @@ constexpr int QT_KP = QT_K + 8;     // padded k pitch of the bf16 tiles (element
 constexpr int QT_UP = QT_N + 4;     // pitch of the fp32 u tile
 }
 
-template <typename T>
+template <typename T, int DH, int NS>
 __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* __restrict__ hs,
                                               const T* __restrict__ Wd, const T* __restrict__ Wu,
                                               float* __restrict__ qhat, float* __restrict__ u_out,
@@ -50,19 +50,22 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
   const int cb = min(c0 + lrow, ncol - 1);          // columns past Hq*r are never stored
   const T* asrc = hs + (size_t)ta * D + lk;
   const T* bsrc = Wd + (size_t)cb * D + lk;
-  FT ra[2], rbv[2];
-  auto fetch = [&](int k0) __attribute__((always_inline)) {
+  // NS k-steps in flight in a register ring (the loop is unrolled by NS, so
+  // the ring indices are fixed; fetches past the end re-read the last step)
+  FT ra[NS][2], rbv[NS][2];
+  auto fetch = [&](int s, int k0) __attribute__((always_inline)) {
+    k0 = min(k0, D - QT_K);
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      ra[v] = ld8<T>(asrc + k0 + VEC * v);
-      rbv[v] = ld8<T>(bsrc + k0 + VEC * v);
+      ra[s][v] = ld8<T>(asrc + k0 + VEC * v);
+      rbv[s][v] = ld8<T>(bsrc + k0 + VEC * v);
     }
   };
-  auto stash = [&]() __attribute__((always_inline)) {
+  auto stash = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      *reinterpret_cast<FT*>(As + lrow * QT_KP + lk + VEC * v) = ra[v];
-      *reinterpret_cast<FT*>(Bs + lrow * QT_KP + lk + VEC * v) = rbv[v];
+      *reinterpret_cast<FT*>(As + lrow * QT_KP + lk + VEC * v) = ra[s][v];
+      *reinterpret_cast<FT*>(Bs + lrow * QT_KP + lk + VEC * v) = rbv[s][v];
     }
   };
 
@@ -72,23 +75,27 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
 #pragma unroll
     for (int b2 = 0; b2 < 4; ++b2) acc[a][b2] = zero4();
 
-  fetch(0);
-  for (int k0 = 0; k0 < D; k0 += QT_K) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (k0 + QT_K < D) fetch(k0 + QT_K);
-    FT af[4], bfr[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      af[mb] = *reinterpret_cast<const FT*>(As + (64 * wm + 16 * mb + col) * QT_KP + 8 * grp);
+  for (int s = 0; s < NS; ++s) fetch(s, s * QT_K);
+  for (int k0 = 0; k0 < D; k0 += NS * QT_K) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      bfr[nb] = *reinterpret_cast<const FT*>(Bs + (64 * wn + 16 * nb + col) * QT_KP + 8 * grp);
+    for (int s = 0; s < NS; ++s) {
+      __syncthreads();
+      stash(s);
+      __syncthreads();
+      fetch(s, k0 + (s + NS) * QT_K);
+      FT af[4], bfr[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
+        af[mb] = *reinterpret_cast<const FT*>(As + (64 * wm + 16 * mb + col) * QT_KP + 8 * grp);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma16(af[mb], bfr[nb], acc[mb][nb]);
+      for (int nb = 0; nb < 4; ++nb)
+        bfr[nb] = *reinterpret_cast<const FT*>(Bs + (64 * wn + 16 * nb + col) * QT_KP + 8 * grp);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma16(af[mb], bfr[nb], acc[mb][nb]);
+    }
   }
   __syncthreads();
   // u tile -> LDS (fp32), and optionally to global
@@ -117,19 +124,23 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
   const int nks = (r + 31) / 32;
   for (int hl = w; hl < nh; hl += 4) {
     const int h = h0 + hl;
-    constexpr int NBM = 8;  // 16-dim blocks for d <= 128
-    const int nnb = d / 16;
+    constexpr int NBM = DH / 16;  // 16-dim blocks
+    constexpr int nnb = NBM;
+    // W_up[h] fragments: loaded unguarded from clamped columns, then zeroed
+    // where the 32-wide k step runs past r (no per-element branches around
+    // loads)
     FT wa[NBM][2];
 #pragma unroll
     for (int nb = 0; nb < NBM; ++nb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        const bool kin = ks < nks && 32 * ks + 8 * grp < r;
+        const int kc = kin ? 32 * ks + 8 * grp : 0;
+        const FT raw = ld8<T>(Wu + ((size_t)h * d + 16 * nb + col) * r + kc);
         float z[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = 0.f;
+        for (int j = 0; j < 8; ++j) z[j] = kin ? (float)raw[j] : 0.f;
         wa[nb][ks] = pack8<T>(z);
-        if (nb < nnb && ks < nks && 32 * ks + 8 * grp < r)
-          wa[nb][ks] = ld8<T>(Wu + ((size_t)h * d + 16 * nb + col) * r + 32 * ks + 8 * grp);
       }
     // q^T fragments of token block mb: 4 consecutive dims per (lane, nb)
     typedef typename std::conditional<sizeof(T) == 2, u16x4, f32x4>::type QV;
@@ -142,22 +153,22 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
     {
       const size_t ro = qrow(0);
 #pragma unroll
-      for (int nb = 0; nb < NBM; ++nb)
-        if (nb < nnb) qv[nb] = *reinterpret_cast<const QV*>(q + ro + 16 * nb);
+      for (int nb = 0; nb < NBM; ++nb) qv[nb] = *reinterpret_cast<const QV*>(q + ro + 16 * nb);
     }
     for (int mb = 0; mb < QT_M / 16; ++mb) {
-      if (mb + 1 < QT_M / 16) {
-        const size_t rn = qrow(mb + 1);
+      {
+        const size_t rn = qrow(min(mb + 1, QT_M / 16 - 1));
 #pragma unroll
-        for (int nb = 0; nb < NBM; ++nb)
-          if (nb < nnb) qn[nb] = *reinterpret_cast<const QV*>(q + rn + 16 * nb);
+        for (int nb = 0; nb < NBM; ++nb) qn[nb] = *reinterpret_cast<const QV*>(q + rn + 16 * nb);
       }
       f32x4 acc[NBM];
 #pragma unroll
       for (int nb = 0; nb < NBM; ++nb) acc[nb] = zero4();
-      for (int ks = 0; ks < nks; ++ks) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks >= nks) break;  // uniform; ks stays a constant index into wa
         const bool kv = 32 * ks + 8 * grp < r;
-        const float* ur = us + (16 * mb + col) * QT_UP + hl * r + 32 * ks + 8 * grp;
+        const float* ur = us + (16 * mb + col) * QT_UP + hl * r + (kv ? 32 * ks + 8 * grp : 0);
         float x[8], y[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = kv ? ur[j] : 0.f;
@@ -200,23 +211,22 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
   dim3 grid((ntok + QT_M - 1) / QT_M, (p.Hq * p.r + QT_N - 1) / QT_N);
   const size_t el = p.dtype == 1 ? 2 : 4;
   const size_t lds = std::max<size_t>((size_t)(QT_M + QT_N) * QT_KP * el, (size_t)QT_M * QT_UP * 4);
-  hipError_t err;
+  auto go = [&](auto kern, auto tq) -> hipError_t {
+    typedef decltype(tq) TT;
+    hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const TT*)q, (const TT*)h, (const TT*)W_down,
+                       (const TT*)W_up, q_hat, u, ntok, Nq, p.Hq, p.d, p.D, p.r);
+    return hipGetLastError();
+  };
+  // four k steps in flight when D is a multiple of 128
+  const bool deep = p.D % (4 * QT_K) == 0;
   if (p.dtype == 1) {
-    auto kern = k_qcal<uint16_t>;
-    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-      return err;
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint16_t*)q, (const uint16_t*)h,
-                       (const uint16_t*)W_down, (const uint16_t*)W_up, q_hat, u, ntok, Nq, p.Hq,
-                       p.d, p.D, p.r);
-  } else {
-    auto kern = k_qcal<float>;
-    if ((err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-      return err;
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const float*)q, (const float*)h,
-                       (const float*)W_down, (const float*)W_up, q_hat, u, ntok, Nq, p.Hq, p.d, p.D,
-                       p.r);
+    if (p.d == 64) return deep ? go(k_qcal<uint16_t, 64, 4>, uint16_t()) : go(k_qcal<uint16_t, 64, 1>, uint16_t());
+    return deep ? go(k_qcal<uint16_t, 128, 4>, uint16_t()) : go(k_qcal<uint16_t, 128, 1>, uint16_t());
   }
-  return hipGetLastError();
+  if (p.d == 64) return deep ? go(k_qcal<float, 64, 4>, float()) : go(k_qcal<float, 64, 1>, float());
+  return deep ? go(k_qcal<float, 128, 4>, float()) : go(k_qcal<float, 128, 1>, float());
 }
 
 }  // namespace hils

@@ -1131,7 +1131,11 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
                          w.delta, p.N, p.Hkv, p.K, p.W, p.S, p.scale, ntiles, p.C);
       return hipGetLastError();
     };
-    err = dq_cb<T, G, DH>(p) == 2 ? go(std::integral_constant<int, 2>()) : go(std::integral_constant<int, 1>());
+    if (bwd_dq_shared_ok(p))
+      err = launch_bwd_dq_shared(p, q, k, v, w.kt, w.Np, dO, kL, topk_idx, w.sT, lse, w.Dv, dq,
+                                 w.dqhat, w.ds, w.beta, w.delta, st);
+    else
+      err = dq_cb<T, G, DH>(p) == 2 ? go(std::integral_constant<int, 2>()) : go(std::integral_constant<int, 1>());
     if (err != hipSuccess) return err;
   }
   // dk / dv pass

@@ -68,6 +68,12 @@ hipError_t gemm(const GemmArgs& g, const void* A, int a_dtype, const void* B, in
                 hipStream_t st);
 
 // Backward.
+bool bwd_dq_shared_ok(const Dims& p);
+hipError_t launch_bwd_dq_shared(const Dims& p, const void* q, const void* k, const void* v,
+                                const void* kt, int Np, const void* dO, const void* kL,
+                                const int32_t* topk_idx, const float* sT, const float* lse,
+                                float* Dv, float* dq, float* dqhat, float* ds, float* beta,
+                                float* delta, hipStream_t st);
 size_t bwd_workspace(const Dims& p);
 hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v, const void* kL,
                       const void* e, const void* h, const void* W_down, const void* W_up,

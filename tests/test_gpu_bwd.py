@@ -39,6 +39,9 @@ SMALL = [
     ("gqa4_d128_qcal", "bf16", 1, 8, 2, 128, 1100, 6, 256, 128, 32, 3.0),
     ("gqa2_d64", "bf16", 1, 4, 2, 64, 900, 5, 192, 0, 0, 8.0),
     ("fp32_d64_qcal", "fp32", 1, 2, 1, 64, 600, 3, 64, 64, 32, 1.0),
+    # bf16 d = 64 with K a multiple of 4: the shared-block dq pass (G = 2, 4)
+    ("gqa2_d64_k8_qcal", "bf16", 1, 4, 2, 64, 1300, 8, 192, 64, 16, 2.0),
+    ("gqa4_d64_k4", "bf16", 1, 8, 2, 64, 800, 4, 128, 0, 0, 3.0),
     ("fp32_d128_gqa2_r16", "fp32", 1, 4, 2, 128, 500, 4, 128, 64, 16, 1.0),
 ]
 
@@ -55,6 +58,26 @@ def test_bwd_small(case):
     names = GRADS + (WGRADS if r else ())
     for n in names:
         compare(f"{name} {n}", g[n].cpu().double().numpy(), ref[n], dt)
+
+
+def test_bwd_extreme_token_scores():
+    """Keys of some distant chunks scaled up, so that their token scores sit
+    far above the rows' L (exp against L overflows; the dq pass redoes those
+    row blocks against the chunk maximum). Gradients then reach magnitudes
+    of tens, so the bf16 tolerance is applied relative to each gradient's
+    largest oracle value."""
+    wl = Workload("bwd_extreme", seed=33, dtype="bf16", B=1, Hq=2, Hkv=2, d=64, N=1000, S=64, K=4,
+                  W=128, D=0, r=0, e_range=2.0, e_shift=4.0, mode="train")
+    say("case bwd extreme token scores")
+    t = make_inputs(wl)
+    kk = t["k"].float()
+    kk[:, :, 128:384] *= 45.0
+    t["k"] = kk.to(torch.bfloat16)
+    o, lse, idx, g = gpu_fwd_bwd(wl, to_dev(t))
+    ref = H.hils_backward(t, t["dO"], wl.S, wl.K, wl.W, forced_topk=idx.cpu().numpy())
+    for n in GRADS:
+        sc = max(1.0, float(np.abs(ref[n]).max()))
+        compare(f"extreme {n}", g[n].cpu().double().numpy() / sc, ref[n] / sc, "bf16")
 
 
 def test_bwd_train_345m_full_size_sampled_groups():

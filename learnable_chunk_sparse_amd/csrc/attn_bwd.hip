@@ -45,18 +45,32 @@ __global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
 
 // fp32 score s_c = scale q_hat . kL_c + e_c of every selected slot. A
 // workgroup takes 16 consecutive query rows: their q_hat rows are staged in
-// LDS with coalesced loads, then each thread owns (row, slot) pairs and reads
-// the selected landmark row with 16-byte loads (landmarks stay in L2).
+// LDS with coalesced loads. Eight adjacent lanes share a (row, slot) pair,
+// each reading DH / 8 elements of the selected landmark row (one wave load
+// covers eight whole rows, which stay in L2), and their partial dot products
+// are summed across the eight lanes. Four pairs per lane are in flight.
 template <typename T, typename QT, int DH>
 __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
                                                   const int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ sT, long rows, int N, int Hq,
                                                   int Hkv, int G, int C, int K, float scale) {
-  constexpr int PR = 16, QP = DH + 4;
+  constexpr int PR = 16, QP = DH + 4, DL = DH / 8, NF = DL / 8, UP = 4;
+  typedef typename Frag<T>::type FT;
   __shared__ __align__(16) float qrow[PR * QP];
+  __shared__ long ibase[PR];  // (bg N + i) K of each row: its selection list
+  __shared__ long cbase[PR];  // bg C: its landmark rows
   const int tid = threadIdx.x;
   const long r0 = (long)blockIdx.x * PR;
+  if (tid < PR) {
+    const long row = std::min(r0 + tid, rows - 1);
+    const int i = (int)(row % N);
+    const long bh = row / N;
+    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+    const long bg = (long)b * Hkv + h / G;
+    ibase[tid] = (bg * N + i) * K;
+    cbase[tid] = bg * C;
+  }
   for (int x = tid; x < PR * DH / 4; x += 256) {
     const int rr = x / (DH / 4), d4 = 4 * (x - rr * (DH / 4));
     const long row = r0 + rr;
@@ -73,34 +87,47 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, con
     *reinterpret_cast<f32x4*>(qrow + rr * QP + d4) = v;
   }
   __syncthreads();
-  for (int x = tid; x < PR * K; x += 256) {
-    const int rr = x / K, kk = x - rr * K;
-    const long row = r0 + rr;
-    if (row >= rows) break;
-    const int i = (int)(row % N);
-    const long bh = row / N;
-    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
-    const long bg = (long)b * Hkv + h / G;
-    const int c = topk_idx[(bg * N + i) * K + kk];
-    float s = __builtin_nanf("");
-    if (c >= 0) {
-      const T* kr = kL + (bg * C + c) * DH;
-      const float* qr = qrow + rr * QP;
+  const int l8 = tid & 7, pr = tid >> 3;  // 32 pairs per pass
+  const int npair = (int)std::min<long>(PR, rows - r0) * K;
+  for (int x0 = pr; x0 < npair; x0 += 32 * UP) {
+    int cc[UP], rrv[UP];
+#pragma unroll
+    for (int t = 0; t < UP; ++t) {
+      const int x = min(x0 + 32 * t, npair - 1);
+      const int rr = x / K, kk = x - rr * K;
+      rrv[t] = rr;
+      cc[t] = topk_idx[ibase[rr] + kk];
+    }
+    FT kv[UP][NF];
+    float ev[UP];
+#pragma unroll
+    for (int t = 0; t < UP; ++t) {
+      const long kc = cbase[rrv[t]] + max(cc[t], 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) kv[t][f] = ld8<T>(kL + kc * DH + DL * l8 + 8 * f);
+      ev[t] = to_f<T>(e[kc]);
+    }
+#pragma unroll
+    for (int t = 0; t < UP; ++t) {
+      const float* qr = qrow + rrv[t] * QP + DL * l8;
       float acc = 0.f;
 #pragma unroll
-      for (int d8 = 0; d8 < DH; d8 += 8) {
-        const typename Frag<T>::type kv = ld8<T>(kr + d8);
-        const f32x4 qa = *reinterpret_cast<const f32x4*>(qr + d8);
-        const f32x4 qb = *reinterpret_cast<const f32x4*>(qr + d8 + 4);
+      for (int f = 0; f < NF; ++f) {
+        const f32x4 qa = *reinterpret_cast<const f32x4*>(qr + 8 * f);
+        const f32x4 qb = *reinterpret_cast<const f32x4*>(qr + 8 * f + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          acc = fmaf(qa[j], (float)kv[j], acc);
-          acc = fmaf(qb[j], (float)kv[j + 4], acc);
+          acc = fmaf(qa[j], (float)kv[t][f][j], acc);
+          acc = fmaf(qb[j], (float)kv[t][f][j + 4], acc);
         }
       }
-      s = fmaf(acc, scale, to_f<T>(e[bg * C + c]));
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      const int x = x0 + 32 * t;
+      if (l8 == 0 && x < npair)
+        sT[r0 * K + x] = cc[t] >= 0 ? fmaf(acc, scale, ev[t]) : __builtin_nanf("");
     }
-    sT[row * K + kk] = s;
   }
 }
 
@@ -939,61 +966,76 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
 
 // Q-Cal part of the landmark gradient: dkL_c += scale sum_h W_up[h] U_h with
 // U_h = sum over the rows of head h that selected chunk c of ds u_row. One
-// workgroup per chunk; r lanes share a row (u rows are read whole).
-template <typename T>
+// workgroup per chunk. R / 4 adjacent lanes share a row (lane q loads u
+// elements 4q .. 4q + 3), so one wave load covers whole 128-byte rows rather
+// than one line per lane; a lane's rows are entries rs, rs + 256 / (R / 4),
+// ... (rs its row slot, so its head rs % G is fixed). Eight rows per lane are
+// in flight, with the next eight rows' list entries. The lanes of a head and
+// quad are summed across the wave's row slots, then across the waves in LDS.
+template <typename T, int R>
 __global__ __launch_bounds__(256) void k_bwd_dklu(const int* __restrict__ ioff,
                                                   const int* __restrict__ ilst,
                                                   const float* __restrict__ ds_i,
                                                   const float* __restrict__ u,
                                                   const T* __restrict__ W_up,
                                                   float* __restrict__ dkL, int N, int Hkv, int G,
-                                                  int K, int C, int d, int r, float scale) {
-  __shared__ float us[4 * 64];  // [G][r]
+                                                  int K, int C, int d, float scale) {
+  constexpr int LPR = R / 4, RPI = 256 / LPR, RU = 8;
+  __shared__ f32x4 part[4][64];
+  __shared__ float us[256];  // [G][R]
   int c, bg;
   xcd_block(c, bg);
-  const int tid = threadIdx.x;
-  const int b = bg / Hkv, g = bg - b * Hkv;
-  const int Hq = Hkv * G;
-  for (int x = tid; x < G * r; x += 256) us[x] = 0.f;
-  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = bg / Hkv, g = bg - b * Hkv, Hq = Hkv * G;
   const int e0 = ioff[(size_t)bg * (C + 1) + c];
   const int nrow = (ioff[(size_t)bg * (C + 1) + c + 1] - e0) * G;
   const int* lst = ilst + (size_t)bg * N * K + e0;
-  const int j = tid % r, slot = tid / r, nslot = 256 / r;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int x = slot;
-  for (; x + 3 * nslot < nrow; x += 4 * nslot) {
-    float dsv[4], uv[4];
-    int hh[4];
+  const int rs = tid / LPR, q = tid - rs * LPR;
+  const int h = g * G + rs % G;
+  const float* ub = u + (size_t)b * N * Hq * R + (size_t)h * R + 4 * q;  // + pos Hq R
+  const float* db = ds_i + (size_t)(b * Hq + h) * N * K;                // + pos K + slot
+  f32x4 acc = zero4();
+  if (nrow > 0) {
+    int en[RU];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int xx = x + t * nslot;
-      const int en = lst[xx / G];
-      hh[t] = xx % G;
-      const int pos = en >> 6, kk = en & 63;
-      dsv[t] = ds_i[((size_t)(b * Hq + g * G + hh[t]) * N + pos) * K + kk];
-      uv[t] = u[((size_t)(b * N + pos) * Hq + g * G + hh[t]) * r + j];
+    for (int t = 0; t < RU; ++t) en[t] = lst[min(rs + RPI * t, nrow - 1) / G];
+    for (int x0 = rs; x0 < nrow; x0 += RPI * RU) {
+      float dsv[RU];
+      f32x4 uv[RU];
+#pragma unroll
+      for (int t = 0; t < RU; ++t) {
+        const int pos = en[t] >> 6, kk = en[t] & 63;
+        const float dv = db[(size_t)pos * K + kk];
+        dsv[t] = x0 + RPI * t < nrow ? dv : 0.f;
+        uv[t] = *reinterpret_cast<const f32x4*>(ub + (size_t)pos * Hq * R);
+      }
+#pragma unroll
+      for (int t = 0; t < RU; ++t) en[t] = lst[min(x0 + RPI * (RU + t), nrow - 1) / G];
+#pragma unroll
+      for (int t = 0; t < RU; ++t) acc += dsv[t] * uv[t];
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int h2 = 0; h2 < 4; ++h2) acc[h2] += hh[t] == h2 ? dsv[t] * uv[t] : 0.f;
   }
-  for (; x < nrow; x += nslot) {
-    const int en = lst[x / G], h1 = x % G;
-    const int pos = en >> 6, kk = en & 63;
-    const float dsv = ds_i[((size_t)(b * Hq + g * G + h1) * N + pos) * K + kk];
-    const float uv = u[((size_t)(b * N + pos) * Hq + g * G + h1) * r + j];
+  // sum over the wave's row slots of one head: lanes l, l ^ m for m >= LPR G
 #pragma unroll
-    for (int h2 = 0; h2 < 4; ++h2) acc[h2] += h1 == h2 ? dsv * uv : 0.f;
+  for (int m = 32; m >= LPR; m >>= 1) {
+    if (m < LPR * G) break;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) acc[e2] += __shfl_xor(acc[e2], m, 64);
   }
-  for (int h2 = 0; h2 < G; ++h2) atomicAdd(&us[h2 * r + j], acc[h2]);
+  if (lane < LPR * G) part[w][lane] = acc;  // lane = head * LPR + quad
+  __syncthreads();
+  if (tid < G * R) {
+    const int h2 = tid / R, j = tid - h2 * R;
+    const int l = h2 * LPR + j / 4;
+    us[tid] = part[0][l][j & 3] + part[1][l][j & 3] + part[2][l][j & 3] + part[3][l][j & 3];
+  }
   __syncthreads();
   for (int dd = tid; dd < d; dd += 256) {
     float val = 0.f;
     for (int h2 = 0; h2 < G; ++h2) {
-      const T* wr = W_up + ((size_t)(g * G + h2) * d + dd) * r;
-      for (int jj = 0; jj < r; ++jj) val = fmaf(to_f<T>(wr[jj]), us[h2 * r + jj], val);
+      const T* wr = W_up + ((size_t)(g * G + h2) * d + dd) * R;
+#pragma unroll 8
+      for (int jj = 0; jj < R; ++jj) val = fmaf(to_f<T>(wr[jj]), us[h2 * R + jj], val);
     }
     dkL[((size_t)bg * C + c) * d + dd] += val * scale;
   }
@@ -1002,7 +1044,7 @@ __global__ __launch_bounds__(256) void k_bwd_dklu(const int* __restrict__ ioff,
 // --------------------------------------------------------------- host side
 namespace {
 struct BwdWs {
-  float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du;
+  float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du, *gwork;
   int *cnt, *off, *lst;
   void* kt;
   const void* W_up;
@@ -1017,6 +1059,21 @@ int inv_ranges(const Dims& p) {
   return (int)std::max<long>(ns, 1);
 }
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+// dW_down[h] += sum_i du[b, i, h, :] (x) h[b, i, :]: all heads and all batch
+// elements in one product, rows (h, j) of du^T [Hq r x B N] times h [B N x D]
+GemmArgs dwdown_args(const Dims& p, float* dW_down) {
+  GemmArgs g;
+  const long Hr = (long)p.Hq * p.r;
+  g.M = (int)Hr; g.N = p.D; g.K = p.B * p.N;
+  g.akm = true; g.bkm = false;
+  g.lda = Hr; g.ldb = p.D; g.ldc = p.D;
+  g.C = dW_down;
+  // split K so the launch holds ~2048 64x64 tiles (atomic split-K path)
+  const long tiles = (long)((Hr + 63) / 64) * ((p.D + 63) / 64);
+  g.splits = (int)std::max(1L, std::min((long)(g.K / 256), (2048 + tiles - 1) / tiles));
+  g.accumulate = true;
+  return g;
+}
 size_t carve(const Dims& p, void* base, BwdWs* w) {
   char* c = static_cast<char*>(base);
   size_t o = 0;
@@ -1037,6 +1094,7 @@ size_t carve(const Dims& p, void* base, BwdWs* w) {
   w->delta = (float*)take(rows * p.K * 4);
   w->dqhat = (float*)take(qc ? rows * p.d * 4 : 0);
   w->du = (float*)take(qc ? (size_t)p.B * p.N * p.Hq * p.r * 4 : 0);
+  w->gwork = (float*)take(qc ? gemm_work_bytes(dwdown_args(p, nullptr)) : 0);
   w->ns = inv_ranges(p);
   w->cnt = (int*)take(bg * p.C * w->ns * 4);
   w->off = (int*)take(bg * (p.C + 1) * 4);
@@ -1151,8 +1209,9 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (p.r > 0 && p.C > 0) {
-    hipLaunchKernelGGL(k_bwd_dklu<T>, dim3(p.C, (unsigned)bg), dim3(256), 0, st, w.off, w.lst, w.ds,
-                       (const float*)w.u, (const T*)w.W_up, dkL, p.N, p.Hkv, G, p.K, p.C, p.d, p.r,
+    auto dklu = p.r == 16 ? k_bwd_dklu<T, 16> : p.r == 32 ? k_bwd_dklu<T, 32> : k_bwd_dklu<T, 64>;
+    hipLaunchKernelGGL(dklu, dim3(p.C, (unsigned)bg), dim3(256), 0, st, w.off, w.lst, w.ds,
+                       (const float*)w.u, (const T*)w.W_up, dkL, p.N, p.Hkv, G, p.K, p.C, p.d,
                        p.scale);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1238,22 +1297,9 @@ hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v
     g.accumulate = true;
     if ((err = gemm(g, w.dqhat, 0, w.u, 0, st)) != hipSuccess) return err;
   }
-  // dW_down[h] += sum_i du[b, i, h, :] (x) h[b, i, :], all heads in one
-  // product per batch element: rows (h, j) of du^T [Hq r x N] times h [N x D]
   {
-    GemmArgs g;
-    g.M = (int)Hr; g.N = p.D; g.K = p.N;
-    g.akm = true; g.bkm = false;
-    g.lda = Hr; g.ldb = p.D; g.ldc = p.D;
-    g.n1 = p.B; g.n2 = 1;
-    g.sA1 = NHr; g.sA2 = 0;
-    g.sB1 = (long)p.N * p.D; g.sB2 = 0;
-    g.sC1 = 0; g.sC2 = 0;
-    g.C = dW_down;
-    // split K so the launch holds ~2048 64x64 tiles
-    const long tiles = (long)((Hr + 63) / 64) * ((p.D + 63) / 64) * p.B;
-    g.splits = (int)std::max(1L, std::min((long)(p.N / 256), (2048 + tiles - 1) / tiles));
-    g.accumulate = true;
+    GemmArgs g = dwdown_args(p, dW_down);
+    g.work = w.gwork;
     if ((err = gemm(g, w.du, 0, h, dt, st)) != hipSuccess) return err;
   }
   // dh[b, i, :] = sum_{h, j} du[b, i, h, j] W_down[h, j, :]

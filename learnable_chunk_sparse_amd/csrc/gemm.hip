@@ -13,6 +13,9 @@
 #include "hils_common.h"
 #include "hils_internal.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace hils {
 
 template <typename TA, typename TB, bool AKM, bool BKM>
@@ -289,6 +292,210 @@ __global__ __launch_bounds__(256) void k_gemm_v(const TA* __restrict__ A, const 
       }
 }
 
+// Products whose operands both have the contraction index outermost (A[k][m]
+// and B[k][n]), as in the weight gradients summed over tokens. Tiles of
+// 128 x 128 (four waves of 64 x 64), k steps of 32, two LDS buffers, and the
+// stage after next held in registers. A thread loads a 4 (k) x 4 (m or n)
+// block of each operand and writes it into LDS as four 4-element k runs
+// ([row][k] layout, 8-byte stores; with a pitch of 40 elements the 32 lanes of
+// a store cover the 64 banks once). The workgroups of one XCD take
+// consecutive (split, tile) ids, so a split's operand slices are shared in
+// that XCD's L2. Split-K partial tiles go to a workspace slab per split and
+// k_gemm_sum adds them (no atomics); without a split the tile goes to C.
+template <typename T> struct V4;
+template <> struct V4<uint16_t> { typedef u16x4 type; };
+template <> struct V4<float> { typedef f32x4 type; };
+
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256, 2) void k_gemm_kk(const TA* A, const TB* B,
+                                                    float* __restrict__ out, int M, int N, int K,
+                                                    long lda, long ldb, long ldo, long slab, int kchunk,
+                                                    int ntn, int ntiles, int accumulate) {
+  constexpr bool ALO = sizeof(TA) == 4, BLO = sizeof(TB) == 4;
+  constexpr int KP = 40, PL = 128 * KP;  // elements of one operand plane
+  constexpr int NPL = 2 + ALO + BLO;     // planes per buffer: A hi (lo), B hi (lo)
+  extern __shared__ __align__(16) uint16_t sm[];  // [2][NPL][128][KP]
+  typedef typename V4<TA>::type VA;
+  typedef typename V4<TB>::type VB;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w & 1, wn = w >> 1;
+  int L, y0;
+  xcd_block(L, y0);
+  const int sp = L / ntiles, tile = L - sp * ntiles;
+  const int mt = tile / ntn, nt = tile - mt * ntn;
+  const int m0 = mt * 128, n0 = nt * 128;
+  const int k_begin = sp * kchunk, nk = (min(K, k_begin + kchunk) - k_begin) / 32;
+  const int kq = tid & 7, rq = tid >> 3;  // this thread's block: k 4 kq + (0..3), row 4 rq + (0..3)
+  const TA* ap = A + (long)(k_begin + 4 * kq) * lda + m0 + 4 * rq;
+  const TB* bp = B + (long)(k_begin + 4 * kq) * ldb + n0 + 4 * rq;
+  VA ra[2][4];
+  VB rb[2][4];
+  auto load = [&](int set, int s) __attribute__((always_inline)) {
+    const long ss = 32 * min(s, nk - 1);  // past the end: a repeated stage, never used
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      ra[set][kk] = *reinterpret_cast<const VA*>(ap + (ss + kk) * lda);
+      rb[set][kk] = *reinterpret_cast<const VB*>(bp + (ss + kk) * ldb);
+    }
+  };
+  auto put = [&](uint16_t* hi_p, uint16_t* lo_p, auto v, auto lo_on) __attribute__((always_inline)) {
+    // v[kk][mm] -> rows 4 rq + mm, k run 4 kq .. 4 kq + 3
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      u16x4 hi, lo;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if constexpr (decltype(lo_on)::value) {
+          const float x = v[kk][mm];
+          hi[kk] = f2bf(x);
+          lo[kk] = f2bf(x - bf2f(hi[kk]));
+        } else {
+          hi[kk] = v[kk][mm];
+        }
+      }
+      const int o = (4 * rq + mm) * KP + 4 * kq;
+      *reinterpret_cast<u16x4*>(hi_p + o) = hi;
+      if constexpr (decltype(lo_on)::value) *reinterpret_cast<u16x4*>(lo_p + o) = lo;
+    }
+  };
+  auto store = [&](int set, int buf) __attribute__((always_inline)) {
+    uint16_t* base = sm + buf * NPL * PL;
+    put(base, base + PL, ra[set], std::integral_constant<bool, ALO>());
+    put(base + (1 + ALO) * PL, base + (2 + ALO) * PL, rb[set], std::integral_constant<bool, BLO>());
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const uint16_t* base = sm + buf * NPL * PL;
+    const uint16_t* ah = base;
+    const uint16_t* al = base + PL;
+    const uint16_t* bh = base + (1 + ALO) * PL;
+    const uint16_t* bl = base + (2 + ALO) * PL;
+    const int fo = (lane & 15) * KP + 8 * (lane >> 4);
+    bf16x8 bhf[4], blf[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int o = (64 * wn + 16 * nb) * KP + fo;
+      bhf[nb] = *reinterpret_cast<const bf16x8*>(bh + o);
+      if constexpr (BLO) blf[nb] = *reinterpret_cast<const bf16x8*>(bl + o);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int o = (64 * wm + 16 * mb) * KP + fo;
+      const bf16x8 ahf = *reinterpret_cast<const bf16x8*>(ah + o);
+      bf16x8 alf;
+      if constexpr (ALO) alf = *reinterpret_cast<const bf16x8*>(al + o);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        acc[mb][nb] = mma16(ahf, bhf[nb], acc[mb][nb]);
+        if constexpr (BLO) acc[mb][nb] = mma16(ahf, blf[nb], acc[mb][nb]);
+        if constexpr (ALO) acc[mb][nb] = mma16(alf, bhf[nb], acc[mb][nb]);
+      }
+    }
+  };
+  load(0, 0);
+  load(1, 1);
+  store(0, 0);
+  __syncthreads();
+  // (the empty asm statements keep the compiler from sinking the loads of
+  // the stage after next below the products; A and B are not restrict-
+  // qualified so that the statements order them)
+  for (int s = 0; s < nk; s += 2) {
+    load(0, s + 2);
+    asm volatile("" ::: "memory");
+    compute(0);
+    store(1, 1);
+    __syncthreads();
+    if (s + 1 >= nk) break;
+    load(1, s + 3);
+    asm volatile("" ::: "memory");
+    compute(1);
+    store(0, 0);
+    __syncthreads();
+  }
+  float* o = out + (size_t)sp * slab + (long)(m0 + 64 * wm + 4 * (lane >> 4)) * ldo + n0 + 64 * wn +
+             (lane & 15);
+  auto emit = [&](auto acc_on) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* c = o + (long)(16 * mb + i) * ldo + 16 * nb;
+          if constexpr (decltype(acc_on)::value)
+            *c += acc[mb][nb][i];
+          else
+            *c = acc[mb][nb][i];
+        }
+  };
+  if (accumulate)
+    emit(std::true_type());
+  else
+    emit(std::false_type());
+}
+
+// C[m][n] (+)= sum over the splits of the partial slabs P[s][m][n] (pitch N);
+// four consecutive n per thread.
+__global__ __launch_bounds__(256) void k_gemm_sum(const float* __restrict__ P, float* __restrict__ Cm,
+                                                  int M, int N, long ldc, int splits, int accumulate) {
+  const long n4 = (long)M * N / 4;
+  const long slab = (long)M * N;
+  for (long x = blockIdx.x * 256L + threadIdx.x; x < n4; x += (long)gridDim.x * 256) {
+    const long e = 4 * x;
+    const int m = (int)(e / N), n = (int)(e - (long)m * N);
+    f32x4 s = zero4();
+    for (int sp = 0; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(P + sp * slab + e);
+    f32x4* c = reinterpret_cast<f32x4*>(Cm + (long)m * ldc + n);
+    *c = accumulate ? *c + s : s;
+  }
+}
+
+// Launch shape of the k_gemm_kk path; false when the product does not have
+// its form (A k-major, B row-major, one batch, 128-multiples, 4-aligned rows).
+static bool kk_plan(const GemmArgs& g, int* splits, int* kchunk) {
+  if (!g.akm || g.bkm || g.n1 != 1 || g.n2 != 1) return false;
+  if (g.M % 128 || g.N % 128 || g.K % 32 || g.lda % 4 || g.ldb % 4 || g.ldc % 4) return false;
+  const int ntiles = (g.M / 128) * (g.N / 128);
+  int sp = std::max(1, std::min((512 + ntiles - 1) / ntiles, g.K / 1024));
+  int kc = (g.K + sp - 1) / sp;
+  kc = (kc + 31) / 32 * 32;
+  *splits = (g.K + kc - 1) / kc;
+  *kchunk = kc;
+  return true;
+}
+
+size_t gemm_work_bytes(const GemmArgs& g) {
+  int sp, kc;
+  if (!kk_plan(g, &sp, &kc) || sp == 1) return 0;
+  return (size_t)sp * g.M * g.N * sizeof(float);
+}
+
+template <typename TA, typename TB>
+static hipError_t gemm_kk_go(const GemmArgs& g, const TA* A, const TB* B, int splits, int kchunk,
+                             hipStream_t st) {
+  const int ntn = g.N / 128, ntiles = (g.M / 128) * ntn;
+  constexpr int NPL = 2 + (sizeof(TA) == 4) + (sizeof(TB) == 4);
+  const size_t lds = 2 * NPL * 128 * 40 * sizeof(uint16_t);
+  auto kern = k_gemm_kk<TA, TB>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  const bool direct = splits == 1;
+  float* out = direct ? g.C : g.work;
+  hipLaunchKernelGGL(kern, dim3(ntiles * splits), dim3(256), lds, st, A, B, out, g.M, g.N, g.K, g.lda,
+                     g.ldb, direct ? g.ldc : (long)g.N, direct ? 0L : (long)g.M * g.N, kchunk, ntn,
+                     ntiles, direct && g.accumulate ? 1 : 0);
+  if ((err = hipGetLastError()) != hipSuccess || direct) return err;
+  const long n4 = (long)g.M * g.N / 4;
+  const unsigned nb = (unsigned)std::min<long>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_gemm_sum, dim3(nb), dim3(256), 0, st, g.work, g.C, g.M, g.N, g.ldc, splits,
+                     g.accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
 // C[z] (+)= A[z] * B[z] over the batch z = (z1, z2), z1 < g.n1, z2 < g.n2.
 template <typename TA, typename TB, bool AKM, bool BKM>
 static hipError_t gemm_go(const GemmArgs& g, const TA* A, const TB* B, hipStream_t st) {
@@ -296,6 +503,12 @@ static hipError_t gemm_go(const GemmArgs& g, const TA* A, const TB* B, hipStream
   int kchunk = (g.K + splits - 1) / splits;
   kchunk = (kchunk + 31) / 32 * 32;
   splits = (g.K + kchunk - 1) / kchunk;
+  if constexpr (AKM && !BKM) {
+    int sk, kc;
+    if (kk_plan(g, &sk, &kc) && (uintptr_t)A % 16 == 0 && (uintptr_t)B % 16 == 0 &&
+        (sk == 1 || g.work != nullptr))
+      return gemm_kk_go<TA, TB>(g, A, B, sk, kc, st);
+  }
   dim3 grid((g.M + 63) / 64, (g.N + 63) / 64, g.n1 * g.n2 * splits);
   auto m8 = [](long x) { return x % 8 == 0; };
   const bool vec = m8(g.M) && m8(g.N) && m8(g.K) && m8(g.lda) && m8(g.ldb) && m8(g.sA1) && m8(g.sA2) &&

@@ -63,7 +63,11 @@ struct GemmArgs {
   float* C;
   int splits = 1;
   bool accumulate = false;
+  // workspace for split-K partial tiles of the token-major weight-gradient
+  // path (gemm_work_bytes); null selects the atomic split-K path
+  float* work = nullptr;
 };
+size_t gemm_work_bytes(const GemmArgs& g);
 hipError_t gemm(const GemmArgs& g, const void* A, int a_dtype, const void* B, int b_dtype,
                 hipStream_t st);
 

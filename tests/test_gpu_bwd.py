@@ -43,6 +43,10 @@ SMALL = [
     ("gqa2_d64_k8_qcal", "bf16", 1, 4, 2, 64, 1300, 8, 192, 64, 16, 2.0),
     ("gqa4_d64_k4", "bf16", 1, 8, 2, 64, 800, 4, 128, 0, 0, 3.0),
     ("fp32_d128_gqa2_r16", "fp32", 1, 4, 2, 128, 500, 4, 128, 64, 16, 1.0),
+    # Hq r and D multiples of 128: dW_down on the token-major weight-gradient
+    # GEMM (two K splits summed in bf16; one split written directly in fp32)
+    ("mha4_d64_qcal_wgemm", "bf16", 2, 4, 4, 64, 1024, 8, 128, 256, 32, 2.0),
+    ("fp32_gqa2_qcal_wgemm", "fp32", 1, 4, 2, 64, 1024, 4, 128, 128, 32, 1.0),
 ]
 
 

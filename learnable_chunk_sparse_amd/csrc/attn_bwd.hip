@@ -680,7 +680,7 @@ struct DkdvRow {
 };
 
 template <typename T, int G, int DH>
-__global__ __launch_bounds__(256) void k_bwd_dkdv(
+__global__ __launch_bounds__(256, sizeof(T) == 2 && DH == 64 ? 2 : 1) void k_bwd_dkdv(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dv,
     const int* __restrict__ ioff, const int* __restrict__ ilst, const float* __restrict__ ds_i,
@@ -689,7 +689,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
     int K, int W, float scale, int C) {
   typedef typename Frag<T>::type FT;
   constexpr int KS = DH / 32, MB = DH / 16;
-  constexpr int TW = DH == 64 ? 4 : 2;        // 16-token blocks per wave
+  // 16-token blocks per wave: two keep the dK / dV accumulators small enough
+  // for two waves per SIMD (all 64 tokens per wave would need one)
+  constexpr int TW = 2;
   constexpr int NTG = 4 / TW, WPG = 4 / NTG;  // token groups, waves per token group
   constexpr int MBL = MB / NTG;               // d blocks of the dkL product per token group
   extern __shared__ __align__(16) float red[];  // [2][64][DH]

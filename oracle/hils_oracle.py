@@ -45,6 +45,10 @@ notes of the repository):
   * fewer than K distant chunks: all are taken; none: plain causal window
     attention.
 
+Upstream of step 2, landmark_summary builds kL and e themselves from each
+chunk's landmark query (paperglide, "The HiLS-Attention Mechanism", the
+landmark worked example), with its chain-rule backward landmark_backward.
+
 The backward pass is not printed on the pages; it is the chain rule applied
 to steps 1-6 with the selected set held fixed (selection is not
 differentiated), and is pinned by finite differences in the tests.
@@ -409,3 +413,67 @@ def hils_route(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
                 order = np.lexsort((np.arange(nd), -sel))
                 ranked[(b, g, i)] = (sel[order], order)
     return dict(topk=topk, ranked=ranked)
+
+
+# --------------------------------------------------------------------------
+# landmark summary (upstream of the routed attention)
+# --------------------------------------------------------------------------
+def landmark_summary(qL, k, S: int, scale: Optional[float] = None):
+    """Landmark key and entropy bias of every complete chunk (paperglide, "The
+    HiLS-Attention Mechanism": the landmark query of a chunk scores the
+    chunk's tokens, their softmax weights the keys into the summary key and
+    the entropy of those weights is the bias; the overview calls this the
+    first-order Taylor expansion of the chunk's attention mass).
+
+    qL [B, Hkv, C, d] (one landmark query per chunk and KV head), k
+    [B, Hkv, N, d]; C <= N // S. For chunk c with tokens t = cS .. cS+S-1:
+      s_t = scale * qL_c . k_t,  p = softmax(s),
+      kL_c = sum_t p_t k_t,      e_c = -sum_t p_t log p_t.
+    Returns kL [B, Hkv, C, d] and e [B, Hkv, C] in float64."""
+    qL = f64(qL)
+    k = f64(k)
+    B, Hkv, C, d = qL.shape
+    sc = _scale(d, scale)
+    kL = np.zeros((B, Hkv, C, d))
+    e = np.zeros((B, Hkv, C))
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(C):
+                Kc = k[b, g, c * S:(c + 1) * S]
+                s = sc * (Kc @ qL[b, g, c])
+                logp = s - logsumexp(s)
+                p = np.exp(logp)
+                kL[b, g, c] = p @ Kc
+                e[b, g, c] = -(p * logp).sum()
+    return kL, e
+
+
+def landmark_backward(qL, k, dkL, de, S: int, scale: Optional[float] = None):
+    """Chain rule through landmark_summary (the pages print no backward; the
+    gradient reaches the landmark query and the chunk's keys through both
+    the summary key and the entropy). Per chunk, with s, p as above:
+      dE/dp_t = dkL_c . k_t - de_c (log p_t + 1)
+      dE/ds_t = p_t (dE/dp_t - sum_u p_u dE/dp_u)      (softmax backward)
+      dqL_c   = scale sum_t dE/ds_t k_t
+      dk_t    = scale dE/ds_t qL_c + p_t dkL_c          (through s and kL)
+    Returns dqL [B, Hkv, C, d] and dk [B, Hkv, N, d] (zero past C S)."""
+    qL = f64(qL)
+    k = f64(k)
+    dkL = f64(dkL)
+    de = f64(de)
+    B, Hkv, C, d = qL.shape
+    sc = _scale(d, scale)
+    dqL = np.zeros_like(qL)
+    dk = np.zeros_like(k)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(C):
+                Kc = k[b, g, c * S:(c + 1) * S]
+                s = sc * (Kc @ qL[b, g, c])
+                logp = s - logsumexp(s)
+                p = np.exp(logp)
+                dp = Kc @ dkL[b, g, c] - de[b, g, c] * (logp + 1.0)
+                ds = p * (dp - p @ dp)
+                dqL[b, g, c] = sc * (ds @ Kc)
+                dk[b, g, c * S:(c + 1) * S] = sc * np.outer(ds, qL[b, g, c]) + np.outer(p, dkL[b, g, c])
+    return dqL, dk

@@ -358,3 +358,99 @@ def test_decode_equals_last_prefill_row():
         of = H.hils_forward(tb, S, K, W, rows=[n - 1])
         np.testing.assert_allclose(od["o"][b], of["o"][0, :, n - 1], atol=1e-13)
         np.testing.assert_array_equal(od["topk"][b], of["topk"][0, :, n - 1])
+
+
+# ---------------------------------------------------------------- landmark summary
+def test_landmark_summary_taylor_point_and_gibbs_bound():
+    """At its own landmark query the surrogate scale*q.kL + e equals the
+    chunk's exact log-mass (scipy's logsumexp), and for any other query it
+    lies below it (Gibbs); pins kL = sum p k and e = H(p) together."""
+    from scipy.special import logsumexp as lse_ref
+    S, d, C = 8, 8, 3
+    sc = 1 / math.sqrt(d)
+    rng = np.random.default_rng(41)
+    qL = rng.standard_normal((1, 2, C, d)) * 1.5
+    k = rng.standard_normal((1, 2, C * S + 5, d))
+    kL, e = H.landmark_summary(qL, k, S)
+    for g in range(2):
+        for c in range(C):
+            Kc = k[0, g, c * S:(c + 1) * S]
+            exact = lse_ref(sc * Kc @ qL[0, g, c])
+            assert abs(sc * qL[0, g, c] @ kL[0, g, c] + e[0, g, c] - exact) < 1e-12
+            for _ in range(20):
+                qq = rng.standard_normal(d) * 2
+                assert sc * qq @ kL[0, g, c] + e[0, g, c] <= lse_ref(sc * Kc @ qq) + 1e-12
+
+
+def test_landmark_summary_uniform_chunk_and_one_hot_limit():
+    """All keys equal: the summary key is that key and the bias is ln S
+    (uniform weights). A landmark query far along one key (orthogonal keys):
+    the weights become one-hot, the summary key that key, the bias 0."""
+    S, d = 16, 16
+    rng = np.random.default_rng(42)
+    kap = rng.standard_normal(d)
+    k = np.tile(kap, (1, 1, S, 1))
+    kL, e = H.landmark_summary(rng.standard_normal((1, 1, 1, d)), k, S)
+    np.testing.assert_allclose(kL[0, 0, 0], kap, atol=1e-12)
+    assert abs(e[0, 0, 0] - math.log(S)) < 1e-12
+    eye = np.eye(S)[None, None]  # keys = unit vectors
+    j = 5
+    qL = (200.0 * eye[0, 0, j])[None, None, None]
+    kL, e = H.landmark_summary(qL, eye, S)
+    np.testing.assert_allclose(kL[0, 0, 0], eye[0, 0, j], atol=1e-10)
+    assert 0.0 <= e[0, 0, 0] < 1e-10
+
+
+def test_landmark_summary_two_token_example_structure():
+    """The pages' two-token example: scores (0.2, 0.8) give the softmax
+    weights, the weighted key and their entropy (scipy's softmax and
+    entropy); the page's printed numbers are inconsistent with each other,
+    so only the structure is checked."""
+    from scipy.special import softmax as sm
+    from scipy.stats import entropy
+    d = 4
+    sc = 1 / math.sqrt(d)
+    k = np.array([[0.2, 1.0, -1.0, 0.5], [0.8, -0.3, 2.0, 0.0]])[None, None]
+    qL = np.array([1.0 / sc, 0.0, 0.0, 0.0])[None, None, None]
+    kL, e = H.landmark_summary(qL, k, 2)
+    p = sm([0.2, 0.8])
+    np.testing.assert_allclose(kL[0, 0, 0], p[0] * k[0, 0, 0] + p[1] * k[0, 0, 1], atol=1e-14)
+    assert abs(e[0, 0, 0] - entropy(p)) < 1e-14
+    np.testing.assert_allclose(p, [0.35434369, 0.64565631], atol=1e-8)
+
+
+def test_landmark_backward_matches_autograd_and_finite_differences():
+    """dqL and dk of E = sum dkL . kL + sum de e: torch fp64 autograd of the
+    definition, and central differences of the oracle's forward."""
+    S, d, C, N = 8, 8, 3, 29
+    rng = np.random.default_rng(43)
+    qL = rng.standard_normal((1, 2, C, d))
+    k = rng.standard_normal((1, 2, N, d))
+    dkL = rng.standard_normal((1, 2, C, d))
+    de = rng.standard_normal((1, 2, C))
+    dqL, dk = H.landmark_backward(qL, k, dkL, de, S)
+    Q = torch.tensor(qL, requires_grad=True)
+    Kt = torch.tensor(k, requires_grad=True)
+    sc = 1 / math.sqrt(d)
+    Kc = Kt[:, :, :C * S].reshape(1, 2, C, S, d)
+    s = sc * torch.einsum("bgcsd,bgcd->bgcs", Kc, Q)
+    logp = torch.log_softmax(s, -1)
+    p = logp.exp()
+    kLt = torch.einsum("bgcs,bgcsd->bgcd", p, Kc)
+    et = -(p * logp).sum(-1)
+    ((kLt * torch.tensor(dkL)).sum() + (et * torch.tensor(de)).sum()).backward()
+    np.testing.assert_allclose(dqL, Q.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, Kt.grad.numpy(), atol=1e-12)
+
+    def E(qq, kk):
+        a, b = H.landmark_summary(qq, kk, S)
+        return (a * dkL).sum() + (b * de).sum()
+    h = 1e-6
+    for idx in [(0, 0, 1, 3), (0, 1, 2, 7)]:
+        qp = qL.copy(); qp[idx] += h
+        qm = qL.copy(); qm[idx] -= h
+        assert abs((E(qp, k) - E(qm, k)) / (2 * h) - dqL[idx]) < 1e-7
+    for idx in [(0, 0, 5, 2), (0, 1, 17, 0), (0, 1, 27, 4)]:
+        kp = k.copy(); kp[idx] += h
+        km = k.copy(); km[idx] -= h
+        assert abs((E(qL, kp) - E(qL, km)) / (2 * h) - dk[idx]) < 1e-7

@@ -12,7 +12,8 @@ Prints ONE JSON line: prefill tokens/s, the roofline of the dominant kernel
 the timed region) and the fp64 CPU oracle timed on a bounded sample of the
 same workload. Extra legs in the same line: "decode" (the 512K-context decode
 step of 32 sequences, microseconds per step against the HBM roofline, cold
-last-level cache) and "train" (forward + backward tokens/s).
+last-level cache), "train" (forward + backward tokens/s) and "landmark" (the
+landmark summary's forward and backward against the HBM roofline).
 """
 from __future__ import annotations
 
@@ -321,6 +322,54 @@ def bench_train(args, torch, L):
     return out
 
 
+def landmark_bytes(wl):
+    """HBM bytes the landmark summary has to move per call: the forward reads
+    the keys and landmark queries and writes kL, e; the backward reads the
+    keys, queries, dkL and de, writes dqL and reads and writes the fp32 dk it
+    adds into."""
+    bg, C, d = wl.B * wl.Hkv, wl.N // wl.S, wl.d
+    el = 2 if wl.dtype == "bf16" else 4
+    keys = bg * C * wl.S * d
+    fwd = keys * el + bg * C * d * el * 2 + bg * C * el
+    bwd = keys * el + bg * C * d * el + bg * C * (d + 1) * 4 + bg * C * d * 4 + 2 * keys * 4
+    return fwd, bwd
+
+
+def bench_landmark(args, torch, L):
+    """Landmark summary forward and backward at the 345M training shape."""
+    from workloads import WORKLOADS, make_landmark_inputs
+    wl = WORKLOADS["train_345m"]
+    t = make_landmark_inputs(wl, device="cuda")
+    dk = torch.zeros(t["k"].shape, dtype=torch.float32, device="cuda")
+
+    def step():
+        L.hils_landmark_fwd(t["qL"], t["k"], wl.S)
+        L.hils_landmark_bwd(t["qL"], t["k"], t["dkL"], t["de"], wl.S, dk=dk)
+
+    for _ in range(max(2, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    rings = {sid: event_ring(n, torch) for sid in (L.STEP_LANDMARK_FWD, L.STEP_LANDMARK_BWD)}
+    for sid, r in rings.items():
+        L.hils_set_timing_events(sid, *r)
+    timed_steps(step, n, 0, torch)
+    for sid in rings:
+        L.hils_set_timing_events(sid)
+    ms = {sid: avg_ms(*r) for sid, r in rings.items()}
+    fb, bb = landmark_bytes(wl)
+    fg = fb / (ms[L.STEP_LANDMARK_FWD] * 1e-3) / 1e9
+    bgs = bb / (ms[L.STEP_LANDMARK_BWD] * 1e-3) / 1e9
+    out = {"workload": wl.name + " landmark summary", "fwd_us": ms[L.STEP_LANDMARK_FWD] * 1e3,
+           "bwd_us": ms[L.STEP_LANDMARK_BWD] * 1e3,
+           "hbm": {"fwd_gbs": fg, "bwd_gbs": bgs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac_fwd": fg / HBM_PEAK_GBS, "frac_bwd": bgs / HBM_PEAK_GBS,
+                   "bytes_fwd": fb, "bytes_bwd": bb}}
+    del t, dk
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,7 +382,7 @@ def main():
     ap.add_argument("--decode-workload", default="decode_7b_512k")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-train", action="store_true", help="skip the training (fwd+bwd) leg")
-    ap.add_argument("--legs", default="prefill,decode,train",
+    ap.add_argument("--legs", default="prefill,decode,train,landmark",
                     help="comma list of legs to run (prefill is always reported)")
     ap.add_argument("--profile-sample", action="store_true",
                     help="run the short fixed sample used for rocprofv3 counter passes and exit")
@@ -356,6 +405,8 @@ def main():
         res["decode"] = bench_decode(args, torch, L)
     if not args.no_train and "train" in legs:
         res["train"] = bench_train(args, torch, L)
+    if "landmark" in legs:
+        res["landmark"] = bench_landmark(args, torch, L)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, args.cpu_budget)
     res["vs_baseline"] = None
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),

@@ -157,6 +157,41 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
                         int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Landmark summary (paper: "The HiLS-Attention Mechanism", the landmark
+ * worked example; the overview's first-order Taylor expansion of a chunk's
+ * attention mass around its landmark query). For every complete chunk c of
+ * every (b, KV head), with the chunk's S tokens t:
+ *   s_t = scale * qL_c . k_t,  p = softmax(s),
+ *   kL_c = sum_t p_t k_t,      e_c = -sum_t p_t log p_t   (fp32 arithmetic).
+ * qL [B, Hkv, C, d] holds one landmark query per chunk and KV head; k
+ * [B, Hkv, Nk, d]; C = Nk / S. Outputs kL [B, Hkv, C, d] and e [B, Hkv, C]
+ * in the problem dtype (rounded to nearest even from fp32: the layout and
+ * dtype hils_route, hils_attn_fwd and hils_decode take), and, when non-NULL,
+ * the same values in fp32 (kL32, e32). Only dtype, B, Hkv, d, Nk, S and scale
+ * of the problem are read (Hq, Nq, K, W, D, r are ignored); no workspace.
+ * Errors: HILS_ERR_INVALID (null qL, k, kL or e; B, Hkv, d or Nk <= 0; bad
+ * scale), HILS_ERR_UNSUPPORTED (d not in {64, 128}, S != 64).
+ */
+hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void* k, void* kL,
+                              void* e, float* kL32, float* e32, void* stream);
+
+/*
+ * Backward of hils_landmark_fwd (the chain rule; the pages print none): from
+ * dkL [B, Hkv, C, d] and de [B, Hkv, C] (fp32, as hils_attn_bwd writes them),
+ * with s, p of the forward recomputed in fp32 and sbar = sum_t p_t s_t:
+ *   ds_t  = p_t (dkL_c . k_t - dkL_c . kL_c - de_c (s_t - sbar)),
+ *   dqL_c = scale sum_t ds_t k_t                       (written, fp32),
+ *   dk_t += scale ds_t qL_c + p_t dkL_c                (ADDED into dk, fp32
+ *           [B, Hkv, Nk, d], e.g. after hils_attn_bwd wrote it; tokens past
+ *           C * S are not touched).
+ * Same problem fields and errors as hils_landmark_fwd (null dkL, de, dqL or
+ * dk is HILS_ERR_INVALID).
+ */
+hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void* k,
+                              const float* dkL, const float* de, float* dqL, float* dk,
+                              void* stream);
+
+/*
  * Measurement hook (not part of the method): ids of the launch steps whose
  * device time can be recorded with caller-owned events.
  */
@@ -166,7 +201,9 @@ typedef enum {
   HILS_STEP_ATTN_FWD = 2,   /* window + selected chunks + fusion (prefill) */
   HILS_STEP_DECODE = 3,     /* the whole decode step after Q-Cal */
   HILS_STEP_BWD = 4,        /* the whole backward */
-  HILS_STEP_COUNT = 5
+  HILS_STEP_LANDMARK_FWD = 5, /* landmark summary */
+  HILS_STEP_LANDMARK_BWD = 6, /* its backward */
+  HILS_STEP_COUNT = 7
 } hils_step;
 
 /*

@@ -24,8 +24,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
           3: "workspace too small or misaligned", 4: "HIP launch failure"}
 
 EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
-           "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_set_timing_events")
+           "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_landmark_fwd",
+           "hils_landmark_bwd", "hils_set_timing_events")
 STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
+STEP_LANDMARK_FWD, STEP_LANDMARK_BWD = 5, 6
 
 
 class HilsError(RuntimeError):
@@ -68,6 +70,10 @@ def lib():
         L.hils_attn_bwd.argtypes = [P] + [vp] * 21 + [sz, vp]
         L.hils_decode.restype = ctypes.c_int
         L.hils_decode.argtypes = [P] + [vp] * 13 + [sz, vp]
+        L.hils_landmark_fwd.restype = ctypes.c_int
+        L.hils_landmark_fwd.argtypes = [P] + [vp] * 7
+        L.hils_landmark_bwd.restype = ctypes.c_int
+        L.hils_landmark_bwd.argtypes = [P] + [vp] * 7
         L.hils_set_timing_events.restype = ctypes.c_int
         L.hils_set_timing_events.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
         _lib = L
@@ -254,3 +260,48 @@ def hils_set_timing_events(step: int, starts=None, stops=None):
     b = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in stops])
     _event_keepalive[step] = (a, b, starts, stops)
     _check("hils_set_timing_events", lib().hils_set_timing_events(step, a, b, n))
+
+
+def _landmark_problem(qL, k, S, scale) -> Problem:
+    B, Hkv, C, d = qL.shape
+    if k.shape[0] != B or k.shape[1] != Hkv or k.shape[3] != d or k.dtype != qL.dtype:
+        raise ValueError("qL [B, Hkv, C, d] and k [B, Hkv, N, d] must agree")
+    if C != k.shape[2] // S:
+        raise ValueError("qL needs one landmark query per complete chunk (C = N // S)")
+    return Problem(_dtype_code(qL), B, Hkv, Hkv, d, k.shape[2], k.shape[2], S, 1, 1, 0, 0, 0,
+                   float(scale))
+
+
+def hils_landmark_fwd(qL, k, S: int, scale=0.0, want_f32=False):
+    """Landmark key kL [B, Hkv, C, d] and entropy bias e [B, Hkv, C] of every
+    complete chunk from its landmark query qL (dtype of qL); with want_f32 also
+    their fp32 values: returns (kL, e) or (kL, e, kL32, e32)."""
+    _contig(qL, k)
+    p = _landmark_problem(qL, k, S, scale)
+    dev = qL.device
+    kL = torch.empty(qL.shape, dtype=qL.dtype, device=dev)
+    e = torch.empty(qL.shape[:3], dtype=qL.dtype, device=dev)
+    kL32 = torch.empty(qL.shape, dtype=torch.float32, device=dev) if want_f32 else None
+    e32 = torch.empty(qL.shape[:3], dtype=torch.float32, device=dev) if want_f32 else None
+    _check("hils_landmark_fwd", lib().hils_landmark_fwd(ctypes.byref(p), _ptr(qL), _ptr(k), _ptr(kL),
+                                                        _ptr(e), _ptr(kL32), _ptr(e32), _stream(dev)))
+    return (kL, e, kL32, e32) if want_f32 else (kL, e)
+
+
+def hils_landmark_bwd(qL, k, dkL, de, S: int, dk=None, scale=0.0):
+    """Gradients of the landmark summary: returns (dqL, dk) with dqL fp32
+    [B, Hkv, C, d]; the keys' part is ADDED into dk (fp32 [B, Hkv, N, d],
+    zero-initialised when not given)."""
+    _contig(qL, k, dkL, de, dk)
+    p = _landmark_problem(qL, k, S, scale)
+    dev = qL.device
+    if dkL.dtype != torch.float32 or de.dtype != torch.float32:
+        raise TypeError("dkL and de are fp32")
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
+    elif dk.dtype != torch.float32 or dk.shape != k.shape:
+        raise ValueError("dk must be fp32 with the shape of k")
+    dqL = torch.empty(qL.shape, dtype=torch.float32, device=dev)
+    _check("hils_landmark_bwd", lib().hils_landmark_bwd(ctypes.byref(p), _ptr(qL), _ptr(k), _ptr(dkL),
+                                                        _ptr(de), _ptr(dqL), _ptr(dk), _stream(dev)))
+    return dqL, dk

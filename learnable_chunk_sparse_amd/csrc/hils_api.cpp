@@ -63,6 +63,32 @@ hils_status check_problem(const hils_problem* p, int op) {
   return HILS_OK;
 }
 
+// Checks of the landmark summary ops, which read only dtype, B, Hkv, d, Nk,
+// S and scale.
+hils_status check_landmark(const hils_problem* p) {
+  if (p == nullptr) return HILS_ERR_INVALID;
+  if (p->dtype != HILS_FP32 && p->dtype != HILS_BF16) return HILS_ERR_UNSUPPORTED;
+  if (p->B <= 0 || p->Hkv <= 0 || p->d <= 0 || p->Nk <= 0 || p->S <= 0) return HILS_ERR_INVALID;
+  if (!(p->scale >= 0.f) || std::isinf(p->scale)) return HILS_ERR_INVALID;
+  if (p->d != 64 && p->d != 128) return HILS_ERR_UNSUPPORTED;
+  if (p->S != 64) return HILS_ERR_UNSUPPORTED;
+  if ((long long)p->Nk > (1LL << 26)) return HILS_ERR_UNSUPPORTED;
+  return HILS_OK;
+}
+
+Dims landmark_dims(const hils_problem* p) {
+  Dims d{};
+  d.dtype = p->dtype;
+  d.B = p->B;
+  d.Hkv = p->Hkv;
+  d.d = p->d;
+  d.N = p->Nk;
+  d.S = p->S;
+  d.C = p->Nk / p->S;
+  d.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+  return d;
+}
+
 Dims dims_of(const hils_problem* p) {
   Dims d;
   d.dtype = p->dtype;
@@ -292,6 +318,31 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
   return hip_status(timed(HILS_STEP_DECODE, st, [&] {
     return hils::launch_decode(d, qs, qf32, q, k_cache, v_cache, seq_len, kL, e, o, lse, topk_idx,
                                ws, st);
+  }));
+}
+
+hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void* k, void* kL,
+                              void* e, float* kL32, float* e32, void* stream) {
+  hils_status s = check_landmark(p);
+  if (s != HILS_OK) return s;
+  if (!qL || !k || !kL || !e) return HILS_ERR_INVALID;
+  const Dims d = landmark_dims(p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed(HILS_STEP_LANDMARK_FWD, st, [&] {
+    return hils::launch_landmark_fwd(d, qL, k, kL, e, kL32, e32, st);
+  }));
+}
+
+hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void* k,
+                              const float* dkL, const float* de, float* dqL, float* dk,
+                              void* stream) {
+  hils_status s = check_landmark(p);
+  if (s != HILS_OK) return s;
+  if (!qL || !k || !dkL || !de || !dqL || !dk) return HILS_ERR_INVALID;
+  const Dims d = landmark_dims(p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed(HILS_STEP_LANDMARK_BWD, st, [&] {
+    return hils::launch_landmark_bwd(d, qL, k, dkL, de, dqL, dk, st);
   }));
 }
 

@@ -85,4 +85,11 @@ hipError_t launch_bwd(const Dims& p, const void* q, const void* k, const void* v
                       float* dq, float* dk, float* dv, float* dkL, float* de, float* dW_down,
                       float* dW_up, float* dh, void* ws, hipStream_t st);
 
+// Landmark summary (landmark.hip): kL, e of every complete chunk from its
+// landmark query, and the backward into the landmark queries and keys.
+hipError_t launch_landmark_fwd(const Dims& p, const void* qL, const void* k, void* kL, void* e,
+                               float* kL32, float* e32, hipStream_t st);
+hipError_t launch_landmark_bwd(const Dims& p, const void* qL, const void* k, const float* dkL,
+                               const float* de, float* dqL, float* dk, hipStream_t st);
+
 }  // namespace hils

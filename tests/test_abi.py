@@ -85,3 +85,20 @@ def test_calls_reject_before_launch():
                          fake, null, fake, 1 << 40, null)
     assert st == 1
     assert lib.hils_status_string(3) == b"workspace too small or misaligned"
+
+
+def test_landmark_calls_reject_before_launch():
+    """The landmark entry points validate their own fields (Hq, K, W, r are
+    not read) and return before any launch."""
+    lib = L.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    ok = prob(Hq=3, K=0, W=0, r=5, D=0)  # fields the landmark ops ignore
+    assert lib.hils_landmark_fwd(ctypes.byref(ok), null, fake, fake, fake, null, null, null) == 1
+    assert lib.hils_landmark_fwd(ctypes.byref(ok), fake, fake, fake, null, null, null, null) == 1
+    assert lib.hils_landmark_bwd(ctypes.byref(ok), fake, fake, fake, fake, fake, null, null) == 1
+    for kw, code in [(dict(d=96), 2), (dict(S=32), 2), (dict(B=0), 1), (dict(Nk=0), 1),
+                     (dict(scale=float("inf")), 1), (dict(dtype=5), 2)]:
+        p = prob(**kw)
+        assert lib.hils_landmark_fwd(ctypes.byref(p), fake, fake, fake, fake, null, null, null) == code, kw
+        assert lib.hils_landmark_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, null) == code, kw

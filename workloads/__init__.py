@@ -34,7 +34,7 @@ import torch
 M32 = 0xFFFFFFFF
 
 # tensor ids used in the slab keys
-TID = dict(q=0, k=1, v=2, kL=3, e=4, h=5, W_down=6, W_up=7, dO=8, needle=9)
+TID = dict(q=0, k=1, v=2, kL=3, e=4, h=5, W_down=6, W_up=7, dO=8, needle=9, qL=10, dkL=11, de=12)
 
 
 # --------------------------------------------------------------------------
@@ -274,6 +274,30 @@ def make_inputs(wl: Workload, device="cpu", with_grad_inputs: Optional[bool] = N
     plant_needles(wl, out)
     if dec:
         out["seq_len"] = torch.tensor(seq_lens(wl), dtype=torch.int32, device=device)
+    return out
+
+
+def make_landmark_inputs(wl: Workload, device="cpu", keys: bool = True) -> dict:
+    """Inputs of the landmark summary for a workload: the keys k
+    [B,Hkv,N,d] (the same slabs as make_inputs, without needles; omitted when
+    keys=False), one landmark query per complete chunk and KV head qL
+    [B,Hkv,C,d] (normal, workload dtype), and upstream gradients dkL
+    [B,Hkv,C,d] and de [B,Hkv,C] (normal, fp32)."""
+    B, Hkv, d, N, C = wl.B, wl.Hkv, wl.d, wl.N, wl.C
+    qL = _alloc((B, Hkv, C, d), wl, device)
+    dkL = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=device)
+    de = torch.empty((B, Hkv, C), dtype=torch.float32, device=device)
+    k = _alloc((B, Hkv, N, d), wl, device) if keys else None
+    for b in range(B):
+        for g in range(Hkv):
+            qL[b, g] = gen_slab(wl, "qL", b, g, (C, d), device)
+            dkL[b, g] = normal_at(slab_key(wl.seed, "dkL", b, g), _counters(C * d, device)).reshape(C, d)
+            de[b, g] = normal_at(slab_key(wl.seed, "de", b, g), _counters(C, device))
+            if keys:
+                k[b, g] = gen_slab(wl, "k", b, g, (N, d), device)
+    out = dict(qL=qL, dkL=dkL, de=de)
+    if keys:
+        out["k"] = k
     return out
 
 

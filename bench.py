@@ -13,7 +13,9 @@ the timed region) and the fp64 CPU oracle timed on a bounded sample of the
 same workload. Extra legs in the same line: "decode" (the 512K-context decode
 step of 32 sequences, microseconds per step against the HBM roofline, cold
 last-level cache), "train" (forward + backward tokens/s) and "landmark" (the
-landmark summary's forward and backward against the HBM roofline).
+landmark summary's forward and backward against the HBM roofline) and "packing"
+(chunk-id overlap of adjacent queries and the two forward strategies on
+independent and on position-correlated queries).
 """
 from __future__ import annotations
 
@@ -370,6 +372,67 @@ def bench_landmark(args, torch, L):
     return out
 
 
+def selection_locality(idx, wl, torch):
+    """Chunk-id overlap of the selections (the paper's Fig. 7 measures): mean
+    |T_i & T_i+1| / K of adjacent rows, and the mean union of the selections of
+    M adjacent positions per KV head with the fraction of the visible distant
+    chunks it is, for M = 16 and for the 128-position tile of the packed-union
+    kernel."""
+    a, b = idx[..., :-1, :], idx[..., 1:, :]
+    full = (a >= 0).all(-1) & (b >= 0).all(-1)
+    inter = torch.zeros(full.shape, dtype=torch.float32, device=idx.device)
+    for j in range(idx.shape[-1]):
+        inter += (a == b[..., j:j + 1]).sum(-1).float()
+    out = {"adjacent_overlap": float(inter[full].mean()) / wl.K}
+    B, Hkv, N, K = idx.shape
+    for M in (16, 128 // wl.G):
+        T = N // M
+        x = idx[:, :, :T * M].reshape(B, Hkv, T, M * K)
+        ok = (x >= 0).all(-1)
+        xs, _ = torch.sort(x, -1)
+        uniq = 1 + (xs[..., 1:] != xs[..., :-1]).sum(-1)
+        last = torch.arange(T, device=idx.device) * M + M - 1
+        nd = torch.clamp((last - wl.W + 1) // wl.S, min=1).to(torch.float32)
+        out[f"union_m{M}"] = float(uniq[ok].float().mean())
+        out[f"loaded_frac_m{M}"] = float((uniq.float() / nd)[ok].mean())
+    return out
+
+
+def bench_packing(args, torch, L):
+    """The two forward strategies (packed union, compacted) on independent and
+    on position-correlated queries (prefill_345m and prefill_345m_local)."""
+    from workloads import WORKLOADS, make_inputs
+    res = {}
+    for name in ("prefill_345m", "prefill_345m_local"):
+        wl = WORKLOADS[name]
+        t = make_inputs(wl, device="cuda")
+        fb = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+
+        def step():
+            return L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
+                                   h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=fb)
+
+        r = selection_locality(step()[2], wl, torch)
+        for sname, sid in (("union", L.FWD_UNION), ("compact", L.FWD_COMPACT)):
+            L.hils_set_fwd_strategy(sid)
+            try:
+                for _ in range(max(2, args.warmup)):
+                    step()
+                torch.cuda.synchronize()
+                n = max(5, args.steps)
+                ring = event_ring(n, torch)
+                L.hils_set_timing_events(L.STEP_ATTN_FWD, *ring)
+                timed_steps(step, n, 0, torch)
+                L.hils_set_timing_events(L.STEP_ATTN_FWD)
+            finally:
+                L.hils_set_fwd_strategy(L.FWD_AUTO)
+            r[f"attn_ms_{sname}"] = avg_ms(*ring)
+        res[name] = r
+        del t, fb
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,7 +445,7 @@ def main():
     ap.add_argument("--decode-workload", default="decode_7b_512k")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-train", action="store_true", help="skip the training (fwd+bwd) leg")
-    ap.add_argument("--legs", default="prefill,decode,train,landmark",
+    ap.add_argument("--legs", default="prefill,decode,train,landmark,packing",
                     help="comma list of legs to run (prefill is always reported)")
     ap.add_argument("--profile-sample", action="store_true",
                     help="run the short fixed sample used for rocprofv3 counter passes and exit")
@@ -407,6 +470,8 @@ def main():
         res["train"] = bench_train(args, torch, L)
     if "landmark" in legs:
         res["landmark"] = bench_landmark(args, torch, L)
+    if "packing" in legs:
+        res["packing"] = bench_packing(args, torch, L)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, args.cpu_budget)
     res["vs_baseline"] = None
     line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),

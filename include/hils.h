@@ -192,6 +192,25 @@ hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void*
                               void* stream);
 
 /*
+ * Forward strategy (a tuning switch, not part of the method; process-wide,
+ * like the timing hook). The paper packs adjacent queries against the union of
+ * their selected chunks (its Fig. 4 kernel design); both strategies here give
+ * the same per-query result:
+ *   HILS_FWD_AUTO (0)    chosen by shape (default): packed union when a
+ *                        128-row tile selects at least 4 slots per candidate
+ *                        chunk, compacted otherwise;
+ *   HILS_FWD_UNION (1)   packed union: a tile's rows stream the union of their
+ *                        selected chunks through LDS once, rows that did not
+ *                        select a chunk add it with weight zero;
+ *   HILS_FWD_COMPACT (2) compacted: each chunk's selecting rows are packed into
+ *                        dense 16-row blocks and only those are computed.
+ * Applies to later hils_attn_fwd calls (and their LDS checks); returns
+ * HILS_ERR_INVALID for any other value.
+ */
+typedef enum { HILS_FWD_AUTO = 0, HILS_FWD_UNION = 1, HILS_FWD_COMPACT = 2 } hils_fwd_strategy;
+hils_status hils_set_fwd_strategy(int32_t strategy);
+
+/*
  * Measurement hook (not part of the method): ids of the launch steps whose
  * device time can be recorded with caller-owned events.
  */

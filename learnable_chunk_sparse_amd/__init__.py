@@ -25,7 +25,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
 
 EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
            "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_landmark_fwd",
-           "hils_landmark_bwd", "hils_set_timing_events")
+           "hils_landmark_bwd", "hils_set_fwd_strategy", "hils_set_timing_events")
+FWD_AUTO, FWD_UNION, FWD_COMPACT = 0, 1, 2
 STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
 STEP_LANDMARK_FWD, STEP_LANDMARK_BWD = 5, 6
 
@@ -74,6 +75,8 @@ def lib():
         L.hils_landmark_fwd.argtypes = [P] + [vp] * 7
         L.hils_landmark_bwd.restype = ctypes.c_int
         L.hils_landmark_bwd.argtypes = [P] + [vp] * 7
+        L.hils_set_fwd_strategy.restype = ctypes.c_int
+        L.hils_set_fwd_strategy.argtypes = [i32]
         L.hils_set_timing_events.restype = ctypes.c_int
         L.hils_set_timing_events.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
         _lib = L
@@ -305,3 +308,10 @@ def hils_landmark_bwd(qL, k, dkL, de, S: int, dk=None, scale=0.0):
     _check("hils_landmark_bwd", lib().hils_landmark_bwd(ctypes.byref(p), _ptr(qL), _ptr(k), _ptr(dkL),
                                                         _ptr(de), _ptr(dqL), _ptr(dk), _stream(dev)))
     return dqL, dk
+
+
+def hils_set_fwd_strategy(strategy: int):
+    """Force the forward strategy for later hils_attn_fwd calls: FWD_AUTO (by
+    shape), FWD_UNION (packed union of a tile's chunks) or FWD_COMPACT (each
+    chunk's selecting rows packed into dense blocks). Process-wide."""
+    _check("hils_set_fwd_strategy", lib().hils_set_fwd_strategy(int(strategy)))

@@ -181,6 +181,12 @@ const char* hils_status_string(hils_status s) {
 
 int32_t hils_version(void) { return 100; }
 
+hils_status hils_set_fwd_strategy(int32_t strategy) {
+  if (strategy < HILS_FWD_AUTO || strategy > HILS_FWD_COMPACT) return HILS_ERR_INVALID;
+  hils::set_fwd_strategy(strategy);
+  return HILS_OK;
+}
+
 hils_status hils_set_timing_events(int32_t step, void* const* start, void* const* stop, int32_t n) {
   if (step < 0 || step >= HILS_STEP_COUNT || n < 0) return HILS_ERR_INVALID;
   EventRing& r = g_rings[step];

@@ -39,6 +39,8 @@ hipError_t launch_fwd_sparse(const Dims& p, const void* q, const void* k, const 
                              const int32_t* idx, const float* sc, const float* sl, void* o,
                              float* lse, hipStream_t st);
 size_t attn_fwd_vt_bytes(const Dims& p);
+// forward strategy: 0 by shape, 1 shared block (packed union), 2 bucketed
+void set_fwd_strategy(int s);
 
 // Decode.
 size_t decode_workspace(const Dims& p);

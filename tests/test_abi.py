@@ -102,3 +102,19 @@ def test_landmark_calls_reject_before_launch():
         p = prob(**kw)
         assert lib.hils_landmark_fwd(ctypes.byref(p), fake, fake, fake, fake, null, null, null) == code, kw
         assert lib.hils_landmark_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, null) == code, kw
+
+
+def test_fwd_strategy_switch():
+    lib = L.lib()
+    try:
+        for s in (L.FWD_UNION, L.FWD_COMPACT, L.FWD_AUTO):
+            assert lib.hils_set_fwd_strategy(s) == 0
+        assert lib.hils_set_fwd_strategy(3) == 1 and lib.hils_set_fwd_strategy(-1) == 1
+        # the forced strategy decides the LDS check: the 1.4B shape fits either way
+        big = prob(B=1, Hq=32, Hkv=8, d=128, Nq=131072, Nk=131072, W=1024, D=2048)
+        for s in (L.FWD_UNION, L.FWD_COMPACT):
+            lib.hils_set_fwd_strategy(s)
+            st, n = ws(big, L.OP_FWD)
+            assert st in (0, 2), (s, st)
+    finally:
+        lib.hils_set_fwd_strategy(L.FWD_AUTO)

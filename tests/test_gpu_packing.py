@@ -1,0 +1,88 @@
+"""Locality-structured queries and the two forward strategies.
+
+Adjacent queries of the paper's trained models share most of their selected
+chunks (its Fig. 7), which is what makes packing adjacent queries against the
+union of their chunks pay (its Fig. 4 kernel design). The workload
+prefill_345m_local reproduces that locality with queries correlated along
+positions. Both forward strategies, forced in turn, must give the oracle's
+per-query result on it (the paper's packing-invariance claim), and their
+outputs must agree with each other."""
+import numpy as np
+import pytest
+import torch
+
+from workloads import WORKLOADS, Workload, make_inputs
+from tests.hils_testutil import fwd_parity, say, to_dev
+from tests.test_gpu_fwd import group_parity, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def L():
+    import learnable_chunk_sparse_amd as lib
+    return lib
+
+
+def run_fwd(wl, td, strategy):
+    lib = L()
+    lib.hils_set_fwd_strategy(strategy)
+    try:
+        out = lib.hils_attn_fwd(td["q"], td["k"], td["v"], td["kL"], td["e"], wl.S, wl.K, wl.W,
+                                h=td.get("h"), W_down=td.get("W_down"), W_up=td.get("W_up"))
+        torch.cuda.synchronize()
+    finally:
+        lib.hils_set_fwd_strategy(lib.FWD_AUTO)
+    return out
+
+
+LOCAL = [
+    # name, dtype, B, Hq, Hkv, d, N, K, W, D, r
+    ("local_mha_d64_qcal", "bf16", 1, 2, 2, 64, 2048, 8, 256, 64, 32),
+    ("local_gqa4_d128", "bf16", 1, 8, 2, 128, 2300, 4, 256, 0, 0),
+    ("local_fp32_gqa2_d64", "fp32", 1, 4, 2, 64, 1500, 6, 128, 64, 16),
+]
+
+
+def adjacent_overlap(idx):
+    """Mean |T_i & T_{i+1}| / K over adjacent rows that both hold K chunks."""
+    a, b = idx[..., :-1, :], idx[..., 1:, :]
+    full = (a >= 0).all(-1) & (b >= 0).all(-1)
+    inter = (a[..., :, None] == b[..., None, :]).sum((-1, -2)).float()
+    return float(inter[full].mean()) / idx.shape[-1]
+
+
+@pytest.mark.parametrize("case", LOCAL, ids=[c[0] for c in LOCAL])
+def test_local_queries_both_strategies_all_rows(case):
+    name, dt, B, Hq, Hkv, d, N, K, W, D, r = case
+    wl = Workload(name, seed=21, dtype=dt, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N, S=64, K=K, W=W, D=D,
+                  r=r, e_range=2.0, q_corr=0.97)
+    say(f"case {name}")
+    t = make_inputs(wl)
+    td = to_dev(t)
+    lib = L()
+    outs = {}
+    for st in (lib.FWD_UNION, lib.FWD_COMPACT):
+        outs[st] = run_fwd(wl, td, st)
+        fwd_parity(t, outs[st], wl.S, wl.K, wl.W, dt, label=f"{name} strategy {st}")
+    (ou, lu, iu), (oc, lc, ic) = outs[lib.FWD_UNION], outs[lib.FWD_COMPACT]
+    assert torch.equal(iu, ic)  # same routing
+    tol = 2e-2 if dt == "bf16" else 1e-5
+    assert float((ou.float() - oc.float()).abs().max()) <= tol
+    assert float((lu - lc).abs().max()) <= (2e-3 if dt == "bf16" else 1e-5)
+    ov = adjacent_overlap(iu.cpu())
+    say(f"  adjacent top-K overlap {ov:.3f}")
+    assert ov > 0.8
+
+
+def test_local_345m_full_size_sampled_both_strategies():
+    wl = WORKLOADS["prefill_345m_local"]
+    say("case prefill_345m_local full size")
+    t = make_inputs(wl, device="cuda")
+    lib = L()
+    rows = sample_rows(wl, 120)
+    for st in (lib.FWD_UNION, lib.FWD_COMPACT):
+        out = tuple(x.cpu() for x in run_fwd(wl, t, st))
+        group_parity(wl, t, out, [(0, 0), (2, 9)], rows, f"local strategy {st}")
+    ov = adjacent_overlap(out[2])
+    say(f"  adjacent top-K overlap {ov:.3f}")
+    assert 0.85 < ov < 0.99

@@ -131,6 +131,7 @@ class Workload:
     needle: str = "none"  # "none" | "chunk7" | "segments" | "decode_random"
     seq_len: Optional[Sequence[int]] = None  # decode: per-sequence lengths (default N)
     e_shift: float = 0.0  # added to every entropy bias (chunk-path-dominant variants)
+    q_corr: float = 0.0  # AR(1) correlation of consecutive query positions (0: independent)
     notes: str = ""
 
     @property
@@ -168,6 +169,12 @@ WORKLOADS: Dict[str, Workload] = {
     "train_345m": Workload("train_345m", seed=4, dtype="bf16", B=8, Hq=16, Hkv=16, d=64,
                            N=8192, S=64, K=16, W=512, D=1024, r=32, e_range=2.0,
                            mode="train"),
+    # the 345M prefill with queries correlated along positions (AR(1), 0.97): adjacent
+    # queries share ~92 % of their top-16, the locality the paper measures on trained
+    # models (Fig. 7) and that independent queries lack
+    "prefill_345m_local": Workload("prefill_345m_local", seed=1, dtype="bf16", B=4, Hq=16,
+                                   Hkv=16, d=64, N=8192, S=64, K=16, W=512, D=1024, r=32,
+                                   e_range=2.0, q_corr=0.97),
 }
 
 
@@ -203,6 +210,30 @@ def gen_slab(wl: Workload, tensor: str, b: int, head: int, shape, device="cpu",
     else:
         x = normal_at(key, ctr)
     return _round(x.reshape(shape), wl)
+
+
+def correlate_positions(z: torch.Tensor, rho: float) -> torch.Tensor:
+    """AR(1) filter along the position axis (dim -2) in fp32, unit variance
+    kept: x_0 = z_0, x_i = rho x_{i-1} + sqrt(1 - rho^2) z_i. Plain fp32
+    multiplies and adds in a fixed order, so CPU and GPU agree bit for bit."""
+    a = torch.tensor(math.sqrt(1.0 - rho * rho), dtype=torch.float32, device=z.device)
+    r = torch.tensor(rho, dtype=torch.float32, device=z.device)
+    x = torch.empty_like(z)
+    x[..., 0, :] = z[..., 0, :]
+    for i in range(1, z.shape[-2]):
+        x[..., i, :] = torch.add(torch.mul(x[..., i - 1, :], r), torch.mul(z[..., i, :], a))
+    return x
+
+
+def correlated_queries(wl: Workload, slabs, device="cpu") -> torch.Tensor:
+    """Query slabs [(b, h), ...] -> [len, N, d] of a workload with q_corr > 0:
+    each slab's normal draw filtered along positions (elementwise identical
+    whether slabs are filtered together or alone), then rounded."""
+    N, d = wl.N, wl.d
+    z = torch.empty((len(slabs), N, d), dtype=torch.float32, device=device)
+    for j, (b, h) in enumerate(slabs):
+        z[j] = normal_at(slab_key(wl.seed, "q", b, h), _counters(N * d, device)).reshape(N, d)
+    return _round(correlate_positions(z, wl.q_corr), wl)
 
 
 def _alloc(shape, wl, device):
@@ -246,9 +277,13 @@ def make_inputs(wl: Workload, device="cpu", with_grad_inputs: Optional[bool] = N
     v = _alloc((B, Hkv, N, d), wl, device)
     kL = _alloc((B, Hkv, C, d), wl, device)
     e = _alloc((B, Hkv, C), wl, device)
+    if wl.q_corr > 0 and not dec:
+        q.copy_(correlated_queries(wl, [(b, h) for b in range(B) for h in range(Hq)],
+                                   device).reshape(B, Hq, N, d))
     for b in range(B):
         for h in range(Hq):
-            q[b, h] = gen_slab(wl, "q", b, h, q.shape[2:], device)
+            if not (wl.q_corr > 0 and not dec):
+                q[b, h] = gen_slab(wl, "q", b, h, q.shape[2:], device)
         for g in range(Hkv):
             k[b, g] = gen_slab(wl, "k", b, g, (N, d), device)
             v[b, g] = gen_slab(wl, "v", b, g, (N, d), device)
@@ -363,8 +398,11 @@ def make_group_inputs(wl: Workload, b: int, g: int, h_rows: Optional[Sequence[in
     dec = wl.mode == "decode"
     n = N if kv_len is None else kv_len
     out = {}
-    qs = [gen_slab(wl, "q", b, g * G + hh, (d,) if dec else (N, d)) for hh in range(G)]
-    out["q"] = torch.stack(qs)[None]
+    if wl.q_corr > 0 and not dec:
+        out["q"] = correlated_queries(wl, [(b, g * G + hh) for hh in range(G)])[None]
+    else:
+        qs = [gen_slab(wl, "q", b, g * G + hh, (d,) if dec else (N, d)) for hh in range(G)]
+        out["q"] = torch.stack(qs)[None]
     if kv_rows is None:
         out["k"] = gen_slab(wl, "k", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]
         out["v"] = gen_slab(wl, "v", b, g, (n, d), rows=torch.arange(n), row_len=d)[None, None]

@@ -12,7 +12,7 @@ Prints ONE JSON line: prefill tokens/s, the roofline of the dominant kernel
 the timed region) and the fp64 CPU oracle timed on a bounded sample of the
 same workload. Extra legs in the same line: "decode" (the 512K-context decode
 step of 32 sequences, microseconds per step against the HBM roofline, cold
-last-level cache), "train" (forward + backward tokens/s) and "landmark" (the
+last-level cache; also replayed from a HIP graph and over a paged cache), "train" (forward + backward tokens/s) and "landmark" (the
 landmark summary's forward and backward against the HBM roofline) and "packing"
 (chunk-id overlap of adjacent queries and the two forward strategies on
 independent and on position-correlated queries).
@@ -272,6 +272,63 @@ def bench_decode(args, torch, L):
     out = {"workload": wl.name, "us_per_step": med * 1e3, "median_of": n, "cold_cache": True,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+
+    def graph_median(fn):
+        """Median µs of replays of fn captured in a HIP graph (cold cache)."""
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        ev = event_ring(n, torch)
+        for j in range(n):
+            torch.sum(flush, dim=0, out=sink)
+            ev[0][j].record()
+            g.replay()
+            ev[1][j].record()
+        torch.cuda.synchronize()
+        tt = sorted(a.elapsed_time(b) for a, b in zip(*ev))
+        del g
+        return tt[len(tt) // 2] * 1e3
+
+    out["graph_us_per_step"] = graph_median(step)
+    if not args.no_paged:
+        # the same caches as pages of one chunk each, in a shuffled order
+        B, Hkv, N, d = t["k"].shape
+        maxp = N // wl.S
+        perm = torch.randperm(B * maxp, generator=torch.Generator().manual_seed(3)).reshape(B, maxp)
+        perm = perm.to("cuda")
+        pages = {}
+        for name in ("k", "v"):
+            pg = torch.empty((B * maxp, Hkv, wl.S, d), dtype=t[name].dtype, device="cuda")
+            for b in range(B):
+                pg[perm[b]] = t[name][b].reshape(Hkv, maxp, wl.S, d).permute(1, 0, 2, 3)
+            pages[name] = pg
+            del t[name]
+        C = t["kL"].shape[2]
+        kLp = torch.zeros((B * maxp, Hkv, d), dtype=t["kL"].dtype, device="cuda")
+        ep = torch.zeros((B * maxp, Hkv), dtype=t["e"].dtype, device="cuda")
+        kLp[perm[:, :C]] = t["kL"].permute(0, 2, 1, 3)
+        ep[perm[:, :C]] = t["e"].permute(0, 2, 1)
+        ptab = perm.to(torch.int32).contiguous()
+
+        def pstep():
+            L.hils_decode_paged(t["q"], pages["k"], pages["v"], ptab, t["seq_len"], kLp, ep, wl.S,
+                                wl.K, wl.W, h=t.get("h"), W_down=t.get("W_down"),
+                                W_up=t.get("W_up"), out=bufs)
+
+        pstep()
+        st, sp = event_ring(n, torch)
+        L.hils_set_timing_events(L.STEP_DECODE, st, sp)
+        for _ in range(n):
+            torch.sum(flush, dim=0, out=sink)
+            pstep()
+        torch.cuda.synchronize()
+        L.hils_set_timing_events(L.STEP_DECODE)
+        tt = sorted(a.elapsed_time(b) for a, b in zip(st, sp))
+        out["paged_us_per_step"] = tt[len(tt) // 2] * 1e3
+        out["paged_graph_us_per_step"] = graph_median(pstep)
+        del pages, kLp, ep, ptab
     del t, bufs, flush, sink
     torch.cuda.empty_cache()
     return out
@@ -444,6 +501,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the 512K decode leg")
     ap.add_argument("--decode-workload", default="decode_7b_512k")
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode timing")
     ap.add_argument("--no-train", action="store_true", help="skip the training (fwd+bwd) leg")
     ap.add_argument("--legs", default="prefill,decode,train,landmark,packing",
                     help="comma list of legs to run (prefill is always reported)")

@@ -157,6 +157,30 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
                         int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Decode step over a paged KV cache (the serving layout of the pages'
+ * released backend, whose page size equals the 64-token chunk: one chunk is
+ * one page). Same method and outputs as hils_decode; only where the cache
+ * rows live differs:
+ *   k_pages, v_pages [P, Hkv, S, d]   tokens of page p
+ *   kL_pages [P, Hkv, d], e_pages [P, Hkv]   landmark key and bias of page p
+ *   page_table [B, max_pages] int32    page of chunk c of sequence b (tokens
+ *                                      c*S .. c*S+S-1); entries for chunks at
+ *                                      or past ceil(seq_len[b] / S) are not read
+ *   seq_len [B] int32 (required), each in [1, max_pages * S].
+ * p->Nk must equal max_pages * S (the per-sequence capacity; it sizes the
+ * workspace like hils_decode's). Page ids must lie in [0, P) (not checked).
+ * kL_pages / e_pages are read only for complete chunks below the distant
+ * boundary. Errors as hils_decode, plus HILS_ERR_INVALID for a null
+ * page_table or seq_len or an inconsistent max_pages.
+ */
+hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_len, const void* kL_pages, const void* e_pages,
+                              const void* h, const void* W_down, const void* W_up, void* o,
+                              float* lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
  * Landmark summary (paper: "The HiLS-Attention Mechanism", the landmark
  * worked example; the overview's first-order Taylor expansion of a chunk's
  * attention mass around its landmark query). For every complete chunk c of

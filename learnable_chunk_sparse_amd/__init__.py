@@ -24,7 +24,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
           3: "workspace too small or misaligned", 4: "HIP launch failure"}
 
 EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
-           "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_landmark_fwd",
+           "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_decode_paged", "hils_landmark_fwd",
            "hils_landmark_bwd", "hils_set_fwd_strategy", "hils_set_timing_events")
 FWD_AUTO, FWD_UNION, FWD_COMPACT = 0, 1, 2
 STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
@@ -71,6 +71,8 @@ def lib():
         L.hils_attn_bwd.argtypes = [P] + [vp] * 21 + [sz, vp]
         L.hils_decode.restype = ctypes.c_int
         L.hils_decode.argtypes = [P] + [vp] * 13 + [sz, vp]
+        L.hils_decode_paged.restype = ctypes.c_int
+        L.hils_decode_paged.argtypes = [P, vp, vp, vp, vp, i32] + [vp] * 10 + [sz, vp]
         L.hils_landmark_fwd.restype = ctypes.c_int
         L.hils_landmark_fwd.argtypes = [P] + [vp] * 7
         L.hils_landmark_bwd.restype = ctypes.c_int
@@ -234,6 +236,36 @@ def hils_decode(q, k_cache, v_cache, kL, e, S: int, K: int, W: int, seq_len=None
                                             _ptr(seq_len), _ptr(kL), _ptr(e), _ptr(h), _ptr(W_down),
                                             _ptr(W_up), _ptr(o), _ptr(lse), _ptr(idx), _ptr(ws),
                                             ws.numel(), _stream(dev)))
+    return o, lse, idx
+
+
+def hils_decode_paged(q, k_pages, v_pages, page_table, seq_len, kL_pages, e_pages, S: int, K: int,
+                      W: int, h=None, W_down=None, W_up=None, scale=0.0, out=None, with_topk=True):
+    """One decode step over a paged cache: k_pages / v_pages [P, Hkv, S, d],
+    kL_pages [P, Hkv, d], e_pages [P, Hkv], page_table [B, max_pages] int32
+    (page of each chunk), seq_len [B] int32 (device). Returns (o, lse,
+    topk_idx or None) as hils_decode."""
+    _contig(q, k_pages, v_pages, page_table, seq_len, kL_pages, e_pages, h, W_down, W_up)
+    B, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    if k_pages.shape[2] != S or page_table.dtype != torch.int32 or page_table.shape[0] != B:
+        raise ValueError("pages hold S tokens; page_table is int32 [B, max_pages]")
+    max_pages = page_table.shape[1]
+    r = 0 if W_down is None else W_down.shape[-2]
+    D = 0 if h is None else h.shape[-1]
+    p = Problem(_dtype_code(q), B, Hq, Hkv, d, 1, max_pages * S, S, K, W, D, r, 0, float(scale))
+    dev = q.device
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Hkv, K), dtype=torch.int32, device=dev) if with_topk else None
+        ws = _workspace(p, OP_DECODE, dev)
+    else:
+        o, lse, idx, ws = out
+    _check("hils_decode_paged", lib().hils_decode_paged(
+        ctypes.byref(p), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), max_pages,
+        _ptr(seq_len), _ptr(kL_pages), _ptr(e_pages), _ptr(h), _ptr(W_down), _ptr(W_up), _ptr(o),
+        _ptr(lse), _ptr(idx), _ptr(ws), ws.numel(), _stream(dev)))
     return o, lse, idx
 
 

@@ -176,10 +176,14 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, 
 // and lo bf16 halves of an fp32 query accumulate into the same product), the
 // landmark rows the B operand (columns), so lane (g, c) ends with the scores
 // of chunk c for heads 4 g .. 4 g + 3 and the max over heads is in-lane.
-template <typename T, typename QT, int G, int DH>
+// Paged caches (PG): pages of 64 tokens, k / v [P, Hkv, 64, d], landmark rows
+// [P, Hkv, d] and biases [P, Hkv]; ptab [B, maxp] holds the page of chunk c
+// of sequence b (a chunk is a page).
+template <typename T, typename QT, int G, int DH, bool PG>
 __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
                                                   const int32_t* __restrict__ seq_len,
+                                                  const int32_t* __restrict__ ptab, int maxp,
                                                   float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
                                                   int cstride, int Kc, int N, int C, int Hkv, int W,
                                                   int S, float scale) {
@@ -198,8 +202,18 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   const int nd = n_distant(n - 1, W, S);
   const int c_w = split * CPW + (CPW / 4) * w;  // this wave's first chunk
   if (c_w >= nd) return;
-  const T* kLg = kL + (size_t)bg * C * DH;
-  const T* eg = e + (size_t)bg * C;
+  // landmark row of chunk c: bg C + c, or (page of c) Hkv + g; a paged
+  // wave first copies the page ids of its chunks into LDS
+  __shared__ int spg[PG ? 4 : 1][PG ? CPW / 4 : 1];
+  if constexpr (PG) {
+#pragma unroll
+    for (int x = lane; x < CPW / 4; x += 64) spg[w][x] = ptab[(size_t)b * maxp + min(c_w + x, nd - 1)];
+    wave_lds_sync();
+  }
+  auto lrow = [&](int c) __attribute__((always_inline)) {
+    if constexpr (PG) return (size_t)spg[w][c - c_w] * Hkv + g;
+    else return (size_t)bg * C + c;
+  };
   // ring of PD steps: landmark rows chunk c_w + 16 st + col, dims 8 gl + 32 ks
   // (B operand), and the chunk's bias
   FT kb[PD][KS];
@@ -210,10 +224,10 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   const int rot = (bg * 7 + split * 13 + w * 5) & (NST - 1);
   auto cstep = [&](int st) __attribute__((always_inline)) { return c_w + 16 * ((st + rot) & (NST - 1)); };
   auto load = [&](int st, FT (&kd)[KS], float& ed) __attribute__((always_inline)) {
-    const int c = min(cstep(st) + col, nd - 1);
+    const size_t r = lrow(min(cstep(st) + col, nd - 1));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kd[ks] = ld8<T>(kLg + (size_t)c * DH + 8 * gl + 32 * ks);
-    ed = to_f<T>(eg[c]);
+    for (int ks = 0; ks < KS; ++ks) kd[ks] = ld8<T>(kL + r * DH + 8 * gl + 32 * ks);
+    ed = to_f<T>(e[r]);
   };
 #pragma unroll
   for (int j = 0; j < PD; ++j) load(j, kb[j], eb[j]);
@@ -564,6 +578,8 @@ __device__ __forceinline__ void select_block_big(const float* __restrict__ sc, c
 // partials per (bg, unit, head): pml = [m, l], po = U[0..DH)
 struct DecArgs {
   const int32_t* seq_len;
+  const int32_t* ptab;  // paged caches: page of chunk c of sequence b at b maxp + c
+  int maxp;
   const int32_t* sel;
   float *pml, *po;
   int N, C, Hkv, K, W, S, units;
@@ -574,7 +590,7 @@ struct DecArgs {
 // head) bg, software-pipelined: the next unit's K rows are requested as soon
 // as the current scores are formed, its V rows as soon as the current output
 // is, so loads stay in flight while the wave computes.
-template <typename T, typename QT, int G, int DH, int NUW>
+template <typename T, typename QT, int G, int DH, int NUW, bool PG>
 __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __restrict__ qs,
                                           const T* __restrict__ k, const T* __restrict__ v,
                                           const T* __restrict__ kL, const T* __restrict__ e,
@@ -591,7 +607,9 @@ __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __r
   const int n = seq_n(a.seq_len, b, N);
   const int ws = n_distant(n - 1, a.W, S) * S;
   // what each unit covers (wave-uniform): a selected chunk, or a window block
+  // (both 64-token aligned: one page of a paged cache)
   int uu[NUW], t0[NUW], cnt[NUW], chunk[NUW];
+  size_t kvb[NUW], lmr[NUW];  // first K/V row of the unit, landmark row of its chunk
 #pragma unroll
   for (int j = 0; j < NUW; ++j) {
     const int u = u0 + j * us;
@@ -605,6 +623,16 @@ __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __r
       t0[j] = ws + 64 * (u - K);
       cnt[j] = u < units ? min(64, n - t0[j]) : 0;
       if (cnt[j] <= 0) t0[j] = 0;
+    }
+    const int cl = chunk[j] >= 0 ? chunk[j] : 0;
+    if constexpr (PG) {
+      const size_t pk = (size_t)__builtin_amdgcn_readfirstlane(a.ptab[(size_t)b * a.maxp + t0[j] / 64]);
+      const size_t pl = (size_t)__builtin_amdgcn_readfirstlane(a.ptab[(size_t)b * a.maxp + cl]);
+      kvb[j] = (pk * Hkv + g) * 64;
+      lmr[j] = pl * Hkv + g;
+    } else {
+      kvb[j] = (size_t)bg * N + t0[j];
+      lmr[j] = (size_t)bg * C + cl;
     }
   }
   // loop-invariant operands: raw query heads (B operand of S^T = K Q^T), the
@@ -645,19 +673,19 @@ __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __r
   // 32 ks) and the chunk's landmark row (every A row = kL_c)
   FT kf[4][KS], vf[4][KS], kr[KS];
   auto loadK = [&](int j) __attribute__((always_inline)) {
-    const T* kb = k + ((size_t)bg * N + t0[j]) * DH;
+    const T* kb = k + kvb[j] * DH;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int tok = 16 * tb + col < cnt[j] ? 16 * tb + col : 0;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[tb][ks] = ld8<T>(kb + (size_t)tok * DH + 8 * gl + 32 * ks);
     }
-    const T* krow = kL + ((size_t)bg * C + (chunk[j] >= 0 ? chunk[j] : 0)) * DH + 8 * gl;
+    const T* krow = kL + lmr[j] * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kr[ks] = ld8<T>(krow + 32 * ks);
   };
   auto loadV = [&](int j) __attribute__((always_inline)) {
-    const T* vb = v + ((size_t)bg * N + t0[j]) * DH;
+    const T* vb = v + kvb[j] * DH;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int tok = 16 * tb + col < cnt[j] ? 16 * tb + col : 0;
@@ -684,7 +712,7 @@ __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __r
       if constexpr (HAS_LO) lm = mma16(kr[ks], qsl[ks], lm);
     }
     const int cj = cnt[j], chj = chunk[j];
-    const float ebias = chj >= 0 ? to_f<T>(e[(size_t)bg * C + chj]) : 0.f;
+    const float ebias = chj >= 0 ? to_f<T>(e[lmr[j]]) : 0.f;
     if (j + 1 < NUW) loadK(j + 1);
     float mx = NEG_INF;
 #pragma unroll
@@ -750,7 +778,7 @@ __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __r
 
 // selections (one block per (sequence, KV head)) and, alongside in the same
 // launch, the window units, which do not depend on them
-template <typename T, typename QT, int G, int DH, int PER>
+template <typename T, typename QT, int G, int DH, int PER, bool PG>
 __global__ __launch_bounds__(256) void k_dec_select_window(const float* __restrict__ cand_s,
                                                            const int32_t* __restrict__ cand_i,
                                                            int32_t* __restrict__ topk_out, int cstride,
@@ -779,19 +807,19 @@ __global__ __launch_bounds__(256) void k_dec_select_window(const float* __restri
   const int x = blk - nbg;
   const int bg = x / wpb;
   const int u = a.K + 4 * (x - bg * wpb) + (threadIdx.x >> 6);
-  if (u < a.units) dec_units<T, QT, G, DH, 1>(q, qs, k, v, kL, e, a, bg, u, 1);
+  if (u < a.units) dec_units<T, QT, G, DH, 1, PG>(q, qs, k, v, kL, e, a, bg, u, 1);
 }
 
 // the selected-chunk units: wave x of a (sequence, KV head) takes units x,
 // x + wpg, ... (DEC_NUW of them)
 constexpr int DEC_NUW = 2;
-template <typename T, typename QT, int G, int DH>
+template <typename T, typename QT, int G, int DH, bool PG>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
                                                     const T* __restrict__ k, const T* __restrict__ v,
                                                     const T* __restrict__ kL, const T* __restrict__ e,
                                                     DecArgs a, int wpg) {
   const int x = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (x < wpg) dec_units<T, QT, G, DH, DEC_NUW>(q, qs, k, v, kL, e, a, blockIdx.y, x, wpg);
+  if (x < wpg) dec_units<T, QT, G, DH, DEC_NUW, PG>(q, qs, k, v, kL, e, a, blockIdx.y, x, wpg);
 }
 
 // ---------------------------------------------------------------- combine
@@ -891,17 +919,20 @@ size_t decode_workspace(const Dims& p) {
   return s;
 }
 
-template <typename T, typename QT, int G, int DH>
+template <typename T, typename QT, int G, int DH, bool PG>
 static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const void* k, const void* v,
-                         const int32_t* seq_len, const void* kL, const void* e, void* o, float* lse,
-                         int32_t* topk_idx, const DecWs& w, hipStream_t st) {
-  hipLaunchKernelGGL((k_dec_scan<T, QT, G, DH>), dim3(w.nsplit, p.B * p.Hkv), dim3(256), 0, st,
-                     (const QT*)qs, (const T*)kL, (const T*)e, seq_len, w.cand_s, w.cand_i, w.cstride,
-                     w.Kc, p.N, p.C, p.Hkv, p.W, p.S, p.scale);
+                         const int32_t* seq_len, const int32_t* ptab, int maxp, const void* kL,
+                         const void* e, void* o, float* lse, int32_t* topk_idx, const DecWs& w,
+                         hipStream_t st) {
+  hipLaunchKernelGGL((k_dec_scan<T, QT, G, DH, PG>), dim3(w.nsplit, p.B * p.Hkv), dim3(256), 0, st,
+                     (const QT*)qs, (const T*)kL, (const T*)e, seq_len, ptab, maxp, w.cand_s, w.cand_i,
+                     w.cstride, w.Kc, p.N, p.C, p.Hkv, p.W, p.S, p.scale);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   DecArgs a;
   a.seq_len = seq_len;
+  a.ptab = ptab;
+  a.maxp = maxp;
   a.sel = w.sel;
   a.pml = w.pml;
   a.po = w.po;
@@ -909,13 +940,13 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
   a.scale = p.scale;
   const int nbg = p.B * p.Hkv;
   const int wpb = (w.units - p.K + 3) / 4;  // window units: four per block
-  hipLaunchKernelGGL((k_dec_select_window<T, QT, G, DH, 8>), dim3(nbg * (1 + wpb)), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_dec_select_window<T, QT, G, DH, 8, PG>), dim3(nbg * (1 + wpb)), dim3(256), 0, st,
                      (const float*)w.cand_s, (const int32_t*)w.cand_i, topk_idx, w.cstride, w.Kc, nbg,
                      wpb, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
                      (const T*)e, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int wpg = (p.K + DEC_NUW - 1) / DEC_NUW;
-  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH>), dim3((wpg + 3) / 4, nbg), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG>), dim3((wpg + 3) / 4, nbg), dim3(256), 0, st,
                      (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a,
                      wpg);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -926,35 +957,42 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
 
 template <typename T, typename QT, int G>
 static hipError_t dec_d(const Dims& p, const void* qs, const void* q, const void* k, const void* v,
-                        const int32_t* sl, const void* kL, const void* e, void* o, float* lse,
-                        int32_t* idx, const DecWs& w, hipStream_t st) {
-  if (p.d == 64) return dec_go<T, QT, G, 64>(p, qs, q, k, v, sl, kL, e, o, lse, idx, w, st);
-  return dec_go<T, QT, G, 128>(p, qs, q, k, v, sl, kL, e, o, lse, idx, w, st);
+                        const int32_t* sl, const int32_t* pt, int mp, const void* kL, const void* e,
+                        void* o, float* lse, int32_t* idx, const DecWs& w, hipStream_t st) {
+  if (pt != nullptr) {
+    if (p.d == 64) return dec_go<T, QT, G, 64, true>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
+    return dec_go<T, QT, G, 128, true>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
+  }
+  if (p.d == 64) return dec_go<T, QT, G, 64, false>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
+  return dec_go<T, QT, G, 128, false>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
 }
 
 template <typename T, typename QT>
 static hipError_t dec_g(const Dims& p, const void* qs, const void* q, const void* k, const void* v,
-                        const int32_t* sl, const void* kL, const void* e, void* o, float* lse,
-                        int32_t* idx, const DecWs& w, hipStream_t st) {
+                        const int32_t* sl, const int32_t* pt, int mp, const void* kL, const void* e,
+                        void* o, float* lse, int32_t* idx, const DecWs& w, hipStream_t st) {
   switch (p.G) {
-    case 1: return dec_d<T, QT, 1>(p, qs, q, k, v, sl, kL, e, o, lse, idx, w, st);
-    case 2: return dec_d<T, QT, 2>(p, qs, q, k, v, sl, kL, e, o, lse, idx, w, st);
-    case 4: return dec_d<T, QT, 4>(p, qs, q, k, v, sl, kL, e, o, lse, idx, w, st);
-    case 8: return dec_d<T, QT, 8>(p, qs, q, k, v, sl, kL, e, o, lse, idx, w, st);
+    case 1: return dec_d<T, QT, 1>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
+    case 2: return dec_d<T, QT, 2>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
+    case 4: return dec_d<T, QT, 4>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
+    case 8: return dec_d<T, QT, 8>(p, qs, q, k, v, sl, pt, mp, kL, e, o, lse, idx, w, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(const Dims& p, const void* qs, bool q_is_f32, const void* q, const void* k,
-                         const void* v, const int32_t* seq_len, const void* kL, const void* e,
-                         void* o, float* lse, int32_t* topk_idx, void* ws, hipStream_t st) {
+                         const void* v, const int32_t* seq_len, const int32_t* page_table,
+                         int max_pages, const void* kL, const void* e, void* o, float* lse,
+                         int32_t* topk_idx, void* ws, hipStream_t st) {
   DecWs w;
   carve(p, ws, &w);
+  const int32_t* pt = page_table;
+  const int mp = max_pages;
   if (p.dtype == 1) {
-    if (q_is_f32) return dec_g<uint16_t, float>(p, qs, q, k, v, seq_len, kL, e, o, lse, topk_idx, w, st);
-    return dec_g<uint16_t, uint16_t>(p, qs, q, k, v, seq_len, kL, e, o, lse, topk_idx, w, st);
+    if (q_is_f32) return dec_g<uint16_t, float>(p, qs, q, k, v, seq_len, pt, mp, kL, e, o, lse, topk_idx, w, st);
+    return dec_g<uint16_t, uint16_t>(p, qs, q, k, v, seq_len, pt, mp, kL, e, o, lse, topk_idx, w, st);
   }
-  return dec_g<float, float>(p, qs, q, k, v, seq_len, kL, e, o, lse, topk_idx, w, st);
+  return dec_g<float, float>(p, qs, q, k, v, seq_len, pt, mp, kL, e, o, lse, topk_idx, w, st);
 }
 
 }  // namespace hils

@@ -322,8 +322,40 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
     qf32 = true;
   }
   return hip_status(timed(HILS_STEP_DECODE, st, [&] {
-    return hils::launch_decode(d, qs, qf32, q, k_cache, v_cache, seq_len, kL, e, o, lse, topk_idx,
+    return hils::launch_decode(d, qs, qf32, q, k_cache, v_cache, seq_len, nullptr, 0, kL, e, o, lse, topk_idx,
                                ws, st);
+  }));
+}
+
+hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_len, const void* kL_pages, const void* e_pages,
+                              const void* h, const void* W_down, const void* W_up, void* o,
+                              float* lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                              void* stream) {
+  hils_status s = check_problem(p, HILS_OP_DECODE);
+  if (s != HILS_OK) return s;
+  if (!q || !k_pages || !v_pages || !page_table || !seq_len || !kL_pages || !e_pages || !o || !lse)
+    return HILS_ERR_INVALID;
+  if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  if (max_pages <= 0 || (long long)max_pages * p->S != p->Nk) return HILS_ERR_INVALID;
+  const Dims d = dims_of(p);
+  const size_t need = hils::decode_workspace(d);
+  if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* qs = q;
+  bool qf32 = d.dtype == HILS_FP32;
+  if (d.r > 0) {
+    float* qhat = static_cast<float*>(ws);
+    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, 1, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
+      return s;
+    qs = qhat;
+    qf32 = true;
+  }
+  return hip_status(timed(HILS_STEP_DECODE, st, [&] {
+    return hils::launch_decode(d, qs, qf32, q, k_pages, v_pages, seq_len, page_table, max_pages,
+                               kL_pages, e_pages, o, lse, topk_idx, ws, st);
   }));
 }
 

@@ -44,10 +44,13 @@ void set_fwd_strategy(int s);
 
 // Decode.
 size_t decode_workspace(const Dims& p);
+// page_table == nullptr: contiguous caches; otherwise pages of 64 tokens
+// (k, v [P, Hkv, 64, d], kL [P, Hkv, d], e [P, Hkv]) with the page of chunk c
+// of sequence b at page_table[b * max_pages + c].
 hipError_t launch_decode(const Dims& p, const void* q_or_qhat, bool q_is_f32, const void* q,
-                         const void* k, const void* v, const int32_t* seq_len, const void* kL,
-                         const void* e, void* o, float* lse, int32_t* topk_idx, void* ws,
-                         hipStream_t st);
+                         const void* k, const void* v, const int32_t* seq_len,
+                         const int32_t* page_table, int max_pages, const void* kL, const void* e,
+                         void* o, float* lse, int32_t* topk_idx, void* ws, hipStream_t st);
 
 // Batched GEMM C (+)= A * B on bf16 MFMA (fp32 operands split hi + lo).
 // A is M x K: element (m, k) at A[m * lda + k] (akm = false) or A[k * lda + m]

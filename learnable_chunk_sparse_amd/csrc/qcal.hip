@@ -213,8 +213,10 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
   const size_t lds = std::max<size_t>((size_t)(QT_M + QT_N) * QT_KP * el, (size_t)QT_M * QT_UP * 4);
   auto go = [&](auto kern, auto tq) -> hipError_t {
     typedef decltype(tq) TT;
-    hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e2 != hipSuccess) return e2;
+    if (lds > 64 * 1024) {  // beyond the default dynamic LDS limit only
+      hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e2 != hipSuccess) return e2;
+    }
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const TT*)q, (const TT*)h, (const TT*)W_down,
                        (const TT*)W_up, q_hat, u, ntok, Nq, p.Hq, p.d, p.D, p.r);
     return hipGetLastError();

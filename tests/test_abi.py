@@ -118,3 +118,16 @@ def test_fwd_strategy_switch():
             assert st in (0, 2), (s, st)
     finally:
         lib.hils_set_fwd_strategy(L.FWD_AUTO)
+
+
+def test_decode_paged_rejects_before_launch():
+    lib = L.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    p = prob(Nq=1, Nk=64 * 100, r=0, D=0)
+    args = lambda pt, mp, sl, wsb: (ctypes.byref(p), fake, fake, fake, pt, mp, sl, fake, fake, null,
+                                    null, null, fake, fake, null, fake, wsb, null)
+    assert lib.hils_decode_paged(*args(null, 100, fake, 1 << 40)) == 1  # no page table
+    assert lib.hils_decode_paged(*args(fake, 100, null, 1 << 40)) == 1  # no seq_len
+    assert lib.hils_decode_paged(*args(fake, 99, fake, 1 << 40)) == 1   # max_pages * S != Nk
+    assert lib.hils_decode_paged(*args(fake, 100, fake, 16)) == 3       # workspace too small

@@ -31,43 +31,63 @@ constexpr int RT_PAD = 8;   // kL tile row padding (elements)
 }  // namespace
 
 // One lane per position keeps that position's running top-KC (KC >= K) in
-// registers, sorted by (score desc, chunk asc). A candidate that beats the
-// K-th entry is bubbled in by a fixed compare-exchange chain (no divergence
-// inside the chain); the wave skips the chain when no lane's candidate
-// qualifies.
+// registers as 64-bit keys, sorted descending: the order-preserving bits of
+// the score above the complement of the chunk id, so that one unsigned
+// comparison orders by (score desc, chunk asc) and 0 lies below every real
+// candidate. Each 16-chunk step's candidates are sorted by a bitonic network
+// and merged in one pass (a half-cleaner against the current list, then a
+// bitonic merge): ~112 compare-exchanges per step whatever the lanes do,
+// where inserting the candidates one by one costs 16 per candidate and runs
+// for every candidate some lane of the wave keeps. A step is skipped when no
+// lane has a candidate above its K-th key.
+__device__ __forceinline__ uint64_t sel_key(float sc, int c) {
+  const uint32_t u = __float_as_uint(sc);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)c;
+}
+__device__ __forceinline__ float key_score(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_chunk(uint64_t k) { return (int)~(uint32_t)k; }
+
+// a keeps the larger key when desc, the smaller otherwise
+__device__ __forceinline__ void cex(uint64_t& a, uint64_t& b, bool desc) {
+  const bool sw = desc ? (b > a) : (a > b);
+  const uint64_t x = a;
+  a = sw ? b : a;
+  b = sw ? x : b;
+}
+
+template <int NS>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&a)[NS]) {
+#pragma unroll
+  for (int k = 2; k <= NS; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int l = i ^ j;
+        if (l > i) cex(a[i], a[l], (i & k) == 0);
+      }
+}
+
+// t (KC keys, descending) := the KC largest of t and n (16 keys, descending)
 template <int KC>
-struct TopK {
-  float s[KC];
-  int c[KC];
-  __device__ __forceinline__ void init() {
+__device__ __forceinline__ void merge_top(uint64_t (&t)[KC], const uint64_t (&n)[16]) {
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      s[k] = NEG_INF;
-      c[k] = -1;
+  for (int i = 0; i < KC; ++i) {
+    const int m = KC - 1 - i;
+    if (m < 16) t[i] = n[m] > t[i] ? n[m] : t[i];
+  }
+#pragma unroll
+  for (int j = KC >> 1; j > 0; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int l = i ^ j;
+      if (l > i) cex(t[i], t[l], true);
     }
-  }
-  __device__ __forceinline__ float kth(int K) const {
-    if (K == KC) return s[KC - 1];
-    float t = NEG_INF;
-#pragma unroll
-    for (int k = 0; k < KC; ++k) t = (k == K - 1) ? s[k] : t;
-    return t;
-  }
-  // insert (v, ci) when it beats the current entries; equal scores keep the
-  // earlier (lower) chunk since chunks arrive in ascending order
-  __device__ __forceinline__ void insert(float v, int ci) {
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      const bool sw = v > s[k];
-      const float ts = s[k];
-      const int tc = c[k];
-      s[k] = sw ? v : ts;
-      c[k] = sw ? ci : tc;
-      v = sw ? ts : v;
-      ci = sw ? tc : ci;
-    }
-  }
-};
+}
 
 template <typename T, typename QT, int G, int DH, int KC>
 __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
@@ -126,9 +146,9 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
   // selection state: lane p < PW owns position pw0 + p
   const int mypos = pw0 + lane;
   const int mynd = (lane < PW && mypos < N) ? n_distant(mypos, W, S) : 0;
-  TopK<KC> top;
-  top.init();
-  float thr = NEG_INF;
+  uint64_t tk[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) tk[k] = 0;
   const int nd_w = (pw0 < N) ? n_distant(min(pw0 + PW - 1, N - 1), W, S) : 0;
   const int nd_wg = n_distant(min(tile * PWG + PWG - 1, N - 1), W, S);
   const T* kLg = kL + (size_t)bg * C * DH;
@@ -212,16 +232,21 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
           const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
           v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
         }
+        uint64_t thr = tk[KC - 1];
+        if (K < KC) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = (c0 + j < mynd) ? v[j] : NEG_INF;
-        // candidates in ascending chunk order
+          for (int k = 0; k < KC; ++k) thr = k == K - 1 ? tk[k] : thr;
+        }
+        uint64_t nk[16];
+        bool any = false;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const bool pass = v[j] > thr;
-          if (__ballot(pass) != 0) {
-            if (pass) top.insert(v[j], c0 + j);
-            thr = top.kth(K);
-          }
+          nk[j] = c0 + j < mynd ? sel_key(v[j], c0 + j) : 0ull;
+          any |= nk[j] > thr;
+        }
+        if (__ballot(any) != 0) {
+          bitonic_sort_desc<16>(nk);
+          merge_top<KC>(tk, nk);
         }
       }
       wave_lds_sync();
@@ -235,8 +260,8 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
     float sv[KC];
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      ids[k] = (k < K && top.c[k] >= 0) ? top.c[k] : 0x7FFFFFFF;
-      sv[k] = top.s[k];
+      ids[k] = (k < K && tk[k] != 0) ? key_chunk(tk[k]) : 0x7FFFFFFF;
+      sv[k] = key_score(tk[k]);
     }
 #pragma unroll
     for (int a = 0; a < KC; ++a)

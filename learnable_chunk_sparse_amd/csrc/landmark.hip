@@ -12,12 +12,15 @@
 //             dqL  = scale sum_t ds_t k_t
 //             dk_t += scale ds_t qL + p_t dkL
 //
-// One wave per (b, kv head, chunk), one wave per workgroup. The chunk's 64
-// keys are staged in LDS as fp32 rows padded to DH + 1 floats, so lane t
-// reading row t (scores, dkL . k_t) and lane j reading column j (the
-// key-weighted sums) are both free of bank conflicts. Lane t owns token t for
-// the scores and the softmax (wave reductions); lane j owns dims j and
-// j + 64 for the sums over tokens. All arithmetic is fp32.
+// One wave per (b, kv head, chunk), up to four independent waves per
+// workgroup (as many as keep the workgroup's LDS under 48 KB). The chunk's 64
+// keys are staged in LDS in their own type (bf16 keys stay bf16: half the
+// LDS, twice the resident waves), rows padded so that lane t reading row t
+// (scores, dkL . k_t) and lane j reading column j (the key-weighted sums) are
+// both free of bank conflicts (bf16: pitch DH + 2, an odd number of words;
+// fp32: DH + 1). Lane t owns token t for the scores and the softmax (wave
+// reductions); lane j owns dims j and j + 64 for the sums over tokens. All
+// arithmetic is fp32.
 #include "hils_common.h"
 #include "hils_internal.h"
 
@@ -37,22 +40,47 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// the chunk's keys -> kf[t][j] (fp32, pitch DH + 1); 16-byte loads
+// LDS row pitch of the staged keys (elements)
 template <typename T, int DH>
-__device__ __forceinline__ void stage_keys(const T* __restrict__ kc, float* kf, int lane) {
-  constexpr int V = 16 / sizeof(T), PER = LS * DH / (64 * V);
+constexpr int kpitch() { return sizeof(T) == 2 ? DH + 2 : DH + 1; }
+// waves (chunks) per workgroup
+template <typename T, int DH>
+constexpr int lm_waves() {
+  constexpr int per = LS * kpitch<T, DH>() * (int)sizeof(T) + (2 * DH + 2 * LS) * 4;
+  return per * 4 <= 48 * 1024 ? 4 : per * 2 <= 48 * 1024 ? 2 : 1;
+}
+
+// the chunk's keys -> kf[t][j] (pitch kpitch); 16-byte loads
+template <typename T, int DH>
+__device__ __forceinline__ void stage_keys(const T* __restrict__ kc, T* kf, int lane) {
+  constexpr int V = 16 / sizeof(T), PER = LS * DH / (64 * V), P = kpitch<T, DH>();
+  // all loads first, then the LDS stores
+  T v[PER][V];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int x = (it * 64 + lane) * V;
+    if constexpr (sizeof(T) == 2) {
+      const u16x8 a = *reinterpret_cast<const u16x8*>(kc + x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[it][i] = a[i];
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(kc + x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[it][i] = a[i];
+    }
+  }
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int x = (it * 64 + lane) * V;
     const int t = x / DH, j = x - t * DH;
     if constexpr (sizeof(T) == 2) {
-      const u16x8 v = *reinterpret_cast<const u16x8*>(kc + x);
+      // j is a multiple of 8 and the pitch even: 4-byte aligned pairs
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kf[t * (DH + 1) + j + i] = bf2f(v[i]);
+      for (int i = 0; i < 8; i += 2)
+        *reinterpret_cast<uint32_t*>(kf + t * P + j + i) = (uint32_t)v[it][i] | ((uint32_t)v[it][i + 1] << 16);
     } else {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(kc + x);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kf[t * (DH + 1) + j + i] = v[i];
+      for (int i = 0; i < 4; ++i) kf[t * P + j + i] = v[it][i];
     }
   }
 }
@@ -63,13 +91,13 @@ struct ChunkSoftmax {
   float logZ;   // log sum_t exp(s_t)
   float sbar;   // sum_t p_t s_t
 };
-template <int DH>
-__device__ __forceinline__ ChunkSoftmax chunk_softmax(const float* kf, const float* qs, float* ps,
+template <typename T, int DH>
+__device__ __forceinline__ ChunkSoftmax chunk_softmax(const T* kf, const float* qs, float* ps,
                                                       float scale, int lane) {
   float acc = 0.f;
-  const float* kr = kf + lane * (DH + 1);
+  const T* kr = kf + lane * kpitch<T, DH>();
 #pragma unroll 16
-  for (int j = 0; j < DH; ++j) acc = fmaf(qs[j], kr[j], acc);
+  for (int j = 0; j < DH; ++j) acc = fmaf(qs[j], to_f<T>(kr[j]), acc);
   ChunkSoftmax r;
   r.s = acc * scale;
   const float m = wave_max(r.s);
@@ -84,25 +112,29 @@ __device__ __forceinline__ ChunkSoftmax chunk_softmax(const float* kf, const flo
 }  // namespace
 
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k_landmark_fwd(const T* __restrict__ qL, const T* __restrict__ k,
+__global__ __launch_bounds__(256) void k_landmark_fwd(const T* __restrict__ qL, const T* __restrict__ k,
                                                      T* __restrict__ kL, T* __restrict__ e,
                                                      float* __restrict__ kL32, float* __restrict__ e32,
                                                      int N, int C, float scale) {
-  __shared__ float kf[LS * (DH + 1)];
-  __shared__ float qs[DH], ps[LS];
-  const int lane = threadIdx.x;
-  const int c = blockIdx.x, bg = blockIdx.y;
+  constexpr int P = kpitch<T, DH>(), WB = lm_waves<T, DH>();
+  __shared__ __align__(16) T kf_all[WB][LS * P];
+  __shared__ float qs_all[WB][DH], ps_all[WB][LS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * WB + w, bg = blockIdx.y;
+  if (c >= C) return;  // whole waves; the waves share no data
+  T* kf = kf_all[w];
+  float *qs = qs_all[w], *ps = ps_all[w];
   const size_t cr = (size_t)bg * C + c;  // (b, kv head, chunk)
   stage_keys<T, DH>(k + ((size_t)bg * N + (size_t)c * LS) * DH, kf, lane);
   for (int j = lane; j < DH; j += 64) qs[j] = to_f<T>(qL[cr * DH + j]);
-  __syncthreads();
-  const ChunkSoftmax r = chunk_softmax<DH>(kf, qs, ps, scale, lane);
-  __syncthreads();
+  wave_lds_sync();
+  const ChunkSoftmax r = chunk_softmax<T, DH>(kf, qs, ps, scale, lane);
+  wave_lds_sync();
 #pragma unroll
   for (int j = lane; j < DH; j += 64) {
     float a = 0.f;
 #pragma unroll 16
-    for (int t = 0; t < LS; ++t) a = fmaf(ps[t], kf[t * (DH + 1) + j], a);
+    for (int t = 0; t < LS; ++t) a = fmaf(ps[t], to_f<T>(kf[t * P + j]), a);
     kL[cr * DH + j] = from_f<T>(a);
     if (kL32 != nullptr) kL32[cr * DH + j] = a;
   }
@@ -114,15 +146,19 @@ __global__ __launch_bounds__(64) void k_landmark_fwd(const T* __restrict__ qL, c
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k_landmark_bwd(const T* __restrict__ qL, const T* __restrict__ k,
+__global__ __launch_bounds__(256) void k_landmark_bwd(const T* __restrict__ qL, const T* __restrict__ k,
                                                      const float* __restrict__ dkL,
                                                      const float* __restrict__ de,
                                                      float* __restrict__ dqL, float* __restrict__ dk,
                                                      int N, int C, float scale) {
-  __shared__ float kf[LS * (DH + 1)];
-  __shared__ float qs[DH], gs[DH], ps[LS], dss[LS];
-  const int lane = threadIdx.x;
-  const int c = blockIdx.x, bg = blockIdx.y;
+  constexpr int P = kpitch<T, DH>(), WB = lm_waves<T, DH>();
+  __shared__ __align__(16) T kf_all[WB][LS * P];
+  __shared__ float qs_all[WB][DH], gs_all[WB][DH], ps_all[WB][LS], dss_all[WB][LS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = blockIdx.x * WB + w, bg = blockIdx.y;
+  if (c >= C) return;  // whole waves; the waves share no data
+  T* kf = kf_all[w];
+  float *qs = qs_all[w], *gs = gs_all[w], *ps = ps_all[w], *dss = dss_all[w];
   const size_t cr = (size_t)bg * C + c;
   const size_t t0 = (size_t)bg * N + (size_t)c * LS;  // first token row of the chunk
   stage_keys<T, DH>(k + t0 * DH, kf, lane);
@@ -131,33 +167,33 @@ __global__ __launch_bounds__(64) void k_landmark_bwd(const T* __restrict__ qL, c
     gs[j] = dkL[cr * DH + j];
   }
   const float dev = de[cr];
-  __syncthreads();
-  const ChunkSoftmax r = chunk_softmax<DH>(kf, qs, ps, scale, lane);
-  __syncthreads();
+  wave_lds_sync();
+  const ChunkSoftmax r = chunk_softmax<T, DH>(kf, qs, ps, scale, lane);
+  wave_lds_sync();
   // dkL . kL with kL = sum_t p_t k_t (lane j: its dims)
   float gk = 0.f;
 #pragma unroll
   for (int j = lane; j < DH; j += 64) {
     float a = 0.f;
 #pragma unroll 16
-    for (int t = 0; t < LS; ++t) a = fmaf(ps[t], kf[t * (DH + 1) + j], a);
+    for (int t = 0; t < LS; ++t) a = fmaf(ps[t], to_f<T>(kf[t * P + j]), a);
     gk = fmaf(gs[j], a, gk);
   }
   gk = wave_sum(gk);
   // ds_t (lane t)
   {
     float g = 0.f;
-    const float* kr = kf + lane * (DH + 1);
+    const T* kr = kf + lane * P;
 #pragma unroll 16
-    for (int j = 0; j < DH; ++j) g = fmaf(gs[j], kr[j], g);
+    for (int j = 0; j < DH; ++j) g = fmaf(gs[j], to_f<T>(kr[j]), g);
     dss[lane] = r.p * (g - gk - dev * (r.s - r.sbar));
   }
-  __syncthreads();
+  wave_lds_sync();
 #pragma unroll
   for (int j = lane; j < DH; j += 64) {
     float a = 0.f;
 #pragma unroll 16
-    for (int t = 0; t < LS; ++t) a = fmaf(dss[t], kf[t * (DH + 1) + j], a);
+    for (int t = 0; t < LS; ++t) a = fmaf(dss[t], to_f<T>(kf[t * P + j]), a);
     dqL[cr * DH + j] = a * scale;
     const float qj = qs[j] * scale, gj = gs[j];
     float* dkc = dk + t0 * DH + j;
@@ -171,12 +207,13 @@ template <typename T, int DH>
 hipError_t lm_go(const Dims& p, bool bwd, const void* qL, const void* k, void* kL, void* e,
                  float* kL32, float* e32, const float* dkL, const float* de, float* dqL, float* dk,
                  hipStream_t st) {
-  const dim3 grid((unsigned)p.C, (unsigned)(p.B * p.Hkv));
+  constexpr int WB = lm_waves<T, DH>();
+  const dim3 grid((unsigned)((p.C + WB - 1) / WB), (unsigned)(p.B * p.Hkv));
   if (!bwd)
-    hipLaunchKernelGGL((k_landmark_fwd<T, DH>), grid, dim3(64), 0, st, (const T*)qL, (const T*)k,
+    hipLaunchKernelGGL((k_landmark_fwd<T, DH>), grid, dim3(64 * WB), 0, st, (const T*)qL, (const T*)k,
                        (T*)kL, (T*)e, kL32, e32, p.N, p.C, p.scale);
   else
-    hipLaunchKernelGGL((k_landmark_bwd<T, DH>), grid, dim3(64), 0, st, (const T*)qL, (const T*)k,
+    hipLaunchKernelGGL((k_landmark_bwd<T, DH>), grid, dim3(64 * WB), 0, st, (const T*)qL, (const T*)k,
                        dkL, de, dqL, dk, p.N, p.C, p.scale);
   return hipGetLastError();
 }

@@ -48,24 +48,67 @@ namespace hils {
 // every 32-token group stored in the order 0-3,16-19, 4-7,20-23, 8-11,24-27,
 // 12-15,28-31, so that lane group g of an MFMA fragment finds its 8 tokens
 // {4g..4g+3, 16+4g..16+4g+3} contiguous at slots 8g..8g+7.
+// One workgroup per 64-token block: the block's rows come in as 16-byte
+// vectors into an LDS tile, and each output vector (8 consecutive slots of
+// one d row) is gathered from the tile's column and written as 16 bytes.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_vt_perm(const T* __restrict__ v, T* __restrict__ vt, int N,
                                                  int Np) {
-  __shared__ T tile[64][DH + 1];
+  constexpr int V = 16 / sizeof(T);      // elements per 16-byte vector
+  constexpr int TP = sizeof(T) == 2 ? DH + 2 : DH + 1;  // tile pitch: an odd number of words
+  constexpr int NV = 64 * DH / V;                         // vectors per block
+  __shared__ __align__(16) T tile[64 * TP];
   const int bg = blockIdx.y, t0 = blockIdx.x * 64;
   const T* src = v + (size_t)bg * N * DH;
-  for (int x = threadIdx.x; x < 64 * DH; x += 256) {
-    const int t = x / DH, dd = x - t * DH;
-    tile[t][dd] = (t0 + t < N) ? src[(size_t)(t0 + t) * DH + dd] : from_f<T>(0.f);
+  // rows in: vector x = token t, dims dv .. dv + V - 1 (rows past N read as 0)
+  T in[NV / 256][V];
+#pragma unroll
+  for (int i = 0; i < NV / 256; ++i) {
+    const int x = threadIdx.x + 256 * i;
+    const int t = x / (DH / V), dv = (x - t * (DH / V)) * V;
+    const bool ok = t0 + t < N;
+    const T* p = src + (size_t)(ok ? t0 + t : 0) * DH + dv;
+    if constexpr (sizeof(T) == 2) {
+      const u16x8 a = *reinterpret_cast<const u16x8*>(p);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) in[i][j] = ok ? a[j] : (T)0;
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) in[i][j] = ok ? a[j] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV / 256; ++i) {
+    const int x = threadIdx.x + 256 * i;
+    const int t = x / (DH / V), dv = (x - t * (DH / V)) * V;
+#pragma unroll
+    for (int j = 0; j < V; ++j) tile[t * TP + dv + j] = in[i][j];
   }
   __syncthreads();
+  // vectors out: row dd, slots s .. s + V - 1 of the block
   T* dst = vt + (size_t)bg * DH * Np + t0;
-  for (int x = threadIdx.x; x < 64 * DH; x += 256) {
-    const int dd = x / 64, s = x - dd * 64;  // storage slot within the 64-token block
-    const int half = s >> 5, sl = s & 31;
-    const int g8 = sl >> 3, e = sl & 7;
-    const int t = 32 * half + (e < 4 ? 4 * g8 + e : 16 + 4 * g8 + (e - 4));
-    dst[(size_t)dd * Np + s] = tile[t][dd];
+#pragma unroll
+  for (int i = 0; i < NV / 256; ++i) {
+    const int x = threadIdx.x + 256 * i;
+    const int dd = x / (64 / V), s0 = (x - dd * (64 / V)) * V;
+    T o[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int s = s0 + j;  // storage slot within the 64-token block
+      const int half = s >> 5, sl = s & 31;
+      const int g8 = sl >> 3, e = sl & 7;
+      const int t = 32 * half + (e < 4 ? 4 * g8 + e : 16 + 4 * g8 + (e - 4));
+      o[j] = tile[t * TP + dd];
+    }
+    if constexpr (sizeof(T) == 2) {
+      u16x8 w;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = o[j];
+      *reinterpret_cast<u16x8*>(dst + (size_t)dd * Np + s0) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(dst + (size_t)dd * Np + s0) = f32x4{o[0], o[1], o[2], o[3]};
+    }
   }
 }
 

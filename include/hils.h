@@ -28,6 +28,9 @@
  *   misaligned), HILS_ERR_HIP (a kernel launch failed). A fault inside a
  *   kernel surfaces at the caller's next synchronisation. Nothing prints,
  *   aborts or throws across this boundary.
+ * - A sequence shorter than one chunk (Nk < S) has no complete chunk: the
+ *   chunk tensors (kL, e, their gradients, landmark queries) are then empty
+ *   and may be NULL.
  *
  * Notation (the paper's): B batch, Hq query heads, Hkv KV heads, G = Hq/Hkv
  * (query head h uses KV head h / G), d head dim, S chunk size, C = Nk / S

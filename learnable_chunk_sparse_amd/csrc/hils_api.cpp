@@ -76,6 +76,18 @@ hils_status check_landmark(const hils_problem* p) {
   return HILS_OK;
 }
 
+// chunk tensors (kL, e and their gradients) may be NULL when the sequence
+// holds no complete chunk: they are empty and never touched
+inline bool chunks_ok(const hils_problem* p, const void* a, const void* b) {
+  return (p->Nk / p->S) == 0 || (a != nullptr && b != nullptr);
+}
+
+// Without a complete chunk the kernels still form (and discard, or weight by
+// zero) the landmark row and bias of chunk 0 for empty slots: a NULL kL / e
+// is replaced by another input of the same dtype with at least d finite
+// elements, which keeps those reads in bounds.
+inline const void* or_stand_in(const void* x, const void* stand_in) { return x ? x : stand_in; }
+
 Dims landmark_dims(const hils_problem* p) {
   Dims d{};
   d.dtype = p->dtype;
@@ -234,8 +246,10 @@ hils_status hils_route(const hils_problem* p, const void* q, const void* kL, con
                        float* topk_score, void* ws, size_t ws_bytes, void* stream) {
   hils_status s = check_problem(p, HILS_OP_ROUTE);
   if (s != HILS_OK) return s;
-  if (!q || !kL || !e || !topk_idx) return HILS_ERR_INVALID;
+  if (!q || !chunks_ok(p, kL, e) || !topk_idx) return HILS_ERR_INVALID;
   if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  kL = or_stand_in(kL, q);
+  e = or_stand_in(e, q);
   const Dims d = dims_of(p);
   float* qhat = nullptr;
   const size_t need = carve_route(d, nullptr, &qhat);
@@ -256,8 +270,10 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
                           size_t ws_bytes, void* stream) {
   hils_status s = check_problem(p, HILS_OP_FWD);
   if (s != HILS_OK) return s;
-  if (!q || !k || !v || !kL || !e || !o || !lse || !topk_idx) return HILS_ERR_INVALID;
+  if (!q || !k || !v || !chunks_ok(p, kL, e) || !o || !lse || !topk_idx) return HILS_ERR_INVALID;
   if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  kL = or_stand_in(kL, k);
+  e = or_stand_in(e, k);
   const Dims d = dims_of(p);
   if (!fwd_fits_lds(d)) return HILS_ERR_UNSUPPORTED;
   FwdWs w;
@@ -284,9 +300,12 @@ hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, c
                           void* ws, size_t ws_bytes, void* stream) {
   hils_status s = check_problem(p, HILS_OP_BWD);
   if (s != HILS_OK) return s;
-  if (!q || !k || !v || !kL || !e || !lse || !topk_idx || !dO || !dq || !dk || !dv || !dkL || !de)
+  if (!q || !k || !v || !chunks_ok(p, kL, e) || !lse || !topk_idx || !dO || !dq || !dk || !dv ||
+      !chunks_ok(p, dkL, de))
     return HILS_ERR_INVALID;
   if (p->r > 0 && (!h || !W_down || !W_up || !dW_down || !dW_up)) return HILS_ERR_INVALID;
+  kL = or_stand_in(kL, k);
+  e = or_stand_in(e, k);
   const Dims d = dims_of(p);
   const size_t need = hils::bwd_workspace(d);
   if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
@@ -304,8 +323,10 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
                         int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
   hils_status s = check_problem(p, HILS_OP_DECODE);
   if (s != HILS_OK) return s;
-  if (!q || !k_cache || !v_cache || !kL || !e || !o || !lse) return HILS_ERR_INVALID;
+  if (!q || !k_cache || !v_cache || !chunks_ok(p, kL, e) || !o || !lse) return HILS_ERR_INVALID;
   if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
+  kL = or_stand_in(kL, k_cache);
+  e = or_stand_in(e, k_cache);
   const Dims d = dims_of(p);
   const size_t need = hils::decode_workspace(d);
   if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
@@ -335,7 +356,8 @@ hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* 
                               void* stream) {
   hils_status s = check_problem(p, HILS_OP_DECODE);
   if (s != HILS_OK) return s;
-  if (!q || !k_pages || !v_pages || !page_table || !seq_len || !kL_pages || !e_pages || !o || !lse)
+  if (!q || !k_pages || !v_pages || !page_table || !seq_len || !chunks_ok(p, kL_pages, e_pages) || !o ||
+      !lse)
     return HILS_ERR_INVALID;
   if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
   if (max_pages <= 0 || (long long)max_pages * p->S != p->Nk) return HILS_ERR_INVALID;
@@ -363,7 +385,7 @@ hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void*
                               void* e, float* kL32, float* e32, void* stream) {
   hils_status s = check_landmark(p);
   if (s != HILS_OK) return s;
-  if (!qL || !k || !kL || !e) return HILS_ERR_INVALID;
+  if (!k || !chunks_ok(p, qL, qL) || !chunks_ok(p, kL, e)) return HILS_ERR_INVALID;
   const Dims d = landmark_dims(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(timed(HILS_STEP_LANDMARK_FWD, st, [&] {
@@ -376,7 +398,7 @@ hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void*
                               void* stream) {
   hils_status s = check_landmark(p);
   if (s != HILS_OK) return s;
-  if (!qL || !k || !dkL || !de || !dqL || !dk) return HILS_ERR_INVALID;
+  if (!k || !dk || !chunks_ok(p, qL, dqL) || !chunks_ok(p, dkL, de)) return HILS_ERR_INVALID;
   const Dims d = landmark_dims(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(timed(HILS_STEP_LANDMARK_BWD, st, [&] {

@@ -131,3 +131,14 @@ def test_decode_paged_rejects_before_launch():
     assert lib.hils_decode_paged(*args(fake, 100, null, 1 << 40)) == 1  # no seq_len
     assert lib.hils_decode_paged(*args(fake, 99, fake, 1 << 40)) == 1   # max_pages * S != Nk
     assert lib.hils_decode_paged(*args(fake, 100, fake, 16)) == 3       # workspace too small
+
+
+def test_chunk_tensors_may_be_null_only_without_complete_chunks():
+    lib = L.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    for Nk, code in [(50, 3), (8192, 1)]:  # 3: passed validation, then the workspace check
+        p = prob(Nq=Nk, Nk=Nk, r=0, D=0)
+        st = lib.hils_attn_fwd(ctypes.byref(p), fake, fake, fake, null, null, null, null, null, fake,
+                               fake, fake, fake, 16, null)
+        assert st == code, (Nk, st)

@@ -241,7 +241,9 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
         bool any = false;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          nk[j] = c0 + j < mynd ? sel_key(v[j], c0 + j) : 0ull;
+          // masked arithmetically: a select here became a branch per candidate
+          const uint64_t live = 0ull - (uint64_t)(c0 + j < mynd);
+          nk[j] = sel_key(v[j], c0 + j) & live;
           any |= nk[j] > thr;
         }
         if (__ballot(any) != 0) {

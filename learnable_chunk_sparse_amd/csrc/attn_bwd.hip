@@ -44,31 +44,54 @@ __global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
 }
 
 // fp32 score s_c = scale q_hat . kL_c + e_c of every selected slot. A
-// workgroup takes 16 consecutive query rows: their q_hat rows are staged in
-// LDS with coalesced loads. Eight adjacent lanes share a (row, slot) pair,
-// each reading DH / 8 elements of the selected landmark row (one wave load
-// covers eight whole rows, which stay in L2), and their partial dot products
-// are summed across the eight lanes. Four pairs per lane are in flight.
+// workgroup takes 64 consecutive query rows: their q_hat rows and their
+// (row, slot) chunk ids are staged in LDS together (one round trip), then
+// eight adjacent lanes share a (row, slot) pair, each reading DH / 8 elements
+// of the selected landmark row (one wave load covers eight whole rows, which
+// stay in L2), with all of a lane's landmark loads in flight at once; the
+// partial dot products are summed across the eight lanes.
 template <typename T, typename QT, int DH>
 __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                   const T* __restrict__ e,
                                                   const int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ sT, long rows, int N, int Hq,
                                                   int Hkv, int G, int C, int K, float scale) {
-  constexpr int PR = 16, QP = DH + 4, DL = DH / 8, NF = DL / 8, UP = 4;
+  constexpr int PR = 64, QP = DH + 4, DL = DH / 8, NF = DL / 8, UP = 8, KMAX = 32;
   typedef typename Frag<T>::type FT;
   __shared__ __align__(16) float qrow[PR * QP];
-  __shared__ long ibase[PR];  // (bg N + i) K of each row: its selection list
-  __shared__ long cbase[PR];  // bg C: its landmark rows
+  __shared__ int cid[PR * KMAX];  // chunk id of pair x = row * K + slot
+  __shared__ long cbase[PR];      // bg C: the row's landmark rows
   const int tid = threadIdx.x;
   const long r0 = (long)blockIdx.x * PR;
-  if (tid < PR) {
-    const long row = std::min(r0 + tid, rows - 1);
-    const int i = (int)(row % N);
-    const long bh = row / N;
-    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
-    const long bg = (long)b * Hkv + h / G;
-    ibase[tid] = (bg * N + i) * K;
+  const int nrow = (int)std::min<long>(PR, rows - r0);
+  const int npair = nrow * K;
+  // x / K for pair ids x < 2^11 through a float reciprocal: (x + 1/2) / K
+  // lies at least 1/(2K) away from an integer, far beyond the rounding
+  const float invK = 1.f / (float)K;
+  auto row_idx = [&](int x) __attribute__((always_inline)) { return (int)(((float)x + 0.5f) * invK); };
+  // (b, h, i) of the first row; rows r0 + rr follow it
+  const long bh0 = r0 / N;
+  const int i0 = (int)(r0 - bh0 * N), h0 = (int)(bh0 % Hq), b0 = (int)(bh0 / Hq);
+  auto row_of = [&](int rr, long& bg, int& i) __attribute__((always_inline)) {
+    int ii = i0 + rr, h = h0, b = b0;
+    while (ii >= N) {
+      ii -= N;
+      if (++h == Hq) h = 0, ++b;
+    }
+    bg = (long)b * Hkv + h / G;
+    i = ii;
+  };
+  for (int x = tid; x < npair; x += 256) {
+    const int rr = row_idx(x), kk = x - rr * K;
+    long bg;
+    int i;
+    row_of(rr, bg, i);
+    cid[x] = topk_idx[(bg * N + i) * K + kk];
+  }
+  if (tid < nrow) {
+    long bg;
+    int i;
+    row_of(tid, bg, i);
     cbase[tid] = bg * C;
   }
   for (int x = tid; x < PR * DH / 4; x += 256) {
@@ -88,28 +111,23 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, con
   }
   __syncthreads();
   const int l8 = tid & 7, pr = tid >> 3;  // 32 pairs per pass
-  const int npair = (int)std::min<long>(PR, rows - r0) * K;
   for (int x0 = pr; x0 < npair; x0 += 32 * UP) {
-    int cc[UP], rrv[UP];
+    FT kv[UP][NF];
+    float ev[UP];
+    int cc[UP];
 #pragma unroll
     for (int t = 0; t < UP; ++t) {
       const int x = min(x0 + 32 * t, npair - 1);
-      const int rr = x / K, kk = x - rr * K;
-      rrv[t] = rr;
-      cc[t] = topk_idx[ibase[rr] + kk];
-    }
-    FT kv[UP][NF];
-    float ev[UP];
-#pragma unroll
-    for (int t = 0; t < UP; ++t) {
-      const long kc = cbase[rrv[t]] + max(cc[t], 0);
+      cc[t] = cid[x];
+      const long kc = cbase[row_idx(x)] + max(cc[t], 0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) kv[t][f] = ld8<T>(kL + kc * DH + DL * l8 + 8 * f);
       ev[t] = to_f<T>(e[kc]);
     }
 #pragma unroll
     for (int t = 0; t < UP; ++t) {
-      const float* qr = qrow + rrv[t] * QP + DL * l8;
+      const int x = x0 + 32 * t;
+      const float* qr = qrow + row_idx(min(x, npair - 1)) * QP + DL * l8;
       float acc = 0.f;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
@@ -124,7 +142,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, con
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
       acc += __shfl_xor(acc, 4, 64);
-      const int x = x0 + 32 * t;
       if (l8 == 0 && x < npair)
         sT[r0 * K + x] = cc[t] >= 0 ? fmaf(acc, scale, ev[t]) : __builtin_nanf("");
     }
@@ -1161,7 +1178,7 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
   const size_t rows = (size_t)p.B * p.Hq * p.N;
   const size_t bg = (size_t)p.B * p.Hkv;
   hipError_t err;
-  hipLaunchKernelGGL((k_bwd_prep<T, QT, DH>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_bwd_prep<T, QT, DH>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, st,
                      (const QT*)qsrc, (const T*)kL, (const T*)e, topk_idx, w.sT, (long)rows, p.N,
                      p.Hq, p.Hkv, G, p.C, p.K, p.scale);
   if ((err = hipGetLastError()) != hipSuccess) return err;

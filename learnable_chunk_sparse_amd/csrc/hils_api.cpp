@@ -121,8 +121,22 @@ Dims dims_of(const hils_problem* p) {
 }
 
 // Workspace layout of each op (the same function computes sizes and carves).
+// Routing scratch with Q-Cal: the fp32 calibrated queries, or on the u path
+// (hils::route_u_ok) u = W_down h in the same region (r <= d) and the
+// W_up^T kL planes.
+struct RouteWs {
+  float* qhat = nullptr;  // q_hat [B, Hq, N, d], or u [B N, Hq r] on the u path
+  uint16_t *klh = nullptr, *kll = nullptr;
+};
+void carve_route_ws(const Dims& d, Carver& c, RouteWs* out) {
+  const size_t rows = (size_t)d.B * d.Hq * d.N;
+  out->qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
+  const size_t kp = hils::route_u_ok(d) ? (size_t)d.B * d.Hq * d.C * d.r * sizeof(uint16_t) : 0;
+  out->klh = (uint16_t*)c.take(kp);
+  out->kll = (uint16_t*)c.take(kp);
+}
 struct FwdWs {
-  float* qhat;
+  RouteWs rt;
   float* s_T;
   float* sel_lse;
   void* vt;
@@ -130,16 +144,15 @@ struct FwdWs {
 size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
   Carver c(ws);
   const size_t rows = (size_t)d.B * d.Hq * d.N;
-  out->qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
+  carve_route_ws(d, c, &out->rt);
   out->s_T = (float*)c.take(rows * d.K * sizeof(float));
   out->sel_lse = (float*)c.take(rows * sizeof(float));
   out->vt = c.take(hils::attn_fwd_vt_bytes(d));
   return c.used;
 }
-size_t carve_route(const Dims& d, void* ws, float** qhat) {
+size_t carve_route(const Dims& d, void* ws, RouteWs* rt) {
   Carver c(ws);
-  const size_t rows = (size_t)d.B * d.Hq * d.N;
-  *qhat = d.r > 0 ? (float*)c.take(rows * d.d * sizeof(float)) : nullptr;
+  carve_route_ws(d, c, rt);
   return c.used;
 }
 
@@ -174,6 +187,32 @@ hipError_t timed(int step, hipStream_t st, F&& launch) {
   e = launch();
   if (e != hipSuccess) return e;
   return hipEventRecord(static_cast<hipEvent_t>(r.stop[j]), st);
+}
+
+// Q-Cal and routing of a prefill call (timed as two steps)
+hils_status route_with_qcal(const Dims& d, const RouteWs& w, const void* q, const void* h,
+                            const void* W_down, const void* W_up, const void* kL, const void* e,
+                            int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st) {
+  hils_status s;
+  if (d.r > 0 && hils::route_u_ok(d)) {
+    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, nullptr, w.qhat, st); }))) != HILS_OK)
+      return s;
+    return hip_status(timed(HILS_STEP_ROUTE, st, [&] {
+      hipError_t e2 = hils::launch_route_klp(d, W_up, kL, w.klh, w.kll, st);
+      if (e2 != hipSuccess) return e2;
+      hils::RouteU ru;
+      ru.u = w.qhat;
+      ru.klh = w.klh;
+      ru.kll = w.kll;
+      return hils::launch_route(d, q, false, kL, e, topk_idx, topk_score, sel_lse, st, ru);
+    }));
+  }
+  if (d.r > 0) {
+    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, w.qhat, nullptr, st); }))) != HILS_OK)
+      return s;
+    return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, topk_score, sel_lse, st); }));
+  }
+  return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, sel_lse, st); }));
 }
 
 }  // namespace
@@ -221,8 +260,8 @@ hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes
   const Dims d = dims_of(p);
   switch (op) {
     case HILS_OP_ROUTE: {
-      float* q;
-      *bytes = carve_route(d, nullptr, &q);
+      RouteWs rt;
+      *bytes = carve_route(d, nullptr, &rt);
       return HILS_OK;
     }
     case HILS_OP_FWD: {
@@ -251,17 +290,12 @@ hils_status hils_route(const hils_problem* p, const void* q, const void* kL, con
   kL = or_stand_in(kL, q);
   e = or_stand_in(e, q);
   const Dims d = dims_of(p);
-  float* qhat = nullptr;
-  const size_t need = carve_route(d, nullptr, &qhat);
+  RouteWs rt;
+  const size_t need = carve_route(d, nullptr, &rt);
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
-  carve_route(d, ws, &qhat);
+  carve_route(d, ws, &rt);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d.r > 0) {
-    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
-      return s;
-    return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, qhat, true, kL, e, topk_idx, topk_score, nullptr, st); }));
-  }
-  return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, nullptr, st); }));
+  return route_with_qcal(d, rt, q, h, W_down, W_up, kL, e, topk_idx, topk_score, nullptr, st);
 }
 
 hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, const void* v,
@@ -281,13 +315,7 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
   carve_fwd(d, ws, &w);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d.r > 0) {
-    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, w.qhat, nullptr, st); }))) != HILS_OK)
-      return s;
-    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, w.s_T, w.sel_lse, st); }));
-  } else {
-    s = hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, w.s_T, w.sel_lse, st); }));
-  }
+  s = route_with_qcal(d, w.rt, q, h, W_down, W_up, kL, e, topk_idx, w.s_T, w.sel_lse, st);
   if (s != HILS_OK) return s;
   return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
 }

@@ -24,8 +24,20 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
 // Routing over a prefill sequence: scores every distant chunk, GQA max,
 // top-K. qs: scoring queries ([B, Hq, N, d], fp32 when q_is_f32 else in the
 // input dtype). Writes topk_idx and, if non-null, topk_score.
+// u path of the routing (route_u_ok: bf16, G = 1, r in {32, 64}): qs is the raw
+// query and u = W_down h [B N, Hq r] fp32 (launch_qcal with no q_hat), klh / klo
+// the W_up^T kL planes of launch_route_klp; u == nullptr selects the q_hat path.
+struct RouteU {
+  const float* u = nullptr;
+  const uint16_t* klh = nullptr;
+  const uint16_t* kll = nullptr;
+};
+bool route_u_ok(const Dims& p);
+hipError_t launch_route_klp(const Dims& p, const void* W_up, const void* kL, uint16_t* klh,
+                            uint16_t* kll, hipStream_t st);
 hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void* kL, const void* e,
-                        int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st);
+                        int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st,
+                        const RouteU& ru = RouteU());
 
 // Fused window attention + selected-chunk attention + fusion.
 // vt: workspace for the transposed, token-permuted copy of V (attn_fwd_vt_bytes).

@@ -9,7 +9,8 @@
 // over LDS tiles of 32-deep k steps, with the next step's global loads
 // prefetched into registers while the current one is multiplied. GEMM 2
 // (k = r) reuses the u tile from LDS, split into hi + lo bf16 halves so that
-// the fp32 u keeps ~16 significant bits, and adds q in the epilogue.
+// the fp32 u keeps ~16 significant bits, and adds q in the epilogue. With no
+// q_hat output only u is produced (GEMM 1 alone).
 #include "hils_common.h"
 #include "hils_internal.h"
 
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
   // loaded once per head), u^T the B operand read from LDS and split into hi
   // + lo bf16 halves (fp32 u keeps ~16 significant bits); the q values for
   // the next 16 tokens are fetched while the current ones are multiplied.
+  if (qhat == nullptr) return;  // u only (routing folds W_up into the landmark side)
   const int h0 = c0 / r, nh = min(QT_N / r, Hq - h0);
   const int nks = (r + 31) / 32;
   for (int hl = w; hl < nh; hl += 4) {

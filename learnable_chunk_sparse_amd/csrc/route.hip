@@ -89,12 +89,22 @@ __device__ __forceinline__ void merge_top(uint64_t (&t)[KC], const uint64_t (&n)
     }
 }
 
-template <typename T, typename QT, int G, int DH, int KC>
-__global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
+// UR > 0 (bf16, one head per KV head, Q-Cal rank r = 32 UR): the calibrated
+// query is never formed. Since q_hat . kL = q . kL + u . (W_up^T kL), the A
+// operand is the raw query (exact bf16) followed by the fp32 u = W_down h
+// (hi + lo halves), and the B operand the landmark key followed by the
+// precomputed W_up^T kL (hi + lo planes, k_route_klp): three more products
+// per k step of r, and no fp32 q_hat written or read.
+template <typename T, typename QT, int G, int DH, int KC, int UR>
+__global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                const T* __restrict__ e, int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_score,
                                                float* __restrict__ sel_lse, int N, int C, int Hkv,
-                                               int K, int W, int S, float scale, int ntiles) {
+                                               int K, int W, int S, float scale, int ntiles,
+                                               const float* __restrict__ uq,
+                                               const uint16_t* __restrict__ klh,
+                                               const uint16_t* __restrict__ kll) {
+  static_assert(UR == 0 || (G == 1 && sizeof(T) == 2 && sizeof(QT) == 2), "u path: bf16, G = 1");
   typedef typename Frag<T>::type FT;
   constexpr bool HAS_LO = (sizeof(T) == 2) && (sizeof(QT) == 4);
   constexpr int KS = DH / 32;
@@ -107,6 +117,8 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
   constexpr int NV = TILE_ELEMS / 256 / VEC;
   __shared__ __align__(16) T kl_s[RT_TC * KP];
   __shared__ float e_s[RT_TC];
+  constexpr int URN = UR > 0 ? UR : 1, RR = 32 * URN, RP = RR + 8;
+  __shared__ __align__(16) uint16_t klh_s[UR ? RT_TC * RP : 8], kll_s[UR ? RT_TC * RP : 8];
   __shared__ __align__(16) float sc_s[4][PW][16 + 4];  // per-wave score tile (positions x chunks)
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
@@ -143,6 +155,28 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
       }
     }
   }
+  // u fragments (u path): rows as above, k = the head's r entries of u
+  FT uhi[RB][URN], ulo[RB][URN];
+  if constexpr (UR > 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      int pos = pw0 + 16 * rb + col;
+      pos = pos < N ? pos : N - 1;
+      const float* src = uq + ((size_t)b * N + pos) * (size_t)Hq * RR + (size_t)g * RR + 8 * grp;
+#pragma unroll
+      for (int kr = 0; kr < UR; ++kr) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src + 32 * kr);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + 32 * kr + 4);
+        float x[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        uhi[rb][kr] = pack8<T>(x);
+        const u16x8 hb = __builtin_bit_cast(u16x8, uhi[rb][kr]);
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = x[j] - bf2f(hb[j]);
+        ulo[rb][kr] = pack8<T>(y);
+      }
+    }
+  }
   // selection state: lane p < PW owns position pw0 + p
   const int mypos = pw0 + lane;
   const int mynd = (lane < PW && mypos < N) ? n_distant(mypos, W, S) : 0;
@@ -157,6 +191,7 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
   typedef typename Frag<T>::type VT;
   VT pre[NV > 0 ? NV : 1];
   float pre_e = 0.f;
+  u16x8 preh[URN], prel[URN];  // kL' tile vectors (u path)
   auto fetch = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -173,6 +208,16 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
       }
     }
     if (tid < RT_TC) pre_e = to_f<T>(eg[min(t0 + tid, C - 1)]);
+    if constexpr (UR > 0) {
+#pragma unroll
+      for (int v = 0; v < UR; ++v) {
+        const int el = (tid * UR + v) * 8;
+        const int row = el / RR, cc = el - row * RR;
+        const size_t o = ((size_t)bg * C + min(t0 + row, C - 1)) * RR + cc;
+        preh[v] = *reinterpret_cast<const u16x8*>(klh + o);
+        prel[v] = *reinterpret_cast<const u16x8*>(kll + o);
+      }
+    }
   };
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -188,6 +233,15 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
       }
     }
     if (tid < RT_TC) e_s[tid] = pre_e;
+    if constexpr (UR > 0) {
+#pragma unroll
+      for (int v = 0; v < UR; ++v) {
+        const int el = (tid * UR + v) * 8;
+        const int row = el / RR, cc = el - row * RR;
+        *reinterpret_cast<u16x8*>(klh_s + row * RP + cc) = preh[v];
+        *reinterpret_cast<u16x8*>(kll_s + row * RP + cc) = prel[v];
+      }
+    }
   };
 
   if (nd_wg > 0) fetch(0);
@@ -203,6 +257,15 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
       for (int ks = 0; ks < KS; ++ks)
         bf[ks] = *reinterpret_cast<const FT*>(kl_s + (c0 + col - t0) * KP + 8 * grp + 32 * ks);
       const float ev = e_s[c0 + col - t0];
+      FT kh[URN], kq[URN];
+      if constexpr (UR > 0) {
+#pragma unroll
+        for (int kr = 0; kr < UR; ++kr) {
+          const int o = (c0 + col - t0) * RP + 8 * grp + 32 * kr;
+          kh[kr] = *reinterpret_cast<const FT*>(klh_s + o);
+          kq[kr] = *reinterpret_cast<const FT*>(kll_s + o);
+        }
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 best;
@@ -213,6 +276,14 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
           for (int ks = 0; ks < KS; ++ks) {
             acc = mma16(ahi[rb][hh][ks], bf[ks], acc);
             if constexpr (HAS_LO) acc = mma16(alo[rb][hh][ks], bf[ks], acc);
+          }
+          if constexpr (UR > 0) {
+#pragma unroll
+            for (int kr = 0; kr < UR; ++kr) {
+              acc = mma16(uhi[rb][kr], kh[kr], acc);
+              acc = mma16(uhi[rb][kr], kq[kr], acc);
+              acc = mma16(ulo[rb][kr], kh[kr], acc);
+            }
           }
           if (hh == 0)
             best = acc;
@@ -326,52 +397,125 @@ __global__ __launch_bounds__(256) void k_route(const QT* __restrict__ qs, const 
   }
 }
 
-template <typename T, typename QT, int G, int DH, int KC>
+template <typename T, typename QT, int G, int DH, int KC, int UR>
 static hipError_t route_go(const Dims& p, const void* qs, const void* kL, const void* e,
-                           int32_t* idx, float* sc, float* sl, hipStream_t st) {
+                           int32_t* idx, float* sc, float* sl, const RouteU& ru, hipStream_t st) {
   constexpr int PWG = 4 * 16 * (G >= 4 ? 1 : 4 / G);
   const int ntiles = (p.N + PWG - 1) / PWG;
-  auto kern = k_route<T, QT, G, DH, KC>;
+  auto kern = k_route<T, QT, G, DH, KC, UR>;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), 0, st, (const QT*)qs,
                      (const T*)kL, (const T*)e, idx, sc, sl, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
-                     ntiles);
+                     ntiles, ru.u, ru.klh, ru.kll);
   return hipGetLastError();
 }
 
-template <typename T, typename QT, int G, int DH>
+template <typename T, typename QT, int G, int DH, int UR>
 static hipError_t route_k(const Dims& p, const void* qs, const void* kL, const void* e,
-                          int32_t* idx, float* sc, float* sl, hipStream_t st) {
-  if (p.K <= 4) return route_go<T, QT, G, DH, 4>(p, qs, kL, e, idx, sc, sl, st);
-  if (p.K <= 8) return route_go<T, QT, G, DH, 8>(p, qs, kL, e, idx, sc, sl, st);
-  if (p.K <= 16) return route_go<T, QT, G, DH, 16>(p, qs, kL, e, idx, sc, sl, st);
-  return route_go<T, QT, G, DH, 32>(p, qs, kL, e, idx, sc, sl, st);
+                          int32_t* idx, float* sc, float* sl, const RouteU& ru, hipStream_t st) {
+  if (p.K <= 4) return route_go<T, QT, G, DH, 4, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
+  if (p.K <= 8) return route_go<T, QT, G, DH, 8, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
+  if (p.K <= 16) return route_go<T, QT, G, DH, 16, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
+  return route_go<T, QT, G, DH, 32, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
 }
 
 template <typename T, typename QT, int G>
 static hipError_t route_d(const Dims& p, const void* qs, const void* kL, const void* e, int32_t* idx,
-                          float* sc, float* sl, hipStream_t st) {
-  if (p.d == 64) return route_k<T, QT, G, 64>(p, qs, kL, e, idx, sc, sl, st);
-  return route_k<T, QT, G, 128>(p, qs, kL, e, idx, sc, sl, st);
+                          float* sc, float* sl, const RouteU& ru, hipStream_t st) {
+  if constexpr (G == 1 && sizeof(T) == 2 && sizeof(QT) == 2) {
+    if (ru.u != nullptr) {
+      if (p.d == 64)
+        return p.r == 32 ? route_k<T, QT, G, 64, 1>(p, qs, kL, e, idx, sc, sl, ru, st)
+                         : route_k<T, QT, G, 64, 2>(p, qs, kL, e, idx, sc, sl, ru, st);
+      return p.r == 32 ? route_k<T, QT, G, 128, 1>(p, qs, kL, e, idx, sc, sl, ru, st)
+                       : route_k<T, QT, G, 128, 2>(p, qs, kL, e, idx, sc, sl, ru, st);
+    }
+  }
+  if (p.d == 64) return route_k<T, QT, G, 64, 0>(p, qs, kL, e, idx, sc, sl, ru, st);
+  return route_k<T, QT, G, 128, 0>(p, qs, kL, e, idx, sc, sl, ru, st);
 }
 
 template <typename T, typename QT>
 static hipError_t route_g(const Dims& p, const void* qs, const void* kL, const void* e, int32_t* idx,
-                          float* sc, float* sl, hipStream_t st) {
+                          float* sc, float* sl, const RouteU& ru, hipStream_t st) {
   switch (p.G) {
-    case 1: return route_d<T, QT, 1>(p, qs, kL, e, idx, sc, sl, st);
-    case 2: return route_d<T, QT, 2>(p, qs, kL, e, idx, sc, sl, st);
-    case 4: return route_d<T, QT, 4>(p, qs, kL, e, idx, sc, sl, st);
+    case 1: return route_d<T, QT, 1>(p, qs, kL, e, idx, sc, sl, ru, st);
+    case 2: return route_d<T, QT, 2>(p, qs, kL, e, idx, sc, sl, ru, st);
+    case 4: return route_d<T, QT, 4>(p, qs, kL, e, idx, sc, sl, ru, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void* kL, const void* e,
-                        int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st) {
+                        int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st,
+                        const RouteU& ru) {
+  if (ru.u != nullptr && !route_u_ok(p)) return hipErrorInvalidValue;
   if (p.dtype == 1) {
-    if (q_is_f32) return route_g<uint16_t, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, st);
-    return route_g<uint16_t, uint16_t>(p, qs, kL, e, topk_idx, topk_score, sel_lse, st);
+    if (q_is_f32) return route_g<uint16_t, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, ru, st);
+    return route_g<uint16_t, uint16_t>(p, qs, kL, e, topk_idx, topk_score, sel_lse, ru, st);
   }
-  return route_g<float, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, st);
+  return route_g<float, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, ru, st);
+}
+
+bool route_u_ok(const Dims& p) {
+  return p.dtype == 1 && p.G == 1 && (p.r == 32 || p.r == 64);
+}
+
+// W_up[h]^T kL_c for every (b, query head, chunk): the Q-Cal part of the
+// surrogate score moved onto the landmark side, as bf16 hi + lo planes
+// [B, Hq, C, r] (fp32 sums of exact bf16 products). One workgroup per
+// (b, head, 2048 / r chunks): W_up[h] and the chunks' landmark rows are
+// staged in LDS with coalesced loads, r / 8 lanes share a chunk and each
+// computes 8 of its r outputs.
+template <int DH>
+__global__ __launch_bounds__(256) void k_route_klp(const uint16_t* __restrict__ W_up,
+                                                   const uint16_t* __restrict__ kL,
+                                                   uint16_t* __restrict__ klh,
+                                                   uint16_t* __restrict__ kll, int Hq, int Hkv,
+                                                   int C, int r) {
+  __shared__ float wu[DH * 64];            // W_up[h] [DH][r], r <= 64
+  __shared__ float kt[64 * (DH + 1)];      // landmark rows of the block's chunks
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y, b = bh / Hq, h = bh - b * Hq, g = h / (Hq / Hkv);
+  const int cpb = 2048 / r, c0 = blockIdx.x * cpb;
+  for (int x = tid; x < DH * r; x += 256) wu[x] = bf2f(W_up[(size_t)h * DH * r + x]);
+  const uint16_t* kg = kL + ((size_t)b * Hkv + g) * C * DH;
+  for (int x = tid; x < cpb * DH; x += 256) {
+    const int cl = x / DH, dd = x - cl * DH;
+    kt[cl * (DH + 1) + dd] = bf2f(kg[(size_t)min(c0 + cl, C - 1) * DH + dd]);
+  }
+  __syncthreads();
+  const int lpc = r / 8, cl = tid / lpc, j0 = (tid - cl * lpc) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* kr = kt + cl * (DH + 1);
+#pragma unroll 8
+  for (int dd = 0; dd < DH; ++dd) {
+    const float kv = kr[dd];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[jj] = fmaf(kv, wu[dd * r + j0 + jj], acc[jj]);
+  }
+  const int c = c0 + cl;
+  if (c < C) {
+    const size_t o = (((size_t)b * Hq + h) * C + c) * r + j0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const uint16_t hi = f2bf(acc[jj]);
+      klh[o + jj] = hi;
+      kll[o + jj] = f2bf(acc[jj] - bf2f(hi));
+    }
+  }
+}
+
+hipError_t launch_route_klp(const Dims& p, const void* W_up, const void* kL, uint16_t* klh,
+                            uint16_t* kll, hipStream_t st) {
+  if ((long)p.B * p.Hq * p.C * p.r == 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.C + 2048 / p.r - 1) / (2048 / p.r)), (unsigned)(p.B * p.Hq));
+  if (p.d == 64)
+    hipLaunchKernelGGL(k_route_klp<64>, grid, dim3(256), 0, st, (const uint16_t*)W_up,
+                       (const uint16_t*)kL, klh, kll, p.Hq, p.Hkv, p.C, p.r);
+  else
+    hipLaunchKernelGGL(k_route_klp<128>, grid, dim3(256), 0, st, (const uint16_t*)W_up,
+                       (const uint16_t*)kL, klh, kll, p.Hq, p.Hkv, p.C, p.r);
+  return hipGetLastError();
 }
 
 }  // namespace hils

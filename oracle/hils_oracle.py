@@ -49,6 +49,12 @@ Upstream of step 2, landmark_summary builds kL and e themselves from each
 chunk's landmark query (paperglide, "The HiLS-Attention Mechanism", the
 landmark worked example), with its chain-rule backward landmark_backward.
 
+hope_rotate applies HoPE, the partial rotary position encoding of queries and
+keys (paperglide, "Implementation and Training Recipes"; dev.to, "Engineering
+Details"), ahead of all of the above. The paperglide page also describes HoPE
+as additive embeddings at token and chunk granularity; that reading is not
+the one built (the two other passages agree on partial rotation).
+
 The backward pass is not printed on the pages; it is the chain rule applied
 to steps 1-6 with the selected set held fixed (selection is not
 differentiated), and is pinned by finite differences in the tests.
@@ -477,3 +483,57 @@ def landmark_backward(qL, k, dkL, de, S: int, scale: Optional[float] = None):
                 dqL[b, g, c] = sc * (ds @ Kc)
                 dk[b, g, c * S:(c + 1) * S] = sc * np.outer(ds, qL[b, g, c]) + np.outer(p, dkL[b, g, c])
     return dqL, dk
+
+
+# --------------------------------------------------------------------------
+# HoPE: partial rotary position encoding of queries and keys
+# --------------------------------------------------------------------------
+def hope_theta(d: int, base: float) -> np.ndarray:
+    """Rotary frequencies theta_j = base^(-2j/d), j = 0 .. d/2 - 1 (the
+    standard rotary schedule that HoPE starts from)."""
+    return base ** (-2.0 * np.arange(d // 2) / d)
+
+
+def hope_rotating(d: int, base: float, train_len: int) -> np.ndarray:
+    """Which pairs keep their rotation (paperglide, "Implementation and
+    Training Recipes", HoPE; dev.to, "Engineering Details", Hierarchical
+    Positional Encoding): pair j rotates only if its period 2 pi / theta_j
+    fits the training length; the others carry no position (NoPE)."""
+    return 2.0 * math.pi / hope_theta(d, base) <= train_len
+
+
+def hope_pairs(d: int, interleaved: bool):
+    """Index arrays (a, b) of the rotation pairs: (j, j + d/2) by default,
+    (2j, 2j + 1) when interleaved."""
+    j = np.arange(d // 2)
+    return (2 * j, 2 * j + 1) if interleaved else (j, j + d // 2)
+
+
+def hope_rotate(x, pos=None, base: float = 10000.0, train_len: int = 8192,
+                interleaved: bool = False, inverse: bool = False) -> np.ndarray:
+    """Apply HoPE to x [B, H, N, d] at positions pos [B, N] (default: n).
+
+    Every rotating pair (a, b) of row (b, h, n) is turned by the angle
+    phi = pos * theta_j (by -phi when inverse, the transpose, which carries
+    gradients back):
+      y_a = x_a cos phi - x_b sin phi,  y_b = x_a sin phi + x_b cos phi;
+    NoPE pairs are copied. Returns float64."""
+    x = f64(x)
+    B, H, N, d = x.shape
+    if pos is None:
+        pos = np.broadcast_to(np.arange(N), (B, N))
+    pos = np.asarray(pos, dtype=np.float64)
+    theta = hope_theta(d, base)
+    rot = hope_rotating(d, base, train_len)
+    a, b = hope_pairs(d, interleaved)
+    y = x.copy()
+    sign = -1.0 if inverse else 1.0
+    for bi in range(B):
+        phi = sign * np.outer(pos[bi], theta)            # [N, d/2]
+        c = np.where(rot, np.cos(phi), 1.0)
+        s = np.where(rot, np.sin(phi), 0.0)
+        xa = x[bi][..., a]
+        xb = x[bi][..., b]
+        y[bi][..., a] = xa * c - xb * s
+        y[bi][..., b] = xa * s + xb * c
+    return y

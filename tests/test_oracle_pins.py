@@ -454,3 +454,119 @@ def test_landmark_backward_matches_autograd_and_finite_differences():
         kp = k.copy(); kp[idx] += h
         km = k.copy(); km[idx] -= h
         assert abs((E(qL, kp) - E(qL, km)) / (2 * h) - dk[idx]) < 1e-7
+
+
+# ---------------------------------------------------------------- HoPE
+def _hope_generator(d, thetas, pairs):
+    """Skew-symmetric generator whose exponential turns each listed pair
+    (a, b) by theta * position (counter-clockwise: a towards b)."""
+    A = np.zeros((d, d))
+    for (a, b), t in zip(pairs, thetas):
+        A[b, a] = t
+        A[a, b] = -t
+    return A
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_hope_is_the_exponential_of_its_rotation_generator(interleaved):
+    """d = 8, base 1e4: theta = 1, 0.1, 0.01, 0.001 (10^-j), periods 6.28,
+    62.8, 628, 6283. With a training length of 100 the first two pairs rotate
+    and the last two carry no position. Every row must equal expm(pos A) x,
+    with A built from the hand-written pairs, not from the oracle's tables."""
+    from scipy.linalg import expm
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, 3, 5, 8))
+    pos = rng.integers(0, 5000, size=(2, 5))
+    pairs = [(0, 1), (2, 3), (4, 5), (6, 7)] if interleaved else [(0, 4), (1, 5), (2, 6), (3, 7)]
+    A = _hope_generator(8, [1.0, 0.1, 0.0, 0.0], pairs)
+    y = H.hope_rotate(x, pos, base=1e4, train_len=100, interleaved=interleaved)
+    for b in range(2):
+        for n in range(5):
+            R = expm(pos[b, n] * A)
+            for h in range(3):
+                np.testing.assert_allclose(y[b, h, n], R @ x[b, h, n], rtol=0, atol=1e-9)
+    yi = H.hope_rotate(x, pos, base=1e4, train_len=100, interleaved=interleaved, inverse=True)
+    for b in range(2):
+        for n in range(5):
+            R = expm(-pos[b, n] * A)
+            np.testing.assert_allclose(yi[b, 0, n], R @ x[b, 0, n], rtol=0, atol=1e-9)
+
+
+def test_hope_period_cut_worked_numbers():
+    """d = 64, base 1e4: pair j has period 2 pi 10^(j/8): pair 22 3533.3,
+    pair 23 4711.7, pair 24 6283.19, pair 25 8378.8, pair 31 47117. A
+    training length of 8192 keeps pairs 0 .. 24; 6283 keeps 0 .. 23; 6284
+    keeps 0 .. 24 again; 4096 keeps 0 .. 22."""
+    assert list(H.hope_rotating(64, 1e4, 8192)) == [True] * 25 + [False] * 7
+    assert list(H.hope_rotating(64, 1e4, 6283)) == [True] * 24 + [False] * 8
+    assert list(H.hope_rotating(64, 1e4, 6284)) == [True] * 25 + [False] * 7
+    assert list(H.hope_rotating(64, 1e4, 4096)) == [True] * 23 + [False] * 9
+    assert not H.hope_rotating(64, 1e4, 6).any()        # shortest period 2 pi
+    assert H.hope_rotating(64, 1e4, 47118).all()       # longest 2 pi 10^(31/8)
+
+
+def test_hope_worked_rotation_of_a_unit_vector():
+    """One pair, theta_0 = 1: the unit vector (1, 0) at position p becomes
+    (cos p, sin p); at position 1: (0.5403023058681398, 0.8414709848078965)."""
+    x = np.zeros((1, 1, 3, 2))
+    x[..., 0] = 1.0
+    y = H.hope_rotate(x, None, base=1e4, train_len=10)
+    np.testing.assert_allclose(y[0, 0, 0], [1.0, 0.0], atol=1e-15)
+    np.testing.assert_allclose(y[0, 0, 1], [0.5403023058681398, 0.8414709848078965], atol=1e-15)
+    np.testing.assert_allclose(y[0, 0, 2], [-0.4161468365471424, 0.9092974268256817], atol=1e-15)
+
+
+def test_hope_scores_depend_on_relative_position_only_and_nope_part_on_none():
+    """<R(m) q, R(n) k> is unchanged when both positions shift by the same
+    amount (rotations compose); the NoPE pairs contribute the plain product
+    whatever the positions; nothing rotates below the shortest period."""
+    rng = np.random.default_rng(3)
+    d = 16
+    q = rng.standard_normal((1, 1, 1, d))
+    k = rng.standard_normal((1, 1, 1, d))
+    rot = H.hope_rotating(d, 1e4, 200)
+    assert rot.any() and not rot.all()
+    a, b = H.hope_pairs(d, False)
+    nope = np.concatenate([a[~rot], b[~rot]])
+
+    def score(m, n):
+        return float((H.hope_rotate(q, [[m]], 1e4, 200) * H.hope_rotate(k, [[n]], 1e4, 200)).sum())
+
+    for m, n in [(10, 3), (700, 650), (123456, 100000)]:
+        for s in (1, 17, 4096):
+            assert abs(score(m, n) - score(m + s, n + s)) < 1e-9
+    # positions change the rotating part only
+    qn = H.hope_rotate(q, [[999]], 1e4, 200)
+    np.testing.assert_allclose(qn[..., nope], q[..., nope], rtol=0, atol=0)
+    np.testing.assert_allclose(H.hope_rotate(q, [[999]], 1e4, 5), q, rtol=0, atol=0)
+
+
+def test_hope_inverse_is_the_transpose_and_pairs_keep_their_norm():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 2, 7, 64))
+    y = rng.standard_normal((2, 2, 7, 64))
+    pos = rng.integers(0, 1 << 20, size=(2, 7))
+    for il in (False, True):
+        Rx = H.hope_rotate(x, pos, 1e4, 8192, interleaved=il)
+        np.testing.assert_allclose(H.hope_rotate(Rx, pos, 1e4, 8192, interleaved=il, inverse=True), x,
+                                   rtol=0, atol=1e-12)
+        RTy = H.hope_rotate(y, pos, 1e4, 8192, interleaved=il, inverse=True)
+        assert abs((Rx * y).sum() - (x * RTy).sum()) < 1e-9
+        a, b = H.hope_pairs(64, il)
+        np.testing.assert_allclose(Rx[..., a] ** 2 + Rx[..., b] ** 2, x[..., a] ** 2 + x[..., b] ** 2,
+                                   rtol=1e-12)
+
+
+def test_hope_interleaved_layout_is_a_permutation_of_the_split_layout():
+    """Moving dims (j, j + d/2) to (2j, 2j + 1) maps one convention onto the
+    other."""
+    rng = np.random.default_rng(9)
+    d = 64
+    x = rng.standard_normal((1, 3, 11, d))
+    pos = rng.integers(0, 100000, size=(1, 11))
+    perm = np.empty(d, dtype=int)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2      # interleaved slot -> split dim
+    ys = H.hope_rotate(x, pos, 1e4, 8192)
+    yi = H.hope_rotate(x[..., perm], pos, 1e4, 8192, interleaved=True)
+    np.testing.assert_allclose(yi, ys[..., perm], rtol=0, atol=1e-12)

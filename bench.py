@@ -15,7 +15,8 @@ step of 32 sequences, microseconds per step against the HBM roofline, cold
 last-level cache; also replayed from a HIP graph and over a paged cache), "train" (forward + backward tokens/s) and "landmark" (the
 landmark summary's forward and backward against the HBM roofline) and "packing"
 (chunk-id overlap of adjacent queries and the two forward strategies on
-independent and on position-correlated queries).
+independent and on position-correlated queries) and "hope" (the HoPE rotation
+of the 345M prefill queries and keys against the HBM roofline).
 """
 from __future__ import annotations
 
@@ -429,6 +430,40 @@ def bench_landmark(args, torch, L):
     return out
 
 
+def bench_hope(args, torch, L):
+    """HoPE rotation of the 345M prefill query and key tensors (bf16
+    [4, 16, 8192, 64] each, positions n, training length 8192), in place:
+    an HBM stream that reads and writes every element once."""
+    from workloads import WORKLOADS
+    wl = WORKLOADS["prefill_345m"]
+    g = torch.Generator(device="cuda").manual_seed(7)
+    shape = (wl.B, wl.Hq, wl.N, wl.d)
+    q = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+
+    def step():
+        L.hils_hope(q, None, train_len=wl.N, out=q)
+        L.hils_hope(k, None, train_len=wl.N, out=k)
+
+    for _ in range(max(2, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    ring = event_ring(2 * n, torch)
+    L.hils_set_timing_events(L.STEP_HOPE, *ring)
+    timed_steps(step, n, 0, torch)
+    L.hils_set_timing_events(L.STEP_HOPE)
+    ms = avg_ms(*ring)
+    nbytes = 2 * q.numel() * q.element_size()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"workload": wl.name + " HoPE rotation of q (and k)", "us_per_tensor": ms * 1e3,
+           "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                   "bytes": nbytes}}
+    del q, k
+    torch.cuda.empty_cache()
+    return out
+
+
 def selection_locality(idx, wl, torch):
     """Chunk-id overlap of the selections (the paper's Fig. 7 measures): mean
     |T_i & T_i+1| / K of adjacent rows, and the mean union of the selections of
@@ -503,7 +538,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode timing")
     ap.add_argument("--no-train", action="store_true", help="skip the training (fwd+bwd) leg")
-    ap.add_argument("--legs", default="prefill,decode,train,landmark,packing",
+    ap.add_argument("--legs", default="prefill,decode,train,landmark,packing,hope",
                     help="comma list of legs to run (prefill is always reported)")
     ap.add_argument("--profile-sample", action="store_true",
                     help="run the short fixed sample used for rocprofv3 counter passes and exit")
@@ -528,6 +563,8 @@ def main():
         res["train"] = bench_train(args, torch, L)
     if "landmark" in legs:
         res["landmark"] = bench_landmark(args, torch, L)
+    if "hope" in legs:
+        res["hope"] = bench_hope(args, torch, L)
     if "packing" in legs:
         res["packing"] = bench_packing(args, torch, L)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, args.cpu_budget)

@@ -219,6 +219,40 @@ hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void*
                               void* stream);
 
 /*
+ * HoPE, the partial rotary position encoding of queries and keys (paper:
+ * "Implementation and Training Recipes", HoPE; dev.to summary, "Engineering
+ * Details", Hierarchical Positional Encoding): the rotary frequencies
+ * theta_j = base^(-2j/d), j < d/2, are kept only where the period
+ * 2 pi / theta_j fits the training length; the other pairs carry no position
+ * (NoPE). For row (b, h, n) of x [B, H, N, d] at position p = pos[b, n]
+ * (pos == NULL: p = n) and each rotating pair (a, b):
+ *   y_a = x_a cos(p theta_j) - x_b sin(p theta_j)
+ *   y_b = x_a sin(p theta_j) + x_b cos(p theta_j)
+ * (angle -p theta_j when inverse = 1: the transpose, which maps gradients of
+ * y to gradients of x); NoPE pairs are copied. Pairs are (j, j + d/2), or
+ * (2j, 2j + 1) when interleaved = 1. The angle is reduced to a fraction of a
+ * turn in fp64, the rotation is computed in fp32 and rounded to the dtype.
+ * Apply it to q and k before Q-Cal, routing, the landmark summary and the
+ * attention calls (and its inverse to dq and dk after the backward); decode
+ * rotates the new query at position seq_len - 1.
+ * y may be x (in place); x and y must be 16-byte aligned, pos (int32 [B, N])
+ * holds positions >= 0. B, H or N == 0: nothing to do (x and y may be NULL).
+ * Errors: HILS_ERR_INVALID (null p; null x or y with work to do; negative sizes; base not finite
+ * or <= 1; train_len < 0; flags not 0 / 1; misaligned x or y; more than
+ * 2^31 16-byte units), HILS_ERR_UNSUPPORTED (d not in {64, 128}).
+ */
+typedef struct {
+  int32_t dtype;       /* hils_dtype of x and y */
+  int32_t B, H, N, d;
+  float base;          /* rotary base, e.g. 10000 */
+  int32_t train_len;   /* training context length (tokens) */
+  int32_t interleaved; /* 0: pairs (j, j + d/2); 1: pairs (2j, 2j + 1) */
+  int32_t inverse;     /* 1: rotate by -angle (gradients) */
+} hils_hope_params;
+hils_status hils_hope(const hils_hope_params* p, const void* x, void* y, const int32_t* pos,
+                      void* stream);
+
+/*
  * Forward strategy (a tuning switch, not part of the method; process-wide,
  * like the timing hook). The paper packs adjacent queries against the union of
  * their selected chunks (its Fig. 4 kernel design); both strategies here give
@@ -249,7 +283,8 @@ typedef enum {
   HILS_STEP_BWD = 4,        /* the whole backward */
   HILS_STEP_LANDMARK_FWD = 5, /* landmark summary */
   HILS_STEP_LANDMARK_BWD = 6, /* its backward */
-  HILS_STEP_COUNT = 7
+  HILS_STEP_HOPE = 7,       /* HoPE rotation */
+  HILS_STEP_COUNT = 8
 } hils_step;
 
 /*

@@ -25,10 +25,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
 
 EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
            "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_decode_paged", "hils_landmark_fwd",
-           "hils_landmark_bwd", "hils_set_fwd_strategy", "hils_set_timing_events")
+           "hils_landmark_bwd", "hils_hope", "hils_set_fwd_strategy", "hils_set_timing_events")
 FWD_AUTO, FWD_UNION, FWD_COMPACT = 0, 1, 2
 STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
-STEP_LANDMARK_FWD, STEP_LANDMARK_BWD = 5, 6
+STEP_LANDMARK_FWD, STEP_LANDMARK_BWD, STEP_HOPE = 5, 6, 7
 
 
 class HilsError(RuntimeError):
@@ -43,6 +43,13 @@ class Problem(ctypes.Structure):
                 ("Nk", ctypes.c_int32), ("S", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("W", ctypes.c_int32), ("D", ctypes.c_int32), ("r", ctypes.c_int32),
                 ("qcal_shared", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class HopeParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("base", ctypes.c_float),
+                ("train_len", ctypes.c_int32), ("interleaved", ctypes.c_int32),
+                ("inverse", ctypes.c_int32)]
 
 
 _lib = None
@@ -78,6 +85,8 @@ def lib():
         L.hils_landmark_bwd.restype = ctypes.c_int
         L.hils_landmark_bwd.argtypes = [P] + [vp] * 7
         L.hils_set_fwd_strategy.restype = ctypes.c_int
+        L.hils_hope.argtypes = [ctypes.POINTER(HopeParams), vp, vp, vp, vp]
+        L.hils_hope.restype = ctypes.c_int
         L.hils_set_fwd_strategy.argtypes = [i32]
         L.hils_set_timing_events.restype = ctypes.c_int
         L.hils_set_timing_events.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
@@ -340,6 +349,30 @@ def hils_landmark_bwd(qL, k, dkL, de, S: int, dk=None, scale=0.0):
     _check("hils_landmark_bwd", lib().hils_landmark_bwd(ctypes.byref(p), _ptr(qL), _ptr(k), _ptr(dkL),
                                                         _ptr(de), _ptr(dqL), _ptr(dk), _stream(dev)))
     return dqL, dk
+
+
+def hils_hope(x, pos=None, base: float = 10000.0, train_len: int = 8192, interleaved=False,
+              inverse=False, out=None):
+    """HoPE rotation of x [B, H, N, d] (bf16 or fp32): the rotary pairs whose
+    period 2 pi base^(2j/d) fits train_len turn by pos * theta_j (by minus
+    that when inverse, the transpose used for gradients); the other pairs are
+    copied. pos: int32 [B, N] or None (position n). out may be x (in place);
+    returns out."""
+    _contig(x, pos, out)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    if pos is not None and (pos.dtype != torch.int32 or tuple(pos.shape) != (B, N)):
+        raise ValueError("pos must be int32 [B, N]")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    p = HopeParams(_dtype_code(x), B, H, N, d, float(base), int(train_len), int(bool(interleaved)),
+                   int(bool(inverse)))
+    _check("hils_hope", lib().hils_hope(ctypes.byref(p), _ptr(x), _ptr(out), _ptr(pos),
+                                        _stream(x.device)))
+    return out
 
 
 def hils_set_fwd_strategy(strategy: int):

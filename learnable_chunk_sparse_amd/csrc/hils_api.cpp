@@ -434,4 +434,25 @@ hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void*
   }));
 }
 
+hils_status hils_hope(const hils_hope_params* p, const void* x, void* y, const int32_t* pos,
+                      void* stream) {
+  if (!p) return HILS_ERR_INVALID;
+  if (p->dtype != HILS_FP32 && p->dtype != HILS_BF16) return HILS_ERR_INVALID;
+  if (p->B < 0 || p->H < 0 || p->N < 0 || p->d <= 0) return HILS_ERR_INVALID;
+  if (!std::isfinite(p->base) || !(p->base > 1.f) || p->train_len < 0) return HILS_ERR_INVALID;
+  if ((p->interleaved != 0 && p->interleaved != 1) || (p->inverse != 0 && p->inverse != 1))
+    return HILS_ERR_INVALID;
+  if (p->d != 64 && p->d != 128) return HILS_ERR_UNSUPPORTED;
+  if (p->B == 0 || p->H == 0 || p->N == 0) return HILS_OK;
+  if (!x || !y) return HILS_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) return HILS_ERR_INVALID;
+  const long long units = (long long)p->B * p->N * (p->d / 2) / (p->dtype == HILS_BF16 ? 8 : 4);
+  if (units > 0x7fffff00LL) return HILS_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed(HILS_STEP_HOPE, st, [&] {
+    return hils::launch_hope(p->dtype, p->B, p->H, p->N, p->d, x, y, pos, (double)p->base,
+                             p->train_len, p->interleaved == 1, p->inverse == 1, st);
+  }));
+}
+
 }  // extern "C"

@@ -109,4 +109,9 @@ hipError_t launch_landmark_fwd(const Dims& p, const void* qL, const void* k, voi
 hipError_t launch_landmark_bwd(const Dims& p, const void* qL, const void* k, const float* dkL,
                                const float* de, float* dqL, float* dk, hipStream_t st);
 
+// HoPE rotation of x [B, H, N, d] into y (may alias x); pos [B, N] or null.
+hipError_t launch_hope(int dtype, int B, int H, int N, int d, const void* x, void* y,
+                       const int32_t* pos, double base, int train_len, bool interleaved,
+                       bool inverse, hipStream_t st);
+
 }  // namespace hils

@@ -104,6 +104,32 @@ def test_landmark_calls_reject_before_launch():
         assert lib.hils_landmark_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, null) == code, kw
 
 
+def test_hope_rejects_before_launch_and_empty_is_a_no_op():
+    """hils_hope validates its parameters and returns before any launch; an
+    empty tensor (B, H or N == 0) is a successful no-op."""
+    lib = L.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+
+    def hp(**kw):
+        f = dict(dtype=1, B=2, H=4, N=100, d=64, base=1e4, train_len=8192, interleaved=0, inverse=0)
+        f.update(kw)
+        return L.HopeParams(**f)
+
+    assert lib.hils_hope(None, fake, fake, null, null) == 1
+    assert lib.hils_hope(ctypes.byref(hp()), null, fake, null, null) == 1
+    assert lib.hils_hope(ctypes.byref(hp()), fake, null, null, null) == 1
+    assert lib.hils_hope(ctypes.byref(hp()), ctypes.c_void_p(0x1008), fake, null, null) == 1
+    for kw, code in [(dict(d=96), 2), (dict(d=32), 2), (dict(dtype=3), 1), (dict(B=-1), 1),
+                     (dict(base=1.0), 1), (dict(base=float("nan")), 1), (dict(train_len=-5), 1),
+                     (dict(interleaved=2), 1), (dict(inverse=-1), 1),
+                     (dict(B=1 << 20, N=1 << 20), 1)]:
+        assert lib.hils_hope(ctypes.byref(hp(**kw)), fake, fake, null, null) == code, kw
+    for kw in (dict(B=0), dict(H=0), dict(N=0)):
+        assert lib.hils_hope(ctypes.byref(hp(**kw)), fake, fake, null, null) == 0, kw
+        assert lib.hils_hope(ctypes.byref(hp(**kw)), null, null, null, null) == 0, kw
+
+
 def test_fwd_strategy_switch():
     lib = L.lib()
     try:

@@ -1,0 +1,116 @@
+"""HoPE rotation (hils_hope) against the oracle: both pair layouts, both
+directions, bf16 and fp32, d = 64 and 128, ragged sizes, positions from a
+table up to 2^31 - 1, in place, the decode form (one position per sequence)
+and sampled rows of the 345M prefill query tensor."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hils_oracle as H
+from tests.hils_testutil import TOL, compare, say
+from workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def L():
+    import learnable_chunk_sparse_amd as lib
+    return lib
+
+
+def check(name, got, ref, dt):
+    """The method's tolerance, and for bf16 at most one rounding of the exact
+    value (half an ulp, 2^-9 relative, plus the fp32 arithmetic)."""
+    got = got.cpu().double().numpy()
+    compare(name, got, ref, dt)
+    if dt == "bf16":
+        err = np.abs(got - ref)
+        bound = np.abs(ref) * 2.0 ** -8 + 1e-6
+        assert (err <= bound).all(), f"{name}: {int((err > bound).sum())} values beyond one bf16 rounding"
+
+
+def rand(shape, dt, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(shape, generator=g, dtype=torch.float32)
+    return x.to(torch.bfloat16) if dt == "bf16" else x
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("il", [False, True])
+@pytest.mark.parametrize("inv", [False, True])
+def test_hope_matches_oracle(dt, d, il, inv):
+    lib = L()
+    B, Hh, N = 2, 3, 37
+    say(f"case hope {dt} d={d} interleaved={il} inverse={inv}")
+    x = rand((B, Hh, N, d), dt, 11 + d)
+    g = torch.Generator().manual_seed(5)
+    pos = torch.randint(0, 1 << 24, (B, N), generator=g, dtype=torch.int32)
+    pos[0, :4] = torch.tensor([0, 1, 2 ** 31 - 1, 2 ** 30 + 12345], dtype=torch.int32)
+    for L_train in (8192, 100, 10 ** 7):
+        y = lib.hils_hope(x.cuda(), pos.cuda(), base=10000.0, train_len=L_train, interleaved=il, inverse=inv)
+        y0 = lib.hils_hope(x.cuda(), None, base=500000.0, train_len=L_train, interleaved=il, inverse=inv)
+        torch.cuda.synchronize()
+        ref = H.hope_rotate(x, pos.numpy(), 10000.0, L_train, interleaved=il, inverse=inv)
+        ref0 = H.hope_rotate(x, None, 500000.0, L_train, interleaved=il, inverse=inv)
+        check(f"hope L={L_train}", y, ref, dt)
+        check(f"hope L={L_train} pos=n", y0, ref0, dt)
+        # NoPE pairs are copied bit for bit
+        rot = H.hope_rotating(d, 10000.0, L_train)
+        a, b = H.hope_pairs(d, il)
+        keep = np.concatenate([a[~rot], b[~rot]])
+        assert torch.equal(y.cpu()[..., keep], x[..., keep])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_hope_in_place_and_round_trip(dt):
+    lib = L()
+    say(f"case hope in place {dt}")
+    x = rand((3, 5, 130, 64), dt, 21).cuda()
+    pos = torch.randint(0, 1 << 20, (3, 130), dtype=torch.int32, generator=torch.Generator().manual_seed(2)).cuda()
+    y = lib.hils_hope(x, pos, train_len=4096)
+    z = x.clone()
+    lib.hils_hope(z, pos, train_len=4096, out=z)
+    torch.cuda.synchronize()
+    assert torch.equal(y, z)
+    back = lib.hils_hope(y, pos, train_len=4096, inverse=True)
+    torch.cuda.synchronize()
+    ref = H.hope_rotate(H.hope_rotate(x.cpu(), pos.cpu().numpy(), 1e4, 4096), pos.cpu().numpy(), 1e4, 4096,
+                        inverse=True)
+    np.testing.assert_allclose(ref, x.cpu().double().numpy(), atol=1e-12)
+    # fp32: back = x to rounding; bf16: two roundings
+    compare("round trip", back.cpu().double().numpy(), x.cpu().double().numpy(), dt,
+            dict(max_abs=1e-5, mean_abs=1e-6) if dt == "fp32" else None)
+
+
+def test_hope_decode_form_and_empty():
+    """Decode rotates one new query per sequence at position seq_len - 1;
+    an empty batch is a no-op."""
+    lib = L()
+    say("case hope decode form")
+    q = rand((4, 8, 1, 128), "bf16", 31)
+    seq = torch.tensor([[1], [64], [70000], [524288]], dtype=torch.int32)
+    y = lib.hils_hope(q.cuda(), (seq - 1).cuda(), train_len=32768)
+    torch.cuda.synchronize()
+    check("decode", y, H.hope_rotate(q, (seq - 1).numpy(), 1e4, 32768), "bf16")
+    e = torch.empty((0, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    assert lib.hils_hope(e).shape == e.shape
+
+
+def test_hope_prefill_345m_sampled_rows():
+    """The 345M prefill query tensor [4, 16, 8192, 64] (bf16) at positions n,
+    training length 8192: sampled positions of every (batch, head) against
+    the oracle."""
+    lib = L()
+    wl = WORKLOADS["prefill_345m"]
+    say("case hope prefill_345m sampled rows")
+    x = rand((wl.B, wl.Hq, wl.N, wl.d), "bf16", 41).cuda()
+    y = lib.hils_hope(x, None, train_len=wl.N)
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(0).choice(wl.N, 48, replace=False))
+    idx[:2] = [0, wl.N - 1]
+    idx = np.sort(idx)
+    xs = x[:, :, idx].cpu()
+    pos = np.broadcast_to(idx, (wl.B, len(idx)))
+    ref = H.hope_rotate(xs, pos, 1e4, wl.N)
+    check("prefill_345m rows", y[:, :, idx], ref, "bf16")

@@ -196,8 +196,10 @@ hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* 
  * dtype hils_route, hils_attn_fwd and hils_decode take), and, when non-NULL,
  * the same values in fp32 (kL32, e32). Only dtype, B, Hkv, d, Nk, S and scale
  * of the problem are read (Hq, Nq, K, W, D, r are ignored); no workspace.
+ * qL, k, kL and kL32 must be 16-byte aligned (rows move as 16-byte vectors).
  * Errors: HILS_ERR_INVALID (null qL, k, kL or e; B, Hkv, d or Nk <= 0; bad
- * scale), HILS_ERR_UNSUPPORTED (d not in {64, 128}, S != 64).
+ * scale; a misaligned pointer), HILS_ERR_UNSUPPORTED (d not in {64, 128},
+ * S != 64).
  */
 hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void* k, void* kL,
                               void* e, float* kL32, float* e32, void* stream);
@@ -212,7 +214,7 @@ hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void*
  *           [B, Hkv, Nk, d], e.g. after hils_attn_bwd wrote it; tokens past
  *           C * S are not touched).
  * Same problem fields and errors as hils_landmark_fwd (null dkL, de, dqL or
- * dk is HILS_ERR_INVALID).
+ * dk, or a misaligned qL, k, dkL, dqL or dk, is HILS_ERR_INVALID).
  */
 hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void* k,
                               const float* dkL, const float* de, float* dqL, float* dk,

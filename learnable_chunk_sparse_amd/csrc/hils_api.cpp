@@ -82,6 +82,14 @@ inline bool chunks_ok(const hils_problem* p, const void* a, const void* b) {
   return (p->Nk / p->S) == 0 || (a != nullptr && b != nullptr);
 }
 
+// 16-byte alignment of every non-null pointer (kernels that read or write
+// rows as 16-byte vectors)
+inline bool al16() { return true; }
+template <typename... R>
+inline bool al16(const void* a, R... rest) {
+  return (reinterpret_cast<uintptr_t>(a) & 15) == 0 && al16(rest...);
+}
+
 // Without a complete chunk the kernels still form (and discard, or weight by
 // zero) the landmark row and bias of chunk 0 for empty slots: a NULL kL / e
 // is replaced by another input of the same dtype with at least d finite
@@ -414,6 +422,7 @@ hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void*
   hils_status s = check_landmark(p);
   if (s != HILS_OK) return s;
   if (!k || !chunks_ok(p, qL, qL) || !chunks_ok(p, kL, e)) return HILS_ERR_INVALID;
+  if (!al16(qL, k, kL, kL32)) return HILS_ERR_INVALID;
   const Dims d = landmark_dims(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(timed(HILS_STEP_LANDMARK_FWD, st, [&] {
@@ -427,6 +436,7 @@ hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void*
   hils_status s = check_landmark(p);
   if (s != HILS_OK) return s;
   if (!k || !dk || !chunks_ok(p, qL, dqL) || !chunks_ok(p, dkL, de)) return HILS_ERR_INVALID;
+  if (!al16(qL, k, dkL, dqL, dk)) return HILS_ERR_INVALID;
   const Dims d = landmark_dims(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(timed(HILS_STEP_LANDMARK_BWD, st, [&] {
@@ -445,7 +455,7 @@ hils_status hils_hope(const hils_hope_params* p, const void* x, void* y, const i
   if (p->d != 64 && p->d != 128) return HILS_ERR_UNSUPPORTED;
   if (p->B == 0 || p->H == 0 || p->N == 0) return HILS_OK;
   if (!x || !y) return HILS_ERR_INVALID;
-  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) return HILS_ERR_INVALID;
+  if (!al16(x, y)) return HILS_ERR_INVALID;
   const long long units = (long long)p->B * p->N * (p->d / 2) / (p->dtype == HILS_BF16 ? 8 : 4);
   if (units > 0x7fffff00LL) return HILS_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -12,8 +12,9 @@
 //             dqL  = scale sum_t ds_t k_t
 //             dk_t += scale ds_t qL + p_t dkL
 //
-// One wave per (b, kv head, chunk), up to four independent waves per
-// workgroup (as many as keep the workgroup's LDS under 48 KB). The chunk's 64
+// One wave per (b, kv head, chunk). The forward keeps the chunk's keys in
+// registers (layout below). The backward runs up to four independent waves per
+// workgroup (as many as keep the workgroup's LDS under 48 KB); the chunk's 64
 // keys are staged in LDS in their own type (bf16 keys stay bf16: half the
 // LDS, twice the resident waves), rows padded so that lane t reading row t
 // (scores, dkL . k_t) and lane j reading column j (the key-weighted sums) are
@@ -111,37 +112,105 @@ __device__ __forceinline__ ChunkSoftmax chunk_softmax(const T* kf, const float* 
 }
 }  // namespace
 
+// Forward in registers: lane l holds the 16-byte slices l, l + 64, ... of the
+// chunk's key block (token tl + TPI it, dims part V .. part V + V - 1 with
+// part = l % LPT, tl = l / LPT), so each load round reads 1 KB contiguously.
+// Scores: partial dots (bf16: two-element dot instructions on the raw
+// words, products exact in fp32) reduced over the LPT lanes of a token;
+// softmax statistics and the weighted key sums: reduced over the TPI token
+// groups. One wave per chunk, four chunks per workgroup, no LDS (more chunks
+// per wave, or a loop with the next chunk's loads in flight, measured slower).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_landmark_fwd(const T* __restrict__ qL, const T* __restrict__ k,
                                                      T* __restrict__ kL, T* __restrict__ e,
                                                      float* __restrict__ kL32, float* __restrict__ e32,
                                                      int N, int C, float scale) {
-  constexpr int P = kpitch<T, DH>(), WB = lm_waves<T, DH>();
-  __shared__ __align__(16) T kf_all[WB][LS * P];
-  __shared__ float qs_all[WB][DH], ps_all[WB][LS];
+  constexpr int V = 16 / (int)sizeof(T);  // elements per 16-byte slice
+  constexpr int LPT = DH / V;             // lanes per token row
+  constexpr int TPI = 64 / LPT;           // tokens per load round
+  constexpr int PER = LS / TPI;           // load rounds
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = blockIdx.x * WB + w, bg = blockIdx.y;
+  const int c = blockIdx.x * 4 + w, bg = blockIdx.y;
   if (c >= C) return;  // whole waves; the waves share no data
-  T* kf = kf_all[w];
-  float *qs = qs_all[w], *ps = ps_all[w];
+  const int part = lane % LPT, tl = lane / LPT;
   const size_t cr = (size_t)bg * C + c;  // (b, kv head, chunk)
-  stage_keys<T, DH>(k + ((size_t)bg * N + (size_t)c * LS) * DH, kf, lane);
-  for (int j = lane; j < DH; j += 64) qs[j] = to_f<T>(qL[cr * DH + j]);
-  wave_lds_sync();
-  const ChunkSoftmax r = chunk_softmax<T, DH>(kf, qs, ps, scale, lane);
-  wave_lds_sync();
+  const T* kc = k + ((size_t)bg * N + (size_t)c * LS) * DH + (size_t)tl * DH + part * V;
+  u32x4 raw[PER];
 #pragma unroll
-  for (int j = lane; j < DH; j += 64) {
+  for (int it = 0; it < PER; ++it) raw[it] = *reinterpret_cast<const u32x4*>(kc + (size_t)it * TPI * DH);
+  const u32x4 rq = *reinterpret_cast<const u32x4*>(qL + cr * DH + part * V);
+  auto key = [&](int it, int i) __attribute__((always_inline)) -> float {
+    T tk[V];
+    __builtin_memcpy(tk, &raw[it], 16);
+    return to_f<T>(tk[i]);
+  };
+  float sc[PER];
+  float mx = NEG_INF;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
     float a = 0.f;
-#pragma unroll 16
-    for (int t = 0; t < LS; ++t) a = fmaf(ps[t], to_f<T>(kf[t * P + j]), a);
-    kL[cr * DH + j] = from_f<T>(a);
-    if (kL32 != nullptr) kL32[cr * DH + j] = a;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // (copies: a bit cast of a vector component would read component 0)
+        const uint32_t qi = rq[i], ki = raw[it][i];
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qi),
+                                            __builtin_bit_cast(bf16x2_t, ki), a, false);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) a = fmaf(__uint_as_float(rq[i]), key(it, i), a);
+    }
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) a += __shfl_xor(a, m, 64);
+    sc[it] = a * scale;
+    mx = fmaxf(mx, sc[it]);
   }
-  if (lane == 0) {
-    const float ent = r.logZ - r.sbar;
-    e[cr] = from_f<T>(ent);
-    if (e32 != nullptr) e32[cr] = ent;
+#pragma unroll
+  for (int m = LPT; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  float ex[PER], Z = 0.f;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    ex[it] = expf(sc[it] - mx);
+    Z += ex[it];
+  }
+#pragma unroll
+  for (int m = LPT; m < 64; m <<= 1) Z += __shfl_xor(Z, m, 64);
+  const float rz = 1.f / Z;
+  float acc[V], sbar = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const float p = ex[it] * rz;
+    sbar = fmaf(p, sc[it], sbar);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(p, key(it, i), acc[i]);
+  }
+#pragma unroll
+  for (int m = LPT; m < 64; m <<= 1) {
+    sbar += __shfl_xor(sbar, m, 64);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += __shfl_xor(acc[i], m, 64);
+  }
+  if (tl == 0) {
+    T o[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) o[i] = from_f<T>(acc[i]);
+    u32x4 ov;
+    __builtin_memcpy(&ov, o, 16);
+    *reinterpret_cast<u32x4*>(kL + cr * DH + part * V) = ov;
+    if (kL32 != nullptr) {
+#pragma unroll
+      for (int i = 0; i < V; i += 4)
+        *reinterpret_cast<f32x4*>(kL32 + cr * DH + part * V + i) = f32x4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+    }
+    if (lane == 0) {
+      const float ent = mx + logf(Z) - sbar;
+      e[cr] = from_f<T>(ent);
+      if (e32 != nullptr) e32[cr] = ent;
+    }
   }
 }
 
@@ -209,12 +278,14 @@ hipError_t lm_go(const Dims& p, bool bwd, const void* qL, const void* k, void* k
                  hipStream_t st) {
   constexpr int WB = lm_waves<T, DH>();
   const dim3 grid((unsigned)((p.C + WB - 1) / WB), (unsigned)(p.B * p.Hkv));
-  if (!bwd)
-    hipLaunchKernelGGL((k_landmark_fwd<T, DH>), grid, dim3(64 * WB), 0, st, (const T*)qL, (const T*)k,
-                       (T*)kL, (T*)e, kL32, e32, p.N, p.C, p.scale);
-  else
+  if (!bwd) {
+    hipLaunchKernelGGL((k_landmark_fwd<T, DH>), dim3((unsigned)((p.C + 3) / 4), (unsigned)(p.B * p.Hkv)),
+                       dim3(256), 0, st, (const T*)qL, (const T*)k, (T*)kL, (T*)e, kL32, e32, p.N,
+                       p.C, p.scale);
+  } else {
     hipLaunchKernelGGL((k_landmark_bwd<T, DH>), grid, dim3(64 * WB), 0, st, (const T*)qL, (const T*)k,
                        dkL, de, dqL, dk, p.N, p.C, p.scale);
+  }
   return hipGetLastError();
 }
 

@@ -97,6 +97,10 @@ def test_landmark_calls_reject_before_launch():
     assert lib.hils_landmark_fwd(ctypes.byref(ok), null, fake, fake, fake, null, null, null) == 1
     assert lib.hils_landmark_fwd(ctypes.byref(ok), fake, fake, fake, null, null, null, null) == 1
     assert lib.hils_landmark_bwd(ctypes.byref(ok), fake, fake, fake, fake, fake, null, null) == 1
+    odd = ctypes.c_void_p(0x1004)  # rows move as 16-byte vectors
+    assert lib.hils_landmark_fwd(ctypes.byref(ok), odd, fake, fake, fake, null, null, null) == 1
+    assert lib.hils_landmark_fwd(ctypes.byref(ok), fake, fake, fake, fake, odd, null, null) == 1
+    assert lib.hils_landmark_bwd(ctypes.byref(ok), fake, fake, fake, fake, fake, odd, null) == 1
     for kw, code in [(dict(d=96), 2), (dict(S=32), 2), (dict(B=0), 1), (dict(Nk=0), 1),
                      (dict(scale=float("inf")), 1), (dict(dtype=5), 2)]:
         p = prob(**kw)

@@ -1,7 +1,8 @@
 """HoPE rotation (hils_hope) against the oracle: both pair layouts, both
 directions, bf16 and fp32, d = 64 and 128, ragged sizes, positions from a
-table up to 2^31 - 1, in place, the decode form (one position per sequence)
-and sampled rows of the 345M prefill query tensor."""
+table up to 2^31 - 1, in place, the decode form (one position per sequence),
+sampled rows of the 345M prefill query tensor, and the rotation in its place
+on the path (landmark summary, routing, attention, backward) in fp32."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +115,51 @@ def test_hope_prefill_345m_sampled_rows():
     pos = np.broadcast_to(idx, (wl.B, len(idx)))
     ref = H.hope_rotate(xs, pos, 1e4, wl.N)
     check("prefill_345m rows", y[:, :, idx], ref, "bf16")
+
+
+def test_hope_landmark_attention_chain_forward_and_backward():
+    """The rotation in its place on the path (fp32): q and k rotated, the
+    landmark summary built from the rotated keys, routing and attention on
+    the rotated inputs; backward through attention, the landmark summary
+    (added into dk) and the transposed rotation. Every stage's output against
+    the same chain of oracle functions run on the original inputs."""
+    from tests.hils_testutil import fwd_parity, grad_tol
+    from workloads import Workload, make_inputs, make_landmark_inputs
+    lib = L()
+    Ltr = 512  # pairs 0 .. 15 rotate, 16 .. 31 carry no position
+    wl = Workload("hope_chain", seed=51, dtype="fp32", B=1, Hq=4, Hkv=2, d=64, N=700, S=64, K=4, W=128,
+                  D=64, r=16, e_range=2.0, mode="train")
+    say("case hope + landmark + attention chain (fp32)")
+    t = make_inputs(wl)
+    qL = make_landmark_inputs(wl, keys=False)["qL"]
+    # GPU chain
+    dev = {n: x.cuda() for n, x in t.items() if isinstance(x, torch.Tensor)}
+    q_r = lib.hils_hope(dev["q"], None, train_len=Ltr)
+    k_r = lib.hils_hope(dev["k"], None, train_len=Ltr)
+    kL, e = lib.hils_landmark_fwd(qL.cuda(), k_r, wl.S)
+    out = lib.hils_attn_fwd(q_r, k_r, dev["v"], kL, e, wl.S, wl.K, wl.W, h=dev["h"],
+                            W_down=dev["W_down"], W_up=dev["W_up"])
+    g = lib.hils_attn_bwd(q_r, k_r, dev["v"], kL, e, out[0], out[1], out[2], dev["dO"], wl.S, wl.K,
+                          wl.W, h=dev["h"], W_down=dev["W_down"], W_up=dev["W_up"])
+    dqL, dk_r = lib.hils_landmark_bwd(qL.cuda(), k_r, g["dkL"], g["de"], wl.S, dk=g["dk"])
+    dq = lib.hils_hope(g["dq"], None, train_len=Ltr, inverse=True)
+    dk = lib.hils_hope(dk_r, None, train_len=Ltr, inverse=True)
+    torch.cuda.synchronize()
+    # oracle chain
+    rq = H.hope_rotate(t["q"], None, 1e4, Ltr)
+    rk = H.hope_rotate(t["k"], None, 1e4, Ltr)
+    rkL, re = H.landmark_summary(qL, rk, wl.S)
+    compare("chain q_r", q_r.cpu().double().numpy(), rq, "fp32")
+    compare("chain kL", kL.cpu().double().numpy(), rkL, "fp32")
+    compare("chain e", e.cpu().double().numpy(), re, "fp32")
+    t2 = dict(t)
+    t2.update(q=rq, k=rk, kL=rkL, e=re)
+    fwd_parity(t2, out, wl.S, wl.K, wl.W, "fp32", label="chain fwd")
+    ref = H.hils_backward(t2, t["dO"], wl.S, wl.K, wl.W, forced_topk=out[2].cpu().numpy())
+    rdqL, rdk_lm = H.landmark_backward(qL, rk, ref["dkL"], ref["de"], wl.S)
+    want = {"dq": H.hope_rotate(ref["dq"], None, 1e4, Ltr, inverse=True),
+            "dk": H.hope_rotate(ref["dk"] + rdk_lm, None, 1e4, Ltr, inverse=True),
+            "dv": ref["dv"], "dqL": rdqL, "dW_down": ref["dW_down"], "dW_up": ref["dW_up"]}
+    got = {"dq": dq, "dk": dk, "dv": g["dv"], "dqL": dqL, "dW_down": g["dW_down"], "dW_up": g["dW_up"]}
+    for n in want:
+        compare(f"chain {n}", got[n].cpu().double().numpy(), want[n], "fp32", grad_tol("fp32", want[n]))

@@ -11,7 +11,9 @@ step by step and row by row, in float64 NumPy:
 
   1. Q-Cal (paperglide, "Implementation and Training Recipes", the Q-Cal
      worked example; dev.to, "Engineering Details"): the scoring query is
-     q_hat = q + W_up (W_down h); token-level attention keeps the raw q.
+     q_hat = q + W_up (W_down h); token-level attention keeps the raw q. The
+     pair is per query head, or one pair shared by all heads (W_down [r, D],
+     W_up [d, r]; its gradient is then the sum over the heads).
   2. Surrogate chunk score (paperglide, "The HiLS-Attention Mechanism", the
      worked surrogate-score step and Fig. 3): s_c = q_hat . kL_c / sqrt(d) + e_c
      for every distant chunk, i.e. a complete chunk whose newest token is at
@@ -71,6 +73,15 @@ import numpy as np
 # --------------------------------------------------------------------------
 # helpers
 # --------------------------------------------------------------------------
+def per_head(W, Hq: int):
+    """Q-Cal factors as one matrix per query head: [Hq, a, b] as given, or a
+    single shared [a, b] (one pair for all heads) repeated Hq times."""
+    if W is None:
+        return None
+    W = f64(W)
+    return np.repeat(W[None], Hq, axis=0) if W.ndim == 2 else W
+
+
 def f64(x) -> np.ndarray:
     """Exact upcast of a torch tensor (any dtype) or array to float64 NumPy."""
     if hasattr(x, "detach"):
@@ -251,10 +262,12 @@ class Problem:
         self.kL = f64(t["kL"])
         self.e = f64(t["e"])
         self.h = f64(t["h"]) if t.get("h") is not None else None
-        self.W_down = f64(t["W_down"]) if t.get("W_down") is not None else None
-        self.W_up = f64(t["W_up"]) if t.get("W_up") is not None else None
-        self.S, self.K, self.W = S, K, W
         self.B, self.Hq = self.q.shape[0], self.q.shape[1]
+        # a shared Q-Cal pair ([r, D], [d, r]) is the same matrix for every head
+        self.qcal_shared = t.get("W_down") is not None and f64(t["W_down"]).ndim == 2
+        self.W_down = per_head(t.get("W_down"), self.Hq)
+        self.W_up = per_head(t.get("W_up"), self.Hq)
+        self.S, self.K, self.W = S, K, W
         self.Hkv = self.k.shape[1]
         self.G = self.Hq // self.Hkv
         self.d = self.q.shape[-1]
@@ -351,6 +364,9 @@ def hils_backward(t: dict, dO, S: int, K: int, W: int, scale: Optional[float] = 
                     du = np.einsum("gdr,gd->gr", P.W_up[hs], ddq)
                     dWd[hs] += np.einsum("gr,D->grD", du, P.h[b, i])
                     dh[b, i] += np.einsum("grD,gr->D", P.W_down[hs], du)
+    if qc and P.qcal_shared:
+        # one pair used by every head: its gradient sums the heads' uses
+        dWd, dWu = dWd.sum(axis=0), dWu.sum(axis=0)
     return dict(dq=dq, dk=dk, dv=dv, dkL=dkL, de=de, dW_down=dWd, dW_up=dWu, dh=dh,
                 o=o, lse=lse, topk=topk)
 
@@ -372,6 +388,7 @@ def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
     lse = np.full((B, Hq), np.nan)
     topk = np.full((B, Hkv, K), -2, dtype=np.int64)
     qc = t.get("W_down") is not None
+    Wd, Wu = per_head(t.get("W_down"), Hq), per_head(t.get("W_up"), Hq)
     for b in (range(B) if batches is None else batches):
         n = seq[b]
         i = n - 1
@@ -383,7 +400,7 @@ def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
             kL = f64(t["kL"][b, g, :C])
             e = f64(t["e"][b, g, :C])
             if qc:
-                q_hat, u = qcal(q[b, hs], f64(t["h"][b]), f64(t["W_down"][hs]), f64(t["W_up"][hs]))
+                q_hat, u = qcal(q[b, hs], f64(t["h"][b]), Wd[hs], Wu[hs])
             else:
                 q_hat, u = q[b, hs].copy(), None
             fT = None if forced_topk is None else np.asarray(forced_topk)[b, g]

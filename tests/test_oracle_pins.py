@@ -570,3 +570,60 @@ def test_hope_interleaved_layout_is_a_permutation_of_the_split_layout():
     ys = H.hope_rotate(x, pos, 1e4, 8192)
     yi = H.hope_rotate(x[..., perm], pos, 1e4, 8192, interleaved=True)
     np.testing.assert_allclose(yi, ys[..., perm], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- shared Q-Cal
+def _shared(t, seed):
+    """The same inputs with one Q-Cal pair for all heads (W_down [r, D],
+    W_up [d, r])."""
+    rng = np.random.default_rng(seed)
+    Hq, r, D = t["W_down"].shape
+    d = t["W_up"].shape[1]
+    ts = dict(t)
+    ts["W_down"] = rng.standard_normal((r, D)) * 0.3
+    ts["W_up"] = rng.standard_normal((d, r)) * 0.3
+    return ts
+
+
+def test_shared_qcal_is_the_per_head_form_with_equal_pairs():
+    """Sharing one pair is the per-head form with that pair in every head:
+    prefill outputs, selections, decode, and (gradients of a tied weight) the
+    per-head gradients summed over heads."""
+    S, K, W, N, d = 4, 3, 8, 44, 8
+    t = _shared(small_inputs(3, Hq=4, Hkv=2, N=N, d=d, S=S, qcal=True, e_shift=1.5), 7)
+    tp = dict(t)
+    tp["W_down"] = np.repeat(t["W_down"][None], 4, axis=0)
+    tp["W_up"] = np.repeat(t["W_up"][None], 4, axis=0)
+    dO = rnd(5, 1, 4, N, d)
+    a = H.hils_backward(t, dO, S, K, W)
+    b = H.hils_backward(tp, dO, S, K, W)
+    assert a["dW_down"].shape == t["W_down"].shape and a["dW_up"].shape == t["W_up"].shape
+    np.testing.assert_array_equal(a["topk"], b["topk"])
+    for n in ("o", "lse", "dq", "dk", "dv", "dkL", "de", "dh"):
+        np.testing.assert_allclose(a[n], b[n], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["dW_down"], b["dW_down"].sum(0), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["dW_up"], b["dW_up"].sum(0), rtol=0, atol=1e-12)
+    td = dict(t, q=t["q"][:, :, -1], h=t["h"][:, -1], seq_len=torch.tensor([N]))
+    tdp = dict(tp, q=t["q"][:, :, -1], h=t["h"][:, -1], seq_len=torch.tensor([N]))
+    x, y = H.hils_decode(td, S, K, W), H.hils_decode(tdp, S, K, W)
+    np.testing.assert_allclose(x["o"], y["o"], rtol=0, atol=1e-12)
+
+
+def test_shared_qcal_backward_matches_finite_differences():
+    """Gradients with a shared pair against central differences of the
+    oracle's own forward (the tied weight moves in every head at once)."""
+    S, K, W, N, d = 4, 3, 8, 44, 8
+    t = _shared(small_inputs(11, Hq=4, Hkv=2, N=N, d=d, S=S, qcal=True, e_shift=1.5), 13)
+    dO = rnd(111, 1, 4, N, d)
+    g = H.hils_backward(t, dO, S, K, W)
+    T = g["topk"]
+    rng = np.random.default_rng(11)
+    eps = 1e-6
+    for name, gname in dict(W_down="dW_down", W_up="dW_up", h="dh", q="dq").items():
+        for _ in range(2):
+            u = rng.standard_normal(np.shape(t[name]))
+            tp = dict(t); tp[name] = t[name] + eps * u
+            tm = dict(t); tm[name] = t[name] - eps * u
+            fd = (_loss(tp, dO, S, K, W, T) - _loss(tm, dO, S, K, W, T)) / (2 * eps)
+            an = float((g[gname] * u).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)

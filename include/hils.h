@@ -86,7 +86,9 @@ typedef struct {
                            decode: Nq == 1, Nk = cache capacity */
   int32_t S, K, W;      /* chunk size, top-K (>= 1), window in tokens (>= 1) */
   int32_t D, r;         /* Q-Cal hidden size and rank; r == 0 => no Q-Cal */
-  int32_t qcal_shared;  /* 1 => one (W_down, W_up) pair shared by all heads */
+  int32_t qcal_shared;  /* 1 => one (W_down, W_up) pair shared by all heads:
+                           W_down [r, D], W_up [d, r], dW_down / dW_up the same
+                           shapes (the sum of the heads' gradients); 0 or 1 */
   float scale;          /* 0 => 1/sqrt(d) */
 } hils_problem;
 

@@ -131,7 +131,9 @@ def make_problem(q, k, S, K, W, h=None, W_down=None, scale=0.0, decode=False) ->
     Nq = 1 if decode else q.shape[2]
     r = 0 if W_down is None else W_down.shape[-2]
     D = 0 if h is None else h.shape[-1]
-    return Problem(_dtype_code(q), B, Hq, Hkv, d, Nq, Nk, S, K, W, D, r, 0, float(scale))
+    # W_down [r, D] (and W_up [d, r]): one Q-Cal pair shared by all heads
+    shared = int(W_down is not None and W_down.dim() == 2)
+    return Problem(_dtype_code(q), B, Hq, Hkv, d, Nq, Nk, S, K, W, D, r, shared, float(scale))
 
 
 def workspace_size(p: Problem, op: int) -> int:

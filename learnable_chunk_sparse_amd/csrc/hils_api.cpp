@@ -46,7 +46,7 @@ hils_status check_problem(const hils_problem* p, int op) {
   }
   if (p->d != 64 && p->d != 128) return HILS_ERR_UNSUPPORTED;
   if (p->S != 64) return HILS_ERR_UNSUPPORTED;
-  if (p->qcal_shared != 0) return HILS_ERR_UNSUPPORTED;
+  if (p->qcal_shared != 0 && p->qcal_shared != 1) return HILS_ERR_INVALID;
   const int G = p->Hq / p->Hkv;
   if (!pow2ish_group(G)) return HILS_ERR_UNSUPPORTED;
   if (p->r > 0) {
@@ -164,6 +164,43 @@ size_t carve_route(const Dims& d, void* ws, RouteWs* rt) {
   return c.used;
 }
 
+// One Q-Cal pair shared by all heads (qcal_shared = 1): the per-head kernels
+// read a copy of the pair per head, and the backward's per-head weight
+// gradients are summed over the heads into the caller's [r, D] / [d, r]. The
+// copies and those gradients live in a tail of the workspace, after the op's
+// own scratch.
+struct SharedQcal {
+  void* wd = nullptr;    // [Hq, r, D] in the problem dtype
+  void* wu = nullptr;    // [Hq, d, r]
+  float* dwd = nullptr;  // [Hq, r, D] fp32 (backward)
+  float* dwu = nullptr;  // [Hq, d, r] fp32 (backward)
+};
+size_t shared_tail(const hils_problem* p, const Dims& d, bool bwd, void* tail, SharedQcal* out) {
+  if (p->qcal_shared != 1 || d.r == 0) return 0;
+  Carver c(tail);
+  const size_t es = d.dtype == HILS_BF16 ? 2 : 4;
+  const size_t nd = (size_t)d.r * d.D, nu = (size_t)d.d * d.r;
+  out->wd = c.take(d.Hq * nd * es);
+  out->wu = c.take(d.Hq * nu * es);
+  if (bwd) {
+    out->dwd = static_cast<float*>(c.take(d.Hq * nd * sizeof(float)));
+    out->dwu = static_cast<float*>(c.take(d.Hq * nu * sizeof(float)));
+  }
+  return c.used;
+}
+// per-head copies of a shared pair; W_down / W_up then point at them
+hils_status expand_shared(const Dims& d, const SharedQcal& sq, const void*& W_down,
+                          const void*& W_up, hipStream_t st) {
+  if (sq.wd == nullptr) return HILS_OK;
+  const size_t es = d.dtype == HILS_BF16 ? 2 : 4;
+  if (hils::launch_repeat_heads(W_down, sq.wd, (size_t)d.r * d.D * es, d.Hq, st) != hipSuccess ||
+      hils::launch_repeat_heads(W_up, sq.wu, (size_t)d.d * d.r * es, d.Hq, st) != hipSuccess)
+    return HILS_ERR_HIP;
+  W_down = sq.wd;
+  W_up = sq.wu;
+  return HILS_OK;
+}
+
 hils_status ws_check(void* ws, size_t have, size_t need) {
   if (need > have) return HILS_ERR_WORKSPACE;
   if (need > 0 && (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (ALIGN - 1)) != 0))
@@ -266,24 +303,31 @@ hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes
   hils_status s = check_problem(p, op);
   if (s != HILS_OK) return s;
   const Dims d = dims_of(p);
+  SharedQcal sq;
   switch (op) {
     case HILS_OP_ROUTE: {
       RouteWs rt;
-      *bytes = carve_route(d, nullptr, &rt);
+      *bytes = up(carve_route(d, nullptr, &rt)) + shared_tail(p, d, false, nullptr, &sq);
       return HILS_OK;
     }
     case HILS_OP_FWD: {
       if (!fwd_fits_lds(d)) return HILS_ERR_UNSUPPORTED;
       FwdWs w;
-      *bytes = carve_fwd(d, nullptr, &w);
+      *bytes = up(carve_fwd(d, nullptr, &w)) + shared_tail(p, d, false, nullptr, &sq);
       return HILS_OK;
     }
-    case HILS_OP_BWD:
-      *bytes = hils::bwd_workspace(d);
-      return *bytes == (size_t)-1 ? HILS_ERR_UNSUPPORTED : HILS_OK;
-    case HILS_OP_DECODE:
-      *bytes = hils::decode_workspace(d);
-      return *bytes == (size_t)-1 ? HILS_ERR_UNSUPPORTED : HILS_OK;
+    case HILS_OP_BWD: {
+      const size_t b = hils::bwd_workspace(d);
+      if (b == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+      *bytes = up(b) + shared_tail(p, d, true, nullptr, &sq);
+      return HILS_OK;
+    }
+    case HILS_OP_DECODE: {
+      const size_t b = hils::decode_workspace(d);
+      if (b == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+      *bytes = up(b) + shared_tail(p, d, false, nullptr, &sq);
+      return HILS_OK;
+    }
   }
   return HILS_ERR_INVALID;
 }
@@ -299,10 +343,15 @@ hils_status hils_route(const hils_problem* p, const void* q, const void* kL, con
   e = or_stand_in(e, q);
   const Dims d = dims_of(p);
   RouteWs rt;
-  const size_t need = carve_route(d, nullptr, &rt);
+  SharedQcal sq;
+  const size_t base = up(carve_route(d, nullptr, &rt));
+  const size_t need = base + shared_tail(p, d, false, nullptr, &sq);
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  if (!al16(W_down, W_up)) return HILS_ERR_INVALID;
   carve_route(d, ws, &rt);
+  shared_tail(p, d, false, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   return route_with_qcal(d, rt, q, h, W_down, W_up, kL, e, topk_idx, topk_score, nullptr, st);
 }
 
@@ -319,10 +368,15 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
   const Dims d = dims_of(p);
   if (!fwd_fits_lds(d)) return HILS_ERR_UNSUPPORTED;
   FwdWs w;
-  const size_t need = carve_fwd(d, nullptr, &w);
+  SharedQcal sq;
+  const size_t base = up(carve_fwd(d, nullptr, &w));
+  const size_t need = base + shared_tail(p, d, false, nullptr, &sq);
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  if (!al16(W_down, W_up)) return HILS_ERR_INVALID;
   carve_fwd(d, ws, &w);
+  shared_tail(p, d, false, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   s = route_with_qcal(d, w.rt, q, h, W_down, W_up, kL, e, topk_idx, w.s_T, w.sel_lse, st);
   if (s != HILS_OK) return s;
   return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
@@ -343,13 +397,26 @@ hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, c
   kL = or_stand_in(kL, k);
   e = or_stand_in(e, k);
   const Dims d = dims_of(p);
-  const size_t need = hils::bwd_workspace(d);
-  if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  const size_t b0 = hils::bwd_workspace(d);
+  if (b0 == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  SharedQcal sq;
+  const size_t base = up(b0);
+  const size_t need = base + shared_tail(p, d, true, nullptr, &sq);
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  if (!al16(W_down, W_up)) return HILS_ERR_INVALID;
+  shared_tail(p, d, true, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   return hip_status(timed(HILS_STEP_BWD, st, [&] {
-    return hils::launch_bwd(d, q, k, v, kL, e, h, W_down, W_up, o, lse, topk_idx, dO, dq, dk, dv,
-                            dkL, de, dW_down, dW_up, dh, ws, st);
+    // a shared pair: per-head gradients into the tail, then summed over heads
+    float* gd = sq.dwd ? sq.dwd : dW_down;
+    float* gu = sq.dwu ? sq.dwu : dW_up;
+    hipError_t e2 = hils::launch_bwd(d, q, k, v, kL, e, h, W_down, W_up, o, lse, topk_idx, dO, dq,
+                                     dk, dv, dkL, de, gd, gu, dh, ws, st);
+    if (e2 != hipSuccess || sq.dwd == nullptr) return e2;
+    e2 = hils::launch_sum_heads(sq.dwd, dW_down, (size_t)d.r * d.D, d.Hq, st);
+    if (e2 != hipSuccess) return e2;
+    return hils::launch_sum_heads(sq.dwu, dW_up, (size_t)d.d * d.r, d.Hq, st);
   }));
 }
 
@@ -364,10 +431,16 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
   kL = or_stand_in(kL, k_cache);
   e = or_stand_in(e, k_cache);
   const Dims d = dims_of(p);
-  const size_t need = hils::decode_workspace(d);
-  if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  const size_t b0 = hils::decode_workspace(d);
+  if (b0 == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  SharedQcal sq;
+  const size_t base = up(b0);
+  const size_t need = base + shared_tail(p, d, false, nullptr, &sq);
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  if (!al16(W_down, W_up)) return HILS_ERR_INVALID;
+  shared_tail(p, d, false, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   // the decode workspace starts with the fp32 calibrated queries when Q-Cal is on
   const void* qs = q;
   bool qf32 = d.dtype == HILS_FP32;
@@ -398,10 +471,16 @@ hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* 
   if (p->r > 0 && (!h || !W_down || !W_up)) return HILS_ERR_INVALID;
   if (max_pages <= 0 || (long long)max_pages * p->S != p->Nk) return HILS_ERR_INVALID;
   const Dims d = dims_of(p);
-  const size_t need = hils::decode_workspace(d);
-  if (need == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  const size_t b0 = hils::decode_workspace(d);
+  if (b0 == (size_t)-1) return HILS_ERR_UNSUPPORTED;
+  SharedQcal sq;
+  const size_t base = up(b0);
+  const size_t need = base + shared_tail(p, d, false, nullptr, &sq);
   if ((s = ws_check(ws, ws_bytes, need)) != HILS_OK) return s;
+  if (!al16(W_down, W_up)) return HILS_ERR_INVALID;
+  shared_tail(p, d, false, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   const void* qs = q;
   bool qf32 = d.dtype == HILS_FP32;
   if (d.r > 0) {

@@ -114,4 +114,10 @@ hipError_t launch_hope(int dtype, int B, int H, int N, int d, const void* x, voi
                        const int32_t* pos, double base, int train_len, bool interleaved,
                        bool inverse, hipStream_t st);
 
+// One Q-Cal pair shared by all heads: dst = Hq copies of src (bytes_per_head
+// a multiple of 16); dst[x] = sum over the Hq blocks of n floats of src.
+hipError_t launch_repeat_heads(const void* src, void* dst, size_t bytes_per_head, int Hq,
+                               hipStream_t st);
+hipError_t launch_sum_heads(const float* src, float* dst, size_t n, int Hq, hipStream_t st);
+
 }  // namespace hils

@@ -233,4 +233,38 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
   return deep ? go(k_qcal<float, 128, 4>, float()) : go(k_qcal<float, 128, 1>, float());
 }
 
+// ---------------------------------------------------------------- shared pair
+// One Q-Cal pair for all heads: the per-head kernels read a copy per head
+// (16-byte vectors; blockIdx.y = head), and the per-head weight gradients
+// are summed over the heads afterwards.
+__global__ __launch_bounds__(256) void k_repeat_heads(const u32x4* __restrict__ src,
+                                                      u32x4* __restrict__ dst, long nvec) {
+  const long x = (long)blockIdx.x * 256 + threadIdx.x;
+  if (x < nvec) dst[(long)blockIdx.y * nvec + x] = src[x];
+}
+
+__global__ __launch_bounds__(256) void k_sum_heads(const float* __restrict__ src,
+                                                   float* __restrict__ dst, long n, int Hq) {
+  const long x = (long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  float a = 0.f;
+  for (int h = 0; h < Hq; ++h) a += src[(long)h * n + x];
+  dst[x] = a;
+}
+
+hipError_t launch_repeat_heads(const void* src, void* dst, size_t bytes_per_head, int Hq,
+                               hipStream_t st) {
+  if (bytes_per_head % 16 != 0) return hipErrorInvalidValue;
+  const long nvec = (long)(bytes_per_head / 16);
+  hipLaunchKernelGGL(k_repeat_heads, dim3((unsigned)((nvec + 255) / 256), (unsigned)Hq), dim3(256), 0,
+                     st, (const u32x4*)src, (u32x4*)dst, nvec);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_heads(const float* src, float* dst, size_t n, int Hq, hipStream_t st) {
+  hipLaunchKernelGGL(k_sum_heads, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst,
+                     (long)n, Hq);
+  return hipGetLastError();
+}
+
 }  // namespace hils

@@ -50,12 +50,27 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(Hq=6, Hkv=4), 1), (dict(B=0), 1), (dict(K=0), 1), (dict(Nq=100, Nk=200), 1),
-    (dict(d=96), 2), (dict(S=32), 2), (dict(dtype=7), 2), (dict(qcal_shared=1), 2),
+    (dict(d=96), 2), (dict(S=32), 2), (dict(dtype=7), 2), (dict(qcal_shared=2), 1),
     (dict(r=8), 2), (dict(Hq=16, Hkv=1), 2), (dict(scale=-1.0), 1),
 ])
 def test_validation_codes(kw, code):
     st, _ = ws(prob(**kw), L.OP_FWD)
     assert st == code, (kw, st)
+
+
+def test_shared_qcal_workspace_holds_the_per_head_copies():
+    """qcal_shared = 1: each op's workspace grows by the per-head copies of the
+    pair (and, for the backward, the per-head weight gradients)."""
+    Hq, r, D, d = 16, 32, 1024, 64
+    for op, extra in [(L.OP_ROUTE, 2 * Hq * (r * D + d * r)), (L.OP_FWD, 2 * Hq * (r * D + d * r)),
+                      (L.OP_BWD, (2 + 4) * Hq * (r * D + d * r))]:
+        st0, n0 = ws(prob(), op)
+        st1, n1 = ws(prob(qcal_shared=1), op)
+        assert st0 == 0 and st1 == 0
+        assert extra <= n1 - n0 <= extra + 4 * 256, (op, n1 - n0, extra)
+        st2, n2 = ws(prob(qcal_shared=1, r=0, D=0), op)
+        st3, n3 = ws(prob(r=0, D=0), op)
+        assert n2 == n3  # no Q-Cal: nothing shared
 
 
 def test_fp32_d128_backward_has_a_workspace():

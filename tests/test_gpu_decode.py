@@ -32,7 +32,9 @@ def oracle_ranked(t, b, g, S, K, W):
     kL = H.f64(t["kL"][b, g, :C])
     e = H.f64(t["e"][b, g, :C])
     if t.get("W_down") is not None:
-        qh, _ = H.qcal(q[b, hs], H.f64(t["h"][b]), H.f64(t["W_down"][hs]), H.f64(t["W_up"][hs]))
+        Hq = q.shape[1]
+        qh, _ = H.qcal(q[b, hs], H.f64(t["h"][b]), H.per_head(t["W_down"], Hq)[hs],
+                       H.per_head(t["W_up"], Hq)[hs])
     else:
         qh = q[b, hs]
     nd = H.n_distant(i, W, S)

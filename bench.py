@@ -12,7 +12,8 @@ Prints ONE JSON line: prefill tokens/s, the roofline of the dominant kernel
 the timed region) and the fp64 CPU oracle timed on a bounded sample of the
 same workload. Extra legs in the same line: "decode" (the 512K-context decode
 step of 32 sequences, microseconds per step against the HBM roofline, cold
-last-level cache; also replayed from a HIP graph and over a paged cache), "train" (forward + backward tokens/s) and "landmark" (the
+last-level cache; also replayed from a HIP graph and over a paged cache; and
+the 4M-token single-sequence decode as "long_context"), "train" (forward + backward tokens/s) and "landmark" (the
 landmark summary's forward and backward against the HBM roofline) and "packing"
 (chunk-id overlap of adjacent queries and the two forward strategies on
 independent and on position-correlated queries) and "hope" (the HoPE rotation
@@ -335,6 +336,57 @@ def bench_decode(args, torch, L):
     return out
 
 
+def bench_decode_long(args, torch, L):
+    """The 4M-token decode (one sequence of 4194304 tokens, 16 heads, d = 64,
+    K = 16, W = 512: 65528 distant landmarks per head): µs per step from a
+    cold cache, eager and replayed from a HIP graph, against the HBM roofline
+    of its 0.143 GB of algorithmic bytes."""
+    from workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["decode_4m"]
+    t = make_inputs(wl, device="cuda")
+    bufs = L.decode_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+    flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def step():
+        L.hils_decode(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
+                      seq_len=t["seq_len"], h=t.get("h"), W_down=t.get("W_down"),
+                      W_up=t.get("W_up"), out=bufs)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    n = args.decode_steps
+    st, sp = event_ring(n, torch)
+    L.hils_set_timing_events(L.STEP_DECODE, st, sp)
+    for _ in range(n):
+        torch.sum(flush, dim=0, out=sink)
+        step()
+    torch.cuda.synchronize()
+    L.hils_set_timing_events(L.STEP_DECODE)
+    times = sorted(a.elapsed_time(b) for a, b in zip(st, sp))
+    med = times[len(times) // 2]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    ev = event_ring(n, torch)
+    for j in range(n):
+        torch.sum(flush, dim=0, out=sink)
+        ev[0][j].record()
+        g.replay()
+        ev[1][j].record()
+    torch.cuda.synchronize()
+    tg = sorted(a.elapsed_time(b) for a, b in zip(*ev))
+    nbytes = decode_bytes(wl)
+    gbs = nbytes / (med * 1e-3) / 1e9
+    out = {"workload": wl.name, "us_per_step": med * 1e3, "graph_us_per_step": tg[len(tg) // 2] * 1e3,
+           "median_of": n, "cold_cache": True,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+    del g, t, bufs, flush, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def train_algorithmic_flops(wl):
     """Forward 4*d and backward 10*d flops per (query head, attended token)
     (backward: S, dP, dq, dk and dv products), plus the routing scores."""
@@ -546,7 +598,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode timing")
     ap.add_argument("--no-train", action="store_true", help="skip the training (fwd+bwd) leg")
-    ap.add_argument("--legs", default="prefill,decode,train,landmark,packing,hope",
+    ap.add_argument("--legs", default="prefill,decode,decode_long,train,landmark,packing,hope",
                     help="comma list of legs to run (prefill is always reported)")
     ap.add_argument("--profile-sample", action="store_true",
                     help="run the short fixed sample used for rocprofv3 counter passes and exit")
@@ -567,6 +619,8 @@ def main():
     legs = set(args.legs.split(","))
     if not args.no_decode and "decode" in legs:
         res["decode"] = bench_decode(args, torch, L)
+        if "decode_long" in legs:
+            res["decode"]["long_context"] = bench_decode_long(args, torch, L)
     if not args.no_train and "train" in legs:
         res["train"] = bench_train(args, torch, L)
     if "landmark" in legs:

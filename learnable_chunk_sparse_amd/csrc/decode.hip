@@ -811,15 +811,16 @@ __global__ __launch_bounds__(256) void k_dec_select_window(const float* __restri
 }
 
 // the selected-chunk units: wave x of a (sequence, KV head) takes units x,
-// x + wpg, ... (DEC_NUW of them)
+// x + wpg, ... (NUW of them: two when the batch has units enough to fill the
+// chip, else one per wave, which halves each wave's chain)
 constexpr int DEC_NUW = 2;
-template <typename T, typename QT, int G, int DH, bool PG>
+template <typename T, typename QT, int G, int DH, bool PG, int NUW>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
                                                     const T* __restrict__ k, const T* __restrict__ v,
                                                     const T* __restrict__ kL, const T* __restrict__ e,
                                                     DecArgs a, int wpg) {
   const int x = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (x < wpg) dec_units<T, QT, G, DH, DEC_NUW, PG>(q, qs, k, v, kL, e, a, blockIdx.y, x, wpg);
+  if (x < wpg) dec_units<T, QT, G, DH, NUW, PG>(q, qs, k, v, kL, e, a, blockIdx.y, x, wpg);
 }
 
 // ---------------------------------------------------------------- combine
@@ -945,10 +946,17 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
                      wpb, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
                      (const T*)e, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const int wpg = (p.K + DEC_NUW - 1) / DEC_NUW;
-  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG>), dim3((wpg + 3) / 4, nbg), dim3(256), 0, st,
-                     (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a,
-                     wpg);
+  if ((long)nbg * p.K >= 4096) {
+    const int wpg = (p.K + DEC_NUW - 1) / DEC_NUW;
+    hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG, DEC_NUW>), dim3((wpg + 3) / 4, nbg), dim3(256), 0,
+                       st, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
+                       (const T*)e, a, wpg);
+  } else {
+    const int wpg = p.K;
+    hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG, 1>), dim3((wpg + 3) / 4, nbg), dim3(256), 0, st,
+                       (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e,
+                       a, wpg);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, (const float*)w.pml,
                      (const float*)w.po, (T*)o, lse, p.Hkv, G, w.units);

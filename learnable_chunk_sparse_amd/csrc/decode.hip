@@ -810,12 +810,11 @@ __global__ __launch_bounds__(256) void k_dec_select_window(const float* __restri
   if (u < a.units) dec_units<T, QT, G, DH, 1, PG>(q, qs, k, v, kL, e, a, bg, u, 1);
 }
 
-// the selected-chunk units: wave x of a (sequence, KV head) takes units x,
-// x + wpg, ... (NUW of them: two when the batch has units enough to fill the
-// chip, else one per wave, which halves each wave's chain)
-constexpr int DEC_NUW = 2;
+// the selected-chunk units: wave x of a (sequence, KV head) takes unit x
+// (one per wave: at <= 128 VGPRs four waves per SIMD stay resident, which
+// measured faster than two units per wave at two waves per SIMD)
 template <typename T, typename QT, int G, int DH, bool PG, int NUW>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? (NUW == 1 ? 4 : 2) : 1) void k_dec_chunks(const T* __restrict__ q, const QT* __restrict__ qs,
                                                     const T* __restrict__ k, const T* __restrict__ v,
                                                     const T* __restrict__ kL, const T* __restrict__ e,
                                                     DecArgs a, int wpg) {
@@ -946,17 +945,9 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
                      wpb, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
                      (const T*)e, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((long)nbg * p.K >= 4096) {
-    const int wpg = (p.K + DEC_NUW - 1) / DEC_NUW;
-    hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG, DEC_NUW>), dim3((wpg + 3) / 4, nbg), dim3(256), 0,
-                       st, (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL,
-                       (const T*)e, a, wpg);
-  } else {
-    const int wpg = p.K;
-    hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG, 1>), dim3((wpg + 3) / 4, nbg), dim3(256), 0, st,
-                       (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e,
-                       a, wpg);
-  }
+  hipLaunchKernelGGL((k_dec_chunks<T, QT, G, DH, PG, 1>), dim3((p.K + 3) / 4, nbg), dim3(256), 0, st,
+                     (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a,
+                     p.K);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, (const float*)w.pml,
                      (const float*)w.po, (T*)o, lse, p.Hkv, G, w.units);

@@ -777,9 +777,10 @@ __device__ __forceinline__ void dec_units(const T* __restrict__ q, const QT* __r
 }
 
 // selections (one block per (sequence, KV head)) and, alongside in the same
-// launch, the window units, which do not depend on them
+// launch, the window units, which do not depend on them (bf16: at most 128
+// registers with the accumulators, four waves per SIMD)
 template <typename T, typename QT, int G, int DH, int PER, bool PG>
-__global__ __launch_bounds__(256) void k_dec_select_window(const float* __restrict__ cand_s,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k_dec_select_window(const float* __restrict__ cand_s,
                                                            const int32_t* __restrict__ cand_i,
                                                            int32_t* __restrict__ topk_out, int cstride,
                                                            int Kc, int nbg, int wpb, const T* __restrict__ q,

@@ -123,6 +123,19 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _qcal_shared(W_down, Hq: int, D: int) -> int:
+    """1 for one Q-Cal pair shared by all heads (W_down [r, D]), 0 for a pair
+    per head (W_down [Hq, r, D]); any other shape is an error (the library
+    reads the weights by these shapes)."""
+    if W_down is None:
+        return 0
+    if W_down.dim() == 2 and W_down.shape[1] == D:
+        return 1
+    if W_down.dim() == 3 and W_down.shape[0] == Hq and W_down.shape[2] == D:
+        return 0
+    raise ValueError(f"W_down must be [Hq, r, D] or [r, D] (shared); got {tuple(W_down.shape)}")
+
+
 def make_problem(q, k, S, K, W, h=None, W_down=None, scale=0.0, decode=False) -> Problem:
     B, Hq = q.shape[0], q.shape[1]
     d = q.shape[-1]
@@ -132,7 +145,7 @@ def make_problem(q, k, S, K, W, h=None, W_down=None, scale=0.0, decode=False) ->
     r = 0 if W_down is None else W_down.shape[-2]
     D = 0 if h is None else h.shape[-1]
     # W_down [r, D] (and W_up [d, r]): one Q-Cal pair shared by all heads
-    shared = int(W_down is not None and W_down.dim() == 2)
+    shared = _qcal_shared(W_down, Hq, D)
     return Problem(_dtype_code(q), B, Hq, Hkv, d, Nq, Nk, S, K, W, D, r, shared, float(scale))
 
 
@@ -264,7 +277,8 @@ def hils_decode_paged(q, k_pages, v_pages, page_table, seq_len, kL_pages, e_page
     max_pages = page_table.shape[1]
     r = 0 if W_down is None else W_down.shape[-2]
     D = 0 if h is None else h.shape[-1]
-    p = Problem(_dtype_code(q), B, Hq, Hkv, d, 1, max_pages * S, S, K, W, D, r, 0, float(scale))
+    p = Problem(_dtype_code(q), B, Hq, Hkv, d, 1, max_pages * S, S, K, W, D, r,
+                _qcal_shared(W_down, Hq, D), float(scale))
     dev = q.device
     if out is None:
         o = torch.empty_like(q)

@@ -63,3 +63,21 @@ def test_shared_qcal_decode():
     out = run_decode(wl, to_dev(t))
     torch.cuda.synchronize()
     decode_parity(wl, t, out, [(b, g) for b in range(wl.B) for g in range(wl.Hkv)], "dec_shared")
+
+
+def test_shared_qcal_paged_decode_equals_contiguous():
+    """The paged entry point with a shared pair: bit for bit the contiguous
+    decode, and the oracle."""
+    from tests.test_gpu_paged import run_paged, to_pages
+    wl = Workload("paged_shared", seed=65, dtype="bf16", B=2, Hq=4, Hkv=4, d=64, N=4096, S=64, K=8,
+                  W=256, D=128, r=32, e_range=2.0, e_shift=1.0, mode="decode", seq_len=[4096, 2500])
+    say("case shared Q-Cal paged decode")
+    t = shared(make_inputs(wl))
+    td = to_dev(t)
+    pg = to_pages(td)
+    ref = run_decode(wl, td)
+    got = run_paged(wl, td, pg)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("o", "lse", "topk_idx"), got, ref):
+        assert torch.equal(a, b), f"paged {name} differs from contiguous"
+    decode_parity(wl, t, got, [(b, g) for b in range(wl.B) for g in range(wl.Hkv)], "paged_shared")

@@ -604,7 +604,7 @@ def main():
                     help="run the short fixed sample used for rocprofv3 counter passes and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import learnable_chunk_sparse_amd as L

@@ -31,36 +31,41 @@ constexpr int RT_PAD = 8;   // kL tile row padding (elements)
 }  // namespace
 
 // One lane per position keeps that position's running top-KC (KC >= K) in
-// registers as 64-bit keys, sorted descending: the order-preserving bits of
-// the score above the complement of the chunk id, so that one unsigned
-// comparison orders by (score desc, chunk asc) and 0 lies below every real
-// candidate. Each 16-chunk step's candidates are sorted by a bitonic network
+// registers as keys, sorted descending: the order-preserving bits of the
+// score above the complement of the chunk id, so that one comparison orders
+// by (score desc, chunk asc) and 0 lies below every real candidate. Each 16-chunk step's candidates are sorted by a bitonic network
 // and merged in one pass (a half-cleaner against the current list, then a
 // bitonic merge): ~112 compare-exchanges per step whatever the lanes do,
 // where inserting the candidates one by one costs 16 per candidate and runs
 // for every candidate some lane of the wave keeps. A step is skipped when no
 // lane has a candidate above its K-th key.
-__device__ __forceinline__ uint64_t sel_key(float sc, int c) {
+// The key is that integer held exactly in a double: the order-preserving 32
+// bits of the score times 2^20 plus (2^20 - 1 - chunk), below 2^52 for the
+// at most 2^20 chunks a call may have, so that a compare-exchange is one fp64
+// max and one fp64 min (a 64-bit integer one took a compare, four selects and
+// two hazard waits).
+typedef double Key;
+constexpr double KEY_CH = 1048576.0;  // 2^20: chunk ids below it
+__device__ __forceinline__ Key sel_key(float sc, int c) {
   const uint32_t u = __float_as_uint(sc);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)c;
+  return fma((double)o, KEY_CH, (double)(1048575 - c));
 }
-__device__ __forceinline__ float key_score(uint64_t k) {
-  const uint32_t o = (uint32_t)(k >> 32);
+__device__ __forceinline__ float key_score(Key k) {
+  const uint32_t o = (uint32_t)((uint64_t)k >> 20);
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ int key_chunk(uint64_t k) { return (int)~(uint32_t)k; }
+__device__ __forceinline__ int key_chunk(Key k) { return 1048575 - (int)((uint64_t)k & 0xFFFFFu); }
 
 // a keeps the larger key when desc, the smaller otherwise
-__device__ __forceinline__ void cex(uint64_t& a, uint64_t& b, bool desc) {
-  const bool sw = desc ? (b > a) : (a > b);
-  const uint64_t x = a;
-  a = sw ? b : a;
-  b = sw ? x : b;
+__device__ __forceinline__ void cex(Key& a, Key& b, bool desc) {
+  const Key hi = fmax(a, b), lo = fmin(a, b);
+  a = desc ? hi : lo;
+  b = desc ? lo : hi;
 }
 
 template <int NS>
-__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&a)[NS]) {
+__device__ __forceinline__ void bitonic_sort_desc(Key (&a)[NS]) {
 #pragma unroll
   for (int k = 2; k <= NS; k <<= 1)
 #pragma unroll
@@ -74,11 +79,11 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&a)[NS]) {
 
 // t (KC keys, descending) := the KC largest of t and n (16 keys, descending)
 template <int KC>
-__device__ __forceinline__ void merge_top(uint64_t (&t)[KC], const uint64_t (&n)[16]) {
+__device__ __forceinline__ void merge_top(Key (&t)[KC], const Key (&n)[16]) {
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     const int m = KC - 1 - i;
-    if (m < 16) t[i] = n[m] > t[i] ? n[m] : t[i];
+    if (m < 16) t[i] = fmax(n[m], t[i]);
   }
 #pragma unroll
   for (int j = KC >> 1; j > 0; j >>= 1)
@@ -180,9 +185,9 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
   // selection state: lane p < PW owns position pw0 + p
   const int mypos = pw0 + lane;
   const int mynd = (lane < PW && mypos < N) ? n_distant(mypos, W, S) : 0;
-  uint64_t tk[KC];
+  Key tk[KC];
 #pragma unroll
-  for (int k = 0; k < KC; ++k) tk[k] = 0;
+  for (int k = 0; k < KC; ++k) tk[k] = 0.0;
   const int nd_w = (pw0 < N) ? n_distant(min(pw0 + PW - 1, N - 1), W, S) : 0;
   const int nd_wg = n_distant(min(tile * PWG + PWG - 1, N - 1), W, S);
   const T* kLg = kL + (size_t)bg * C * DH;
@@ -303,18 +308,18 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
           const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
           v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
         }
-        uint64_t thr = tk[KC - 1];
+        Key thr = tk[KC - 1];
         if (K < KC) {
 #pragma unroll
           for (int k = 0; k < KC; ++k) thr = k == K - 1 ? tk[k] : thr;
         }
-        uint64_t nk[16];
+        Key nk[16];
         bool any = false;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          // masked arithmetically: a select here became a branch per candidate
-          const uint64_t live = 0ull - (uint64_t)(c0 + j < mynd);
-          nk[j] = sel_key(v[j], c0 + j) & live;
+          // masked arithmetically (a select here became a branch per
+          // candidate): absent candidates get key 0, below every real one
+          nk[j] = sel_key(v[j], c0 + j) * (double)(c0 + j < mynd);
           any |= nk[j] > thr;
         }
         if (__ballot(any) != 0) {
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
     float sv[KC];
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      ids[k] = (k < K && tk[k] != 0) ? key_chunk(tk[k]) : 0x7FFFFFFF;
+      ids[k] = (k < K && tk[k] != 0.0) ? key_chunk(tk[k]) : 0x7FFFFFFF;
       sv[k] = key_score(tk[k]);
     }
 #pragma unroll
@@ -449,6 +454,7 @@ hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void
                         int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st,
                         const RouteU& ru) {
   if (ru.u != nullptr && !route_u_ok(p)) return hipErrorInvalidValue;
+  if (p.C > (1 << 20)) return hipErrorInvalidValue;  // selection keys hold 20-bit chunk ids
   if (p.dtype == 1) {
     if (q_is_f32) return route_g<uint16_t, float>(p, qs, kL, e, topk_idx, topk_score, sel_lse, ru, st);
     return route_g<uint16_t, uint16_t>(p, qs, kL, e, topk_idx, topk_score, sel_lse, ru, st);

@@ -824,57 +824,77 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (NUW == 1 ? 4 : 2) : 1) void 
 }
 
 // ---------------------------------------------------------------- combine
-// one wave per (sequence, query head): lanes first take units (max, weights),
-// then dims (the weighted sum, eight units' loads in flight at a time)
+// one workgroup per (sequence, query head): wave 0 takes the units' maxima
+// and weights, then the four waves each sum a quarter of the units' outputs
+// (eight units' loads in flight per wave) and wave 0 adds the four parts
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k_dec_combine(const float* __restrict__ pml,
-                                                    const float* __restrict__ po, T* __restrict__ o,
-                                                    float* __restrict__ lse, int Hkv, int G,
-                                                    int units) {
+__global__ __launch_bounds__(256) void k_dec_combine(const float* __restrict__ pml,
+                                                     const float* __restrict__ po, T* __restrict__ o,
+                                                     float* __restrict__ lse, int Hkv, int G,
+                                                     int units) {
   __shared__ float wgt[256];
+  __shared__ float part[4][DH];
+  __shared__ float stat[2];
   const int bh = blockIdx.x;  // b * Hq + h
   const int Hq = Hkv * G;
   const int b = bh / Hq, h = bh - b * Hq;
   const int g = h / G, hh = h - g * G;
   const int bg = b * Hkv + g;
-  const int lane = threadIdx.x;
-  float M = NEG_INF;
-  for (int u = lane; u < units; u += 64) M = fmaxf(M, pml[(((size_t)bg * units + u) * G + hh) * 2]);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w == 0) {
+    float M = NEG_INF;
+    for (int u = lane; u < units; u += 64) M = fmaxf(M, pml[(((size_t)bg * units + u) * G + hh) * 2]);
 #pragma unroll
-  for (int m2 = 32; m2 >= 1; m2 >>= 1) M = fmaxf(M, __shfl_xor(M, m2, 64));
-  float Z = 0.f;
-  for (int u = lane; u < units; u += 64) {
-    const float* p = pml + (((size_t)bg * units + u) * G + hh) * 2;
-    const float m = p[0];
-    const float wu = m == NEG_INF ? 0.f : __expf(m - M);
-    wgt[u] = wu;
-    Z += wu * p[1];
+    for (int m2 = 32; m2 >= 1; m2 >>= 1) M = fmaxf(M, __shfl_xor(M, m2, 64));
+    float Z = 0.f;
+    for (int u = lane; u < units; u += 64) {
+      const float* p = pml + (((size_t)bg * units + u) * G + hh) * 2;
+      const float m = p[0];
+      const float wu = m == NEG_INF ? 0.f : __expf(m - M);
+      wgt[u] = wu;
+      Z += wu * p[1];
+    }
+#pragma unroll
+    for (int m2 = 32; m2 >= 1; m2 >>= 1) Z += __shfl_xor(Z, m2, 64);
+    if (lane == 0) {
+      stat[0] = M;
+      stat[1] = Z;
+    }
   }
-#pragma unroll
-  for (int m2 = 32; m2 >= 1; m2 >>= 1) Z += __shfl_xor(Z, m2, 64);
   __syncthreads();
+  // wave w sums the batches of eight consecutive units starting at 8 w, 8 w + 32, ...
   float acc[DH / 64];
 #pragma unroll
   for (int j = 0; j < DH / 64; ++j) acc[j] = 0.f;
   const float* base = po + ((size_t)bg * units * G + hh) * DH;
-  int u = 0;
-  for (; u + 8 <= units; u += 8) {
+  for (int u = 8 * w; u < units; u += 32) {
     float x[8][DH / 64];
+    // units past the last re-read the last one (in bounds) with weight 0
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t) {
+      const int uc = min(u + t, units - 1);
 #pragma unroll
-      for (int j = 0; j < DH / 64; ++j) x[t][j] = base[(size_t)(u + t) * G * DH + lane + 64 * j];
+      for (int j = 0; j < DH / 64; ++j) x[t][j] = base[(size_t)uc * G * DH + lane + 64 * j];
+    }
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t) {
+      const float wt = u + t < units ? wgt[min(u + t, units - 1)] : 0.f;
 #pragma unroll
-      for (int j = 0; j < DH / 64; ++j) acc[j] = fmaf(wgt[u + t], x[t][j], acc[j]);
+      for (int j = 0; j < DH / 64; ++j) acc[j] = fmaf(wt, x[t][j], acc[j]);
+    }
   }
-  for (; u < units; ++u)
 #pragma unroll
-    for (int j = 0; j < DH / 64; ++j) acc[j] = fmaf(wgt[u], base[(size_t)u * G * DH + lane + 64 * j], acc[j]);
+  for (int j = 0; j < DH / 64; ++j) part[w][lane + 64 * j] = acc[j];
+  __syncthreads();
+  if (w == 0) {
+    const float Z = stat[1];
 #pragma unroll
-  for (int j = 0; j < DH / 64; ++j) o[(size_t)bh * DH + lane + 64 * j] = from_f<T>(acc[j] / Z);
-  if (lane == 0) lse[bh] = M + __logf(Z);
+    for (int j = 0; j < DH / 64; ++j) {
+      const int x = lane + 64 * j;
+      o[(size_t)bh * DH + x] = from_f<T>((part[0][x] + part[1][x] + part[2][x] + part[3][x]) / Z);
+    }
+    if (lane == 0) lse[bh] = stat[0] + __logf(Z);
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -950,7 +970,7 @@ static hipError_t dec_go(const Dims& p, const void* qs, const void* q, const voi
                      (const T*)q, (const QT*)qs, (const T*)k, (const T*)v, (const T*)kL, (const T*)e, a,
                      p.K);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(64), 0, st, (const float*)w.pml,
+  hipLaunchKernelGGL((k_dec_combine<T, DH>), dim3(p.B * p.Hq), dim3(256), 0, st, (const float*)w.pml,
                      (const float*)w.po, (T*)o, lse, p.Hkv, G, w.units);
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@
 //                 columns = chunks), a ring of four 16-chunk steps in flight;
 //                 the max over heads is in-lane. The wave then keeps the top
 //                 min(K, 512) of its 512 scores (by score, then lower index;
-//                 a wave-level radix select in LDS) as candidates, in chunk
+//                 the K-th key found bit by bit from ballots) as candidates, in chunk
 //                 order: every chunk of the overall top-K is among them.
 //   k_dec_select_window
 //                 blocks 0 .. B Hkv - 1: the top-K of one (sequence, KV head)'s
@@ -73,12 +73,12 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
 // those >= nd absent) by (score desc, index asc), written in ascending chunk
 // order to os / oi; slots kc .. Kc-1 get id -1. One wave; lane l holds
 // entries 8l .. 8l + 7 as order-preserving keys; the exact key T of the
-// kc-th best comes from a 4-pass 8-bit radix select over a wave-private
-// LDS histogram, and the first krem keys equal to T (lowest indices) are
-// taken. Any chunk of the overall top-K is in the top-K of its own 512.
+// kc-th best is found bit by bit from the top with wave-wide counts
+// (popcounts of ballots), and the first krem keys equal to T (lowest
+// indices) are taken. Any chunk of the overall top-K is in the top-K of its
+// own 512.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, int nd, int Kc,
-                                          float* __restrict__ os, int32_t* __restrict__ oi,
-                                          int* __restrict__ hist) {
+                                          float* __restrict__ os, int32_t* __restrict__ oi) {
   const int lane = threadIdx.x & 63;
   uint32_t kk[8];
   float sv[8];
@@ -96,44 +96,24 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, 
   const int nv = min(512, nd - c0);
   const int kc = min(Kc, nv);
   const bool all = nv <= kc;
-  uint32_t prefix = 0u, mask = 0u;
+  uint32_t prefix = 0u;
   int krem = kc;
   if (!all) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      *reinterpret_cast<int4*>(hist + 4 * lane) = int4{0, 0, 0, 0};
-      wave_lds_sync();
+    // the kc-th largest key T, bit by bit from the top: the largest T with
+    // #(keys >= T) >= kc, each count a popcount of ballots (no LDS, no
+    // atomics); krem = how many keys equal to T complete the kc
+#pragma unroll 4
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = prefix | (1u << bit);
+      int c = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (kk[i] != 0u && (kk[i] & mask) == prefix) atomicAdd(&hist[(kk[i] >> shift) & 255], 1);
-      wave_lds_sync();
-      const int4 h = *reinterpret_cast<const int4*>(hist + 4 * lane);
-      const int h4[4] = {h.x, h.y, h.z, h.w};
-      const int sum = h4[0] + h4[1] + h4[2] + h4[3];
-      int x = sum;  // sum over lanes >= this one (higher bins rank above)
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(x, o, 64);
-        if (lane + o < 64) x += y;
-      }
-      int above = x - sum, hit_bin = -1, hit_k = 0;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        const int with = above + h4[j];
-        if (above < krem && krem <= with) {
-          hit_bin = 4 * lane + j;
-          hit_k = krem - above;
-        }
-        above = with;
-      }
-      const unsigned long long hb = __ballot(hit_bin >= 0);
-      const int src = __builtin_ctzll(hb);
-      const int bin = __shfl(hit_bin, src, 64);
-      krem = __shfl(hit_k, src, 64);
-      prefix |= (uint32_t)bin << shift;
-      mask |= 255u << shift;
-      wave_lds_sync();
+      for (int i = 0; i < 8; ++i) c += __popcll(__ballot(kk[i] >= t));
+      if (c >= kc) prefix = t;
     }
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) above += __popcll(__ballot(kk[i] > prefix));
+    krem = kc - above;
   }
   const uint32_t T = prefix;
   int ties = 0;
@@ -256,7 +236,6 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   // scores are collected in LDS; the wave then keeps its own top-K as
   // candidates for the selection
   __shared__ __align__(16) float sbuf[4][CPW / 4];
-  __shared__ __align__(16) int whist[4][256];
   float* sw = sbuf[w];
   // fully unrolled, so the waits on the ring are exact (a loop back edge
   // would drain every load in flight)
@@ -284,7 +263,7 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   }
   wave_lds_sync();
   const size_t ob = (size_t)bg * cstride + (size_t)(c_w / (CPW / 4)) * Kc;
-  wave_topk(sw, c_w, nd, Kc, cand_s + ob, cand_i + ob, whist[w]);
+  wave_topk(sw, c_w, nd, Kc, cand_s + ob, cand_i + ob);
 }
 
 // ---------------------------------------------------------------- select

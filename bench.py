@@ -143,6 +143,28 @@ def avg_ms(st, sp):
     return sum(a.elapsed_time(b) for a, b in zip(st, sp)) / len(st)
 
 
+class Recorder:
+    """Rings of (start, stop) events for some library steps: call j of the
+    timed loop passes timing(j), so the library records ring slot j around
+    that call's launches of each step (per call, no library state)."""
+
+    def __init__(self, steps, n, torch):
+        self.n = n
+        self.rings = {sid: event_ring(n, torch) for sid in steps}
+        self.j = 0
+
+    def timing(self):
+        j = self.j % self.n
+        self.j += 1
+        return {sid: (r[0][j], r[1][j]) for sid, r in self.rings.items()}
+
+    def ms(self, sid):
+        return avg_ms(*self.rings[sid])
+
+    def times(self, sid):
+        return [a.elapsed_time(b) for a, b in zip(*self.rings[sid])]
+
+
 def cpu_baseline_prefill(wl, budget_s=12.0):
     """The fp64 oracle on stride-sampled query positions of a few (batch, KV
     group) pairs, run until about budget_s seconds of oracle time, then
@@ -183,21 +205,19 @@ def bench_prefill(args, torch, L, W_):
     t = make_inputs(wl, device="cuda")
     bufs = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
 
+    rec = None
+
     def step():
         L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W, h=t.get("h"),
-                        W_down=t.get("W_down"), W_up=t.get("W_up"), out=bufs)
+                        W_down=t.get("W_down"), W_up=t.get("W_up"), out=bufs,
+                        timing=rec.timing() if rec else None)
 
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
-    rings = {}
-    for sid in (L.STEP_QCAL, L.STEP_ROUTE, L.STEP_ATTN_FWD):
-        rings[sid] = event_ring(args.steps, torch)
-        L.hils_set_timing_events(sid, *rings[sid])
+    rec = Recorder((L.STEP_QCAL, L.STEP_ROUTE, L.STEP_ATTN_FWD), args.steps, torch)
     sec = timed_steps(step, args.steps, 0, torch)
-    for sid in rings:
-        L.hils_set_timing_events(sid)
-    k_ms = {sid: avg_ms(*rings[sid]) for sid in rings}
+    k_ms = {sid: rec.ms(sid) for sid in rec.rings}
     win_f, chk_f = fwd_algorithmic_flops(wl)
     attn_flops = win_f + chk_f
     attn_tf = attn_flops / (k_ms[L.STEP_ATTN_FWD] * 1e-3) / 1e12
@@ -252,22 +272,23 @@ def bench_decode(args, torch, L):
     flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
+    rec = None
+
     def step():
         L.hils_decode(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
                       seq_len=t["seq_len"], h=t.get("h"), W_down=t.get("W_down"),
-                      W_up=t.get("W_up"), out=bufs)
+                      W_up=t.get("W_up"), out=bufs, timing=rec.timing() if rec else None)
 
     for _ in range(max(1, args.warmup)):
         step()
     n = args.decode_steps
-    st, sp = event_ring(n, torch)
-    L.hils_set_timing_events(L.STEP_DECODE, st, sp)
+    rec = Recorder((L.STEP_DECODE,), n, torch)
     for _ in range(n):
         torch.sum(flush, dim=0, out=sink)
         step()
     torch.cuda.synchronize()
-    L.hils_set_timing_events(L.STEP_DECODE)
-    times = sorted(a.elapsed_time(b) for a, b in zip(st, sp))
+    times = sorted(rec.times(L.STEP_DECODE))
+    rec = None
     med = times[len(times) // 2]
     nbytes = decode_bytes(wl)
     gbs = nbytes / (med * 1e-3) / 1e9
@@ -314,20 +335,22 @@ def bench_decode(args, torch, L):
         ep[perm[:, :C]] = t["e"].permute(0, 2, 1)
         ptab = perm.to(torch.int32).contiguous()
 
+        prec = None
+
         def pstep():
             L.hils_decode_paged(t["q"], pages["k"], pages["v"], ptab, t["seq_len"], kLp, ep, wl.S,
                                 wl.K, wl.W, h=t.get("h"), W_down=t.get("W_down"),
-                                W_up=t.get("W_up"), out=bufs)
+                                W_up=t.get("W_up"), out=bufs,
+                                timing=prec.timing() if prec else None)
 
         pstep()
-        st, sp = event_ring(n, torch)
-        L.hils_set_timing_events(L.STEP_DECODE, st, sp)
+        prec = Recorder((L.STEP_DECODE,), n, torch)
         for _ in range(n):
             torch.sum(flush, dim=0, out=sink)
             pstep()
         torch.cuda.synchronize()
-        L.hils_set_timing_events(L.STEP_DECODE)
-        tt = sorted(a.elapsed_time(b) for a, b in zip(st, sp))
+        tt = sorted(prec.times(L.STEP_DECODE))
+        prec = None
         out["paged_us_per_step"] = tt[len(tt) // 2] * 1e3
         out["paged_graph_us_per_step"] = graph_median(pstep)
         del pages, kLp, ep, ptab
@@ -348,22 +371,23 @@ def bench_decode_long(args, torch, L):
     flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
+    rec = None
+
     def step():
         L.hils_decode(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
                       seq_len=t["seq_len"], h=t.get("h"), W_down=t.get("W_down"),
-                      W_up=t.get("W_up"), out=bufs)
+                      W_up=t.get("W_up"), out=bufs, timing=rec.timing() if rec else None)
 
     for _ in range(max(1, args.warmup)):
         step()
     n = args.decode_steps
-    st, sp = event_ring(n, torch)
-    L.hils_set_timing_events(L.STEP_DECODE, st, sp)
+    rec = Recorder((L.STEP_DECODE,), n, torch)
     for _ in range(n):
         torch.sum(flush, dim=0, out=sink)
         step()
     torch.cuda.synchronize()
-    L.hils_set_timing_events(L.STEP_DECODE)
-    times = sorted(a.elapsed_time(b) for a, b in zip(st, sp))
+    times = sorted(rec.times(L.STEP_DECODE))
+    rec = None
     med = times[len(times) // 2]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -401,13 +425,17 @@ def bench_train(args, torch, L):
     t = make_inputs(wl, device="cuda")
     fb = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
     gb = None
+    rec = None
 
     def step():
         nonlocal gb
+        tm = rec.timing() if rec else None
         o, lse, idx = L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
-                                      h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=fb)
+                                      h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=fb,
+                                      timing=tm)
         g = L.hils_attn_bwd(t["q"], t["k"], t["v"], t["kL"], t["e"], o, lse, idx, t["dO"], wl.S,
-                            wl.K, wl.W, h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=gb)
+                            wl.K, wl.W, h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=gb,
+                            timing=tm)
         if gb is None:
             gb = (g, L._workspace(L.make_problem(t["q"], t["k"], wl.S, wl.K, wl.W, t["h"],
                                                  t["W_down"]), L.OP_BWD, t["q"].device))
@@ -416,13 +444,9 @@ def bench_train(args, torch, L):
         step()
     torch.cuda.synchronize()
     n = max(3, args.steps // 2)
-    rings = {sid: event_ring(n, torch) for sid in (L.STEP_ATTN_FWD, L.STEP_BWD)}
-    for sid, r in rings.items():
-        L.hils_set_timing_events(sid, *r)
+    rec = Recorder((L.STEP_ATTN_FWD, L.STEP_BWD), n, torch)
     sec = timed_steps(step, n, 0, torch)
-    for sid in rings:
-        L.hils_set_timing_events(sid)
-    ms = {sid: avg_ms(*r) for sid, r in rings.items()}
+    ms = {sid: rec.ms(sid) for sid in rec.rings}
     fl = train_algorithmic_flops(wl)
     tf = fl / sec / 1e12
     out = {"workload": wl.name, "tokens_per_s": wl.B * wl.N / sec, "ms_per_step": sec * 1e3,
@@ -459,23 +483,22 @@ def bench_landmark(args, torch, L):
     flush = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
+    rec = None
+
     def step():
+        tm = rec.timing() if rec else None
         torch.sum(flush, dim=0, out=sink)
-        L.hils_landmark_fwd(t["qL"], t["k"], wl.S)
+        L.hils_landmark_fwd(t["qL"], t["k"], wl.S, timing=tm)
         torch.sum(flush, dim=0, out=sink)
-        L.hils_landmark_bwd(t["qL"], t["k"], t["dkL"], t["de"], wl.S, dk=dk)
+        L.hils_landmark_bwd(t["qL"], t["k"], t["dkL"], t["de"], wl.S, dk=dk, timing=tm)
 
     for _ in range(max(2, args.warmup)):
         step()
     torch.cuda.synchronize()
     n = max(5, args.steps)
-    rings = {sid: event_ring(n, torch) for sid in (L.STEP_LANDMARK_FWD, L.STEP_LANDMARK_BWD)}
-    for sid, r in rings.items():
-        L.hils_set_timing_events(sid, *r)
+    rec = Recorder((L.STEP_LANDMARK_FWD, L.STEP_LANDMARK_BWD), n, torch)
     timed_steps(step, n, 0, torch)
-    for sid in rings:
-        L.hils_set_timing_events(sid)
-    ms = {sid: avg_ms(*r) for sid, r in rings.items()}
+    ms = {sid: rec.ms(sid) for sid in rec.rings}
     fb, bb = landmark_bytes(wl)
     fg = fb / (ms[L.STEP_LANDMARK_FWD] * 1e-3) / 1e9
     bgs = bb / (ms[L.STEP_LANDMARK_BWD] * 1e-3) / 1e9
@@ -501,19 +524,19 @@ def bench_hope(args, torch, L):
     q = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
     k = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
 
+    rec = None
+
     def step():
-        L.hils_hope(q, None, train_len=wl.N, out=q)
-        L.hils_hope(k, None, train_len=wl.N, out=k)
+        L.hils_hope(q, None, train_len=wl.N, out=q, timing=rec.timing() if rec else None)
+        L.hils_hope(k, None, train_len=wl.N, out=k, timing=rec.timing() if rec else None)
 
     for _ in range(max(2, args.warmup)):
         step()
     torch.cuda.synchronize()
     n = max(5, args.steps)
-    ring = event_ring(2 * n, torch)
-    L.hils_set_timing_events(L.STEP_HOPE, *ring)
+    rec = Recorder((L.STEP_HOPE,), 2 * n, torch)
     timed_steps(step, n, 0, torch)
-    L.hils_set_timing_events(L.STEP_HOPE)
-    ms = avg_ms(*ring)
+    ms = rec.ms(L.STEP_HOPE)
     nbytes = 2 * q.numel() * q.element_size()
     gbs = nbytes / (ms * 1e-3) / 1e9
     out = {"workload": wl.name + " HoPE rotation of q (and k)", "us_per_tensor": ms * 1e3,
@@ -558,29 +581,33 @@ def bench_packing(args, torch, L):
     for name in ("prefill_345m", "prefill_345m_local"):
         wl = WORKLOADS[name]
         t = make_inputs(wl, device="cuda")
-        fb = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+        rec = None
+        strat = L.FWD_AUTO
 
         def step():
+            fb = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"),
+                               strategy=strat) if bufs.get(strat) is None else bufs[strat]
+            bufs[strat] = fb
             return L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
-                                   h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=fb)
+                                   h=t["h"], W_down=t["W_down"], W_up=t["W_up"], out=fb,
+                                   strategy=strat, timing=rec.timing() if rec else None)
 
+        bufs = {}
         r = selection_locality(step()[2], wl, torch)
         for sname, sid in (("union", L.FWD_UNION), ("compact", L.FWD_COMPACT)):
-            L.hils_set_fwd_strategy(sid)
-            try:
-                for _ in range(max(2, args.warmup)):
-                    step()
-                torch.cuda.synchronize()
-                n = max(5, args.steps)
-                ring = event_ring(n, torch)
-                L.hils_set_timing_events(L.STEP_ATTN_FWD, *ring)
-                timed_steps(step, n, 0, torch)
-                L.hils_set_timing_events(L.STEP_ATTN_FWD)
-            finally:
-                L.hils_set_fwd_strategy(L.FWD_AUTO)
-            r[f"attn_ms_{sname}"] = avg_ms(*ring)
+            strat = sid
+            rec = None
+            for _ in range(max(2, args.warmup)):
+                step()
+            torch.cuda.synchronize()
+            n = max(5, args.steps)
+            rec = Recorder((L.STEP_ATTN_FWD,), n, torch)
+            timed_steps(step, n, 0, torch)
+            r[f"attn_ms_{sname}"] = rec.ms(L.STEP_ATTN_FWD)
+            rec = None
+            bufs.pop(sid, None)
         res[name] = r
-        del t, fb
+        del t, bufs
         torch.cuda.empty_cache()
     return res
 

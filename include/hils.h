@@ -19,7 +19,8 @@
  *   and op. The workspace must be 256-byte aligned.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *   and the call returns without synchronising. Calls on different streams
- *   with different workspaces may run concurrently.
+ *   with different workspaces may run concurrently: everything a call uses
+ *   comes through its arguments (the library holds no mutable state).
  * - Validation happens before anything is enqueued and has no side effects.
  *   Errors: HILS_ERR_INVALID (null required pointer, size <= 0, Hq % Hkv != 0,
  *   Nq/Nk inconsistent with the op), HILS_ERR_UNSUPPORTED (a valid problem
@@ -79,6 +80,56 @@ typedef enum { HILS_FP32 = 0, HILS_BF16 = 1 } hils_dtype;
 /* Operation ids for hils_workspace_size. */
 typedef enum { HILS_OP_ROUTE = 0, HILS_OP_FWD = 1, HILS_OP_BWD = 2, HILS_OP_DECODE = 3 } hils_op;
 
+/*
+ * Measurement hook (not part of the method), per call: ids of the launch
+ * steps whose device time a caller can bracket with its own events.
+ */
+typedef enum {
+  HILS_STEP_QCAL = 0,         /* Q-Cal (fp32 calibrated queries, or u) */
+  HILS_STEP_ROUTE = 1,        /* scoring + GQA max + top-K (prefill) */
+  HILS_STEP_ATTN_FWD = 2,     /* window + selected chunks + fusion (prefill) */
+  HILS_STEP_DECODE = 3,       /* the whole decode step after Q-Cal */
+  HILS_STEP_BWD = 4,          /* the whole backward */
+  HILS_STEP_LANDMARK_FWD = 5, /* landmark summary */
+  HILS_STEP_LANDMARK_BWD = 6, /* its backward */
+  HILS_STEP_HOPE = 7,         /* HoPE rotation */
+  HILS_STEP_WINDOW = 8,       /* chunk-major forward: window + fusion launch */
+  HILS_STEP_CHUNKS = 9,       /* chunk-major forward: selected-chunk launch */
+  HILS_STEP_COUNT = 10
+} hils_step;
+
+/*
+ * Caller-owned events (hipEvent_t handles, NULL = not timed) for one call:
+ * a call records start[s] on its stream right before the launches of step s
+ * and stop[s] right after them. The library keeps no pointer past the call.
+ */
+typedef struct {
+  void* start[HILS_STEP_COUNT];
+  void* stop[HILS_STEP_COUNT];
+} hils_timing;
+
+/*
+ * Forward strategy (how the prefill forward is scheduled, not what it
+ * computes; every strategy gives the same per-query result):
+ *   HILS_FWD_AUTO (0)        chosen by shape;
+ *   HILS_FWD_UNION (1)       packed union (the paper's Fig. 4 kernel design):
+ *                            a tile of adjacent queries streams the union of
+ *                            their selected chunks through LDS once;
+ *   HILS_FWD_COMPACT (2)     per query tile, each selected chunk's rows are
+ *                            packed into dense row blocks;
+ *   HILS_FWD_CHUNK_MAJOR (3) chunk-major: every selected chunk is loaded once
+ *                            and serves all the rows that selected it; the
+ *                            per-chunk outputs are fused with the window's in
+ *                            a second pass (for long sequences, where adjacent
+ *                            queries share few chunks).
+ */
+typedef enum {
+  HILS_FWD_AUTO = 0,
+  HILS_FWD_UNION = 1,
+  HILS_FWD_COMPACT = 2,
+  HILS_FWD_CHUNK_MAJOR = 3
+} hils_fwd_strategy;
+
 typedef struct {
   int32_t dtype;        /* hils_dtype of q, k, v, kL, e, h, W_down, W_up, o, dO */
   int32_t B, Hq, Hkv, d;
@@ -90,6 +141,9 @@ typedef struct {
                            W_down [r, D], W_up [d, r], dW_down / dW_up the same
                            shapes (the sum of the heads' gradients); 0 or 1 */
   float scale;          /* 0 => 1/sqrt(d) */
+  int32_t fwd_strategy; /* hils_fwd_strategy of the prefill forward (0 = auto);
+                           hils_workspace_size(HILS_OP_FWD) sizes for it */
+  const hils_timing* timing; /* NULL, or events to record around this call's steps */
 } hils_problem;
 
 /* Text for a status code (static storage). */
@@ -252,56 +306,10 @@ typedef struct {
   int32_t train_len;   /* training context length (tokens) */
   int32_t interleaved; /* 0: pairs (j, j + d/2); 1: pairs (2j, 2j + 1) */
   int32_t inverse;     /* 1: rotate by -angle (gradients) */
+  const hils_timing* timing; /* NULL, or events around the rotation (HILS_STEP_HOPE) */
 } hils_hope_params;
 hils_status hils_hope(const hils_hope_params* p, const void* x, void* y, const int32_t* pos,
                       void* stream);
-
-/*
- * Forward strategy (a tuning switch, not part of the method; process-wide,
- * like the timing hook). The paper packs adjacent queries against the union of
- * their selected chunks (its Fig. 4 kernel design); both strategies here give
- * the same per-query result:
- *   HILS_FWD_AUTO (0)    chosen by shape (default): packed union when a
- *                        128-row tile selects at least 4 slots per candidate
- *                        chunk, compacted otherwise;
- *   HILS_FWD_UNION (1)   packed union: a tile's rows stream the union of their
- *                        selected chunks through LDS once, rows that did not
- *                        select a chunk add it with weight zero;
- *   HILS_FWD_COMPACT (2) compacted: each chunk's selecting rows are packed into
- *                        dense 16-row blocks and only those are computed.
- * Applies to later hils_attn_fwd calls (and their LDS checks); returns
- * HILS_ERR_INVALID for any other value.
- */
-typedef enum { HILS_FWD_AUTO = 0, HILS_FWD_UNION = 1, HILS_FWD_COMPACT = 2 } hils_fwd_strategy;
-hils_status hils_set_fwd_strategy(int32_t strategy);
-
-/*
- * Measurement hook (not part of the method): ids of the launch steps whose
- * device time can be recorded with caller-owned events.
- */
-typedef enum {
-  HILS_STEP_QCAL = 0,       /* Q-Cal (fp32 calibrated queries) */
-  HILS_STEP_ROUTE = 1,      /* scoring + GQA max + top-K (prefill) */
-  HILS_STEP_ATTN_FWD = 2,   /* window + selected chunks + fusion (prefill) */
-  HILS_STEP_DECODE = 3,     /* the whole decode step after Q-Cal */
-  HILS_STEP_BWD = 4,        /* the whole backward */
-  HILS_STEP_LANDMARK_FWD = 5, /* landmark summary */
-  HILS_STEP_LANDMARK_BWD = 6, /* its backward */
-  HILS_STEP_HOPE = 7,       /* HoPE rotation */
-  HILS_STEP_COUNT = 8
-} hils_step;
-
-/*
- * Registers a ring of n (start, stop) event pairs (hipEvent_t handles created
- * by the caller, n >= 1) for step `step`: every later launch of that step
- * records start[j] before and stop[j] after it on the call's stream, with j
- * cycling 0, 1, ..., n-1, 0, ... from the registration on. n == 0 or NULL
- * arrays unregister. The handles are borrowed (the caller keeps them alive
- * while registered). Process-wide state: meant for benchmarks, not for
- * concurrent use from several threads. Returns HILS_ERR_INVALID for a bad
- * step id or n < 0.
- */
-hils_status hils_set_timing_events(int32_t step, void* const* start, void* const* stop, int32_t n);
 
 #ifdef __cplusplus
 }

@@ -728,13 +728,11 @@ static hipError_t vt_go(const Dims& p, const void* v, void* vt, int Np, hipStrea
 // streamed chunks would serve a single row block, and the bucketed kernel
 // (rows of a chunk packed into dense row blocks, chunks taken by waves
 // independently) does less work.
-// forced strategy: 0 chooses by the rule above, 1 shared block, 2 bucketed
-static int g_fwd_strategy = 0;
-void set_fwd_strategy(int s) { g_fwd_strategy = s; }
-
+// The caller's strategy (Dims::fwd_strategy): 0 chooses by the rule above,
+// 1 shared block, 2 bucketed.
 static bool fwd_use_shared(const Dims& p) {
-  if (g_fwd_strategy == 1) return true;
-  if (g_fwd_strategy == 2) return false;
+  if (p.fwd_strategy == 1) return true;
+  if (p.fwd_strategy == 2) return false;
   const long tp = 128 / p.G;
   return tp * p.K >= 4L * p.C;
 }

@@ -47,6 +47,7 @@ hils_status check_problem(const hils_problem* p, int op) {
   if (p->d != 64 && p->d != 128) return HILS_ERR_UNSUPPORTED;
   if (p->S != 64) return HILS_ERR_UNSUPPORTED;
   if (p->qcal_shared != 0 && p->qcal_shared != 1) return HILS_ERR_INVALID;
+  if (p->fwd_strategy < HILS_FWD_AUTO || p->fwd_strategy > HILS_FWD_CHUNK_MAJOR) return HILS_ERR_INVALID;
   const int G = p->Hq / p->Hkv;
   if (!pow2ish_group(G)) return HILS_ERR_UNSUPPORTED;
   if (p->r > 0) {
@@ -125,6 +126,7 @@ Dims dims_of(const hils_problem* p) {
   d.D = p->D;
   d.r = p->r;
   d.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->d);
+  d.fwd_strategy = p->fwd_strategy;
   return d;
 }
 
@@ -210,39 +212,34 @@ hils_status ws_check(void* ws, size_t have, size_t need) {
 
 hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
 
-bool fwd_fits_lds(const Dims& d) { return hils::attn_fwd_lds_bytes(d) <= 160 * 1024; }
+bool fwd_fits_lds(const Dims& d) {
+  if (d.fwd_strategy == HILS_FWD_CHUNK_MAJOR) return false;  // not built yet
+  return hils::attn_fwd_lds_bytes(d) <= 160 * 1024;
+}
 
 // ---------------------------------------------------------------- timing hook
-struct EventRing {
-  void* const* start = nullptr;
-  void* const* stop = nullptr;
-  int n = 0;
-  int next = 0;
-};
-EventRing g_rings[HILS_STEP_COUNT];
-
+// events of the caller's hils_timing (per call; NULL = none) around step's launches
 template <typename F>
-hipError_t timed(int step, hipStream_t st, F&& launch) {
-  EventRing& r = g_rings[step];
-  if (r.n <= 0) return launch();
-  const int j = r.next;
-  r.next = (r.next + 1) % r.n;
-  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(r.start[j]), st);
+hipError_t timed(const hils_timing* tm, int step, hipStream_t st, F&& launch) {
+  void* a = tm ? tm->start[step] : nullptr;
+  void* b = tm ? tm->stop[step] : nullptr;
+  if (a == nullptr || b == nullptr) return launch();
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(a), st);
   if (e != hipSuccess) return e;
   e = launch();
   if (e != hipSuccess) return e;
-  return hipEventRecord(static_cast<hipEvent_t>(r.stop[j]), st);
+  return hipEventRecord(static_cast<hipEvent_t>(b), st);
 }
 
 // Q-Cal and routing of a prefill call (timed as two steps)
-hils_status route_with_qcal(const Dims& d, const RouteWs& w, const void* q, const void* h,
+hils_status route_with_qcal(const hils_timing* tm, const Dims& d, const RouteWs& w, const void* q, const void* h,
                             const void* W_down, const void* W_up, const void* kL, const void* e,
                             int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st) {
   hils_status s;
   if (d.r > 0 && hils::route_u_ok(d)) {
-    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, nullptr, w.qhat, st); }))) != HILS_OK)
+    if ((s = hip_status(timed(tm, HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, nullptr, w.qhat, st); }))) != HILS_OK)
       return s;
-    return hip_status(timed(HILS_STEP_ROUTE, st, [&] {
+    return hip_status(timed(tm, HILS_STEP_ROUTE, st, [&] {
       hipError_t e2 = hils::launch_route_klp(d, W_up, kL, w.klh, w.kll, st);
       if (e2 != hipSuccess) return e2;
       hils::RouteU ru;
@@ -253,11 +250,11 @@ hils_status route_with_qcal(const Dims& d, const RouteWs& w, const void* q, cons
     }));
   }
   if (d.r > 0) {
-    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, w.qhat, nullptr, st); }))) != HILS_OK)
+    if ((s = hip_status(timed(tm, HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, d.N, q, h, W_down, W_up, w.qhat, nullptr, st); }))) != HILS_OK)
       return s;
-    return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, topk_score, sel_lse, st); }));
+    return hip_status(timed(tm, HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, w.qhat, true, kL, e, topk_idx, topk_score, sel_lse, st); }));
   }
-  return hip_status(timed(HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, sel_lse, st); }));
+  return hip_status(timed(tm, HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, sel_lse, st); }));
 }
 
 }  // namespace
@@ -276,26 +273,6 @@ const char* hils_status_string(hils_status s) {
 }
 
 int32_t hils_version(void) { return 100; }
-
-hils_status hils_set_fwd_strategy(int32_t strategy) {
-  if (strategy < HILS_FWD_AUTO || strategy > HILS_FWD_COMPACT) return HILS_ERR_INVALID;
-  hils::set_fwd_strategy(strategy);
-  return HILS_OK;
-}
-
-hils_status hils_set_timing_events(int32_t step, void* const* start, void* const* stop, int32_t n) {
-  if (step < 0 || step >= HILS_STEP_COUNT || n < 0) return HILS_ERR_INVALID;
-  EventRing& r = g_rings[step];
-  if (n == 0 || start == nullptr || stop == nullptr) {
-    r = EventRing();
-    return HILS_OK;
-  }
-  r.start = start;
-  r.stop = stop;
-  r.n = n;
-  r.next = 0;
-  return HILS_OK;
-}
 
 hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes) {
   if (bytes == nullptr) return HILS_ERR_INVALID;
@@ -352,7 +329,7 @@ hils_status hils_route(const hils_problem* p, const void* q, const void* kL, con
   shared_tail(p, d, false, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
-  return route_with_qcal(d, rt, q, h, W_down, W_up, kL, e, topk_idx, topk_score, nullptr, st);
+  return route_with_qcal(p->timing, d, rt, q, h, W_down, W_up, kL, e, topk_idx, topk_score, nullptr, st);
 }
 
 hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, const void* v,
@@ -377,9 +354,9 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
   shared_tail(p, d, false, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
-  s = route_with_qcal(d, w.rt, q, h, W_down, W_up, kL, e, topk_idx, w.s_T, w.sel_lse, st);
+  s = route_with_qcal(p->timing, d, w.rt, q, h, W_down, W_up, kL, e, topk_idx, w.s_T, w.sel_lse, st);
   if (s != HILS_OK) return s;
-  return hip_status(timed(HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
+  return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
 }
 
 hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,
@@ -407,7 +384,7 @@ hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, c
   shared_tail(p, d, true, static_cast<char*>(ws) + base, &sq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
-  return hip_status(timed(HILS_STEP_BWD, st, [&] {
+  return hip_status(timed(p->timing, HILS_STEP_BWD, st, [&] {
     // a shared pair: per-head gradients into the tail, then summed over heads
     float* gd = sq.dwd ? sq.dwd : dW_down;
     float* gu = sq.dwu ? sq.dwu : dW_up;
@@ -446,12 +423,12 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
   bool qf32 = d.dtype == HILS_FP32;
   if (d.r > 0) {
     float* qhat = static_cast<float*>(ws);
-    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, 1, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
+    if ((s = hip_status(timed(p->timing, HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, 1, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
       return s;
     qs = qhat;
     qf32 = true;
   }
-  return hip_status(timed(HILS_STEP_DECODE, st, [&] {
+  return hip_status(timed(p->timing, HILS_STEP_DECODE, st, [&] {
     return hils::launch_decode(d, qs, qf32, q, k_cache, v_cache, seq_len, nullptr, 0, kL, e, o, lse, topk_idx,
                                ws, st);
   }));
@@ -485,12 +462,12 @@ hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* 
   bool qf32 = d.dtype == HILS_FP32;
   if (d.r > 0) {
     float* qhat = static_cast<float*>(ws);
-    if ((s = hip_status(timed(HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, 1, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
+    if ((s = hip_status(timed(p->timing, HILS_STEP_QCAL, st, [&] { return hils::launch_qcal(d, 1, q, h, W_down, W_up, qhat, nullptr, st); }))) != HILS_OK)
       return s;
     qs = qhat;
     qf32 = true;
   }
-  return hip_status(timed(HILS_STEP_DECODE, st, [&] {
+  return hip_status(timed(p->timing, HILS_STEP_DECODE, st, [&] {
     return hils::launch_decode(d, qs, qf32, q, k_pages, v_pages, seq_len, page_table, max_pages,
                                kL_pages, e_pages, o, lse, topk_idx, ws, st);
   }));
@@ -504,7 +481,7 @@ hils_status hils_landmark_fwd(const hils_problem* p, const void* qL, const void*
   if (!al16(qL, k, kL, kL32)) return HILS_ERR_INVALID;
   const Dims d = landmark_dims(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(timed(HILS_STEP_LANDMARK_FWD, st, [&] {
+  return hip_status(timed(p->timing, HILS_STEP_LANDMARK_FWD, st, [&] {
     return hils::launch_landmark_fwd(d, qL, k, kL, e, kL32, e32, st);
   }));
 }
@@ -518,7 +495,7 @@ hils_status hils_landmark_bwd(const hils_problem* p, const void* qL, const void*
   if (!al16(qL, k, dkL, dqL, dk)) return HILS_ERR_INVALID;
   const Dims d = landmark_dims(p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(timed(HILS_STEP_LANDMARK_BWD, st, [&] {
+  return hip_status(timed(p->timing, HILS_STEP_LANDMARK_BWD, st, [&] {
     return hils::launch_landmark_bwd(d, qL, k, dkL, de, dqL, dk, st);
   }));
 }
@@ -538,7 +515,7 @@ hils_status hils_hope(const hils_hope_params* p, const void* x, void* y, const i
   const long long units = (long long)p->B * p->N * (p->d / 2) / (p->dtype == HILS_BF16 ? 8 : 4);
   if (units > 0x7fffff00LL) return HILS_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(timed(HILS_STEP_HOPE, st, [&] {
+  return hip_status(timed(p->timing, HILS_STEP_HOPE, st, [&] {
     return hils::launch_hope(p->dtype, p->B, p->H, p->N, p->d, x, y, pos, (double)p->base,
                              p->train_len, p->interleaved == 1, p->inverse == 1, st);
   }));

@@ -14,6 +14,7 @@ struct Dims {
   int C;      // N / S
   int D, r;
   float scale;
+  int fwd_strategy = 0;  // prefill forward schedule: 0 by shape, 1 union, 2 compact, 3 chunk-major
 };
 
 // Q-Cal: q_hat = q + W_up (W_down h) in fp32; u = W_down h (fp32, optional).
@@ -51,8 +52,6 @@ hipError_t launch_fwd_sparse(const Dims& p, const void* q, const void* k, const 
                              const int32_t* idx, const float* sc, const float* sl, void* o,
                              float* lse, hipStream_t st);
 size_t attn_fwd_vt_bytes(const Dims& p);
-// forward strategy: 0 by shape, 1 shared block (packed union), 2 bucketed
-void set_fwd_strategy(int s);
 
 // Decode.
 size_t decode_workspace(const Dims& p);

@@ -5,5 +5,6 @@ bench.py may import anything here. The product library never does, and the
 oracle never imports the product library.
 """
 from .hils_oracle import (hils_forward, hils_backward, hils_decode, hils_route, row_forward,
+                          surrogate_scores, rank_chunks,
                           row_backward, select_topk, n_distant, window_start, qcal, f64,
                           logsumexp, softmax)

@@ -28,6 +28,33 @@ def rank_count_topk(sel, k):
     return out
 
 
+def qcal_row(q, hvec, W_down, W_up):
+    """q_hat = q + W_up (W_down h) for one head, by scalar loops (W_down r x D,
+    W_up d x r as nested lists)."""
+    u = [dot(row, hvec) for row in W_down]
+    return [q[t] + dot(W_up[t], u) for t in range(len(q))]
+
+
+def selection_scores(qhat, kL, e, nd, scale):
+    """Per-head surrogate scores s[h][c] and the group's selection score
+    sel[c] = max over heads, by scalar loops over the nd distant chunks."""
+    s = [[scale * dot(qh, kL[c]) + e[c] for c in range(nd)] for qh in qhat]
+    sel = [max(s[h][c] for h in range(len(qhat))) for c in range(nd)]
+    return s, sel
+
+
+def rank_order(sel):
+    """Chunk ids sorted so that c comes before c' when it beats c' (higher
+    score, or equal score and lower id), by counting how many beat each."""
+    n = len(sel)
+    pos = [sum(1 for c2 in range(n) if sel[c2] > sel[c] or (sel[c2] == sel[c] and c2 < c))
+           for c in range(n)]
+    out = [0] * n
+    for c, p in enumerate(pos):
+        out[p] = c
+    return out
+
+
 def lse(xs):
     m = max(xs)
     return m + math.log(sum(math.exp(x - m) for x in xs))

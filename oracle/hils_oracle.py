@@ -109,13 +109,29 @@ def softmax(x: np.ndarray, axis=-1) -> np.ndarray:
     return np.exp(x - np.expand_dims(logsumexp(x, axis), axis))
 
 
+def rank_chunks(sel: np.ndarray) -> np.ndarray:
+    """Chunk ids ordered by (selection score desc, chunk id asc): the order in
+    which top-K takes them (ties go to the lower chunk index)."""
+    return np.lexsort((np.arange(sel.shape[0]), -sel))
+
+
 def select_topk(sel: np.ndarray, k: int) -> np.ndarray:
     """Indices of the k best entries of `sel` ordered by (score desc, index
     asc), returned in ascending index order."""
     if k <= 0:
         return np.zeros(0, dtype=np.int64)
-    order = np.lexsort((np.arange(sel.shape[0]), -sel))
-    return np.sort(order[:k])
+    return np.sort(rank_chunks(sel)[:k])
+
+
+def surrogate_scores(q_hat: np.ndarray, kL: np.ndarray, e: np.ndarray, nd: int, scale: float):
+    """Step 2 and the GQA max of step 3 for one query position of one KV group.
+
+    q_hat: [G, d]; kL: [>= nd, d]; e: [>= nd]. Returns s [G, nd] with
+    s[h, c] = scale * q_hat_h . kL_c + e_c over the nd distant chunks, and the
+    group's selection score sel [nd] = the max of s over the heads."""
+    s = scale * (q_hat @ kL[:nd].T) + e[None, :nd]
+    sel = s.max(axis=0) if nd > 0 else np.zeros(0)
+    return s, sel
 
 
 def qcal(q: np.ndarray, hvec: Optional[np.ndarray], W_down: Optional[np.ndarray],
@@ -160,10 +176,10 @@ def row_forward(q: np.ndarray, q_hat: np.ndarray, K: np.ndarray, V: np.ndarray,
     e: [C]. forced_T replaces the selection; forced_s_T ([G, |T|]) replaces
     the fusion scores of the selected chunks."""
     nd = n_distant(i, W, S)
-    # step 2: surrogate scores of every distant chunk, per head
-    s = scale * (q_hat @ kL[:nd].T) + e[None, :nd]
-    # step 3/4: group selection on the max over heads, then top-K
-    sel = s.max(axis=0) if nd > 0 else np.zeros(0)
+    # step 2/3: surrogate scores of every distant chunk, per head, and the
+    # group's selection score (max over its heads)
+    s, sel = surrogate_scores(q_hat, kL, e, nd, scale)
+    # step 4: top-K
     if forced_T is None:
         T = select_topk(sel, min(Ktop, nd))
     else:
@@ -373,13 +389,17 @@ def hils_backward(t: dict, dO, S: int, K: int, W: int, scale: Optional[float] = 
 
 def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
                 batches: Optional[Sequence[int]] = None, groups: Optional[Sequence[int]] = None,
-                forced_topk=None):
+                forced_topk=None, rank_only: bool = False):
     """Single-query decode: the new token sits at position seq_len[b]-1 and
     its key/value are already in the cache. q: [B,Hq,d]; k/v cache
-    [B,Hkv,Nmax,d]; h: [B,D]. Returns o [B,Hq,d], lse [B,Hq], topk [B,Hkv,K]."""
+    [B,Hkv,Nmax,d]; h: [B,D]. Returns o [B,Hq,d], lse [B,Hq], topk [B,Hkv,K]
+    and ranked[(b, g)] = (selection scores in rank order, chunk ids in rank
+    order) over the distant chunks of that sequence and KV group, for the
+    near-tie checks of a selection computed elsewhere. With rank_only, only
+    steps 1-4 run (topk and ranked; the caches are not read)."""
     q = f64(t["q"])
     B, Hq, d = q.shape
-    Hkv = t["k"].shape[1]
+    Hkv = t["kL"].shape[1]
     G = Hq // Hkv
     sc = _scale(d, scale)
     seq = [int(x) for x in (t["seq_len"].tolist() if t.get("seq_len") is not None
@@ -387,6 +407,7 @@ def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
     o = np.full((B, Hq, d), np.nan)
     lse = np.full((B, Hq), np.nan)
     topk = np.full((B, Hkv, K), -2, dtype=np.int64)
+    ranked = {}
     qc = t.get("W_down") is not None
     Wd, Wu = per_head(t.get("W_down"), Hq), per_head(t.get("W_up"), Hq)
     for b in (range(B) if batches is None else batches):
@@ -394,8 +415,6 @@ def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
         i = n - 1
         for g in (range(Hkv) if groups is None else groups):
             hs = slice(g * G, (g + 1) * G)
-            Kc = f64(t["k"][b, g, :n])
-            Vc = f64(t["v"][b, g, :n])
             C = n // S
             kL = f64(t["kL"][b, g, :C])
             e = f64(t["e"][b, g, :C])
@@ -403,13 +422,26 @@ def hils_decode(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
                 q_hat, u = qcal(q[b, hs], f64(t["h"][b]), Wd[hs], Wu[hs])
             else:
                 q_hat, u = q[b, hs].copy(), None
+            if rank_only:
+                nd = n_distant(i, W, S)
+                _, sel = surrogate_scores(q_hat, kL, e, nd, sc)
+                order = rank_chunks(sel)
+                T = np.sort(order[:min(K, nd)])
+                topk[b, g] = -1
+                topk[b, g, :len(T)] = T
+                ranked[(b, g)] = (sel[order], order)
+                continue
+            Kc = f64(t["k"][b, g, :n])
+            Vc = f64(t["v"][b, g, :n])
             fT = None if forced_topk is None else np.asarray(forced_topk)[b, g]
             r = row_forward(q[b, hs], q_hat, Kc, Vc, kL, e, i, S, K, W, sc, forced_T=fT, u=u)
             o[b, hs] = r.o
             lse[b, hs] = r.lse
             topk[b, g] = -1
             topk[b, g, :len(r.T)] = r.T
-    return dict(o=o, lse=lse, topk=topk)
+            order = rank_chunks(r.sel)
+            ranked[(b, g)] = (r.sel[order], order)
+    return dict(o=o, lse=lse, topk=topk, ranked=ranked)
 
 
 def hils_route(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
@@ -425,15 +457,14 @@ def hils_route(t: dict, S: int, K: int, W: int, scale: Optional[float] = None,
         for g in (range(P.Hkv) if groups is None else groups):
             hs = P.heads(g)
             for i in (range(N) if rows is None else rows):
-                q_row = P.q[b, hs, i]
-                q_hat, _ = P.qhat_row(b, g, i, q_row)
+                q_hat, _ = P.qhat_row(b, g, i, P.q[b, hs, i])
                 nd = n_distant(i, W, S)
-                s = P.scale * (q_hat @ P.kL[b, g, :nd].T) + P.e[b, g, None, :nd]
-                sel = s.max(axis=0) if nd else np.zeros(0)
-                T = select_topk(sel, min(K, nd))
+                # the same steps 1-4 as row_forward, without the attention
+                _, sel = surrogate_scores(q_hat, P.kL[b, g], P.e[b, g], nd, P.scale)
+                order = rank_chunks(sel)
+                T = np.sort(order[:min(K, nd)])
                 topk[b, g, i] = -1
                 topk[b, g, i, :len(T)] = T
-                order = np.lexsort((np.arange(nd), -sel))
                 ranked[(b, g, i)] = (sel[order], order)
     return dict(topk=topk, ranked=ranked)
 

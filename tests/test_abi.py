@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import learnable_chunk_sparse_amd as L
 
@@ -28,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def prob(**kw):
     base = dict(dtype=1, B=4, Hq=16, Hkv=16, d=64, Nq=8192, Nk=8192, S=64, K=16, W=512, D=1024,
-                r=32, qcal_shared=0, scale=0.0)
+                r=32, qcal_shared=0, scale=0.0, fwd_strategy=0, timing=None)
     base.update(kw)
     return L.Problem(*[base[f[0]] for f in L.Problem._fields_])
 
@@ -149,20 +150,34 @@ def test_hope_rejects_before_launch_and_empty_is_a_no_op():
         assert lib.hils_hope(ctypes.byref(hp(**kw)), null, null, null, null) == 0, kw
 
 
-def test_fwd_strategy_switch():
-    lib = L.lib()
-    try:
-        for s in (L.FWD_UNION, L.FWD_COMPACT, L.FWD_AUTO):
-            assert lib.hils_set_fwd_strategy(s) == 0
-        assert lib.hils_set_fwd_strategy(3) == 1 and lib.hils_set_fwd_strategy(-1) == 1
-        # the forced strategy decides the LDS check: the 1.4B shape fits either way
-        big = prob(B=1, Hq=32, Hkv=8, d=128, Nq=131072, Nk=131072, W=1024, D=2048)
-        for s in (L.FWD_UNION, L.FWD_COMPACT):
-            lib.hils_set_fwd_strategy(s)
-            st, n = ws(big, L.OP_FWD)
-            assert st in (0, 2), (s, st)
-    finally:
-        lib.hils_set_fwd_strategy(L.FWD_AUTO)
+def test_fwd_strategy_is_a_field_of_the_call():
+    """The forward strategy travels in the problem (no process-wide switch):
+    the workspace size is computed for the strategy the call names, and
+    values outside the enum are rejected."""
+    assert not hasattr(L.lib(), "hils_set_fwd_strategy")
+    assert not hasattr(L.lib(), "hils_set_timing_events")
+    for s_ in (L.FWD_AUTO, L.FWD_UNION, L.FWD_COMPACT):
+        st, _ = ws(prob(fwd_strategy=s_), L.OP_FWD)
+        assert st == 0, s_
+    for bad in (-1, 4):
+        assert ws(prob(fwd_strategy=bad), L.OP_FWD)[0] == 1
+    # the strategy decides the LDS check: the 1.4B shape fits either way
+    big = prob(B=1, Hq=32, Hkv=8, d=128, Nq=131072, Nk=131072, W=1024, D=2048)
+    for s_ in (L.FWD_UNION, L.FWD_COMPACT):
+        big.fwd_strategy = s_
+        st, n = ws(big, L.OP_FWD)
+        assert st in (0, 2), (s_, st)
+
+
+def test_timing_struct_layout():
+    """hils_timing is STEP_COUNT start handles then STEP_COUNT stop handles,
+    and the problem carries a pointer to it after the strategy field."""
+    assert ctypes.sizeof(L.Timing) == 2 * L.STEP_COUNT * ctypes.sizeof(ctypes.c_void_p)
+    assert L.Problem.timing.offset % ctypes.sizeof(ctypes.c_void_p) == 0
+    assert L.Problem.fwd_strategy.offset == 14 * 4
+    tm = L.Timing()
+    p = prob(timing=ctypes.pointer(tm))
+    assert ws(p, L.OP_FWD)[0] == 0  # sizing reads no events
 
 
 def test_decode_paged_rejects_before_launch():
@@ -187,3 +202,65 @@ def test_chunk_tensors_may_be_null_only_without_complete_chunks():
         st = lib.hils_attn_fwd(ctypes.byref(p), fake, fake, fake, null, null, null, null, null, fake,
                                fake, fake, fake, 16, null)
         assert st == code, (Nk, st)
+
+
+# ---------------------------------------------------------------- binding argument checks
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _fwd_args(**over):
+    B, Hq, Hkv, N, d, S = 1, 4, 2, 256, 64, 64
+    a = dict(q=_t(B, Hq, N, d), k=_t(B, Hkv, N, d), v=_t(B, Hkv, N, d), kL=_t(B, Hkv, N // S, d),
+             e=_t(B, Hkv, N // S))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("over,exc", [
+    (dict(k=_t(1, 2, 256, 64, dtype=torch.float32)), TypeError),       # k dtype != q dtype
+    (dict(v=_t(1, 2, 255, 64)), ValueError),                           # v shape
+    (dict(kL=_t(1, 2, 3, 64)), ValueError),                            # wrong chunk count
+    (dict(e=_t(1, 2, 4, dtype=torch.float32)), TypeError),             # e dtype
+    (dict(q=_t(1, 4, 256, 64, dtype=torch.float16)), TypeError),       # unsupported dtype
+    (dict(kL=_t(1, 2, 64, 4).transpose(2, 3)), ValueError),           # not contiguous
+    ({}, ValueError),                                                  # host tensors
+])
+def test_binding_rejects_bad_prefill_arguments(over, exc):
+    a = _fwd_args(**over)
+    with pytest.raises(exc):
+        L.hils_attn_fwd(a["q"], a["k"], a["v"], a["kL"], a["e"], 64, 2, 64)
+
+
+def test_binding_rejects_bad_qcal_and_backward_arguments():
+    a = _fwd_args()
+    h, Wd, Wu = _t(1, 256, 128), _t(4, 32, 128), _t(4, 64, 32)
+    with pytest.raises(ValueError):  # Q-Cal tensors come together
+        L.hils_attn_fwd(a["q"], a["k"], a["v"], a["kL"], a["e"], 64, 2, 64, h=h, W_down=Wd)
+    with pytest.raises(TypeError):  # W_up dtype
+        L.hils_attn_fwd(a["q"], a["k"], a["v"], a["kL"], a["e"], 64, 2, 64, h=h, W_down=Wd,
+                        W_up=Wu.float())
+    with pytest.raises(ValueError):  # W_up shape
+        L.hils_attn_fwd(a["q"], a["k"], a["v"], a["kL"], a["e"], 64, 2, 64, h=h, W_down=Wd,
+                        W_up=_t(4, 64, 16))
+    lse, idx, dO = _t(1, 4, 256, dtype=torch.float32), _t(1, 2, 256, 2, dtype=torch.int32), _t(1, 4, 256, 64)
+    with pytest.raises(TypeError):  # int64 selection
+        L.hils_attn_bwd(a["q"], a["k"], a["v"], a["kL"], a["e"], None, lse, idx.long(), dO, 64, 2, 64)
+    with pytest.raises(ValueError):  # K of topk_idx
+        L.hils_attn_bwd(a["q"], a["k"], a["v"], a["kL"], a["e"], None, lse, idx, dO, 64, 3, 64)
+    with pytest.raises(ValueError):  # host tensors
+        L.hils_attn_bwd(a["q"], a["k"], a["v"], a["kL"], a["e"], None, lse, idx, dO, 64, 2, 64)
+
+
+def test_binding_rejects_bad_decode_arguments():
+    q = _t(2, 4, 64)
+    kc = _t(2, 2, 640, 64)
+    kL, e = _t(2, 2, 10, 64), _t(2, 2, 10)
+    with pytest.raises(TypeError):  # int64 seq_len would be read as int32 halves
+        L.hils_decode(q, kc, kc, kL, e, 64, 4, 128, seq_len=torch.tensor([640, 600]))
+    with pytest.raises(ValueError):  # seq_len length
+        L.hils_decode(q, kc, kc, kL, e, 64, 4, 128, seq_len=torch.tensor([640], dtype=torch.int32))
+    with pytest.raises(ValueError):  # landmark count
+        L.hils_decode(q, kc, kc, _t(2, 2, 9, 64), e, 64, 4, 128)
+    with pytest.raises(ValueError):  # host tensors
+        L.hils_decode(q, kc, kc, kL, e, 64, 4, 128, seq_len=torch.tensor([640, 600], dtype=torch.int32))

@@ -22,27 +22,11 @@ def run_decode(wl, td):
 
 
 def oracle_ranked(t, b, g, S, K, W):
-    """The oracle's ranking of the distant chunks of sequence b, group g."""
-    q = H.f64(t["q"])
-    G = q.shape[1] // t["k"].shape[1]
-    n = int(t["seq_len"][b])
-    i = n - 1
-    hs = slice(g * G, (g + 1) * G)
-    C = n // S
-    kL = H.f64(t["kL"][b, g, :C])
-    e = H.f64(t["e"][b, g, :C])
-    if t.get("W_down") is not None:
-        Hq = q.shape[1]
-        qh, _ = H.qcal(q[b, hs], H.f64(t["h"][b]), H.per_head(t["W_down"], Hq)[hs],
-                       H.per_head(t["W_up"], Hq)[hs])
-    else:
-        qh = q[b, hs]
-    nd = H.n_distant(i, W, S)
-    sc = 1.0 / np.sqrt(q.shape[-1])
-    s = sc * (qh @ kL[:nd].T) + e[None, :nd]
-    sel = s.max(axis=0) if nd else np.zeros(0)
-    order = np.lexsort((np.arange(nd), -sel))
-    return sel[order], order, nd
+    """The oracle's ranking of the distant chunks of sequence b, group g
+    (selection steps only: the caches are not read)."""
+    r = H.hils_decode(t, S, K, W, batches=[b], groups=[g], rank_only=True)
+    sel_sorted, order = r["ranked"][(b, g)]
+    return sel_sorted, order, len(order)
 
 
 def decode_parity(wl, t_cpu, out, pairs, label):

@@ -25,13 +25,10 @@ def L():
 
 def run_fwd(wl, td, strategy):
     lib = L()
-    lib.hils_set_fwd_strategy(strategy)
-    try:
-        out = lib.hils_attn_fwd(td["q"], td["k"], td["v"], td["kL"], td["e"], wl.S, wl.K, wl.W,
-                                h=td.get("h"), W_down=td.get("W_down"), W_up=td.get("W_up"))
-        torch.cuda.synchronize()
-    finally:
-        lib.hils_set_fwd_strategy(lib.FWD_AUTO)
+    out = lib.hils_attn_fwd(td["q"], td["k"], td["v"], td["kL"], td["e"], wl.S, wl.K, wl.W,
+                            h=td.get("h"), W_down=td.get("W_down"), W_up=td.get("W_up"),
+                            strategy=strategy)
+    torch.cuda.synchronize()
     return out
 
 

@@ -108,6 +108,110 @@ def test_topk_matches_subset_enumeration():
         assert set(H.select_topk(sel, k).tolist()) == ok[0]
 
 
+# ---------------------------------------------------------------- selection-only path
+def _tie_inputs(seed, B, Hq, Hkv, N, d, S):
+    """Integer-valued queries, landmark keys and biases (d = 4: scale 1/2), so
+    that scores are exact multiples of 1/2 and many of them tie exactly."""
+    rng = np.random.default_rng(seed)
+    C = N // S
+    return dict(q=rng.integers(-1, 2, (B, Hq, N, d)).astype(float),
+                k=rng.standard_normal((B, Hkv, N, d)), v=rng.standard_normal((B, Hkv, N, d)),
+                kL=rng.integers(-1, 2, (B, Hkv, C, d)).astype(float),
+                e=rng.integers(-1, 2, (B, Hkv, C)).astype(float))
+
+
+def _brute_selection(t, b, g, i, S, W, scale):
+    """Selection scores of row (b, g, i) from scalar loops only (Q-Cal
+    included, per head or one shared pair)."""
+    q = np.asarray(t["q"])
+    Hq, Hkv = q.shape[1], t["k"].shape[1]
+    G = Hq // Hkv
+    qhat = []
+    for hh in range(G):
+        h = g * G + hh
+        qv = q[b, h, i].tolist()
+        if t.get("W_down") is not None:
+            Wd = np.asarray(t["W_down"])
+            Wu = np.asarray(t["W_up"])
+            Wd, Wu = (Wd, Wu) if Wd.ndim == 2 else (Wd[h], Wu[h])
+            qv = brute.qcal_row(qv, np.asarray(t["h"])[b, i].tolist(), Wd.tolist(), Wu.tolist())
+        qhat.append(qv)
+    nd = H.n_distant(i, W, S)
+    _, sel = brute.selection_scores(qhat, np.asarray(t["kL"])[b, g].tolist(),
+                                    np.asarray(t["e"])[b, g].tolist(), nd, scale)
+    return sel
+
+
+@pytest.mark.parametrize("case", ["ties_gqa2", "ties_mha", "qcal_gqa2", "qcal_shared_gqa4",
+                                  "qcal_mha_bias"])
+def test_route_matches_forward_and_scalar_rank_count(case):
+    """hils_route (selection only) takes the same sets as hils_forward and as
+    scalar scores ranked by the rank-count definition; its ranking is the
+    rank-count order. Integer-valued cases tie exactly (a reversed tie-break
+    fails them); the bias case shifts every bias by its chunk id (a bias
+    taken from the wrong slice fails it)."""
+    S, K, W, N = 4, 3, 6, 60
+    if case.startswith("ties"):
+        Hq, Hkv = (2, 1) if case == "ties_gqa2" else (1, 1)
+        t = _tie_inputs(21 if Hq == 2 else 22, 2, Hq, Hkv, N, 4, S)
+    else:
+        Hq, Hkv = dict(qcal_gqa2=(2, 1), qcal_shared_gqa4=(4, 1), qcal_mha_bias=(2, 2))[case]
+        t = small_inputs(23, B=2, Hq=Hq, Hkv=Hkv, N=N, d=8, S=S, qcal=True)
+        if case == "qcal_shared_gqa4":
+            t = _shared(t, 29)
+        if case == "qcal_mha_bias":
+            t["e"] = t["e"] + 0.25 * np.arange(N // S)[None, None, :]
+    d = t["q"].shape[-1]
+    sc = 1 / math.sqrt(d)
+    rt = H.hils_route(t, S, K, W)
+    fw = H.hils_forward(t, S, K, W)
+    np.testing.assert_array_equal(rt["topk"], fw["topk"])
+    ties = 0
+    for b in range(2):
+        for g in range(Hkv):
+            for i in range(N):
+                sel = _brute_selection(t, b, g, i, S, W, sc)
+                nd = len(sel)
+                ties += nd - len(set(sel))
+                T = brute.rank_count_topk(sel, min(K, nd))
+                got = [int(c) for c in rt["topk"][b, g, i] if c >= 0]
+                assert got == T, (case, b, g, i, got, T)
+                scores, order = rt["ranked"][(b, g, i)]
+                assert list(order) == brute.rank_order(sel)
+                np.testing.assert_allclose(scores, np.asarray(sel)[list(order)], rtol=0,
+                                           atol=1e-12)
+    if case.startswith("ties"):
+        assert ties > 100  # the tie-break decides many rows
+
+
+def test_decode_ranking_matches_scalar_rank_count():
+    """The decode oracle's ranking of each (sequence, KV group) is the
+    rank-count order of scalar scores at position seq_len - 1 (ragged
+    lengths, GQA, Q-Cal per head and shared)."""
+    S, K, W, N, d = 4, 3, 6, 52, 8
+    for shared in (False, True):
+        t = small_inputs(31, B=3, Hq=4, Hkv=2, N=N, d=d, S=S, qcal=True)
+        if shared:
+            t = _shared(t, 37)
+        lens = [N, N - 7, 11]
+        dec = dict(q=np.stack([t["q"][b, :, n - 1] for b, n in enumerate(lens)]), k=t["k"],
+                   v=t["v"], kL=t["kL"], e=t["e"],
+                   h=np.stack([t["h"][b, n - 1] for b, n in enumerate(lens)]),
+                   W_down=t["W_down"], W_up=t["W_up"], seq_len=torch.tensor(lens))
+        od = H.hils_decode(dec, S, K, W)
+        ro = H.hils_decode(dict(dec, k=None, v=None), S, K, W, rank_only=True)
+        np.testing.assert_array_equal(ro["topk"], od["topk"])
+        for b, n in enumerate(lens):
+            for g in range(2):
+                np.testing.assert_array_equal(ro["ranked"][(b, g)][1], od["ranked"][(b, g)][1])
+                sel = _brute_selection(t, b, g, n - 1, S, W, 1 / math.sqrt(d))
+                scores, order = od["ranked"][(b, g)]
+                assert list(order) == brute.rank_order(sel)
+                np.testing.assert_allclose(scores, np.asarray(sel)[list(order)], rtol=0, atol=1e-12)
+                T = brute.rank_count_topk(sel, min(K, len(sel)))
+                assert [int(c) for c in od["topk"][b, g] if c >= 0] == T
+
+
 # ---------------------------------------------------------------- window only
 def test_no_distant_chunk_is_causal_window_attention():
     """Rows with no distant chunk reduce to textbook causal attention."""

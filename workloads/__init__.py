@@ -16,9 +16,12 @@ its own, which is how the oracle re-creates the few slabs it checks at
 full-size shapes.
 
 Distributions:
-  * "normal": the sum of four independent 16-bit uniforms, centred and scaled
-    to unit variance (an Irwin-Hall(4) approximation of N(0,1), support
-    +-3.46).
+  * "normal": N(0,1) by inversion. The top 22 bits of the hash pick one of
+    2^22 equal-probability bins, and the value is the N(0,1) quantile at the
+    bin's midpoint probability (k + 1/2) / 2^22: a table computed once in
+    fp64 (scipy's inverse normal CDF) and rounded to fp32. Every bin has the
+    probability of the normal law, so the tails are the normal tails down to
+    probability 2^-23 (|z| up to 5.17).
   * "uniform(a)": U(-a, a) with a a power of two, on a 2^-22*a grid (exact).
 Values are drawn in fp32 and rounded to bf16 (round to nearest even) for the
 bf16 workloads.
@@ -83,16 +86,30 @@ def _hash(counter: torch.Tensor, key: int, stream: int) -> torch.Tensor:
     return x
 
 
-_NORM_SCALE = torch.tensor(math.sqrt(3.0) / 65536.0, dtype=torch.float32).item()
+NORMAL_BITS = 22
+_NORMAL_TABLES: Dict[str, torch.Tensor] = {}
+
+
+def normal_table(device="cpu") -> torch.Tensor:
+    """fp32 N(0,1) quantiles at the probabilities (k + 1/2) / 2^22,
+    k = 0 .. 2^22 - 1 (computed in fp64, rounded once), cached per device."""
+    key = str(torch.device(device))
+    if key not in _NORMAL_TABLES:
+        if "cpu" not in _NORMAL_TABLES:
+            import numpy as np
+            from scipy.special import ndtri
+            n = 1 << NORMAL_BITS
+            p = (np.arange(n, dtype=np.float64) + 0.5) / n
+            _NORMAL_TABLES["cpu"] = torch.from_numpy(ndtri(p).astype(np.float32))
+        _NORMAL_TABLES[key] = _NORMAL_TABLES["cpu"].to(device)
+    return _NORMAL_TABLES[key]
 
 
 def normal_at(key: int, counter: torch.Tensor) -> torch.Tensor:
-    """Approximate N(0,1) in fp32 at the given int64 counters."""
-    h1 = _hash(counter, key, 0)
-    h2 = _hash(counter, key, 1)
-    s = (h1 & 0xFFFF) + (h1 >> 16) + (h2 & 0xFFFF) + (h2 >> 16)
-    t = (s - 131070).to(torch.float32)  # exact: |t| < 2^24
-    return t * torch.tensor(_NORM_SCALE, dtype=torch.float32, device=t.device)
+    """N(0,1) in fp32 at the given int64 counters (inversion through the
+    quantile table: the same value on any device)."""
+    h = _hash(counter, key, 0) >> (32 - NORMAL_BITS)
+    return normal_table(counter.device)[h]
 
 
 def uniform_at(key: int, counter: torch.Tensor, a: float) -> torch.Tensor:

@@ -216,6 +216,29 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
                         int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hils_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and outputs as hils_decode, with the workspace
+ * replaced by a static device buffer of HILS_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its address is
+ * looked up once per device, on the first call with that device current; the
+ * calling thread's current device must be the stream's). The call itself
+ * allocates nothing. Every call on one GPU shares that GPU's buffer: calls
+ * that overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller; a call may start once the previous one's work is
+ * ordered before it on the stream. Errors: those of hils_decode, plus
+ * HILS_ERR_WORKSPACE when hils_workspace_size(p, HILS_OP_DECODE) exceeds
+ * HILS_NOALLOC_SCRATCH_BYTES (e.g. 32 sequences x 32 heads x d = 128 at
+ * K = 32 and a 1024-token window need ~31 MB and fit), and HILS_ERR_HIP when
+ * the buffer's address cannot be obtained.
+ */
+#define HILS_NOALLOC_SCRATCH_BYTES (64u << 20)
+hils_status hils_decode_noalloc(const hils_problem* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_len, const void* kL,
+                                const void* e, const void* h, const void* W_down, const void* W_up,
+                                void* o, float* lse, int32_t* topk_idx, void* stream);
+
+/*
  * Decode step over a paged KV cache (the serving layout of the pages'
  * released backend, whose page size equals the 64-token chunk: one chunk is
  * one page). Same method and outputs as hils_decode; only where the cache

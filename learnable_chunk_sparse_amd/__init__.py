@@ -25,7 +25,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
 
 EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
            "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_decode_paged", "hils_landmark_fwd",
-           "hils_landmark_bwd", "hils_hope")
+           "hils_landmark_bwd", "hils_hope", "hils_decode_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 FWD_AUTO, FWD_UNION, FWD_COMPACT, FWD_CHUNK_MAJOR = 0, 1, 2, 3
 STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
 STEP_LANDMARK_FWD, STEP_LANDMARK_BWD, STEP_HOPE, STEP_WINDOW, STEP_CHUNKS = 5, 6, 7, 8, 9
@@ -109,6 +110,8 @@ def lib():
         L.hils_attn_bwd.argtypes = [P] + [vp] * 21 + [sz, vp]
         L.hils_decode.restype = ctypes.c_int
         L.hils_decode.argtypes = [P] + [vp] * 13 + [sz, vp]
+        L.hils_decode_noalloc.restype = ctypes.c_int
+        L.hils_decode_noalloc.argtypes = [P] + [vp] * 13
         L.hils_decode_paged.restype = ctypes.c_int
         L.hils_decode_paged.argtypes = [P, vp, vp, vp, vp, i32] + [vp] * 10 + [sz, vp]
         L.hils_landmark_fwd.restype = ctypes.c_int
@@ -376,6 +379,30 @@ def hils_decode(q, k_cache, v_cache, kL, e, S: int, K: int, W: int, seq_len=None
                                             _ptr(seq_len), _ptr(kL), _ptr(e), _ptr(h), _ptr(W_down),
                                             _ptr(W_up), _ptr(o), _ptr(lse), _ptr(idx), _ptr(ws),
                                             ws.numel(), _stream(dev)))
+    return o, lse, idx
+
+
+def hils_decode_noalloc(q, k_cache, v_cache, kL, e, S: int, K: int, W: int, seq_len=None, h=None,
+                        W_down=None, W_up=None, scale=0.0, out=None, with_topk=True, timing=None):
+    """hils_decode on the library's static per-GPU scratch (no workspace, no
+    device allocation inside the call; pass `out` = (o, lse, topk_idx or None)
+    to allocate nothing at all). Calls on one GPU must not overlap."""
+    _validate(q, _decode_specs(q, k_cache, v_cache, kL, e, S, seq_len, h, W_down, W_up))
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    p = make_problem(q, k_cache, S, K, W, h, W_down, scale, decode=True, timing=timing)
+    dev = q.device
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Hkv, K), dtype=torch.int32, device=dev) if with_topk else None
+    else:
+        o, lse, idx = out
+        _validate(q, [("o", o, tuple(q.shape), "ref"), ("lse", lse, (B, Hq), torch.float32),
+                      ("topk_idx", idx, (B, Hkv, K), torch.int32)])
+    _check("hils_decode_noalloc", lib().hils_decode_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_len), _ptr(kL), _ptr(e),
+        _ptr(h), _ptr(W_down), _ptr(W_up), _ptr(o), _ptr(lse), _ptr(idx), _stream(dev)))
     return o, lse, idx
 
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/hils.h"
 #include "hils_internal.h"
@@ -257,6 +258,33 @@ hils_status route_with_qcal(const hils_timing* tm, const Dims& d, const RouteWs&
   return hip_status(timed(tm, HILS_STEP_ROUTE, st, [&] { return hils::launch_route(d, q, d.dtype == HILS_FP32, kL, e, topk_idx, topk_score, sel_lse, st); }));
 }
 
+// ---------------------------------------------------------------- no-alloc scratch
+// The scratch of hils_decode_noalloc: one copy per GPU the library runs on,
+// held until the process ends. Host code never uses this name as an address
+// (on the host it is only a stand-in for the symbol): the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current and kept in g_scratch_addr.
+static __device__ __align__(256) unsigned char scratch[HILS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[MAX_DEVICES];  // written once per device, under the mutex
+
+// device address of the current device's scratch (set up on its first use)
+hils_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return HILS_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return HILS_ERR_HIP;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return HILS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +460,22 @@ hils_status hils_decode(const hils_problem* p, const void* q, const void* k_cach
     return hils::launch_decode(d, qs, qf32, q, k_cache, v_cache, seq_len, nullptr, 0, kL, e, o, lse, topk_idx,
                                ws, st);
   }));
+}
+
+hils_status hils_decode_noalloc(const hils_problem* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_len, const void* kL,
+                                const void* e, const void* h, const void* W_down, const void* W_up,
+                                void* o, float* lse, int32_t* topk_idx, void* stream) {
+  size_t need = 0;
+  hils_status s = hils_workspace_size(p, HILS_OP_DECODE, &need);
+  if (s != HILS_OK) return s;
+  if (need > (size_t)HILS_NOALLOC_SCRATCH_BYTES) return HILS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != HILS_OK) return s;
+  // the same kernels as hils_decode, on the device's static scratch (every
+  // scratch buffer of the decode is written before it is read: nothing to clear)
+  return hils_decode(p, q, k_cache, v_cache, seq_len, kL, e, h, W_down, W_up, o, lse, topk_idx, ws,
+                     (size_t)HILS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 hils_status hils_decode_paged(const hils_problem* p, const void* q, const void* k_pages,

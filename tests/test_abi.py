@@ -264,3 +264,24 @@ def test_binding_rejects_bad_decode_arguments():
         L.hils_decode(q, kc, kc, _t(2, 2, 9, 64), e, 64, 4, 128)
     with pytest.raises(ValueError):  # host tensors
         L.hils_decode(q, kc, kc, kL, e, 64, 4, 128, seq_len=torch.tensor([640, 600], dtype=torch.int32))
+
+
+def test_decode_noalloc_rejects_oversize_and_invalid_before_touching_the_device():
+    """The static-scratch decode sizes the problem first: a problem whose
+    decode workspace exceeds the static buffer is refused with
+    HILS_ERR_WORKSPACE, an invalid one with its validation code, both without
+    any device call (this runs with no GPU)."""
+    lib = L.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)
+    small = prob(B=2, Hq=4, Hkv=2, d=64, Nq=1, Nk=4096, K=8, W=256, r=0, D=0)
+    st, need = ws(small, L.OP_DECODE)
+    assert st == 0 and need <= L.NOALLOC_SCRATCH_BYTES
+    big = prob(B=256, Hq=64, Hkv=8, d=128, Nq=1, Nk=1 << 20, K=64, W=2048, r=0, D=0)
+    st, need = ws(big, L.OP_DECODE)
+    assert st == 0 and need > L.NOALLOC_SCRATCH_BYTES
+    args = lambda p: (ctypes.byref(p), fake, fake, fake, null, fake, fake, null, null, null, fake,
+                      fake, null, null)
+    assert lib.hils_decode_noalloc(*args(big)) == 3
+    assert lib.hils_decode_noalloc(*args(prob(B=0, Nq=1, Nk=4096))) == 1
+    assert lib.hils_decode_noalloc(*args(prob(d=96, Nq=1, Nk=4096))) == 2

@@ -16,8 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libhils.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["qcal.hip", "route.hip", "attn_fwd.hip", "attn_fwd_sparse.hip", "decode.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "gemm.hip", "landmark.hip", "hope.hip",
-           "hils_api.cpp"]
+SOURCES = ["qcal.hip", "route.hip", "attn_fwd.hip", "attn_fwd_sparse.hip", "attn_fwd_cm.hip",
+           "inv_index.hip", "decode.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "gemm.hip",
+           "landmark.hip", "hope.hip", "hils_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 math stays off (hipcc's host pass warns that it does not
          # know the feature; that is harmless)

@@ -148,84 +148,6 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const QT* __restrict__ qs, con
   }
 }
 
-// Inverse index (for each chunk, the (position, slot) pairs that selected
-// it), built as a counting sort per (b, kv head): the positions are cut into
-// `ns` ranges, each range histograms its selections in LDS, an exclusive scan
-// over (chunk, range) gives every range its first slot per chunk, and the
-// fill pass places the entries through LDS cursors.
-__global__ __launch_bounds__(256) void k_inv_hist(const int32_t* __restrict__ topk_idx,
-                                                  int* __restrict__ cnt, int N, int K, int C, int ns) {
-  extern __shared__ int hist[];
-  const int sp = blockIdx.x, bg = blockIdx.y, tid = threadIdx.x;
-  for (int c = tid; c < C; c += 256) hist[c] = 0;
-  __syncthreads();
-  const long per = ((long)N + ns - 1) / ns;
-  const long i0 = sp * per, i1 = min((long)N, i0 + per);
-  const int32_t* src = topk_idx + (long)bg * N * K;
-  for (long x = i0 * K + tid; x < i1 * K; x += 256) {
-    const int c = src[x];
-    if (c >= 0 && c < C) atomicAdd(&hist[c], 1);
-  }
-  __syncthreads();
-  int* dst = cnt + (long)bg * C * ns;
-  for (int c = tid; c < C; c += 256) dst[(long)c * ns + sp] = hist[c];
-}
-
-// exclusive scan of cnt[bg][c][range] in place; off[bg][c] = first slot of chunk c
-__global__ __launch_bounds__(256) void k_inv_scan(int* __restrict__ cnt, int* __restrict__ off, int C, int ns) {
-  __shared__ int wsum[4];
-  __shared__ int carry;
-  const int bg = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int* cb = cnt + (long)bg * C * ns;
-  int* ob = off + (long)bg * (C + 1);
-  const long n = (long)C * ns;
-  if (t == 0) carry = 0;
-  __syncthreads();
-  for (long base = 0; base < n; base += 256) {
-    const long idx = base + t;
-    const int x = idx < n ? cb[idx] : 0;
-    int v = x;
-#pragma unroll
-    for (int o2 = 1; o2 < 64; o2 <<= 1) {
-      const int y = __shfl_up(v, o2, 64);
-      if (lane >= o2) v += y;
-    }
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    int pre = carry;
-    for (int j = 0; j < w; ++j) pre += wsum[j];
-    if (idx < n) {
-      cb[idx] = pre + v - x;
-      if (idx % ns == 0) ob[idx / ns] = pre + v - x;
-    }
-    __syncthreads();
-    if (t == 255) carry = pre + v;
-    __syncthreads();
-  }
-  if (t == 0) ob[C] = carry;
-}
-
-__global__ __launch_bounds__(256) void k_inv_fill(const int32_t* __restrict__ topk_idx,
-                                                  const int* __restrict__ start, int* __restrict__ lst,
-                                                  int N, int K, int C, int ns) {
-  extern __shared__ int cur[];
-  const int sp = blockIdx.x, bg = blockIdx.y, tid = threadIdx.x;
-  const int* sb = start + (long)bg * C * ns;
-  for (int c = tid; c < C; c += 256) cur[c] = sb[(long)c * ns + sp];
-  __syncthreads();
-  const long per = ((long)N + ns - 1) / ns;
-  const long i0 = sp * per, i1 = min((long)N, i0 + per);
-  const int32_t* src = topk_idx + (long)bg * N * K;
-  int* dst = lst + (long)bg * N * K;
-  for (long x = i0 * K + tid; x < i1 * K; x += 256) {
-    const int c = src[x];
-    if (c >= 0 && c < C) {
-      const int i = (int)(x / K), k = (int)(x - (long)i * K);
-      dst[atomicAdd(&cur[c], 1)] = (i << 6) | k;
-    }
-  }
-}
-
 // --------------------------------------------------------------- helpers
 
 __device__ int bwd_block_scan(int* a, int n, int* wsum) {
@@ -1064,19 +986,12 @@ __global__ __launch_bounds__(256) void k_bwd_dklu(const int* __restrict__ ioff,
 namespace {
 struct BwdWs {
   float *qhat, *u, *Dv, *sT, *ds, *beta, *delta, *dqhat, *du, *gwork;
-  int *cnt, *off, *lst;
+  int *off, *lst;
+  InvIndex ix;
   void* kt;
   const void* W_up;
   int Np, ns;
 };
-// position ranges of the inverse-index counting sort: enough workgroups to
-// fill the chip, at least 256 positions each
-int inv_ranges(const Dims& p) {
-  const long bg = (long)p.B * p.Hkv;
-  long ns = (2048 + bg - 1) / bg;
-  ns = std::min<long>(ns, (p.N + 255) / 256);
-  return (int)std::max<long>(ns, 1);
-}
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // dW_down[h] += sum_i du[b, i, h, :] (x) h[b, i, :]: all heads and all batch
 // elements in one product, rows (h, j) of du^T [Hq r x B N] times h [B N x D]
@@ -1114,10 +1029,14 @@ size_t carve(const Dims& p, void* base, BwdWs* w) {
   w->dqhat = (float*)take(qc ? rows * p.d * 4 : 0);
   w->du = (float*)take(qc ? (size_t)p.B * p.N * p.Hq * p.r * 4 : 0);
   w->gwork = (float*)take(qc ? gemm_work_bytes(dwdown_args(p, nullptr)) : 0);
-  w->ns = inv_ranges(p);
-  w->cnt = (int*)take(bg * p.C * w->ns * 4);
-  w->off = (int*)take(bg * (p.C + 1) * 4);
-  w->lst = (int*)take(bg * (size_t)p.N * p.K * 4);
+  {
+    InvIndex ix;
+    void* ib = take(inv_index_carve(p, nullptr, &ix));
+    inv_index_carve(p, ib, &ix);
+    w->ix = ix;
+    w->off = ix.off;
+    w->lst = ix.lst;
+  }
   w->Np = (p.N + 63) / 64 * 64;
   w->kt = take(bg * (size_t)p.d * w->Np * (p.dtype == 1 ? 2 : 4));
   return o;
@@ -1165,7 +1084,7 @@ unsigned grid1(size_t n) { return (unsigned)std::min<size_t>((n + 255) / 256, 65
 size_t bwd_workspace(const Dims& p) {
   if (dq_lds_bytes(p) > 160 * 1024 || dkdv_lds(p) + 1024 > 160 * 1024) return (size_t)-1;
   if ((size_t)p.N * p.K >= (1u << 31)) return (size_t)-1;
-  if ((size_t)p.C * sizeof(int) > 64 * 1024) return (size_t)-1;
+  if (!inv_index_ok(p)) return (size_t)-1;
   BwdWs w;
   return carve(p, nullptr, &w);
 }
@@ -1182,14 +1101,8 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
                      (const QT*)qsrc, (const T*)kL, (const T*)e, topk_idx, w.sT, (long)rows, p.N,
                      p.Hq, p.Hkv, G, p.C, p.K, p.scale);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // inverse index
-  const size_t hl = (size_t)p.C * sizeof(int);
-  hipLaunchKernelGGL(k_inv_hist, dim3(w.ns, (unsigned)bg), dim3(256), hl, st, topk_idx, w.cnt, p.N,
-                     p.K, p.C, w.ns);
-  hipLaunchKernelGGL(k_inv_scan, dim3((unsigned)bg), dim3(256), 0, st, w.cnt, w.off, p.C, w.ns);
-  hipLaunchKernelGGL(k_inv_fill, dim3(w.ns, (unsigned)bg), dim3(256), hl, st, topk_idx, w.cnt, w.lst,
-                     p.N, p.K, p.C, w.ns);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // inverse index (deterministic: each chunk's rows in ascending position order)
+  if ((err = launch_inv_index(p, topk_idx, w.ix, st)) != hipSuccess) return err;
   // dq pass (K^T copy first)
   {
     hipLaunchKernelGGL((k_vt_perm<T, DH>), dim3(w.Np / 64, (unsigned)bg), dim3(256), 0, st,

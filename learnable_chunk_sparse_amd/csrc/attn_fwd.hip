@@ -728,13 +728,23 @@ static hipError_t vt_go(const Dims& p, const void* v, void* vt, int Np, hipStrea
 // streamed chunks would serve a single row block, and the bucketed kernel
 // (rows of a chunk packed into dense row blocks, chunks taken by waves
 // independently) does less work.
-// The caller's strategy (Dims::fwd_strategy): 0 chooses by the rule above,
-// 1 shared block, 2 bucketed.
-static bool fwd_use_shared(const Dims& p) {
-  if (p.fwd_strategy == 1) return true;
-  if (p.fwd_strategy == 2) return false;
+// The caller's strategy (Dims::fwd_strategy), or by the rule above when 0:
+// 1 shared block; otherwise chunk-major (3, attn_fwd_cm.hip) where its
+// envelope allows, else bucketed (2).
+int fwd_strategy_of(const Dims& p) {
+  if (p.fwd_strategy != 0) return p.fwd_strategy;
   const long tp = 128 / p.G;
-  return tp * p.K >= 4L * p.C;
+  if (tp * p.K >= 4L * p.C) return 1;
+  return fwd_cm_ok(p) ? 3 : 2;
+}
+
+static bool fwd_use_shared(const Dims& p) { return fwd_strategy_of(p) == 1; }
+
+hipError_t launch_vt_perm(const Dims& p, const void* v, void* vt, hipStream_t st) {
+  const int Np = (p.N + 63) / 64 * 64;
+  if (p.dtype == 1)
+    return p.d == 64 ? vt_go<uint16_t, 64>(p, v, vt, Np, st) : vt_go<uint16_t, 128>(p, v, vt, Np, st);
+  return p.d == 64 ? vt_go<float, 64>(p, v, vt, Np, st) : vt_go<float, 128>(p, v, vt, Np, st);
 }
 
 template <typename T>
@@ -744,6 +754,7 @@ static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void*
   const int Np = (p.N + 63) / 64 * 64;
   hipError_t err = p.d == 64 ? vt_go<T, 64>(p, v, vt, Np, st) : vt_go<T, 128>(p, v, vt, Np, st);
   if (err != hipSuccess) return err;
+  if (fwd_strategy_of(p) == 3) return hipErrorInvalidValue;  // run from the C ABI step by step
   if (!fwd_use_shared(p)) return launch_fwd_sparse(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
   switch (p.G * 1000 + p.d) {
     case 1064: return fwd_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
@@ -770,7 +781,9 @@ static size_t lds_t(const Dims& p) {
 }
 
 size_t attn_fwd_lds_bytes(const Dims& p) {
-  if (!fwd_use_shared(p)) return fwd_sparse_lds_bytes(p);
+  const int strat = fwd_strategy_of(p);
+  if (strat == 3) return fwd_cm_ok(p) ? 0 : (size_t)-1;  // checked by fwd_cm_ok
+  if (strat == 2) return fwd_sparse_lds_bytes(p);
   const size_t stat = 64;
   return (p.dtype == 1 ? lds_t<uint16_t>(p) : lds_t<float>(p)) + stat;
 }

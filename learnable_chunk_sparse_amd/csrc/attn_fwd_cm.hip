@@ -1,0 +1,572 @@
+// HiLS prefill forward, chunk-major strategy (long sequences).
+//
+// Paper: Fig. 3 (each selected chunk gets its inter-chunk mass exp(s_c - L),
+// spread over its tokens by the intra-chunk softmax), the engineersofai
+// abstract (each query attends to each retrieved chunk independently and the
+// per-chunk outputs are fused by the retrieval scores), "Limitations of Naive
+// Sparse Attention" (local window plus distant chunks); the same result as
+// the query-tile strategies of attn_fwd.hip and attn_fwd_sparse.hip.
+//
+// Why chunk-major: when adjacent queries share few chunks (independent
+// queries over thousands of distant chunks), a query tile reuses each chunk
+// it loads for about one position, so every (position, chunk) selection costs
+// a whole 64-token K and V block of traffic. Here every selected chunk is
+// loaded once per (batch, KV head) and serves all the rows that chose it,
+// found through the inverse index (inv_index.hip); the price is one per-chunk
+// output per (position, slot, head) written and read back once.
+//
+//   k_fwd_cm_chunks  one workgroup per (chunk, b, KV head); the chunk's K rows
+//                    and V^T stay in every wave's registers while the waves
+//                    take 16-row blocks of the chunk's rows (16 / G entries x
+//                    G heads): S^T = K Q^T, softmax over the 64 tokens,
+//                    O_c^T = V^T P^T, O_c normalised and stored in the input
+//                    dtype at part[b, g][pos][slot][head] (dims in MFMA
+//                    D-fragment order: lane group gl's dims 16 mb + 4 gl + i
+//                    contiguous, so both kernels move 16-byte vectors).
+//   k_fwd_cm_window  query tiles of 128 rows (128 / G positions x G heads):
+//                    banded flash attention over the window with K / V^T
+//                    blocks staged through LDS for the four waves; then
+//                    L = log(exp(lse_W) + exp(lse_sel)) and
+//                    o = exp(lse_W - L) O_W + sum_k exp(s_k - L) O_{c_k}.
+#include "hils_common.h"
+#include "hils_internal.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace hils {
+
+namespace {
+
+// ---------------------------------------------------------------- chunk pass
+template <typename T, int DH>
+struct ChunkRegs {
+  typename Frag<T>::type k[4][DH / 32];  // A operand of S^T: K rows (tokens)
+  typename Frag<T>::type v[DH / 16][2];  // A operand of O^T: V^T rows (dims), token-permuted
+};
+
+template <typename T, int DH>
+struct RowBlock {
+  typename Frag<T>::type q[DH / 32];
+  int pos, slot;
+  bool valid;
+};
+
+template <typename T, int G, int DH>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_fwd_cm_chunks(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
+    const int* __restrict__ off, const int* __restrict__ lst, T* __restrict__ part, int N, int Np,
+    int Hkv, int K, int C, float scale) {
+  typedef typename Frag<T>::type FT;
+  constexpr int KS = DH / 32;
+  constexpr int MB = DH / 16;
+  constexpr int EPB = 16 / G;  // entries per 16-row block
+  const int c = blockIdx.x, bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int Hq = Hkv * G;
+  const int* ob = off + (size_t)bg * (C + 1);
+  const int e0 = ob[c], n = ob[c + 1] - e0;
+  const int nb = (n + EPB - 1) / EPB;
+  const int lane = threadIdx.x & 63, gl = lane >> 4, cl = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= nb) return;  // no barrier below: idle waves leave early
+
+  // the chunk's K rows and V^T columns as fragments (every wave holds them)
+  ChunkRegs<T, DH> f;
+  {
+    const T* kb = k + ((size_t)bg * N + (size_t)c * 64) * DH + 8 * gl;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) f.k[tb][ks] = ld8<T>(kb + (size_t)(16 * tb + cl) * DH + 32 * ks);
+    const T* vb = vt + (size_t)bg * DH * Np + (size_t)c * 64 + 8 * gl;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) f.v[mb][ks] = ld8<T>(vb + (size_t)(16 * mb + cl) * Np + 32 * ks);
+  }
+  const int* lb = lst + (size_t)bg * N * K + e0;
+  const int hh = cl % G;
+  const float sc2 = scale * LOG2E;
+
+  auto load_rows = [&](RowBlock<T, DH>& r, int j) __attribute__((always_inline)) {
+    const int x = j * EPB + cl / G;
+    r.valid = x < n;
+    const int en = lb[min(x, n - 1)];
+    r.pos = en >> 6;
+    r.slot = en & 63;
+    const T* src = q + (((size_t)b * Hq + g * G + hh) * N + r.pos) * DH + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) r.q[ks] = ld8<T>(src + 32 * ks);
+  };
+  auto process = [&](const RowBlock<T, DH>& r) __attribute__((always_inline)) {
+    f32x4 sacc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      sacc[tb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(f.k[tb][ks], r.q[ks], sacc[tb]);
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[tb][i]);
+    const float mref = col_max4(mx) * sc2;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[tb][i] = fast_exp2(fmaf(sacc[tb][i], sc2, -mref));
+    FT pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pf[ks] = pk8<T>(sacc[2 * ks], sacc[2 * ks + 1]);
+    float ps;
+    if constexpr (sizeof(T) == 2) {
+      // the sum of exactly the rounded weights the PV product uses
+      f32x4 s4 = mma16(ones_frag(), pf[0], zero4());
+      s4 = mma16(ones_frag(), pf[1], s4);
+      ps = s4[0];
+    } else {
+      float s = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += sacc[tb][i];
+      ps = col_sum4(s);
+    }
+    f32x4 oc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oc[mb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oc[mb] = mma16(f.v[mb][ks], pf[ks], oc[mb]);
+    if (r.valid) {
+      const float inv = 1.0f / ps;
+      T* dst = part + (((size_t)bg * N + r.pos) * K + r.slot) * G * DH + (size_t)hh * DH + gl * 4 * MB;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int m2 = 0; m2 < MB; m2 += 2) {
+          u16x8 hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[i] = f2bf(oc[m2][i] * inv);
+            hv[4 + i] = f2bf(oc[m2 + 1][i] * inv);
+          }
+          *reinterpret_cast<u16x8*>(dst + 4 * m2) = hv;
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(dst + 4 * mb) = oc[mb] * inv;
+      }
+    }
+  };
+  // row blocks w, w + 4, ...: the next block's queries are in flight while
+  // the current one is multiplied
+  RowBlock<T, DH> ra, rb;
+  load_rows(ra, w);
+  for (int j = w; j < nb; j += 8) {
+    if (j + 4 < nb) load_rows(rb, j + 4);
+    process(ra);
+    if (j + 4 >= nb) break;
+    if (j + 8 < nb) load_rows(ra, j + 8);
+    process(rb);
+  }
+}
+
+// ---------------------------------------------------------------- window pass
+// LDS slot holding one 64-token block: K rows and V^T rows (token-permuted),
+// pitches padded by 16 bytes so the 16-byte fragment reads of 16 lanes hit
+// distinct banks.
+template <typename T, int DH>
+struct WSlot {
+  static constexpr int VE = 16 / (int)sizeof(T);
+  static constexpr int KP = DH + VE;
+  static constexpr int VP = 64 + VE;
+  static constexpr int KE = 64 * KP;
+  static constexpr int ELEMS = KE + DH * VP;
+  static constexpr int KV = 64 * DH / VE;
+  static constexpr int VPT = 2 * KV / 256;
+};
+
+template <typename T, int G, int DH>
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_fwd_cm_window(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score,
+    const float* __restrict__ sel_lse, const T* __restrict__ part, T* __restrict__ o,
+    float* __restrict__ lse, int N, int Np, int Hkv, int K, int W, int S, float scale, int ntiles) {
+  typedef typename Frag<T>::type FT;
+  typedef WSlot<T, DH> SG;
+  constexpr int R = 128;
+  constexpr int TP = R / G;
+  constexpr int KS = DH / 32;
+  constexpr int MB = DH / 16;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* slots = reinterpret_cast<T*>(smem);  // [2][ELEMS]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gl = lane >> 4, cl = lane & 15;
+  int tx, bg;
+  xcd_block(tx, bg);
+  const int tile = ntiles - 1 - tx;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int Hq = Hkv * G;
+  const int p0 = tile * TP;
+  const int plast = min(p0 + TP - 1, N - 1);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (size_t)bg * N * DH, N * DH * (int)sizeof(T));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)bg * DH * Np, DH * Np * (int)sizeof(T));
+
+  // wave w owns rows 32 w + 16 cb + cl
+  FT qf[2][KS];
+  int prow[2], wsr[2];
+  float lsel[2], Lr[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = 32 * w + 16 * cb + cl;
+    const int pos = p0 + r / G, hh = r % G;
+    prow[cb] = pos < N ? pos : -1;
+    wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
+    const int pc = pos < N ? pos : N - 1;
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pc;
+    lsel[cb] = sel_lse[ro];
+    const T* src = q + ro * DH + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld8<T>(src + 32 * ks);
+  }
+  const int pw_lo = p0 + 32 * w / G;
+  const int pw_hi = min(p0 + (32 * w + 31) / G, N - 1);
+  const bool wave_live = pw_lo < N;
+  const bool all_valid = p0 + (32 * w + 31) / G < N;
+  const int ws_lo = wave_live ? n_distant(pw_lo, W, S) * S : 0;
+  const int ws_hi = wave_live ? n_distant(pw_hi, W, S) * S : 0;
+
+  float m[2], lsum[2];
+  f32x4 oacc[MB][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    m[cb] = NEG_INF;
+    lsum[cb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] = zero4();
+  }
+  const float sc2 = scale * LOG2E;
+
+  const int kv_lo = n_distant(p0, W, S) * S;
+  const int nW = (plast - kv_lo) / 64 + 1;
+  // blocks in flight in registers: two sets (blocks n + 2, n + 3) at d = 64,
+  // one (n + 2) at d = 128, where two sets push the wave past the register
+  // budget of two waves per SIMD
+  constexpr int NSET = DH == 64 ? 2 : 1;
+  u32x4 stg[2][SG::VPT];
+  auto issue = [&](u32x4 (&rg)[SG::VPT], int n) __attribute__((always_inline)) {
+    const int kv0 = kv_lo + 64 * min(n, nW - 1);
+#pragma unroll
+    for (int s = 0; s < SG::VPT; ++s) {
+      const int vi = tid + 256 * s;
+      if (s < SG::VPT / 2) {
+        const int tok = vi / (DH / SG::VE), pt = vi - tok * (DH / SG::VE);
+        rg[s] = buf_ld16(krs, ((kv0 + tok) * DH + pt * SG::VE) * (int)sizeof(T));
+      } else {
+        const int vj = vi - SG::KV;
+        const int dd = vj / (64 / SG::VE), pt = vj - dd * (64 / SG::VE);
+        rg[s] = buf_ld16(vrs, (dd * Np + kv0 + pt * SG::VE) * (int)sizeof(T));
+      }
+    }
+  };
+  auto commit = [&](const u32x4 (&rg)[SG::VPT], int slot) __attribute__((always_inline)) {
+    T* base = slots + slot * SG::ELEMS;
+#pragma unroll
+    for (int s = 0; s < SG::VPT; ++s) {
+      const int vi = tid + 256 * s;
+      T* dst;
+      if (s < SG::VPT / 2) {
+        const int tok = vi / (DH / SG::VE), pt = vi - tok * (DH / SG::VE);
+        dst = base + tok * SG::KP + pt * SG::VE;
+      } else {
+        const int vj = vi - SG::KV;
+        const int dd = vj / (64 / SG::VE), pt = vj - dd * (64 / SG::VE);
+        dst = base + SG::KE + dd * SG::VP + pt * SG::VE;
+      }
+      *reinterpret_cast<u32x4*>(dst) = rg[s];
+    }
+  };
+
+  // banded flash attention of the wave's rows over one staged block; the
+  // reference m moves only when a block's scores exceed it by more than 16
+  // (log2 units), or on a row's first scores
+  auto window_block = [&](const T* sl, int kv0, auto masked) __attribute__((always_inline)) {
+    constexpr bool MSK = decltype(masked)::value;
+    constexpr float SHIFT_AT = 16.f;
+    f32x4 sacc[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const FT kf = ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = mma16(kf, qf[cb][ks], sacc[tb][cb]);
+      }
+    }
+    float bmx[2];
+    bool shift = false;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float bmax = NEG_INF;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = sacc[tb][cb][i];
+          if constexpr (MSK) {
+            const int j = kv0 + 16 * tb + 4 * gl + i;
+            x = (j <= prow[cb] && j >= wsr[cb]) ? x : NEG_INF;
+            sacc[tb][cb][i] = x;
+          }
+          bmax = fmaxf(bmax, x);
+        }
+      bmx[cb] = col_max4(bmax) * sc2 - (m[cb] == NEG_INF ? 0.f : m[cb]);
+      shift |= bmx[cb] > SHIFT_AT || (m[cb] == NEG_INF && bmx[cb] != NEG_INF);
+    }
+    if (__ballot(shift) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const bool first = m[cb] == NEG_INF;
+        const bool up = bmx[cb] > SHIFT_AT || (first && bmx[cb] != NEG_INF);
+        const float dlt = up ? bmx[cb] : 0.f;
+        const float alpha = first ? 0.f : fast_exp2(-dlt);
+        if (up) m[cb] = (first ? 0.f : m[cb]) + dlt;
+        lsum[cb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
+      }
+    }
+    FT pf[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float mc = m[cb] == NEG_INF ? 0.f : m[cb];
+      float ps = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = fast_exp2(fmaf(sacc[tb][cb][i], sc2, -mc));
+          sacc[tb][cb][i] = pv;
+          ps += pv;
+        }
+      lsum[cb] += ps;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pf[cb][ks] = pk8<T>(sacc[2 * ks][cb], sacc[2 * ks + 1][cb]);
+    }
+    const T* vb = sl + SG::KE;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const FT vf = ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) oacc[mb][cb] = mma16(vf, pf[cb][ks], oacc[mb][cb]);
+      }
+  };
+
+  // one step: publish block n + 1 from register set rg into the other slot
+  // (whose block n - 1 every wave has finished), reload rg with block n + 3,
+  // then multiply block n
+  auto wstep = [&](int n, u32x4 (&rg)[SG::VPT]) __attribute__((always_inline)) {
+    commit(rg, (n + 1) & 1);
+    issue(rg, n + 1 + NSET);
+    const T* sl = slots + (n & 1) * SG::ELEMS;
+    const int kv0 = kv_lo + 64 * n;
+    if (wave_live && kv0 <= pw_hi && kv0 + 63 >= ws_lo) {
+      const bool clean = all_valid && kv0 >= ws_hi && kv0 + 63 <= pw_lo;
+      if (clean)
+        window_block(sl, kv0, std::false_type());
+      else
+        window_block(sl, kv0, std::true_type());
+    }
+    __syncthreads();
+  };
+  int n = 0;
+  if constexpr (NSET == 2) {
+    issue(stg[0], 0);
+    issue(stg[1], 1);
+    commit(stg[0], 0);
+    issue(stg[0], 2);
+    __syncthreads();
+    for (; n + 1 < nW; n += 2) {
+      wstep(n, stg[1]);
+      wstep(n + 1, stg[0]);
+    }
+    if (n < nW) wstep(n, stg[1]);
+  } else {
+    issue(stg[0], 0);
+    commit(stg[0], 0);
+    issue(stg[0], 1);
+    __syncthreads();
+    for (; n < nW; ++n) wstep(n, stg[0]);
+  }
+
+  // fusion normaliser and the window's weight exp(lse_W - L)
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float ls = col_sum4(lsum[cb]);
+    const float lW = (m[cb] + __log2f(ls)) * LN2;
+    const float mx = fmaxf(lW, lsel[cb]);
+    const bool live = prow[cb] >= 0;
+    const float L = live ? mx + __logf(__expf(lW - mx) + __expf(lsel[cb] - mx)) : 0.f;
+    const float coef = live ? fast_exp2(m[cb] - L * LOG2E) : 0.f;
+    Lr[cb] = L;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= coef;
+  }
+
+  // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (dims in
+  // fragment order: this lane's 4 MB values are contiguous)
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = 32 * w + 16 * cb + cl;
+    const int hh = r % G;
+    const int pc = prow[cb] >= 0 ? prow[cb] : N - 1;
+    const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pc;
+    const int32_t* ids = topk_idx + ((size_t)bg * N + pc) * K;
+    const float* scs = topk_score + ro * K;
+    const T* pb = part + ((size_t)bg * N + pc) * K * G * DH + (size_t)hh * DH + gl * 4 * MB;
+    for (int kk = 0; kk < K; ++kk) {
+      const int cc = ids[kk];
+      const float wk = (prow[cb] >= 0 && cc >= 0) ? __expf(scs[kk] - Lr[cb]) : 0.f;
+      if (__ballot(wk != 0.f) == 0) continue;
+      if (wk != 0.f) {
+        const T* src = pb + (size_t)kk * G * DH;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int m2 = 0; m2 < MB; m2 += 2) {
+            const u16x8 hv = *reinterpret_cast<const u16x8*>(src + 4 * m2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              oacc[m2][cb][i] += wk * bf2f(hv[i]);
+              oacc[m2 + 1][cb][i] += wk * bf2f(hv[4 + i]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            oacc[mb][cb] += wk * *reinterpret_cast<const f32x4*>(src + 4 * mb);
+        }
+      }
+    }
+  }
+
+  // write o and lse
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    if (prow[cb] < 0) continue;
+    const int r = 32 * w + 16 * cb + cl;
+    const size_t ro = ((size_t)b * Hq + g * G + r % G) * N + prow[cb];
+    if (gl == 0) lse[ro] = Lr[cb];
+    T* dst = o + ro * DH + 4 * gl;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if constexpr (sizeof(T) == 2) {
+        u16x4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = f2bf(oacc[mb][cb][i]);
+        *reinterpret_cast<u16x4*>(dst + 16 * mb) = hv;
+      } else {
+        *reinterpret_cast<f32x4*>(dst + 16 * mb) = oacc[mb][cb];
+      }
+    }
+  }
+}
+
+template <typename T, int DH>
+size_t cm_window_lds() {
+  return sizeof(T) * 2 * (size_t)WSlot<T, DH>::ELEMS;
+}
+
+template <typename T, int G, int DH>
+hipError_t cm_chunks_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                        const InvIndex& ix, void* part, hipStream_t st) {
+  hipLaunchKernelGGL((k_fwd_cm_chunks<T, G, DH>), dim3(p.C, p.B * p.Hkv), dim3(256), 0, st,
+                     (const T*)q, (const T*)k, (const T*)vt, ix.off, ix.lst, (T*)part, p.N, Np,
+                     p.Hkv, p.K, p.C, p.scale);
+  return hipGetLastError();
+}
+
+template <typename T, int G, int DH>
+hipError_t cm_window_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                        const int32_t* idx, const float* sc, const float* sl, const void* part,
+                        void* o, float* lse, hipStream_t st) {
+  constexpr int TP = 128 / G;
+  const int ntiles = (p.N + TP - 1) / TP;
+  const size_t lds = cm_window_lds<T, DH>();
+  auto kern = k_fwd_cm_window<T, G, DH>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const T*)q, (const T*)k,
+                     (const T*)vt, idx, sc, sl, (const T*)part, (T*)o, lse, p.N, Np, p.Hkv, p.K, p.W,
+                     p.S, p.scale, ntiles);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t cm_chunks_t(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                       const InvIndex& ix, void* part, hipStream_t st) {
+  switch (p.G * 1000 + p.d) {
+    case 1064: return cm_chunks_go<T, 1, 64>(p, q, k, vt, Np, ix, part, st);
+    case 1128: return cm_chunks_go<T, 1, 128>(p, q, k, vt, Np, ix, part, st);
+    case 2064: return cm_chunks_go<T, 2, 64>(p, q, k, vt, Np, ix, part, st);
+    case 2128: return cm_chunks_go<T, 2, 128>(p, q, k, vt, Np, ix, part, st);
+    case 4064: return cm_chunks_go<T, 4, 64>(p, q, k, vt, Np, ix, part, st);
+    case 4128: return cm_chunks_go<T, 4, 128>(p, q, k, vt, Np, ix, part, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t cm_window_t(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                       const int32_t* idx, const float* sc, const float* sl, const void* part,
+                       void* o, float* lse, hipStream_t st) {
+  switch (p.G * 1000 + p.d) {
+    case 1064: return cm_window_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    case 1128: return cm_window_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    case 2064: return cm_window_go<T, 2, 64>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    case 2128: return cm_window_go<T, 2, 128>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    case 4064: return cm_window_go<T, 4, 64>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    case 4128: return cm_window_go<T, 4, 128>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool fwd_cm_ok(const Dims& p) {
+  if (!inv_index_ok(p)) return false;
+  const size_t lds = p.dtype == 1 ? (p.d == 64 ? cm_window_lds<uint16_t, 64>() : cm_window_lds<uint16_t, 128>())
+                                  : (p.d == 64 ? cm_window_lds<float, 64>() : cm_window_lds<float, 128>());
+  return lds <= 160 * 1024 && (p.G == 1 || p.G == 2 || p.G == 4);
+}
+
+size_t fwd_cm_part_bytes(const Dims& p) {
+  return (size_t)p.B * p.Hkv * p.N * p.K * p.G * p.d * (p.dtype == 1 ? 2 : 4);
+}
+
+hipError_t launch_fwd_cm_chunks(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                                const InvIndex& ix, void* part, hipStream_t st) {
+  if (p.C == 0) return hipSuccess;
+  if (p.dtype == 1) return cm_chunks_t<uint16_t>(p, q, k, vt, Np, ix, part, st);
+  return cm_chunks_t<float>(p, q, k, vt, Np, ix, part, st);
+}
+
+hipError_t launch_fwd_cm_window(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                                const int32_t* topk_idx, const float* topk_score,
+                                const float* sel_lse, const void* part, void* o, float* lse,
+                                hipStream_t st) {
+  if (p.dtype == 1)
+    return cm_window_t<uint16_t>(p, q, k, vt, Np, topk_idx, topk_score, sel_lse, part, o, lse, st);
+  return cm_window_t<float>(p, q, k, vt, Np, topk_idx, topk_score, sel_lse, part, o, lse, st);
+}
+
+}  // namespace hils

@@ -151,6 +151,10 @@ struct FwdWs {
   float* s_T;
   float* sel_lse;
   void* vt;
+  // chunk-major strategy: the inverse index of the selection and the
+  // per-(position, slot, head) chunk outputs
+  hils::InvIndex ix;
+  void* part = nullptr;
 };
 size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
   Carver c(ws);
@@ -159,6 +163,12 @@ size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
   out->s_T = (float*)c.take(rows * d.K * sizeof(float));
   out->sel_lse = (float*)c.take(rows * sizeof(float));
   out->vt = c.take(hils::attn_fwd_vt_bytes(d));
+  if (hils::fwd_strategy_of(d) == HILS_FWD_CHUNK_MAJOR) {
+    const size_t ib = hils::inv_index_carve(d, nullptr, &out->ix);
+    void* ibase = c.take(ib);
+    hils::inv_index_carve(d, ibase, &out->ix);
+    out->part = c.take(hils::fwd_cm_part_bytes(d));
+  }
   return c.used;
 }
 size_t carve_route(const Dims& d, void* ws, RouteWs* rt) {
@@ -213,8 +223,9 @@ hils_status ws_check(void* ws, size_t have, size_t need) {
 
 hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
 
+// the forward's strategy fits the hardware (LDS, index limits)
 bool fwd_fits_lds(const Dims& d) {
-  if (d.fwd_strategy == HILS_FWD_CHUNK_MAJOR) return false;  // not built yet
+  if (hils::fwd_strategy_of(d) == HILS_FWD_CHUNK_MAJOR) return hils::fwd_cm_ok(d);
   return hils::attn_fwd_lds_bytes(d) <= 160 * 1024;
 }
 
@@ -384,7 +395,23 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
   if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   s = route_with_qcal(p->timing, d, w.rt, q, h, W_down, W_up, kL, e, topk_idx, w.s_T, w.sel_lse, st);
   if (s != HILS_OK) return s;
-  return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
+  if (hils::fwd_strategy_of(d) != HILS_FWD_CHUNK_MAJOR)
+    return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
+  // chunk-major: V^T copy, inverse index, selected chunks, then window + fusion
+  const int Np = (d.N + 63) / 64 * 64;
+  return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] {
+    hipError_t e2 = hils::launch_vt_perm(d, v, w.vt, st);
+    if (e2 != hipSuccess) return e2;
+    e2 = timed(p->timing, HILS_STEP_CHUNKS, st, [&] {
+      hipError_t e3 = hils::launch_inv_index(d, topk_idx, w.ix, st);
+      if (e3 != hipSuccess) return e3;
+      return hils::launch_fwd_cm_chunks(d, q, k, w.vt, Np, w.ix, w.part, st);
+    });
+    if (e2 != hipSuccess) return e2;
+    return timed(p->timing, HILS_STEP_WINDOW, st, [&] {
+      return hils::launch_fwd_cm_window(d, q, k, w.vt, Np, topk_idx, w.s_T, w.sel_lse, w.part, o, lse, st);
+    });
+  }));
 }
 
 hils_status hils_attn_bwd(const hils_problem* p, const void* q, const void* k, const void* v,

@@ -46,12 +46,46 @@ hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const vo
                            const int32_t* topk_idx, const float* topk_score, const float* sel_lse,
                            void* o, float* lse, hipStream_t st);
 size_t attn_fwd_lds_bytes(const Dims& p);
+// the strategy a forward call runs: 1 shared block, 2 bucketed, 3 chunk-major
+int fwd_strategy_of(const Dims& p);
 // bucketed chunk strategy of the forward (attn_fwd_sparse.hip)
 size_t fwd_sparse_lds_bytes(const Dims& p);
 hipError_t launch_fwd_sparse(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                              const int32_t* idx, const float* sc, const float* sl, void* o,
                              float* lse, hipStream_t st);
 size_t attn_fwd_vt_bytes(const Dims& p);
+
+// Inverse index of a selection (inv_index.hip): per (b, KV head) and chunk,
+// the (position << 6 | slot) entries that selected it, ascending by position
+// (deterministic). off [B Hkv][C + 1]: first entry of each chunk's list in lst
+// [B Hkv][N K]; cnt: per-range counts (scratch).
+constexpr int INV_MAX_CHUNKS = 16384;
+struct InvIndex {
+  int* cnt = nullptr;
+  int* off = nullptr;
+  int* lst = nullptr;
+  int ns = 1;
+};
+int inv_ranges(const Dims& p);
+bool inv_index_ok(const Dims& p);
+size_t inv_index_carve(const Dims& p, void* base, InvIndex* out);
+hipError_t launch_inv_index(const Dims& p, const int32_t* topk_idx, const InvIndex& ix,
+                            hipStream_t st);
+
+// Chunk-major forward (attn_fwd_cm.hip): each selected chunk is loaded once
+// and its selecting rows write their normalised chunk outputs O_c (in the
+// input dtype, dims in MFMA-fragment order) to part [B Hkv][N][K][G][d]; the
+// window kernel then computes the window attention, the fusion normaliser and
+// o = exp(lse_W - L) O_W + sum_k exp(s_k - L) O_{c_k}.
+bool fwd_cm_ok(const Dims& p);
+size_t fwd_cm_part_bytes(const Dims& p);
+hipError_t launch_fwd_cm_chunks(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                                const InvIndex& ix, void* part, hipStream_t st);
+hipError_t launch_fwd_cm_window(const Dims& p, const void* q, const void* k, const void* vt, int Np,
+                                const int32_t* topk_idx, const float* topk_score,
+                                const float* sel_lse, const void* part, void* o, float* lse,
+                                hipStream_t st);
+hipError_t launch_vt_perm(const Dims& p, const void* v, void* vt, hipStream_t st);
 
 // Decode.
 size_t decode_workspace(const Dims& p);

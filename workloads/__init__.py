@@ -186,6 +186,12 @@ WORKLOADS: Dict[str, Workload] = {
     "train_345m": Workload("train_345m", seed=4, dtype="bf16", B=8, Hq=16, Hkv=16, d=64,
                            N=8192, S=64, K=16, W=512, D=1024, r=32, e_range=2.0,
                            mode="train"),
+    # the paper's long-context prefill measurement (Fig. 6): the 345M shape at
+    # batch 1, chunk 64, top-32, a 512-token window, 524288 tokens; one
+    # planted needle chunk per 16384-token segment
+    "prefill_345m_512k": Workload("prefill_345m_512k", seed=5, dtype="bf16", B=1, Hq=16, Hkv=16,
+                                  d=64, N=524288, S=64, K=32, W=512, D=1024, r=32, e_range=2.0,
+                                  needle="segments"),
     # the 345M prefill with queries correlated along positions (AR(1), 0.97): adjacent
     # queries share ~92 % of their top-16, the locality the paper measures on trained
     # models (Fig. 7) and that independent queries lack

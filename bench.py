@@ -97,12 +97,12 @@ def recorded_traffic():
         return None
 
 
-def profile_sample(torch, L):
+def profile_sample(torch, L, workload="prefill_345m"):
     """A short fixed run for rocprofv3 counter passes: three prefill forwards
-    of the default workload, then the calibration copy (1 GiB fp32 read, 1 GiB
+    of the workload, then the calibration copy (1 GiB fp32 read, 1 GiB
     written) whose FETCH_SIZE / WRITE_SIZE scale the kernel's counters."""
     from workloads import WORKLOADS, make_inputs
-    wl = WORKLOADS["prefill_345m"]
+    wl = WORKLOADS[workload]
     t = make_inputs(wl, device="cuda")
     bufs = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
     for _ in range(3):
@@ -640,7 +640,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     if args.profile_sample:
-        profile_sample(torch, L)
+        profile_sample(torch, L, args.workload)
         return
     res, wl = bench_prefill(args, torch, L, None)
     legs = set(args.legs.split(","))

@@ -16,18 +16,22 @@
 // output per (position, slot, head) written and read back once.
 //
 //   k_fwd_cm_chunks  one workgroup per (chunk, b, KV head); the chunk's K rows
-//                    and V^T stay in every wave's registers while the waves
-//                    take 16-row blocks of the chunk's rows (16 / G entries x
-//                    G heads): S^T = K Q^T, softmax over the 64 tokens,
-//                    O_c^T = V^T P^T, O_c normalised and stored in the input
-//                    dtype at part[b, g][pos][slot][head] (dims in MFMA
-//                    D-fragment order: lane group gl's dims 16 mb + 4 gl + i
-//                    contiguous, so both kernels move 16-byte vectors).
+//                    and V^T sit in LDS while the waves take 16-row blocks of
+//                    the chunk's rows (16 / G entries x G heads): S^T = K Q^T,
+//                    softmax over the 64 tokens, O_c^T = V^T P^T, O_c
+//                    normalised and stored in the input dtype at
+//                    part[b, g][entry][head], entries in the inverse index's
+//                    order (each workgroup writes one contiguous run; dims in
+//                    MFMA D-fragment order: lane group gl's dims
+//                    16 mb + 4 gl + i contiguous, so both kernels move
+//                    16-byte vectors).
 //   k_fwd_cm_window  query tiles of 128 rows (128 / G positions x G heads):
 //                    banded flash attention over the window with K / V^T
 //                    blocks staged through LDS for the four waves; then
 //                    L = log(exp(lse_W) + exp(lse_sel)) and
-//                    o = exp(lse_W - L) O_W + sum_k exp(s_k - L) O_{c_k}.
+//                    o = exp(lse_W - L) O_W + sum_k exp(s_k - L) O_{c_k},
+//                    each O_{c_k} found through the entry index of
+//                    (position, slot k) that the inverse index records.
 #include "hils_common.h"
 #include "hils_internal.h"
 
@@ -38,53 +42,104 @@ namespace hils {
 
 namespace {
 
-// ---------------------------------------------------------------- chunk pass
+// ---------------------------------------------------------------- LDS slot
+// One 64-token block: K rows and V^T rows (token-permuted), pitches padded by
+// 16 bytes so the 16-byte fragment reads of 16 lanes hit distinct banks.
 template <typename T, int DH>
-struct ChunkRegs {
-  typename Frag<T>::type k[4][DH / 32];  // A operand of S^T: K rows (tokens)
-  typename Frag<T>::type v[DH / 16][2];  // A operand of O^T: V^T rows (dims), token-permuted
+struct WSlot {
+  static constexpr int VE = 16 / (int)sizeof(T);
+  static constexpr int KP = DH + VE;
+  static constexpr int VP = 64 + VE;
+  static constexpr int KE = 64 * KP;
+  static constexpr int ELEMS = KE + DH * VP;
+  static constexpr int KV = 64 * DH / VE;
+  static constexpr int VPT = 2 * KV / 256;
 };
 
+// ---------------------------------------------------------------- chunk pass
 template <typename T, int DH>
 struct RowBlock {
   typename Frag<T>::type q[DH / 32];
-  int pos, slot;
+  int pos, slot;  // slot: the row block's entry index within the chunk's list
   bool valid;
 };
 
+// The chunk's K and V^T sit in LDS (read as fragments by each row block), so
+// that a wave holds only its row blocks: four waves per SIMD at bf16, and the
+// queries of the next two row blocks in flight while one is multiplied.
+// Work items: a chunk's list cut into pieces of at most CM_ITEM_ROWS rows
+// (CM_ITEM_ROWS / G entries), so that a chunk chosen by a large share of the
+// positions (a high entropy bias makes some chunks far more popular than
+// others) is spread over many workgroups instead of one. One workgroup per
+// (b, KV head) lists them in chunk order: item = (chunk, first entry).
+constexpr int CM_ITEM_ROWS = 1024;
+
+__global__ __launch_bounds__(256) void k_cm_items(const int* __restrict__ off, int2* __restrict__ items,
+                                                  int* __restrict__ nitems, int* __restrict__ scratch,
+                                                  int C, int E, int maxit) {
+  __shared__ int wsum[4];
+  const int bg = blockIdx.x;
+  const int* ob = off + (size_t)bg * (C + 1);
+  int* cnt = scratch + (size_t)bg * C;
+  for (int c = threadIdx.x; c < C; c += 256) cnt[c] = (ob[c + 1] - ob[c] + E - 1) / E;
+  __syncthreads();
+  const int tot = block_excl_scan(cnt, C, wsum);
+  int2* it = items + (size_t)bg * maxit;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    const int n = ob[c + 1] - ob[c];
+    for (int s0 = 0, j = cnt[c]; s0 < n; s0 += E, ++j) it[j] = int2{c, s0};
+  }
+  if (threadIdx.x == 0) nitems[bg] = tot;
+}
+
 template <typename T, int G, int DH>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_fwd_cm_chunks(
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? (DH == 64 ? 3 : 2) : 1) void k_fwd_cm_chunks(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
-    const int* __restrict__ off, const int* __restrict__ lst, T* __restrict__ part, int N, int Np,
-    int Hkv, int K, int C, float scale) {
+    const int* __restrict__ off, const int* __restrict__ lst, const int2* __restrict__ items,
+    const int* __restrict__ nitems, T* __restrict__ part, int N, int Np, int Hkv, int K, int C,
+    int maxit, float scale) {
   typedef typename Frag<T>::type FT;
+  typedef WSlot<T, DH> SG;
   constexpr int KS = DH / 32;
   constexpr int MB = DH / 16;
   constexpr int EPB = 16 / G;  // entries per 16-row block
-  const int c = blockIdx.x, bg = blockIdx.y;
+  constexpr int E = CM_ITEM_ROWS / G;  // entries per work item
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* sl = reinterpret_cast<T*>(smem);
+  const int bg = blockIdx.y;
+  if ((int)blockIdx.x >= nitems[bg]) return;  // uniform over the workgroup
+  const int2 item = items[(size_t)bg * maxit + blockIdx.x];
+  const int c = item.x;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int Hq = Hkv * G;
   const int* ob = off + (size_t)bg * (C + 1);
-  const int e0 = ob[c], n = ob[c + 1] - e0;
+  const int e0 = ob[c] + item.y, n = min(E, ob[c + 1] - e0);
   const int nb = (n + EPB - 1) / EPB;
-  const int lane = threadIdx.x & 63, gl = lane >> 4, cl = lane & 15;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w >= nb) return;  // no barrier below: idle waves leave early
+  const int tid = threadIdx.x, lane = tid & 63, gl = lane >> 4, cl = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // the chunk's K rows and V^T columns as fragments (every wave holds them)
-  ChunkRegs<T, DH> f;
+  // stage the chunk's K rows and V^T columns (16-byte vectors)
   {
-    const T* kb = k + ((size_t)bg * N + (size_t)c * 64) * DH + 8 * gl;
+    const T* kb = k + ((size_t)bg * N + (size_t)c * 64) * DH;
+    const T* vb = vt + (size_t)bg * DH * Np + (size_t)c * 64;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) f.k[tb][ks] = ld8<T>(kb + (size_t)(16 * tb + cl) * DH + 32 * ks);
-    const T* vb = vt + (size_t)bg * DH * Np + (size_t)c * 64 + 8 * gl;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) f.v[mb][ks] = ld8<T>(vb + (size_t)(16 * mb + cl) * Np + 32 * ks);
+    for (int s2 = 0; s2 < SG::VPT; ++s2) {
+      const int vi = tid + 256 * s2;
+      if (s2 < SG::VPT / 2) {
+        const int tok = vi / (DH / SG::VE), pt = vi - tok * (DH / SG::VE);
+        *reinterpret_cast<u32x4*>(sl + tok * SG::KP + pt * SG::VE) =
+            *reinterpret_cast<const u32x4*>(kb + (size_t)tok * DH + pt * SG::VE);
+      } else {
+        const int vj = vi - SG::KV;
+        const int dd = vj / (64 / SG::VE), pt = vj - dd * (64 / SG::VE);
+        *reinterpret_cast<u32x4*>(sl + SG::KE + dd * SG::VP + pt * SG::VE) =
+            *reinterpret_cast<const u32x4*>(vb + (size_t)dd * Np + pt * SG::VE);
+      }
+    }
   }
+  __syncthreads();
+  if (w >= nb) return;  // no barrier below
+
   const int* lb = lst + (size_t)bg * N * K + e0;
   const int hh = cl % G;
   const float sc2 = scale * LOG2E;
@@ -94,7 +149,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_fwd_cm_chunks(
     r.valid = x < n;
     const int en = lb[min(x, n - 1)];
     r.pos = en >> 6;
-    r.slot = en & 63;
+    r.slot = x;  // entry index within the chunk's list
     const T* src = q + (((size_t)b * Hq + g * G + hh) * N + r.pos) * DH + 8 * gl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) r.q[ks] = ld8<T>(src + 32 * ks);
@@ -105,7 +160,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_fwd_cm_chunks(
     for (int tb = 0; tb < 4; ++tb) {
       sacc[tb] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[tb] = mma16(f.k[tb][ks], r.q[ks], sacc[tb]);
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[tb] = mma16(ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks), r.q[ks], sacc[tb]);
     }
     float mx = NEG_INF;
 #pragma unroll
@@ -137,13 +193,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_fwd_cm_chunks(
     f32x4 oc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) oc[mb] = zero4();
+    const T* vbs = sl + SG::KE;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oc[mb] = mma16(f.v[mb][ks], pf[ks], oc[mb]);
+      for (int ks = 0; ks < 2; ++ks)
+        oc[mb] = mma16(ld8<T>(vbs + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks), pf[ks], oc[mb]);
     if (r.valid) {
       const float inv = 1.0f / ps;
-      T* dst = part + (((size_t)bg * N + r.pos) * K + r.slot) * G * DH + (size_t)hh * DH + gl * 4 * MB;
+      T* dst = part + ((size_t)bg * N * K + e0 + r.slot) * G * DH + (size_t)hh * DH + gl * 4 * MB;
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int m2 = 0; m2 < MB; m2 += 2) {
@@ -161,40 +219,43 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_fwd_cm_chunks(
       }
     }
   };
-  // row blocks w, w + 4, ...: the next block's queries are in flight while
-  // the current one is multiplied
-  RowBlock<T, DH> ra, rb;
-  load_rows(ra, w);
-  for (int j = w; j < nb; j += 8) {
-    if (j + 4 < nb) load_rows(rb, j + 4);
-    process(ra);
-    if (j + 4 >= nb) break;
-    if (j + 8 < nb) load_rows(ra, j + 8);
-    process(rb);
+  // row blocks w, w + 4, ...: the queries of the next two (d = 64) or the
+  // next one (d = 128, register budget) are in flight while one is multiplied
+  if constexpr (DH == 64) {
+    RowBlock<T, DH> r0, r1, r2;
+    load_rows(r0, w);
+    if (w + 4 < nb) load_rows(r1, w + 4);
+    for (int j = w; j < nb; j += 12) {
+      if (j + 8 < nb) load_rows(r2, j + 8);
+      process(r0);
+      if (j + 4 >= nb) break;
+      if (j + 12 < nb) load_rows(r0, j + 12);
+      process(r1);
+      if (j + 8 >= nb) break;
+      if (j + 16 < nb) load_rows(r1, j + 16);
+      process(r2);
+    }
+  } else {
+    RowBlock<T, DH> r0, r1;
+    load_rows(r0, w);
+    for (int j = w; j < nb; j += 8) {
+      if (j + 4 < nb) load_rows(r1, j + 4);
+      process(r0);
+      if (j + 4 >= nb) break;
+      if (j + 8 < nb) load_rows(r0, j + 8);
+      process(r1);
+    }
   }
 }
 
 // ---------------------------------------------------------------- window pass
-// LDS slot holding one 64-token block: K rows and V^T rows (token-permuted),
-// pitches padded by 16 bytes so the 16-byte fragment reads of 16 lanes hit
-// distinct banks.
-template <typename T, int DH>
-struct WSlot {
-  static constexpr int VE = 16 / (int)sizeof(T);
-  static constexpr int KP = DH + VE;
-  static constexpr int VP = 64 + VE;
-  static constexpr int KE = 64 * KP;
-  static constexpr int ELEMS = KE + DH * VP;
-  static constexpr int KV = 64 * DH / VE;
-  static constexpr int VPT = 2 * KV / 256;
-};
-
 template <typename T, int G, int DH>
 __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_fwd_cm_window(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score,
-    const float* __restrict__ sel_lse, const T* __restrict__ part, T* __restrict__ o,
-    float* __restrict__ lse, int N, int Np, int Hkv, int K, int W, int S, float scale, int ntiles) {
+    const float* __restrict__ sel_lse, const int* __restrict__ rank, const T* __restrict__ part,
+    T* __restrict__ o, float* __restrict__ lse, int N, int Np, int Hkv, int K, int W, int S,
+    float scale, int ntiles) {
   typedef typename Frag<T>::type FT;
   typedef WSlot<T, DH> SG;
   constexpr int R = 128;
@@ -424,36 +485,56 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
   }
 
   // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (dims in
-  // fragment order: this lane's 4 MB values are contiguous)
+  // fragment order: this lane's 4 MB values are contiguous). Four slots at a
+  // time: their weights, then all their loads, then the sums, so that the
+  // loads are in flight together.
+  constexpr int VPS = 4 * MB * (int)sizeof(T) / 16;  // 16-byte vectors per lane and slot
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int r = 32 * w + 16 * cb + cl;
     const int hh = r % G;
-    const int pc = prow[cb] >= 0 ? prow[cb] : N - 1;
+    const bool live = prow[cb] >= 0;
+    const int pc = live ? prow[cb] : N - 1;
     const size_t ro = ((size_t)b * Hq + g * G + hh) * N + pc;
     const int32_t* ids = topk_idx + ((size_t)bg * N + pc) * K;
+    const int* rks = rank + ((size_t)bg * N + pc) * K;
     const float* scs = topk_score + ro * K;
-    const T* pb = part + ((size_t)bg * N + pc) * K * G * DH + (size_t)hh * DH + gl * 4 * MB;
-    for (int kk = 0; kk < K; ++kk) {
-      const int cc = ids[kk];
-      const float wk = (prow[cb] >= 0 && cc >= 0) ? __expf(scs[kk] - Lr[cb]) : 0.f;
-      if (__ballot(wk != 0.f) == 0) continue;
-      if (wk != 0.f) {
-        const T* src = pb + (size_t)kk * G * DH;
+    const T* pb = part + (size_t)bg * N * K * G * DH + (size_t)hh * DH + gl * 4 * MB;
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      float wk[4];
+      int ek[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = min(k0 + j, K - 1);
+        const int cc = ids[kk];
+        const bool sel = live && k0 + j < K && cc >= 0;
+        wk[j] = sel ? __expf(scs[kk] - Lr[cb]) : 0.f;
+        ek[j] = sel ? rks[kk] : 0;
+      }
+      u32x4 pv[4][VPS];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(pb + (size_t)ek[j] * G * DH);
+#pragma unroll
+        for (int x = 0; x < VPS; ++x)
+          pv[j][x] = wk[j] != 0.f ? src[x] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int m2 = 0; m2 < MB; m2 += 2) {
-            const u16x8 hv = *reinterpret_cast<const u16x8*>(src + 4 * m2);
+          for (int x = 0; x < VPS; ++x) {
+            const u16x8 hv = __builtin_bit_cast(u16x8, pv[j][x]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              oacc[m2][cb][i] += wk * bf2f(hv[i]);
-              oacc[m2 + 1][cb][i] += wk * bf2f(hv[4 + i]);
+              oacc[2 * x][cb][i] += wk[j] * bf2f(hv[i]);
+              oacc[2 * x + 1][cb][i] += wk[j] * bf2f(hv[4 + i]);
             }
           }
         } else {
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            oacc[mb][cb] += wk * *reinterpret_cast<const f32x4*>(src + 4 * mb);
+          for (int x = 0; x < VPS; ++x)
+            oacc[x][cb] += wk[j] * __builtin_bit_cast(f32x4, pv[j][x]);
         }
       }
     }
@@ -486,19 +567,35 @@ size_t cm_window_lds() {
   return sizeof(T) * 2 * (size_t)WSlot<T, DH>::ELEMS;
 }
 
+// an upper bound of the work items of one (b, KV head): the sum over chunks
+// of ceil(n_c / E) is at most N K / E + C
+int cm_max_items(const Dims& p) {
+  const long E = CM_ITEM_ROWS / p.G;
+  return (int)(((long)p.N * p.K + E - 1) / E + p.C);
+}
+
 template <typename T, int G, int DH>
 hipError_t cm_chunks_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                        const InvIndex& ix, void* part, hipStream_t st) {
-  hipLaunchKernelGGL((k_fwd_cm_chunks<T, G, DH>), dim3(p.C, p.B * p.Hkv), dim3(256), 0, st,
-                     (const T*)q, (const T*)k, (const T*)vt, ix.off, ix.lst, (T*)part, p.N, Np,
-                     p.Hkv, p.K, p.C, p.scale);
+                        const InvIndex& ix, const CmItems& it, void* part, hipStream_t st) {
+  const int maxit = cm_max_items(p);
+  hipLaunchKernelGGL(k_cm_items, dim3(p.B * p.Hkv), dim3(256), 0, st, ix.off, it.items, it.nitems,
+                     it.scratch, p.C, CM_ITEM_ROWS / G, maxit);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds = sizeof(T) * (size_t)WSlot<T, DH>::ELEMS;
+  auto kern = k_fwd_cm_chunks<T, G, DH>;
+  err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(maxit, p.B * p.Hkv), dim3(256), lds, st,
+                     (const T*)q, (const T*)k, (const T*)vt, ix.off, ix.lst, it.items, it.nitems,
+                     (T*)part, p.N, Np, p.Hkv, p.K, p.C, maxit, p.scale);
   return hipGetLastError();
 }
 
 template <typename T, int G, int DH>
 hipError_t cm_window_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                        const int32_t* idx, const float* sc, const float* sl, const void* part,
-                        void* o, float* lse, hipStream_t st) {
+                        const int32_t* idx, const float* sc, const float* sl, const int* rank,
+                        const void* part, void* o, float* lse, hipStream_t st) {
   constexpr int TP = 128 / G;
   const int ntiles = (p.N + TP - 1) / TP;
   const size_t lds = cm_window_lds<T, DH>();
@@ -506,36 +603,36 @@ hipError_t cm_window_go(const Dims& p, const void* q, const void* k, const void*
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const T*)q, (const T*)k,
-                     (const T*)vt, idx, sc, sl, (const T*)part, (T*)o, lse, p.N, Np, p.Hkv, p.K, p.W,
-                     p.S, p.scale, ntiles);
+                     (const T*)vt, idx, sc, sl, rank, (const T*)part, (T*)o, lse, p.N, Np, p.Hkv, p.K,
+                     p.W, p.S, p.scale, ntiles);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t cm_chunks_t(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                       const InvIndex& ix, void* part, hipStream_t st) {
+                       const InvIndex& ix, const CmItems& it, void* part, hipStream_t st) {
   switch (p.G * 1000 + p.d) {
-    case 1064: return cm_chunks_go<T, 1, 64>(p, q, k, vt, Np, ix, part, st);
-    case 1128: return cm_chunks_go<T, 1, 128>(p, q, k, vt, Np, ix, part, st);
-    case 2064: return cm_chunks_go<T, 2, 64>(p, q, k, vt, Np, ix, part, st);
-    case 2128: return cm_chunks_go<T, 2, 128>(p, q, k, vt, Np, ix, part, st);
-    case 4064: return cm_chunks_go<T, 4, 64>(p, q, k, vt, Np, ix, part, st);
-    case 4128: return cm_chunks_go<T, 4, 128>(p, q, k, vt, Np, ix, part, st);
+    case 1064: return cm_chunks_go<T, 1, 64>(p, q, k, vt, Np, ix, it, part, st);
+    case 1128: return cm_chunks_go<T, 1, 128>(p, q, k, vt, Np, ix, it, part, st);
+    case 2064: return cm_chunks_go<T, 2, 64>(p, q, k, vt, Np, ix, it, part, st);
+    case 2128: return cm_chunks_go<T, 2, 128>(p, q, k, vt, Np, ix, it, part, st);
+    case 4064: return cm_chunks_go<T, 4, 64>(p, q, k, vt, Np, ix, it, part, st);
+    case 4128: return cm_chunks_go<T, 4, 128>(p, q, k, vt, Np, ix, it, part, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
 hipError_t cm_window_t(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                       const int32_t* idx, const float* sc, const float* sl, const void* part,
-                       void* o, float* lse, hipStream_t st) {
+                       const int32_t* idx, const float* sc, const float* sl, const int* rank,
+                       const void* part, void* o, float* lse, hipStream_t st) {
   switch (p.G * 1000 + p.d) {
-    case 1064: return cm_window_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
-    case 1128: return cm_window_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
-    case 2064: return cm_window_go<T, 2, 64>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
-    case 2128: return cm_window_go<T, 2, 128>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
-    case 4064: return cm_window_go<T, 4, 64>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
-    case 4128: return cm_window_go<T, 4, 128>(p, q, k, vt, Np, idx, sc, sl, part, o, lse, st);
+    case 1064: return cm_window_go<T, 1, 64>(p, q, k, vt, Np, idx, sc, sl, rank, part, o, lse, st);
+    case 1128: return cm_window_go<T, 1, 128>(p, q, k, vt, Np, idx, sc, sl, rank, part, o, lse, st);
+    case 2064: return cm_window_go<T, 2, 64>(p, q, k, vt, Np, idx, sc, sl, rank, part, o, lse, st);
+    case 2128: return cm_window_go<T, 2, 128>(p, q, k, vt, Np, idx, sc, sl, rank, part, o, lse, st);
+    case 4064: return cm_window_go<T, 4, 64>(p, q, k, vt, Np, idx, sc, sl, rank, part, o, lse, st);
+    case 4128: return cm_window_go<T, 4, 128>(p, q, k, vt, Np, idx, sc, sl, rank, part, o, lse, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -553,20 +650,35 @@ size_t fwd_cm_part_bytes(const Dims& p) {
   return (size_t)p.B * p.Hkv * p.N * p.K * p.G * p.d * (p.dtype == 1 ? 2 : 4);
 }
 
+size_t fwd_cm_items_carve(const Dims& p, void* base, CmItems* out) {
+  char* c = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    void* ptr = c ? c + o : nullptr;
+    o += (bytes + 255) & ~(size_t)255;
+    return ptr;
+  };
+  const size_t bg = (size_t)p.B * p.Hkv;
+  out->items = (int2*)take(bg * (size_t)cm_max_items(p) * sizeof(int2));
+  out->nitems = (int*)take(bg * sizeof(int));
+  out->scratch = (int*)take(bg * (size_t)p.C * sizeof(int));
+  return o;
+}
+
 hipError_t launch_fwd_cm_chunks(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                                const InvIndex& ix, void* part, hipStream_t st) {
+                                const InvIndex& ix, const CmItems& it, void* part, hipStream_t st) {
   if (p.C == 0) return hipSuccess;
-  if (p.dtype == 1) return cm_chunks_t<uint16_t>(p, q, k, vt, Np, ix, part, st);
-  return cm_chunks_t<float>(p, q, k, vt, Np, ix, part, st);
+  if (p.dtype == 1) return cm_chunks_t<uint16_t>(p, q, k, vt, Np, ix, it, part, st);
+  return cm_chunks_t<float>(p, q, k, vt, Np, ix, it, part, st);
 }
 
 hipError_t launch_fwd_cm_window(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                                 const int32_t* topk_idx, const float* topk_score,
-                                const float* sel_lse, const void* part, void* o, float* lse,
-                                hipStream_t st) {
+                                const float* sel_lse, const int* rank, const void* part, void* o,
+                                float* lse, hipStream_t st) {
   if (p.dtype == 1)
-    return cm_window_t<uint16_t>(p, q, k, vt, Np, topk_idx, topk_score, sel_lse, part, o, lse, st);
-  return cm_window_t<float>(p, q, k, vt, Np, topk_idx, topk_score, sel_lse, part, o, lse, st);
+    return cm_window_t<uint16_t>(p, q, k, vt, Np, topk_idx, topk_score, sel_lse, rank, part, o, lse, st);
+  return cm_window_t<float>(p, q, k, vt, Np, topk_idx, topk_score, sel_lse, rank, part, o, lse, st);
 }
 
 }  // namespace hils

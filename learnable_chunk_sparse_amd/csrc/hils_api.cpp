@@ -154,6 +154,7 @@ struct FwdWs {
   // chunk-major strategy: the inverse index of the selection and the
   // per-(position, slot, head) chunk outputs
   hils::InvIndex ix;
+  hils::CmItems items;
   void* part = nullptr;
 };
 size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
@@ -164,9 +165,11 @@ size_t carve_fwd(const Dims& d, void* ws, FwdWs* out) {
   out->sel_lse = (float*)c.take(rows * sizeof(float));
   out->vt = c.take(hils::attn_fwd_vt_bytes(d));
   if (hils::fwd_strategy_of(d) == HILS_FWD_CHUNK_MAJOR) {
-    const size_t ib = hils::inv_index_carve(d, nullptr, &out->ix);
+    const size_t ib = hils::inv_index_carve(d, nullptr, &out->ix, true);
     void* ibase = c.take(ib);
-    hils::inv_index_carve(d, ibase, &out->ix);
+    hils::inv_index_carve(d, ibase, &out->ix, true);
+    void* itb = c.take(hils::fwd_cm_items_carve(d, nullptr, &out->items));
+    hils::fwd_cm_items_carve(d, itb, &out->items);
     out->part = c.take(hils::fwd_cm_part_bytes(d));
   }
   return c.used;
@@ -405,11 +408,11 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
     e2 = timed(p->timing, HILS_STEP_CHUNKS, st, [&] {
       hipError_t e3 = hils::launch_inv_index(d, topk_idx, w.ix, st);
       if (e3 != hipSuccess) return e3;
-      return hils::launch_fwd_cm_chunks(d, q, k, w.vt, Np, w.ix, w.part, st);
+      return hils::launch_fwd_cm_chunks(d, q, k, w.vt, Np, w.ix, w.items, w.part, st);
     });
     if (e2 != hipSuccess) return e2;
     return timed(p->timing, HILS_STEP_WINDOW, st, [&] {
-      return hils::launch_fwd_cm_window(d, q, k, w.vt, Np, topk_idx, w.s_T, w.sel_lse, w.part, o, lse, st);
+      return hils::launch_fwd_cm_window(d, q, k, w.vt, Np, topk_idx, w.s_T, w.sel_lse, w.ix.rank, w.part, o, lse, st);
     });
   }));
 }

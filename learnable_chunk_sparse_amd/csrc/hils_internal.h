@@ -64,27 +64,36 @@ struct InvIndex {
   int* cnt = nullptr;
   int* off = nullptr;
   int* lst = nullptr;
+  int* rank = nullptr;  // optional [B Hkv][N][K]: list index of (position, slot)
   int ns = 1;
 };
 int inv_ranges(const Dims& p);
 bool inv_index_ok(const Dims& p);
-size_t inv_index_carve(const Dims& p, void* base, InvIndex* out);
+size_t inv_index_carve(const Dims& p, void* base, InvIndex* out, bool with_rank = false);
 hipError_t launch_inv_index(const Dims& p, const int32_t* topk_idx, const InvIndex& ix,
                             hipStream_t st);
 
 // Chunk-major forward (attn_fwd_cm.hip): each selected chunk is loaded once
 // and its selecting rows write their normalised chunk outputs O_c (in the
-// input dtype, dims in MFMA-fragment order) to part [B Hkv][N][K][G][d]; the
-// window kernel then computes the window attention, the fusion normaliser and
-// o = exp(lse_W - L) O_W + sum_k exp(s_k - L) O_{c_k}.
+// input dtype, dims in MFMA-fragment order) to part [B Hkv][entry][G][d] in
+// the inverse index's order; the window kernel then computes the window
+// attention, the fusion normaliser and o = exp(lse_W - L) O_W +
+// sum_k exp(s_k - L) O_{c_k}, finding each entry through ix.rank.
 bool fwd_cm_ok(const Dims& p);
 size_t fwd_cm_part_bytes(const Dims& p);
+// work items of the chunk pass (pieces of the chunks' lists)
+struct CmItems {
+  int2* items = nullptr;
+  int* nitems = nullptr;
+  int* scratch = nullptr;
+};
+size_t fwd_cm_items_carve(const Dims& p, void* base, CmItems* out);
 hipError_t launch_fwd_cm_chunks(const Dims& p, const void* q, const void* k, const void* vt, int Np,
-                                const InvIndex& ix, void* part, hipStream_t st);
+                                const InvIndex& ix, const CmItems& it, void* part, hipStream_t st);
 hipError_t launch_fwd_cm_window(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                                 const int32_t* topk_idx, const float* topk_score,
-                                const float* sel_lse, const void* part, void* o, float* lse,
-                                hipStream_t st);
+                                const float* sel_lse, const int* rank, const void* part, void* o,
+                                float* lse, hipStream_t st);
 hipError_t launch_vt_perm(const Dims& p, const void* v, void* vt, hipStream_t st);
 
 // Decode.

@@ -18,7 +18,9 @@
 //               chunk comes from an LDS bit mask (bit = position in the step,
 //               set with an order-free atomic OR), so its slot is the chunk's
 //               cursor plus the number of same-chunk bits below its own.
-// Entry format: (position << 6) | slot.
+// Entry format: (position << 6) | slot. Optionally rank[bg][position][slot]
+// records the entry's index in the list (position-major, for readers that go
+// from a selection to its entry).
 #include "hils_common.h"
 #include "hils_internal.h"
 
@@ -73,7 +75,8 @@ __global__ __launch_bounds__(256) void k_ix_chunk_scan(int* __restrict__ off, in
 // thread, SB <= 32 bits of the masks).
 __global__ __launch_bounds__(256) void k_ix_fill(const int32_t* __restrict__ topk_idx,
                                                  const int* __restrict__ cnt, const int* __restrict__ off,
-                                                 int* __restrict__ lst, int N, int K, int C, int ns) {
+                                                 int* __restrict__ lst, int* __restrict__ rank, int N,
+                                                 int K, int C, int ns) {
   extern __shared__ int smem[];
   int* cur = smem;                                           // [C] next slot of each chunk
   unsigned* msk = reinterpret_cast<unsigned*>(smem + C);     // [C] chunk's positions in the step
@@ -101,8 +104,9 @@ __global__ __launch_bounds__(256) void k_ix_fill(const int32_t* __restrict__ top
     unsigned m = 0u;
     if (c >= 0) {
       m = msk[c];
-      const int rank = __popc(m & ((1u << pl) - 1u));
-      dst[cur[c] + rank] = (int)((pos << 6) | kk);
+      const int e = cur[c] + __popc(m & ((1u << pl) - 1u));
+      dst[e] = (int)((pos << 6) | kk);
+      if (rank != nullptr) rank[((size_t)bg * N + pos) * K + kk] = e;
     }
     __syncthreads();
     // the step's last position holding c advances the cursor and clears the mask
@@ -130,7 +134,7 @@ bool inv_index_ok(const Dims& p) {
   return p.C <= INV_MAX_CHUNKS && (long)p.N * 64 < (1L << 31) && p.K <= 32;
 }
 
-size_t inv_index_carve(const Dims& p, void* base, InvIndex* out) {
+size_t inv_index_carve(const Dims& p, void* base, InvIndex* out, bool with_rank) {
   char* c = static_cast<char*>(base);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -143,6 +147,7 @@ size_t inv_index_carve(const Dims& p, void* base, InvIndex* out) {
   out->cnt = (int*)take(bg * out->ns * (size_t)p.C * sizeof(int));
   out->off = (int*)take(bg * ((size_t)p.C + 1) * sizeof(int));
   out->lst = (int*)take(bg * (size_t)p.N * p.K * sizeof(int));
+  out->rank = with_rank ? (int*)take(bg * (size_t)p.N * p.K * sizeof(int)) : nullptr;
   return o;
 }
 
@@ -165,7 +170,7 @@ hipError_t launch_inv_index(const Dims& p, const int32_t* topk_idx, const InvInd
                      p.C, ix.ns);
   hipLaunchKernelGGL(k_ix_chunk_scan, dim3(bg), dim3(256), 0, st, ix.off, p.C);
   hipLaunchKernelGGL(k_ix_fill, dim3(ix.ns, bg), dim3(256), 2 * hl, st, topk_idx, ix.cnt, ix.off,
-                     ix.lst, p.N, p.K, p.C, ix.ns);
+                     ix.lst, ix.rank, p.N, p.K, p.C, ix.ns);
   return hipGetLastError();
 }
 

@@ -316,10 +316,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
 
   const int kv_lo = n_distant(p0, W, S) * S;
   const int nW = (plast - kv_lo) / 64 + 1;
-  // blocks in flight in registers: two sets (blocks n + 2, n + 3) at d = 64,
-  // one (n + 2) at d = 128, where two sets push the wave past the register
-  // budget of two waves per SIMD
-  constexpr int NSET = DH == 64 ? 2 : 1;
+  // blocks in flight in registers: two sets (blocks n + 2, n + 3)
+  constexpr int NSET = 2;
   u32x4 stg[2][SG::VPT];
   auto issue = [&](u32x4 (&rg)[SG::VPT], int n) __attribute__((always_inline)) {
     const int kv0 = kv_lo + 64 * min(n, nW - 1);
@@ -485,10 +483,11 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
   }
 
   // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (dims in
-  // fragment order: this lane's 4 MB values are contiguous). Four slots at a
+  // fragment order: this lane's 4 MB values are contiguous). SG slots at a
   // time: their weights, then all their loads, then the sums, so that the
   // loads are in flight together.
   constexpr int VPS = 4 * MB * (int)sizeof(T) / 16;  // 16-byte vectors per lane and slot
+  constexpr int SLG = (sizeof(T) == 2 && DH == 128) ? 8 : 4;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int r = 32 * w + 16 * cb + cl;
@@ -500,27 +499,27 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
     const int* rks = rank + ((size_t)bg * N + pc) * K;
     const float* scs = topk_score + ro * K;
     const T* pb = part + (size_t)bg * N * K * G * DH + (size_t)hh * DH + gl * 4 * MB;
-    for (int k0 = 0; k0 < K; k0 += 4) {
-      float wk[4];
-      int ek[4];
+    for (int k0 = 0; k0 < K; k0 += SLG) {
+      float wk[SLG];
+      int ek[SLG];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < SLG; ++j) {
         const int kk = min(k0 + j, K - 1);
         const int cc = ids[kk];
         const bool sel = live && k0 + j < K && cc >= 0;
         wk[j] = sel ? __expf(scs[kk] - Lr[cb]) : 0.f;
         ek[j] = sel ? rks[kk] : 0;
       }
-      u32x4 pv[4][VPS];
+      u32x4 pv[SLG][VPS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < SLG; ++j) {
         const u32x4* src = reinterpret_cast<const u32x4*>(pb + (size_t)ek[j] * G * DH);
 #pragma unroll
         for (int x = 0; x < VPS; ++x)
           pv[j][x] = wk[j] != 0.f ? src[x] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < SLG; ++j) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int x = 0; x < VPS; ++x) {

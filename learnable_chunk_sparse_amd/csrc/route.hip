@@ -33,12 +33,14 @@ constexpr int RT_PAD = 8;   // kL tile row padding (elements)
 // One lane per position keeps that position's running top-KC (KC >= K) in
 // registers as keys, sorted descending: the order-preserving bits of the
 // score above the complement of the chunk id, so that one comparison orders
-// by (score desc, chunk asc) and 0 lies below every real candidate. Each 16-chunk step's candidates are sorted by a bitonic network
-// and merged in one pass (a half-cleaner against the current list, then a
-// bitonic merge): ~112 compare-exchanges per step whatever the lanes do,
-// where inserting the candidates one by one costs 16 per candidate and runs
-// for every candidate some lane of the wave keeps. A step is skipped when no
-// lane has a candidate above its K-th key.
+// by (score desc, chunk asc) and 0 lies below every real candidate. A
+// candidate that does not beat the running K-th key can never enter the final
+// top-K, so each step only appends the candidates that do to a per-lane buffer
+// in LDS (one compare and one LDS write per candidate); once the K-th key has
+// settled few candidates pass. When a buffer could overflow, every lane's
+// buffer is sorted 16 at a time by a bitonic network and merged into its list
+// in one pass (a half-cleaner against the current list, then a bitonic merge),
+// and the K-th key is refreshed.
 // The key is that integer held exactly in a double: the order-preserving 32
 // bits of the score times 2^20 plus (2^20 - 1 - chunk), below 2^52 for the
 // at most 2^20 chunks a call may have, so that a compare-exchange is one fp64
@@ -46,6 +48,7 @@ constexpr int RT_PAD = 8;   // kL tile row padding (elements)
 // two hazard waits).
 typedef double Key;
 constexpr double KEY_CH = 1048576.0;  // 2^20: chunk ids below it
+constexpr int SELBUF = 32;            // buffered candidates per position (a multiple of 16)
 __device__ __forceinline__ Key sel_key(float sc, int c) {
   const uint32_t u = __float_as_uint(sc);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -100,8 +103,15 @@ __device__ __forceinline__ void merge_top(Key (&t)[KC], const Key (&n)[16]) {
 // (hi + lo halves), and the B operand the landmark key followed by the
 // precomputed W_up^T kL (hi + lo planes, k_route_klp): three more products
 // per k step of r, and no fp32 q_hat written or read.
-template <typename T, typename QT, int G, int DH, int KC, int UR>
-__global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
+// Selection mode: SM 0 merges each step's candidates into the lists (one lane
+// per position, after the score tile is turned around through LDS); SM 1 does
+// the same turnaround but buffers the candidates that beat the K-th key (one
+// head per KV head with many chunks); SM 2 (grouped heads, where a wave holds
+// fewer positions than lanes) filters the candidates in the MFMA output
+// layout itself, every lane holding 4 RB candidates of a step, and appends
+// the passing ones to their position's buffer at ranks taken from ballots.
+template <typename T, typename QT, int G, int DH, int KC, int UR, bool BUFSEL>
+__global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                const T* __restrict__ e, int32_t* __restrict__ topk_idx,
                                                float* __restrict__ topk_score,
                                                float* __restrict__ sel_lse, int N, int C, int Hkv,
@@ -124,7 +134,15 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
   __shared__ float e_s[RT_TC];
   constexpr int URN = UR > 0 ? UR : 1, RR = 32 * URN, RP = RR + 8;
   __shared__ __align__(16) uint16_t klh_s[UR ? RT_TC * RP : 8], kll_s[UR ? RT_TC * RP : 8];
-  __shared__ __align__(16) float sc_s[4][PW][16 + 4];  // per-wave score tile (positions x chunks)
+  constexpr int SM = G >= 2 ? 2 : (BUFSEL ? 1 : 0);
+  // per-wave score tile (positions x chunks) for the turnaround (SM 0, 1)
+  __shared__ __align__(16) float sc_s[SM == 2 ? 1 : 4][SM == 2 ? 1 : PW][16 + 4];
+  // per-position buffers of candidates that beat the running K-th key
+  // (slot-major: position p's slot j at [j][p]); SM 2 also passes counts and
+  // K-th keys between the output layout and the owner lanes
+  __shared__ Key cb_s[SM ? 4 : 1][SM ? SELBUF : 1][SM ? PW : 1];
+  __shared__ Key thr_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
+  __shared__ int cnt_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   const int grp = lane >> 4, col = lane & 15;
@@ -188,6 +206,70 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
   Key tk[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) tk[k] = 0.0;
+  // buffered candidates of the owner lane and the running K-th key they must
+  // beat (SM 1); the same per D-layout candidate row (SM 2: position
+  // 16 rb + 4 grp + i of this lane's rows)
+  int nbuf = 0;
+  Key thr = 0.0;
+  constexpr int RBD = SM == 2 ? RB : 1;
+  Key thr_d[RBD][4];
+  int cnt_d[RBD][4], nd_d[RBD][4];
+#pragma unroll
+  for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pp = pw0 + 16 * rb + 4 * grp + i;
+      thr_d[rb][i] = 0.0;
+      cnt_d[rb][i] = 0;
+      nd_d[rb][i] = pp < N ? n_distant(pp, W, S) : 0;
+    }
+  // merge every owner lane's buffered candidates into its top-K, 16 at a time
+  // (bitonic sort of the 16, then a bitonic merge into the list); the lanes
+  // of the wave take part together
+  auto flush = [&]() __attribute__((always_inline)) {
+    if constexpr (SM == 2) {
+      if (col == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cnt_s[w][16 * rb + 4 * grp + i] = cnt_d[rb][i];
+      }
+      wave_lds_sync();
+      nbuf = lane < PW ? cnt_s[w][lane] : 0;
+    } else {
+      wave_lds_sync();
+    }
+#pragma unroll
+    for (int g16 = 0; g16 < SELBUF; g16 += 16) {
+      if (__ballot(lane < PW && nbuf > g16) == 0) break;
+      Key nk[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const Key x = cb_s[w][g16 + j][lane < PW ? lane : 0];
+        nk[j] = g16 + j < nbuf ? x : 0.0;
+      }
+      bitonic_sort_desc<16>(nk);
+      merge_top<KC>(tk, nk);
+    }
+    thr = tk[KC - 1];
+    if (K < KC) {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) thr = k == K - 1 ? tk[k] : thr;
+    }
+    nbuf = 0;
+    if constexpr (SM == 2) {
+      if (lane < PW) thr_s[w][lane] = thr;
+      wave_lds_sync();
+#pragma unroll
+      for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          thr_d[rb][i] = thr_s[w][16 * rb + 4 * grp + i];
+          cnt_d[rb][i] = 0;
+        }
+      wave_lds_sync();
+    }
+  };
   const int nd_w = (pw0 < N) ? n_distant(min(pw0 + PW - 1, N - 1), W, S) : 0;
   const int nd_wg = n_distant(min(tile * PWG + PWG - 1, N - 1), W, S);
   const T* kLg = kL + (size_t)bg * C * DH;
@@ -297,10 +379,64 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
             for (int i = 0; i < 4; ++i) best[i] = fmaxf(best[i], acc[i]);
         }
         // D layout: position 16 rb + 4 grp + i, chunk c0 + col
+        if constexpr (SM == 2) {
+          // filter in place: candidates beating their position's K-th key go
+          // to the position's buffer, ranked among the group's 16 lanes
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc_s[w][16 * rb + 4 * grp + i][col] = fmaf(best[i], scale, ev);
+          for (int i = 0; i < 4; ++i) {
+            const int c = c0 + col;
+            const Key key = sel_key(fmaf(best[i], scale, ev), c) * (double)(c < nd_d[rb][i]);
+            const bool pass = key > thr_d[rb][i];
+            const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * grp)) & 0xFFFFu;
+            if (pass) cb_s[w][cnt_d[rb][i] + __popc(gm & ((1u << col) - 1u))][16 * rb + 4 * grp + i] = key;
+            cnt_d[rb][i] += __popc(gm);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc_s[w][16 * rb + 4 * grp + i][col] = fmaf(best[i], scale, ev);
+        }
+      }
+      if constexpr (SM == 2) {
+        bool full = false;
+#pragma unroll
+        for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) full |= cnt_d[rb][i] > SELBUF - 16;
+        if (__ballot(full) != 0) flush();
+        continue;
       }
       wave_lds_sync();
+      if constexpr (SM == 0) {
+        if (lane < PW) {
+          float v[16];
+#pragma unroll
+          for (int j = 0; j < 16; j += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
+            v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
+          }
+          Key nk[16];
+          bool any = false;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            // masked arithmetically (a select here became a branch per
+            // candidate): absent candidates get key 0, below every real one
+            nk[j] = sel_key(v[j], c0 + j) * (double)(c0 + j < mynd);
+            any |= nk[j] > thr;
+          }
+          if (__ballot(any) != 0) {
+            bitonic_sort_desc<16>(nk);
+            merge_top<KC>(tk, nk);
+            thr = tk[KC - 1];
+            if (K < KC) {
+#pragma unroll
+              for (int k = 0; k < KC; ++k) thr = k == K - 1 ? tk[k] : thr;
+            }
+          }
+        }
+        wave_lds_sync();
+        continue;
+      }
+      bool full = false;
       if (lane < PW) {
         float v[16];
 #pragma unroll
@@ -308,27 +444,35 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
           const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
           v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
         }
-        Key thr = tk[KC - 1];
-        if (K < KC) {
-#pragma unroll
-          for (int k = 0; k < KC; ++k) thr = k == K - 1 ? tk[k] : thr;
-        }
-        Key nk[16];
-        bool any = false;
+        // a candidate is kept only if it beats the lane's running K-th key
+        // (no later candidate can push that key down): it is written to the
+        // next free slot of the lane's buffer, a slot the next candidate
+        // overwrites when this one is not kept (no branch per candidate)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          // masked arithmetically (a select here became a branch per
-          // candidate): absent candidates get key 0, below every real one
-          nk[j] = sel_key(v[j], c0 + j) * (double)(c0 + j < mynd);
-          any |= nk[j] > thr;
+          // absent candidates (c >= n_dist) get key 0, below every real one
+          const Key key = sel_key(v[j], c0 + j) * (double)(c0 + j < mynd);
+          cb_s[w][nbuf][lane] = key;
+          nbuf += key > thr ? 1 : 0;
         }
-        if (__ballot(any) != 0) {
-          bitonic_sort_desc<16>(nk);
-          merge_top<KC>(tk, nk);
-        }
+        full = nbuf > SELBUF - 16;
       }
+      // merge the buffers into the running top-K when one could overflow at
+      // the next step
+      if (__ballot(full) != 0) flush();
       wave_lds_sync();
     }
+  }
+
+  if constexpr (SM == 1) {
+    if (__ballot(lane < PW && nbuf > 0) != 0) flush();
+  } else if constexpr (SM == 2) {
+    bool any = false;
+#pragma unroll
+    for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) any |= cnt_d[rb][i] > 0;
+    if (__ballot(any) != 0) flush();
   }
 
   // output: indices ascending, -1 padded; per-head fp32 scores of the selected chunks
@@ -357,7 +501,7 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       if (k < K) dst[k] = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
-    if (topk_score != nullptr) {
+    if (G == 1 && topk_score != nullptr) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float* ds = topk_score + (((size_t)b * Hq + g * G + hh) * N + mypos) * K;
@@ -376,25 +520,8 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
               ds[k] = ok ? sv[k] : __builtin_nanf("");
               if (ok) lse_add(sv[k]);
             }
-        } else {
-          const QT* qh = qs + (((size_t)b * Hq + g * G + hh) * N + mypos) * DH;
-          for (int k = 0; k < K; ++k) {
-            const int ck = ids[k < KC ? k : 0];
-            if (ck == 0x7FFFFFFF) {
-              ds[k] = __builtin_nanf("");
-              continue;
-            }
-            const T* kr = kLg + (size_t)ck * DH;
-            float a = 0.f;
-            for (int dd = 0; dd < DH; dd += 8) {
-              const auto kv = ld8<T>(kr + dd);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) a = fmaf(to_f<QT>(qh[dd + j]), (float)kv[j], a);
-            }
-            ds[k] = fmaf(a, scale, to_f<T>(eg[ck]));
-            lse_add(ds[k]);
-          }
         }
+        // grouped heads: k_route_scores computes each head's scores
         if (sel_lse != nullptr)
           sel_lse[((size_t)b * Hq + g * G + hh) * N + mypos] = lm == NEG_INF ? NEG_INF : lm + __logf(ls);
       }
@@ -402,15 +529,103 @@ __global__ __launch_bounds__(256, UR > 0 ? 2 : 1) void k_route(const QT* __restr
   }
 }
 
+// Each head's fp32 score of every selected chunk, s = scale q_hat . kL_c + e_c
+// (NaN in empty slots), and the log-sum-exp of a head's selected scores, for
+// grouped heads (the selection itself ran on the group maximum). Four lanes
+// per (b, head, position) row, each holding a quarter of q_hat and reading
+// the matching quarter of every selected landmark row (coalesced 16-byte
+// vectors), sums combined by two lane exchanges.
+template <typename T, typename QT, int DH>
+__global__ __launch_bounds__(256) void k_route_scores(const QT* __restrict__ qs, const T* __restrict__ kL,
+                                                      const T* __restrict__ e,
+                                                      const int32_t* __restrict__ topk_idx,
+                                                      float* __restrict__ topk_score,
+                                                      float* __restrict__ sel_lse, long rows, int N,
+                                                      int C, int Hq, int G, int K, float scale) {
+  constexpr int QD = DH / 4;  // dims per lane
+  const long row = (long)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int part = threadIdx.x & 3;
+  const long rc = row < rows ? row : rows - 1;
+  const long bh = rc / N;
+  const int pos = (int)(rc - bh * N);
+  const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+  const int Hkv = Hq / G, g = h / G;
+  float qv[QD];
+  const QT* qr = qs + rc * DH + part * QD;
+#pragma unroll
+  for (int j = 0; j < QD; j += 4) {
+    if constexpr (sizeof(QT) == 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qr + j);
+      qv[j] = x[0]; qv[j + 1] = x[1]; qv[j + 2] = x[2]; qv[j + 3] = x[3];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qv[j + t] = to_f<QT>(qr[j + t]);
+    }
+  }
+  const size_t bg = (size_t)b * Hkv + g;
+  const int32_t* ids = topk_idx + (bg * N + pos) * K;
+  const T* kb = kL + bg * C * DH + part * QD;
+  const T* eb = e + bg * C;
+  float lm = NEG_INF, ls = 0.f;
+  // four slots at a time: their ids, biases and landmark quarters are all
+  // requested before the products
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    int cs[4];
+    float ev[4];
+    typename Frag<T>::type kv[4][QD / 8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cs[j] = k0 + j < K ? ids[k0 + j] : -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cc = cs[j] >= 0 ? cs[j] : 0;
+      ev[j] = to_f<T>(eb[cc]);
+      const T* kr = kb + (size_t)cc * DH;
+#pragma unroll
+      for (int x = 0; x < QD / 8; ++x) kv[j][x] = ld8<T>(kr + 8 * x);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int x = 0; x < QD / 8; ++x)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a = fmaf(qv[8 * x + t], (float)kv[j][x][t], a);
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      const int c = cs[j];
+      const float sc = c >= 0 ? fmaf(a, scale, ev[j]) : __builtin_nanf("");
+      if (c >= 0) {
+        const float mn = fmaxf(lm, sc);
+        ls = ls * __expf(lm - mn) + __expf(sc - mn);
+        lm = mn;
+      }
+      if (part == 0 && row < rows && topk_score != nullptr && k0 + j < K) topk_score[row * K + k0 + j] = sc;
+    }
+  }
+  if (part == 0 && row < rows && sel_lse != nullptr)
+    sel_lse[row] = lm == NEG_INF ? NEG_INF : lm + __logf(ls);
+}
+
 template <typename T, typename QT, int G, int DH, int KC, int UR>
 static hipError_t route_go(const Dims& p, const void* qs, const void* kL, const void* e,
                            int32_t* idx, float* sc, float* sl, const RouteU& ru, hipStream_t st) {
   constexpr int PWG = 4 * 16 * (G >= 4 ? 1 : 4 / G);
   const int ntiles = (p.N + PWG - 1) / PWG;
-  auto kern = k_route<T, QT, G, DH, KC, UR>;
+  // one head per KV head: buffer the candidates only when the scan is long
+  // (with a few hundred chunks most candidates fill the lists anyway)
+  auto kern = (G == 1 && p.C < 512) ? k_route<T, QT, G, DH, KC, UR, false>
+                                    : k_route<T, QT, G, DH, KC, UR, true>;
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), 0, st, (const QT*)qs,
                      (const T*)kL, (const T*)e, idx, sc, sl, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
                      ntiles, ru.u, ru.klh, ru.kll);
+  if constexpr (G > 1) {
+    if (sc != nullptr || sl != nullptr) {
+      const long rows = (long)p.B * p.Hq * p.N;
+      hipLaunchKernelGGL((k_route_scores<T, QT, DH>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0,
+                         st, (const QT*)qs, (const T*)kL, (const T*)e, idx, sc, sl, rows, p.N, p.C,
+                         p.Hq, G, p.K, p.scale);
+    }
+  }
   return hipGetLastError();
 }
 
@@ -420,7 +635,8 @@ static hipError_t route_k(const Dims& p, const void* qs, const void* kL, const v
   if (p.K <= 4) return route_go<T, QT, G, DH, 4, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
   if (p.K <= 8) return route_go<T, QT, G, DH, 8, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
   if (p.K <= 16) return route_go<T, QT, G, DH, 16, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
-  return route_go<T, QT, G, DH, 32, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
+  if constexpr (UR > 0) return hipErrorInvalidValue;  // the u path serves K <= 16
+  else return route_go<T, QT, G, DH, 32, UR>(p, qs, kL, e, idx, sc, sl, ru, st);
 }
 
 template <typename T, typename QT, int G>
@@ -463,7 +679,9 @@ hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void
 }
 
 bool route_u_ok(const Dims& p) {
-  return p.dtype == 1 && p.G == 1 && (p.r == 32 || p.r == 64);
+  // K <= 16: with 32 selection keys per lane on top of the u operands the
+  // kernel would spill (the q_hat path then serves K up to 32)
+  return p.dtype == 1 && p.G == 1 && (p.r == 32 || p.r == 64) && p.K <= 16;
 }
 
 // W_up[h]^T kL_c for every (b, query head, chunk): the Q-Cal part of the

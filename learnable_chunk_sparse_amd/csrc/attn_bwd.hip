@@ -231,15 +231,22 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
   constexpr int RS = DH + 4;  // accumulator row stride
   constexpr int EPT = TP * 32 / 256;
   extern __shared__ __align__(16) unsigned char smem[];
+  const int E = TP * K;                             // the tile's (position, slot) entries
+  int NE = 1;                                       // E rounded up to a power of two
+  while (NE < E) NE <<= 1;
   float* accT = reinterpret_cast<float*>(smem);     // [4][R][RS] per-wave copies
   float* Ls = accT + 4 * R * RS;                    // [R]
   float* Ds = Ls + R;                               // [R] chunk part of D, then D
-  float* dsS = Ds + R;                              // [R][K]
-  int* off = reinterpret_cast<int*>(dsS + R * K);   // [C + 1]
-  int* nzl = off + C + 1;                           // [C]
-  uint16_t* ent = reinterpret_cast<uint16_t*>(nzl + C);
+  float* dsS = Ds + R;                              // [R][K] fusion weights
+  float* dlS = dsS + R * K;                         // [R][K] delta_c of each slot
+  // the tile's selections sorted by (chunk, entry), then grouped into runs
+  uint32_t* skey = reinterpret_cast<uint32_t*>(dlS + R * K);  // [NE] sorted keys
+  int* rfl = reinterpret_cast<int*>(skey + NE);               // [NE] run heads -> run index
+  int* rch = rfl + NE;                                        // [NE] chunk of each run
+  int* rst = rch + NE;                                        // [NE + 1] first entry of each run
+  uint16_t* ent = reinterpret_cast<uint16_t*>(rst + NE + 1);  // [NE] entries in key order
   __shared__ int wsum[4];
-  __shared__ int ctr;
+  __shared__ int etot;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int tx, bg;
@@ -262,13 +269,15 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
     Ls[x] = lse[ro];
     Ds[x] = 0.f;
   }
-  for (int x = tid; x < R * K; x += 256) dsS[x] = 0.f;
-  // bucket the tile's selections by chunk
-  for (int x = tid; x <= ndmax; x += 256) off[x] = 0;
-  if (tid == 0) ctr = 0;
-  __syncthreads();
-  int my_c[EPT], my_r[EPT];
-  const int E = TP * K;
+  for (int x = tid; x < R * K; x += 256) {
+    dsS[x] = 0.f;
+    dlS[x] = 0.f;
+  }
+  // group the tile's selections by chunk: keys (chunk << 12 | entry), absent
+  // ones last, sorted by a bitonic network in LDS (no per-chunk table, so no
+  // bound on the number of chunks; the order is a function of the data)
+  if (tid == 0) etot = 0;
+  int my_c[EPT];
   // all of the thread's ids are requested before any is used (clamped
   // addresses; guarded per-element loads would each wait for the previous)
 #pragma unroll
@@ -281,48 +290,58 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
   for (int j = 0; j < EPT; ++j) {
     const int x = tid + 256 * j;
     const int c = my_c[j];
-    my_r[j] = 0;
     const bool ok = x < E && p0 + x / K < N && c >= 0 && c < ndmax;
-    my_c[j] = ok ? c : -1;
-    if (ok) my_r[j] = atomicAdd(&off[c], 1);
+    if (x < NE) skey[x] = ok ? ((uint32_t)c << 12) | (uint32_t)x : 0xFFFFFFFFu;
   }
+  for (int x = EPT * 256 + tid; x < NE; x += 256) skey[x] = 0xFFFFFFFFu;
   __syncthreads();
-  for (int x = tid; x < ndmax; x += 256) nzl[x] = off[x] > 0 ? 1 : 0;
-  __syncthreads();
-  const int Etot = bwd_block_scan(off, ndmax, wsum);
-  const int NZ = bwd_block_scan(nzl, ndmax, wsum);
-  if (tid == 0) off[ndmax] = Etot;
-  __syncthreads();
-  for (int base = 0; base < ndmax; base += 256) {
-    const int x = base + tid;
-    const int rk = (x < ndmax && off[x + 1] > off[x]) ? nzl[x] : -1;
-    __syncthreads();
-    if (rk >= 0) nzl[rk] = x;
-    __syncthreads();
+  for (int kb = 2; kb <= NE; kb <<= 1)
+    for (int jb = kb >> 1; jb > 0; jb >>= 1) {
+      for (int i = tid; i < NE; i += 256) {
+        const int l = i ^ jb;
+        if (l > i) {
+          const uint32_t a = skey[i], bb = skey[l];
+          if ((a > bb) == ((i & kb) == 0)) {
+            skey[i] = bb;
+            skey[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  // runs of one chunk: heads flagged, exclusive scan gives each head its run
+  int nvalid = 0;
+  for (int i = tid; i < NE; i += 256) {
+    const uint32_t key = skey[i];
+    const bool ok = key != 0xFFFFFFFFu;
+    const int x = (int)(key & 0xFFFu), pl = x / K, kk = x - pl * K;
+    ent[i] = (uint16_t)((pl << 6) | kk);
+    rfl[i] = ok && (i == 0 || (skey[i - 1] >> 12) != (key >> 12)) ? 1 : 0;
+    nvalid += ok ? 1 : 0;
   }
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int c = my_c[j];
-    if (c >= 0) {
-      const int x = tid + 256 * j;
-      const int pl = x / K, kk = x - pl * K;
-      ent[off[c] + my_r[j]] = (uint16_t)((pl << 6) | kk);
+  atomicAdd(&etot, nvalid);  // integer sum: order-free
+  __syncthreads();
+  const int NZ = bwd_block_scan(rfl, NE, wsum);
+  // run r: chunk rch[r], entries rst[r] .. rst[r + 1] - 1 of ent
+  for (int i = tid; i < NE; i += 256) {
+    const uint32_t key = skey[i];
+    if (key != 0xFFFFFFFFu && (i == 0 || (skey[i - 1] >> 12) != (key >> 12))) {
+      rch[rfl[i]] = (int)(key >> 12);
+      rst[rfl[i]] = i;
     }
   }
+  if (tid == 0) rst[NZ] = etot;
   __syncthreads();
 
   const float sc2 = scale * LOG2E;
   // ---------------- selected chunks (terms free of D)
   {
-    auto grab = [&]() __attribute__((always_inline)) {
-      int it = 0;
-      if (lane == 0) it = atomicAdd(&ctr, 1);
-      return __shfl(it, 0, 64);
-    };
+    // runs taken round-robin (a fixed assignment: each row's chunk terms are
+    // summed in the same order on every run)
     BwdChunkFrags<T, DH> f;
-    for (int a = grab(); a < NZ; a = grab()) {
-      const int c = nzl[a];
-      const int e0 = off[c], n = off[c + 1] - e0;
+    for (int a = w; a < NZ; a += 4) {
+      const int c = rch[a];
+      const int e0 = rst[a], n = rst[a + 1] - e0;
       bwd_load_block<T, DH>(f, kg + (size_t)c * 64 * DH, vg + (size_t)c * 64 * DH, 64, ktg + (size_t)c * 64, Np, lane);
       const int nb = (n * G + 15) / 16;
       for (int cbk = 0; cbk < nb; ++cbk) {
@@ -406,13 +425,20 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
           }
           if ((lane >> 4) == 0) {
             dsS[row * K + kk] = wc;  // fusion weight, turned into ds once D is known
-            atomicAdd(&Ds[row], wc * dl);
+            dlS[row * K + kk] = dl;
             beta_o[ro * K + kk] = sc - Lrow - (mx * scale + __logf(ls));
             delta_o[ro * K + kk] = dl;
           }
         }
       }
     }
+  }
+  __syncthreads();
+  // chunk part of D = sum over the row's slots of w_c delta_c, in slot order
+  for (int r = tid; r < R; r += 256) {
+    float a = 0.f;
+    for (int kk = 0; kk < K; ++kk) a += dsS[r * K + kk] * dlS[r * K + kk];
+    Ds[r] = a;
   }
   __syncthreads();
 
@@ -1045,9 +1071,11 @@ size_t carve(const Dims& p, void* base, BwdWs* w) {
 template <typename T, int G, int DH, int CB>
 size_t dq_lds(const Dims& p) {
   constexpr int R = 64 * CB, TP = R / G;
-  size_t s = sizeof(float) * (4 * (size_t)R * (DH + 4) + 2 * R + (size_t)R * p.K);
-  s += sizeof(int) * (2 * (size_t)p.C + 1);
-  s += sizeof(uint16_t) * (size_t)TP * p.K;
+  size_t NE = 1;
+  while (NE < (size_t)TP * p.K) NE <<= 1;
+  if (NE > 4096) return (size_t)-1;  // entry ids take 12 bits of the sort keys
+  size_t s = sizeof(float) * (4 * (size_t)R * (DH + 4) + 2 * R + 2 * (size_t)R * p.K);
+  s += sizeof(int) * (4 * NE + 1) + sizeof(uint16_t) * NE;
   return ((s + 15) & ~(size_t)15) + 64;
 }
 

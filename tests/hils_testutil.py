@@ -53,15 +53,17 @@ def check_topk_row(gpu_set, sel_sorted, order, K, nd):
 
 
 def grad_tol(dtype, ref):
-    """The bar for a gradient. bf16: the method's absolute bar. fp32: 1e-5
-    taken relative to the gradient's scale (max |ref|, at least 1). Gradients
-    such as dv sum hundreds of row contributions and reach magnitudes of ~6
-    here, where 1e-5 absolute is ~20 fp32 ulps: the accumulation's own
-    rounding, whose order also varies from run to run (the rows of a key
-    block come from an inverse index filled with atomic cursors), reaches it."""
+    """The bar for a gradient. bf16: the method's absolute bar (max-abs 2e-2,
+    mean-abs 2e-3). fp32: 1e-5, absolute where |ref| <= 1 and relative to
+    |ref| above (checked element by element). The backward sums its fp32
+    terms in one fixed order (the inverse index is a stable sort and the
+    chunk terms of a row are added in a fixed sequence), and the rounding of
+    an fp32 sum grows with its magnitude: n terms of a sum S carry up to about
+    n u |S| (u = 2^-24); 1e-5 relative is ~170 ulps, the bound for a few
+    hundred terms such as dv's key rows."""
     t = dict(TOL[dtype])
     if dtype == "fp32":
-        t["max_abs"] *= max(1.0, float(np.abs(np.asarray(ref)).max()) if np.size(ref) else 1.0)
+        t["rel_floor"] = 1.0
     return t
 
 
@@ -72,6 +74,9 @@ def compare(name, got, ref, dtype, tol=None):
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     err = np.abs(got - ref)
     t = tol or TOL[dtype]
+    if "rel_floor" in t:
+        # element by element: absolute up to |ref| = rel_floor, relative above
+        err = err / np.maximum(t["rel_floor"], np.abs(ref))
     mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
     say(f"  {name}: max_abs={mx:.3e} mean_abs={mean:.3e} (tol {t['max_abs']:.0e}/{t['mean_abs']:.0e})")
     assert mx <= t["max_abs"], f"{name}: max abs err {mx} > {t['max_abs']}"

@@ -25,7 +25,8 @@
  *   Errors: HILS_ERR_INVALID (null required pointer, size <= 0, Hq % Hkv != 0,
  *   Nq/Nk inconsistent with the op), HILS_ERR_UNSUPPORTED (a valid problem
  *   outside what the kernels implement, e.g. d not in {64,128}, S != 64,
- *   K > 64, Hq/Hkv not in {1,2,4,8}), HILS_ERR_WORKSPACE (ws too small or
+ *   K > 64, Hq/Hkv not in {1,2,4,8}; hils_attn_fwd and hils_attn_bwd accept
+ *   exactly the same problems), HILS_ERR_WORKSPACE (ws too small or
  *   misaligned), HILS_ERR_HIP (a kernel launch failed). A fault inside a
  *   kernel surfaces at the caller's next synchronisation. Nothing prints,
  *   aborts or throws across this boundary.

@@ -226,8 +226,11 @@ hils_status ws_check(void* ws, size_t have, size_t need) {
 
 hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_ERR_HIP; }
 
-// the forward's strategy fits the hardware (LDS, index limits)
+// The prefill envelope: the forward's strategy fits the hardware (LDS, index
+// limits) and the backward can train the same problem, so that
+// hils_attn_fwd and hils_attn_bwd accept exactly the same problems.
 bool fwd_fits_lds(const Dims& d) {
+  if (hils::bwd_workspace(d) == (size_t)-1) return false;
   if (hils::fwd_strategy_of(d) == HILS_FWD_CHUNK_MAJOR) return hils::fwd_cm_ok(d);
   return hils::attn_fwd_lds_bytes(d) <= 160 * 1024;
 }

@@ -285,3 +285,28 @@ def test_decode_noalloc_rejects_oversize_and_invalid_before_touching_the_device(
     assert lib.hils_decode_noalloc(*args(big)) == 3
     assert lib.hils_decode_noalloc(*args(prob(B=0, Nq=1, Nk=4096))) == 1
     assert lib.hils_decode_noalloc(*args(prob(d=96, Nq=1, Nk=4096))) == 2
+
+
+def test_forward_and_backward_accept_the_same_problems():
+    """hils_workspace_size answers alike for the forward and the backward on a
+    grid of shapes (head dims, GQA groups, K, dtypes, 8K to 2M tokens), with
+    the default strategy and the chunk-major one: a problem the forward runs
+    can be trained."""
+    seen_ok = seen_bad = 0
+    for d in (64, 128):
+        for G in (1, 2, 4):
+            for K in (8, 16, 32):
+                for dt in (0, 1):
+                    for N in (8192, 131072, 262144, 524288, 1048576, 2097152):
+                        for strat in (L.FWD_AUTO, L.FWD_CHUNK_MAJOR):
+                            p = prob(dtype=dt, B=1, Hq=8 * G, Hkv=8, d=d, Nq=N, Nk=N, K=K, W=512,
+                                     r=0, D=0, fwd_strategy=strat)
+                            f, _ = ws(p, L.OP_FWD)
+                            b, _ = ws(p, L.OP_BWD)
+                            assert (f == 0) == (b == 0), (d, G, K, dt, N, strat, f, b)
+                            seen_ok += f == 0
+                            seen_bad += f != 0
+    assert seen_ok > 0 and seen_bad > 0
+    # the paper's long-context prefill shape (345M: 16 heads, d 64, top-32, 512K tokens)
+    p = prob(B=1, Hq=16, Hkv=16, d=64, Nq=524288, Nk=524288, K=32, W=512, D=1024, r=32)
+    assert ws(p, L.OP_FWD)[0] == 0 and ws(p, L.OP_BWD)[0] == 0

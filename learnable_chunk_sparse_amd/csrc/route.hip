@@ -104,12 +104,12 @@ __device__ __forceinline__ void merge_top(Key (&t)[KC], const Key (&n)[16]) {
 // precomputed W_up^T kL (hi + lo planes, k_route_klp): three more products
 // per k step of r, and no fp32 q_hat written or read.
 // Selection mode: SM 0 merges each step's candidates into the lists (one lane
-// per position, after the score tile is turned around through LDS); SM 1 does
-// the same turnaround but buffers the candidates that beat the K-th key (one
-// head per KV head with many chunks); SM 2 (grouped heads, where a wave holds
-// fewer positions than lanes) filters the candidates in the MFMA output
-// layout itself, every lane holding 4 RB candidates of a step, and appends
-// the passing ones to their position's buffer at ranks taken from ballots.
+// per position, after the score tile is turned around through LDS), for a
+// short scan where most candidates enter the lists anyway; SM 2 (grouped
+// heads, or long scans) filters the candidates in the MFMA output layout
+// itself, every lane holding 4 RB candidates of a step, against a float
+// threshold per position, and appends the few that pass to their position's
+// buffer at ranks taken from ballots.
 template <typename T, typename QT, int G, int DH, int KC, int UR, bool BUFSEL>
 __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void k_route(const QT* __restrict__ qs, const T* __restrict__ kL,
                                                const T* __restrict__ e, int32_t* __restrict__ topk_idx,
@@ -134,14 +134,15 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
   __shared__ float e_s[RT_TC];
   constexpr int URN = UR > 0 ? UR : 1, RR = 32 * URN, RP = RR + 8;
   __shared__ __align__(16) uint16_t klh_s[UR ? RT_TC * RP : 8], kll_s[UR ? RT_TC * RP : 8];
-  constexpr int SM = G >= 2 ? 2 : (BUFSEL ? 1 : 0);
-  // per-wave score tile (positions x chunks) for the turnaround (SM 0, 1)
+  constexpr int SM = (G >= 2 || BUFSEL) ? 2 : 0;
+  // per-wave score tile (positions x chunks) for the turnaround (SM 0)
   __shared__ __align__(16) float sc_s[SM == 2 ? 1 : 4][SM == 2 ? 1 : PW][16 + 4];
   // per-position buffers of candidates that beat the running K-th key
   // (slot-major: position p's slot j at [j][p]); SM 2 also passes counts and
   // K-th keys between the output layout and the owner lanes
-  __shared__ Key cb_s[SM ? 4 : 1][SM ? SELBUF : 1][SM ? PW : 1];
-  __shared__ Key thr_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
+  __shared__ float cbs_s[SM ? 4 : 1][SM ? SELBUF : 1][SM ? PW : 1];  // buffered scores
+  __shared__ int cbc_s[SM ? 4 : 1][SM ? SELBUF : 1][SM ? PW : 1];    // and their chunks
+  __shared__ float thr_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
   __shared__ int cnt_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
@@ -206,46 +207,53 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
   Key tk[KC];
 #pragma unroll
   for (int k = 0; k < KC; ++k) tk[k] = 0.0;
-  // buffered candidates of the owner lane and the running K-th key they must
-  // beat (SM 1); the same per D-layout candidate row (SM 2: position
-  // 16 rb + 4 grp + i of this lane's rows)
+  // SM 2 state: a conservative score threshold per D-layout candidate row
+  // (position 16 rb + 4 grp + i of this lane's rows): the score of the row's
+  // running K-th key, -inf until K candidates are in (a candidate scoring
+  // below it can never enter the top-K; equal scores go on to the exact key
+  // comparison of the merge); the rows' buffer fills live in LDS (cnt_s)
   int nbuf = 0;
   Key thr = 0.0;
   constexpr int RBD = SM == 2 ? RB : 1;
-  Key thr_d[RBD][4];
-  int cnt_d[RBD][4], nd_d[RBD][4];
+  float thr_d[RBD][4];
+  // the row's buffer fill (the same in the group's 16 lanes): in registers
+  // for one row block per wave, in LDS (cnt_s) when a lane holds 16 rows
+  constexpr bool CREG = RBD == 1;
+  int cnt_d[CREG ? RBD : 1][4];
 #pragma unroll
   for (int rb = 0; rb < RBD; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pp = pw0 + 16 * rb + 4 * grp + i;
-      thr_d[rb][i] = 0.0;
-      cnt_d[rb][i] = 0;
-      nd_d[rb][i] = pp < N ? n_distant(pp, W, S) : 0;
+      thr_d[rb][i] = NEG_INF;
+      if constexpr (CREG) cnt_d[rb][i] = 0;
     }
+  if constexpr (SM == 2 && !CREG) {
+    if (lane < PW) cnt_s[w][lane] = 0;
+    wave_lds_sync();
+  }
+  // the wave's positions span fewer than S: chunks below the first one's
+  // distant count are distant for all of them
+  const int nd_lo = pw0 < N ? n_distant(pw0, W, S) : 0;
   // merge every owner lane's buffered candidates into its top-K, 16 at a time
   // (bitonic sort of the 16, then a bitonic merge into the list); the lanes
   // of the wave take part together
   auto flush = [&]() __attribute__((always_inline)) {
-    if constexpr (SM == 2) {
+    if constexpr (SM == 2 && CREG) {
       if (col == 0) {
 #pragma unroll
-        for (int rb = 0; rb < RBD; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) cnt_s[w][16 * rb + 4 * grp + i] = cnt_d[rb][i];
+        for (int i = 0; i < 4; ++i) cnt_s[w][4 * grp + i] = cnt_d[0][i];
       }
-      wave_lds_sync();
-      nbuf = lane < PW ? cnt_s[w][lane] : 0;
-    } else {
-      wave_lds_sync();
     }
+    wave_lds_sync();
+    if constexpr (SM == 2) nbuf = lane < PW ? cnt_s[w][lane] : 0;
 #pragma unroll
     for (int g16 = 0; g16 < SELBUF; g16 += 16) {
       if (__ballot(lane < PW && nbuf > g16) == 0) break;
       Key nk[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const Key x = cb_s[w][g16 + j][lane < PW ? lane : 0];
+        const int pl = lane < PW ? lane : 0;
+        const Key x = sel_key(cbs_s[w][g16 + j][pl], cbc_s[w][g16 + j][pl]);
         nk[j] = g16 + j < nbuf ? x : 0.0;
       }
       bitonic_sort_desc<16>(nk);
@@ -258,14 +266,17 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
     }
     nbuf = 0;
     if constexpr (SM == 2) {
-      if (lane < PW) thr_s[w][lane] = thr;
+      if (lane < PW) {
+        thr_s[w][lane] = thr == 0.0 ? NEG_INF : key_score(thr);
+        cnt_s[w][lane] = 0;
+      }
       wave_lds_sync();
 #pragma unroll
       for (int rb = 0; rb < RBD; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           thr_d[rb][i] = thr_s[w][16 * rb + 4 * grp + i];
-          cnt_d[rb][i] = 0;
+          if constexpr (CREG) cnt_d[rb][i] = 0;
         }
       wave_lds_sync();
     }
@@ -353,6 +364,7 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
           kq[kr] = *reinterpret_cast<const FT*>(kll_s + o);
         }
       }
+      float sv_d[RBD][4];  // SM 2: this step's scores of the lane's candidate rows
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 best;
@@ -380,28 +392,55 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
         }
         // D layout: position 16 rb + 4 grp + i, chunk c0 + col
         if constexpr (SM == 2) {
-          // filter in place: candidates beating their position's K-th key go
-          // to the position's buffer, ranked among the group's 16 lanes
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = c0 + col;
-            const Key key = sel_key(fmaf(best[i], scale, ev), c) * (double)(c < nd_d[rb][i]);
-            const bool pass = key > thr_d[rb][i];
-            const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * grp)) & 0xFFFFu;
-            if (pass) cb_s[w][cnt_d[rb][i] + __popc(gm & ((1u << col) - 1u))][16 * rb + 4 * grp + i] = key;
-            cnt_d[rb][i] += __popc(gm);
-          }
+          for (int i = 0; i < 4; ++i) sv_d[rb][i] = fmaf(best[i], scale, ev);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sc_s[w][16 * rb + 4 * grp + i][col] = fmaf(best[i], scale, ev);
         }
       }
       if constexpr (SM == 2) {
+        // filter in place: candidates scoring at least their row's threshold
+        // go to the row's buffer, ranked among the group's 16 lanes (one per
+        // chunk of the step); most steps keep none and end at one ballot
+        const int c = c0 + col;
+        const bool edge = c0 + 15 >= nd_lo;  // some chunk may not be distant for some row
+        bool pass[RBD][4];
+        bool anyp = false;
+#pragma unroll
+        for (int rb = 0; rb < RBD; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pass[rb][i] = sv_d[rb][i] >= thr_d[rb][i];
+            if (edge) {
+              const int pp = pw0 + 16 * rb + 4 * grp + i;
+              pass[rb][i] = pass[rb][i] && pp < N && c < n_distant(pp, W, S);
+            }
+            anyp |= pass[rb][i];
+          }
+        if (__ballot(anyp) == 0) continue;
         bool full = false;
 #pragma unroll
         for (int rb = 0; rb < RBD; ++rb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) full |= cnt_d[rb][i] > SELBUF - 16;
+          for (int i = 0; i < 4; ++i) {
+            const uint64_t bm = __ballot(pass[rb][i]);
+            if (bm == 0) continue;
+            const uint32_t gm = (uint32_t)(bm >> (16 * grp)) & 0xFFFFu;
+            const int pr = 16 * rb + 4 * grp + i;
+            int base;
+            if constexpr (CREG) base = cnt_d[rb][i];
+            else base = cnt_s[w][pr];
+            if (pass[rb][i]) {
+              const int slot = base + __popc(gm & ((1u << col) - 1u));
+              cbs_s[w][slot][pr] = sv_d[rb][i];
+              cbc_s[w][slot][pr] = c;
+            }
+            const int nc = base + __popc(gm);
+            if constexpr (CREG) cnt_d[rb][i] = nc;
+            else if (col == 0) cnt_s[w][pr] = nc;
+            full |= nc > SELBUF - 16;
+          }
         if (__ballot(full) != 0) flush();
         continue;
       }
@@ -436,42 +475,18 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
         wave_lds_sync();
         continue;
       }
-      bool full = false;
-      if (lane < PW) {
-        float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; j += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
-          v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
-        }
-        // a candidate is kept only if it beats the lane's running K-th key
-        // (no later candidate can push that key down): it is written to the
-        // next free slot of the lane's buffer, a slot the next candidate
-        // overwrites when this one is not kept (no branch per candidate)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          // absent candidates (c >= n_dist) get key 0, below every real one
-          const Key key = sel_key(v[j], c0 + j) * (double)(c0 + j < mynd);
-          cb_s[w][nbuf][lane] = key;
-          nbuf += key > thr ? 1 : 0;
-        }
-        full = nbuf > SELBUF - 16;
-      }
-      // merge the buffers into the running top-K when one could overflow at
-      // the next step
-      if (__ballot(full) != 0) flush();
-      wave_lds_sync();
     }
   }
 
-  if constexpr (SM == 1) {
-    if (__ballot(lane < PW && nbuf > 0) != 0) flush();
-  } else if constexpr (SM == 2) {
+  if constexpr (SM == 2) {
     bool any = false;
+    if constexpr (CREG) {
 #pragma unroll
-    for (int rb = 0; rb < RBD; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) any |= cnt_d[rb][i] > 0;
+      for (int i = 0; i < 4; ++i) any |= cnt_d[0][i] > 0;
+    } else {
+      wave_lds_sync();
+      any = lane < PW && cnt_s[w][lane] > 0;
+    }
     if (__ballot(any) != 0) flush();
   }
 

@@ -88,15 +88,20 @@ typedef enum { HILS_OP_ROUTE = 0, HILS_OP_FWD = 1, HILS_OP_BWD = 2, HILS_OP_DECO
 typedef enum {
   HILS_STEP_QCAL = 0,         /* Q-Cal (fp32 calibrated queries, or u) */
   HILS_STEP_ROUTE = 1,        /* scoring + GQA max + top-K (prefill) */
-  HILS_STEP_ATTN_FWD = 2,     /* window + selected chunks + fusion (prefill) */
+  HILS_STEP_ATTN_FWD = 2,     /* every attention launch of a prefill forward */
   HILS_STEP_DECODE = 3,       /* the whole decode step after Q-Cal */
   HILS_STEP_BWD = 4,          /* the whole backward */
   HILS_STEP_LANDMARK_FWD = 5, /* landmark summary */
   HILS_STEP_LANDMARK_BWD = 6, /* its backward */
   HILS_STEP_HOPE = 7,         /* HoPE rotation */
-  HILS_STEP_WINDOW = 8,       /* chunk-major forward: window + fusion launch */
-  HILS_STEP_CHUNKS = 9,       /* chunk-major forward: selected-chunk launch */
-  HILS_STEP_COUNT = 10
+  HILS_STEP_WINDOW = 8,       /* prefill forward: the one launch that ends in the
+                                 fusion (chunk-major: window + fusion; the
+                                 query-major strategies: window + selected
+                                 chunks + fusion) */
+  HILS_STEP_CHUNKS = 9,       /* chunk-major forward: the selected-chunk launch */
+  HILS_STEP_PREP = 10,        /* prefill forward: the V^T copy, and for
+                                 chunk-major the inverse index and work items */
+  HILS_STEP_COUNT = 11
 } hils_step;
 
 /*
@@ -155,6 +160,15 @@ int32_t hils_version(void);
 
 /* Bytes of workspace that `op` needs for problem `p` (written to *bytes). */
 hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes);
+
+/*
+ * The forward strategy hils_attn_fwd runs for problem `p` (p->fwd_strategy,
+ * or the one HILS_FWD_AUTO resolves to by shape), written to *strategy as a
+ * hils_fwd_strategy other than AUTO. Errors as hils_workspace_size for
+ * HILS_OP_FWD: HILS_ERR_INVALID for a null or malformed problem,
+ * HILS_ERR_UNSUPPORTED when no strategy runs it.
+ */
+hils_status hils_fwd_strategy_of(const hils_problem* p, int32_t* strategy);
 
 /*
  * Routing only: Q-Cal, surrogate scores, GQA max and top-K selection

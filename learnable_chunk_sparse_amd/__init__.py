@@ -25,12 +25,13 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported problem",
 
 EXPORTS = ("hils_status_string", "hils_version", "hils_workspace_size", "hils_route",
            "hils_attn_fwd", "hils_attn_bwd", "hils_decode", "hils_decode_paged", "hils_landmark_fwd",
-           "hils_landmark_bwd", "hils_hope", "hils_decode_noalloc")
+           "hils_landmark_bwd", "hils_hope", "hils_decode_noalloc", "hils_fwd_strategy_of")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 FWD_AUTO, FWD_UNION, FWD_COMPACT, FWD_CHUNK_MAJOR = 0, 1, 2, 3
 STEP_QCAL, STEP_ROUTE, STEP_ATTN_FWD, STEP_DECODE, STEP_BWD = 0, 1, 2, 3, 4
 STEP_LANDMARK_FWD, STEP_LANDMARK_BWD, STEP_HOPE, STEP_WINDOW, STEP_CHUNKS = 5, 6, 7, 8, 9
-STEP_COUNT = 10
+STEP_PREP = 10
+STEP_COUNT = 11
 
 
 class HilsError(RuntimeError):
@@ -102,6 +103,8 @@ def lib():
         L.hils_version.restype = i32
         L.hils_workspace_size.restype = ctypes.c_int
         L.hils_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz)]
+        L.hils_fwd_strategy_of.restype = ctypes.c_int
+        L.hils_fwd_strategy_of.argtypes = [P, ctypes.POINTER(i32)]
         L.hils_route.restype = ctypes.c_int
         L.hils_route.argtypes = [P] + [vp] * 9 + [sz, vp]
         L.hils_attn_fwd.restype = ctypes.c_int
@@ -242,6 +245,14 @@ def _prefill_specs(q, k, v, kL, e, S, h, W_down, W_up):
 def workspace_size(p: Problem, op: int) -> int:
     n = ctypes.c_size_t(0)
     _check("hils_workspace_size", lib().hils_workspace_size(ctypes.byref(p), op, ctypes.byref(n)))
+    return n.value
+
+
+def fwd_strategy_of(p: Problem) -> int:
+    """The forward strategy hils_attn_fwd runs for p (FWD_UNION, FWD_COMPACT
+    or FWD_CHUNK_MAJOR)."""
+    n = ctypes.c_int32(0)
+    _check("hils_fwd_strategy_of", lib().hils_fwd_strategy_of(ctypes.byref(p), ctypes.byref(n)))
     return n.value
 
 

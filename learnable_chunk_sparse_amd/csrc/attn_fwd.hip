@@ -748,12 +748,10 @@ hipError_t launch_vt_perm(const Dims& p, const void* v, void* vt, hipStream_t st
 }
 
 template <typename T>
-static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void* v, void* vt,
+static hipError_t fwd_t(const Dims& p, const void* q, const void* k, const void* vt,
                         const int32_t* idx, const float* sc, const float* sl, void* o, float* lse,
                         hipStream_t st) {
   const int Np = (p.N + 63) / 64 * 64;
-  hipError_t err = p.d == 64 ? vt_go<T, 64>(p, v, vt, Np, st) : vt_go<T, 128>(p, v, vt, Np, st);
-  if (err != hipSuccess) return err;
   if (fwd_strategy_of(p) == 3) return hipErrorInvalidValue;  // run from the C ABI step by step
   if (!fwd_use_shared(p)) return launch_fwd_sparse(p, q, k, vt, Np, idx, sc, sl, o, lse, st);
   switch (p.G * 1000 + p.d) {
@@ -793,11 +791,11 @@ size_t attn_fwd_vt_bytes(const Dims& p) {
   return (size_t)p.B * p.Hkv * p.d * ((p.N + 63) / 64 * 64) * el;
 }
 
-hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v, void* vt,
+hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* vt,
                            const int32_t* topk_idx, const float* topk_score, const float* sel_lse,
                            void* o, float* lse, hipStream_t st) {
-  if (p.dtype == 1) return fwd_t<uint16_t>(p, q, k, v, vt, topk_idx, topk_score, sel_lse, o, lse, st);
-  return fwd_t<float>(p, q, k, v, vt, topk_idx, topk_score, sel_lse, o, lse, st);
+  if (p.dtype == 1) return fwd_t<uint16_t>(p, q, k, vt, topk_idx, topk_score, sel_lse, o, lse, st);
+  return fwd_t<float>(p, q, k, vt, topk_idx, topk_score, sel_lse, o, lse, st);
 }
 
 }  // namespace hils

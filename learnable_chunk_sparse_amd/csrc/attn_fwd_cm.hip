@@ -577,13 +577,9 @@ template <typename T, int G, int DH>
 hipError_t cm_chunks_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                         const InvIndex& ix, const CmItems& it, void* part, hipStream_t st) {
   const int maxit = cm_max_items(p);
-  hipLaunchKernelGGL(k_cm_items, dim3(p.B * p.Hkv), dim3(256), 0, st, ix.off, it.items, it.nitems,
-                     it.scratch, p.C, CM_ITEM_ROWS / G, maxit);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   const size_t lds = sizeof(T) * (size_t)WSlot<T, DH>::ELEMS;
   auto kern = k_fwd_cm_chunks<T, G, DH>;
-  err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(maxit, p.B * p.Hkv), dim3(256), lds, st,
                      (const T*)q, (const T*)k, (const T*)vt, ix.off, ix.lst, it.items, it.nitems,
@@ -662,6 +658,13 @@ size_t fwd_cm_items_carve(const Dims& p, void* base, CmItems* out) {
   out->nitems = (int*)take(bg * sizeof(int));
   out->scratch = (int*)take(bg * (size_t)p.C * sizeof(int));
   return o;
+}
+
+hipError_t launch_cm_items(const Dims& p, const InvIndex& ix, const CmItems& it, hipStream_t st) {
+  if (p.C == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_cm_items, dim3(p.B * p.Hkv), dim3(256), 0, st, ix.off, it.items, it.nitems,
+                     it.scratch, p.C, CM_ITEM_ROWS / p.G, cm_max_items(p));
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_cm_chunks(const Dims& p, const void* q, const void* k, const void* vt, int Np,

@@ -354,6 +354,16 @@ hils_status hils_workspace_size(const hils_problem* p, int32_t op, size_t* bytes
   return HILS_ERR_INVALID;
 }
 
+hils_status hils_fwd_strategy_of(const hils_problem* p, int32_t* strategy) {
+  if (strategy == nullptr) return HILS_ERR_INVALID;
+  hils_status s = check_problem(p, HILS_OP_FWD);
+  if (s != HILS_OK) return s;
+  const Dims d = dims_of(p);
+  if (!fwd_fits_lds(d)) return HILS_ERR_UNSUPPORTED;
+  *strategy = hils::fwd_strategy_of(d);
+  return HILS_OK;
+}
+
 hils_status hils_route(const hils_problem* p, const void* q, const void* kL, const void* e,
                        const void* h, const void* W_down, const void* W_up, int32_t* topk_idx,
                        float* topk_score, void* ws, size_t ws_bytes, void* stream) {
@@ -401,16 +411,27 @@ hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, c
   if ((s = expand_shared(d, sq, W_down, W_up, st)) != HILS_OK) return s;
   s = route_with_qcal(p->timing, d, w.rt, q, h, W_down, W_up, kL, e, topk_idx, w.s_T, w.sel_lse, st);
   if (s != HILS_OK) return s;
-  if (hils::fwd_strategy_of(d) != HILS_FWD_CHUNK_MAJOR)
-    return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] { return hils::launch_attn_fwd(d, q, k, v, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st); }));
-  // chunk-major: V^T copy, inverse index, selected chunks, then window + fusion
   const int Np = (d.N + 63) / 64 * 64;
+  if (hils::fwd_strategy_of(d) != HILS_FWD_CHUNK_MAJOR)
+    return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] {
+      hipError_t e2 = timed(p->timing, HILS_STEP_PREP, st, [&] { return hils::launch_vt_perm(d, v, w.vt, st); });
+      if (e2 != hipSuccess) return e2;
+      return timed(p->timing, HILS_STEP_WINDOW, st, [&] {
+        return hils::launch_attn_fwd(d, q, k, w.vt, topk_idx, w.s_T, w.sel_lse, o, lse, st);
+      });
+    }));
+  // chunk-major: V^T copy, inverse index and work items; selected chunks;
+  // then window + fusion
   return hip_status(timed(p->timing, HILS_STEP_ATTN_FWD, st, [&] {
-    hipError_t e2 = hils::launch_vt_perm(d, v, w.vt, st);
+    hipError_t e2 = timed(p->timing, HILS_STEP_PREP, st, [&] {
+      hipError_t e3 = hils::launch_vt_perm(d, v, w.vt, st);
+      if (e3 != hipSuccess) return e3;
+      e3 = hils::launch_inv_index(d, topk_idx, w.ix, st);
+      if (e3 != hipSuccess) return e3;
+      return hils::launch_cm_items(d, w.ix, w.items, st);
+    });
     if (e2 != hipSuccess) return e2;
     e2 = timed(p->timing, HILS_STEP_CHUNKS, st, [&] {
-      hipError_t e3 = hils::launch_inv_index(d, topk_idx, w.ix, st);
-      if (e3 != hipSuccess) return e3;
       return hils::launch_fwd_cm_chunks(d, q, k, w.vt, Np, w.ix, w.items, w.part, st);
     });
     if (e2 != hipSuccess) return e2;

@@ -40,9 +40,10 @@ hipError_t launch_route(const Dims& p, const void* qs, bool q_is_f32, const void
                         int32_t* topk_idx, float* topk_score, float* sel_lse, hipStream_t st,
                         const RouteU& ru = RouteU());
 
-// Fused window attention + selected-chunk attention + fusion.
-// vt: workspace for the transposed, token-permuted copy of V (attn_fwd_vt_bytes).
-hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* v, void* vt,
+// Fused window attention + selected-chunk attention + fusion (the query-major
+// strategies). vt: the transposed, token-permuted copy of V that
+// launch_vt_perm wrote (attn_fwd_vt_bytes).
+hipError_t launch_attn_fwd(const Dims& p, const void* q, const void* k, const void* vt,
                            const int32_t* topk_idx, const float* topk_score, const float* sel_lse,
                            void* o, float* lse, hipStream_t st);
 size_t attn_fwd_lds_bytes(const Dims& p);
@@ -88,6 +89,8 @@ struct CmItems {
   int* scratch = nullptr;
 };
 size_t fwd_cm_items_carve(const Dims& p, void* base, CmItems* out);
+// chunk lists cut into work items (after launch_inv_index)
+hipError_t launch_cm_items(const Dims& p, const InvIndex& ix, const CmItems& it, hipStream_t st);
 hipError_t launch_fwd_cm_chunks(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                                 const InvIndex& ix, const CmItems& it, void* part, hipStream_t st);
 hipError_t launch_fwd_cm_window(const Dims& p, const void* q, const void* k, const void* vt, int Np,

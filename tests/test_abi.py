@@ -169,6 +169,27 @@ def test_fwd_strategy_is_a_field_of_the_call():
         assert st in (0, 2), (s_, st)
 
 
+def test_fwd_strategy_of_reports_what_the_call_runs():
+    """hils_fwd_strategy_of returns the problem's own strategy when it names
+    one and resolves AUTO by shape: packed union where a tile's selections
+    cover the chunks several times over (the 345M prefill), chunk-major for
+    the long GQA prefills (131072 and 524288 tokens); errors as the forward's
+    workspace query."""
+    for s_ in (L.FWD_UNION, L.FWD_COMPACT, L.FWD_CHUNK_MAJOR):
+        assert L.fwd_strategy_of(prob(fwd_strategy=s_)) == s_
+    assert L.fwd_strategy_of(prob()) == L.FWD_UNION
+    big = prob(B=1, Hq=32, Hkv=8, d=128, Nq=131072, Nk=131072, W=1024, D=2048)
+    assert L.fwd_strategy_of(big) == L.FWD_CHUNK_MAJOR
+    long_ = prob(B=1, Nq=524288, Nk=524288, K=32, r=0, D=0)
+    assert L.fwd_strategy_of(long_) == L.FWD_CHUNK_MAJOR
+    out = ctypes.c_int32(-7)
+    lib = L.lib()
+    assert lib.hils_fwd_strategy_of(ctypes.byref(prob(Hq=6, Hkv=4)), ctypes.byref(out)) == 1
+    assert lib.hils_fwd_strategy_of(ctypes.byref(prob(d=96)), ctypes.byref(out)) == 2
+    assert lib.hils_fwd_strategy_of(ctypes.byref(prob()), None) == 1
+    assert out.value == -7  # nothing written on error
+
+
 def test_timing_struct_layout():
     """hils_timing is STEP_COUNT start handles then STEP_COUNT stop handles,
     and the problem carries a pointer to it after the strategy field."""

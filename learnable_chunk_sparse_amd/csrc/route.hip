@@ -131,17 +131,20 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
   constexpr int VEC = 16 / sizeof(T);
   constexpr int NV = TILE_ELEMS / 256 / VEC;
   __shared__ __align__(16) T kl_s[RT_TC * KP];
-  __shared__ float e_s[RT_TC];
+  __shared__ __align__(16) float e_s[RT_TC];
   constexpr int URN = UR > 0 ? UR : 1, RR = 32 * URN, RP = RR + 8;
   __shared__ __align__(16) uint16_t klh_s[UR ? RT_TC * RP : 8], kll_s[UR ? RT_TC * RP : 8];
-  constexpr int SM = (G >= 2 || BUFSEL) ? 2 : 0;
-  // per-wave score tile (positions x chunks) for the turnaround (SM 0)
+  constexpr int SM = G >= 2 ? 2 : (BUFSEL ? 1 : 0);
+  static_assert(SM != 1 || PW == 64, "SM 1: one position per lane");
+  // per-wave score tile (positions x chunks) for the turnaround (SM 0, SM 1)
   __shared__ __align__(16) float sc_s[SM == 2 ? 1 : 4][SM == 2 ? 1 : PW][16 + 4];
   // per-position buffers of candidates that beat the running K-th key
   // (slot-major: position p's slot j at [j][p]); SM 2 also passes counts and
-  // K-th keys between the output layout and the owner lanes
-  __shared__ float cbs_s[SM ? 4 : 1][SM ? SELBUF : 1][SM ? PW : 1];  // buffered scores
-  __shared__ int cbc_s[SM ? 4 : 1][SM ? SELBUF : 1][SM ? PW : 1];    // and their chunks
+  // K-th keys between the output layout and the owner lanes. SM 1 flushes as
+  // soon as a buffer is full, also inside a step, so 16 slots do.
+  constexpr int SB = SM == 1 ? 16 : SELBUF;
+  __shared__ float cbs_s[SM ? 4 : 1][SM ? SB : 1][SM ? PW : 1];  // buffered scores
+  __shared__ int cbc_s[SM ? 4 : 1][SM ? SB : 1][SM ? PW : 1];    // and their chunks
   __shared__ float thr_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
   __shared__ int cnt_s[SM == 2 ? 4 : 1][SM == 2 ? PW : 1];
 
@@ -234,6 +237,30 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
   // the wave's positions span fewer than S: chunks below the first one's
   // distant count are distant for all of them
   const int nd_lo = pw0 < N ? n_distant(pw0, W, S) : 0;
+  // SM 1 state: lane p owns position pw0 + p outright: its buffer fill and
+  // its score threshold (the running K-th key's score, -inf until K are in)
+  int cnt1 = 0;
+  float thr1 = NEG_INF;
+  // SM 1: merge every lane's buffer (at most 16) into its list
+  auto flush1 = [&]() __attribute__((always_inline)) {
+    wave_lds_sync();
+    Key nk[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const Key x = sel_key(cbs_s[w][j][lane], cbc_s[w][j][lane]);
+      nk[j] = j < cnt1 ? x : 0.0;
+    }
+    bitonic_sort_desc<16>(nk);
+    merge_top<KC>(tk, nk);
+    Key th = tk[KC - 1];
+    if (K < KC) {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) th = k == K - 1 ? tk[k] : th;
+    }
+    thr1 = th == 0.0 ? NEG_INF : key_score(th);
+    cnt1 = 0;
+    wave_lds_sync();
+  };
   // merge every owner lane's buffered candidates into its top-K, 16 at a time
   // (bitonic sort of the 16, then a bitonic merge into the list); the lanes
   // of the wave take part together
@@ -364,6 +391,65 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
           kq[kr] = *reinterpret_cast<const FT*>(kll_s + o);
         }
       }
+      if constexpr (SM == 1) {
+        // scores transposed (landmark keys as the A operand): lane (grp, col)
+        // holds chunks c0 + 4 grp + i of position 16 rb + col, turned around
+        // through LDS so that lane p holds all 16 chunks of position p
+        const f32x4 ev4 = *reinterpret_cast<const f32x4*>(&e_s[c0 - t0 + 4 * grp]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            acc = mma16(bf[ks], ahi[rb][0][ks], acc);
+            if constexpr (HAS_LO) acc = mma16(bf[ks], alo[rb][0][ks], acc);
+          }
+          if constexpr (UR > 0) {
+#pragma unroll
+            for (int kr = 0; kr < UR; ++kr) {
+              acc = mma16(kh[kr], uhi[rb][kr], acc);
+              acc = mma16(kq[kr], uhi[rb][kr], acc);
+              acc = mma16(kh[kr], ulo[rb][kr], acc);
+            }
+          }
+          f32x4 sv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[i] = fmaf(acc[i], scale, ev4[i]);
+          *reinterpret_cast<f32x4*>(&sc_s[w][16 * rb + col][4 * grp]) = sv;
+        }
+        wave_lds_sync();
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sc_s[w][lane][j]);
+          v[j] = x[0]; v[j + 1] = x[1]; v[j + 2] = x[2]; v[j + 3] = x[3];
+        }
+        if (c0 + 15 >= nd_lo) {
+          // chunks that are not distant for this position never pass (NaN
+          // compares false, also against a threshold of -inf)
+          const int lim = mynd - c0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = j < lim ? v[j] : __builtin_nanf("");
+        }
+        // append the candidates that reach the position's threshold; a full
+        // buffer is merged first (the rest of the step is then filtered
+        // against the refreshed threshold)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          bool p = v[j] >= thr1;
+          if (__ballot(p) == 0) continue;
+          if (__ballot(p && cnt1 == SB) != 0) {
+            flush1();
+            p = v[j] >= thr1;
+          }
+          if (p) {
+            cbs_s[w][cnt1][lane] = v[j];
+            cbc_s[w][cnt1][lane] = c0 + j;
+          }
+          cnt1 += p ? 1 : 0;
+        }
+        continue;
+      }
       float sv_d[RBD][4];  // SM 2: this step's scores of the lane's candidate rows
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -478,6 +564,9 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
     }
   }
 
+  if constexpr (SM == 1) {
+    if (__ballot(cnt1 > 0) != 0) flush1();
+  }
   if constexpr (SM == 2) {
     bool any = false;
     if constexpr (CREG) {

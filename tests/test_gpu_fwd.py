@@ -82,31 +82,68 @@ def test_fwd_tiny_workload():
     fwd_parity(t, out, wl.S, wl.K, wl.W, "fp32", label="tiny")
 
 
-def test_route_scores_match_oracle():
-    wl = Workload("route", seed=5, dtype="bf16", B=1, Hq=8, Hkv=2, d=128, N=1200, S=64, K=6, W=128,
-                  D=64, r=32, e_range=2.0)
+@pytest.mark.parametrize("G,d,r,K", [
+    (4, 128, 32, 6),    # GQA: fp32 calibrated queries, per-head scores in their own pass
+    (1, 64, 32, 6),     # one head per KV group, bf16, rank 32: Q-Cal folded into routing (u)
+    (1, 128, 64, 12),   # the same with rank 64 and d = 128
+    (1, 64, 32, 20),    # K > 16: fp32 calibrated queries with one head per group
+    (2, 64, 0, 6),      # no Q-Cal
+])
+def test_route_scores_match_oracle(G, d, r, K):
+    """The selected chunks' per-head scores that routing returns (the fusion
+    reads them) against the oracle's surrogate scores, within 2e-5."""
+    wl = Workload("route", seed=5, dtype="bf16", B=1, Hq=2 * G, Hkv=2, d=d, N=1200, S=64, K=K,
+                  W=128, D=64 if r else 0, r=r, e_range=2.0)
     t = make_inputs(wl)
     td = to_dev(t)
-    idx, sc = L().hils_route(td["q"], td["kL"], td["e"], wl.S, wl.K, wl.W, h=td["h"],
-                             W_down=td["W_down"], W_up=td["W_up"], with_scores=True)
+    idx, sc = L().hils_route(td["q"], td["kL"], td["e"], wl.S, wl.K, wl.W, h=td.get("h"),
+                             W_down=td.get("W_down"), W_up=td.get("W_up"), with_scores=True)
     idx = idx.cpu().numpy()
     sc = sc.cpu().numpy()
     P = H.Problem(t, wl.S, wl.K, wl.W)
-    G = wl.G
     err = 0.0
+    n = 0
     for g in range(wl.Hkv):
+        hs = slice(g * G, (g + 1) * G)
         for i in range(0, wl.N, 7):
-            hs = slice(g * G, (g + 1) * G)
             qh, _ = P.qhat_row(0, g, i, P.q[0, hs, i])
+            s_ref, _ = H.surrogate_scores(qh, P.kL[0, g], P.e[0, g], H.n_distant(i, wl.W, wl.S),
+                                          P.scale)
             for kk in range(wl.K):
                 c = idx[0, g, i, kk]
                 if c < 0:
                     assert np.all(np.isnan(sc[0, hs, i, kk]))
                     continue
-                ref = P.scale * qh @ P.kL[0, g, c] + P.e[0, g, c]
-                err = max(err, float(np.abs(sc[0, hs, i, kk] - ref).max()))
-    say(f"route score max abs err {err:.3e}")
-    assert err < 2e-5
+                err = max(err, float(np.abs(sc[0, hs, i, kk] - s_ref[:, c]).max()))
+                n += 1
+    say(f"route scores G{G} d{d} r{r} K{K}: {n} checked, max abs err {err:.3e}")
+    assert n > 0 and err < 2e-5
+
+
+# one head per KV group over 625-938 distant chunks: routing's long-scan
+# selection (every position's candidates in its own lane, buffered against
+# its running K-th score), on both scoring paths (fp32 calibrated queries;
+# bf16 with Q-Cal folded into routing), d = 64 and 128, K up to 32
+LONG_SCAN = [
+    # name, dtype, d, N, K, W, D, r
+    ("ls_bf16_d64_k32", "bf16", 64, 40000, 32, 512, 64, 32),
+    ("ls_bf16_d64_k8_u", "bf16", 64, 41000, 8, 256, 64, 32),
+    ("ls_bf16_d128_k16_u", "bf16", 128, 60000, 16, 1024, 64, 64),
+    ("ls_fp32_d64_k16", "fp32", 64, 40000, 16, 512, 0, 0),
+    ("ls_bf16_d128_k4", "bf16", 128, 44000, 4, 128, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", LONG_SCAN, ids=[c[0] for c in LONG_SCAN])
+def test_fwd_long_scan_sampled_rows(case):
+    name, dt, d, N, K, W, D, r = case
+    wl = Workload(name, seed=21, dtype=dt, B=1, Hq=2, Hkv=2, d=d, N=N, S=64, K=K, W=W, D=D, r=r,
+                  e_range=2.0)
+    say(f"case {name}")
+    t = make_inputs(wl)
+    out = run_fwd(wl, t)
+    torch.cuda.synchronize()
+    fwd_parity(t, out, wl.S, wl.K, wl.W, dt, rows=sample_rows(wl, 150), label=name)
 
 
 def group_parity(wl, t_gpu, out, groups, rows, label):

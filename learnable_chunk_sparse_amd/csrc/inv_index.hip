@@ -71,8 +71,9 @@ __global__ __launch_bounds__(256) void k_ix_chunk_scan(int* __restrict__ off, in
   if (threadIdx.x == 0) a[C] = tot;
 }
 
-// Ranges walk their positions SB at a time (SB K <= 256 entries, one per
-// thread, SB <= 32 bits of the masks).
+// Ranges walk their positions SB at a time (SB K <= 512 entries, two per
+// thread, SB <= 32 bits of the masks); the next step's ids are loaded while
+// the current step is placed.
 __global__ __launch_bounds__(256) void k_ix_fill(const int32_t* __restrict__ topk_idx,
                                                  const int* __restrict__ cnt, const int* __restrict__ off,
                                                  int* __restrict__ lst, int* __restrict__ rank, int N,
@@ -92,28 +93,53 @@ __global__ __launch_bounds__(256) void k_ix_fill(const int32_t* __restrict__ top
   const long i0 = sp * per, i1 = min((long)N, i0 + per);
   const int32_t* src = topk_idx + (long)bg * N * K;
   int* dst = lst + (long)bg * N * K;
-  const int SB = min(32, 256 / K);
-  const int pl = tid / K, kk = tid - pl * K;
-  for (long i = i0; i < i1; i += SB) {
-    const long pos = i + pl;
+  const int SB = min(32, 512 / K);
+  int pl[2], kk[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    pl[u] = (tid + 256 * u) / K;
+    kk[u] = tid + 256 * u - pl[u] * K;
+  }
+  auto fetch = [&](long i, int u) __attribute__((always_inline)) {
+    const long pos = i + pl[u];
     int c = -1;
-    if (pl < SB && pos < i1) c = src[pos * K + kk];
-    if (c >= C) c = -1;
-    if (c >= 0) atomicOr(&msk[c], 1u << pl);
+    if (pl[u] < SB && pos < i1) c = src[pos * K + kk[u]];
+    return c < C ? c : -1;
+  };
+  int cn[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) cn[u] = fetch(i0, u);
+  for (long i = i0; i < i1; i += SB) {
+    int c[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      c[u] = cn[u];
+      cn[u] = i + SB < i1 ? fetch(i + SB, u) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (c[u] >= 0) atomicOr(&msk[c[u]], 1u << pl[u]);
     __syncthreads();
-    unsigned m = 0u;
-    if (c >= 0) {
-      m = msk[c];
-      const int e = cur[c] + __popc(m & ((1u << pl) - 1u));
-      dst[e] = (int)((pos << 6) | kk);
-      if (rank != nullptr) rank[((size_t)bg * N + pos) * K + kk] = e;
+    unsigned m[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      m[u] = 0u;
+      if (c[u] >= 0) {
+        m[u] = msk[c[u]];
+        const long pos = i + pl[u];
+        const int e = cur[c[u]] + __popc(m[u] & ((1u << pl[u]) - 1u));
+        dst[e] = (int)((pos << 6) | kk[u]);
+        if (rank != nullptr) rank[((size_t)bg * N + pos) * K + kk[u]] = e;
+      }
     }
     __syncthreads();
     // the step's last position holding c advances the cursor and clears the mask
-    if (c >= 0 && (m >> pl) == 1u) {
-      cur[c] += __popc(m);
-      msk[c] = 0u;
-    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (c[u] >= 0 && (m[u] >> pl[u]) == 1u) {
+        cur[c[u]] += __popc(m[u]);
+        msk[c[u]] = 0u;
+      }
     __syncthreads();
   }
 }

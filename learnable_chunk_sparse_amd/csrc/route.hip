@@ -605,6 +605,14 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       if (k < K) dst[k] = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
+    if constexpr (G >= 2) {
+      // the per-head scores below read every position's ids from LDS,
+      // position-major ([p][k], K <= SELBUF) in the buffer's space
+      int* ids_s = &cbc_s[w][0][0];
+#pragma unroll
+      for (int k = 0; k < KC; ++k)
+        if (k < K) ids_s[lane * SELBUF + k] = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
+    }
     if (G == 1 && topk_score != nullptr) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -625,89 +633,117 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
               if (ok) lse_add(sv[k]);
             }
         }
-        // grouped heads: k_route_scores computes each head's scores
+        // grouped heads: their per-head scores follow below
         if (sel_lse != nullptr)
           sel_lse[((size_t)b * Hq + g * G + hh) * N + mypos] = lm == NEG_INF ? NEG_INF : lm + __logf(ls);
       }
     }
   }
-}
 
-// Each head's fp32 score of every selected chunk, s = scale q_hat . kL_c + e_c
-// (NaN in empty slots), and the log-sum-exp of a head's selected scores, for
-// grouped heads (the selection itself ran on the group maximum). Four lanes
-// per (b, head, position) row, each holding a quarter of q_hat and reading
-// the matching quarter of every selected landmark row (coalesced 16-byte
-// vectors), sums combined by two lane exchanges.
-template <typename T, typename QT, int DH>
-__global__ __launch_bounds__(256) void k_route_scores(const QT* __restrict__ qs, const T* __restrict__ kL,
-                                                      const T* __restrict__ e,
-                                                      const int32_t* __restrict__ topk_idx,
-                                                      float* __restrict__ topk_score,
-                                                      float* __restrict__ sel_lse, long rows, int N,
-                                                      int C, int Hq, int G, int K, float scale) {
-  constexpr int QD = DH / 4;  // dims per lane
-  const long row = (long)blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int part = threadIdx.x & 3;
-  const long rc = row < rows ? row : rows - 1;
-  const long bh = rc / N;
-  const int pos = (int)(rc - bh * N);
-  const int h = (int)(bh % Hq), b = (int)(bh / Hq);
-  const int Hkv = Hq / G, g = h / G;
-  float qv[QD];
-  const QT* qr = qs + rc * DH + part * QD;
+  // Grouped heads: each head's fp32 score of every selected chunk (NaN in
+  // empty slots) and the log-sum-exp of a head's selected scores (the
+  // selection ran on the group maximum). The scoring fragments of all the
+  // wave's positions and heads are still in registers: per position, one MFMA
+  // product per head of that position's 16 selected landmark rows (A,
+  // gathered from L2, the next block's rows in flight) against the 16
+  // positions' queries (B, the scan's fragments), of which the position's own
+  // column of D is kept: lane (grp, r) holds its slots 4 grp .. 4 grp + 3, a
+  // 16-byte run of the scores, and the log-sum-exp combines the four lanes.
+  if constexpr (G >= 2) {
+    if (topk_score != nullptr || sel_lse != nullptr) {
+      wave_lds_sync();
+      constexpr int NKB = (KC + 15) / 16;
+      const int* ids_s = &cbc_s[w][0][0];
+      const int np = min(PW, N - pw0);  // positions of this wave (uniform; <= 0 past the end)
+      struct BIn {
+        FT kf[KS];
+        int c4[4];    // ids of slots 16 kb + 4 grp + i
+        float ev4[4]; // and their biases
+      };
+      auto fetchb = [&](BIn& x, int p, int kb) __attribute__((always_inline)) {
+        const int pp = p < np ? p : 0;
+        const int slot = 16 * kb + col;
+        const int c = (slot < K && p < np) ? ids_s[pp * SELBUF + slot] : -1;
+        const T* kr = kLg + (size_t)(c >= 0 ? c : 0) * DH + 8 * grp;
 #pragma unroll
-  for (int j = 0; j < QD; j += 4) {
-    if constexpr (sizeof(QT) == 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(qr + j);
-      qv[j] = x[0]; qv[j + 1] = x[1]; qv[j + 2] = x[2]; qv[j + 3] = x[3];
-    } else {
+        for (int ks = 0; ks < KS; ++ks) x.kf[ks] = ld8<T>(kr + 32 * ks);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) qv[j + t] = to_f<QT>(qr[j + t]);
-    }
-  }
-  const size_t bg = (size_t)b * Hkv + g;
-  const int32_t* ids = topk_idx + (bg * N + pos) * K;
-  const T* kb = kL + bg * C * DH + part * QD;
-  const T* eb = e + bg * C;
-  float lm = NEG_INF, ls = 0.f;
-  // four slots at a time: their ids, biases and landmark quarters are all
-  // requested before the products
-  for (int k0 = 0; k0 < K; k0 += 4) {
-    int cs[4];
-    float ev[4];
-    typename Frag<T>::type kv[4][QD / 8];
+        for (int i = 0; i < 4; ++i) {
+          const int s4 = 16 * kb + 4 * grp + i;
+          const int ci = (s4 < K && p < np) ? ids_s[pp * SELBUF + s4] : -1;
+          x.c4[i] = ci;
+          x.ev4[i] = to_f<T>(eg[ci >= 0 ? ci : 0]);
+        }
+      };
+      BIn bcur, bnxt;
+      if (np > 0) fetchb(bcur, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cs[j] = k0 + j < K ? ids[k0 + j] : -1;
+      for (int rb = 0; rb < RB; ++rb) {
+        for (int r = 0; r < 16; ++r) {
+          const int p = 16 * rb + r;
+          if (p >= np) break;  // uniform
+          const int pos = pw0 + p;
+          const bool mine = col == r;
+          float lm2[G], ls2[G];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cc = cs[j] >= 0 ? cs[j] : 0;
-      ev[j] = to_f<T>(eb[cc]);
-      const T* kr = kb + (size_t)cc * DH;
+          for (int hh = 0; hh < G; ++hh) {
+            lm2[hh] = NEG_INF;
+            ls2[hh] = 0.f;
+          }
 #pragma unroll
-      for (int x = 0; x < QD / 8; ++x) kv[j][x] = ld8<T>(kr + 8 * x);
-    }
+          for (int kb = 0; kb < NKB; ++kb) {
+            // the next (position, block)'s rows in flight
+            if (kb + 1 < NKB) fetchb(bnxt, p, kb + 1);
+            else fetchb(bnxt, p + 1, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float a = 0.f;
+            for (int hh = 0; hh < G; ++hh) {
+              f32x4 acc = zero4();
 #pragma unroll
-      for (int x = 0; x < QD / 8; ++x)
+              for (int ks = 0; ks < KS; ++ks) {
+                acc = mma16(bcur.kf[ks], ahi[rb][hh][ks], acc);
+                if constexpr (HAS_LO) acc = mma16(bcur.kf[ks], alo[rb][hh][ks], acc);
+              }
+              // D layout: slot 16 kb + 4 grp + i, position 16 rb + col
+              f32x4 sc;
+              float mx = NEG_INF;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) a = fmaf(qv[8 * x + t], (float)kv[j][x][t], a);
-      a += __shfl_xor(a, 1, 64);
-      a += __shfl_xor(a, 2, 64);
-      const int c = cs[j];
-      const float sc = c >= 0 ? fmaf(a, scale, ev[j]) : __builtin_nanf("");
-      if (c >= 0) {
-        const float mn = fmaxf(lm, sc);
-        ls = ls * __expf(lm - mn) + __expf(sc - mn);
-        lm = mn;
+              for (int i = 0; i < 4; ++i) {
+                sc[i] = bcur.c4[i] >= 0 ? fmaf(acc[i], scale, bcur.ev4[i]) : __builtin_nanf("");
+                if (bcur.c4[i] >= 0) mx = fmaxf(mx, sc[i]);
+              }
+              if (mine && topk_score != nullptr) {
+                float* dsc = topk_score + (((size_t)b * Hq + g * G + hh) * N + pos) * K;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int s4 = 16 * kb + 4 * grp + i;
+                  if (s4 < K) dsc[s4] = sc[i];
+                }
+              }
+              // the position's four lanes (grp = 0..3, same col) combine
+              mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+              mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+              const float mn = fmaxf(lm2[hh], mx);
+              float ex = 0.f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                ex += (bcur.c4[i] >= 0 && mn != NEG_INF) ? __expf(sc[i] - mn) : 0.f;
+              ex += __shfl_xor(ex, 16, 64);
+              ex += __shfl_xor(ex, 32, 64);
+              ls2[hh] = (lm2[hh] == NEG_INF ? 0.f : ls2[hh] * __expf(lm2[hh] - mn)) + ex;
+              lm2[hh] = mn;
+            }
+            bcur = bnxt;
+          }
+          if (mine && grp == 0 && sel_lse != nullptr) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh)
+              sel_lse[((size_t)b * Hq + g * G + hh) * N + pos] =
+                  lm2[hh] == NEG_INF ? NEG_INF : lm2[hh] + __logf(ls2[hh]);
+          }
+        }
       }
-      if (part == 0 && row < rows && topk_score != nullptr && k0 + j < K) topk_score[row * K + k0 + j] = sc;
     }
   }
-  if (part == 0 && row < rows && sel_lse != nullptr)
-    sel_lse[row] = lm == NEG_INF ? NEG_INF : lm + __logf(ls);
 }
 
 template <typename T, typename QT, int G, int DH, int KC, int UR>
@@ -722,14 +758,6 @@ static hipError_t route_go(const Dims& p, const void* qs, const void* kL, const 
   hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), 0, st, (const QT*)qs,
                      (const T*)kL, (const T*)e, idx, sc, sl, p.N, p.C, p.Hkv, p.K, p.W, p.S, p.scale,
                      ntiles, ru.u, ru.klh, ru.kll);
-  if constexpr (G > 1) {
-    if (sc != nullptr || sl != nullptr) {
-      const long rows = (long)p.B * p.Hq * p.N;
-      hipLaunchKernelGGL((k_route_scores<T, QT, DH>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0,
-                         st, (const QT*)qs, (const T*)kL, (const T*)e, idx, sc, sl, rows, p.N, p.C,
-                         p.Hq, G, p.K, p.scale);
-    }
-  }
   return hipGetLastError();
 }
 

@@ -73,6 +73,14 @@ struct RowBlock {
 // others) is spread over many workgroups instead of one. One workgroup per
 // (b, KV head) lists them in chunk order: item = (chunk, first entry).
 constexpr int CM_ITEM_ROWS = 1024;
+// the window pass's 128-row tiles: at d = 128 each wave owns one 16-row block
+// (eight waves; with two blocks per wave the accumulators, score tiles,
+// query fragments and staged blocks needed ~480 registers, one wave per
+// SIMD), at d = 64 two (four waves)
+template <int DH>
+constexpr int cm_win_cb() { return DH == 128 ? 1 : 2; }
+template <int DH>
+constexpr int cm_win_threads() { return 512 / cm_win_cb<DH>(); }
 
 __global__ __launch_bounds__(256) void k_cm_items(const int* __restrict__ off, int2* __restrict__ items,
                                                   int* __restrict__ nitems, int* __restrict__ scratch,
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (DH == 64 ? 3 : 2) : 1) void 
 
 // ---------------------------------------------------------------- window pass
 template <typename T, int G, int DH>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_fwd_cm_window(
+__global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 && sizeof(T) == 2) ? 2 : 1) void k_fwd_cm_window(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ vt,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_score,
     const float* __restrict__ sel_lse, const int* __restrict__ rank, const T* __restrict__ part,
@@ -258,6 +266,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
     float scale, int ntiles) {
   typedef typename Frag<T>::type FT;
   typedef WSlot<T, DH> SG;
+  constexpr int CB = cm_win_cb<DH>();      // 16-row blocks per wave
+  constexpr int RW = 16 * CB;              // rows per wave
+  constexpr int NT = cm_win_threads<DH>(); // 128 rows per tile
+  constexpr int VPT = 2 * SG::KV / NT;     // staged 16-byte vectors per thread and block
   constexpr int R = 128;
   constexpr int TP = R / G;
   constexpr int KS = DH / 32;
@@ -280,12 +292,12 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vt + (size_t)bg * DH * Np, DH * Np * (int)sizeof(T));
 
   // wave w owns rows 32 w + 16 cb + cl
-  FT qf[2][KS];
-  int prow[2], wsr[2];
-  float lsel[2], Lr[2];
+  FT qf[CB][KS];
+  int prow[CB], wsr[CB];
+  float lsel[CB], Lr[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = 32 * w + 16 * cb + cl;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int r = RW * w + 16 * cb + cl;
     const int pos = p0 + r / G, hh = r % G;
     prow[cb] = pos < N ? pos : -1;
     wsr[cb] = pos < N ? n_distant(pos, W, S) * S : 0;
@@ -296,17 +308,17 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld8<T>(src + 32 * ks);
   }
-  const int pw_lo = p0 + 32 * w / G;
-  const int pw_hi = min(p0 + (32 * w + 31) / G, N - 1);
+  const int pw_lo = p0 + RW * w / G;
+  const int pw_hi = min(p0 + (RW * w + RW - 1) / G, N - 1);
   const bool wave_live = pw_lo < N;
-  const bool all_valid = p0 + (32 * w + 31) / G < N;
+  const bool all_valid = p0 + (RW * w + RW - 1) / G < N;
   const int ws_lo = wave_live ? n_distant(pw_lo, W, S) * S : 0;
   const int ws_hi = wave_live ? n_distant(pw_hi, W, S) * S : 0;
 
-  float m[2], lsum[2];
-  f32x4 oacc[MB][2];
+  float m[CB], lsum[CB];
+  f32x4 oacc[MB][CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     m[cb] = NEG_INF;
     lsum[cb] = 0.f;
 #pragma unroll
@@ -318,13 +330,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
   const int nW = (plast - kv_lo) / 64 + 1;
   // blocks in flight in registers: two sets (blocks n + 2, n + 3)
   constexpr int NSET = 2;
-  u32x4 stg[2][SG::VPT];
-  auto issue = [&](u32x4 (&rg)[SG::VPT], int n) __attribute__((always_inline)) {
+  u32x4 stg[2][VPT];
+  auto issue = [&](u32x4 (&rg)[VPT], int n) __attribute__((always_inline)) {
     const int kv0 = kv_lo + 64 * min(n, nW - 1);
 #pragma unroll
-    for (int s = 0; s < SG::VPT; ++s) {
-      const int vi = tid + 256 * s;
-      if (s < SG::VPT / 2) {
+    for (int s = 0; s < VPT; ++s) {
+      const int vi = tid + NT * s;
+      if (s < VPT / 2) {
         const int tok = vi / (DH / SG::VE), pt = vi - tok * (DH / SG::VE);
         rg[s] = buf_ld16(krs, ((kv0 + tok) * DH + pt * SG::VE) * (int)sizeof(T));
       } else {
@@ -334,13 +346,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
       }
     }
   };
-  auto commit = [&](const u32x4 (&rg)[SG::VPT], int slot) __attribute__((always_inline)) {
+  auto commit = [&](const u32x4 (&rg)[VPT], int slot) __attribute__((always_inline)) {
     T* base = slots + slot * SG::ELEMS;
 #pragma unroll
-    for (int s = 0; s < SG::VPT; ++s) {
-      const int vi = tid + 256 * s;
+    for (int s = 0; s < VPT; ++s) {
+      const int vi = tid + NT * s;
       T* dst;
-      if (s < SG::VPT / 2) {
+      if (s < VPT / 2) {
         const int tok = vi / (DH / SG::VE), pt = vi - tok * (DH / SG::VE);
         dst = base + tok * SG::KP + pt * SG::VE;
       } else {
@@ -358,22 +370,22 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
   auto window_block = [&](const T* sl, int kv0, auto masked) __attribute__((always_inline)) {
     constexpr bool MSK = decltype(masked)::value;
     constexpr float SHIFT_AT = 16.f;
-    f32x4 sacc[4][2];
+    f32x4 sacc[4][CB];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = zero4();
+      for (int cb = 0; cb < CB; ++cb) sacc[tb][cb] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const FT kf = ld8<T>(sl + (16 * tb + cl) * SG::KP + 8 * gl + 32 * ks);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) sacc[tb][cb] = mma16(kf, qf[cb][ks], sacc[tb][cb]);
+        for (int cb = 0; cb < CB; ++cb) sacc[tb][cb] = mma16(kf, qf[cb][ks], sacc[tb][cb]);
       }
     }
-    float bmx[2];
+    float bmx[CB];
     bool shift = false;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       float bmax = NEG_INF;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
     }
     if (__ballot(shift) != 0) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         const bool first = m[cb] == NEG_INF;
         const bool up = bmx[cb] > SHIFT_AT || (first && bmx[cb] != NEG_INF);
         const float dlt = up ? bmx[cb] : 0.f;
@@ -403,9 +415,9 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
         for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= alpha;
       }
     }
-    FT pf[2][2];
+    FT pf[CB][2];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       const float mc = m[cb] == NEG_INF ? 0.f : m[cb];
       float ps = 0.f;
 #pragma unroll
@@ -427,14 +439,14 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
       for (int ks = 0; ks < 2; ++ks) {
         const FT vf = ld8<T>(vb + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) oacc[mb][cb] = mma16(vf, pf[cb][ks], oacc[mb][cb]);
+        for (int cb = 0; cb < CB; ++cb) oacc[mb][cb] = mma16(vf, pf[cb][ks], oacc[mb][cb]);
       }
   };
 
   // one step: publish block n + 1 from register set rg into the other slot
   // (whose block n - 1 every wave has finished), reload rg with block n + 3,
   // then multiply block n
-  auto wstep = [&](int n, u32x4 (&rg)[SG::VPT]) __attribute__((always_inline)) {
+  auto wstep = [&](int n, u32x4 (&rg)[VPT]) __attribute__((always_inline)) {
     commit(rg, (n + 1) & 1);
     issue(rg, n + 1 + NSET);
     const T* sl = slots + (n & 1) * SG::ELEMS;
@@ -470,7 +482,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
 
   // fusion normaliser and the window's weight exp(lse_W - L)
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     const float ls = col_sum4(lsum[cb]);
     const float lW = (m[cb] + __log2f(ls)) * LN2;
     const float mx = fmaxf(lW, lsel[cb]);
@@ -483,14 +495,17 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
   }
 
   // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (dims in
-  // fragment order: this lane's 4 MB values are contiguous). SG slots at a
+  // fragment order: this lane's 4 MB values are contiguous). SLG slots at a
   // time: their weights, then all their loads, then the sums, so that the
-  // loads are in flight together.
+  // loads are in flight together. The two row blocks run one after the other
+  // (kept rolled: unrolled, both blocks' loads were live at once and the
+  // kernel needed ~480 registers at d = 128, one wave per SIMD; rolled, with
+  // four slots in flight, it fits two waves per SIMD).
   constexpr int VPS = 4 * MB * (int)sizeof(T) / 16;  // 16-byte vectors per lane and slot
-  constexpr int SLG = (sizeof(T) == 2 && DH == 128) ? 8 : 4;
+  constexpr int SLG = 4;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = 32 * w + 16 * cb + cl;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int r = RW * w + 16 * cb + cl;
     const int hh = r % G;
     const bool live = prow[cb] >= 0;
     const int pc = live ? prow[cb] : N - 1;
@@ -541,9 +556,9 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_f
 
   // write o and lse
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     if (prow[cb] < 0) continue;
-    const int r = 32 * w + 16 * cb + cl;
+    const int r = RW * w + 16 * cb + cl;
     const size_t ro = ((size_t)b * Hq + g * G + r % G) * N + prow[cb];
     if (gl == 0) lse[ro] = Lr[cb];
     T* dst = o + ro * DH + 4 * gl;
@@ -597,7 +612,7 @@ hipError_t cm_window_go(const Dims& p, const void* q, const void* k, const void*
   auto kern = k_fwd_cm_window<T, G, DH>;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(256), lds, st, (const T*)q, (const T*)k,
+  hipLaunchKernelGGL(kern, dim3(ntiles, p.B * p.Hkv), dim3(cm_win_threads<DH>()), lds, st, (const T*)q, (const T*)k,
                      (const T*)vt, idx, sc, sl, rank, (const T*)part, (T*)o, lse, p.N, Np, p.Hkv, p.K,
                      p.W, p.S, p.scale, ntiles);
   return hipGetLastError();

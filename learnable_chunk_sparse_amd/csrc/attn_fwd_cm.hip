@@ -73,12 +73,12 @@ struct RowBlock {
 // others) is spread over many workgroups instead of one. One workgroup per
 // (b, KV head) lists them in chunk order: item = (chunk, first entry).
 constexpr int CM_ITEM_ROWS = 1024;
-// the window pass's 128-row tiles: at d = 128 each wave owns one 16-row block
-// (eight waves; with two blocks per wave the accumulators, score tiles,
-// query fragments and staged blocks needed ~480 registers, one wave per
-// SIMD), at d = 64 two (four waves)
+// the window pass's 128-row tiles: each wave owns one 16-row block (eight
+// waves). With two blocks per wave the accumulators, score tiles, query
+// fragments and staged blocks needed ~480 registers at d = 128 (one wave per
+// SIMD) and 235 at d = 64 (two); with one, 198 and 120 (two and four).
 template <int DH>
-constexpr int cm_win_cb() { return DH == 128 ? 1 : 2; }
+constexpr int cm_win_cb() { return 1; }
 template <int DH>
 constexpr int cm_win_threads() { return 512 / cm_win_cb<DH>(); }
 

@@ -80,7 +80,9 @@ constexpr int CM_ITEM_ROWS = 1024;
 template <int DH>
 constexpr int cm_win_cb() { return 1; }
 template <int DH>
-constexpr int cm_win_threads() { return 512 / cm_win_cb<DH>(); }
+constexpr int cm_win_rows() { return 128; }  // (64-row tiles at d = 128, two workgroups per CU: no faster)
+template <int DH>
+constexpr int cm_win_threads() { return cm_win_rows<DH>() / (16 * cm_win_cb<DH>()) * 64; }
 
 __global__ __launch_bounds__(256) void k_cm_items(const int* __restrict__ off, int2* __restrict__ items,
                                                   int* __restrict__ nitems, int* __restrict__ scratch,
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
   constexpr int RW = 16 * CB;              // rows per wave
   constexpr int NT = cm_win_threads<DH>(); // 128 rows per tile
   constexpr int VPT = 2 * SG::KV / NT;     // staged 16-byte vectors per thread and block
-  constexpr int R = 128;
+  constexpr int R = cm_win_rows<DH>();
   constexpr int TP = R / G;
   constexpr int KS = DH / 32;
   constexpr int MB = DH / 16;
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
   const int kv_lo = n_distant(p0, W, S) * S;
   const int nW = (plast - kv_lo) / 64 + 1;
   // blocks in flight in registers: two sets (blocks n + 2, n + 3)
-  constexpr int NSET = 2;
+  constexpr int NSET = VPT > 4 ? 1 : 2;
   u32x4 stg[2][VPT];
   auto issue = [&](u32x4 (&rg)[VPT], int n) __attribute__((always_inline)) {
     const int kv0 = kv_lo + 64 * min(n, nW - 1);
@@ -495,14 +497,16 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
   }
 
   // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (dims in
-  // fragment order: this lane's 4 MB values are contiguous). SLG slots at a
-  // time: their weights, then all their loads, then the sums, so that the
-  // loads are in flight together. The two row blocks run one after the other
-  // (kept rolled: unrolled, both blocks' loads were live at once and the
-  // kernel needed ~480 registers at d = 128, one wave per SIMD; rolled, with
-  // four slots in flight, it fits two waves per SIMD).
-  constexpr int VPS = 4 * MB * (int)sizeof(T) / 16;  // 16-byte vectors per lane and slot
-  constexpr int SLG = 4;
+  // fragment order: this lane's 4 MB values are contiguous, VPS 16-byte
+  // vectors). Slots go in groups of SLG (32 vectors of partials per lane and
+  // group at d = 128, where the window's registers are free by now; 8 at
+  // d = 64, within the window's budget of four waves per SIMD, since larger
+  // groups cost a wave per SIMD and ran slower): a group's partial loads go
+  // out together with the next group's scores, ids and entry indices, so
+  // that each group costs one load latency.
+  constexpr int VPS = 4 * MB * (int)sizeof(T) / 16;
+  constexpr int SLG = (DH == 64 ? 8 : 32) / VPS;
+  constexpr int NGM = (32 + SLG - 1) / SLG;  // groups at the largest K (32)
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int r = RW * w + 16 * cb + cl;
@@ -514,25 +518,34 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
     const int* rks = rank + ((size_t)bg * N + pc) * K;
     const float* scs = topk_score + ro * K;
     const T* pb = part + (size_t)bg * N * K * G * DH + (size_t)hh * DH + gl * 4 * MB;
-    for (int k0 = 0; k0 < K; k0 += SLG) {
-      float wk[SLG];
-      int ek[SLG];
+    // a group's raw meta: the id (empty slot: negative), score and entry
+    int mid[2][SLG], mrk[2][SLG];
+    float msc[2][SLG];
+    auto meta = [&](int gi, int set) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < SLG; ++j) {
-        const int kk = min(k0 + j, K - 1);
-        const int cc = ids[kk];
-        const bool sel = live && k0 + j < K && cc >= 0;
-        wk[j] = sel ? __expf(scs[kk] - Lr[cb]) : 0.f;
-        ek[j] = sel ? rks[kk] : 0;
+        const int kk = min(gi * SLG + j, K - 1);
+        mid[set][j] = ids[kk];
+        msc[set][j] = scs[kk];
+        mrk[set][j] = rks[kk];
       }
+    };
+    meta(0, 0);
+#pragma unroll
+    for (int gi = 0; gi < NGM; ++gi) {
+      if (gi * SLG >= K) break;  // uniform
+      const int set = gi & 1;
+      float wk[SLG];
       u32x4 pv[SLG][VPS];
 #pragma unroll
       for (int j = 0; j < SLG; ++j) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(pb + (size_t)ek[j] * G * DH);
+        const bool sel = live && gi * SLG + j < K && mid[set][j] >= 0;
+        wk[j] = sel ? __expf(msc[set][j] - Lr[cb]) : 0.f;
+        const u32x4* src = reinterpret_cast<const u32x4*>(pb + (size_t)(sel ? mrk[set][j] : 0) * G * DH);
 #pragma unroll
-        for (int x = 0; x < VPS; ++x)
-          pv[j][x] = wk[j] != 0.f ? src[x] : u32x4{0u, 0u, 0u, 0u};
+        for (int x = 0; x < VPS; ++x) pv[j][x] = sel ? src[x] : u32x4{0u, 0u, 0u, 0u};
       }
+      if (gi + 1 < NGM && (gi + 1) * SLG < K) meta(gi + 1, set ^ 1);
 #pragma unroll
       for (int j = 0; j < SLG; ++j) {
         if constexpr (sizeof(T) == 2) {
@@ -547,8 +560,7 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
           }
         } else {
 #pragma unroll
-          for (int x = 0; x < VPS; ++x)
-            oacc[x][cb] += wk[j] * __builtin_bit_cast(f32x4, pv[j][x]);
+          for (int x = 0; x < VPS; ++x) oacc[x][cb] += wk[j] * __builtin_bit_cast(f32x4, pv[j][x]);
         }
       }
     }
@@ -606,7 +618,7 @@ template <typename T, int G, int DH>
 hipError_t cm_window_go(const Dims& p, const void* q, const void* k, const void* vt, int Np,
                         const int32_t* idx, const float* sc, const float* sl, const int* rank,
                         const void* part, void* o, float* lse, hipStream_t st) {
-  constexpr int TP = 128 / G;
+  constexpr int TP = cm_win_rows<DH>() / G;
   const int ntiles = (p.N + TP - 1) / TP;
   const size_t lds = cm_window_lds<T, DH>();
   auto kern = k_fwd_cm_window<T, G, DH>;

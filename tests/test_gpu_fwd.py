@@ -83,8 +83,11 @@ def test_fwd_tiny_workload():
 
 
 @pytest.mark.parametrize("G,d,r,K", [
-    (4, 128, 32, 6),    # GQA: fp32 calibrated queries, per-head scores in their own pass
-    (1, 64, 32, 6),     # one head per KV group, bf16, rank 32: Q-Cal folded into routing (u)
+    (4, 128, 32, 6),    # GQA: fp32 calibrated queries, per-head scores in routing's epilogue
+    (2, 64, 64, 12),    # two heads per group, rank 64
+    (4, 64, 64, 6),     # four heads per group, d = 64
+    (2, 128, 32, 20),   # K > 16 with grouped heads
+    (1, 64, 32, 6),     # one head per KV group, bf16, rank 32: folded
     (1, 128, 64, 12),   # the same with rank 64 and d = 128
     (1, 64, 32, 20),    # K > 16: fp32 calibrated queries with one head per group
     (2, 64, 0, 6),      # no Q-Cal

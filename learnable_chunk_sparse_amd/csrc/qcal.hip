@@ -4,7 +4,9 @@
 // chunk scores, so it is produced in fp32:
 //   u[t, h*r + j] = sum_D h[t, D] W_down[h, j, D]        (GEMM 1)
 //   q_hat[b, h, i, :] = q[b, h, i, :] + W_up[h] u[t, h*r : h*r + r]   (GEMM 2)
-// One workgroup owns 128 tokens x 128 columns of u (128 / r heads).
+// One workgroup owns 128 tokens x 128 columns of u (128 / r heads). The
+// column blocks of one token block run back to back on one XCD, so the
+// hidden-state tile comes from HBM once and from that XCD's L2 after.
 // GEMM 1 runs on 16x16x32 bf16 MFMAs (exact products, fp32 accumulation)
 // over LDS tiles of 32-deep k steps, with the next step's global loads
 // prefetched into registers while the current one is multiplied. GEMM 2
@@ -40,8 +42,16 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
   const int wm = w & 1, wn = w >> 1;
-  const int t0 = blockIdx.x * QT_M, c0 = blockIdx.y * QT_N;
   const int ncol = Hq * r;
+  int t0, c0;
+  {
+    // 1-D grid, column block fastest; each XCD walks one contiguous range
+    const int ncb = (ncol + QT_N - 1) / QT_N, nwg = gridDim.x, L = blockIdx.x;
+    const int xcd = L % NXCD, kx = L / NXCD, qx = nwg / NXCD, rem = nwg % NXCD;
+    const int Lp = xcd * qx + min(xcd, rem) + kx;
+    t0 = (Lp / ncb) * QT_M;
+    c0 = (Lp % ncb) * QT_N;
+  }
 
   // global -> register prefetch: each thread moves 16 elements of A and of B
   // per k step (two 8-element vectors each)
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
 hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, const void* W_down,
                        const void* W_up, float* q_hat, float* u, hipStream_t st) {
   const int ntok = p.B * Nq;
-  dim3 grid((ntok + QT_M - 1) / QT_M, (p.Hq * p.r + QT_N - 1) / QT_N);
+  dim3 grid((unsigned)(((ntok + QT_M - 1) / QT_M) * ((p.Hq * p.r + QT_N - 1) / QT_N)));
   const size_t el = p.dtype == 1 ? 2 : 4;
   const size_t lds = std::max<size_t>((size_t)(QT_M + QT_N) * QT_KP * el, (size_t)QT_M * QT_UP * 4);
   auto go = [&](auto kern, auto tq) -> hipError_t {

@@ -439,6 +439,51 @@ def event_ring(n, torch):
     return st, sp
 
 
+def outer_median_us(fn, n, torch, flush, sink, graph):
+    """Median µs of n calls of fn (graph: replays of fn captured in a HIP
+    graph), each after a read of the flush buffer (cold cache), between two
+    events on torch's stream recorded outside the call: the same clock for
+    eager launches and graph replays."""
+    fn()
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+    ev = event_ring(n, torch)
+    for j in range(n):
+        torch.sum(flush, dim=0, out=sink)
+        ev[0][j].record()
+        if g is not None:
+            g.replay()
+        else:
+            fn()
+        ev[1][j].record()
+    torch.cuda.synchronize()
+    tt = sorted(a.elapsed_time(b) for a, b in zip(*ev))
+    del g
+    return tt[len(tt) // 2] * 1e3
+
+
+def copy_reference_gbs(n, torch, flush):
+    """GB/s (bytes read + bytes written) of a plain device-to-device copy of
+    the flush buffer into a second buffer of its size: what the runtime's own
+    streaming copy reaches on this device, as context for the HBM
+    fractions."""
+    dst = torch.empty_like(flush)
+    dst.copy_(flush)
+    ev = event_ring(n, torch)
+    for j in range(n):
+        ev[0][j].record()
+        dst.copy_(flush)
+        ev[1][j].record()
+    torch.cuda.synchronize()
+    tt = sorted(a.elapsed_time(b) for a, b in zip(*ev))
+    del dst
+    return 2 * flush.numel() * flush.element_size() / (tt[len(tt) // 2] * 1e-3) / 1e9
+
+
 def avg_ms(st, sp):
     return sum(a.elapsed_time(b) for a, b in zip(st, sp)) / len(st)
 
@@ -590,24 +635,14 @@ def bench_decode(args, torch, L):
                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
 
     def graph_median(fn):
-        """Median µs of replays of fn captured in a HIP graph (cold cache)."""
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        ev = event_ring(n, torch)
-        for j in range(n):
-            torch.sum(flush, dim=0, out=sink)
-            ev[0][j].record()
-            g.replay()
-            ev[1][j].record()
-        torch.cuda.synchronize()
-        tt = sorted(a.elapsed_time(b) for a, b in zip(*ev))
-        del g
-        return tt[len(tt) // 2] * 1e3
+        return outer_median_us(fn, n, torch, flush, sink, graph=True)
 
     out["graph_us_per_step"] = graph_median(step)
+    # the eager step on the graph's clock (events outside the call), and a
+    # plain 512 MiB device copy as the device's practical streaming rate
+    out["eager_outer_us_per_step"] = outer_median_us(step, n, torch, flush, sink, graph=False)
+    out["copy_reference"] = {"what": "device copy of a 512 MiB buffer (read + write bytes)",
+                             "unit": "GB/s", "achieved": copy_reference_gbs(n, torch, flush)}
     if not args.no_paged:
         # the same caches as pages of one chunk each, in a shuffled order
         B, Hkv, N, d = t["k"].shape
@@ -682,24 +717,15 @@ def bench_decode_long(args, torch, L):
     times = sorted(rec.times(L.STEP_DECODE))
     rec = None
     med = times[len(times) // 2]
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    ev = event_ring(n, torch)
-    for j in range(n):
-        torch.sum(flush, dim=0, out=sink)
-        ev[0][j].record()
-        g.replay()
-        ev[1][j].record()
-    torch.cuda.synchronize()
-    tg = sorted(a.elapsed_time(b) for a, b in zip(*ev))
+    g_us = outer_median_us(step, n, torch, flush, sink, graph=True)
+    e_us = outer_median_us(step, n, torch, flush, sink, graph=False)
     nbytes = decode_bytes(wl)
     gbs = nbytes / (med * 1e-3) / 1e9
-    out = {"workload": wl.name, "us_per_step": med * 1e3, "graph_us_per_step": tg[len(tg) // 2] * 1e3,
-           "median_of": n, "cold_cache": True,
+    out = {"workload": wl.name, "us_per_step": med * 1e3, "graph_us_per_step": g_us,
+           "eager_outer_us_per_step": e_us, "median_of": n, "cold_cache": True,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
-    del g, t, bufs, flush, sink
+    del t, bufs, flush, sink
     torch.cuda.empty_cache()
     return out
 

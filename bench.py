@@ -132,6 +132,10 @@ TRAFFIC = {
                                  ["attn_fwd.hip", "attn_fwd_sparse.hip", "hils_common.h"]),
     ("route", "prefill_345m_512k"): ("route__prefill_345m_512k__hbm_traffic.md",
                                      ["route.hip", "hils_common.h"]),
+    # decode: the whole step (its four launches) per call
+    ("decode", "decode_7b_512k"): ("decode__decode_7b_512k__hbm_traffic.md",
+                                   ["decode.hip", "hils_common.h"]),
+    ("decode", "decode_4m"): ("decode__decode_4m__hbm_traffic.md", ["decode.hip", "hils_common.h"]),
 }
 
 
@@ -398,15 +402,23 @@ def _decode_long_baseline(wl):
 # --------------------------------------------------------------------------
 def profile_sample(torch, L, workload="prefill_1p4b"):
     """A short fixed run for rocprofv3 counter passes: three prefill forwards
-    of the workload, then the calibration copy (1 GiB fp32 read, 1 GiB
-    written) whose FETCH_SIZE / WRITE_SIZE scale the kernel's counters."""
+    (or decode steps) of the workload, then the calibration copy (1 GiB fp32
+    read, 1 GiB written) whose FETCH_SIZE / WRITE_SIZE scale the kernel's
+    counters."""
     from workloads import WORKLOADS, make_inputs
     wl = WORKLOADS[workload]
     t = make_inputs(wl, device="cuda")
-    bufs = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
-    for _ in range(3):
-        L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W, h=t.get("h"),
-                        W_down=t.get("W_down"), W_up=t.get("W_up"), out=bufs)
+    if wl.mode == "decode":
+        bufs = L.decode_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+        for _ in range(3):
+            L.hils_decode(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
+                          seq_len=t["seq_len"], h=t.get("h"), W_down=t.get("W_down"),
+                          W_up=t.get("W_up"), out=bufs)
+    else:
+        bufs = L.fwd_buffers(t["q"], t["k"], wl.S, wl.K, wl.W, t.get("h"), t.get("W_down"))
+        for _ in range(3):
+            L.hils_attn_fwd(t["q"], t["k"], t["v"], t["kL"], t["e"], wl.S, wl.K, wl.W,
+                            h=t.get("h"), W_down=t.get("W_down"), W_up=t.get("W_up"), out=bufs)
     torch.cuda.synchronize()
     del t, bufs
     torch.cuda.empty_cache()
@@ -632,7 +644,8 @@ def bench_decode(args, torch, L):
     gbs = nbytes / (med * 1e-3) / 1e9
     out = {"workload": wl.name, "us_per_step": med * 1e3, "median_of": n, "cold_cache": True,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                        "traffic": recorded_traffic("decode", wl.name)}}
 
     def graph_median(fn):
         return outer_median_us(fn, n, torch, flush, sink, graph=True)
@@ -724,7 +737,8 @@ def bench_decode_long(args, torch, L):
     out = {"workload": wl.name, "us_per_step": med * 1e3, "graph_us_per_step": g_us,
            "eager_outer_us_per_step": e_us, "median_of": n, "cold_cache": True,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+                        "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                        "traffic": recorded_traffic("decode", wl.name)}}
     del t, bufs, flush, sink
     torch.cuda.empty_cache()
     return out

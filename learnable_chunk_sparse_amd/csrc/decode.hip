@@ -15,10 +15,11 @@
 //                 order: every chunk of the overall top-K is among them.
 //   k_dec_select_window
 //                 blocks 0 .. B Hkv - 1: the top-K of one (sequence, KV head)'s
-//                 candidates by a 4-pass 8-bit radix select over
-//                 order-preserving integer keys held in registers, ties
-//                 resolved by lower chunk index, the chosen ids written in
-//                 ascending order by a prefix sum (no sort). The other blocks
+//                 candidates, ties resolved by lower chunk index, the chosen
+//                 ids in ascending order (no sort): one wave of ballots for
+//                 up to 512 candidates, longer lists by a 4-pass 8-bit radix
+//                 select over order-preserving integer keys held in
+//                 registers, placed by a prefix sum. The other blocks
 //                 run the window units, which do not depend on the selection
 //                 and keep HBM busy meanwhile.
 //   k_dec_chunks  the selected-chunk units.
@@ -69,19 +70,24 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
   return x - v;
 }
 
-// The kc = min(Kc, valid) best of 512 scores sc[0..512) (chunk ids c0 + i,
-// those >= nd absent) by (score desc, index asc), written in ascending chunk
-// order to os / oi; slots kc .. Kc-1 get id -1. One wave; lane l holds
-// entries 8l .. 8l + 7 as order-preserving keys; the exact key T of the
-// kc-th best is found bit by bit from the top with wave-wide counts
-// (popcounts of ballots), and the first krem keys equal to T (lowest
-// indices) are taken. Any chunk of the overall top-K is in the top-K of its
-// own 512.
-__device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, int nd, int Kc,
-                                          float* __restrict__ os, int32_t* __restrict__ oi) {
+// The kc = min(Kc, #entries) best entries of a list of at most 512 (score,
+// chunk id) entries by (score desc, list position asc), written in list
+// order to os / oi (os may be null); slots kc .. Kc-1 get id -1. Entry i
+// exists when i < nv and, given an id list, ids[i] >= 0; without one its id
+// is c0 + i. Both arrays must hold 512 readable entries. One wave; lane l
+// holds entries 8l .. 8l + 7 as order-preserving keys (0 = no entry); the
+// exact key T of the kc-th best is found bit by bit from the top with
+// wave-wide counts (popcounts of ballots), and the first krem keys equal to
+// T (earliest in the list) are taken. Lists in ascending chunk order
+// therefore break ties by lower chunk index, and the best Kc of a
+// concatenation of such lists are among the lists' own best Kc.
+__device__ __forceinline__ void wave_topk(const float* __restrict__ sc, const int32_t* __restrict__ ids,
+                                          int c0, int nv, int Kc, float* __restrict__ os,
+                                          int32_t* __restrict__ oi) {
   const int lane = threadIdx.x & 63;
   uint32_t kk[8];
   float sv[8];
+  int iv[8];
   {
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(sc + 8 * lane);
     const f32x4 x1 = *reinterpret_cast<const f32x4*>(sc + 8 * lane + 4);
@@ -90,12 +96,23 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, 
       sv[i] = x0[i];
       sv[4 + i] = x1[i];
     }
+    if (ids != nullptr) {
+      const int4 y0 = *reinterpret_cast<const int4*>(ids + 8 * lane);
+      const int4 y1 = *reinterpret_cast<const int4*>(ids + 8 * lane + 4);
+      iv[0] = y0.x; iv[1] = y0.y; iv[2] = y0.z; iv[3] = y0.w;
+      iv[4] = y1.x; iv[5] = y1.y; iv[6] = y1.z; iv[7] = y1.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kk[i] = c0 + 8 * lane + i < nd ? ord_f(sv[i]) : 0u;
+      for (int i = 0; i < 8; ++i) iv[i] = c0 + 8 * lane + i;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kk[i] = (8 * lane + i < nv && iv[i] >= 0) ? ord_f(sv[i]) : 0u;
   }
-  const int nv = min(512, nd - c0);
-  const int kc = min(Kc, nv);
-  const bool all = nv <= kc;
+  int nvalid = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nvalid += __popcll(__ballot(kk[i] != 0u));
+  const int kc = min(Kc, nvalid);
+  const bool all = nvalid <= kc;
   uint32_t prefix = 0u;
   int krem = kc;
   if (!all) {
@@ -139,14 +156,14 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ sc, int c0, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (taken(i, tr)) {
-        os[o] = sv[i];
-        oi[o] = c0 + 8 * lane + i;
+        if (os != nullptr) os[o] = sv[i];
+        oi[o] = iv[i];
         ++o;
       }
     }
   }
   for (int x = tot + lane; x < Kc; x += 64) {
-    os[x] = 0.f;
+    if (os != nullptr) os[x] = 0.f;
     oi[x] = -1;
   }
 }
@@ -263,7 +280,7 @@ __global__ __launch_bounds__(256) void k_dec_scan(const QT* __restrict__ qs, con
   }
   wave_lds_sync();
   const size_t ob = (size_t)bg * cstride + (size_t)(c_w / (CPW / 4)) * Kc;
-  wave_topk(sw, c_w, nd, Kc, cand_s + ob, cand_i + ob);
+  wave_topk(sw, nullptr, c_w, nd - c_w, Kc, cand_s + ob, cand_i + ob);
 }
 
 // ---------------------------------------------------------------- select
@@ -778,10 +795,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k_dec_select_wind
     int32_t* to = topk_out != nullptr ? topk_out + (size_t)bg * a.K : nullptr;
     const float* cs = cand_s + (size_t)bg * cstride;
     const int32_t* ci = cand_i + (size_t)bg * cstride;
-    if (n <= 256 * PER)
+    if (n <= 512) {
+      // one wave of ballots (the other three waves have nothing to do here);
+      // longer lists are faster through the radix select below
+      __shared__ __align__(16) int32_t s_sel[64];
+      if (threadIdx.x < 64) {
+        wave_topk(cs, ci, 0, n, a.K, nullptr, s_sel);
+        wave_lds_sync();
+        for (int x = threadIdx.x; x < a.K; x += 64) {
+          sl[x] = s_sel[x];
+          if (to != nullptr) to[x] = s_sel[x];
+        }
+      }
+    } else if (n <= 256 * PER) {
       select_block<PER>(cs, ci, n, a.K, sl, to);
-    else
+    } else {
       select_block_big(cs, ci, n, a.K, sl, to);
+    }
     return;
   }
   const int x = blk - nbg;

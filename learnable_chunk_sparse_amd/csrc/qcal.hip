@@ -8,8 +8,10 @@
 // column blocks of one token block run back to back on one XCD, so the
 // hidden-state tile comes from HBM once and from that XCD's L2 after.
 // GEMM 1 runs on 16x16x32 bf16 MFMAs (exact products, fp32 accumulation)
-// over LDS tiles of 32-deep k steps, with the next step's global loads
-// prefetched into registers while the current one is multiplied. GEMM 2
+// over LDS tiles of KS-deep k steps (64 for bf16 where D allows: each row of
+// a step is then one whole 128-byte line, loaded by eight lanes), with the
+// next steps' global loads prefetched into registers while the current one
+// is multiplied. GEMM 2
 // (k = r) reuses the u tile from LDS, split into hi + lo bf16 halves so that
 // the fp32 u keeps ~16 significant bits, and adds q in the epilogue. With no
 // q_hat output only u is produced (GEMM 1 alone).
@@ -22,21 +24,21 @@
 namespace hils {
 
 namespace {
-constexpr int QT_M = 128, QT_N = 128, QT_K = 32;
-constexpr int QT_KP = QT_K + 8;     // padded k pitch of the bf16 tiles (elements)
+constexpr int QT_M = 128, QT_N = 128;
 constexpr int QT_UP = QT_N + 4;     // pitch of the fp32 u tile
 }
 
-template <typename T, int DH, int NS>
+template <typename T, int DH, int NS, int KS>
 __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* __restrict__ hs,
                                               const T* __restrict__ Wd, const T* __restrict__ Wu,
                                               float* __restrict__ qhat, float* __restrict__ u_out,
                                               int ntok, int Nq, int Hq, int d, int D, int r) {
   typedef typename Frag<T>::type FT;
+  constexpr int KP = KS + 8;  // padded k pitch of the operand tiles (elements)
   // LDS: two k-step tiles of A (tokens) and B (u columns), later reused for u
   extern __shared__ __align__(16) unsigned char smem[];
-  T* As = reinterpret_cast<T*>(smem);            // [QT_M][QT_KP]
-  T* Bs = As + QT_M * QT_KP;                     // [QT_N][QT_KP]
+  T* As = reinterpret_cast<T*>(smem);            // [QT_M][KP]
+  T* Bs = As + QT_M * KP;                        // [QT_N][KP]
   float* us = reinterpret_cast<float*>(smem);    // [QT_M][QT_UP] after the k loop
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -53,30 +55,37 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
     c0 = (Lp % ncb) * QT_N;
   }
 
-  // global -> register prefetch: each thread moves 16 elements of A and of B
-  // per k step (two 8-element vectors each)
-  constexpr int VEC = 8;
-  const int lrow = tid >> 1, lk = (tid & 1) * 16;  // row in tile, first k of this thread
-  const int ta = min(t0 + lrow, ntok - 1);
-  const int cb = min(c0 + lrow, ncol - 1);          // columns past Hq*r are never stored
-  const T* asrc = hs + (size_t)ta * D + lk;
-  const T* bsrc = Wd + (size_t)cb * D + lk;
+  // global -> register prefetch: KS / 8 lanes share one row of a k step,
+  // each moving 8 consecutive elements, so a row's step is read contiguously;
+  // NV passes of 256 / (KS / 8) rows cover the 128 rows of A and of B
+  constexpr int VEC = 8, LPR = KS / VEC, RPP = 256 / LPR, NV = QT_M / RPP;
+  static_assert(QT_M % RPP == 0 && QT_N == QT_M, "loader covers whole tiles");
+  const int lrow = tid / LPR, lk = (tid % LPR) * VEC;  // first row and k of this thread
+  const T* asrc[NV];
+  const T* bsrc[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int ta = min(t0 + lrow + RPP * v, ntok - 1);
+    const int cb = min(c0 + lrow + RPP * v, ncol - 1);  // columns past Hq*r are never stored
+    asrc[v] = hs + (size_t)ta * D + lk;
+    bsrc[v] = Wd + (size_t)cb * D + lk;
+  }
   // NS k-steps in flight in a register ring (the loop is unrolled by NS, so
   // the ring indices are fixed; fetches past the end re-read the last step)
-  FT ra[NS][2], rbv[NS][2];
+  FT ra[NS][NV], rbv[NS][NV];
   auto fetch = [&](int s, int k0) __attribute__((always_inline)) {
-    k0 = min(k0, D - QT_K);
+    k0 = min(k0, D - KS);
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      ra[s][v] = ld8<T>(asrc + k0 + VEC * v);
-      rbv[s][v] = ld8<T>(bsrc + k0 + VEC * v);
+    for (int v = 0; v < NV; ++v) {
+      ra[s][v] = ld8<T>(asrc[v] + k0);
+      rbv[s][v] = ld8<T>(bsrc[v] + k0);
     }
   };
   auto stash = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      *reinterpret_cast<FT*>(As + lrow * QT_KP + lk + VEC * v) = ra[s][v];
-      *reinterpret_cast<FT*>(Bs + lrow * QT_KP + lk + VEC * v) = rbv[s][v];
+    for (int v = 0; v < NV; ++v) {
+      *reinterpret_cast<FT*>(As + (lrow + RPP * v) * KP + lk) = ra[s][v];
+      *reinterpret_cast<FT*>(Bs + (lrow + RPP * v) * KP + lk) = rbv[s][v];
     }
   };
 
@@ -87,25 +96,28 @@ __global__ __launch_bounds__(256) void k_qcal(const T* __restrict__ q, const T* 
     for (int b2 = 0; b2 < 4; ++b2) acc[a][b2] = zero4();
 
 #pragma unroll
-  for (int s = 0; s < NS; ++s) fetch(s, s * QT_K);
-  for (int k0 = 0; k0 < D; k0 += NS * QT_K) {
+  for (int s = 0; s < NS; ++s) fetch(s, s * KS);
+  for (int k0 = 0; k0 < D; k0 += NS * KS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       __syncthreads();
       stash(s);
       __syncthreads();
-      fetch(s, k0 + (s + NS) * QT_K);
-      FT af[4], bfr[4];
+      fetch(s, k0 + (s + NS) * KS);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const FT*>(As + (64 * wm + 16 * mb + col) * QT_KP + 8 * grp);
+      for (int kk = 0; kk < KS; kk += 32) {
+        FT af[4], bfr[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        bfr[nb] = *reinterpret_cast<const FT*>(Bs + (64 * wn + 16 * nb + col) * QT_KP + 8 * grp);
+        for (int mb = 0; mb < 4; ++mb)
+          af[mb] = *reinterpret_cast<const FT*>(As + (64 * wm + 16 * mb + col) * KP + kk + 8 * grp);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+        for (int nb = 0; nb < 4; ++nb)
+          bfr[nb] = *reinterpret_cast<const FT*>(Bs + (64 * wn + 16 * nb + col) * KP + kk + 8 * grp);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma16(af[mb], bfr[nb], acc[mb][nb]);
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mma16(af[mb], bfr[nb], acc[mb][nb]);
+      }
     }
   }
   __syncthreads();
@@ -222,9 +234,9 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
   const int ntok = p.B * Nq;
   dim3 grid((unsigned)(((ntok + QT_M - 1) / QT_M) * ((p.Hq * p.r + QT_N - 1) / QT_N)));
   const size_t el = p.dtype == 1 ? 2 : 4;
-  const size_t lds = std::max<size_t>((size_t)(QT_M + QT_N) * QT_KP * el, (size_t)QT_M * QT_UP * 4);
-  auto go = [&](auto kern, auto tq) -> hipError_t {
+  auto go = [&](auto kern, auto tq, int ks) -> hipError_t {
     typedef decltype(tq) TT;
+    const size_t lds = std::max<size_t>((size_t)(QT_M + QT_N) * (ks + 8) * el, (size_t)QT_M * QT_UP * 4);
     if (lds > 64 * 1024) {  // beyond the default dynamic LDS limit only
       hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e2 != hipSuccess) return e2;
@@ -233,14 +245,21 @@ hipError_t launch_qcal(const Dims& p, int Nq, const void* q, const void* h, cons
                        (const TT*)W_up, q_hat, u, ntok, Nq, p.Hq, p.d, p.D, p.r);
     return hipGetLastError();
   };
-  // four k steps in flight when D is a multiple of 128
-  const bool deep = p.D % (4 * QT_K) == 0;
+  // bf16: 64-deep k steps (whole 128-byte rows), two in flight when D is a
+  // multiple of 128; fp32 rows of a 32-deep step are already 128 bytes, four
+  // in flight when D is a multiple of 128. D is a multiple of 32 (checked by
+  // the caller), the fallback steps.
+  const bool deep = p.D % 128 == 0;
   if (p.dtype == 1) {
-    if (p.d == 64) return deep ? go(k_qcal<uint16_t, 64, 4>, uint16_t()) : go(k_qcal<uint16_t, 64, 1>, uint16_t());
-    return deep ? go(k_qcal<uint16_t, 128, 4>, uint16_t()) : go(k_qcal<uint16_t, 128, 1>, uint16_t());
+    if (p.D % 64 != 0) {
+      if (p.d == 64) return go(k_qcal<uint16_t, 64, 1, 32>, uint16_t(), 32);
+      return go(k_qcal<uint16_t, 128, 1, 32>, uint16_t(), 32);
+    }
+    if (p.d == 64) return deep ? go(k_qcal<uint16_t, 64, 2, 64>, uint16_t(), 64) : go(k_qcal<uint16_t, 64, 1, 64>, uint16_t(), 64);
+    return deep ? go(k_qcal<uint16_t, 128, 2, 64>, uint16_t(), 64) : go(k_qcal<uint16_t, 128, 1, 64>, uint16_t(), 64);
   }
-  if (p.d == 64) return deep ? go(k_qcal<float, 64, 4>, float()) : go(k_qcal<float, 64, 1>, float());
-  return deep ? go(k_qcal<float, 128, 4>, float()) : go(k_qcal<float, 128, 1>, float());
+  if (p.d == 64) return deep ? go(k_qcal<float, 64, 4, 32>, float(), 32) : go(k_qcal<float, 64, 1, 32>, float(), 32);
+  return deep ? go(k_qcal<float, 128, 4, 32>, float(), 32) : go(k_qcal<float, 128, 1, 32>, float(), 32);
 }
 
 // ---------------------------------------------------------------- shared pair

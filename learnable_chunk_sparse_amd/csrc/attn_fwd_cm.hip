@@ -21,10 +21,11 @@
 //                    softmax over the 64 tokens, O_c^T = V^T P^T, O_c
 //                    normalised and stored in the input dtype at
 //                    part[b, g][entry][head], entries in the inverse index's
-//                    order (each workgroup writes one contiguous run; dims in
-//                    MFMA D-fragment order: lane group gl's dims
-//                    16 mb + 4 gl + i contiguous, so both kernels move
-//                    16-byte vectors).
+//                    order (each workgroup writes one contiguous run). A row
+//                    is 16-byte pieces, piece 4 x + gl held by lane group gl
+//                    (its x-th vector of MFMA output dims), so the four lanes
+//                    of a row move 64 contiguous bytes per instruction in
+//                    both kernels.
 //   k_fwd_cm_window  query tiles of 128 rows (128 / G positions x G heads):
 //                    banded flash attention over the window with K / V^T
 //                    blocks staged through LDS for the four waves; then
@@ -211,7 +212,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (DH == 64 ? 3 : 2) : 1) void 
         oc[mb] = mma16(ld8<T>(vbs + (16 * mb + cl) * SG::VP + 8 * gl + 32 * ks), pf[ks], oc[mb]);
     if (r.valid) {
       const float inv = 1.0f / ps;
-      T* dst = part + ((size_t)bg * N * K + e0 + r.slot) * G * DH + (size_t)hh * DH + gl * 4 * MB;
+      // vector x of this lane is the row's 16-byte piece 4 x + gl
+      u32x4* dst = reinterpret_cast<u32x4*>(part + ((size_t)bg * N * K + e0 + r.slot) * G * DH +
+                                            (size_t)hh * DH) + gl;
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int m2 = 0; m2 < MB; m2 += 2) {
@@ -221,11 +224,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (DH == 64 ? 3 : 2) : 1) void 
             hv[i] = f2bf(oc[m2][i] * inv);
             hv[4 + i] = f2bf(oc[m2 + 1][i] * inv);
           }
-          *reinterpret_cast<u16x8*>(dst + 4 * m2) = hv;
+          dst[4 * (m2 / 2)] = __builtin_bit_cast(u32x4, hv);
         }
       } else {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4*>(dst + 4 * mb) = oc[mb] * inv;
+        for (int mb = 0; mb < MB; ++mb) dst[4 * mb] = __builtin_bit_cast(u32x4, oc[mb] * inv);
       }
     }
   };
@@ -496,14 +499,14 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
     for (int mb = 0; mb < MB; ++mb) oacc[mb][cb] *= coef;
   }
 
-  // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (dims in
-  // fragment order: this lane's 4 MB values are contiguous, VPS 16-byte
-  // vectors). Slots go in groups of SLG (32 vectors of partials per lane and
-  // group at d = 128, where the window's registers are free by now; 8 at
-  // d = 64, within the window's budget of four waves per SIMD, since larger
-  // groups cost a wave per SIMD and ran slower): a group's partial loads go
-  // out together with the next group's scores, ids and entry indices, so
-  // that each group costs one load latency.
+  // selected chunks: add exp(s_k - L) O_{c_k} from the chunk pass (this
+  // lane's VPS 16-byte vectors are the row's pieces 4 x + gl). Slots go in
+  // groups of SLG (32 vectors of partials per lane and group at d = 128,
+  // where the window's registers are free by now; 8 at d = 64, within the
+  // window's budget of four waves per SIMD, since larger groups cost a wave
+  // per SIMD and ran slower): a group's partial loads go out together with
+  // the next group's scores, ids and entry indices, so that each group costs
+  // one load latency.
   constexpr int VPS = 4 * MB * (int)sizeof(T) / 16;
   constexpr int SLG = (DH == 64 ? 8 : 32) / VPS;
   constexpr int NGM = (32 + SLG - 1) / SLG;  // groups at the largest K (32)
@@ -517,7 +520,7 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
     const int32_t* ids = topk_idx + ((size_t)bg * N + pc) * K;
     const int* rks = rank + ((size_t)bg * N + pc) * K;
     const float* scs = topk_score + ro * K;
-    const T* pb = part + (size_t)bg * N * K * G * DH + (size_t)hh * DH + gl * 4 * MB;
+    const T* pb = part + (size_t)bg * N * K * G * DH + (size_t)hh * DH;
     // a group's raw meta: the id (empty slot: negative), score and entry
     int mid[2][SLG], mrk[2][SLG];
     float msc[2][SLG];
@@ -541,9 +544,9 @@ __global__ __launch_bounds__(cm_win_threads<DH>(), (cm_win_threads<DH>() == 256 
       for (int j = 0; j < SLG; ++j) {
         const bool sel = live && gi * SLG + j < K && mid[set][j] >= 0;
         wk[j] = sel ? __expf(msc[set][j] - Lr[cb]) : 0.f;
-        const u32x4* src = reinterpret_cast<const u32x4*>(pb + (size_t)(sel ? mrk[set][j] : 0) * G * DH);
+        const u32x4* src = reinterpret_cast<const u32x4*>(pb + (size_t)(sel ? mrk[set][j] : 0) * G * DH) + gl;
 #pragma unroll
-        for (int x = 0; x < VPS; ++x) pv[j][x] = sel ? src[x] : u32x4{0u, 0u, 0u, 0u};
+        for (int x = 0; x < VPS; ++x) pv[j][x] = sel ? src[4 * x] : u32x4{0u, 0u, 0u, 0u};
       }
       if (gi + 1 < NGM && (gi + 1) * SLG < K) meta(gi + 1, set ^ 1);
 #pragma unroll

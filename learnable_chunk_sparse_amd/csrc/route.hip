@@ -602,9 +602,25 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
         sv[bb - 1] = sw ? ts : sv[bb - 1];
       }
     int32_t* dst = topk_idx + ((size_t)bg * N + mypos) * K;
+    // a lane's row of K ids is contiguous: 16-byte stores where K and the
+    // pointer allow it (uniform over the wave)
+    const bool v4i = (K & 3) == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0;
+    if (v4i) {
 #pragma unroll
-    for (int k = 0; k < KC; ++k)
-      if (k < K) dst[k] = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
+      for (int k = 0; k < KC; k += 4)
+        if (k < K) {
+          int4 v;
+          v.x = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
+          v.y = ids[k + 1] == 0x7FFFFFFF ? -1 : ids[k + 1];
+          v.z = ids[k + 2] == 0x7FFFFFFF ? -1 : ids[k + 2];
+          v.w = ids[k + 3] == 0x7FFFFFFF ? -1 : ids[k + 3];
+          *reinterpret_cast<int4*>(dst + k) = v;
+        }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KC; ++k)
+        if (k < K) dst[k] = ids[k] == 0x7FFFFFFF ? -1 : ids[k];
+    }
     if constexpr (G >= 2) {
       // the per-head scores below read every position's ids from LDS,
       // position-major ([p][k], K <= SELBUF) in the buffer's space
@@ -625,13 +641,22 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
           lm = mn;
         };
         if constexpr (G == 1) {
+          float so[KC];
 #pragma unroll
-          for (int k = 0; k < KC; ++k)
-            if (k < K) {
-              const bool ok = ids[k] != 0x7FFFFFFF;
-              ds[k] = ok ? sv[k] : __builtin_nanf("");
-              if (ok) lse_add(sv[k]);
-            }
+          for (int k = 0; k < KC; ++k) {
+            const bool ok = k < K && ids[k] != 0x7FFFFFFF;
+            so[k] = ok ? sv[k] : __builtin_nanf("");
+            if (ok) lse_add(sv[k]);
+          }
+          if (v4i && (reinterpret_cast<uintptr_t>(topk_score) & 15) == 0) {
+#pragma unroll
+            for (int k = 0; k < KC; k += 4)
+              if (k < K) *reinterpret_cast<f32x4*>(ds + k) = f32x4{so[k], so[k + 1], so[k + 2], so[k + 3]};
+          } else {
+#pragma unroll
+            for (int k = 0; k < KC; ++k)
+              if (k < K) ds[k] = so[k];
+          }
         }
         // grouped heads: their per-head scores follow below
         if (sel_lse != nullptr)
@@ -655,6 +680,8 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
       constexpr int NKB = (KC + 15) / 16;
       const int* ids_s = &cbc_s[w][0][0];
       const int np = min(PW, N - pw0);  // positions of this wave (uniform; <= 0 past the end)
+      // a lane's four slots are one 16-byte run where K and the pointer allow
+      const bool sc_v4 = (K & 3) == 0 && (reinterpret_cast<uintptr_t>(topk_score) & 15) == 0;
       struct BIn {
         FT kf[KS];
         int c4[4];    // ids of slots 16 kb + 4 grp + i
@@ -713,10 +740,13 @@ __global__ __launch_bounds__(256, (UR > 0 || (G >= 2 && KC <= 16)) ? 2 : 1) void
               }
               if (mine && topk_score != nullptr) {
                 float* dsc = topk_score + (((size_t)b * Hq + g * G + hh) * N + pos) * K;
+                const int s0 = 16 * kb + 4 * grp;
+                if (sc_v4) {
+                  if (s0 < K) *reinterpret_cast<f32x4*>(dsc + s0) = sc;
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int s4 = 16 * kb + 4 * grp + i;
-                  if (s4 < K) dsc[s4] = sc[i];
+                  for (int i = 0; i < 4; ++i)
+                    if (s0 + i < K) dsc[s0 + i] = sc[i];
                 }
               }
               // the position's four lanes (grp = 0..3, same col) combine

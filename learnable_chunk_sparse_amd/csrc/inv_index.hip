@@ -55,7 +55,19 @@ __global__ __launch_bounds__(256) void k_ix_range_scan(int* __restrict__ cnt, in
   if (c >= C) return;
   int* col = cnt + (long)bg * ns * C + c;
   int s = 0;
-  for (int r = 0; r < ns; ++r) {
+  int r = 0;
+  // eight ranges' counts loaded together, then scanned in order
+  for (; r + 8 <= ns; r += 8) {
+    int x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = col[(long)(r + j) * C];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      col[(long)(r + j) * C] = s;
+      s += x[j];
+    }
+  }
+  for (; r < ns; ++r) {
     const int x = col[(long)r * C];
     col[(long)r * C] = s;
     s += x;

@@ -39,7 +39,27 @@ __global__ __launch_bounds__(256) void k_ix_hist(const int32_t* __restrict__ top
   const long per = ((long)N + ns - 1) / ns;
   const long i0 = sp * per, i1 = min((long)N, i0 + per);
   const int32_t* src = topk_idx + (long)bg * N * K;
-  for (long x = i0 * K + tid; x < i1 * K; x += 256) {
+  long x = i0 * K + tid;
+  if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0) {
+    // 16-byte loads, four per thread in flight (the range starts and ends on
+    // a multiple of K, so on whole vectors)
+    const int4* s4 = reinterpret_cast<const int4*>(src + i0 * K);
+    const long n4 = (i1 - i0) * K / 4;
+    for (long v = tid; v < n4; v += 4 * 256) {
+      int4 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = v + 256 * u < n4 ? s4[v + 256 * u] : int4{-1, -1, -1, -1};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cs[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (cs[j] >= 0 && cs[j] < C) atomicAdd(&hist[cs[j]], 1);
+      }
+    }
+    x = i1 * K;  // done
+  }
+  for (; x < i1 * K; x += 256) {
     const int c = src[x];
     if (c >= 0 && c < C) atomicAdd(&hist[c], 1);
   }

@@ -193,6 +193,9 @@ hils_status hils_route(const hils_problem* p, const void* q, const void* kL, con
  * with O_c, lse_c the exact softmax attention of the raw q over chunk c's
  * S tokens and O_W, lse_W over the window. Writes o, lse and topk_idx (all
  * required); topk_idx and lse are the saved tensors hils_attn_bwd consumes.
+ * topk_idx (here, in hils_route and hils_attn_bwd) needs only int32
+ * alignment: the kernels move the ids as 16-byte vectors where the pointer
+ * is 16-byte aligned and K is a multiple of 4, one at a time otherwise.
  */
 hils_status hils_attn_fwd(const hils_problem* p, const void* q, const void* k, const void* v,
                           const void* kL, const void* e, const void* h, const void* W_down,

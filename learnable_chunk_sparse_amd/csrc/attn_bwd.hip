@@ -1149,7 +1149,8 @@ static hipError_t bwd_go(const Dims& p, const void* q, const void* qsrc, const v
                          w.delta, p.N, p.Hkv, p.K, p.W, p.S, p.scale, ntiles, p.C);
       return hipGetLastError();
     };
-    if (bwd_dq_shared_ok(p))
+    // the shared-tile kernel reads the ids as 16-byte vectors
+    if (bwd_dq_shared_ok(p) && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0)
       err = launch_bwd_dq_shared(p, q, k, v, w.kt, w.Np, dO, kL, topk_idx, w.sT, lse, w.Dv, dq,
                                  w.dqhat, w.ds, w.beta, w.delta, st);
     else

@@ -267,7 +267,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && DH == 64) ? 2 : 1) void k_a
 
   // ------------------------------------------------ selections of the tile
   for (int x = tid; x <= ndmax; x += 256) flg[x] = 0;
-  if (K % 4 == 0) {
+  if (K % 4 == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(topk_score) & 15) == 0) {
     // 16-byte vectors, every load issued before any is used (clamped
     // addresses, no per-element branches); at most four per thread (K <= 32)
     // (ids: TP positions; scores: R = TP G rows)

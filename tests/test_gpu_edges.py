@@ -86,3 +86,54 @@ def test_landmark_few_or_no_chunks(N):
         compare("lm e", e32.cpu().double().numpy(), re, "bf16", tol)
         compare("lm dqL", dqL.cpu().double().numpy(), rdq, "bf16", tol)
         compare("lm dk", (dk - dk0)[:, :, :C * 64].cpu().double().numpy(), rdk[:, :, :C * 64], "bf16", tol)
+
+
+def _misaligned_like(t):
+    """A contiguous int32 tensor of t's shape whose data starts 4 bytes past a
+    16-byte boundary (a caller's buffer the kernels may not load or store as
+    16-byte vectors)."""
+    buf = torch.empty(t.numel() + 4, dtype=t.dtype, device=t.device)
+    off = next(j for j in range(1, 4) if (buf.data_ptr() + 4 * j) % 16 != 0)
+    m = buf[off:off + t.numel()].view(t.shape)
+    assert m.data_ptr() % 16 != 0 and m.is_contiguous()
+    return m
+
+
+@pytest.mark.parametrize("strategy", ["union", "compact", "chunk_major"])
+def test_misaligned_topk_idx_buffers(strategy):
+    """K a multiple of 4 with a topk_idx buffer that is 4-byte but not 16-byte
+    aligned: routing stores and the attention kernels read the ids one at a
+    time instead of as 16-byte vectors. The selections equal those written to
+    an aligned buffer; o and lse equal them bit for bit where the strategy
+    sums in a fixed order (union, chunk-major) and match the oracle for the
+    compacted strategy (its rows reach their buckets through atomic counters,
+    so its sums are ordered by arrival); the backward with the misaligned ids
+    (its query pass then takes the per-tile kernel) matches the oracle."""
+    lib = L()
+    sid = {"union": lib.FWD_UNION, "compact": lib.FWD_COMPACT, "chunk_major": lib.FWD_CHUNK_MAJOR}
+    wl = Workload(f"mis_{strategy}", seed=47, dtype="bf16", B=1, Hq=4, Hkv=4, d=64, N=2048, S=64,
+                  K=8, W=128, D=64, r=32, e_range=2.0, mode="train")
+    say(f"case misaligned topk_idx, strategy {strategy}")
+    t = make_inputs(wl)
+    td = to_dev(t)
+    args = (td["q"], td["k"], td["v"], td["kL"], td["e"], wl.S, wl.K, wl.W)
+    kw = dict(h=td["h"], W_down=td["W_down"], W_up=td["W_up"], strategy=sid[strategy])
+    o0, lse0, idx0 = lib.hils_attn_fwd(*args, **kw)
+    o1, lse1, idx1, ws = lib.fwd_buffers(td["q"], td["k"], wl.S, wl.K, wl.W, h=td["h"],
+                                         W_down=td["W_down"], strategy=sid[strategy])
+    idx_m = _misaligned_like(idx1)
+    lib.hils_attn_fwd(*args, out=(o1, lse1, idx_m, ws), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_m, idx0)
+    if strategy == "compact":
+        fwd_parity(t, (o1, lse1, idx_m), wl.S, wl.K, wl.W, "bf16", label=f"misaligned {strategy}")
+    else:
+        assert torch.equal(o1, o0)
+        assert torch.equal(lse1, lse0)
+    g = lib.hils_attn_bwd(td["q"], td["k"], td["v"], td["kL"], td["e"], o0, lse0, idx_m, td["dO"],
+                          wl.S, wl.K, wl.W, h=td["h"], W_down=td["W_down"], W_up=td["W_up"])
+    torch.cuda.synchronize()
+    ref = H.hils_backward(t, t["dO"], wl.S, wl.K, wl.W, forced_topk=idx0.cpu().numpy())
+    for n in ("dq", "dk", "dv", "dkL", "de", "dW_down", "dW_up"):
+        compare(f"misaligned {strategy} {n}", g[n].cpu().double().numpy(), ref[n], "bf16",
+                grad_tol("bf16", ref[n]))
